@@ -1,0 +1,115 @@
+"""Double-precision CPU oracle for causal GQA attention with RoPE (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the product package.  The arithmetic lives
+in ne_oracle.c (see its header for the passages it follows); this module only
+marshals numpy float64 arrays.
+
+Layouts: q, o, dO, dq [B,T,Hq,D]; k, v, dk, dv [B,T,Hkv,D]; lse [B,Hq,T].
+"""
+import ctypes
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _bind(path):
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(ctypes.c_double)
+    i = ctypes.c_int
+    lib.ne_oracle_fwd.argtypes = [P, P, P, P, P, i, i, i, i, i, ctypes.c_double, i]
+    lib.ne_oracle_fwd.restype = i
+    lib.ne_oracle_bwd.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, ctypes.c_double, i]
+    lib.ne_oracle_bwd.restype = i
+    lib.ne_oracle_rope.argtypes = [P, P, i, i, i, i, ctypes.c_double, i]
+    lib.ne_oracle_rope.restype = i
+    lib.ne_oracle_max_threads.argtypes = []
+    lib.ne_oracle_max_threads.restype = i
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = _bind(_build.build(force=False))
+    return _lib
+
+
+class use_library:
+    """Temporarily route this module's calls to another build of the oracle source
+    (the mutation tests compile deliberately broken copies and check that the pins fail)."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _load()
+        _lib = _bind(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _dims(q, k):
+    B, T, Hq, D = q.shape
+    Bk, Tk, Hkv, Dk = k.shape
+    if (Bk, Tk, Dk) != (B, T, D):
+        raise ValueError(f"q {q.shape} and k {k.shape} disagree")
+    return B, T, Hq, Hkv, D
+
+
+def fwd(q, k, v, rope_base, nthreads=0):
+    """Return (o, lse) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, Hq, Hkv, D = _dims(q, k)
+    o = np.empty_like(q)
+    lse = np.empty((B, Hq, T), dtype=np.float64)
+    rc = _load().ne_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                               B, T, Hq, Hkv, D, float(rope_base), int(nthreads))
+    if rc:
+        raise ValueError(f"ne_oracle_fwd rejected the arguments (rc={rc})")
+    return o, lse
+
+
+def bwd(q, k, v, dO, rope_base, nthreads=0):
+    """Return (dq, dk, dv) in float64: the exact gradients of sum(o * dO)."""
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    B, T, Hq, Hkv, D = _dims(q, k)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = _load().ne_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq), _ptr(dk),
+                               _ptr(dv), B, T, Hq, Hkv, D, float(rope_base), int(nthreads))
+    if rc:
+        raise ValueError(f"ne_oracle_bwd rejected the arguments (rc={rc})")
+    return dq, dk, dv
+
+
+def rope(x, rope_base, inverse=False):
+    """Rotate x [B,T,H,D] by R_t (or R_t^T when inverse)."""
+    x = _f64(x)
+    B, T, H, D = x.shape
+    y = np.empty_like(x)
+    rc = _load().ne_oracle_rope(_ptr(x), _ptr(y), B, T, H, D, float(rope_base), int(bool(inverse)))
+    if rc:
+        raise ValueError("ne_oracle_rope rejected the arguments")
+    return y
+
+
+def max_threads():
+    return int(_load().ne_oracle_max_threads())

@@ -1,0 +1,263 @@
+/*
+ * ne_oracle.c -- double-precision CPU oracle for causal grouped-query attention
+ * with rotary position embeddings (RoPE), forward and backward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark do.  It shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes, and where the pages state it:
+ *   - RoPE applied to queries and keys: "NanoEuler: 使用 C 和 CUDA 从零开始构建的
+ *     GPT-2 规模 LLM" (agentlenshq), section "技术规格" (technical specs).
+ *   - Grouped-query attention: a smaller set of key/value heads is shared by
+ *     groups of query heads -- same page, "技术规格" and the table "模型配置"
+ *     (12 q / 4 kv heads on the GPU model, 4 / 2 on the CPU model).
+ *   - Decoder-only transformer, hence a causal mask -- same page, "核心架构与设计".
+ *   - The tiled online-softmax kernel computes exactly softmax attention without
+ *     storing the T x T matrix -- same page, "内核实现"; and "用 100KB C/CUDA 单文件
+ *     复刻 GPT-2:NanoEuler 116M 单卡可跑的全流程拆解" (cnblogs), section 3.4
+ *     "FlashAttention 是性能关键".  The oracle is the plain definition that the
+ *     tiled kernel reaches: it DOES store the full masked T x T matrix.
+ *   - Hand-written backward checked in double precision -- agentlenshq page,
+ *     "验证与稳定性"; cnblogs page, section 2.1 "编译 + gradient check".
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *   RoPE pairs adjacent elements (2i, 2i+1) and rotates them by +t*theta_i with
+ *   theta_i = base^(-2i/D), positions t = 0..T-1, over the whole head dimension;
+ *   base <= 0 disables RoPE.  Softmax scale 1/sqrt(D) applied after RoPE.  Key j
+ *   is visible to query i iff j <= i.  Query head h reads KV head h / (Hq/Hkv).
+ *   LSE is the natural-log log-sum-exp of the scaled scores.  Gradients are
+ *   returned with respect to the un-rotated q and k (inverse rotation R^T).
+ *
+ * Layouts: q, o, dO, dq are [B][T][Hq][D]; k, v, dk, dv are [B][T][Hkv][D];
+ * lse is [B][Hq][T].  All arrays are dense row-major doubles owned by the caller.
+ *
+ * Determinism: every output element is produced by exactly one thread in a fixed
+ * summation order, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define IDX4(b, t, h, d, T, H, D) ((((size_t)(b) * (T) + (t)) * (H) + (h)) * (D) + (d))
+
+static int check_shape(int B, int T, int Hq, int Hkv, int D, double base) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1) return 1;
+    if (Hq % Hkv != 0) return 1;
+    if (base > 0.0 && (D % 2) != 0) return 1;
+    return 0;
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+/* Rotate one head's rows: y[t][:] = R_t x[t][:] (sign = +1) or R_t^T x[t][:]
+ * (sign = -1).  x and y are [T][D] with row stride `stride` doubles.  With
+ * base <= 0 the rotation is the identity.  cos/sin come from libm in double. */
+static void rope_rows(const double* x, size_t xstride, double* y, size_t ystride,
+                      int T, int D, double base, int sign) {
+    for (int t = 0; t < T; ++t) {
+        const double* xr = x + (size_t)t * xstride;
+        double* yr = y + (size_t)t * ystride;
+        if (base <= 0.0) {
+            for (int d = 0; d < D; ++d) yr[d] = xr[d];
+            continue;
+        }
+        for (int i = 0; i < D / 2; ++i) {
+            double theta = pow(base, -2.0 * (double)i / (double)D);
+            double phi = (double)t * theta;
+            double c = cos(phi), s = sin(phi) * (double)sign;
+            double a = xr[2 * i], b = xr[2 * i + 1];
+            yr[2 * i] = a * c - b * s;
+            yr[2 * i + 1] = a * s + b * c;
+        }
+    }
+}
+
+/* Public helper so the tests can check the rotation on its own:
+ * y = R x (inverse = 0) or y = R^T x (inverse = 1), x and y [B][T][H][D]. */
+int ne_oracle_rope(const double* x, double* y, int B, int T, int H, int D,
+                   double base, int inverse) {
+    if (B < 1 || T < 1 || H < 1 || D < 1 || (base > 0.0 && D % 2)) return 1;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            rope_rows(x + IDX4(b, 0, h, 0, T, H, D), (size_t)H * D,
+                      y + IDX4(b, 0, h, 0, T, H, D), (size_t)H * D, T, D, base,
+                      inverse ? -1 : 1);
+    return 0;
+}
+
+/* Probabilities of one (batch, query head): P[i][j] = softmax_j(S[i][j]) over
+ * the visible keys j <= i, S = q' k'^T / sqrt(D).  qr, kr are the rotated
+ * [T][D] rows.  Entries j > i are set to 0 and never dotted.  lse_row[i] gets
+ * m_i + log(sum_j exp(S_ij - m_i)). */
+static void softmax_probs(const double* qr, const double* kr, double* P,
+                          double* lse_row, int T, int D) {
+    const double scale = 1.0 / sqrt((double)D);
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int i = 0; i < T; ++i) {
+        double* Pi = P + (size_t)i * T;
+        double m = -INFINITY;
+        for (int j = 0; j <= i; ++j) {
+            double s = 0.0;
+            for (int d = 0; d < D; ++d) s += qr[(size_t)i * D + d] * kr[(size_t)j * D + d];
+            s *= scale;
+            Pi[j] = s;
+            if (s > m) m = s;
+        }
+        double l = 0.0;
+        for (int j = 0; j <= i; ++j) {
+            Pi[j] = exp(Pi[j] - m);
+            l += Pi[j];
+        }
+        for (int j = 0; j <= i; ++j) Pi[j] /= l;
+        for (int j = i + 1; j < T; ++j) Pi[j] = 0.0;
+        lse_row[i] = m + log(l);
+    }
+}
+
+/* Forward: o = softmax(mask(q' k'^T / sqrt(D))) v, lse as above. */
+int ne_oracle_fwd(const double* q, const double* k, const double* v, double* o,
+                  double* lse, int B, int T, int Hq, int Hkv, int D, double base,
+                  int nthreads) {
+    if (check_shape(B, T, Hq, Hkv, D, base)) return 1;
+    set_threads(nthreads);
+    const int G = Hq / Hkv;
+    double* qr = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* kr = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* P = (double*)malloc(sizeof(double) * (size_t)T * T);
+    if (!qr || !kr || !P) { free(qr); free(kr); free(P); return 2; }
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hq; ++h) {
+            const int g = h / G;  /* GQA: KV head shared by G consecutive query heads */
+            rope_rows(q + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, qr, (size_t)D, T, D, base, 1);
+            rope_rows(k + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, kr, (size_t)D, T, D, base, 1);
+            softmax_probs(qr, kr, P, lse + ((size_t)b * Hq + h) * T, T, D);
+#pragma omp parallel for schedule(static)
+            for (int i = 0; i < T; ++i) {
+                double* orow = o + IDX4(b, i, h, 0, T, Hq, D);
+                for (int d = 0; d < D; ++d) orow[d] = 0.0;
+                for (int j = 0; j <= i; ++j) {
+                    const double p = P[(size_t)i * T + j];
+                    const double* vrow = v + IDX4(b, j, g, 0, T, Hkv, D);
+                    for (int d = 0; d < D; ++d) orow[d] += p * vrow[d];
+                }
+            }
+        }
+    }
+    free(qr); free(kr); free(P);
+    return 0;
+}
+
+/* Backward, given dO: exact gradients of sum(o * dO) with respect to q, k, v.
+ *   dP_ij = dO_i . v_j,   Delta_i = dO_i . o_i,   dS_ij = P_ij (dP_ij - Delta_i)
+ *   dq'_i = sum_j dS_ij k'_j / sqrt(D)
+ *   dk'_j = sum over heads h of the group, sum_i dS_ij q'_i / sqrt(D)
+ *   dv_j  = sum over heads h of the group, sum_i P_ij dO_i
+ *   dq = R^T dq',  dk = R^T dk'.
+ * The heads of a group are accumulated in ascending order. */
+int ne_oracle_bwd(const double* q, const double* k, const double* v, const double* dO,
+                  double* dq, double* dk, double* dv, int B, int T, int Hq, int Hkv,
+                  int D, double base, int nthreads) {
+    if (check_shape(B, T, Hq, Hkv, D, base)) return 1;
+    set_threads(nthreads);
+    const int G = Hq / Hkv;
+    const double scale = 1.0 / sqrt((double)D);
+    double* qr = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* kr = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* orow = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* delta = (double*)malloc(sizeof(double) * (size_t)T);
+    double* lse_row = (double*)malloc(sizeof(double) * (size_t)T);
+    double* P = (double*)malloc(sizeof(double) * (size_t)T * T);
+    double* dS = (double*)malloc(sizeof(double) * (size_t)T * T);
+    double* dqr = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* dkr = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* dvg = (double*)malloc(sizeof(double) * (size_t)T * D);
+    if (!qr || !kr || !orow || !delta || !lse_row || !P || !dS || !dqr || !dkr || !dvg) {
+        free(qr); free(kr); free(orow); free(delta); free(lse_row); free(P); free(dS);
+        free(dqr); free(dkr); free(dvg);
+        return 2;
+    }
+    for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < Hkv; ++g) {
+            rope_rows(k + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, kr, (size_t)D, T, D, base, 1);
+            memset(dkr, 0, sizeof(double) * (size_t)T * D);
+            memset(dvg, 0, sizeof(double) * (size_t)T * D);
+            for (int h = g * G; h < (g + 1) * G; ++h) {
+                rope_rows(q + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, qr, (size_t)D, T, D, base, 1);
+                softmax_probs(qr, kr, P, lse_row, T, D);
+#pragma omp parallel for schedule(dynamic, 8)
+                for (int i = 0; i < T; ++i) {
+                    /* o_i, Delta_i and the row of dS */
+                    double* oi = orow + (size_t)i * D;
+                    const double* dOi = dO + IDX4(b, i, h, 0, T, Hq, D);
+                    for (int d = 0; d < D; ++d) oi[d] = 0.0;
+                    for (int j = 0; j <= i; ++j) {
+                        const double p = P[(size_t)i * T + j];
+                        const double* vj = v + IDX4(b, j, g, 0, T, Hkv, D);
+                        for (int d = 0; d < D; ++d) oi[d] += p * vj[d];
+                    }
+                    double di = 0.0;
+                    for (int d = 0; d < D; ++d) di += dOi[d] * oi[d];
+                    delta[i] = di;
+                    for (int j = 0; j <= i; ++j) {
+                        const double* vj = v + IDX4(b, j, g, 0, T, Hkv, D);
+                        double dp = 0.0;
+                        for (int d = 0; d < D; ++d) dp += dOi[d] * vj[d];
+                        dS[(size_t)i * T + j] = P[(size_t)i * T + j] * (dp - di);
+                    }
+                    for (int j = i + 1; j < T; ++j) dS[(size_t)i * T + j] = 0.0;
+                    /* dq'_i */
+                    double* dqi = dqr + (size_t)i * D;
+                    for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+                    for (int j = 0; j <= i; ++j) {
+                        const double s = dS[(size_t)i * T + j];
+                        for (int d = 0; d < D; ++d) dqi[d] += s * kr[(size_t)j * D + d];
+                    }
+                    for (int d = 0; d < D; ++d) dqi[d] *= scale;
+                }
+                /* dq = R^T dq' for this head */
+                rope_rows(dqr, (size_t)D, dq + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, T, D, base, -1);
+                /* column sums over the query rows i >= j, one thread per key row j */
+#pragma omp parallel for schedule(dynamic, 8)
+                for (int j = 0; j < T; ++j) {
+                    double* dkj = dkr + (size_t)j * D;
+                    double* dvj = dvg + (size_t)j * D;
+                    for (int i = j; i < T; ++i) {
+                        const double s = dS[(size_t)i * T + j] * scale;
+                        const double p = P[(size_t)i * T + j];
+                        const double* qi = qr + (size_t)i * D;
+                        const double* dOi = dO + IDX4(b, i, h, 0, T, Hq, D);
+                        for (int d = 0; d < D; ++d) {
+                            dkj[d] += s * qi[d];
+                            dvj[d] += p * dOi[d];
+                        }
+                    }
+                }
+            }
+            rope_rows(dkr, (size_t)D, dk + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, T, D, base, -1);
+            for (int t = 0; t < T; ++t)
+                memcpy(dv + IDX4(b, t, g, 0, T, Hkv, D), dvg + (size_t)t * D, sizeof(double) * D);
+        }
+    }
+    free(qr); free(kr); free(orow); free(delta); free(lse_row); free(P); free(dS);
+    free(dqr); free(dkr); free(dvg);
+    return 0;
+}
+
+/* Threads the oracle will use (for the benchmark's report). */
+int ne_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,1 +1,7 @@
-"""Causal grouped-query attention with RoPE for AMD MI355X (gfx950)."""
+"""Causal grouped-query attention with RoPE for AMD MI355X (gfx950).
+
+The compute lives in libne_rope_attn.so (hand-written HIP kernels behind the C ABI of
+include/ne_rope_attn.h); `binding` marshals torch tensors to it, and raises if it is missing.
+"""
+from .binding import (NeError, bwd_workspace_bytes, fwd_workspace_bytes, lib,  # noqa: F401
+                      ne_rope_attn_bwd, ne_rope_attn_fwd)

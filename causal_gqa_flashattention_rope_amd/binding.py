@@ -1,0 +1,138 @@
+"""Thin ctypes binding of libne_rope_attn.so (include/ne_rope_attn.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP stream; every
+step of the computation runs in the library's kernels.  There is no fallback: if the HIP
+library is missing or the tensors are not on a GPU, the calls raise.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libne_rope_attn.so")
+
+NE_F32, NE_BF16, NE_F16 = 0, 1, 2
+_DT = {torch.float32: NE_F32, torch.bfloat16: NE_BF16, torch.float16: NE_F16}
+STATUS = {0: "NE_OK", 1: "NE_ERR_NULL", 2: "NE_ERR_SHAPE", 3: "NE_ERR_UNSUPPORTED",
+          4: "NE_ERR_ALIGN", 5: "NE_ERR_WORKSPACE", 6: "NE_ERR_HIP"}
+
+# Every symbol include/ne_rope_attn.h declares.
+EXPORTS = ("ne_rope_attn_fwd_workspace_bytes", "ne_rope_attn_bwd_workspace_bytes",
+           "ne_rope_attn_fwd", "ne_rope_attn_bwd", "ne_status_str", "ne_last_error",
+           "ne_abi_version")
+
+
+class NeError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library with ctypes signatures (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m causal_gqa_flashattention_rope_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, sz, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+    L.ne_rope_attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.ne_rope_attn_fwd_workspace_bytes.restype = sz
+    L.ne_rope_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.ne_rope_attn_bwd_workspace_bytes.restype = sz
+    L.ne_rope_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp, sz, vp]
+    L.ne_rope_attn_fwd.restype = i
+    L.ne_rope_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp, sz, vp]
+    L.ne_rope_attn_bwd.restype = i
+    L.ne_status_str.argtypes = [i]
+    L.ne_status_str.restype = ctypes.c_char_p
+    L.ne_last_error.argtypes = []
+    L.ne_last_error.restype = ctypes.c_char_p
+    L.ne_abi_version.argtypes = []
+    L.ne_abi_version.restype = i
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != 0:
+        raise NeError(status, lib().ne_last_error().decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k must be [B, T, H, D]")
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    return B, T, Hq, Hkv, D
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise RuntimeError("ne_rope_attn runs on the GPU only: tensors must be on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, T, H, D]")
+
+
+def fwd_workspace_bytes(B, T, Hq, Hkv, D, in_dtype):
+    return int(lib().ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, _DT[in_dtype]))
+
+
+def bwd_workspace_bytes(B, T, Hq, Hkv, D, in_dtype):
+    return int(lib().ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, _DT[in_dtype]))
+
+
+def alloc_workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def ne_rope_attn_fwd(q, k, v, rope_base, out_dtype=torch.float32, o=None, lse=None, workspace=None):
+    """o, lse = attention forward.  q [B,T,Hq,D], k/v [B,T,Hkv,D] of one dtype."""
+    _require_gpu(q, k, v)
+    B, T, Hq, Hkv, D = _dims(q, k)
+    if o is None:
+        o = torch.empty((B, T, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    need = fwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype)
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    _check(lib().ne_rope_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D,
+                                  float(rope_base), _DT[q.dtype], _DT[o.dtype], _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream()))
+    return o, lse
+
+
+def ne_rope_attn_bwd(q, k, v, o, lse, dO, rope_base, dq=None, dk=None, dv=None, workspace=None):
+    """dq, dk, dv = attention backward (out dtype = o's dtype)."""
+    _require_gpu(q, k, v, o, lse, dO)
+    B, T, Hq, Hkv, D = _dims(q, k)
+    if dq is None:
+        dq = torch.empty((B, T, Hq, D), dtype=o.dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, T, Hkv, D), dtype=o.dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, T, Hkv, D), dtype=o.dtype, device=q.device)
+    need = bwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype)
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    _check(lib().ne_rope_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, float(rope_base), _DT[q.dtype],
+                                  _DT[o.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream()))
+    return dq, dk, dv

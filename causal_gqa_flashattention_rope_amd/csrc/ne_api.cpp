@@ -1,0 +1,185 @@
+// ne_api.cpp -- the C ABI (include/ne_rope_attn.h): argument validation, workspace layout and
+// dispatch to the gfx950 kernels.  Nothing here allocates, frees, synchronises or prints.
+#include "../../include/ne_rope_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "ne_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ne_status_t fail(ne_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t qh, kh, vh, dOh, delta, lse2, table, total;
+};
+
+bool dtype_ok(ne_dtype_t in, ne_dtype_t out) {
+    if (in == NE_F32) return out == NE_F32;
+    if (in == NE_BF16) return out == NE_F32 || out == NE_BF16;
+    if (in == NE_F16) return out == NE_F32 || out == NE_F16;
+    return false;
+}
+
+ne_status_t check_shape(int B, int T, int Hq, int Hkv, int D) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1)
+        return fail(NE_ERR_SHAPE, "B=%d T=%d Hq=%d Hkv=%d must all be >= 1", B, T, Hq, Hkv);
+    if (Hq % Hkv != 0) return fail(NE_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (D != 32 && D != 64 && D != 128)
+        return fail(NE_ERR_UNSUPPORTED, "head_dim=%d not in {32, 64, 128}", D);
+    if (B > 65535 || Hkv > 65535) return fail(NE_ERR_SHAPE, "B and Hkv must be <= 65535");
+    const int64_t TG = (int64_t)T * (Hq / Hkv);
+    if (TG + 128 > INT32_MAX) return fail(NE_ERR_SHAPE, "T * Hq / Hkv = %lld is too large", (long long)TG);
+    const int64_t n = (int64_t)B * T * Hq * D;
+    if (n > ((int64_t)1 << 46)) return fail(NE_ERR_SHAPE, "tensor of %lld elements is too large", (long long)n);
+    return NE_OK;
+}
+
+Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, ne_dtype_t in) {
+    const size_t esz = in == NE_F32 ? 4 : 2;
+    const size_t nq = (size_t)B * T * Hq * D, nk = (size_t)B * T * Hkv * D;
+    Layout L{};
+    size_t off = 0;
+    L.qh = off; off += up(nq * esz);
+    L.kh = off; off += up(nk * esz);
+    L.vh = off; off += up(nk * esz);
+    if (bwd) {
+        L.dOh = off; off += up(nq * esz);
+        L.delta = off; off += up((size_t)B * T * Hq * 4);
+        L.lse2 = off; off += up((size_t)B * T * Hq * 4);
+        L.table = off; off += up((size_t)T * (D / 2) * 8);
+    }
+    L.total = off;
+    return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+ne_status_t common_checks(int B, int T, int Hq, int Hkv, int D, ne_dtype_t in, ne_dtype_t out) {
+    ne_status_t s = check_shape(B, T, Hq, Hkv, D);
+    if (s != NE_OK) return s;
+    if (!dtype_ok(in, out))
+        return fail(NE_ERR_UNSUPPORTED, "dtype pair in=%d out=%d is not supported", (int)in, (int)out);
+    return NE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ne_abi_version(void) { return NE_ABI_VERSION; }
+
+const char* ne_last_error(void) { return g_err; }
+
+const char* ne_status_str(ne_status_t s) {
+    switch (s) {
+        case NE_OK: return "ok";
+        case NE_ERR_NULL: return "null pointer";
+        case NE_ERR_SHAPE: return "invalid shape";
+        case NE_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+        case NE_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case NE_ERR_WORKSPACE: return "workspace too small";
+        case NE_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t ne_rope_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim, ne_dtype_t in_dtype) {
+    if (check_shape(B, T, Hq, Hkv, head_dim) != NE_OK) return 0;
+    if (in_dtype != NE_F32 && in_dtype != NE_BF16 && in_dtype != NE_F16) return 0;
+    return layout(false, B, T, Hq, Hkv, head_dim, in_dtype).total;
+}
+
+size_t ne_rope_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim, ne_dtype_t in_dtype) {
+    if (check_shape(B, T, Hq, Hkv, head_dim) != NE_OK) return 0;
+    if (in_dtype != NE_F32 && in_dtype != NE_BF16 && in_dtype != NE_F16) return 0;
+    return layout(true, B, T, Hq, Hkv, head_dim, in_dtype).total;
+}
+
+ne_status_t ne_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !lse || !workspace)
+        return fail(NE_ERR_NULL, "ne_rope_attn_fwd: q, k, v, o, lse and workspace must be non-null");
+    ne_status_t s = common_checks(B, T, Hq, Hkv, head_dim, in_dtype, out_dtype);
+    if (s != NE_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        !aligned16(workspace))
+        return fail(NE_ERR_ALIGN, "ne_rope_attn_fwd: every pointer must be 16-byte aligned");
+    if (!std::isfinite(rope_base)) return fail(NE_ERR_SHAPE, "rope_base must be finite");
+    const Layout L = layout(false, B, T, Hq, Hkv, head_dim, in_dtype);
+    if (workspace_bytes < L.total)
+        return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
+    char* ws = (char*)workspace;
+    const int G = Hq / Hkv;
+    ne::PrepArgs pa{};
+    pa.q = q; pa.k = k; pa.v = v;
+    pa.qh = ws + L.qh; pa.kh = ws + L.kh; pa.vh = ws + L.vh;
+    pa.B = B; pa.T = T; pa.Hq = Hq; pa.Hkv = Hkv; pa.D = head_dim;
+    pa.rope_base = rope_base;
+    pa.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    ne::FwdArgs fa{};
+    fa.qh = pa.qh; fa.kh = pa.kh; fa.vh = pa.vh; fa.o = o; fa.lse = lse;
+    fa.B = B; fa.T = T; fa.Hq = Hq; fa.Hkv = Hkv; fa.G = G;
+    fa.nrb = (int)(((int64_t)T * G + 127) / 128);
+    hipError_t e = ne::launch_fwd((int)in_dtype, (int)out_dtype, head_dim, pa, fa, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_attn_fwd: launch failed: %s", hipGetErrorString(e));
+    return NE_OK;
+}
+
+ne_status_t ne_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dO, void* dq, void* dk, void* dv,
+                             int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
+        return fail(NE_ERR_NULL, "ne_rope_attn_bwd: every tensor pointer and the workspace must be non-null");
+    ne_status_t s = common_checks(B, T, Hq, Hkv, head_dim, in_dtype, out_dtype);
+    if (s != NE_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+        return fail(NE_ERR_ALIGN, "ne_rope_attn_bwd: every pointer must be 16-byte aligned");
+    if (!std::isfinite(rope_base)) return fail(NE_ERR_SHAPE, "rope_base must be finite");
+    const Layout L = layout(true, B, T, Hq, Hkv, head_dim, in_dtype);
+    if (workspace_bytes < L.total)
+        return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
+    char* ws = (char*)workspace;
+    const int G = Hq / Hkv;
+    ne::PrepArgs pa{};
+    pa.q = q; pa.k = k; pa.v = v; pa.o = o; pa.lse = lse; pa.dO = dO;
+    pa.qh = ws + L.qh; pa.kh = ws + L.kh; pa.vh = ws + L.vh; pa.dOh = ws + L.dOh;
+    pa.delta = (float*)(ws + L.delta); pa.lse2 = (float*)(ws + L.lse2); pa.table = (float2*)(ws + L.table);
+    pa.B = B; pa.T = T; pa.Hq = Hq; pa.Hkv = Hkv; pa.D = head_dim;
+    pa.rope_base = rope_base;
+    pa.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    ne::BwdArgs ba{};
+    ba.qh = pa.qh; ba.kh = pa.kh; ba.vh = pa.vh; ba.dOh = pa.dOh;
+    ba.delta = pa.delta; ba.lse2 = pa.lse2; ba.table = pa.table;
+    ba.dq = dq; ba.dk = dk; ba.dv = dv;
+    ba.B = B; ba.T = T; ba.Hq = Hq; ba.Hkv = Hkv; ba.G = G;
+    ba.nrb = (int)(((int64_t)T * G + 127) / 128);
+    ba.rope_base = rope_base;
+    ba.scale = (float)(1.0 / std::sqrt((double)head_dim));
+    hipError_t e = ne::launch_bwd((int)in_dtype, (int)out_dtype, head_dim, pa, ba, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_attn_bwd: launch failed: %s", hipGetErrorString(e));
+    return NE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// ne_common.hpp -- gfx950 building blocks shared by the attention kernels.
+//
+// MFMA lane layouts used throughout (wave of 64 lanes, h = lane / 32, c = lane % 32):
+//   32x32x16 f16  : A[i][k] with i = c, k = 8h + j (j = 0..7);  B[k][n] with n = c, k = 8h + j;
+//   32x32x2  f32  : A[i][k] with i = c, k = h;                   B[k][n] with n = c, k = h;
+//   both          : C[m][n] register r (0..15) holds m = 8*(r/4) + 4h + (r%4), n = c.
+// So a 32x32 accumulator gives each lane one output column and 16 rows in four runs of
+// four consecutive rows.  When such an accumulator (over 32 "rows") is fed back as the
+// contraction operand of the next product, its k index is a permutation of the rows:
+//   f16: k-step kk covers rows 16kk..16kk+15; k = 8h + j  <->  row 16kk + 8*(j/4) + 4h + (j%4)
+//   f32: k-step s (0..15 per 32 rows)        ; k = h      <->  row 8*(s/4) + 4h + (s%4)
+// and the other operand is read in that same row order.
+//
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, output lane i element j is
+// element (i % 4) of the 8 bytes addressed by source lane 4j + i/4.  Giving source lane s the
+// address of row (r0 + s/4), columns (c0 + 4(s%4) .. +3) of a row-major 16-bit tile hands
+// output lane i the four values tile[r0 + j][c0 + i], j = 0..3: a transposed read.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ne {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4_tr __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) fp16x4_tr* lds_tr_ptr;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---- storage element conversions ------------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// ---- cross-lane ---------------------------------------------------------------------------
+// v_permlane32_swap(vdst, vsrc) exchanges lanes 32..63 of vdst with lanes 0..31 of vsrc.  With
+// the same value in both operands, each lane ends up holding its own value in one result and
+// its partner's (lane l ^ 32) in the other, so max/sum of the pair combine the two halves and
+// give both halves bit-identical results.
+__device__ __forceinline__ float max_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---- MFMA operand traits ----------------------------------------------------------------
+template <typename OP> struct Mma;
+
+template <> struct Mma<_Float16> {
+    typedef half8 frag;
+    static constexpr int K = 16;  // contraction elements per instruction
+    __device__ __forceinline__ static floatx16 mma(frag a, frag b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    // Fragment along a contiguous contraction run (row-major operand): k-step ks of a row.
+    __device__ __forceinline__ static frag row_frag(const _Float16* row, int ks, int h, int /*len*/) {
+        return *reinterpret_cast<const half8*>(row + 16 * ks + 8 * h);
+    }
+};
+
+template <> struct Mma<float> {
+    typedef float frag;
+    static constexpr int K = 2;
+    __device__ __forceinline__ static floatx16 mma(frag a, frag b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    // Contraction index of k-step ks for lane half h is 2ks + h (the instruction's own order).
+    __device__ __forceinline__ static frag row_frag(const float* row, int ks, int h, int /*len*/) {
+        return row[2 * ks + h];
+    }
+};
+
+// Row (within a 32-row block) that accumulator register r of lane half h holds.
+__device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Contraction operand built from a 32x32 accumulator (rows = contraction index).
+// f16: k-step c (0/1) of the 32-row block packs registers 8c..8c+7.
+__device__ __forceinline__ half8 pack_frag_f16(const floatx16& acc, int c) {
+    half8 f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = (_Float16)acc[8 * c + j];
+    return f;
+}
+
+// Transposed fragment of a row-major 16-bit LDS tile for the f16 product whose contraction
+// runs over the tile's rows in accumulator order: output lane (h, c) receives
+// tile[row0 + 16kk + 8(j/4) + 4h + (j%4)][col0 + c], j = 0..7.
+__device__ __forceinline__ half8 tr_frag_f16(const _Float16* tile, int stride, int kk, int col0) {
+    const int l = lane_id();
+    const int g = l >> 4, s = l & 15, h = l >> 5;
+    const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
+    const int r1 = 16 * kk + 4 * h + (s >> 2);
+    fp16x4_tr lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr_ptr)(tile + r1 * stride + col));
+    fp16x4_tr hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr_ptr)(tile + (r1 + 8) * stride + col));
+    half8 f;
+    half4v a = __builtin_bit_cast(half4v, lo), b = __builtin_bit_cast(half4v, hi);
+    f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+    f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+    return f;
+}
+
+// f32 counterpart: k-step s (0..15) of the 32-row block mb: lane (h, c) reads
+// tile[32mb + acc_row(s, h)][col0 + c].
+__device__ __forceinline__ float tr_frag_f32(const float* tile, int stride, int mb, int s, int col0) {
+    const int l = lane_id();
+    return tile[(32 * mb + acc_row(s, l >> 5)) * stride + col0 + (l & 31)];
+}
+
+// ---- small vector stores of four consecutive output elements -----------------------------
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<floatx4*>(p) = floatx4{a, b, c, d};
+}
+__device__ __forceinline__ void store4(_Float16* p, float a, float b, float c, float d) {
+    *reinterpret_cast<half4v*>(p) = half4v{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+}
+__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+}
+
+}  // namespace ne

@@ -1,0 +1,677 @@
+// ne_kernels.hip -- gfx950 kernels for causal grouped-query attention with RoPE.
+//
+// Passages followed (titles of the pages the method is described on):
+//  * "NanoEuler: 使用 C 和 CUDA 从零开始构建的 GPT-2 规模 LLM" -- 技术规格 (RoPE on queries and keys;
+//    grouped-query attention sharing a smaller set of key/value heads), 核心架构与设计
+//    (decoder-only, no biases), 内核实现 (tiled FlashAttention with an online softmax so the
+//    T x T matrix is never stored), 验证与稳定性 (hand-written backward).
+//  * "用 100KB C/CUDA 单文件复刻 GPT-2:NanoEuler 116M 单卡可跑的全流程拆解" -- §3.4 (tiles of
+//    query/key/value staged in on-chip shared memory; each separate pass such as RoPE costs a
+//    launch and memory traffic, which is why RoPE is folded into the operand preparation here).
+//
+// Pipeline of one call (all stream-ordered, no host synchronisation):
+//  forward : prep  -> q~ = fp16(R(q) * scale * log2 e), k' = fp16(R(k)), v' = fp16(v)  (workspace)
+//            fwd   -> per 128 flattened (token, head) rows of one KV group: online softmax over
+//                     64-key tiles staged once in LDS for all query heads of the group; o, lse.
+//  backward: prep  -> q~, k', v', dO' and Delta = rowsum(dO * o), lse2 = lse * log2 e, cos/sin table
+//            dkdv  -> per 128 keys of one KV head: dK, dV accumulated over every query row of the
+//                     group (all G heads), written once; inverse RoPE in the epilogue.
+//            dq    -> per 128 flattened rows: dQ accumulated over the visible key tiles, written
+//                     once; inverse RoPE in the epilogue.  No atomics: bit-reproducible.
+//
+// Flattened rows: within a (batch, KV head) group the G query heads are interleaved with the
+// tokens, row R = t * G + hh (hh = head within the group).  In the [B][T][Hq][D] input these
+// rows are exactly the memory order of one token's heads, and the causal mask depends only on
+// t = R / G, so any G packs into fixed 128-row blocks that share one K/V tile.
+#include "ne_common.hpp"
+#include "ne_launch.hpp"
+
+namespace ne {
+
+// =====================================================================================
+// Operand preparation.
+// =====================================================================================
+template <int D>
+__device__ __forceinline__ void rope_cs_fill(float2* cs, int t0, int TT, int T, double base) {
+    // cos/sin of t * base^(-2i/D) in double precision, rounded to fp32.
+    for (int idx = threadIdx.x; idx < TT * (D / 2); idx += blockDim.x) {
+        const int tl = idx / (D / 2), i = idx % (D / 2);
+        const int t = t0 + tl;
+        float2 v = make_float2(1.f, 0.f);
+        if (base > 0.0 && t < T) {
+            const double theta = exp2(-2.0 * (double)i / (double)D * log2(base));
+            const double phi = (double)t * theta;
+            v = make_float2((float)cos(phi), (float)sin(phi));
+        }
+        cs[idx] = v;
+    }
+}
+
+template <typename TI, typename OP, int D, bool ROT>
+__device__ __forceinline__ void convert8(const TI* src, OP* dst, const float2* cs_row, int chunk, float mul) {
+    // 8 consecutive elements: chunk*8 .. chunk*8+7, pairs (2i, 2i+1) rotated by cs_row[i].
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = to_f32(src[e]);
+    if (ROT) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const float2 r = cs_row[chunk * 4 + p];
+            const float a = x[2 * p], b = x[2 * p + 1];
+            x[2 * p] = a * r.x - b * r.y;
+            x[2 * p + 1] = a * r.y + b * r.x;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = from_f32<OP>(x[e] * mul);
+}
+
+// grid (ceil(T / TT), B), 256 threads.  Forward: q, k, v.  Backward adds dO, Delta, lse2, table.
+template <typename TI, typename TO, typename OP, int D, bool BWD>
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+    constexpr int TT = 8;
+    constexpr int CPR = D / 8;  // 8-element chunks per row
+    __shared__ float2 cs[TT * (D / 2)];
+    const int t0 = blockIdx.x * TT, b = blockIdx.y;
+    const int T = a.T, Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
+    const bool rope = a.rope_base > 0.0;
+    rope_cs_fill<D>(cs, t0, TT, T, a.rope_base);
+    __syncthreads();
+    if (BWD && b == 0 && rope) {
+        for (int idx = threadIdx.x; idx < TT * (D / 2); idx += blockDim.x) {
+            const int t = t0 + idx / (D / 2);
+            if (t < T) a.table[(size_t)t * (D / 2) + idx % (D / 2)] = cs[idx];
+        }
+    }
+    const int rows_per_tok = BWD ? (2 * Hq + 2 * Hkv) : (Hq + 2 * Hkv);
+    const int items = TT * rows_per_tok * CPR;
+    const int items_pad = (items + 255) / 256 * 256;  // whole waves iterate together
+    const size_t TG = (size_t)T * G;
+    for (int idx = threadIdx.x; idx < items_pad; idx += 256) {
+        const int chunk = idx % CPR;
+        const int rowid = idx / CPR;
+        const int tl = rowid / rows_per_tok;
+        const int which = rowid % rows_per_tok;
+        const int t = t0 + tl;
+        const bool live = idx < items && t < T;
+        const float2* csr = cs + tl * (D / 2);
+        float part = 0.f;  // Delta partial (dO rows only)
+        int dO_row = -1;
+        if (live) {
+            if (which < Hq) {  // q -> q~ (rotated, scaled by scale*log2e), flattened rows
+                const int hq = which, g = hq / G, hh = hq % G;
+                const TI* src = (const TI*)a.q + (((size_t)b * T + t) * Hq + hq) * D + chunk * 8;
+                OP* dst = (OP*)a.qh + (((size_t)b * Hkv + g) * TG + (size_t)t * G + hh) * D + chunk * 8;
+                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, a.qscale);
+                else convert8<TI, OP, D, false>(src, dst, csr, chunk, a.qscale);
+            } else if (which < Hq + Hkv) {  // k -> k'
+                const int g = which - Hq;
+                const TI* src = (const TI*)a.k + (((size_t)b * T + t) * Hkv + g) * D + chunk * 8;
+                OP* dst = (OP*)a.kh + (((size_t)b * Hkv + g) * T + t) * D + chunk * 8;
+                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, 1.f);
+                else convert8<TI, OP, D, false>(src, dst, csr, chunk, 1.f);
+            } else if (which < Hq + 2 * Hkv) {  // v -> v'
+                const int g = which - Hq - Hkv;
+                const TI* src = (const TI*)a.v + (((size_t)b * T + t) * Hkv + g) * D + chunk * 8;
+                OP* dst = (OP*)a.vh + (((size_t)b * Hkv + g) * T + t) * D + chunk * 8;
+                convert8<TI, OP, D, false>(src, dst, csr, chunk, 1.f);
+            } else if (BWD) {  // dO -> dO' (flattened) and the Delta partial sum
+                const int hq = which - Hq - 2 * Hkv, g = hq / G, hh = hq % G;
+                const size_t in_off = (((size_t)b * T + t) * Hq + hq) * D + chunk * 8;
+                const TI* src = (const TI*)a.dO + in_off;
+                const TO* osrc = (const TO*)a.o + in_off;
+                const size_t frow = ((size_t)b * Hkv + g) * TG + (size_t)t * G + hh;
+                OP* dst = (OP*)a.dOh + frow * D + chunk * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = to_f32(src[e]);
+                    part += x * to_f32(osrc[e]);
+                    dst[e] = from_f32<OP>(x);
+                }
+                dO_row = (int)hq;
+                if (chunk == 0) a.lse2[frow] = a.lse[((size_t)b * Hq + hq) * T + t] * kLog2e;
+            }
+        }
+        if (BWD) {
+            // reduce the Delta partials over the CPR consecutive lanes of one row
+#pragma unroll
+            for (int off = 1; off < CPR; off <<= 1) part += __shfl_xor(part, off, 64);
+            if (live && dO_row >= 0 && chunk == 0) {
+                const int g = dO_row / G, hh = dO_row % G;
+                a.delta[((size_t)b * Hkv + g) * TG + (size_t)t * G + hh] = part;
+            }
+        }
+    }
+}
+
+// =====================================================================================
+// Tile staging helpers: a BN x D tile of OP, rows [n0, n0 + BN) of a [rows][D] array, into LDS
+// with row stride STR (elements), zero-filled past `nrows`.
+// =====================================================================================
+template <typename OP, int D, int BN>
+struct TileLoader {
+    static constexpr int EPC = 16 / sizeof(OP);      // elements per 16-byte chunk
+    static constexpr int CPR = D / EPC;              // chunks per row
+    static constexpr int NL = (BN * CPR + 255) / 256;
+    uint4 r[NL];
+    __device__ __forceinline__ void load(const OP* src, int n0, int nrows) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int idx = threadIdx.x + 256 * i;
+            const int row = idx / CPR, ch = idx % CPR;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (idx < BN * CPR && n0 + row < nrows)
+                v = *reinterpret_cast<const uint4*>(src + (size_t)(n0 + row) * D + ch * EPC);
+            r[i] = v;
+        }
+    }
+    template <int STR>
+    __device__ __forceinline__ void store(OP* dst) const {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int idx = threadIdx.x + 256 * i;
+            if (idx >= BN * CPR) continue;
+            const int row = idx / CPR, ch = idx % CPR;
+            OP* p = dst + row * STR + ch * EPC;
+            if ((STR * sizeof(OP)) % 16 == 0) {
+                *reinterpret_cast<uint4*>(p) = r[i];
+            } else {
+                reinterpret_cast<uint2*>(p)[0] = make_uint2(r[i].x, r[i].y);
+                reinterpret_cast<uint2*>(p)[1] = make_uint2(r[i].z, r[i].w);
+            }
+        }
+    }
+};
+
+template <typename OP> struct Strides;
+template <> struct Strides<_Float16> {
+    // row reads of 16 bytes per lane: +8 elements keeps 16 consecutive rows on distinct banks;
+    // transposed reads of 4 rows x 32 bytes per 16 lanes: +16 elements.
+    template <int D> static constexpr int row = D + 8;
+    template <int D> static constexpr int col = D + 16;
+};
+template <> struct Strides<float> {
+    // fp32 row reads (k = 2ks + h): stride = 2 mod 64 banks; column reads: stride = 8 mod 16.
+    template <int D> static constexpr int row = D + 2;
+    template <int D> static constexpr int col = D + 8;
+};
+
+// =====================================================================================
+// Forward.  grid (nrb, Hkv, B), 256 threads = 4 waves x 32 flattened rows.
+// S^T = K Q^T puts one query row per lane (and its 16+16 keys in the two lane halves), so the
+// online-softmax row max and sum are in-lane plus one half swap.  O^T = V^T P^T reuses the
+// accumulator registers of S^T as the contraction operand.
+// =====================================================================================
+template <typename OP, int D, typename TOUT>
+__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+    using M = Mma<OP>;
+    constexpr bool F16 = sizeof(OP) == 2;
+    constexpr int BM = 128, BN = 64;
+    constexpr int KSTR = Strides<OP>::template row<D>;
+    constexpr int VSTR = Strides<OP>::template col<D>;
+    constexpr int KS = D / M::K;
+    constexpr int NDB = D / 32;
+    constexpr int STAGE = BN * (KSTR + VSTR);
+    __shared__ __attribute__((aligned(16))) OP lds[2 * STAGE];
+
+    const int T = a.T, G = a.G, TG = T * G;
+    const int rb = a.nrb - 1 - blockIdx.x;  // longest row blocks first
+    const int hkv = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int R0 = rb * BM;
+    const int Rw = R0 + 32 * w;
+    const int R = Rw + c;
+    const bool rvalid = R < TG;
+    const int t_lane = R / G;
+    const int wave_tmin = Rw / G;
+    const int wave_tmax = min(Rw + 31, TG - 1) / G;
+    const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;
+
+    const size_t grp = (size_t)b * a.Hkv + hkv;
+    const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
+    const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
+    const OP* vg = (const OP*)a.vh + grp * (size_t)T * D;
+
+    typename M::frag qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (rvalid) qf[ks] = M::row_frag(qg + (size_t)R * D, ks, h, D);
+        else qf[ks] = typename M::frag{};
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    floatx16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
+
+    TileLoader<OP, D, BN> kl, vl;
+    kl.load(kg, 0, T);
+    vl.load(vg, 0, T);
+    for (int it = 0; it < ntiles; ++it) {
+        OP* Ks = lds + (it & 1) * STAGE;
+        OP* Vs = Ks + BN * KSTR;
+        kl.template store<KSTR>(Ks);
+        vl.template store<VSTR>(Vs);
+        __syncthreads();
+        if (it + 1 < ntiles) {
+            kl.load(kg, (it + 1) * BN, T);
+            vl.load(vg, (it + 1) * BN, T);
+        }
+        const int n0 = it * BN;
+        if (n0 > wave_tmax) continue;  // every row of this wave precedes the whole tile
+
+        floatx16 s[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            s[mb] = floatx16{};
+            const OP* krow = Ks + (32 * mb + c) * KSTR;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) s[mb] = M::mma(M::row_frag(krow, ks, h, D), qf[ks], s[mb]);
+        }
+        if (n0 + BN - 1 > wave_tmin) {  // tile reaches past some row's diagonal
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (n0 + 32 * mb + acc_row(r, h) > t_lane) s[mb][r] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+        mx = max_halves(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(s[mb][r] - m_new);
+                s[mb][r] = p;
+                psum += p;
+            }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+        if constexpr (F16) {
+            half8 pf[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) pf[kk] = pack_frag_f16(s[kk >> 1], kk & 1);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    oacc[db] = M::mma(tr_frag_f16((const _Float16*)Vs, VSTR, kk, 32 * db), pf[kk], oacc[db]);
+        } else {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int st = 0; st < 16; ++st)
+                        oacc[db] = M::mma(tr_frag_f32((const float*)Vs, VSTR, mb, st, 32 * db), s[mb][st], oacc[db]);
+        }
+    }
+
+    const float l_tot = sum_halves(l_run);
+    const float inv = 1.f / l_tot;
+    if (rvalid) {
+        const int t = t_lane, hh = R - t * G, hq = hkv * G + hh;
+        TOUT* orow = (TOUT*)a.o + (((size_t)b * T + t) * a.Hq + hq) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                store4(orow + 32 * db + 8 * q4 + 4 * h, oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv,
+                       oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
+        if (h == 0) a.lse[((size_t)b * a.Hq + hq) * T + t] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+}
+
+// =====================================================================================
+// Backward, dK/dV.  grid (ceil(T / 128), Hkv, B), 256 threads = 4 waves x 32 keys.
+// S = Q K^T and dP = dO V^T put one key per lane and 16 query rows per lane half, so P and dS
+// feed dV^T += dO^T P and dK^T += Q^T dS directly as contraction operands; dO^T and Q^T come
+// from transposed LDS reads of the row-major tiles.  Every flattened row of the group (all G
+// query heads) passes through the same accumulators: dK and dV of a KV head are summed over
+// its query-head group in registers and written once.
+// =====================================================================================
+template <typename OP, int D, typename TOUT>
+__global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
+    using M = Mma<OP>;
+    constexpr bool F16 = sizeof(OP) == 2;
+    constexpr int BN = 128, BMR = 64;
+    constexpr int QSTR = Strides<OP>::template row<D>;
+    constexpr int KS = D / M::K;
+    constexpr int NDB = D / 32;
+    constexpr int STAGE = 2 * BMR * QSTR;
+    __shared__ __attribute__((aligned(16))) OP lds[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) float rowv[2][2][BMR];  // [stage][lse2 | delta][row]
+
+    const int T = a.T, G = a.G, TG = T * G;
+    const int kb = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int n0 = kb * BN;
+    const int nw = n0 + 32 * w;            // first key of this wave
+    const int key = nw + c;
+    const bool kvalid = key < T;
+    const int keyG = key * G;              // row R sees this key iff R >= key * G
+    const int rstart = (n0 * G) / BMR * BMR;
+    const int ntiles = (TG - rstart + BMR - 1) / BMR;
+
+    const size_t grp = (size_t)b * a.Hkv + hkv;
+    const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
+    const OP* og = (const OP*)a.dOh + grp * (size_t)TG * D;
+    const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
+    const OP* vg = (const OP*)a.vh + grp * (size_t)T * D;
+    const float* lse2g = a.lse2 + grp * (size_t)TG;
+    const float* delg = a.delta + grp * (size_t)TG;
+
+    typename M::frag kf[KS], vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (kvalid) {
+            kf[ks] = M::row_frag(kg + (size_t)key * D, ks, h, D);
+            vf[ks] = M::row_frag(vg + (size_t)key * D, ks, h, D);
+        } else {
+            kf[ks] = typename M::frag{};
+            vf[ks] = typename M::frag{};
+        }
+    }
+    floatx16 dk[NDB], dv[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) { dk[db] = floatx16{}; dv[db] = floatx16{}; }
+
+    TileLoader<OP, D, BMR> ql, ol;
+    float rl = 0.f, rd = 0.f;  // this thread's lse2 / delta prefetch (threads 0..BMR-1)
+    auto gload = [&](int R0) {
+        ql.load(qg, R0, TG);
+        ol.load(og, R0, TG);
+        if (tid < BMR) {
+            const int Rr = R0 + tid;
+            rl = Rr < TG ? lse2g[Rr] : INFINITY;  // padded rows: P = exp2(-inf) = 0
+            rd = Rr < TG ? delg[Rr] : 0.f;
+        }
+    };
+    gload(rstart);
+    for (int it = 0; it < ntiles; ++it) {
+        const int st = it & 1;
+        OP* Qs = lds + st * STAGE;
+        OP* Os = Qs + BMR * QSTR;
+        ql.template store<QSTR>(Qs);
+        ol.template store<QSTR>(Os);
+        if (tid < BMR) { rowv[st][0][tid] = rl; rowv[st][1][tid] = rd; }
+        __syncthreads();
+        const int R0 = rstart + it * BMR;
+        if (it + 1 < ntiles) gload(R0 + BMR);
+        const int Rlast = min(R0 + BMR - 1, TG - 1);
+        if (Rlast < nw * G) continue;  // every row of the tile precedes this wave's keys
+        const bool need_mask = R0 < (nw + 31) * G;
+
+        floatx16 p[2], ds[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            floatx16 sacc = floatx16{}, dpacc = floatx16{};
+            const OP* qrow = Qs + (32 * mb + c) * QSTR;
+            const OP* orow = Os + (32 * mb + c) * QSTR;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                sacc = M::mma(M::row_frag(qrow, ks, h, D), kf[ks], sacc);
+                dpacc = M::mma(M::row_frag(orow, ks, h, D), vf[ks], dpacc);
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int rr = 32 * mb + 8 * q4 + 4 * h;
+                const floatx4 L = *reinterpret_cast<const floatx4*>(&rowv[st][0][rr]);
+                const floatx4 Dl = *reinterpret_cast<const floatx4*>(&rowv[st][1][rr]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q4 + e;
+                    float pv = __builtin_amdgcn_exp2f(sacc[r] - L[e]);
+                    if (need_mask && R0 + rr + e < keyG) pv = 0.f;
+                    p[mb][r] = pv;
+                    ds[mb][r] = pv * (dpacc[r] - Dl[e]);
+                }
+            }
+        }
+        if constexpr (F16) {
+            half8 pf[4], dsf[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                pf[kk] = pack_frag_f16(p[kk >> 1], kk & 1);
+                dsf[kk] = pack_frag_f16(ds[kk >> 1], kk & 1);
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    dv[db] = M::mma(tr_frag_f16((const _Float16*)Os, QSTR, kk, 32 * db), pf[kk], dv[db]);
+                    dk[db] = M::mma(tr_frag_f16((const _Float16*)Qs, QSTR, kk, 32 * db), dsf[kk], dk[db]);
+                }
+        } else {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int s2 = 0; s2 < 16; ++s2) {
+                        dv[db] = M::mma(tr_frag_f32((const float*)Os, QSTR, mb, s2, 32 * db), p[mb][s2], dv[db]);
+                        dk[db] = M::mma(tr_frag_f32((const float*)Qs, QSTR, mb, s2, 32 * db), ds[mb][s2], dk[db]);
+                    }
+        }
+    }
+
+    if (!kvalid) return;
+    // epilogue: dk' = ln2 * sum dS q~ (q~ carries scale * log2 e), then dk = R^T dk'
+    TOUT* dkrow = (TOUT*)a.dk + (((size_t)b * T + key) * a.Hkv + hkv) * D;
+    TOUT* dvrow = (TOUT*)a.dv + (((size_t)b * T + key) * a.Hkv + hkv) * D;
+    const bool rope = a.rope_base > 0.0;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d = 32 * db + 8 * q4 + 4 * h;
+            float x0 = dk[db][4 * q4] * kLn2, x1 = dk[db][4 * q4 + 1] * kLn2;
+            float x2 = dk[db][4 * q4 + 2] * kLn2, x3 = dk[db][4 * q4 + 3] * kLn2;
+            if (rope) {
+                const float2 r0 = a.table[(size_t)key * (D / 2) + d / 2];
+                const float2 r1 = a.table[(size_t)key * (D / 2) + d / 2 + 1];
+                const float y0 = x0 * r0.x + x1 * r0.y, y1 = -x0 * r0.y + x1 * r0.x;
+                const float y2 = x2 * r1.x + x3 * r1.y, y3 = -x2 * r1.y + x3 * r1.x;
+                x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+            }
+            store4(dkrow + d, x0, x1, x2, x3);
+            store4(dvrow + d, dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]);
+        }
+}
+
+// =====================================================================================
+// Backward, dQ (deterministic: a separate pass that recomputes S and dP, no atomics).
+// grid (nrb, Hkv, B), 256 threads = 4 waves x 32 flattened rows, 64-key tiles.
+// S^T = K Q^T and dP^T = V dO^T put one query row per lane; dQ^T += K^T dS^T reads K^T from the
+// same row-major K tile with transposed reads.
+// =====================================================================================
+template <typename OP, int D, typename TOUT>
+__global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
+    using M = Mma<OP>;
+    constexpr bool F16 = sizeof(OP) == 2;
+    constexpr int BM = 128, BN = 64;
+    constexpr int KSTR = Strides<OP>::template row<D>;
+    constexpr int VSTR = Strides<OP>::template row<D>;
+    constexpr int KS = D / M::K;
+    constexpr int NDB = D / 32;
+    constexpr int STAGE = BN * (KSTR + VSTR);
+    __shared__ __attribute__((aligned(16))) OP lds[2 * STAGE];
+
+    const int T = a.T, G = a.G, TG = T * G;
+    const int rb = a.nrb - 1 - blockIdx.x;
+    const int hkv = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int R0 = rb * BM;
+    const int Rw = R0 + 32 * w;
+    const int R = Rw + c;
+    const bool rvalid = R < TG;
+    const int t_lane = R / G;
+    const int wave_tmin = Rw / G;
+    const int wave_tmax = min(Rw + 31, TG - 1) / G;
+    const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;
+
+    const size_t grp = (size_t)b * a.Hkv + hkv;
+    const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
+    const OP* og = (const OP*)a.dOh + grp * (size_t)TG * D;
+    const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
+    const OP* vg = (const OP*)a.vh + grp * (size_t)T * D;
+
+    typename M::frag qf[KS], of[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (rvalid) {
+            qf[ks] = M::row_frag(qg + (size_t)R * D, ks, h, D);
+            of[ks] = M::row_frag(og + (size_t)R * D, ks, h, D);
+        } else {
+            qf[ks] = typename M::frag{};
+            of[ks] = typename M::frag{};
+        }
+    }
+    const float L = rvalid ? a.lse2[grp * (size_t)TG + R] : INFINITY;
+    const float Dl = rvalid ? a.delta[grp * (size_t)TG + R] : 0.f;
+
+    floatx16 dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = floatx16{};
+
+    TileLoader<OP, D, BN> kl, vl;
+    kl.load(kg, 0, T);
+    vl.load(vg, 0, T);
+    for (int it = 0; it < ntiles; ++it) {
+        OP* Ks = lds + (it & 1) * STAGE;
+        OP* Vs = Ks + BN * KSTR;
+        kl.template store<KSTR>(Ks);
+        vl.template store<VSTR>(Vs);
+        __syncthreads();
+        if (it + 1 < ntiles) {
+            kl.load(kg, (it + 1) * BN, T);
+            vl.load(vg, (it + 1) * BN, T);
+        }
+        const int n0 = it * BN;
+        if (n0 > wave_tmax) continue;
+        const bool need_mask = n0 + BN - 1 > wave_tmin;
+
+        floatx16 ds[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            floatx16 sacc = floatx16{}, dpacc = floatx16{};
+            const OP* krow = Ks + (32 * mb + c) * KSTR;
+            const OP* vrow = Vs + (32 * mb + c) * VSTR;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                sacc = M::mma(M::row_frag(krow, ks, h, D), qf[ks], sacc);
+                dpacc = M::mma(M::row_frag(vrow, ks, h, D), of[ks], dpacc);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float pv = __builtin_amdgcn_exp2f(sacc[r] - L);
+                if (need_mask && n0 + 32 * mb + acc_row(r, h) > t_lane) pv = 0.f;
+                ds[mb][r] = pv * (dpacc[r] - Dl);
+            }
+        }
+        if constexpr (F16) {
+            half8 dsf[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) dsf[kk] = pack_frag_f16(ds[kk >> 1], kk & 1);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    dq[db] = M::mma(tr_frag_f16((const _Float16*)Ks, KSTR, kk, 32 * db), dsf[kk], dq[db]);
+        } else {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int s2 = 0; s2 < 16; ++s2)
+                        dq[db] = M::mma(tr_frag_f32((const float*)Ks, KSTR, mb, s2, 32 * db), ds[mb][s2], dq[db]);
+        }
+    }
+
+    if (!rvalid) return;
+    const int t = t_lane, hh = R - t * G, hq = hkv * G + hh;
+    TOUT* dqrow = (TOUT*)a.dq + (((size_t)b * T + t) * a.Hq + hq) * D;
+    const float sc = a.scale;
+    const bool rope = a.rope_base > 0.0;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d = 32 * db + 8 * q4 + 4 * h;
+            float x0 = dq[db][4 * q4] * sc, x1 = dq[db][4 * q4 + 1] * sc;
+            float x2 = dq[db][4 * q4 + 2] * sc, x3 = dq[db][4 * q4 + 3] * sc;
+            if (rope) {
+                const float2 r0 = a.table[(size_t)t * (D / 2) + d / 2];
+                const float2 r1 = a.table[(size_t)t * (D / 2) + d / 2 + 1];
+                const float y0 = x0 * r0.x + x1 * r0.y, y1 = -x0 * r0.y + x1 * r0.x;
+                const float y2 = x2 * r1.x + x3 * r1.y, y3 = -x2 * r1.y + x3 * r1.x;
+                x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+            }
+            store4(dqrow + d, x0, x1, x2, x3);
+        }
+}
+
+// =====================================================================================
+// Launchers.
+// =====================================================================================
+template <typename TI, typename TO, typename OP, int D>
+static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, hipStream_t s) {
+    hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, false>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fwd_kernel<OP, D, TO>), dim3(fa.nrb, fa.Hkv, fa.B), dim3(256), 0, s, fa);
+    return hipGetLastError();
+}
+
+template <typename TI, typename TO, typename OP, int D>
+static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_t s) {
+    hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, true>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3((ba.T + 127) / 128, ba.Hkv, ba.B), dim3(256), 0, s, ba);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb, ba.Hkv, ba.B), dim3(256), 0, s, ba);
+    return hipGetLastError();
+}
+
+#define NE_DISPATCH_D(FN, TI, TO, OP, D, ...)                       \
+    switch (D) {                                                   \
+        case 32: return FN<TI, TO, OP, 32>(__VA_ARGS__);           \
+        case 64: return FN<TI, TO, OP, 64>(__VA_ARGS__);           \
+        case 128: return FN<TI, TO, OP, 128>(__VA_ARGS__);         \
+        default: return hipErrorInvalidValue;                      \
+    }
+
+hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, hipStream_t s) {
+    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, float, float, float, D, pa, fa, s) }
+    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, __bf16, float, _Float16, D, pa, fa, s) }
+    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_fwd_t, __bf16, __bf16, _Float16, D, pa, fa, s) }
+    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, _Float16, float, _Float16, D, pa, fa, s) }
+    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_fwd_t, _Float16, _Float16, _Float16, D, pa, fa, s) }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const BwdArgs& ba, hipStream_t s) {
+    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, float, float, float, D, pa, ba, s) }
+    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, __bf16, float, _Float16, D, pa, ba, s) }
+    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_bwd_t, __bf16, __bf16, _Float16, D, pa, ba, s) }
+    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, _Float16, float, _Float16, D, pa, ba, s) }
+    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_bwd_t, _Float16, _Float16, _Float16, D, pa, ba, s) }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ne

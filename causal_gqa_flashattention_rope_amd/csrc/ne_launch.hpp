@@ -1,0 +1,38 @@
+// ne_launch.hpp -- argument blocks and launchers between the C ABI (ne_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace ne {
+
+// Operand preparation: rotate/scale/convert into the workspace copies.
+struct PrepArgs {
+    const void* q; const void* k; const void* v;   // in dtype, [B][T][H][D]
+    const void* o; const float* lse; const void* dO;  // backward only (o in out dtype)
+    void* qh; void* kh; void* vh; void* dOh;        // operand copies (fp16 or fp32)
+    float* delta; float* lse2; float2* table;       // backward only
+    int B, T, Hq, Hkv, D;
+    double rope_base;
+    float qscale;                                   // softmax scale * log2(e)
+};
+
+struct FwdArgs {
+    const void* qh; const void* kh; const void* vh;
+    void* o; float* lse;
+    int B, T, Hq, Hkv, G, nrb;
+};
+
+struct BwdArgs {
+    const void* qh; const void* kh; const void* vh; const void* dOh;
+    const float* delta; const float* lse2; const float2* table;
+    void* dq; void* dk; void* dv;
+    int B, T, Hq, Hkv, G, nrb;
+    double rope_base;
+    float scale;                                    // softmax scale 1/sqrt(D)
+};
+
+// dtype codes follow ne_dtype_t: 0 = f32, 1 = bf16, 2 = f16.
+hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, hipStream_t s);
+hipError_t launch_bwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const BwdArgs& ba, hipStream_t s);
+
+}  // namespace ne

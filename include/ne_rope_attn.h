@@ -1,0 +1,103 @@
+/*
+ * ne_rope_attn.h -- C ABI of the causal grouped-query attention library with rotary
+ * position embeddings (RoPE), forward and backward, for AMD MI355X (gfx950).
+ *
+ * The operation (see each call below for the passages it follows):
+ *   q' = R(q), k' = R(k)         RoPE on queries and keys ("NanoEuler: 使用 C 和 CUDA 从零
+ *                                开始构建的 GPT-2 规模 LLM", section 技术规格)
+ *   S  = q' k'^T / sqrt(D)       query head h reads key/value head h / (Hq/Hkv): grouped-query
+ *                                attention (same page, 技术规格 and table 模型配置)
+ *   P  = softmax(S masked to key <= query)     decoder-only, hence causal (same page, 核心架构与设计)
+ *   o  = P v,  lse = log sum exp(S) per row    computed tile by tile with an online softmax so that
+ *                                the T x T matrix is never stored (same page, 内核实现; "用 100KB
+ *                                C/CUDA 单文件复刻 GPT-2:NanoEuler 116M 单卡可跑的全流程拆解", §3.4)
+ *   backward: gradients of sum(o * dO) with respect to the un-rotated q, k and v
+ *                                (hand-written backward: agentlenshq page, 验证与稳定性).
+ * Readings where the pages are silent: RoPE rotates adjacent pairs (2i, 2i+1) by +t*theta_i,
+ * theta_i = rope_base^(-2i/D), positions t = 0..T-1; rope_base <= 0 disables RoPE; the softmax
+ * scale is 1/sqrt(head_dim); key j is visible to query i iff j <= i; lse is the natural log.
+ *
+ * Layouts (dense, row-major, element strides only):
+ *   q, o, dO, dq : [B][T][Hq][head_dim]
+ *   k, v, dk, dv : [B][T][Hkv][head_dim]
+ *   lse          : [B][Hq][T], always float32
+ *
+ * Ownership: every tensor pointer and the workspace are DEVICE pointers allocated and owned by
+ * the caller.  The library never allocates, frees, synchronises or prints on the compute calls.
+ * Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs asynchronously;
+ * device-side faults surface at the caller's next synchronisation.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued; on failure the call
+ * returns a non-zero ne_status_t, enqueues nothing, and ne_last_error() gives a thread-local
+ * message.  NE_ERR_HIP means a launch was rejected by the HIP runtime (hipGetLastError).
+ *
+ * Thread safety: calls are re-entrant; the only mutable library state is the thread-local error
+ * message.  Two calls that share a workspace must be ordered on one stream.
+ */
+#ifndef NE_ROPE_ATTN_H
+#define NE_ROPE_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NE_ABI_VERSION 1
+
+typedef enum { NE_F32 = 0, NE_BF16 = 1, NE_F16 = 2 } ne_dtype_t;
+
+typedef enum {
+    NE_OK = 0,
+    NE_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+    NE_ERR_SHAPE = 2,       /* B, T, Hq, Hkv < 1, Hq % Hkv != 0, or sizes overflow            */
+    NE_ERR_UNSUPPORTED = 3, /* head_dim not in {32, 64, 128}, or dtype pair not supported     */
+    NE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                               */
+    NE_ERR_WORKSPACE = 5,   /* workspace_bytes smaller than the matching *_workspace_bytes()  */
+    NE_ERR_HIP = 6          /* the HIP runtime rejected a launch                              */
+} ne_status_t;
+
+/* Supported (in_dtype -> out_dtype) pairs: F32->F32 (fp32 operands on fp32 MFMA),
+ * BF16->F32, BF16->BF16, F16->F32, F16->F16 (fp16 MFMA operands, fp32 accumulation).
+ * q, k, v and dO are in_dtype; o, dq, dk and dv are out_dtype. */
+
+/* Bytes of device workspace the forward needs (256-byte aligned base recommended; 16 is
+ * required).  Holds the rotated, scaled, converted operand copies.  Returns 0 for invalid
+ * arguments. */
+size_t ne_rope_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim,
+                                        ne_dtype_t in_dtype);
+
+/* Bytes of device workspace the backward needs (operand copies, the per-row
+ * Delta = rowsum(dO * o), the log2-scaled lse and the cos/sin table). */
+size_t ne_rope_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim,
+                                        ne_dtype_t in_dtype);
+
+/* Forward: o = softmax(mask(R(q) R(k)^T / sqrt(D))) v, lse = log-sum-exp of each score row.
+ * rope_base <= 0 disables the rotation. */
+ne_status_t ne_rope_attn_fwd(const void* q, const void* k, const void* v,
+                             void* o, float* lse,
+                             int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward: given q, k, v, the forward's o (out_dtype) and lse, and dO (in_dtype), writes the
+ * gradients of sum(o * dO): dq (w.r.t. the un-rotated q), dk (un-rotated k, summed over the
+ * query heads of each group) and dv.  Deterministic: every output element is written once by
+ * one thread in a fixed order (no atomics), so repeated calls give identical bits.
+ * Delta = rowsum(dO * o) is computed from the o passed in. */
+ne_status_t ne_rope_attn_bwd(const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dO,
+                             void* dq, void* dk, void* dv,
+                             int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+const char* ne_status_str(ne_status_t status);
+const char* ne_last_error(void);
+int ne_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NE_ROPE_ATTN_H */

@@ -24,6 +24,8 @@ def _bind(path):
     lib.ne_oracle_fwd.restype = i
     lib.ne_oracle_bwd.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, ctypes.c_double, i]
     lib.ne_oracle_bwd.restype = i
+    lib.ne_oracle_bwd_given_o.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, ctypes.c_double, i]
+    lib.ne_oracle_bwd_given_o.restype = i
     lib.ne_oracle_rope.argtypes = [P, P, i, i, i, i, ctypes.c_double, i]
     lib.ne_oracle_rope.restype = i
     lib.ne_oracle_max_threads.argtypes = []
@@ -97,6 +99,21 @@ def bwd(q, k, v, dO, rope_base, nthreads=0):
                                _ptr(dv), B, T, Hq, Hkv, D, float(rope_base), int(nthreads))
     if rc:
         raise ValueError(f"ne_oracle_bwd rejected the arguments (rc={rc})")
+    return dq, dk, dv
+
+
+def bwd_given_o(q, k, v, o, dO, rope_base, nthreads=0):
+    """(dq, dk, dv) with Delta = rowsum(dO * o) from the given o (e.g. o stored in bf16)."""
+    q, k, v, o, dO = _f64(q), _f64(k), _f64(v), _f64(o), _f64(dO)
+    B, T, Hq, Hkv, D = _dims(q, k)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = _load().ne_oracle_bwd_given_o(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, float(rope_base),
+                                       int(nthreads))
+    if rc:
+        raise ValueError(f"ne_oracle_bwd_given_o rejected the arguments (rc={rc})")
     return dq, dk, dv
 
 

@@ -164,9 +164,29 @@ int ne_oracle_fwd(const double* q, const double* k, const double* v, double* o,
  *   dv_j  = sum over heads h of the group, sum_i P_ij dO_i
  *   dq = R^T dq',  dk = R^T dk'.
  * The heads of a group are accumulated in ascending order. */
+static int bwd_impl(const double* q, const double* k, const double* v, const double* dO,
+                    const double* o_given, double* dq, double* dk, double* dv, int B, int T,
+                    int Hq, int Hkv, int D, double base, int nthreads);
+
 int ne_oracle_bwd(const double* q, const double* k, const double* v, const double* dO,
                   double* dq, double* dk, double* dv, int B, int T, int Hq, int Hkv,
                   int D, double base, int nthreads) {
+    return bwd_impl(q, k, v, dO, NULL, dq, dk, dv, B, T, Hq, Hkv, D, base, nthreads);
+}
+
+/* The same backward with Delta_i = dO_i . o_i taken from a caller-supplied o ([B][T][Hq][D])
+ * instead of the exact forward output: the function the library's backward computes when it
+ * is handed an o stored in a narrower format.  Everything else is exact. */
+int ne_oracle_bwd_given_o(const double* q, const double* k, const double* v, const double* o,
+                          const double* dO, double* dq, double* dk, double* dv, int B, int T,
+                          int Hq, int Hkv, int D, double base, int nthreads) {
+    if (!o) return 1;
+    return bwd_impl(q, k, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, nthreads);
+}
+
+static int bwd_impl(const double* q, const double* k, const double* v, const double* dO,
+                    const double* o_given, double* dq, double* dk, double* dv, int B, int T,
+                    int Hq, int Hkv, int D, double base, int nthreads) {
     if (check_shape(B, T, Hq, Hkv, D, base)) return 1;
     set_threads(nthreads);
     const int G = Hq / Hkv;
@@ -205,8 +225,9 @@ int ne_oracle_bwd(const double* q, const double* k, const double* v, const doubl
                         const double* vj = v + IDX4(b, j, g, 0, T, Hkv, D);
                         for (int d = 0; d < D; ++d) oi[d] += p * vj[d];
                     }
+                    const double* od = o_given ? o_given + IDX4(b, i, h, 0, T, Hq, D) : oi;
                     double di = 0.0;
-                    for (int d = 0; d < D; ++d) di += dOi[d] * oi[d];
+                    for (int d = 0; d < D; ++d) di += dOi[d] * od[d];
                     delta[i] = di;
                     for (int j = 0; j <= i; ++j) {
                         const double* vj = v + IDX4(b, j, g, 0, T, Hkv, D);

@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects invalid arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from causal_gqa_flashattention_rope_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ne_rope_attn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ne_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        from causal_gqa_flashattention_rope_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert set(names) == set(binding.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.ne_abi_version() == 1
+    for s in range(7):
+        assert L.ne_status_str(s)
+    assert L.ne_status_str(99) == b"unknown status"
+
+
+def test_workspace_sizes(L):
+    B, T, Hq, Hkv, D = 4, 2048, 12, 4, 128
+
+    def up(x):
+        return (x + 255) // 256 * 256
+    nq, nk = B * T * Hq * D, B * T * Hkv * D
+    fwd = L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
+    assert fwd == up(2 * nq) + 2 * up(2 * nk)
+    bwd = L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
+    assert bwd == 2 * up(2 * nq) + 2 * up(2 * nk) + 2 * up(4 * B * T * Hq) + up(T * (D // 2) * 8)
+    assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_F32) == up(4 * nq) + 2 * up(4 * nk)
+    assert L.ne_rope_attn_fwd_workspace_bytes(B, T, 12, 5, D, binding.NE_BF16) == 0
+    assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, 96, binding.NE_BF16) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def fwd_call(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, T=16, Hq=4, Hkv=2, D=64, base=1e4,
+             i=binding.NE_BF16, out=binding.NE_F32, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, i) if D in (32, 64, 128) else 1 << 20
+    return L.ne_rope_attn_fwd(q, k, v, o, lse, B, T, Hq, Hkv, D, base, i, out, ws, wsb, None)
+
+
+def bwd_call(L, ptrs=None, B=1, T=16, Hq=4, Hkv=2, D=64, base=1e4, i=binding.NE_BF16,
+             out=binding.NE_F32, ws=FAKE, wsb=1 << 30):
+    p = [FAKE] * 9 if ptrs is None else ptrs
+    return L.ne_rope_attn_bwd(*p, B, T, Hq, Hkv, D, base, i, out, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(lse=None), 1), (dict(ws=None), 1),
+    (dict(B=0), 2), (dict(T=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(Hq=6, Hkv=4), 2),
+    (dict(D=96), 3), (dict(D=16), 3), (dict(i=binding.NE_F32, out=binding.NE_BF16), 3),
+    (dict(i=binding.NE_BF16, out=binding.NE_F16), 3), (dict(i=7), 3),
+    (dict(q=FAKE + 8), 4), (dict(ws=FAKE + 4), 4),
+    (dict(wsb=16), 5),
+    (dict(base=float("nan")), 2),
+])
+def test_fwd_rejects_before_launch(L, kw, status):
+    assert fwd_call(L, **kw) == status
+    assert L.ne_last_error()
+
+
+@pytest.mark.parametrize("idx,status", [(0, 1), (5, 1), (8, 1)])
+def test_bwd_rejects_null(L, idx, status):
+    p = [FAKE] * 9
+    p[idx] = None
+    assert bwd_call(L, ptrs=p) == status
+
+
+def test_bwd_rejects_misaligned_and_small_workspace(L):
+    p = [FAKE] * 9
+    p[6] = FAKE + 2
+    assert bwd_call(L, ptrs=p) == 4
+    assert bwd_call(L, wsb=100) == 5
+    assert bwd_call(L, Hq=5, Hkv=2) == 2
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 32)
+    with pytest.raises(RuntimeError):
+        binding.ne_rope_attn_fwd(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous(), 1e4)

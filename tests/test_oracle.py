@@ -403,3 +403,34 @@ def test_workloads_follow_the_pages_model_configs():
     assert (w1.Hq, w1.Hkv, w1.Hq * w1.D, w1.T) == (cpu["q_heads"], cpu["kv_heads"], cpu["dim"], cpu["context"])
     assert (w2.Hq, w2.Hkv, w2.Hq * w2.D, w2.T) == (gpu["q_heads"], gpu["kv_heads"], gpu["dim"], gpu["context"])
     assert w2.D == gpu["head_dim"]
+
+
+def test_bwd_given_exact_o_reproduces_bwd_bitwise():
+    """bwd_given_o with the exact o is the plain backward; dv never depends on o."""
+    q, k, v, dO = case(2, 41, 6, 2, 16, seed=151)
+    o, _ = oracle.fwd(q, k, v, 10000.0)
+    a = oracle.bwd(q, k, v, dO, 10000.0)
+    b = oracle.bwd_given_o(q, k, v, o, dO, 10000.0)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    o2 = o + 1e-3 * rnd(o.shape, 152)
+    dq2, dk2, dv2 = oracle.bwd_given_o(q, k, v, o2, dO, 10000.0)
+    np.testing.assert_array_equal(dv2, a[2])
+    assert relerr(dq2, a[0]) > 1e-6  # Delta does enter dq
+
+
+def test_bwd_given_o_matches_autograd_with_delta_from_o():
+    """Against torch: with Delta from a perturbed o, the backward equals autograd of
+    sum(o * dO) plus the extra term -sum_i (Delta~_i - Delta_i) * lse_i (lse's gradient is P)."""
+    q, k, v, dO = case(1, 23, 4, 2, 8, seed=161)
+    o, _ = oracle.fwd(q, k, v, 100.0)
+    o2 = o + 1e-2 * rnd(o.shape, 162)
+    dq2, dk2, dv2 = oracle.bwd_given_o(q, k, v, o2, dO, 100.0)
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    to, tlse = torch_attention(tq, tk, tv, 100.0)
+    extra = torch.tensor(np.einsum("bthd,bthd->bht", dO, o2 - o))  # Delta~ - Delta
+    loss = (to * torch.tensor(dO)).sum() - (extra * tlse).sum()
+    loss.backward()
+    assert relerr(dq2, tq.grad.numpy()) < 1e-11
+    assert relerr(dk2, tk.grad.numpy()) < 1e-11
+    assert relerr(dv2, tv.grad.numpy()) < 1e-11

@@ -19,8 +19,8 @@ STATUS = {0: "NE_OK", 1: "NE_ERR_NULL", 2: "NE_ERR_SHAPE", 3: "NE_ERR_UNSUPPORTE
 
 # Every symbol include/ne_rope_attn.h declares.
 EXPORTS = ("ne_rope_attn_fwd_workspace_bytes", "ne_rope_attn_bwd_workspace_bytes",
-           "ne_rope_attn_fwd", "ne_rope_attn_bwd", "ne_status_str", "ne_last_error",
-           "ne_abi_version")
+           "ne_rope_attn_fwd", "ne_rope_attn_bwd", "ne_rope_attn_fwd_timed", "ne_rope_attn_bwd_timed",
+           "ne_status_str", "ne_last_error", "ne_abi_version")
 
 
 class NeError(RuntimeError):
@@ -50,6 +50,10 @@ def lib():
     L.ne_rope_attn_fwd.restype = i
     L.ne_rope_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp, sz, vp]
     L.ne_rope_attn_bwd.restype = i
+    L.ne_rope_attn_fwd_timed.argtypes = L.ne_rope_attn_fwd.argtypes + [ctypes.POINTER(vp)]
+    L.ne_rope_attn_fwd_timed.restype = i
+    L.ne_rope_attn_bwd_timed.argtypes = L.ne_rope_attn_bwd.argtypes + [ctypes.POINTER(vp)]
+    L.ne_rope_attn_bwd_timed.restype = i
     L.ne_status_str.argtypes = [i]
     L.ne_status_str.restype = ctypes.c_char_p
     L.ne_last_error.argtypes = []
@@ -101,8 +105,23 @@ def alloc_workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
-def ne_rope_attn_fwd(q, k, v, rope_base, out_dtype=torch.float32, o=None, lse=None, workspace=None):
-    """o, lse = attention forward.  q [B,T,Hq,D], k/v [B,T,Hkv,D] of one dtype."""
+def _events_arg(events, n):
+    """torch.cuda.Event list -> void*[n] of their hipEvent_t handles (None -> untimed call)."""
+    if events is None:
+        return None
+    if len(events) != n:
+        raise ValueError(f"need {n} events")
+    for e in events:
+        if e.cuda_event == 0:   # torch creates the HIP event lazily on first record
+            e.record()
+    return (ctypes.c_void_p * n)(*[e.cuda_event for e in events])
+
+
+def ne_rope_attn_fwd(q, k, v, rope_base, out_dtype=torch.float32, o=None, lse=None, workspace=None,
+                     events=None):
+    """o, lse = attention forward.  q [B,T,Hq,D], k/v [B,T,Hkv,D] of one dtype.
+
+    events: optional 4 torch.cuda.Event(enable_timing=True) recorded around the two kernels."""
     _require_gpu(q, k, v)
     B, T, Hq, Hkv, D = _dims(q, k)
     if o is None:
@@ -112,14 +131,22 @@ def ne_rope_attn_fwd(q, k, v, rope_base, out_dtype=torch.float32, o=None, lse=No
     need = fwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype)
     if workspace is None:
         workspace = alloc_workspace(need, q.device)
-    _check(lib().ne_rope_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D,
-                                  float(rope_base), _DT[q.dtype], _DT[o.dtype], _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream()))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D, float(rope_base),
+            _DT[q.dtype], _DT[o.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream())
+    ev = _events_arg(events, 4)
+    if ev is None:
+        _check(lib().ne_rope_attn_fwd(*args))
+    else:
+        _check(lib().ne_rope_attn_fwd_timed(*args, ev))
     return o, lse
 
 
-def ne_rope_attn_bwd(q, k, v, o, lse, dO, rope_base, dq=None, dk=None, dv=None, workspace=None):
-    """dq, dk, dv = attention backward (out dtype = o's dtype)."""
+def ne_rope_attn_bwd(q, k, v, o, lse, dO, rope_base, dq=None, dk=None, dv=None, workspace=None,
+                     events=None):
+    """dq, dk, dv = attention backward (out dtype = o's dtype).
+
+    events: optional 6 torch.cuda.Event(enable_timing=True) recorded around the three kernels."""
     _require_gpu(q, k, v, o, lse, dO)
     B, T, Hq, Hkv, D = _dims(q, k)
     if dq is None:
@@ -131,8 +158,12 @@ def ne_rope_attn_bwd(q, k, v, o, lse, dO, rope_base, dq=None, dk=None, dv=None, 
     need = bwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype)
     if workspace is None:
         workspace = alloc_workspace(need, q.device)
-    _check(lib().ne_rope_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
-                                  _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, float(rope_base), _DT[q.dtype],
-                                  _DT[o.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  _stream()))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, T, Hq, Hkv, D, float(rope_base), _DT[q.dtype], _DT[o.dtype], _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream())
+    ev = _events_arg(events, 6)
+    if ev is None:
+        _check(lib().ne_rope_attn_bwd(*args))
+    else:
+        _check(lib().ne_rope_attn_bwd_timed(*args, ev))
     return dq, dk, dv

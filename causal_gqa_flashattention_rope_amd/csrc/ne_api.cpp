@@ -112,10 +112,14 @@ size_t ne_rope_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_
     return layout(true, B, T, Hq, Hkv, head_dim, in_dtype).total;
 }
 
-ne_status_t ne_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                             int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                     ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     if (!q || !k || !v || !o || !lse || !workspace)
         return fail(NE_ERR_NULL, "ne_rope_attn_fwd: q, k, v, o, lse and workspace must be non-null");
     ne_status_t s = common_checks(B, T, Hq, Hkv, head_dim, in_dtype, out_dtype);
@@ -139,16 +143,17 @@ ne_status_t ne_rope_attn_fwd(const void* q, const void* k, const void* v, void* 
     fa.qh = pa.qh; fa.kh = pa.kh; fa.vh = pa.vh; fa.o = o; fa.lse = lse;
     fa.B = B; fa.T = T; fa.Hq = Hq; fa.Hkv = Hkv; fa.G = G;
     fa.nrb = (int)(((int64_t)T * G + 127) / 128);
-    hipError_t e = ne::launch_fwd((int)in_dtype, (int)out_dtype, head_dim, pa, fa, (hipStream_t)stream);
+    hipError_t e = ne::launch_fwd((int)in_dtype, (int)out_dtype, head_dim, pa, fa, (hipStream_t)stream,
+                                  (hipEvent_t const*)events);
     if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_attn_fwd: launch failed: %s", hipGetErrorString(e));
     return NE_OK;
 }
 
-ne_status_t ne_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                             const void* dO, void* dq, void* dk, void* dv,
-                             int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, void* dq, void* dk, void* dv,
+                     int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                     ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
         return fail(NE_ERR_NULL, "ne_rope_attn_bwd: every tensor pointer and the workspace must be non-null");
     ne_status_t s = common_checks(B, T, Hq, Hkv, head_dim, in_dtype, out_dtype);
@@ -177,9 +182,56 @@ ne_status_t ne_rope_attn_bwd(const void* q, const void* k, const void* v, const 
     ba.nrb = (int)(((int64_t)T * G + 127) / 128);
     ba.rope_base = rope_base;
     ba.scale = (float)(1.0 / std::sqrt((double)head_dim));
-    hipError_t e = ne::launch_bwd((int)in_dtype, (int)out_dtype, head_dim, pa, ba, (hipStream_t)stream);
+    hipError_t e = ne::launch_bwd((int)in_dtype, (int)out_dtype, head_dim, pa, ba, (hipStream_t)stream,
+                                  (hipEvent_t const*)events);
     if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_attn_bwd: launch failed: %s", hipGetErrorString(e));
     return NE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ne_status_t ne_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, out_dtype, workspace,
+                    workspace_bytes, stream, nullptr);
+}
+
+ne_status_t ne_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dO, void* dq, void* dk, void* dv,
+                             int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, out_dtype,
+                    workspace, workspace_bytes, stream, nullptr);
+}
+
+ne_status_t ne_rope_attn_fwd_timed(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                                   ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   void* const* events) {
+    if (!events) return fail(NE_ERR_NULL, "ne_rope_attn_fwd_timed: events must be non-null");
+    for (int i = 0; i < 4; ++i)
+        if (!events[i]) return fail(NE_ERR_NULL, "ne_rope_attn_fwd_timed: events[%d] is null", i);
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, out_dtype, workspace,
+                    workspace_bytes, stream, events);
+}
+
+ne_status_t ne_rope_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                   const void* dO, void* dq, void* dk, void* dv,
+                                   int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                                   ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   void* const* events) {
+    if (!events) return fail(NE_ERR_NULL, "ne_rope_attn_bwd_timed: events must be non-null");
+    for (int i = 0; i < 6; ++i)
+        if (!events[i]) return fail(NE_ERR_NULL, "ne_rope_attn_bwd_timed: events[%d] is null", i);
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, out_dtype,
+                    workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -627,25 +627,48 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 // =====================================================================================
 // Launchers.
 // =====================================================================================
+// Records ev[2i] / ev[2i + 1] around launch i when events are given.
+struct Marks {
+    hipEvent_t const* ev;
+    hipStream_t s;
+    hipError_t before(int i) const { return ev ? hipEventRecord(ev[2 * i], s) : hipSuccess; }
+    hipError_t after(int i) const { return ev ? hipEventRecord(ev[2 * i + 1], s) : hipSuccess; }
+};
+
+#define NE_TRY(x)                             \
+    do {                                      \
+        hipError_t e_ = (x);                  \
+        if (e_ != hipSuccess) return e_;      \
+    } while (0)
+
 template <typename TI, typename TO, typename OP, int D>
-static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, hipStream_t s) {
+static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, hipStream_t s, hipEvent_t const* ev) {
+    const Marks m{ev, s};
+    NE_TRY(m.before(0));
     hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, false>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    NE_TRY(hipGetLastError());
+    NE_TRY(m.after(0));
+    NE_TRY(m.before(1));
     hipLaunchKernelGGL((fwd_kernel<OP, D, TO>), dim3(fa.nrb, fa.Hkv, fa.B), dim3(256), 0, s, fa);
-    return hipGetLastError();
+    NE_TRY(hipGetLastError());
+    return m.after(1);
 }
 
 template <typename TI, typename TO, typename OP, int D>
-static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_t s) {
+static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_t s, hipEvent_t const* ev) {
+    const Marks m{ev, s};
+    NE_TRY(m.before(0));
     hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, true>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    NE_TRY(hipGetLastError());
+    NE_TRY(m.after(0));
+    NE_TRY(m.before(1));
     hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3((ba.T + 127) / 128, ba.Hkv, ba.B), dim3(256), 0, s, ba);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    NE_TRY(hipGetLastError());
+    NE_TRY(m.after(1));
+    NE_TRY(m.before(2));
     hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb, ba.Hkv, ba.B), dim3(256), 0, s, ba);
-    return hipGetLastError();
+    NE_TRY(hipGetLastError());
+    return m.after(2);
 }
 
 #define NE_DISPATCH_D(FN, TI, TO, OP, D, ...)                       \
@@ -656,21 +679,23 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
         default: return hipErrorInvalidValue;                      \
     }
 
-hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, hipStream_t s) {
-    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, float, float, float, D, pa, fa, s) }
-    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, __bf16, float, _Float16, D, pa, fa, s) }
-    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_fwd_t, __bf16, __bf16, _Float16, D, pa, fa, s) }
-    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, _Float16, float, _Float16, D, pa, fa, s) }
-    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_fwd_t, _Float16, _Float16, _Float16, D, pa, fa, s) }
+hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, hipStream_t s,
+                      hipEvent_t const* ev) {
+    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, float, float, float, D, pa, fa, s, ev) }
+    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, __bf16, float, _Float16, D, pa, fa, s, ev) }
+    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_fwd_t, __bf16, __bf16, _Float16, D, pa, fa, s, ev) }
+    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, _Float16, float, _Float16, D, pa, fa, s, ev) }
+    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_fwd_t, _Float16, _Float16, _Float16, D, pa, fa, s, ev) }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const BwdArgs& ba, hipStream_t s) {
-    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, float, float, float, D, pa, ba, s) }
-    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, __bf16, float, _Float16, D, pa, ba, s) }
-    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_bwd_t, __bf16, __bf16, _Float16, D, pa, ba, s) }
-    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, _Float16, float, _Float16, D, pa, ba, s) }
-    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_bwd_t, _Float16, _Float16, _Float16, D, pa, ba, s) }
+hipError_t launch_bwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const BwdArgs& ba, hipStream_t s,
+                      hipEvent_t const* ev) {
+    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, float, float, float, D, pa, ba, s, ev) }
+    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, __bf16, float, _Float16, D, pa, ba, s, ev) }
+    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_bwd_t, __bf16, __bf16, _Float16, D, pa, ba, s, ev) }
+    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, _Float16, float, _Float16, D, pa, ba, s, ev) }
+    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_bwd_t, _Float16, _Float16, _Float16, D, pa, ba, s, ev) }
     return hipErrorInvalidValue;
 }
 

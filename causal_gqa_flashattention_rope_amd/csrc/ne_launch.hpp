@@ -32,7 +32,11 @@ struct BwdArgs {
 };
 
 // dtype codes follow ne_dtype_t: 0 = f32, 1 = bf16, 2 = f16.
-hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, hipStream_t s);
-hipError_t launch_bwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const BwdArgs& ba, hipStream_t s);
+// ev (nullable): hipEvent_t pairs recorded on `s` around each kernel launch, in launch order
+// (forward: prep, fwd; backward: prep, dkdv, dq).
+hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, hipStream_t s,
+                      hipEvent_t const* ev);
+hipError_t launch_bwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const BwdArgs& ba, hipStream_t s,
+                      hipEvent_t const* ev);
 
 }  // namespace ne

@@ -121,6 +121,92 @@ __device__ __forceinline__ float tr_frag_f32(const float* tile, int stride, int 
     return tile[(32 * mb + acc_row(s, l >> 5)) * stride + col0 + (l & 31)];
 }
 
+// ---- swizzled LDS tiles --------------------------------------------------------------------
+// A tile of rows x D elements is stored densely (row = D * sizeof(OP) bytes) with the 16-byte
+// chunks of row r permuted: chunk c lives in slot c ^ swz(r).  The permutations are chosen so
+// that the two read patterns hit distinct banks: 16 lanes reading one 16-byte chunk from 16
+// consecutive rows (row fragments), and 32 lanes reading 8 bytes each from 4 consecutive rows
+// x 4 chunks (transposed reads).  Dense rows let a wave fill 1 KiB of the tile per
+// global_load_lds_dwordx4 (lane i writes bytes 16i..16i+15 of that kilobyte).
+template <typename OP, int D>
+struct Tile {
+    static constexpr int ROWB = D * (int)sizeof(OP);  // bytes per row
+    static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+    static constexpr int EPC = 16 / (int)sizeof(OP);  // elements per chunk
+    __device__ __forceinline__ static constexpr int swz(int r) {
+        if constexpr (CPR == 16) return 4 * (r & 3) + ((r >> 2) & 3);
+        else if constexpr (CPR == 8) return ((r >> 2) & 3) | (((r >> 1) & 1) << 2);
+        else if constexpr (CPR == 4) return (r >> 2) & 3;
+        else return r & (CPR - 1);                     // fp32 tiles: 8, 16 or 32 chunks
+    }
+    // byte offset of element e of row r
+    __device__ __forceinline__ static int off(int r, int e) {
+        return r * ROWB + (((e / EPC) ^ swz(r)) << 4) + (e % EPC) * (int)sizeof(OP);
+    }
+    __device__ __forceinline__ static const OP* ptr(const OP* base, int r, int e) {
+        return reinterpret_cast<const OP*>(reinterpret_cast<const char*>(base) + off(r, e));
+    }
+};
+
+// Copy rows [n0, n0 + ROWS) of a dense [nrows][D] array into a swizzled LDS tile with direct
+// global->LDS loads issued by the NW waves of the block.  Rows at or past nrows are filled from
+// row nrows - 1 (finite data that the callers mask out).  Completion: s_waitcnt vmcnt(0) then
+// a barrier (ne::lds_fill_wait).
+template <typename OP, int D, int ROWS, int NW>
+__device__ __forceinline__ void lds_fill(OP* tile, const OP* src, int n0, int nrows) {
+    using TL = Tile<OP, D>;
+    constexpr int CHUNKS = ROWS * TL::CPR;
+    static_assert(CHUNKS % (64 * NW) == 0, "tile must be a whole number of wave loads");
+    const int l = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < CHUNKS / (64 * NW); ++i) {
+        const int q = 64 * (i * NW + w) + l;           // LDS slot index of this lane
+        const int r = q / TL::CPR, p = q % TL::CPR;
+        const int gr = min(n0 + r, nrows - 1);
+        const OP* g = src + (size_t)gr * D + (p ^ TL::swz(r)) * TL::EPC;
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                         (void __attribute__((address_space(3)))*)
+                                             (reinterpret_cast<char*>(tile) + 1024 * (i * NW + w)),
+                                         16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void lds_fill_wait() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
+// Transposed f16 fragment from a swizzled tile (same meaning as tr_frag_f16).
+template <int D>
+__device__ __forceinline__ half8 tr_frag_f16_sw(const _Float16* tile, int kk, int col0) {
+    using TL = Tile<_Float16, D>;
+    const int l = lane_id();
+    const int g = l >> 4, s = l & 15, h = l >> 5;
+    const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
+    const int r1 = 16 * kk + 4 * h + (s >> 2);
+    fp16x4_tr lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr_ptr)TL::ptr(tile, r1, col));
+    fp16x4_tr hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr_ptr)TL::ptr(tile, r1 + 8, col));
+    half8 f;
+    half4v a = __builtin_bit_cast(half4v, lo), b = __builtin_bit_cast(half4v, hi);
+    f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+    f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+    return f;
+}
+
+// f32 column fragment from a swizzled tile: lane (h, c) reads tile[32mb + acc_row(s, h)][col0 + c].
+template <int D>
+__device__ __forceinline__ float tr_frag_f32_sw(const float* tile, int mb, int s, int col0) {
+    const int l = lane_id();
+    return *Tile<float, D>::ptr(tile, 32 * mb + acc_row(s, l >> 5), col0 + (l & 31));
+}
+
+// Row fragment from a swizzled tile (k-step ks of row r), both operand types.
+template <typename OP, int D>
+__device__ __forceinline__ typename Mma<OP>::frag row_frag_sw(const OP* tile, int r, int ks, int h) {
+    if constexpr (sizeof(OP) == 2) return *reinterpret_cast<const half8*>(Tile<OP, D>::ptr(tile, r, 16 * ks + 8 * h));
+    else return *Tile<OP, D>::ptr(tile, r, 2 * ks + h);
+}
+
 // ---- small vector stores of four consecutive output elements -----------------------------
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<floatx4*>(p) = floatx4{a, b, c, d};

@@ -197,26 +197,55 @@ template <> struct Strides<float> {
 };
 
 // =====================================================================================
-// Forward.  grid (nrb, Hkv, B), 256 threads = 4 waves x 32 flattened rows.
+// Block -> work mapping.  Workgroups are dispatched round-robin over the 8 XCDs (each with its
+// own L2), so dispatch index i runs on XCD i % 8.  When the (batch, KV head) groups divide
+// evenly, XCD x takes groups x, x + 8, ... and walks their row blocks longest-first, so the K/V
+// (or Q/dO) of a group are fetched into one L2 only; otherwise blocks go longest-first in order.
+// =====================================================================================
+struct Work {
+    int blk, grp;  // row/key block index and (b * Hkv + hkv)
+};
+__device__ __forceinline__ Work map_block(int nblk, int ngrp, bool longest_last) {
+    const int i = blockIdx.x;
+    int j, g;
+    if ((ngrp & 7) == 0) {
+        const int x = i & 7, k = i >> 3, per = ngrp >> 3;
+        j = k / per;
+        g = x + 8 * (k % per);
+    } else {
+        j = i / ngrp;
+        g = i % ngrp;
+    }
+    return Work{longest_last ? nblk - 1 - j : j, g};
+}
+
+// =====================================================================================
+// Forward.  grid (nrb * B * Hkv), 256 threads = 4 waves x 32 flattened rows.
 // S^T = K Q^T puts one query row per lane (and its 16+16 keys in the two lane halves), so the
 // online-softmax row max and sum are in-lane plus one half swap.  O^T = V^T P^T reuses the
-// accumulator registers of S^T as the contraction operand.
+// accumulator registers of S^T as the contraction operand.  K and V tiles (64 keys) are copied
+// HBM->LDS by direct loads into swizzled, double-buffered tiles; a wave skips the tiles that
+// lie wholly past its rows and masks only the tiles that cross its diagonal.  The running max
+// is refreshed only when a row's new maximum exceeds it by more than 2^8 (the probabilities stay
+// below 256 in between), so the rescale of O is rare.
 // =====================================================================================
 template <typename OP, int D, typename TOUT>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_kernel(FwdArgs a) {
     using M = Mma<OP>;
+    using TL = Tile<OP, D>;
     constexpr bool F16 = sizeof(OP) == 2;
-    constexpr int BM = 128, BN = 64;
-    constexpr int KSTR = Strides<OP>::template row<D>;
-    constexpr int VSTR = Strides<OP>::template col<D>;
+    constexpr int BM = 128, BN = 64, NW = 4;
     constexpr int KS = D / M::K;
     constexpr int NDB = D / 32;
-    constexpr int STAGE = BN * (KSTR + VSTR);
-    __shared__ __attribute__((aligned(16))) OP lds[2 * STAGE];
+    constexpr int TILE = BN * D;                      // elements per K or V tile
+    constexpr float TAU = 8.f;
+    __shared__ __attribute__((aligned(1024))) OP lds[2 * 2 * TILE];
 
     const int T = a.T, G = a.G, TG = T * G;
-    const int rb = a.nrb - 1 - blockIdx.x;  // longest row blocks first
-    const int hkv = blockIdx.y, b = blockIdx.z;
+    const Work wk = map_block(a.nrb, a.B * a.Hkv, true);
+    const int rb = wk.blk;
+    const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
     const int R0 = rb * BM;
     const int Rw = R0 + 32 * w;
@@ -227,10 +256,13 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     const int wave_tmax = min(Rw + 31, TG - 1) / G;
     const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;
 
-    const size_t grp = (size_t)b * a.Hkv + hkv;
+    const size_t grp = (size_t)wk.grp;
     const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
     const OP* vg = (const OP*)a.vh + grp * (size_t)T * D;
+
+    lds_fill<OP, D, BN, NW>(lds, kg, 0, T);
+    lds_fill<OP, D, BN, NW>(lds + TILE, vg, 0, T);
 
     typename M::frag qf[KS];
 #pragma unroll
@@ -244,18 +276,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
 
-    TileLoader<OP, D, BN> kl, vl;
-    kl.load(kg, 0, T);
-    vl.load(vg, 0, T);
     for (int it = 0; it < ntiles; ++it) {
-        OP* Ks = lds + (it & 1) * STAGE;
-        OP* Vs = Ks + BN * KSTR;
-        kl.template store<KSTR>(Ks);
-        vl.template store<VSTR>(Vs);
-        __syncthreads();
+        const OP* Ks = lds + (it & 1) * 2 * TILE;
+        const OP* Vs = Ks + TILE;
+        lds_fill_wait();
         if (it + 1 < ntiles) {
-            kl.load(kg, (it + 1) * BN, T);
-            vl.load(vg, (it + 1) * BN, T);
+            OP* nxt = lds + ((it + 1) & 1) * 2 * TILE;
+            lds_fill<OP, D, BN, NW>(nxt, kg, (it + 1) * BN, T);
+            lds_fill<OP, D, BN, NW>(nxt + TILE, vg, (it + 1) * BN, T);
         }
         const int n0 = it * BN;
         if (n0 > wave_tmax) continue;  // every row of this wave precedes the whole tile
@@ -264,40 +292,43 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             s[mb] = floatx16{};
-            const OP* krow = Ks + (32 * mb + c) * KSTR;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) s[mb] = M::mma(M::row_frag(krow, ks, h, D), qf[ks], s[mb]);
+            for (int ks = 0; ks < KS; ++ks)
+                s[mb] = M::mma(row_frag_sw<OP, D>(Ks, 32 * mb + c, ks, h), qf[ks], s[mb]);
         }
-        if (n0 + BN - 1 > wave_tmin) {  // tile reaches past some row's diagonal
+        if (n0 + BN - 1 > wave_tmin) {  // tile crosses some row's diagonal
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (n0 + 32 * mb + acc_row(r, h) > t_lane) s[mb][r] = -INFINITY;
         }
-        float mx = -INFINITY;
+        float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
         mx = max_halves(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {  // rare: refresh the reference max
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = m_new;
+        }
         float psum = 0.f;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(s[mb][r] - m_new);
+                const float p = __builtin_amdgcn_exp2f(s[mb][r] - m_run);
                 s[mb][r] = p;
                 psum += p;
             }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        l_run += psum;
 
         if constexpr (F16) {
             half8 pf[4];
@@ -307,7 +338,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    oacc[db] = M::mma(tr_frag_f16((const _Float16*)Vs, VSTR, kk, 32 * db), pf[kk], oacc[db]);
+                    oacc[db] = M::mma(tr_frag_f16_sw<D>((const _Float16*)Vs, kk, 32 * db), pf[kk], oacc[db]);
         } else {
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -315,7 +346,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                     for (int st = 0; st < 16; ++st)
-                        oacc[db] = M::mma(tr_frag_f32((const float*)Vs, VSTR, mb, st, 32 * db), s[mb][st], oacc[db]);
+                        oacc[db] = M::mma(tr_frag_f32_sw<D>((const float*)Vs, mb, st, 32 * db), s[mb][st], oacc[db]);
         }
     }
 
@@ -649,7 +680,7 @@ static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, hipStream_
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(0));
     NE_TRY(m.before(1));
-    hipLaunchKernelGGL((fwd_kernel<OP, D, TO>), dim3(fa.nrb, fa.Hkv, fa.B), dim3(256), 0, s, fa);
+    hipLaunchKernelGGL((fwd_kernel<OP, D, TO>), dim3(fa.nrb * fa.Hkv * fa.B), dim3(256), 0, s, fa);
     NE_TRY(hipGetLastError());
     return m.after(1);
 }

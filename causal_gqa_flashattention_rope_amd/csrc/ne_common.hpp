@@ -97,30 +97,6 @@ __device__ __forceinline__ half8 pack_frag_f16(const floatx16& acc, int c) {
     return f;
 }
 
-// Transposed fragment of a row-major 16-bit LDS tile for the f16 product whose contraction
-// runs over the tile's rows in accumulator order: output lane (h, c) receives
-// tile[row0 + 16kk + 8(j/4) + 4h + (j%4)][col0 + c], j = 0..7.
-__device__ __forceinline__ half8 tr_frag_f16(const _Float16* tile, int stride, int kk, int col0) {
-    const int l = lane_id();
-    const int g = l >> 4, s = l & 15, h = l >> 5;
-    const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
-    const int r1 = 16 * kk + 4 * h + (s >> 2);
-    fp16x4_tr lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr_ptr)(tile + r1 * stride + col));
-    fp16x4_tr hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr_ptr)(tile + (r1 + 8) * stride + col));
-    half8 f;
-    half4v a = __builtin_bit_cast(half4v, lo), b = __builtin_bit_cast(half4v, hi);
-    f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
-    f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
-    return f;
-}
-
-// f32 counterpart: k-step s (0..15) of the 32-row block mb: lane (h, c) reads
-// tile[32mb + acc_row(s, h)][col0 + c].
-__device__ __forceinline__ float tr_frag_f32(const float* tile, int stride, int mb, int s, int col0) {
-    const int l = lane_id();
-    return tile[(32 * mb + acc_row(s, l >> 5)) * stride + col0 + (l & 31)];
-}
-
 // ---- swizzled LDS tiles --------------------------------------------------------------------
 // A tile of rows x D elements is stored densely (row = D * sizeof(OP) bytes) with the 16-byte
 // chunks of row r permuted: chunk c lives in slot c ^ swz(r).  The permutations are chosen so

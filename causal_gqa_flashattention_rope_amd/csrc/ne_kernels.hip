@@ -145,58 +145,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 }
 
 // =====================================================================================
-// Tile staging helpers: a BN x D tile of OP, rows [n0, n0 + BN) of a [rows][D] array, into LDS
-// with row stride STR (elements), zero-filled past `nrows`.
-// =====================================================================================
-template <typename OP, int D, int BN>
-struct TileLoader {
-    static constexpr int EPC = 16 / sizeof(OP);      // elements per 16-byte chunk
-    static constexpr int CPR = D / EPC;              // chunks per row
-    static constexpr int NL = (BN * CPR + 255) / 256;
-    uint4 r[NL];
-    __device__ __forceinline__ void load(const OP* src, int n0, int nrows) {
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int idx = threadIdx.x + 256 * i;
-            const int row = idx / CPR, ch = idx % CPR;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (idx < BN * CPR && n0 + row < nrows)
-                v = *reinterpret_cast<const uint4*>(src + (size_t)(n0 + row) * D + ch * EPC);
-            r[i] = v;
-        }
-    }
-    template <int STR>
-    __device__ __forceinline__ void store(OP* dst) const {
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int idx = threadIdx.x + 256 * i;
-            if (idx >= BN * CPR) continue;
-            const int row = idx / CPR, ch = idx % CPR;
-            OP* p = dst + row * STR + ch * EPC;
-            if ((STR * sizeof(OP)) % 16 == 0) {
-                *reinterpret_cast<uint4*>(p) = r[i];
-            } else {
-                reinterpret_cast<uint2*>(p)[0] = make_uint2(r[i].x, r[i].y);
-                reinterpret_cast<uint2*>(p)[1] = make_uint2(r[i].z, r[i].w);
-            }
-        }
-    }
-};
-
-template <typename OP> struct Strides;
-template <> struct Strides<_Float16> {
-    // row reads of 16 bytes per lane: +8 elements keeps 16 consecutive rows on distinct banks;
-    // transposed reads of 4 rows x 32 bytes per 16 lanes: +16 elements.
-    template <int D> static constexpr int row = D + 8;
-    template <int D> static constexpr int col = D + 16;
-};
-template <> struct Strides<float> {
-    // fp32 row reads (k = 2ks + h): stride = 2 mod 64 banks; column reads: stride = 8 mod 16.
-    template <int D> static constexpr int row = D + 2;
-    template <int D> static constexpr int col = D + 8;
-};
-
-// =====================================================================================
 // Block -> work mapping.  Workgroups are dispatched round-robin over the 8 XCDs (each with its
 // own L2), so dispatch index i runs on XCD i % 8.  When the (batch, KV head) groups divide
 // evenly, XCD x takes groups x, x + 8, ... and walks their row blocks longest-first, so the K/V
@@ -366,27 +314,29 @@ void fwd_kernel(FwdArgs a) {
 }
 
 // =====================================================================================
-// Backward, dK/dV.  grid (ceil(T / 128), Hkv, B), 256 threads = 4 waves x 32 keys.
+// Backward, dK/dV.  grid (ceil(T / 128) * B * Hkv), 256 threads = 4 waves x 32 keys.
 // S = Q K^T and dP = dO V^T put one key per lane and 16 query rows per lane half, so P and dS
 // feed dV^T += dO^T P and dK^T += Q^T dS directly as contraction operands; dO^T and Q^T come
-// from transposed LDS reads of the row-major tiles.  Every flattened row of the group (all G
-// query heads) passes through the same accumulators: dK and dV of a KV head are summed over
-// its query-head group in registers and written once.
+// from transposed reads of the same swizzled row-major LDS tiles that feed S and dP.  Every
+// flattened row of the group (all G query heads) passes through the same accumulators: dK and
+// dV of a KV head are summed over its query-head group in registers and written once.
+// Q/dO tiles (64 rows) arrive by direct HBM->LDS loads, double-buffered.
 // =====================================================================================
 template <typename OP, int D, typename TOUT>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     using M = Mma<OP>;
     constexpr bool F16 = sizeof(OP) == 2;
-    constexpr int BN = 128, BMR = 64;
-    constexpr int QSTR = Strides<OP>::template row<D>;
+    constexpr int BN = 128, BMR = 64, NW = 4;
     constexpr int KS = D / M::K;
     constexpr int NDB = D / 32;
-    constexpr int STAGE = 2 * BMR * QSTR;
-    __shared__ __attribute__((aligned(16))) OP lds[2 * STAGE];
+    constexpr int TILE = BMR * D;
+    __shared__ __attribute__((aligned(1024))) OP lds[2 * 2 * TILE];
     __shared__ __attribute__((aligned(16))) float rowv[2][2][BMR];  // [stage][lse2 | delta][row]
 
     const int T = a.T, G = a.G, TG = T * G;
-    const int kb = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+    const Work wk = map_block((T + BN - 1) / BN, a.B * a.Hkv, false);
+    const int kb = wk.blk;
+    const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
     const int n0 = kb * BN;
     const int nw = n0 + 32 * w;            // first key of this wave
@@ -396,13 +346,25 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     const int rstart = (n0 * G) / BMR * BMR;
     const int ntiles = (TG - rstart + BMR - 1) / BMR;
 
-    const size_t grp = (size_t)b * a.Hkv + hkv;
+    const size_t grp = (size_t)wk.grp;
     const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
     const OP* og = (const OP*)a.dOh + grp * (size_t)TG * D;
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
     const OP* vg = (const OP*)a.vh + grp * (size_t)T * D;
     const float* lse2g = a.lse2 + grp * (size_t)TG;
     const float* delg = a.delta + grp * (size_t)TG;
+
+    auto fill = [&](int stage, int R0) {
+        OP* dst = lds + stage * 2 * TILE;
+        lds_fill<OP, D, BMR, NW>(dst, qg, R0, TG);
+        lds_fill<OP, D, BMR, NW>(dst + TILE, og, R0, TG);
+        if (tid < BMR) {
+            const int Rr = R0 + tid;
+            rowv[stage][0][tid] = Rr < TG ? lse2g[Rr] : INFINITY;  // padded rows: P = exp2(-inf) = 0
+            rowv[stage][1][tid] = Rr < TG ? delg[Rr] : 0.f;
+        }
+    };
+    fill(0, rstart);
 
     typename M::frag kf[KS], vf[KS];
 #pragma unroll
@@ -419,82 +381,61 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) { dk[db] = floatx16{}; dv[db] = floatx16{}; }
 
-    TileLoader<OP, D, BMR> ql, ol;
-    float rl = 0.f, rd = 0.f;  // this thread's lse2 / delta prefetch (threads 0..BMR-1)
-    auto gload = [&](int R0) {
-        ql.load(qg, R0, TG);
-        ol.load(og, R0, TG);
-        if (tid < BMR) {
-            const int Rr = R0 + tid;
-            rl = Rr < TG ? lse2g[Rr] : INFINITY;  // padded rows: P = exp2(-inf) = 0
-            rd = Rr < TG ? delg[Rr] : 0.f;
-        }
-    };
-    gload(rstart);
     for (int it = 0; it < ntiles; ++it) {
         const int st = it & 1;
-        OP* Qs = lds + st * STAGE;
-        OP* Os = Qs + BMR * QSTR;
-        ql.template store<QSTR>(Qs);
-        ol.template store<QSTR>(Os);
-        if (tid < BMR) { rowv[st][0][tid] = rl; rowv[st][1][tid] = rd; }
-        __syncthreads();
+        const OP* Qs = lds + st * 2 * TILE;
+        const OP* Os = Qs + TILE;
         const int R0 = rstart + it * BMR;
-        if (it + 1 < ntiles) gload(R0 + BMR);
+        lds_fill_wait();
+        if (it + 1 < ntiles) fill(st ^ 1, R0 + BMR);
         const int Rlast = min(R0 + BMR - 1, TG - 1);
         if (Rlast < nw * G) continue;  // every row of the tile precedes this wave's keys
         const bool need_mask = R0 < (nw + 31) * G;
 
-        floatx16 p[2], ds[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             floatx16 sacc = floatx16{}, dpacc = floatx16{};
-            const OP* qrow = Qs + (32 * mb + c) * QSTR;
-            const OP* orow = Os + (32 * mb + c) * QSTR;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                sacc = M::mma(M::row_frag(qrow, ks, h, D), kf[ks], sacc);
-                dpacc = M::mma(M::row_frag(orow, ks, h, D), vf[ks], dpacc);
+                sacc = M::mma(row_frag_sw<OP, D>(Qs, 32 * mb + c, ks, h), kf[ks], sacc);
+                dpacc = M::mma(row_frag_sw<OP, D>(Os, 32 * mb + c, ks, h), vf[ks], dpacc);
             }
+            floatx16 p, ds;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int rr = 32 * mb + 8 * q4 + 4 * h;
-                const floatx4 L = *reinterpret_cast<const floatx4*>(&rowv[st][0][rr]);
-                const floatx4 Dl = *reinterpret_cast<const floatx4*>(&rowv[st][1][rr]);
+                const floatx4 Lv = *reinterpret_cast<const floatx4*>(&rowv[st][0][rr]);
+                const floatx4 Dv = *reinterpret_cast<const floatx4*>(&rowv[st][1][rr]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * q4 + e;
-                    float pv = __builtin_amdgcn_exp2f(sacc[r] - L[e]);
-                    if (need_mask && R0 + rr + e < keyG) pv = 0.f;
-                    p[mb][r] = pv;
-                    ds[mb][r] = pv * (dpacc[r] - Dl[e]);
+                    float sv = sacc[r];
+                    if (need_mask && R0 + rr + e < keyG) sv = -INFINITY;
+                    const float pv = __builtin_amdgcn_exp2f(sv - Lv[e]);
+                    p[r] = pv;
+                    ds[r] = pv * (dpacc[r] - Dv[e]);
                 }
             }
-        }
-        if constexpr (F16) {
-            half8 pf[4], dsf[4];
+            if constexpr (F16) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                pf[kk] = pack_frag_f16(p[kk >> 1], kk & 1);
-                dsf[kk] = pack_frag_f16(ds[kk >> 1], kk & 1);
-            }
+                for (int cc = 0; cc < 2; ++cc) {
+                    const half8 pf = pack_frag_f16(p, cc), dsf = pack_frag_f16(ds, cc);
+                    const int kk = 2 * mb + cc;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    dv[db] = M::mma(tr_frag_f16((const _Float16*)Os, QSTR, kk, 32 * db), pf[kk], dv[db]);
-                    dk[db] = M::mma(tr_frag_f16((const _Float16*)Qs, QSTR, kk, 32 * db), dsf[kk], dk[db]);
+                    for (int db = 0; db < NDB; ++db) {
+                        dv[db] = M::mma(tr_frag_f16_sw<D>((const _Float16*)Os, kk, 32 * db), pf, dv[db]);
+                        dk[db] = M::mma(tr_frag_f16_sw<D>((const _Float16*)Qs, kk, 32 * db), dsf, dk[db]);
+                    }
                 }
-        } else {
+            } else {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int s2 = 0; s2 < 16; ++s2) {
-                        dv[db] = M::mma(tr_frag_f32((const float*)Os, QSTR, mb, s2, 32 * db), p[mb][s2], dv[db]);
-                        dk[db] = M::mma(tr_frag_f32((const float*)Qs, QSTR, mb, s2, 32 * db), ds[mb][s2], dk[db]);
+                        dv[db] = M::mma(tr_frag_f32_sw<D>((const float*)Os, mb, s2, 32 * db), p[s2], dv[db]);
+                        dk[db] = M::mma(tr_frag_f32_sw<D>((const float*)Qs, mb, s2, 32 * db), ds[s2], dk[db]);
                     }
+            }
         }
     }
 
@@ -524,25 +465,25 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 
 // =====================================================================================
 // Backward, dQ (deterministic: a separate pass that recomputes S and dP, no atomics).
-// grid (nrb, Hkv, B), 256 threads = 4 waves x 32 flattened rows, 64-key tiles.
+// grid (nrb * B * Hkv), 256 threads = 4 waves x 32 flattened rows, 64-key tiles.
 // S^T = K Q^T and dP^T = V dO^T put one query row per lane; dQ^T += K^T dS^T reads K^T from the
-// same row-major K tile with transposed reads.
+// same swizzled K tile with transposed reads.  K and V tiles arrive by direct HBM->LDS loads.
 // =====================================================================================
 template <typename OP, int D, typename TOUT>
-__global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void dq_kernel(BwdArgs a) {
     using M = Mma<OP>;
     constexpr bool F16 = sizeof(OP) == 2;
-    constexpr int BM = 128, BN = 64;
-    constexpr int KSTR = Strides<OP>::template row<D>;
-    constexpr int VSTR = Strides<OP>::template row<D>;
+    constexpr int BM = 128, BN = 64, NW = 4;
     constexpr int KS = D / M::K;
     constexpr int NDB = D / 32;
-    constexpr int STAGE = BN * (KSTR + VSTR);
-    __shared__ __attribute__((aligned(16))) OP lds[2 * STAGE];
+    constexpr int TILE = BN * D;
+    __shared__ __attribute__((aligned(1024))) OP lds[2 * 2 * TILE];
 
     const int T = a.T, G = a.G, TG = T * G;
-    const int rb = a.nrb - 1 - blockIdx.x;
-    const int hkv = blockIdx.y, b = blockIdx.z;
+    const Work wk = map_block(a.nrb, a.B * a.Hkv, true);
+    const int rb = wk.blk;
+    const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
     const int R0 = rb * BM;
     const int Rw = R0 + 32 * w;
@@ -553,11 +494,14 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     const int wave_tmax = min(Rw + 31, TG - 1) / G;
     const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;
 
-    const size_t grp = (size_t)b * a.Hkv + hkv;
+    const size_t grp = (size_t)wk.grp;
     const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
     const OP* og = (const OP*)a.dOh + grp * (size_t)TG * D;
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
     const OP* vg = (const OP*)a.vh + grp * (size_t)T * D;
+
+    lds_fill<OP, D, BN, NW>(lds, kg, 0, T);
+    lds_fill<OP, D, BN, NW>(lds + TILE, vg, 0, T);
 
     typename M::frag qf[KS], of[KS];
 #pragma unroll
@@ -577,18 +521,14 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[db] = floatx16{};
 
-    TileLoader<OP, D, BN> kl, vl;
-    kl.load(kg, 0, T);
-    vl.load(vg, 0, T);
     for (int it = 0; it < ntiles; ++it) {
-        OP* Ks = lds + (it & 1) * STAGE;
-        OP* Vs = Ks + BN * KSTR;
-        kl.template store<KSTR>(Ks);
-        vl.template store<VSTR>(Vs);
-        __syncthreads();
+        const OP* Ks = lds + (it & 1) * 2 * TILE;
+        const OP* Vs = Ks + TILE;
+        lds_fill_wait();
         if (it + 1 < ntiles) {
-            kl.load(kg, (it + 1) * BN, T);
-            vl.load(vg, (it + 1) * BN, T);
+            OP* nxt = lds + ((it + 1) & 1) * 2 * TILE;
+            lds_fill<OP, D, BN, NW>(nxt, kg, (it + 1) * BN, T);
+            lds_fill<OP, D, BN, NW>(nxt + TILE, vg, (it + 1) * BN, T);
         }
         const int n0 = it * BN;
         if (n0 > wave_tmax) continue;
@@ -598,17 +538,19 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             floatx16 sacc = floatx16{}, dpacc = floatx16{};
-            const OP* krow = Ks + (32 * mb + c) * KSTR;
-            const OP* vrow = Vs + (32 * mb + c) * VSTR;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                sacc = M::mma(M::row_frag(krow, ks, h, D), qf[ks], sacc);
-                dpacc = M::mma(M::row_frag(vrow, ks, h, D), of[ks], dpacc);
+                sacc = M::mma(row_frag_sw<OP, D>(Ks, 32 * mb + c, ks, h), qf[ks], sacc);
+                dpacc = M::mma(row_frag_sw<OP, D>(Vs, 32 * mb + c, ks, h), of[ks], dpacc);
+            }
+            if (need_mask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (n0 + 32 * mb + acc_row(r, h) > t_lane) sacc[r] = -INFINITY;
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float pv = __builtin_amdgcn_exp2f(sacc[r] - L);
-                if (need_mask && n0 + 32 * mb + acc_row(r, h) > t_lane) pv = 0.f;
+                const float pv = __builtin_amdgcn_exp2f(sacc[r] - L);
                 ds[mb][r] = pv * (dpacc[r] - Dl);
             }
         }
@@ -620,7 +562,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    dq[db] = M::mma(tr_frag_f16((const _Float16*)Ks, KSTR, kk, 32 * db), dsf[kk], dq[db]);
+                    dq[db] = M::mma(tr_frag_f16_sw<D>((const _Float16*)Ks, kk, 32 * db), dsf[kk], dq[db]);
         } else {
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -628,7 +570,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                     for (int s2 = 0; s2 < 16; ++s2)
-                        dq[db] = M::mma(tr_frag_f32((const float*)Ks, KSTR, mb, s2, 32 * db), ds[mb][s2], dq[db]);
+                        dq[db] = M::mma(tr_frag_f32_sw<D>((const float*)Ks, mb, s2, 32 * db), ds[mb][s2], dq[db]);
         }
     }
 
@@ -693,11 +635,11 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(0));
     NE_TRY(m.before(1));
-    hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3((ba.T + 127) / 128, ba.Hkv, ba.B), dim3(256), 0, s, ba);
+    hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3((ba.T + 127) / 128 * ba.Hkv * ba.B), dim3(256), 0, s, ba);
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(1));
     NE_TRY(m.before(2));
-    hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb, ba.Hkv, ba.B), dim3(256), 0, s, ba);
+    hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
     NE_TRY(hipGetLastError());
     return m.after(2);
 }

@@ -56,15 +56,15 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, ne_dtype_t in) {
     const size_t nq = (size_t)B * T * Hq * D, nk = (size_t)B * T * Hkv * D;
     Layout L{};
     size_t off = 0;
-    L.qh = off; off += up(nq * esz);
+    if (bwd) { L.qh = off; off += up(nq * esz); }
     L.kh = off; off += up(nk * esz);
     L.vh = off; off += up(nk * esz);
     if (bwd) {
         L.dOh = off; off += up(nq * esz);
         L.delta = off; off += up((size_t)B * T * Hq * 4);
         L.lse2 = off; off += up((size_t)B * T * Hq * 4);
-        L.table = off; off += up((size_t)T * (D / 2) * 8);
     }
+    L.table = off; off += up((size_t)T * (D / 2) * 8);
     L.total = off;
     return L;
 }
@@ -135,12 +135,13 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     const int G = Hq / Hkv;
     ne::PrepArgs pa{};
     pa.q = q; pa.k = k; pa.v = v;
-    pa.qh = ws + L.qh; pa.kh = ws + L.kh; pa.vh = ws + L.vh;
+    pa.kh = ws + L.kh; pa.vh = ws + L.vh; pa.table = (float2*)(ws + L.table);
     pa.B = B; pa.T = T; pa.Hq = Hq; pa.Hkv = Hkv; pa.D = head_dim;
     pa.rope_base = rope_base;
     pa.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
     ne::FwdArgs fa{};
-    fa.qh = pa.qh; fa.kh = pa.kh; fa.vh = pa.vh; fa.o = o; fa.lse = lse;
+    fa.q = q; fa.kh = pa.kh; fa.vh = pa.vh; fa.table = pa.table; fa.o = o; fa.lse = lse;
+    fa.rope_base = rope_base; fa.qscale = pa.qscale;
     fa.B = B; fa.T = T; fa.Hq = Hq; fa.Hkv = Hkv; fa.G = G;
     fa.nrb = (int)(((int64_t)T * G + 127) / 128);
     hipError_t e = ne::launch_fwd((int)in_dtype, (int)out_dtype, head_dim, pa, fa, (hipStream_t)stream,

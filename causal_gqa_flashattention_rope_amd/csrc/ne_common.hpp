@@ -124,6 +124,29 @@ struct Tile {
     }
 };
 
+// Direct global->LDS loads (global_load_lds_dwordx4 / _dword): each lane of the wave fetches
+// 16 (or 4) bytes from its own global address into LDS bytes [16 lane, 16 lane + 16) (or
+// [4 lane, 4 lane + 4)) above the wave-uniform base in M0.  They are issued from inline assembly
+// so that the compiler does not guard every later LDS read with a wait for all outstanding
+// loads (it cannot tell the ring stages apart); the kernels wait explicitly with
+// lds_fill_wait / lds_fill_wait_keep, which count this wave's outstanding vector-memory
+// operations.  No compiler-generated code in these kernels keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane(
+        (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p);
+}
+__device__ __forceinline__ void dma16(const void* g, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(lds_base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(g), "s"(lds_base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Copy rows [n0, n0 + ROWS) of a dense [nrows][D] array into a swizzled LDS tile with direct
 // global->LDS loads issued by the NW waves of the block.  Rows at or past nrows are filled from
 // row nrows - 1 (finite data that the callers mask out).  Completion: s_waitcnt vmcnt(0) then
@@ -132,23 +155,62 @@ template <typename OP, int D, int ROWS, int NW>
 __device__ __forceinline__ void lds_fill(OP* tile, const OP* src, int n0, int nrows) {
     using TL = Tile<OP, D>;
     constexpr int CHUNKS = ROWS * TL::CPR;
-    static_assert(CHUNKS % (64 * NW) == 0, "tile must be a whole number of wave loads");
+    constexpr int WL = CHUNKS / 64;                    // 1 KiB wave loads per tile
+    static_assert(CHUNKS % 64 == 0, "tile must be a whole number of wave loads");
     const int l = lane_id(), w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < CHUNKS / (64 * NW); ++i) {
-        const int q = 64 * (i * NW + w) + l;           // LDS slot index of this lane
+    for (int i = 0; i < (WL + NW - 1) / NW; ++i) {
+        const int j = i * NW + w;                      // wave load index (uniform per wave)
+        if (WL % NW != 0 && j >= WL) break;
+        const int q = 64 * j + l;                      // LDS slot index of this lane
         const int r = q / TL::CPR, p = q % TL::CPR;
         const int gr = min(n0 + r, nrows - 1);
         const OP* g = src + (size_t)gr * D + (p ^ TL::swz(r)) * TL::EPC;
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                         (void __attribute__((address_space(3)))*)
-                                             (reinterpret_cast<char*>(tile) + 1024 * (i * NW + w)),
-                                         16, 0, 0);
+        dma16(g, lds_addr(reinterpret_cast<char*>(tile) + 1024 * j));
     }
 }
 
+// s_waitcnt immediate (gfx9 layout): vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Everything this wave issued to memory has completed (also tells the compiler's wait
+// tracking that no earlier load is pending, so it adds no waits of its own inside the loops).
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
 __device__ __forceinline__ void lds_fill_wait() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmcnt<0>();
+    __syncthreads();
+}
+
+// Number of direct loads one wave issues in lds_fill<OP, D, ROWS, NW>.
+template <typename OP, int D, int ROWS, int NW>
+__device__ __forceinline__ int lds_fill_count(int w) {
+    constexpr int WL = ROWS * Tile<OP, D>::CPR / 64;
+    return WL / NW + (w < WL % NW ? 1 : 0);
+}
+
+// Wait until at most n of this wave's vector-memory operations are outstanding (they complete
+// in order), then barrier: the fills issued before the n most recent loads have landed.
+__device__ __forceinline__ void lds_fill_wait_keep(int n) {
+    switch (n) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 9: wait_vmcnt<9>(); break;
+        case 10: wait_vmcnt<10>(); break;
+        case 11: wait_vmcnt<11>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
     __syncthreads();
 }
 
@@ -181,6 +243,46 @@ template <typename OP, int D>
 __device__ __forceinline__ typename Mma<OP>::frag row_frag_sw(const OP* tile, int r, int ks, int h) {
     if constexpr (sizeof(OP) == 2) return *reinterpret_cast<const half8*>(Tile<OP, D>::ptr(tile, r, 16 * ks + 8 * h));
     else return *Tile<OP, D>::ptr(tile, r, 2 * ks + h);
+}
+
+// ---- coalesced row stores through LDS ------------------------------------------------------
+// A wave holds 32 rows x D outputs in the 32x32 accumulator layout (lane (h, c) holds row c,
+// columns 32db + acc_row(r, h)).  store_rows writes them, times `mul`, as whole rows: first
+// into a per-wave LDS scratch of 32 rows (16-byte chunks of row r XOR-permuted by r, so the
+// 32 lanes writing one chunk column hit distinct banks), then 64 lanes store two contiguous
+// rows per instruction.  row_ptr(i) gives the destination of row i (nullptr: skip).
+template <typename T> struct Pack4;
+template <> struct Pack4<float> { typedef floatx4 type; };
+template <> struct Pack4<_Float16> { typedef half4v type; };
+template <> struct Pack4<__bf16> { typedef __bf16 type __attribute__((ext_vector_type(4))); };
+
+template <typename TOUT, int D, typename RowPtr>
+__device__ __forceinline__ void store_rows(const floatx16 (&acc)[D / 32], float mul, char* scratch,
+                                           RowPtr row_ptr) {
+    constexpr int RB = D * (int)sizeof(TOUT);  // bytes per row
+    constexpr int CPR = RB / 16;               // 16-byte chunks per row
+    const int l = lane_id(), h = l >> 5, c = l & 31;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int byte = (32 * db + 8 * q4 + 4 * h) * (int)sizeof(TOUT);
+            const int off = c * RB + (((byte >> 4) ^ (c % CPR)) << 4) + (byte & 15);
+            typename Pack4<TOUT>::type v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = from_f32<TOUT>(acc[db][4 * q4 + e] * mul);
+            *reinterpret_cast<typename Pack4<TOUT>::type*>(scratch + off) = v;
+        }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+        const int idx = 64 * i + l;
+        const int row = idx / CPR, ch = idx % CPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(scratch + row * RB + ((ch ^ (row % CPR)) << 4));
+        TOUT* dst = row_ptr(row);
+        if (dst) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(dst) + ch * 16) = v;
+    }
 }
 
 // ---- small vector stores of four consecutive output elements -----------------------------

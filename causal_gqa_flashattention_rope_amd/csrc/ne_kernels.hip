@@ -10,9 +10,10 @@
 //    launch and memory traffic, which is why RoPE is folded into the operand preparation here).
 //
 // Pipeline of one call (all stream-ordered, no host synchronisation):
-//  forward : prep  -> q~ = fp16(R(q) * scale * log2 e), k' = fp16(R(k)), v' = fp16(v)  (workspace)
-//            fwd   -> per 128 flattened (token, head) rows of one KV group: online softmax over
-//                     64-key tiles staged once in LDS for all query heads of the group; o, lse.
+//  forward : prep  -> k' = fp16(R(k)), v' = fp16(v), cos/sin table (workspace)
+//            fwd   -> per 128 flattened (token, head) rows of one KV group: q~ = fp16(R(q) * scale *
+//                     log2 e) in registers, online softmax over 64-key tiles staged once in LDS for
+//                     all query heads of the group; o, lse.
 //  backward: prep  -> q~, k', v', dO' and Delta = rowsum(dO * o), lse2 = lse * log2 e, cos/sin table
 //            dkdv  -> per 128 keys of one KV head: dK, dV accumulated over every query row of the
 //                     group (all G heads), written once; inverse RoPE in the epilogue.
@@ -66,7 +67,8 @@ __device__ __forceinline__ void convert8(const TI* src, OP* dst, const float2* c
     for (int e = 0; e < 8; ++e) dst[e] = from_f32<OP>(x[e] * mul);
 }
 
-// grid (ceil(T / TT), B), 256 threads.  Forward: q, k, v.  Backward adds dO, Delta, lse2, table.
+// grid (ceil(T / TT), B), 256 threads.  Forward: k, v and the cos/sin table.  Backward: q, k, v,
+// dO, Delta, lse2 and the table.
 template <typename TI, typename TO, typename OP, int D, bool BWD>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     constexpr int TT = 8;
@@ -77,13 +79,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const bool rope = a.rope_base > 0.0;
     rope_cs_fill<D>(cs, t0, TT, T, a.rope_base);
     __syncthreads();
-    if (BWD && b == 0 && rope) {
+    if (b == 0 && rope) {
         for (int idx = threadIdx.x; idx < TT * (D / 2); idx += blockDim.x) {
             const int t = t0 + idx / (D / 2);
             if (t < T) a.table[(size_t)t * (D / 2) + idx % (D / 2)] = cs[idx];
         }
     }
-    const int rows_per_tok = BWD ? (2 * Hq + 2 * Hkv) : (Hq + 2 * Hkv);
+    const int qrows = BWD ? Hq : 0;  // the forward rotates q inside the attention kernel
+    const int rows_per_tok = qrows + 2 * Hkv + (BWD ? Hq : 0);
     const int items = TT * rows_per_tok * CPR;
     const int items_pad = (items + 255) / 256 * 256;  // whole waves iterate together
     const size_t TG = (size_t)T * G;
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         const int chunk = idx % CPR;
         const int rowid = idx / CPR;
         const int tl = rowid / rows_per_tok;
-        const int which = rowid % rows_per_tok;
+        const int which = rowid % rows_per_tok + (BWD ? 0 : Hq);  // forward: skip the q rows
         const int t = t0 + tl;
         const bool live = idx < items && t < T;
         const float2* csr = cs + tl * (D / 2);
@@ -177,7 +180,70 @@ __device__ __forceinline__ Work map_block(int nblk, int ngrp, bool longest_last)
 // is refreshed only when a row's new maximum exceeds it by more than 2^8 (the probabilities stay
 // below 256 in between), so the rescale of O is rare.
 // =====================================================================================
-template <typename OP, int D, typename TOUT>
+// Eight consecutive input elements as fp32, with 16-byte loads.
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(p), b = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+}
+template <typename T16>
+__device__ __forceinline__ void load8(const T16* p, float (&x)[8]) {
+    typedef T16 v8 __attribute__((ext_vector_type(8)));
+    const v8 a = *reinterpret_cast<const v8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+}
+
+// Query fragments (B operand of S^T = K Q^T) of one row, rotated, scaled and converted.
+template <typename TI, typename OP, int D>
+__device__ __forceinline__ void load_q_frags(typename Mma<OP>::frag (&qf)[D / Mma<OP>::K], const TI* row,
+                                             const float2* cs, float mul, int h, bool valid) {
+    constexpr int KS = D / Mma<OP>::K;
+    if constexpr (sizeof(OP) == 2) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            float x[8];
+            if (valid) {
+                const int e0 = 16 * ks + 8 * h;
+                load8(row + e0, x);
+                if (cs) {
+                    const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs + e0 / 2);
+                    const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs + e0 / 2 + 2);
+                    const float2 rr[4] = {{c01[0], c01[1]}, {c01[2], c01[3]}, {c23[0], c23[1]}, {c23[2], c23[3]}};
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float2 r = rr[p];
+                        const float u = x[2 * p], v = x[2 * p + 1];
+                        x[2 * p] = u * r.x - v * r.y;
+                        x[2 * p + 1] = u * r.y + v * r.x;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[ks][e] = (_Float16)(x[e] * mul);
+        }
+    } else {
+        // fp32 operands: k-step ks uses element 2ks + h, i.e. one element of rotary pair ks
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            float val = 0.f;
+            if (valid) {
+                const float u = to_f32(row[2 * ks]), v = to_f32(row[2 * ks + 1]);
+                val = h == 0 ? u : v;
+                if (cs) {
+                    const float2 r = cs[ks];
+                    val = h == 0 ? u * r.x - v * r.y : u * r.y + v * r.x;
+                }
+            }
+            qf[ks] = val * mul;
+        }
+    }
+}
+
+template <typename TI, typename OP, int D, typename TOUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdArgs a) {
     using M = Mma<OP>;
@@ -205,19 +271,19 @@ void fwd_kernel(FwdArgs a) {
     const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;
 
     const size_t grp = (size_t)wk.grp;
-    const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
     const OP* vg = (const OP*)a.vh + grp * (size_t)T * D;
-
-    lds_fill<OP, D, BN, NW>(lds, kg, 0, T);
-    lds_fill<OP, D, BN, NW>(lds + TILE, vg, 0, T);
+    const bool rope = a.rope_base > 0.0;
 
     typename M::frag qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        if (rvalid) qf[ks] = M::row_frag(qg + (size_t)R * D, ks, h, D);
-        else qf[ks] = typename M::frag{};
+    {
+        const int t = min(t_lane, T - 1), hh = R - t_lane * G;
+        const TI* qrow = (const TI*)a.q + (((size_t)b * T + t) * a.Hq + hkv * G + hh) * D;
+        load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, a.qscale, h, rvalid);
     }
+    wait_all();
+    lds_fill<OP, D, BN, NW>(lds, kg, 0, T);
+    lds_fill<OP, D, BN, NW>(lds + TILE, vg, 0, T);
 
     float m_run = -INFINITY, l_run = 0.f;
     floatx16 oacc[NDB];
@@ -300,51 +366,62 @@ void fwd_kernel(FwdArgs a) {
 
     const float l_tot = sum_halves(l_run);
     const float inv = 1.f / l_tot;
-    if (rvalid) {
-        const int t = t_lane, hh = R - t * G, hq = hkv * G + hh;
-        TOUT* orow = (TOUT*)a.o + (((size_t)b * T + t) * a.Hq + hq) * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                store4(orow + 32 * db + 8 * q4 + 4 * h, oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv,
-                       oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
-        if (h == 0) a.lse[((size_t)b * a.Hq + hq) * T + t] = (m_run + __log2f(l_tot)) * kLn2;
+    if (rvalid && h == 0) {
+        const int t = t_lane, hq = hkv * G + (R - t * G);
+        a.lse[((size_t)b * a.Hq + hq) * T + t] = (m_run + __log2f(l_tot)) * kLn2;
     }
+    // o rows through LDS (the K/V stages are free once every wave has left the loop)
+    static_assert(2 * 2 * TILE * sizeof(OP) >= 4 * 32 * D * sizeof(TOUT), "LDS holds the output rows");
+    __syncthreads();
+    store_rows<TOUT, D>(oacc, inv, reinterpret_cast<char*>(lds) + w * 32 * D * (int)sizeof(TOUT), [&](int i) {
+        const int Ri = Rw + i;
+        if (Ri >= TG) return (TOUT*)nullptr;
+        const int t = Ri / G;
+        return (TOUT*)a.o + (((size_t)b * T + t) * a.Hq + hkv * G + (Ri - t * G)) * D;
+    });
 }
 
 // =====================================================================================
-// Backward, dK/dV.  grid (ceil(T / 128) * B * Hkv), 256 threads = 4 waves x 32 keys.
-// S = Q K^T and dP = dO V^T put one key per lane and 16 query rows per lane half, so P and dS
-// feed dV^T += dO^T P and dK^T += Q^T dS directly as contraction operands; dO^T and Q^T come
-// from transposed reads of the same swizzled row-major LDS tiles that feed S and dP.  Every
-// flattened row of the group (all G query heads) passes through the same accumulators: dK and
-// dV of a KV head are summed over its query-head group in registers and written once.
-// Q/dO tiles (64 rows) arrive by direct HBM->LDS loads, double-buffered.
+// Backward, dK/dV.  One workgroup = 8 waves owns a pair of 64-key blocks of one KV head, the
+// block kb and its mirror nkb - 1 - kb, processed one after the other, so every workgroup has
+// the same causal work.  grid (ceil(nkb / 2) * B * Hkv), nkb = ceil(T / 64).
+//   wave w: row half rh = w & 1 of each 64-row tile, 32-key sub-block kq = (w >> 1) & 1,
+//   role = w >> 2:
+//     role 0: S = Q K^T, P = exp2(S - lse2) (masked), dV^T += dO^T P;
+//     role 1: dP = dO V^T, dS = P (dP - Delta), dK^T += Q^T dS,
+//   P passes from the role-0 wave to the role-1 wave of the same row half through LDS (both
+//   waves hold the same (key, row) in the same lane and register).  S and dP put one key per
+//   lane and 16 rows per lane half, so P and dS feed the dV / dK products directly as
+//   contraction operands; dO^T and Q^T come from transposed reads of the swizzled row-major
+//   tiles.  Every flattened row of the group (all G query heads) passes through the same
+//   accumulators, so dK and dV are summed over the query-head group in registers; the two row
+//   halves are added in a fixed order through LDS at the end of a key block and written once.
 // =====================================================================================
 template <typename OP, int D, typename TOUT>
-__global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void dkdv_kernel(BwdArgs a) {
     using M = Mma<OP>;
     constexpr bool F16 = sizeof(OP) == 2;
-    constexpr int BN = 128, BMR = 64, NW = 4;
+    constexpr int KSUB = 2, BN = 32 * KSUB, BMR = 64, NW = 8, NST = F16 ? 3 : 2;  // ring of row tiles
     constexpr int KS = D / M::K;
     constexpr int NDB = D / 32;
     constexpr int TILE = BMR * D;
-    __shared__ __attribute__((aligned(1024))) OP lds[2 * 2 * TILE];
-    __shared__ __attribute__((aligned(16))) float rowv[2][2][BMR];  // [stage][lse2 | delta][row]
+    static_assert(NST * 2 * TILE * sizeof(OP) >= KSUB * 2 * NDB * 16 * 64 * sizeof(float),
+                  "staging area holds the partials");
+    __shared__ __attribute__((aligned(1024))) OP lds[NST * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) float pbuf[KSUB][2][4][64][4];  // [kq][row half][r/4][lane][r%4]
+    __shared__ __attribute__((aligned(16))) float rowv[NST][2][BMR];   // [stage][lse2 | delta][row]
 
     const int T = a.T, G = a.G, TG = T * G;
-    const Work wk = map_block((T + BN - 1) / BN, a.B * a.Hkv, false);
-    const int kb = wk.blk;
+    const int nkb = (T + BN - 1) / BN;
+    const int npair = (nkb + 1) / 2;
+    const Work wk = map_block(npair, a.B * a.Hkv, false);
     const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
-    const int n0 = kb * BN;
-    const int nw = n0 + 32 * w;            // first key of this wave
-    const int key = nw + c;
-    const bool kvalid = key < T;
-    const int keyG = key * G;              // row R sees this key iff R >= key * G
-    const int rstart = (n0 * G) / BMR * BMR;
-    const int ntiles = (TG - rstart + BMR - 1) / BMR;
+    // waves w and w + 4 (one per role, same row half and key sub-block) share a SIMD, so the
+    // exp/VALU phase of one overlaps the MFMA phase of the other
+    const int rh = w & 1, kq = (w >> 1) & 1, role = w >> 2;
+    const int per_fill = 2 * lds_fill_count<OP, D, BMR, NW>(w) + (w < 2 ? 1 : 0);  // loads per fill
 
     const size_t grp = (size_t)wk.grp;
     const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
@@ -353,114 +430,174 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     const OP* vg = (const OP*)a.vh + grp * (size_t)T * D;
     const float* lse2g = a.lse2 + grp * (size_t)TG;
     const float* delg = a.delta + grp * (size_t)TG;
+    const bool rope = a.rope_base > 0.0;
 
+    // Q and dO rows, lse2 (wave 0) and Delta (wave 1) of rows [R0, R0 + 64), all by direct loads;
+    // rows past TG are copies of row TG - 1 and are masked out (P = 0) below.
     auto fill = [&](int stage, int R0) {
         OP* dst = lds + stage * 2 * TILE;
         lds_fill<OP, D, BMR, NW>(dst, qg, R0, TG);
         lds_fill<OP, D, BMR, NW>(dst + TILE, og, R0, TG);
-        if (tid < BMR) {
-            const int Rr = R0 + tid;
-            rowv[stage][0][tid] = Rr < TG ? lse2g[Rr] : INFINITY;  // padded rows: P = exp2(-inf) = 0
-            rowv[stage][1][tid] = Rr < TG ? delg[Rr] : 0.f;
+        if (w < 2) {
+            const float* src = (w == 0 ? lse2g : delg) + min(R0 + l, TG - 1);
+            dma4(src, lds_addr(&rowv[stage][w][0]));
         }
     };
-    fill(0, rstart);
 
-    typename M::frag kf[KS], vf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        if (kvalid) {
-            kf[ks] = M::row_frag(kg + (size_t)key * D, ks, h, D);
-            vf[ks] = M::row_frag(vg + (size_t)key * D, ks, h, D);
-        } else {
-            kf[ks] = typename M::frag{};
-            vf[ks] = typename M::frag{};
-        }
-    }
-    floatx16 dk[NDB], dv[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) { dk[db] = floatx16{}; dv[db] = floatx16{}; }
+    for (int pass = 0; pass < 2; ++pass) {
+        const int kb = pass == 0 ? wk.blk : nkb - 1 - wk.blk;
+        if (pass == 1 && kb == wk.blk) break;  // odd nkb: the middle block has no mirror
+        const int n0 = kb * BN + 32 * kq;                      // first key of this wave
+        const int key = n0 + c;
+        const bool kvalid = key < T;
+        const int keyG = key * G;              // row R sees this key iff R >= key * G
+        const int rstart = (kb * BN * G) / BMR * BMR;
+        const int ntiles = (TG - rstart + BMR - 1) / BMR;
 
-    for (int it = 0; it < ntiles; ++it) {
-        const int st = it & 1;
-        const OP* Qs = lds + st * 2 * TILE;
-        const OP* Os = Qs + TILE;
-        const int R0 = rstart + it * BMR;
-        lds_fill_wait();
-        if (it + 1 < ntiles) fill(st ^ 1, R0 + BMR);
-        const int Rlast = min(R0 + BMR - 1, TG - 1);
-        if (Rlast < nw * G) continue;  // every row of the tile precedes this wave's keys
-        const bool need_mask = R0 < (nw + 31) * G;
+        // role 0 keeps K^T fragments, role 1 keeps V^T fragments (B operands, one key per lane)
+        typename M::frag kvf[KS];
+        const OP* kvrow = (role == 0 ? kg : vg) + (size_t)key * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kvf[ks] = kvalid ? M::row_frag(kvrow, ks, h, D) : typename M::frag{};
+        floatx16 acc[NDB];  // role 0: dV^T, role 1: dK^T (d rows, this lane's key column)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = floatx16{};
+        wait_all();
 
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            floatx16 sacc = floatx16{}, dpacc = floatx16{};
+        for (int s0 = 0; s0 < NST - 1; ++s0)
+            if (s0 < ntiles) fill(s0, rstart + s0 * BMR);
+        for (int it = 0; it < ntiles; ++it) {
+            const int st = it % NST;
+            const OP* Qs = lds + st * 2 * TILE;
+            const OP* Os = Qs + TILE;
+            const int R0 = rstart + it * BMR;
+            // barrier 1: tile it is in LDS (the fills of the younger tiles may still be in flight)
+            lds_fill_wait_keep(per_fill * min(NST - 2, ntiles - 1 - it));
+            if (it + NST - 1 < ntiles) fill((it + NST - 1) % NST, R0 + (NST - 1) * BMR);
+            const int Rh = R0 + 32 * rh;                       // first row of this wave's half
+            const bool active = min(Rh + 31, TG - 1) >= n0 * G && Rh < TG;
+            const bool need_mask = Rh < (n0 + 31) * G || Rh + 32 > TG;
+            floatx16 x = floatx16{};                           // role 0: S, role 1: dP
+            if (active) {
+                const OP* rows = role == 0 ? Qs : Os;
+                typename M::frag af[KS];  // all A fragments first: one LDS round trip per phase
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                sacc = M::mma(row_frag_sw<OP, D>(Qs, 32 * mb + c, ks, h), kf[ks], sacc);
-                dpacc = M::mma(row_frag_sw<OP, D>(Os, 32 * mb + c, ks, h), vf[ks], dpacc);
-            }
-            floatx16 p, ds;
+                for (int ks = 0; ks < KS; ++ks) af[ks] = row_frag_sw<OP, D>(rows, 32 * rh + c, ks, h);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int rr = 32 * mb + 8 * q4 + 4 * h;
-                const floatx4 Lv = *reinterpret_cast<const floatx4*>(&rowv[st][0][rr]);
-                const floatx4 Dv = *reinterpret_cast<const floatx4*>(&rowv[st][1][rr]);
+                for (int ks = 0; ks < KS; ++ks) x = M::mma(af[ks], kvf[ks], x);
+                if (role == 0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * q4 + e;
-                    float sv = sacc[r];
-                    if (need_mask && R0 + rr + e < keyG) sv = -INFINITY;
-                    const float pv = __builtin_amdgcn_exp2f(sv - Lv[e]);
-                    p[r] = pv;
-                    ds[r] = pv * (dpacc[r] - Dv[e]);
-                }
-            }
-            if constexpr (F16) {
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int rr = 32 * rh + 8 * q4 + 4 * h;
+                        const floatx4 Lv = *reinterpret_cast<const floatx4*>(&rowv[st][0][rr]);
+                        floatx4 pv;
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    const half8 pf = pack_frag_f16(p, cc), dsf = pack_frag_f16(ds, cc);
-                    const int kk = 2 * mb + cc;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        dv[db] = M::mma(tr_frag_f16_sw<D>((const _Float16*)Os, kk, 32 * db), pf, dv[db]);
-                        dk[db] = M::mma(tr_frag_f16_sw<D>((const _Float16*)Qs, kk, 32 * db), dsf, dk[db]);
+                        for (int e = 0; e < 4; ++e) {
+                            float sv = x[4 * q4 + e];
+                            if (need_mask && (R0 + rr + e < keyG || R0 + rr + e >= TG)) sv = -INFINITY;
+                            pv[e] = __builtin_amdgcn_exp2f(sv - Lv[e]);
+                            x[4 * q4 + e] = pv[e];
+                        }
+                        *reinterpret_cast<floatx4*>(&pbuf[kq][rh][q4][l][0]) = pv;
                     }
                 }
-            } else {
+            }
+            __syncthreads();                                   // barrier 2: P of this tile shared
+            if (active) {
+                if (role == 0) {
+                    if constexpr (F16) {
+                        half8 tf[2][NDB];
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                        for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-                    for (int s2 = 0; s2 < 16; ++s2) {
-                        dv[db] = M::mma(tr_frag_f32_sw<D>((const float*)Os, mb, s2, 32 * db), p[s2], dv[db]);
-                        dk[db] = M::mma(tr_frag_f32_sw<D>((const float*)Qs, mb, s2, 32 * db), ds[s2], dk[db]);
+                            for (int db = 0; db < NDB; ++db)
+                                tf[cc][db] = tr_frag_f16_sw<D>((const _Float16*)Os, 2 * rh + cc, 32 * db);
+#pragma unroll
+                        for (int cc = 0; cc < 2; ++cc) {
+                            const half8 pf = pack_frag_f16(x, cc);
+#pragma unroll
+                            for (int db = 0; db < NDB; ++db) acc[db] = M::mma(tf[cc][db], pf, acc[db]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                            for (int s2 = 0; s2 < 16; ++s2)
+                                acc[db] = M::mma(tr_frag_f32_sw<D>((const float*)Os, rh, s2, 32 * db), x[s2], acc[db]);
                     }
+                } else {
+                    floatx16 ds;
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int rr = 32 * rh + 8 * q4 + 4 * h;
+                        const floatx4 Dv = *reinterpret_cast<const floatx4*>(&rowv[st][1][rr]);
+                        const floatx4 pv = *reinterpret_cast<const floatx4*>(&pbuf[kq][rh][q4][l][0]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ds[4 * q4 + e] = pv[e] * (x[4 * q4 + e] - Dv[e]);
+                    }
+                    if constexpr (F16) {
+                        half8 tf[2][NDB];
+#pragma unroll
+                        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                            for (int db = 0; db < NDB; ++db)
+                                tf[cc][db] = tr_frag_f16_sw<D>((const _Float16*)Qs, 2 * rh + cc, 32 * db);
+#pragma unroll
+                        for (int cc = 0; cc < 2; ++cc) {
+                            const half8 dsf = pack_frag_f16(ds, cc);
+#pragma unroll
+                            for (int db = 0; db < NDB; ++db) acc[db] = M::mma(tf[cc][db], dsf, acc[db]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                            for (int s2 = 0; s2 < 16; ++s2)
+                                acc[db] = M::mma(tr_frag_f32_sw<D>((const float*)Qs, rh, s2, 32 * db), ds[s2], acc[db]);
+                    }
+                }
             }
         }
-    }
 
-    if (!kvalid) return;
-    // epilogue: dk' = ln2 * sum dS q~ (q~ carries scale * log2 e), then dk = R^T dk'
-    TOUT* dkrow = (TOUT*)a.dk + (((size_t)b * T + key) * a.Hkv + hkv) * D;
-    TOUT* dvrow = (TOUT*)a.dv + (((size_t)b * T + key) * a.Hkv + hkv) * D;
-    const bool rope = a.rope_base > 0.0;
+        // add the two row halves in a fixed order (half 0 + half 1) through the staging area
+        __syncthreads();
+        float* part = reinterpret_cast<float*>(lds) + (kq * 2 + role) * (NDB * 16 * 64);
+        if (rh == 1) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int d = 32 * db + 8 * q4 + 4 * h;
-            float x0 = dk[db][4 * q4] * kLn2, x1 = dk[db][4 * q4 + 1] * kLn2;
-            float x2 = dk[db][4 * q4 + 2] * kLn2, x3 = dk[db][4 * q4 + 3] * kLn2;
-            if (rope) {
-                const float2 r0 = a.table[(size_t)key * (D / 2) + d / 2];
-                const float2 r1 = a.table[(size_t)key * (D / 2) + d / 2 + 1];
-                const float y0 = x0 * r0.x + x1 * r0.y, y1 = -x0 * r0.y + x1 * r0.x;
-                const float y2 = x2 * r1.x + x3 * r1.y, y3 = -x2 * r1.y + x3 * r1.x;
-                x0 = y0; x1 = y1; x2 = y2; x3 = y3;
-            }
-            store4(dkrow + d, x0, x1, x2, x3);
-            store4(dvrow + d, dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]);
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *reinterpret_cast<floatx4*>(&part[((db * 4 + q4) * 64 + l) * 4]) =
+                        floatx4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
         }
+        __syncthreads();
+        if (rh == 0 && kvalid) {
+            TOUT* orow = (TOUT*)(role == 0 ? a.dv : a.dk) + (((size_t)b * T + key) * a.Hkv + hkv) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const floatx4 o1 = *reinterpret_cast<const floatx4*>(&part[((db * 4 + q4) * 64 + l) * 4]);
+                    const int d = 32 * db + 8 * q4 + 4 * h;
+                    float x0 = acc[db][4 * q4] + o1[0], x1 = acc[db][4 * q4 + 1] + o1[1];
+                    float x2 = acc[db][4 * q4 + 2] + o1[2], x3 = acc[db][4 * q4 + 3] + o1[3];
+                    if (role == 1) {
+                        // dk' = ln2 * sum dS q~ (q~ carries scale * log2 e), then dk = R^T dk'
+                        x0 *= kLn2; x1 *= kLn2; x2 *= kLn2; x3 *= kLn2;
+                        if (rope) {
+                            const float2 r0 = a.table[(size_t)key * (D / 2) + d / 2];
+                            const float2 r1 = a.table[(size_t)key * (D / 2) + d / 2 + 1];
+                            const float y0 = x0 * r0.x + x1 * r0.y, y1 = -x0 * r0.y + x1 * r0.x;
+                            const float y2 = x2 * r1.x + x3 * r1.y, y3 = -x2 * r1.y + x3 * r1.x;
+                            x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+                        }
+                    }
+                    store4(orow + d, x0, x1, x2, x3);
+                }
+        }
+        __syncthreads();  // the staging area is refilled by the next key block
+    }
 }
 
 // =====================================================================================
@@ -500,9 +637,6 @@ void dq_kernel(BwdArgs a) {
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
     const OP* vg = (const OP*)a.vh + grp * (size_t)T * D;
 
-    lds_fill<OP, D, BN, NW>(lds, kg, 0, T);
-    lds_fill<OP, D, BN, NW>(lds + TILE, vg, 0, T);
-
     typename M::frag qf[KS], of[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -516,6 +650,9 @@ void dq_kernel(BwdArgs a) {
     }
     const float L = rvalid ? a.lse2[grp * (size_t)TG + R] : INFINITY;
     const float Dl = rvalid ? a.delta[grp * (size_t)TG + R] : 0.f;
+    wait_all();
+    lds_fill<OP, D, BN, NW>(lds, kg, 0, T);
+    lds_fill<OP, D, BN, NW>(lds + TILE, vg, 0, T);
 
     floatx16 dq[NDB];
 #pragma unroll
@@ -622,7 +759,7 @@ static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, hipStream_
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(0));
     NE_TRY(m.before(1));
-    hipLaunchKernelGGL((fwd_kernel<OP, D, TO>), dim3(fa.nrb * fa.Hkv * fa.B), dim3(256), 0, s, fa);
+    hipLaunchKernelGGL((fwd_kernel<TI, OP, D, TO>), dim3(fa.nrb * fa.Hkv * fa.B), dim3(256), 0, s, fa);
     NE_TRY(hipGetLastError());
     return m.after(1);
 }
@@ -635,7 +772,7 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(0));
     NE_TRY(m.before(1));
-    hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3((ba.T + 127) / 128 * ba.Hkv * ba.B), dim3(256), 0, s, ba);
+    hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3(((ba.T + 63) / 64 + 1) / 2 * ba.Hkv * ba.B), dim3(512), 0, s, ba);
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(1));
     NE_TRY(m.before(2));

@@ -17,9 +17,13 @@ struct PrepArgs {
 };
 
 struct FwdArgs {
-    const void* qh; const void* kh; const void* vh;
+    const void* q;                                  // raw queries (in dtype), rotated in the kernel
+    const void* kh; const void* vh;                 // prepared keys / values
+    const float2* table;                            // cos/sin [T][D/2] (RoPE on)
     void* o; float* lse;
     int B, T, Hq, Hkv, G, nrb;
+    double rope_base;
+    float qscale;                                   // softmax scale * log2(e)
 };
 
 struct BwdArgs {

@@ -46,11 +46,12 @@ def test_workspace_sizes(L):
     def up(x):
         return (x + 255) // 256 * 256
     nq, nk = B * T * Hq * D, B * T * Hkv * D
+    table = up(T * (D // 2) * 8)
     fwd = L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
-    assert fwd == up(2 * nq) + 2 * up(2 * nk)
+    assert fwd == 2 * up(2 * nk) + table
     bwd = L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
-    assert bwd == 2 * up(2 * nq) + 2 * up(2 * nk) + 2 * up(4 * B * T * Hq) + up(T * (D // 2) * 8)
-    assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_F32) == up(4 * nq) + 2 * up(4 * nk)
+    assert bwd == 2 * up(2 * nq) + 2 * up(2 * nk) + 2 * up(4 * B * T * Hq) + table
+    assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_F32) == 2 * up(4 * nk) + table
     assert L.ne_rope_attn_fwd_workspace_bytes(B, T, 12, 5, D, binding.NE_BF16) == 0
     assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, 96, binding.NE_BF16) == 0
 

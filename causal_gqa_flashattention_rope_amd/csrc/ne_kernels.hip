@@ -478,84 +478,109 @@ void dkdv_kernel(BwdArgs a) {
             const int Rh = R0 + 32 * rh;                       // first row of this wave's half
             const bool active = min(Rh + 31, TG - 1) >= n0 * G && Rh < TG;
             const bool need_mask = Rh < (n0 + 31) * G || Rh + 32 > TG;
-            floatx16 x = floatx16{};                           // role 0: S, role 1: dP
-            if (active) {
-                const OP* rows = role == 0 ? Qs : Os;
-                typename M::frag af[KS];  // all A fragments first: one LDS round trip per phase
+            floatx16 x;                                        // role 0: S -> P, role 1: dP
+            if constexpr (F16) {
+                // every LDS fragment of this tile first (one round trip), then the products
+                half8 af[KS], tf[2][NDB];
+                if (active) {
+                    const OP* rows = role == 0 ? Qs : Os;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) af[ks] = row_frag_sw<OP, D>(rows, 32 * rh + c, ks, h);
+                    for (int ks = 0; ks < KS; ++ks) af[ks] = row_frag_sw<OP, D>(rows, 32 * rh + c, ks, h);
+                    const _Float16* trt = (const _Float16*)(role == 0 ? Os : Qs);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) x = M::mma(af[ks], kvf[ks], x);
-                if (role == 0) {
+                    for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int rr = 32 * rh + 8 * q4 + 4 * h;
-                        const floatx4 Lv = *reinterpret_cast<const floatx4*>(&rowv[st][0][rr]);
-                        floatx4 pv;
+                        for (int db = 0; db < NDB; ++db) tf[cc][db] = tr_frag_f16_sw<D>(trt, 2 * rh + cc, 32 * db);
+                    x = M::mma(af[0], kvf[0], floatx16{});
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            float sv = x[4 * q4 + e];
-                            if (need_mask && (R0 + rr + e < keyG || R0 + rr + e >= TG)) sv = -INFINITY;
-                            pv[e] = __builtin_amdgcn_exp2f(sv - Lv[e]);
-                            x[4 * q4 + e] = pv[e];
+                    for (int ks = 1; ks < KS; ++ks) x = M::mma(af[ks], kvf[ks], x);
+                    if (role == 0) {
+                        if (need_mask) {
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int row = Rh + acc_row(r, h);
+                                if (row < keyG || row >= TG) x[r] = -INFINITY;
+                            }
                         }
-                        *reinterpret_cast<floatx4*>(&pbuf[kq][rh][q4][l][0]) = pv;
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const int rr = 32 * rh + 8 * q4 + 4 * h;
+                            const floatx4 Lv = *reinterpret_cast<const floatx4*>(&rowv[st][0][rr]);
+                            floatx4 pv;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) pv[e] = x[4 * q4 + e] = __builtin_amdgcn_exp2f(x[4 * q4 + e] - Lv[e]);
+                            *reinterpret_cast<floatx4*>(&pbuf[kq][rh][q4][l][0]) = pv;
+                        }
                     }
                 }
-            }
-            __syncthreads();                                   // barrier 2: P of this tile shared
-            if (active) {
-                if (role == 0) {
-                    if constexpr (F16) {
-                        half8 tf[2][NDB];
-#pragma unroll
-                        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                            for (int db = 0; db < NDB; ++db)
-                                tf[cc][db] = tr_frag_f16_sw<D>((const _Float16*)Os, 2 * rh + cc, 32 * db);
-#pragma unroll
-                        for (int cc = 0; cc < 2; ++cc) {
-                            const half8 pf = pack_frag_f16(x, cc);
-#pragma unroll
-                            for (int db = 0; db < NDB; ++db) acc[db] = M::mma(tf[cc][db], pf, acc[db]);
-                        }
+                __syncthreads();                               // barrier 2: P of this tile shared
+                if (active) {
+                    floatx16 src;                              // role 0: P, role 1: dS
+                    if (role == 0) {
+                        src = x;
                     } else {
 #pragma unroll
-                        for (int db = 0; db < NDB; ++db)
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const int rr = 32 * rh + 8 * q4 + 4 * h;
+                            const floatx4 Dv = *reinterpret_cast<const floatx4*>(&rowv[st][1][rr]);
+                            const floatx4 pv = *reinterpret_cast<const floatx4*>(&pbuf[kq][rh][q4][l][0]);
 #pragma unroll
-                            for (int s2 = 0; s2 < 16; ++s2)
-                                acc[db] = M::mma(tr_frag_f32_sw<D>((const float*)Os, rh, s2, 32 * db), x[s2], acc[db]);
-                    }
-                } else {
-                    floatx16 ds;
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int rr = 32 * rh + 8 * q4 + 4 * h;
-                        const floatx4 Dv = *reinterpret_cast<const floatx4*>(&rowv[st][1][rr]);
-                        const floatx4 pv = *reinterpret_cast<const floatx4*>(&pbuf[kq][rh][q4][l][0]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) ds[4 * q4 + e] = pv[e] * (x[4 * q4 + e] - Dv[e]);
-                    }
-                    if constexpr (F16) {
-                        half8 tf[2][NDB];
-#pragma unroll
-                        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                            for (int db = 0; db < NDB; ++db)
-                                tf[cc][db] = tr_frag_f16_sw<D>((const _Float16*)Qs, 2 * rh + cc, 32 * db);
-#pragma unroll
-                        for (int cc = 0; cc < 2; ++cc) {
-                            const half8 dsf = pack_frag_f16(ds, cc);
-#pragma unroll
-                            for (int db = 0; db < NDB; ++db) acc[db] = M::mma(tf[cc][db], dsf, acc[db]);
+                            for (int e = 0; e < 4; ++e) src[4 * q4 + e] = pv[e] * (x[4 * q4 + e] - Dv[e]);
                         }
+                    }
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) {
+                        const half8 f = pack_frag_f16(src, cc);
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) acc[db] = M::mma(tf[cc][db], f, acc[db]);
+                    }
+                }
+            } else {
+                x = floatx16{};
+                if (active) {
+                    const OP* rows = role == 0 ? Qs : Os;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) x = M::mma(row_frag_sw<OP, D>(rows, 32 * rh + c, ks, h), kvf[ks], x);
+                    if (role == 0) {
+                        if (need_mask) {
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int row = Rh + acc_row(r, h);
+                                if (row < keyG || row >= TG) x[r] = -INFINITY;
+                            }
+                        }
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const int rr = 32 * rh + 8 * q4 + 4 * h;
+                            const floatx4 Lv = *reinterpret_cast<const floatx4*>(&rowv[st][0][rr]);
+                            floatx4 pv;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) pv[e] = x[4 * q4 + e] = __builtin_amdgcn_exp2f(x[4 * q4 + e] - Lv[e]);
+                            *reinterpret_cast<floatx4*>(&pbuf[kq][rh][q4][l][0]) = pv;
+                        }
+                    }
+                }
+                __syncthreads();                               // barrier 2: P of this tile shared
+                if (active) {
+                    floatx16 src;
+                    if (role == 0) {
+                        src = x;
                     } else {
 #pragma unroll
-                        for (int db = 0; db < NDB; ++db)
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const int rr = 32 * rh + 8 * q4 + 4 * h;
+                            const floatx4 Dv = *reinterpret_cast<const floatx4*>(&rowv[st][1][rr]);
+                            const floatx4 pv = *reinterpret_cast<const floatx4*>(&pbuf[kq][rh][q4][l][0]);
 #pragma unroll
-                            for (int s2 = 0; s2 < 16; ++s2)
-                                acc[db] = M::mma(tr_frag_f32_sw<D>((const float*)Qs, rh, s2, 32 * db), ds[s2], acc[db]);
+                            for (int e = 0; e < 4; ++e) src[4 * q4 + e] = pv[e] * (x[4 * q4 + e] - Dv[e]);
+                        }
                     }
+                    const float* trt = (const float*)(role == 0 ? Os : Qs);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int s2 = 0; s2 < 16; ++s2)
+                            acc[db] = M::mma(tr_frag_f32_sw<D>(trt, rh, s2, 32 * db), src[s2], acc[db]);
                 }
             }
         }

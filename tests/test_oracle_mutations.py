@@ -37,7 +37,7 @@ MUTATIONS = {
     "dv_uses_ds": ("dvj[d] += p * dOi[d];", "dvj[d] += s * dOi[d];"),
     "dk_uses_rotated_k": ("dkj[d] += s * qi[d];", "dkj[d] += s * kr[(size_t)i * D + d];"),
     "lse_without_max": ("lse_row[i] = m + log(l);", "lse_row[i] = log(l);"),
-    "delta_from_value": ("di += dOi[d] * oi[d];", "di += dOi[d] * oi[d] * 0.5;"),
+    "delta_from_value": ("di += dOi[d] * od[d];", "di += dOi[d] * od[d] * 0.5;"),
 }
 
 

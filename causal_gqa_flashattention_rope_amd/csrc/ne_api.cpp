@@ -57,8 +57,10 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, ne_dtype_t in) {
     Layout L{};
     size_t off = 0;
     if (bwd) { L.qh = off; off += up(nq * esz); }
+    // the forward keeps V'^T as [B * Hkv][D][Tp], Tp = T rounded up to 64 (zeros past T)
+    const size_t nv = bwd ? nk : (size_t)B * Hkv * D * (((size_t)T + 63) / 64 * 64);
     L.kh = off; off += up(nk * esz);
-    L.vh = off; off += up(nk * esz);
+    L.vh = off; off += up(nv * esz);
     if (bwd) {
         L.dOh = off; off += up(nq * esz);
         L.delta = off; off += up((size_t)B * T * Hq * 4);

@@ -238,6 +238,47 @@ __device__ __forceinline__ float tr_frag_f32_sw(const float* tile, int mb, int s
     return *Tile<float, D>::ptr(tile, 32 * mb + acc_row(s, l >> 5), col0 + (l & 31));
 }
 
+// ---- transposed value tiles (16-bit operands) ----------------------------------------------
+// V'^T of one (batch, KV head) group is stored as D rows of Tp keys (Tp = T rounded up to 64),
+// with the keys of every aligned group of 16 stored in the order 0-3, 8-11, 4-7, 12-15.  That is
+// the order in which a 32x32 accumulator hands its rows to the next product as contraction
+// index (pack_frag_f16), so the 16 bytes at key position 16 kk + 8 h of a row are exactly the A
+// operand a lane of half h needs for k-step kk of O^T += V^T P^T.  An LDS tile holds BN keys of
+// every row (BN = 32 or 64); chunk c of row r sits in slot c ^ ((r / (16 / CPR)) % CPR), CPR =
+// BN / 8 chunks per row, so the 16 lanes of one read touch 16 distinct 16-byte bank groups.
+__device__ __forceinline__ constexpr int vt_key_of_pos(int pos) {
+    return (pos & ~15) + 8 * ((pos >> 2) & 1) + 4 * ((pos >> 3) & 1) + (pos & 3);
+}
+template <int BN>
+struct VtTile {
+    static constexpr int CPR = BN / 8, RPG = 16 / CPR;  // chunks per row, rows per 256 bytes
+    __device__ __forceinline__ static constexpr int slot(int r, int c) { return c ^ ((r / RPG) % CPR); }
+};
+template <int BN>
+__device__ __forceinline__ half8 vt_frag(const _Float16* tile, int row, int kk, int h) {
+    return *reinterpret_cast<const half8*>(reinterpret_cast<const char*>(tile) + row * (2 * BN) +
+                                           (VtTile<BN>::slot(row, 2 * kk + h) << 4));
+}
+template <int D, int BN, int NW>
+__device__ __forceinline__ constexpr int lds_fill_vt_count(int w) {
+    return (D * BN / 512) / NW + (w < (D * BN / 512) % NW ? 1 : 0);
+}
+// Keys [n0, n0 + BN) of all D rows of a transposed value array (row stride Tp) into a tile.
+template <int D, int BN, int NW>
+__device__ __forceinline__ void lds_fill_vt(_Float16* tile, const _Float16* src, int n0, int Tp) {
+    constexpr int CPR = BN / 8, WL = D * CPR / 64;     // 1 KiB wave loads per tile
+    const int l = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < (WL + NW - 1) / NW; ++i) {
+        const int j = i * NW + w;
+        if (WL % NW != 0 && j >= WL) break;
+        const int q = 64 * j + l;
+        const int r = q / CPR, sl = q % CPR;
+        const _Float16* g = src + (size_t)r * Tp + n0 + 8 * VtTile<BN>::slot(r, sl);
+        dma16(g, lds_addr(reinterpret_cast<char*>(tile) + 1024 * j));
+    }
+}
+
 // Row fragment from a swizzled tile (k-step ks of row r), both operand types.
 template <typename OP, int D>
 __device__ __forceinline__ typename Mma<OP>::frag row_frag_sw(const OP* tile, int r, int ks, int h) {

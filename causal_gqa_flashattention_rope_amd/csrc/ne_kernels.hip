@@ -10,13 +10,15 @@
 //    launch and memory traffic, which is why RoPE is folded into the operand preparation here).
 //
 // Pipeline of one call (all stream-ordered, no host synchronisation):
-//  forward : prep  -> k' = fp16(R(k)), v' = fp16(v), cos/sin table (workspace)
-//            fwd   -> per 128 flattened (token, head) rows of one KV group: q~ = fp16(R(q) * scale *
-//                     log2 e) in registers, online softmax over 64-key tiles staged once in LDS for
-//                     all query heads of the group; o, lse.
+//  forward : prep  -> k' = fp16(R(k)) rows, v' = fp16(v) transposed (16-bit operands), cos/sin
+//                     table (workspace)
+//            fwd   -> per 256 (16-bit operands; 128 for fp32) flattened (token, head) rows of one
+//                     KV group: q~ = fp16(R(q) * scale * log2 e) in registers, online softmax over
+//                     64-key tiles staged once in LDS for all query heads of the group; o, lse.
 //  backward: prep  -> q~, k', v', dO' and Delta = rowsum(dO * o), lse2 = lse * log2 e, cos/sin table
-//            dkdv  -> per 128 keys of one KV head: dK, dV accumulated over every query row of the
-//                     group (all G heads), written once; inverse RoPE in the epilogue.
+//            dkdv  -> per pair of mirrored 64-key blocks of one KV head: dK, dV accumulated over
+//                     every query row of the group (all G heads), written once; inverse RoPE in
+//                     the epilogue.
 //            dq    -> per 128 flattened rows: dQ accumulated over the visible key tiles, written
 //                     once; inverse RoPE in the epilogue.  No atomics: bit-reproducible.
 //
@@ -32,17 +34,29 @@ namespace ne {
 // =====================================================================================
 // Operand preparation.
 // =====================================================================================
+// cos/sin of t * theta_i, theta_i = base^(-2i/D), for tokens [t0, t0 + TT) into cs[TT][D/2].
+// theta_i and the phase t * theta_i are formed in double precision and the phase is reduced to
+// [-pi, pi] there (two-term 2 pi), so the single-precision sincos sees a small argument and the
+// table entries are within a few fp32 ulps of the exactly rounded values at any position.
 template <int D>
-__device__ __forceinline__ void rope_cs_fill(float2* cs, int t0, int TT, int T, double base) {
-    // cos/sin of t * base^(-2i/D) in double precision, rounded to fp32.
+__device__ __forceinline__ void rope_cs_fill(float2* cs, double* theta, int t0, int TT, int T, double base) {
+    for (int i = threadIdx.x; i < D / 2; i += blockDim.x)
+        theta[i] = base > 0.0 ? exp2(-2.0 * (double)i / (double)D * log2(base)) : 0.0;
+    __syncthreads();
+    constexpr double kTwoPiHi = 6.283185307179586;        // 2 pi rounded to double
+    constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2 pi - kTwoPiHi
+    constexpr double kInvTwoPi = 0.15915494309189535;
     for (int idx = threadIdx.x; idx < TT * (D / 2); idx += blockDim.x) {
         const int tl = idx / (D / 2), i = idx % (D / 2);
         const int t = t0 + tl;
         float2 v = make_float2(1.f, 0.f);
         if (base > 0.0 && t < T) {
-            const double theta = exp2(-2.0 * (double)i / (double)D * log2(base));
-            const double phi = (double)t * theta;
-            v = make_float2((float)cos(phi), (float)sin(phi));
+            const double phi = (double)t * theta[i];
+            const double n = rint(phi * kInvTwoPi);
+            const double r = fma(-n, kTwoPiLo, fma(-n, kTwoPiHi, phi));
+            float sv, cv;
+            sincosf((float)r, &sv, &cv);
+            v = make_float2(cv, sv);
         }
         cs[idx] = v;
     }
@@ -74,10 +88,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     constexpr int TT = 8;
     constexpr int CPR = D / 8;  // 8-element chunks per row
     __shared__ float2 cs[TT * (D / 2)];
+    __shared__ double theta[D / 2];
     const int t0 = blockIdx.x * TT, b = blockIdx.y;
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
     const bool rope = a.rope_base > 0.0;
-    rope_cs_fill<D>(cs, t0, TT, T, a.rope_base);
+    rope_cs_fill<D>(cs, theta, t0, TT, T, a.rope_base);
     __syncthreads();
     if (b == 0 && rope) {
         for (int idx = threadIdx.x; idx < TT * (D / 2); idx += blockDim.x) {
@@ -147,6 +162,69 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
 }
 
+// Eight consecutive input elements as fp32, with 16-byte loads.
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(p), b = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+}
+template <typename T16>
+__device__ __forceinline__ void load8(const T16* p, float (&x)[8]) {
+    typedef T16 v8 __attribute__((ext_vector_type(8)));
+    const v8 a = *reinterpret_cast<const v8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+}
+
+// Forward preparation for 16-bit operands.  grid (Tp / 64, B * Hkv), 256 threads: 64 tokens of
+// one (batch, KV head) group.  k' = fp16(R(k)) rows as [group][T][D]; v' = fp16(v) transposed to
+// [group][D][Tp] with the key order of vt_key_of_pos and zeros past T; the cos/sin table rows of
+// these tokens (written by the group-0 blocks).
+template <typename TI, int D>
+__global__ __launch_bounds__(256) void prep_fwd_h(PrepArgs a) {
+    constexpr int TB = 64, CPR = D / 8;
+    __shared__ float2 cs[TB * (D / 2)];
+    __shared__ double theta[D / 2];
+    __shared__ _Float16 vts[D][TB + 8];                // v'^T of the 64 tokens (144-byte rows)
+    const int t0 = blockIdx.x * TB, grp = blockIdx.y;
+    const int T = a.T, Hkv = a.Hkv, b = grp / Hkv, hkv = grp % Hkv;
+    const int Tp = (T + TB - 1) / TB * TB;
+    const bool rope = a.rope_base > 0.0;
+    if (rope) {
+        rope_cs_fill<D>(cs, theta, t0, TB, T, a.rope_base);
+        __syncthreads();
+        if (grp == 0)
+            for (int idx = threadIdx.x; idx < TB * (D / 2); idx += 256) {
+                const int t = t0 + idx / (D / 2);
+                if (t < T) a.table[(size_t)t * (D / 2) + idx % (D / 2)] = cs[idx];
+            }
+    }
+    for (int idx = threadIdx.x; idx < TB * CPR; idx += 256) {
+        const int tl = idx / CPR, chunk = idx % CPR, t = t0 + tl;
+        float x[8];
+        if (t < T) {
+            const size_t in_off = (((size_t)b * T + t) * Hkv + hkv) * D + chunk * 8;
+            _Float16* kdst = (_Float16*)a.kh + ((size_t)grp * T + t) * D + chunk * 8;
+            if (rope) convert8<TI, _Float16, D, true>((const TI*)a.k + in_off, kdst, cs + tl * (D / 2), chunk, 1.f);
+            else convert8<TI, _Float16, D, false>((const TI*)a.k + in_off, kdst, cs, chunk, 1.f);
+            load8((const TI*)a.v + in_off, x);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vts[chunk * 8 + e][tl] = (_Float16)x[e];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < D * (TB / 8); idx += 256) {
+        const int d = idx / (TB / 8), pc = idx % (TB / 8);
+        half8 out;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) out[j] = vts[d][vt_key_of_pos(8 * pc + j)];
+        *reinterpret_cast<half8*>((_Float16*)a.vh + ((size_t)grp * D + d) * Tp + t0 + 8 * pc) = out;
+    }
+}
+
 // =====================================================================================
 // Block -> work mapping.  Workgroups are dispatched round-robin over the 8 XCDs (each with its
 // own L2), so dispatch index i runs on XCD i % 8.  When the (batch, KV head) groups divide
@@ -180,20 +258,6 @@ __device__ __forceinline__ Work map_block(int nblk, int ngrp, bool longest_last)
 // is refreshed only when a row's new maximum exceeds it by more than 2^8 (the probabilities stay
 // below 256 in between), so the rescale of O is rare.
 // =====================================================================================
-// Eight consecutive input elements as fp32, with 16-byte loads.
-__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
-    const floatx4 a = *reinterpret_cast<const floatx4*>(p), b = *reinterpret_cast<const floatx4*>(p + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
-}
-template <typename T16>
-__device__ __forceinline__ void load8(const T16* p, float (&x)[8]) {
-    typedef T16 v8 __attribute__((ext_vector_type(8)));
-    const v8 a = *reinterpret_cast<const v8*>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
-}
-
 // Query fragments (B operand of S^T = K Q^T) of one row, rotated, scaled and converted.
 template <typename TI, typename OP, int D>
 __device__ __forceinline__ void load_q_frags(typename Mma<OP>::frag (&qf)[D / Mma<OP>::K], const TI* row,
@@ -379,6 +443,239 @@ void fwd_kernel(FwdArgs a) {
         const int t = Ri / G;
         return (TOUT*)a.o + (((size_t)b * T + t) * a.Hq + hkv * G + (Ri - t * G)) * D;
     });
+}
+
+// =====================================================================================
+// Forward, 16-bit operands.  grid (ceil(T G / 256) * B * Hkv), 512 threads = 8 waves x 32
+// flattened rows (two waves per SIMD share every 64-key K and V tile), software-pipelined
+// inside each wave.  Iteration j of a wave:
+//   phase 1  O^T += V^T P^T for tile j - 1 on the matrix cores while the ALU exponentiates the
+//            scores of tile j (independent, so the two interleave in a fixed issue order);
+//   phase 2  the scores of tile j + 1;
+//   then its mask (diagonal tiles only), row max and the rare refresh of the reference max m.
+// A refresh rescales the row sum at once and O after the next phase 1, which adds the last
+// probabilities that still use the old m.  The row sums are packed dot products of the fp16
+// probabilities that the product consumes.  V arrives transposed (vt_frag), so both operand
+// streams are plain 16-byte LDS reads, four products ahead of their use.  K and V^T tiles go
+// through 3-stage LDS rings filled two iterations ahead by direct loads.
+// =====================================================================================
+template <int V> struct IC { static constexpr int value = V; };
+
+template <typename TI, int D, typename TOUT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_kernel_h(FwdArgs a) {
+    using OP = _Float16;
+    using M = Mma<OP>;
+    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+    constexpr int BM = 256, BN = 64, NW = 8, KS = D / 16, NDB = D / 32, TILE = BN * D;
+    constexpr int N1 = 4 * NDB, N2 = 2 * KS;             // products in phase 1 and phase 2
+    constexpr float TAU = 8.f;
+    constexpr int NST = 3;
+    constexpr int RING = 2 * NST * TILE * (int)sizeof(OP), OUTB = 4 * 32 * D * (int)sizeof(TOUT);
+    __shared__ __attribute__((aligned(1024))) char lds_raw[RING > OUTB ? RING : OUTB];
+    OP* const lds = reinterpret_cast<OP*>(lds_raw);    // K stages 0..2, then V^T stages 0..2
+
+    const int T = a.T, G = a.G, TG = T * G, Tp = (T + 63) / 64 * 64;
+    const Work wk = map_block(a.nrb, a.B * a.Hkv, true);
+    const int rb = wk.blk;
+    const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int R0 = rb * BM;
+    const int Rw = R0 + 32 * w;
+    const int R = Rw + c;
+    const bool rvalid = R < TG;
+    const int t_lane = R / G;
+    const int wave_tmin = Rw / G;
+    const int wave_tmax = min(Rw + 31, TG - 1) / G;
+    const int last = Rw < TG ? wave_tmax / BN : -1;           // this wave's last key tile
+    const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;  // the block's
+
+    const size_t grp = (size_t)wk.grp;
+    const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
+    const OP* vtg = (const OP*)a.vh + grp * (size_t)D * Tp;
+    const bool rope = a.rope_base > 0.0;
+    auto kst = [&](int j) { return lds + (j % NST) * TILE; };
+    auto vst = [&](int j) { return lds + (NST + j % NST) * TILE; };
+    auto fill_k = [&](int j) { lds_fill<OP, D, BN, NW>(kst(j), kg, j * BN, T); };
+    auto fill_v = [&](int j) { lds_fill_vt<D, BN, NW>(vst(j), vtg, j * BN, Tp); };
+    const int nkw = lds_fill_count<OP, D, BN, NW>(w), nvw = lds_fill_vt_count<D, BN, NW>(w);
+    auto kept = [&](int it) {  // loads this wave issued in iteration it - 1 (K of it + 2, V of it)
+        return (it + 2 < ntiles ? nkw : 0) + (it < ntiles ? nvw : 0);
+    };
+
+    half8 qf[KS];
+    {
+        const int t = min(t_lane, T - 1), hh = R - t_lane * G;
+        const TI* qrow = (const TI*)a.q + (((size_t)b * T + t) * a.Hq + hkv * G + hh) * D;
+        load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, a.qscale, h, rvalid);
+    }
+    wait_all();
+    fill_k(0);
+    if (ntiles > 1) fill_k(1);
+    lds_fill_wait_keep(ntiles > 1 ? nkw : 0);  // K of tile 0
+
+    floatx16 s[2];        // scores of one tile (32 keys per accumulator)
+    half8 p[2][4];        // fp16 probabilities of two consecutive tiles (index: tile parity)
+    floatx16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
+    float m_run = 0.f, l_run = 0.f, apend = 1.f;
+    bool pend = false;
+
+    auto mask_max = [&](int j) {  // mask of tile j (if it crosses a diagonal), then the row max
+        const int n0 = j * BN;
+        if (n0 + BN - 1 > wave_tmin) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (n0 + 32 * mb + acc_row(r, h) > t_lane) s[mb][r] = -INFINITY;
+        }
+        float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+        return max_halves(mx);
+    };
+    // phase 2: scores of tile j, products alternating between the two 32-key accumulators
+    auto phase2 = [&](int j) {
+        const OP* Ks = kst(j);
+        constexpr int AH = N2 < 4 ? N2 : 4;
+        half8 fr[N2];
+#pragma unroll
+        for (int i = 0; i < AH; ++i) fr[i] = row_frag_sw<OP, D>(Ks, 32 * (i & 1) + c, i >> 1, h);
+        s[0] = floatx16{};
+        s[1] = floatx16{};
+#pragma unroll
+        for (int i = 0; i < N2; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            s[i & 1] = M::mma(fr[i], qf[i >> 1], s[i & 1]);
+            if (i + AH < N2) fr[i + AH] = row_frag_sw<OP, D>(Ks, 32 * ((i + AH) & 1) + c, (i + AH) >> 1, h);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // phase 1 of iteration j: O^T += V^T P^T for tile j - 1 (when PV) and the probabilities of
+    // tile j (parity C), whose sum is returned; the 32 exponentials are spread over the products
+    auto phase1 = [&](int j, auto PAR, auto PV) -> float {
+        constexpr int C = decltype(PAR)::value, NP = C ^ 1;
+        constexpr bool DO_PV = decltype(PV)::value;
+        constexpr int NS = DO_PV ? N1 : 1;              // issue slots
+        constexpr int AH = N1 < 4 ? N1 : 4;
+        const OP* Vs = vst(j - 1);
+        auto rd = [&](int i) { return vt_frag<BN>(Vs, 32 * (i % NDB) + c, i / NDB, h); };
+        half8 fr[N1];
+        half2v hp[16];
+        float ps = 0.f;
+        if constexpr (DO_PV) {
+#pragma unroll
+            for (int i = 0; i < AH; ++i) fr[i] = rd(i);
+        }
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (DO_PV) {
+                oacc[i % NDB] = M::mma(fr[i], p[NP][i / NDB], oacc[i % NDB]);
+                if (i + AH < N1) fr[i + AH] = rd(i + AH);
+            }
+#pragma unroll
+            for (int e = 32 * i / NS; e < 32 * (i + 1) / NS; ++e) {
+                const float x = __builtin_amdgcn_exp2f(s[e >> 4][e & 15] - m_run);
+                if (e & 1) {
+                    hp[e >> 1][1] = (_Float16)x;
+                    ps = __builtin_amdgcn_fdot2(hp[e >> 1], half2v{1, 1}, ps, false);
+                    asm volatile("" ::"v"(hp[e >> 1]), "v"(ps));  // keep this slot's share here
+                } else {
+                    hp[e >> 1][0] = (_Float16)x;
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            p[C][kk] = half8{hp[4 * kk][0], hp[4 * kk][1], hp[4 * kk + 1][0], hp[4 * kk + 1][1],
+                             hp[4 * kk + 2][0], hp[4 * kk + 2][1], hp[4 * kk + 3][0], hp[4 * kk + 3][1]};
+        return ps;
+    };
+    // after the scores of tile j are in s: mask, max and the (rare) refresh of m
+    auto refresh = [&](int j) {
+        const float mx = mask_max(j);
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {  // raise m to this tile's max
+            const float m_new = fmaxf(m_run, mx);
+            apend = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= apend;
+            pend = true;
+        }
+    };
+    auto sync_fill = [&](int it) {
+        // K of tile it + 1 and V of tile it - 1 have landed (K of it + 2 and V of it may still be
+        // in flight); every wave is done with the stages the new loads overwrite (K of tile it,
+        // V of tile it - 2)
+        lds_fill_wait_keep(kept(it));
+        if (it + 3 < ntiles) fill_k(it + 3);
+        if (it + 1 < ntiles) fill_v(it + 1);
+    };
+    auto step = [&](int it, auto PAR) {
+        sync_fill(it);
+        if (it <= last + 1) {
+            const float ps = phase1(it, PAR, IC<1>{});
+            l_run += it <= last ? ps : 0.f;  // iteration last + 1 only finishes the product
+            if (it + 1 <= last) phase2(it + 1);
+            if (pend) {  // O now holds every tile whose probabilities used the old m
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= apend;
+                pend = false;
+            }
+            if (it + 1 <= last) refresh(it + 1);
+        }
+    };
+
+    // iteration -1: the scores of tile 0, which every row sees, fix the first m exactly
+    if (ntiles > 2) fill_k(2);
+    fill_v(0);
+    if (last >= 0) {
+        phase2(0);
+        m_run = mask_max(0);
+    }
+    // iteration 0: no product yet
+    sync_fill(0);
+    if (last >= 0) {
+        l_run = phase1(0, IC<0>{}, IC<0>{});
+        if (last >= 1) {
+            phase2(1);
+            refresh(1);
+        }
+    }
+    // iterations 1 .. ntiles, run by every wave (the barriers are block-wide)
+    for (int it = 1; it <= ntiles; it += 2) {
+        step(it, IC<1>{});
+        if (it + 1 > ntiles) break;
+        step(it + 1, IC<0>{});
+    }
+
+    const float l_tot = sum_halves(l_run);
+    const float inv = 1.f / l_tot;
+    if (rvalid && h == 0) {
+        const int t = t_lane, hq = hkv * G + (R - t * G);
+        a.lse[((size_t)b * a.Hq + hq) * T + t] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+    // o rows through LDS, waves 0-3 then 4-7: the last iteration waited for every load; the
+    // first barrier makes sure no wave still reads a stage
+    auto out = [&]() {
+        store_rows<TOUT, D>(oacc, inv, lds_raw + (w & 3) * 32 * D * (int)sizeof(TOUT), [&](int i) {
+            const int Ri = Rw + i;
+            if (Ri >= TG) return (TOUT*)nullptr;
+            const int t = Ri / G;
+            return (TOUT*)a.o + (((size_t)b * T + t) * a.Hq + hkv * G + (Ri - t * G)) * D;
+        });
+    };
+    __syncthreads();
+    if (w < 4) out();
+    __syncthreads();
+    if (w >= 4) out();
 }
 
 // =====================================================================================
@@ -780,11 +1077,20 @@ template <typename TI, typename TO, typename OP, int D>
 static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, hipStream_t s, hipEvent_t const* ev) {
     const Marks m{ev, s};
     NE_TRY(m.before(0));
-    hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, false>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);
+    if constexpr (sizeof(OP) == 2)
+        hipLaunchKernelGGL((prep_fwd_h<TI, D>), dim3((pa.T + 63) / 64, pa.B * pa.Hkv), dim3(256), 0, s, pa);
+    else
+        hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, false>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(0));
     NE_TRY(m.before(1));
-    hipLaunchKernelGGL((fwd_kernel<TI, OP, D, TO>), dim3(fa.nrb * fa.Hkv * fa.B), dim3(256), 0, s, fa);
+    if constexpr (sizeof(OP) == 2) {
+        FwdArgs f2 = fa;
+        f2.nrb = (int)(((int64_t)fa.T * fa.G + 255) / 256);
+        hipLaunchKernelGGL((fwd_kernel_h<TI, D, TO>), dim3(f2.nrb * fa.Hkv * fa.B), dim3(512), 0, s, f2);
+    }
+    else
+        hipLaunchKernelGGL((fwd_kernel<TI, OP, D, TO>), dim3(fa.nrb * fa.Hkv * fa.B), dim3(256), 0, s, fa);
     NE_TRY(hipGetLastError());
     return m.after(1);
 }

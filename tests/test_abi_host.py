@@ -52,6 +52,11 @@ def test_workspace_sizes(L):
     bwd = L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
     assert bwd == 2 * up(2 * nq) + 2 * up(2 * nk) + 2 * up(4 * B * T * Hq) + table
     assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_F32) == 2 * up(4 * nk) + table
+    # ragged T: the forward's transposed V' copy pads every row of keys to a multiple of 64
+    Tr = 100
+    nkr, Tp = B * Tr * Hkv * D, 128
+    assert L.ne_rope_attn_fwd_workspace_bytes(B, Tr, Hq, Hkv, D, binding.NE_BF16) == \
+        up(2 * nkr) + up(2 * B * Hkv * D * Tp) + up(Tr * (D // 2) * 8)
     assert L.ne_rope_attn_fwd_workspace_bytes(B, T, 12, 5, D, binding.NE_BF16) == 0
     assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, 96, binding.NE_BF16) == 0
 

@@ -923,6 +923,210 @@ void dkdv_kernel(BwdArgs a) {
 }
 
 // =====================================================================================
+// Backward dK/dV, 16-bit operands.  Same work split as dkdv_kernel (8 waves: row half, 32-key
+// sub-block, role; mirrored 64-key block pairs), but the two roles work one row tile apart, so
+// a step needs one barrier: at step s the role-0 wave computes S and P of tile s, hands P to its
+// role-1 partner through an LDS buffer of step parity s & 1 and adds dO^T P to dV^T, while the
+// role-1 wave computes dP of tile s - 1, dS with the P handed over one step earlier and adds
+// Q^T dS to dK^T.  The shifts by lse2 and by Delta ride on one extra k-step of the S and dP
+// products: the A operand carries three fp16 terms of -lse2 (or -Delta) of the lane's row
+// (fold_frag) against B = (256, 1, 1), so the accumulators come out as S - lse2 and
+// dP - Delta with fp32 accuracy and no per-element subtraction.  Row tiles go through a 4-stage
+// ring filled two steps ahead.
+// =====================================================================================
+// Three fp16 terms with 256 a + b + c = x to about 2^-33 |x| (|x| < 2^24): lane half 0 of the
+// A operand of an extra k-step (k = 0, 1, 2); lane half 1 holds zeros.
+__device__ __forceinline__ half8 fold_frag(float x, int h) {
+    const _Float16 a = (_Float16)(x * (1.f / 256.f));
+    const float r1 = x - 256.f * (float)a;
+    const _Float16 b = (_Float16)r1;
+    const _Float16 c = (_Float16)(r1 - (float)b);
+    const _Float16 z = (_Float16)0.f;
+    return h == 0 ? half8{a, b, c, z, z, z, z, z} : half8{z, z, z, z, z, z, z, z};
+}
+// The matching B operand (k = 0, 1, 2 weighted 256, 1, 1 for every column).
+__device__ __forceinline__ half8 fold_weights(int h) {
+    const _Float16 z = (_Float16)0.f;
+    return h == 0 ? half8{(_Float16)256.f, (_Float16)1.f, (_Float16)1.f, z, z, z, z, z} : half8{z, z, z, z, z, z, z, z};
+}
+
+template <int D, typename TOUT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void dkdv_kernel_h(BwdArgs a) {
+    using OP = _Float16;
+    using M = Mma<OP>;
+    constexpr int KSUB = 2, BN = 32 * KSUB, BMR = 64, NW = 8, NST = 4;
+    constexpr int KS = D / 16, NDB = D / 32, TILE = BMR * D;
+    static_assert(NST * 2 * TILE * sizeof(OP) >= KSUB * 2 * NDB * 16 * 64 * sizeof(float),
+                  "the ring holds the partials of the final reduction");
+    __shared__ __attribute__((aligned(1024))) OP lds[NST * 2 * TILE];     // [stage][Q~ | dO'] row tiles
+    __shared__ __attribute__((aligned(16))) half8 pbuf[2][KSUB][2][2][64];  // [s & 1][kq][rh][cc][lane]
+    __shared__ __attribute__((aligned(16))) float rowv[NST][2][BMR];       // [stage][lse2 | delta][row]
+
+    const int T = a.T, G = a.G, TG = T * G;
+    const int nkb = (T + BN - 1) / BN;
+    const int npair = (nkb + 1) / 2;
+    const Work wk = map_block(npair, a.B * a.Hkv, false);
+    const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    // waves w and w + 4 (same row half and key sub-block, the two roles) share a SIMD
+    const int rh = w & 1, kq = (w >> 1) & 1, role = w >> 2;
+    const int per_fill = 2 * lds_fill_count<OP, D, BMR, NW>(w) + (w < 2 ? 1 : 0);  // loads per fill
+
+    const size_t grp = (size_t)wk.grp;
+    const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
+    const OP* og = (const OP*)a.dOh + grp * (size_t)TG * D;
+    const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
+    const OP* vg = (const OP*)a.vh + grp * (size_t)T * D;
+    const float* lse2g = a.lse2 + grp * (size_t)TG;
+    const float* delg = a.delta + grp * (size_t)TG;
+    const bool rope = a.rope_base > 0.0;
+    const half8 fw = fold_weights(h);
+
+    // Q and dO rows, lse2 (wave 0) and Delta (wave 1) of rows [R0, R0 + 64), all by direct loads;
+    // rows past TG are copies of row TG - 1 and are masked out (P = 0) below.
+    auto fill = [&](int stage, int R0) {
+        OP* dst = lds + stage * 2 * TILE;
+        lds_fill<OP, D, BMR, NW>(dst, qg, R0, TG);
+        lds_fill<OP, D, BMR, NW>(dst + TILE, og, R0, TG);
+        if (w < 2) {
+            const float* src = (w == 0 ? lse2g : delg) + min(R0 + l, TG - 1);
+            dma4(src, lds_addr(&rowv[stage][w][0]));
+        }
+    };
+
+    for (int pass = 0; pass < 2; ++pass) {
+        const int kb = pass == 0 ? wk.blk : nkb - 1 - wk.blk;
+        if (pass == 1 && kb == wk.blk) break;  // odd nkb: the middle block has no mirror
+        const int n0 = kb * BN + 32 * kq;                      // first key of this wave
+        const int key = n0 + c;
+        const bool kvalid = key < T;
+        const int keyG = key * G;              // row R sees this key iff R >= key * G
+        const int rstart = (kb * BN * G) / BMR * BMR;
+        const int ntiles = (TG - rstart + BMR - 1) / BMR;
+        // does this wave's row half of tile j see any of its keys, and does it need the mask
+        auto active = [&](int j) {
+            const int Rh = rstart + j * BMR + 32 * rh;
+            return min(Rh + 31, TG - 1) >= n0 * G && Rh < TG;
+        };
+        auto needs_mask = [&](int j) {
+            const int Rh = rstart + j * BMR + 32 * rh;
+            return Rh < (n0 + 31) * G || Rh + 32 > TG;
+        };
+
+        // role 0 keeps K^T fragments, role 1 keeps V^T fragments (B operands, one key per lane)
+        half8 kvf[KS];
+        const OP* kvrow = (role == 0 ? kg : vg) + (size_t)key * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kvf[ks] = kvalid ? M::row_frag(kvrow, ks, h, D) : half8{};
+        floatx16 acc[NDB];  // role 0: dV^T, role 1: dK^T (d rows, this lane's key column)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = floatx16{};
+        wait_all();
+
+        fill(0, rstart);
+        if (ntiles > 1) fill(1, rstart + BMR);
+        for (int s = 0; s <= ntiles; ++s) {
+            // tile s has landed (tile s + 1 may still be in flight); the P of tile s - 1 is in
+            // pbuf[(s - 1) & 1]; every wave is done with tile s - 2 and with pbuf[s & 1]
+            lds_fill_wait_keep(s + 1 < ntiles ? per_fill : 0);
+            if (s + 2 < ntiles) fill((s + 2) % NST, rstart + (s + 2) * BMR);
+            if (role == 0) {
+                if (s < ntiles && active(s)) {
+                    const int st = s % NST;
+                    const OP* Qs = lds + st * 2 * TILE;
+                    const OP* Os = Qs + TILE;
+                    const int Rh = rstart + s * BMR + 32 * rh;
+                    floatx16 x = floatx16{};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) x = M::mma(row_frag_sw<OP, D>(Qs, 32 * rh + c, ks, h), kvf[ks], x);
+                    x = M::mma(fold_frag(-rowv[st][0][32 * rh + c], h), fw, x);  // S - lse2
+                    if (needs_mask(s)) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int row = Rh + acc_row(r, h);
+                            if (row < keyG || row >= TG) x[r] = -INFINITY;
+                        }
+                    }
+                    half8 pf[2];
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) pf[cc][j] = (_Float16)__builtin_amdgcn_exp2f(x[8 * cc + j]);
+                        pbuf[s & 1][kq][rh][cc][l] = pf[cc];
+                    }
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+                            acc[db] = M::mma(tr_frag_f16_sw<D>(Os, 2 * rh + cc, 32 * db), pf[cc], acc[db]);
+                }
+            } else {
+                if (s >= 1 && active(s - 1)) {
+                    const int st = (s - 1) % NST;
+                    const OP* Qs = lds + st * 2 * TILE;
+                    const OP* Os = Qs + TILE;
+                    floatx16 y = floatx16{};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) y = M::mma(row_frag_sw<OP, D>(Os, 32 * rh + c, ks, h), kvf[ks], y);
+                    y = M::mma(fold_frag(-rowv[st][1][32 * rh + c], h), fw, y);  // dP - Delta
+                    half8 dsf[2];
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) {
+                        const half8 pv = pbuf[(s - 1) & 1][kq][rh][cc][l];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) dsf[cc][j] = (_Float16)((float)pv[j] * y[8 * cc + j]);
+                    }
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+                            acc[db] = M::mma(tr_frag_f16_sw<D>(Qs, 2 * rh + cc, 32 * db), dsf[cc], acc[db]);
+                }
+            }
+        }
+
+        // add the two row halves in a fixed order (half 0 + half 1) through the staging area
+        __syncthreads();
+        float* part = reinterpret_cast<float*>(lds) + (kq * 2 + role) * (NDB * 16 * 64);
+        if (rh == 1) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *reinterpret_cast<floatx4*>(&part[((db * 4 + q4) * 64 + l) * 4]) =
+                        floatx4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
+        }
+        __syncthreads();
+        if (rh == 0 && kvalid) {
+            TOUT* orow = (TOUT*)(role == 0 ? a.dv : a.dk) + (((size_t)b * T + key) * a.Hkv + hkv) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const floatx4 o1 = *reinterpret_cast<const floatx4*>(&part[((db * 4 + q4) * 64 + l) * 4]);
+                    const int d = 32 * db + 8 * q4 + 4 * h;
+                    float x0 = acc[db][4 * q4] + o1[0], x1 = acc[db][4 * q4 + 1] + o1[1];
+                    float x2 = acc[db][4 * q4 + 2] + o1[2], x3 = acc[db][4 * q4 + 3] + o1[3];
+                    if (role == 1) {
+                        // dk' = ln2 * sum dS q~ (q~ carries scale * log2 e), then dk = R^T dk'
+                        x0 *= kLn2; x1 *= kLn2; x2 *= kLn2; x3 *= kLn2;
+                        if (rope) {
+                            const float2 r0 = a.table[(size_t)key * (D / 2) + d / 2];
+                            const float2 r1 = a.table[(size_t)key * (D / 2) + d / 2 + 1];
+                            const float y0 = x0 * r0.x + x1 * r0.y, y1 = -x0 * r0.y + x1 * r0.x;
+                            const float y2 = x2 * r1.x + x3 * r1.y, y3 = -x2 * r1.y + x3 * r1.x;
+                            x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+                        }
+                    }
+                    store4(orow + d, x0, x1, x2, x3);
+                }
+        }
+        __syncthreads();  // the staging area is refilled by the next key block
+    }
+}
+
+// =====================================================================================
 // Backward, dQ (deterministic: a separate pass that recomputes S and dP, no atomics).
 // grid (nrb * B * Hkv), 256 threads = 4 waves x 32 flattened rows, 64-key tiles.
 // S^T = K Q^T and dP^T = V dO^T put one query row per lane; dQ^T += K^T dS^T reads K^T from the
@@ -1103,7 +1307,10 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(0));
     NE_TRY(m.before(1));
-    hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3(((ba.T + 63) / 64 + 1) / 2 * ba.Hkv * ba.B), dim3(512), 0, s, ba);
+    if constexpr (sizeof(OP) == 2)
+        hipLaunchKernelGGL((dkdv_kernel_h<D, TO>), dim3(((ba.T + 63) / 64 + 1) / 2 * ba.Hkv * ba.B), dim3(512), 0, s, ba);
+    else
+        hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3(((ba.T + 63) / 64 + 1) / 2 * ba.Hkv * ba.B), dim3(512), 0, s, ba);
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(1));
     NE_TRY(m.before(2));

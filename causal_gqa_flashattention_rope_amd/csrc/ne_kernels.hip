@@ -995,6 +995,46 @@ void dkdv_kernel_h(BwdArgs a) {
         }
     };
 
+    half8 kvf[KS];  // role 0: K^T fragments, role 1: V^T fragments (B operands, one key per lane)
+    // x = rows(this wave's half of `rows`) . kvf over D, the row fragments read four products ahead
+    auto chain = [&](const OP* rows) {
+        constexpr int AH = KS < 4 ? KS : 4;
+        half8 fr[KS];
+#pragma unroll
+        for (int i = 0; i < AH; ++i) fr[i] = row_frag_sw<OP, D>(rows, 32 * rh + c, i, h);
+        floatx16 x = floatx16{};
+#pragma unroll
+        for (int i = 0; i < KS; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            x = M::mma(fr[i], kvf[i], x);
+            if (i + AH < KS) fr[i + AH] = row_frag_sw<OP, D>(rows, 32 * rh + c, i + AH, h);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        return x;
+    };
+    // second product of a step: acc[db] += trt^T (this wave's rows, transposed reads) . pf; the
+    // fragments of the first k-step were read before the exponentials (tf0), those of the second
+    // are read while the first k-step's products run
+    auto tr_frags0 = [&](const OP* trt, half8 (&tf0)[NDB]) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) tf0[db] = tr_frag_f16_sw<D>((const _Float16*)trt, 2 * rh, 32 * db);
+    };
+    auto product2 = [&](const OP* trt, const half8 (&tf0)[NDB], const half8 (&pf)[2], floatx16 (&acc)[NDB]) {
+        half8 tf1[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            __builtin_amdgcn_sched_barrier(0);
+            acc[db] = M::mma(tf0[db], pf[0], acc[db]);
+            tf1[db] = tr_frag_f16_sw<D>((const _Float16*)trt, 2 * rh + 1, 32 * db);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            __builtin_amdgcn_sched_barrier(0);
+            acc[db] = M::mma(tf1[db], pf[1], acc[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
     for (int pass = 0; pass < 2; ++pass) {
         const int kb = pass == 0 ? wk.blk : nkb - 1 - wk.blk;
         if (pass == 1 && kb == wk.blk) break;  // odd nkb: the middle block has no mirror
@@ -1014,8 +1054,6 @@ void dkdv_kernel_h(BwdArgs a) {
             return Rh < (n0 + 31) * G || Rh + 32 > TG;
         };
 
-        // role 0 keeps K^T fragments, role 1 keeps V^T fragments (B operands, one key per lane)
-        half8 kvf[KS];
         const OP* kvrow = (role == 0 ? kg : vg) + (size_t)key * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kvf[ks] = kvalid ? M::row_frag(kvrow, ks, h, D) : half8{};
@@ -1037,10 +1075,10 @@ void dkdv_kernel_h(BwdArgs a) {
                     const OP* Qs = lds + st * 2 * TILE;
                     const OP* Os = Qs + TILE;
                     const int Rh = rstart + s * BMR + 32 * rh;
-                    floatx16 x = floatx16{};
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) x = M::mma(row_frag_sw<OP, D>(Qs, 32 * rh + c, ks, h), kvf[ks], x);
+                    floatx16 x = chain(Qs);
                     x = M::mma(fold_frag(-rowv[st][0][32 * rh + c], h), fw, x);  // S - lse2
+                    half8 tf0[NDB];
+                    tr_frags0(Os, tf0);  // in flight during the exponentials
                     if (needs_mask(s)) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
@@ -1055,21 +1093,17 @@ void dkdv_kernel_h(BwdArgs a) {
                         for (int j = 0; j < 8; ++j) pf[cc][j] = (_Float16)__builtin_amdgcn_exp2f(x[8 * cc + j]);
                         pbuf[s & 1][kq][rh][cc][l] = pf[cc];
                     }
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db)
-                            acc[db] = M::mma(tr_frag_f16_sw<D>(Os, 2 * rh + cc, 32 * db), pf[cc], acc[db]);
+                    product2(Os, tf0, pf, acc);
                 }
             } else {
                 if (s >= 1 && active(s - 1)) {
                     const int st = (s - 1) % NST;
                     const OP* Qs = lds + st * 2 * TILE;
                     const OP* Os = Qs + TILE;
-                    floatx16 y = floatx16{};
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) y = M::mma(row_frag_sw<OP, D>(Os, 32 * rh + c, ks, h), kvf[ks], y);
+                    floatx16 y = chain(Os);
                     y = M::mma(fold_frag(-rowv[st][1][32 * rh + c], h), fw, y);  // dP - Delta
+                    half8 tf0[NDB];
+                    tr_frags0(Qs, tf0);  // in flight during dS
                     half8 dsf[2];
 #pragma unroll
                     for (int cc = 0; cc < 2; ++cc) {
@@ -1077,11 +1111,7 @@ void dkdv_kernel_h(BwdArgs a) {
 #pragma unroll
                         for (int j = 0; j < 8; ++j) dsf[cc][j] = (_Float16)((float)pv[j] * y[8 * cc + j]);
                     }
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db)
-                            acc[db] = M::mma(tr_frag_f16_sw<D>(Qs, 2 * rh + cc, 32 * db), dsf[cc], acc[db]);
+                    product2(Qs, tf0, dsf, acc);
                 }
             }
         }
@@ -1261,6 +1291,159 @@ void dq_kernel(BwdArgs a) {
 }
 
 // =====================================================================================
+// Backward dQ, 16-bit operands.  Same work split as dq_kernel.  The shifts by lse2 and Delta
+// ride on an extra k-step of the S^T and dP^T products (fold_frag: here the B operand carries
+// the lane's row terms, constant for the whole kernel, against A = (256, 1, 1)), so P^T and
+// dS^T cost one exponential and one multiply per element.  Per key tile the four accumulator
+// chains (S^T and dP^T, two 32-key halves each) advance in turn, and every product's LDS operand
+// is read four products ahead.
+// =====================================================================================
+template <int D, typename TOUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void dq_kernel_h(BwdArgs a) {
+    using OP = _Float16;
+    using M = Mma<OP>;
+    constexpr int BM = 128, BN = 64, NW = 4, KS = D / 16, NDB = D / 32, TILE = BN * D;
+    __shared__ __attribute__((aligned(1024))) OP lds[2 * 2 * TILE];  // [stage][K | V]
+
+    const int T = a.T, G = a.G, TG = T * G;
+    const Work wk = map_block(a.nrb, a.B * a.Hkv, true);
+    const int rb = wk.blk;
+    const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int R0 = rb * BM;
+    const int Rw = R0 + 32 * w;
+    const int R = Rw + c;
+    const bool rvalid = R < TG;
+    const int t_lane = R / G;
+    const int wave_tmin = Rw / G;
+    const int wave_tmax = min(Rw + 31, TG - 1) / G;
+    const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;
+
+    const size_t grp = (size_t)wk.grp;
+    const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
+    const OP* og = (const OP*)a.dOh + grp * (size_t)TG * D;
+    const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
+    const OP* vg = (const OP*)a.vh + grp * (size_t)T * D;
+
+    // this lane's row: q~ and dO' fragments (B operands), and the folded -lse2 / -Delta; rows
+    // past TG use zeros (their dS is 0 and they are not stored)
+    half8 qf[KS], of[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = rvalid ? M::row_frag(qg + (size_t)R * D, ks, h, D) : half8{};
+        of[ks] = rvalid ? M::row_frag(og + (size_t)R * D, ks, h, D) : half8{};
+    }
+    const half8 fl = fold_frag(rvalid ? -a.lse2[grp * (size_t)TG + R] : 0.f, h);
+    const half8 fd = fold_frag(rvalid ? -a.delta[grp * (size_t)TG + R] : 0.f, h);
+    const half8 fw = fold_weights(h);
+    wait_all();
+    lds_fill<OP, D, BN, NW>(lds, kg, 0, T);
+    lds_fill<OP, D, BN, NW>(lds + TILE, vg, 0, T);
+
+    floatx16 dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = floatx16{};
+
+    for (int it = 0; it < ntiles; ++it) {
+        const OP* Ks = lds + (it & 1) * 2 * TILE;
+        const OP* Vs = Ks + TILE;
+        lds_fill_wait();
+        if (it + 1 < ntiles) {
+            OP* nxt = lds + ((it + 1) & 1) * 2 * TILE;
+            lds_fill<OP, D, BN, NW>(nxt, kg, (it + 1) * BN, T);
+            lds_fill<OP, D, BN, NW>(nxt + TILE, vg, (it + 1) * BN, T);
+        }
+        const int n0 = it * BN;
+        if (n0 > wave_tmax) continue;
+
+        const bool diag = n0 + BN - 1 > wave_tmin;  // the tile crosses some row's diagonal
+        // Per 32-key half mb: two chains, S^T - lse2 (even slots) and dP^T - Delta (odd slots),
+        // operands read four products ahead, then the ALU work of the half (P, dS and their fp16
+        // packing); that of half 1 runs between the first dQ products.  dQ^T += K^T dS^T reads
+        // its K^T fragments four products ahead.
+        constexpr int NC = 2 * KS, NQ = 4 * NDB;
+        auto rd = [&](int mb, int i) {
+            return row_frag_sw<OP, D>((i & 1) ? Vs : Ks, 32 * mb + c, i >> 1, h);
+        };
+        auto rk = [&](int i) { return tr_frag_f16_sw<D>((const _Float16*)Ks, i / NDB, 32 * (i % NDB)); };
+        half8 dsf[4];
+        // element e (0..15) of half mb: dS^T = 2^(S^T - lse2) (dP^T - Delta) into fp16
+        auto elem = [&](const floatx16 (&x)[2], int mb, int e) {
+            dsf[2 * mb + (e >> 3)][e & 7] = (_Float16)(__builtin_amdgcn_exp2f(x[0][e]) * x[1][e]);
+            if ((e & 7) == 7) asm volatile("" ::"v"(dsf[2 * mb + (e >> 3)]));  // keep it in its slot
+        };
+        auto mask = [&](floatx16 (&x)[2], int mb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (n0 + 32 * mb + acc_row(r, h) > t_lane) x[0][r] = -INFINITY;
+        };
+        // the chains of half mb into x; with WITH_PREV, half 0's ALU work (from prev) in between
+        auto chains = [&](int mb, floatx16 (&x)[2], floatx16 (&prev)[2], auto WITH_PREV) {
+            half8 fr[NC];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fr[i] = rd(mb, i);
+            x[0] = M::mma(fw, fl, floatx16{});
+            x[1] = M::mma(fw, fd, floatx16{});
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                __builtin_amdgcn_sched_barrier(0);
+                x[i & 1] = M::mma(fr[i], (i & 1) ? of[i >> 1] : qf[i >> 1], x[i & 1]);
+                if (i + 4 < NC) fr[i + 4] = rd(mb, i + 4);
+                if constexpr (decltype(WITH_PREV)::value) {
+#pragma unroll
+                    for (int e = 16 * i / NC; e < 16 * (i + 1) / NC; ++e) elem(prev, 0, e);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        floatx16 x0[2], x1[2];
+        chains(0, x0, x1, IC<0>{});
+        if (diag) mask(x0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) elem(x0, 0, e);
+        chains(1, x1, x0, IC<0>{});
+        if (diag) mask(x1, 1);
+        half8 kt[NQ];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kt[i] = rk(i);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < NQ / 2) {
+#pragma unroll
+                for (int e = 32 * i / NQ; e < 32 * (i + 1) / NQ; ++e) elem(x1, 1, e);
+            }
+            dq[i % NDB] = M::mma(kt[i], dsf[i / NDB], dq[i % NDB]);
+            if (i + 4 < NQ) kt[i + 4] = rk(i + 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if (!rvalid) return;
+    const int t = t_lane, hh = R - t * G, hq = hkv * G + hh;
+    TOUT* dqrow = (TOUT*)a.dq + (((size_t)b * T + t) * a.Hq + hq) * D;
+    const float sc = a.scale;
+    const bool rope = a.rope_base > 0.0;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d = 32 * db + 8 * q4 + 4 * h;
+            float x0 = dq[db][4 * q4] * sc, x1 = dq[db][4 * q4 + 1] * sc;
+            float x2 = dq[db][4 * q4 + 2] * sc, x3 = dq[db][4 * q4 + 3] * sc;
+            if (rope) {
+                const float2 r0 = a.table[(size_t)t * (D / 2) + d / 2];
+                const float2 r1 = a.table[(size_t)t * (D / 2) + d / 2 + 1];
+                const float y0 = x0 * r0.x + x1 * r0.y, y1 = -x0 * r0.y + x1 * r0.x;
+                const float y2 = x2 * r1.x + x3 * r1.y, y3 = -x2 * r1.y + x3 * r1.x;
+                x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+            }
+            store4(dqrow + d, x0, x1, x2, x3);
+        }
+}
+
+// =====================================================================================
 // Launchers.
 // =====================================================================================
 // Records ev[2i] / ev[2i + 1] around launch i when events are given.
@@ -1314,7 +1497,10 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(1));
     NE_TRY(m.before(2));
-    hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
+    if constexpr (sizeof(OP) == 2)
+        hipLaunchKernelGGL((dq_kernel_h<D, TO>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
+    else
+        hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
     NE_TRY(hipGetLastError());
     return m.after(2);
 }

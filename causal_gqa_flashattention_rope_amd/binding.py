@@ -106,22 +106,29 @@ def alloc_workspace(nbytes, device):
 
 
 def _events_arg(events, n):
-    """torch.cuda.Event list -> void*[n] of their hipEvent_t handles (None -> untimed call)."""
+    """List of torch.cuda.Event or raw hipEvent_t handles (int) -> void*[n] (None -> untimed call;
+    a None entry -> that record is skipped)."""
     if events is None:
         return None
     if len(events) != n:
         raise ValueError(f"need {n} events")
+    handles = []
     for e in events:
+        if e is None or isinstance(e, int):
+            handles.append(e)
+            continue
         if e.cuda_event == 0:   # torch creates the HIP event lazily on first record
             e.record()
-    return (ctypes.c_void_p * n)(*[e.cuda_event for e in events])
+        handles.append(e.cuda_event)
+    return (ctypes.c_void_p * n)(*handles)
 
 
 def ne_rope_attn_fwd(q, k, v, rope_base, out_dtype=torch.float32, o=None, lse=None, workspace=None,
                      events=None):
     """o, lse = attention forward.  q [B,T,Hq,D], k/v [B,T,Hkv,D] of one dtype.
 
-    events: optional 4 torch.cuda.Event(enable_timing=True) recorded around the two kernels."""
+    events: optional 4 torch.cuda.Event(enable_timing=True) (or None) recorded around the two
+    kernels."""
     _require_gpu(q, k, v)
     B, T, Hq, Hkv, D = _dims(q, k)
     if o is None:
@@ -146,7 +153,8 @@ def ne_rope_attn_bwd(q, k, v, o, lse, dO, rope_base, dq=None, dk=None, dv=None, 
                      events=None):
     """dq, dk, dv = attention backward (out dtype = o's dtype).
 
-    events: optional 6 torch.cuda.Event(enable_timing=True) recorded around the three kernels."""
+    events: optional 6 torch.cuda.Event(enable_timing=True) (or None) recorded around the three
+    kernels."""
     _require_gpu(q, k, v, o, lse, dO)
     B, T, Hq, Hkv, D = _dims(q, k)
     if dq is None:

@@ -218,8 +218,6 @@ ne_status_t ne_rope_attn_fwd_timed(const void* q, const void* k, const void* v, 
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    void* const* events) {
     if (!events) return fail(NE_ERR_NULL, "ne_rope_attn_fwd_timed: events must be non-null");
-    for (int i = 0; i < 4; ++i)
-        if (!events[i]) return fail(NE_ERR_NULL, "ne_rope_attn_fwd_timed: events[%d] is null", i);
     return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, out_dtype, workspace,
                     workspace_bytes, stream, events);
 }
@@ -231,8 +229,6 @@ ne_status_t ne_rope_attn_bwd_timed(const void* q, const void* k, const void* v, 
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    void* const* events) {
     if (!events) return fail(NE_ERR_NULL, "ne_rope_attn_bwd_timed: events must be non-null");
-    for (int i = 0; i < 6; ++i)
-        if (!events[i]) return fail(NE_ERR_NULL, "ne_rope_attn_bwd_timed: events[%d] is null", i);
     return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, out_dtype,
                     workspace, workspace_bytes, stream, events);
 }

@@ -1446,12 +1446,13 @@ void dq_kernel_h(BwdArgs a) {
 // =====================================================================================
 // Launchers.
 // =====================================================================================
-// Records ev[2i] / ev[2i + 1] around launch i when events are given.
+// Records ev[2i] / ev[2i + 1] around launch i when events are given (null entries skipped).
 struct Marks {
     hipEvent_t const* ev;
     hipStream_t s;
-    hipError_t before(int i) const { return ev ? hipEventRecord(ev[2 * i], s) : hipSuccess; }
-    hipError_t after(int i) const { return ev ? hipEventRecord(ev[2 * i + 1], s) : hipSuccess; }
+    hipError_t rec(int j) const { return ev && ev[j] ? hipEventRecord(ev[j], s) : hipSuccess; }
+    hipError_t before(int i) const { return rec(2 * i); }
+    hipError_t after(int i) const { return rec(2 * i + 1); }
 };
 
 #define NE_TRY(x)                             \

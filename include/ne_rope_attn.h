@@ -92,10 +92,12 @@ ne_status_t ne_rope_attn_bwd(const void* q, const void* k, const void* v,
                              ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Instrumented variants for measurement: identical work, plus hipEvent_t pairs recorded on
- * `stream` around each kernel launch -- events[2i] before and events[2i+1] after launch i.
- * Forward: i = 0 operand preparation, 1 attention (4 events).  Backward: i = 0 preparation
- * with Delta, 1 dK/dV, 2 dQ (6 events).  The events are created and owned by the caller. */
+/* Instrumented variants for measurement: identical work, plus hipEvent_t records on `stream`
+ * around each kernel launch -- events[2i] before and events[2i+1] after launch i.  Forward:
+ * i = 0 operand preparation, 1 attention (an array of 4).  Backward: i = 0 preparation with
+ * Delta, 1 dK/dV, 2 dQ (an array of 6).  The array must be non-null; a null entry skips that
+ * record (a record costs microseconds of stream time, so a measurement brackets only the
+ * launches it needs).  The events are created and owned by the caller. */
 ne_status_t ne_rope_attn_fwd_timed(const void* q, const void* k, const void* v,
                                    void* o, float* lse,
                                    int B, int T, int Hq, int Hkv, int head_dim, double rope_base,

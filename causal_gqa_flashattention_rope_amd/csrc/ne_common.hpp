@@ -141,6 +141,12 @@ __device__ __forceinline__ void dma16(const void* g, unsigned lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(lds_base)
                  : "memory", "m0");
 }
+// Same with the global address split into a wave-uniform 64-bit base (SGPRs) and a per-lane
+// 32-bit byte offset (one VGPR instead of a 64-bit address per load).
+__device__ __forceinline__ void dma16_s(unsigned voff, const void* sbase, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase),
+                 "s"(lds_base) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* g, unsigned lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(g), "s"(lds_base)
                  : "memory", "m0");
@@ -149,8 +155,9 @@ __device__ __forceinline__ void dma4(const void* g, unsigned lds_base) {
 
 // Copy rows [n0, n0 + ROWS) of a dense [nrows][D] array into a swizzled LDS tile with direct
 // global->LDS loads issued by the NW waves of the block.  Rows at or past nrows are filled from
-// row nrows - 1 (finite data that the callers mask out).  Completion: s_waitcnt vmcnt(0) then
-// a barrier (ne::lds_fill_wait).
+// row nrows - 1 (finite data that the callers mask out).  src must be wave-uniform and
+// nrows * D * sizeof(OP) below 2^31 (byte offsets are 32-bit).  Completion: s_waitcnt vmcnt(0)
+// then a barrier (ne::lds_fill_wait).
 template <typename OP, int D, int ROWS, int NW>
 __device__ __forceinline__ void lds_fill(OP* tile, const OP* src, int n0, int nrows) {
     using TL = Tile<OP, D>;
@@ -165,8 +172,8 @@ __device__ __forceinline__ void lds_fill(OP* tile, const OP* src, int n0, int nr
         const int q = 64 * j + l;                      // LDS slot index of this lane
         const int r = q / TL::CPR, p = q % TL::CPR;
         const int gr = min(n0 + r, nrows - 1);
-        const OP* g = src + (size_t)gr * D + (p ^ TL::swz(r)) * TL::EPC;
-        dma16(g, lds_addr(reinterpret_cast<char*>(tile) + 1024 * j));
+        const unsigned off = (unsigned)((gr * D + (p ^ TL::swz(r)) * TL::EPC) * (int)sizeof(OP));
+        dma16_s(off, src, lds_addr(reinterpret_cast<char*>(tile) + 1024 * j));
     }
 }
 

@@ -26,6 +26,12 @@ def _bind(path):
     lib.ne_oracle_bwd.restype = i
     lib.ne_oracle_bwd_given_o.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, ctypes.c_double, i]
     lib.ne_oracle_bwd_given_o.restype = i
+    lib.ne_oracle_fwd_w.argtypes = [P, P, P, P, P, i, i, i, i, i, ctypes.c_double, i, i]
+    lib.ne_oracle_fwd_w.restype = i
+    lib.ne_oracle_bwd_w.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, ctypes.c_double, i, i]
+    lib.ne_oracle_bwd_w.restype = i
+    lib.ne_oracle_bwd_given_o_w.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, ctypes.c_double, i, i]
+    lib.ne_oracle_bwd_given_o_w.restype = i
     lib.ne_oracle_rope.argtypes = [P, P, i, i, i, i, ctypes.c_double, i]
     lib.ne_oracle_rope.restype = i
     lib.ne_oracle_max_threads.argtypes = []
@@ -75,43 +81,43 @@ def _dims(q, k):
     return B, T, Hq, Hkv, D
 
 
-def fwd(q, k, v, rope_base, nthreads=0):
-    """Return (o, lse) in float64."""
+def fwd(q, k, v, rope_base, nthreads=0, window=0):
+    """Return (o, lse) in float64.  window W > 0: query i sees keys i-W+1 .. i."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, Hq, Hkv, D = _dims(q, k)
     o = np.empty_like(q)
     lse = np.empty((B, Hq, T), dtype=np.float64)
-    rc = _load().ne_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                               B, T, Hq, Hkv, D, float(rope_base), int(nthreads))
+    rc = _load().ne_oracle_fwd_w(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                 B, T, Hq, Hkv, D, float(rope_base), int(window), int(nthreads))
     if rc:
         raise ValueError(f"ne_oracle_fwd rejected the arguments (rc={rc})")
     return o, lse
 
 
-def bwd(q, k, v, dO, rope_base, nthreads=0):
+def bwd(q, k, v, dO, rope_base, nthreads=0, window=0):
     """Return (dq, dk, dv) in float64: the exact gradients of sum(o * dO)."""
     q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
     B, T, Hq, Hkv, D = _dims(q, k)
     dq = np.empty_like(q)
     dk = np.empty_like(k)
     dv = np.empty_like(v)
-    rc = _load().ne_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq), _ptr(dk),
-                               _ptr(dv), B, T, Hq, Hkv, D, float(rope_base), int(nthreads))
+    rc = _load().ne_oracle_bwd_w(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), B, T, Hq, Hkv, D, float(rope_base), int(window), int(nthreads))
     if rc:
         raise ValueError(f"ne_oracle_bwd rejected the arguments (rc={rc})")
     return dq, dk, dv
 
 
-def bwd_given_o(q, k, v, o, dO, rope_base, nthreads=0):
+def bwd_given_o(q, k, v, o, dO, rope_base, nthreads=0, window=0):
     """(dq, dk, dv) with Delta = rowsum(dO * o) from the given o (e.g. o stored in bf16)."""
     q, k, v, o, dO = _f64(q), _f64(k), _f64(v), _f64(o), _f64(dO)
     B, T, Hq, Hkv, D = _dims(q, k)
     dq = np.empty_like(q)
     dk = np.empty_like(k)
     dv = np.empty_like(v)
-    rc = _load().ne_oracle_bwd_given_o(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(dq),
-                                       _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, float(rope_base),
-                                       int(nthreads))
+    rc = _load().ne_oracle_bwd_given_o_w(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(dq),
+                                         _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, float(rope_base),
+                                         int(window), int(nthreads))
     if rc:
         raise ValueError(f"ne_oracle_bwd_given_o rejected the arguments (rc={rc})")
     return dq, dk, dv

@@ -20,6 +20,10 @@
  *     tiled kernel reaches: it DOES store the full masked T x T matrix.
  *   - Hand-written backward checked in double precision -- agentlenshq page,
  *     "验证与稳定性"; cnblogs page, section 2.1 "编译 + gradient check".
+ *   - Sliding-window attention (the *_w entry points): "nanochat 全栈 LLM 训练实践指南"
+ *     (the nanochat guide), section "模型架构速览" (architecture overview), the feature
+ *     list entry on window_pattern: "S" layers see a quarter of the context, "L" layers
+ *     the full context.
  *
  * Readings taken where the pages are silent (each is listed in the design doc):
  *   RoPE pairs adjacent elements (2i, 2i+1) and rotates them by +t*theta_i with
@@ -28,6 +32,8 @@
  *   is visible to query i iff j <= i.  Query head h reads KV head h / (Hq/Hkv).
  *   LSE is the natural-log log-sum-exp of the scaled scores.  Gradients are
  *   returned with respect to the un-rotated q and k (inverse rotation R^T).
+ *   A window of W > 0 keys means query i sees keys i - W + 1 .. i (its own position
+ *   and the W - 1 before it); W <= 0 is the full causal prefix.
  *
  * Layouts: q, o, dO, dq are [B][T][Hq][D]; k, v, dk, dv are [B][T][Hkv][D];
  * lse is [B][Hq][T].  All arrays are dense row-major doubles owned by the caller.
@@ -49,6 +55,16 @@ static int check_shape(int B, int T, int Hq, int Hkv, int D, double base) {
     if (Hq % Hkv != 0) return 1;
     if (base > 0.0 && (D % 2) != 0) return 1;
     return 0;
+}
+
+/* First key visible to query i (window as in the header). */
+static int first_key(int i, int window) {
+    return (window > 0 && i - window + 1 > 0) ? i - window + 1 : 0;
+}
+
+/* Last query row that sees key j. */
+static int last_row(int j, int T, int window) {
+    return (window > 0 && j + window - 1 < T - 1) ? j + window - 1 : T - 1;
 }
 
 static void set_threads(int nthreads) {
@@ -96,17 +112,19 @@ int ne_oracle_rope(const double* x, double* y, int B, int T, int H, int D,
 }
 
 /* Probabilities of one (batch, query head): P[i][j] = softmax_j(S[i][j]) over
- * the visible keys j <= i, S = q' k'^T / sqrt(D).  qr, kr are the rotated
- * [T][D] rows.  Entries j > i are set to 0 and never dotted.  lse_row[i] gets
- * m_i + log(sum_j exp(S_ij - m_i)). */
+ * the visible keys lo <= j <= i (lo = first_key(i, window)), S = q' k'^T / sqrt(D).
+ * qr, kr are the rotated [T][D] rows.  Invisible entries are set to 0 and never
+ * dotted.  lse_row[i] gets m_i + log(sum_j exp(S_ij - m_i)). */
 static void softmax_probs(const double* qr, const double* kr, double* P,
-                          double* lse_row, int T, int D) {
+                          double* lse_row, int T, int D, int window) {
     const double scale = 1.0 / sqrt((double)D);
 #pragma omp parallel for schedule(dynamic, 8)
     for (int i = 0; i < T; ++i) {
         double* Pi = P + (size_t)i * T;
+        const int lo = first_key(i, window);
         double m = -INFINITY;
-        for (int j = 0; j <= i; ++j) {
+        for (int j = 0; j < lo; ++j) Pi[j] = 0.0;
+        for (int j = lo; j <= i; ++j) {
             double s = 0.0;
             for (int d = 0; d < D; ++d) s += qr[(size_t)i * D + d] * kr[(size_t)j * D + d];
             s *= scale;
@@ -114,20 +132,21 @@ static void softmax_probs(const double* qr, const double* kr, double* P,
             if (s > m) m = s;
         }
         double l = 0.0;
-        for (int j = 0; j <= i; ++j) {
+        for (int j = lo; j <= i; ++j) {
             Pi[j] = exp(Pi[j] - m);
             l += Pi[j];
         }
-        for (int j = 0; j <= i; ++j) Pi[j] /= l;
+        for (int j = lo; j <= i; ++j) Pi[j] /= l;
         for (int j = i + 1; j < T; ++j) Pi[j] = 0.0;
         lse_row[i] = m + log(l);
     }
 }
 
-/* Forward: o = softmax(mask(q' k'^T / sqrt(D))) v, lse as above. */
-int ne_oracle_fwd(const double* q, const double* k, const double* v, double* o,
-                  double* lse, int B, int T, int Hq, int Hkv, int D, double base,
-                  int nthreads) {
+/* Forward: o = softmax(mask(q' k'^T / sqrt(D))) v, lse as above; window W as in
+ * the header (W <= 0: full causal prefix). */
+int ne_oracle_fwd_w(const double* q, const double* k, const double* v, double* o,
+                    double* lse, int B, int T, int Hq, int Hkv, int D, double base,
+                    int window, int nthreads) {
     if (check_shape(B, T, Hq, Hkv, D, base)) return 1;
     set_threads(nthreads);
     const int G = Hq / Hkv;
@@ -140,12 +159,12 @@ int ne_oracle_fwd(const double* q, const double* k, const double* v, double* o,
             const int g = h / G;  /* GQA: KV head shared by G consecutive query heads */
             rope_rows(q + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, qr, (size_t)D, T, D, base, 1);
             rope_rows(k + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, kr, (size_t)D, T, D, base, 1);
-            softmax_probs(qr, kr, P, lse + ((size_t)b * Hq + h) * T, T, D);
+            softmax_probs(qr, kr, P, lse + ((size_t)b * Hq + h) * T, T, D, window);
 #pragma omp parallel for schedule(static)
             for (int i = 0; i < T; ++i) {
                 double* orow = o + IDX4(b, i, h, 0, T, Hq, D);
                 for (int d = 0; d < D; ++d) orow[d] = 0.0;
-                for (int j = 0; j <= i; ++j) {
+                for (int j = first_key(i, window); j <= i; ++j) {
                     const double p = P[(size_t)i * T + j];
                     const double* vrow = v + IDX4(b, j, g, 0, T, Hkv, D);
                     for (int d = 0; d < D; ++d) orow[d] += p * vrow[d];
@@ -157,6 +176,12 @@ int ne_oracle_fwd(const double* q, const double* k, const double* v, double* o,
     return 0;
 }
 
+int ne_oracle_fwd(const double* q, const double* k, const double* v, double* o,
+                  double* lse, int B, int T, int Hq, int Hkv, int D, double base,
+                  int nthreads) {
+    return ne_oracle_fwd_w(q, k, v, o, lse, B, T, Hq, Hkv, D, base, 0, nthreads);
+}
+
 /* Backward, given dO: exact gradients of sum(o * dO) with respect to q, k, v.
  *   dP_ij = dO_i . v_j,   Delta_i = dO_i . o_i,   dS_ij = P_ij (dP_ij - Delta_i)
  *   dq'_i = sum_j dS_ij k'_j / sqrt(D)
@@ -166,12 +191,18 @@ int ne_oracle_fwd(const double* q, const double* k, const double* v, double* o,
  * The heads of a group are accumulated in ascending order. */
 static int bwd_impl(const double* q, const double* k, const double* v, const double* dO,
                     const double* o_given, double* dq, double* dk, double* dv, int B, int T,
-                    int Hq, int Hkv, int D, double base, int nthreads);
+                    int Hq, int Hkv, int D, double base, int window, int nthreads);
 
 int ne_oracle_bwd(const double* q, const double* k, const double* v, const double* dO,
                   double* dq, double* dk, double* dv, int B, int T, int Hq, int Hkv,
                   int D, double base, int nthreads) {
-    return bwd_impl(q, k, v, dO, NULL, dq, dk, dv, B, T, Hq, Hkv, D, base, nthreads);
+    return bwd_impl(q, k, v, dO, NULL, dq, dk, dv, B, T, Hq, Hkv, D, base, 0, nthreads);
+}
+
+int ne_oracle_bwd_w(const double* q, const double* k, const double* v, const double* dO,
+                    double* dq, double* dk, double* dv, int B, int T, int Hq, int Hkv,
+                    int D, double base, int window, int nthreads) {
+    return bwd_impl(q, k, v, dO, NULL, dq, dk, dv, B, T, Hq, Hkv, D, base, window, nthreads);
 }
 
 /* The same backward with Delta_i = dO_i . o_i taken from a caller-supplied o ([B][T][Hq][D])
@@ -181,12 +212,19 @@ int ne_oracle_bwd_given_o(const double* q, const double* k, const double* v, con
                           const double* dO, double* dq, double* dk, double* dv, int B, int T,
                           int Hq, int Hkv, int D, double base, int nthreads) {
     if (!o) return 1;
-    return bwd_impl(q, k, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, nthreads);
+    return bwd_impl(q, k, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, 0, nthreads);
+}
+
+int ne_oracle_bwd_given_o_w(const double* q, const double* k, const double* v, const double* o,
+                            const double* dO, double* dq, double* dk, double* dv, int B, int T,
+                            int Hq, int Hkv, int D, double base, int window, int nthreads) {
+    if (!o) return 1;
+    return bwd_impl(q, k, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, window, nthreads);
 }
 
 static int bwd_impl(const double* q, const double* k, const double* v, const double* dO,
                     const double* o_given, double* dq, double* dk, double* dv, int B, int T,
-                    int Hq, int Hkv, int D, double base, int nthreads) {
+                    int Hq, int Hkv, int D, double base, int window, int nthreads) {
     if (check_shape(B, T, Hq, Hkv, D, base)) return 1;
     set_threads(nthreads);
     const int G = Hq / Hkv;
@@ -213,14 +251,15 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
             memset(dvg, 0, sizeof(double) * (size_t)T * D);
             for (int h = g * G; h < (g + 1) * G; ++h) {
                 rope_rows(q + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, qr, (size_t)D, T, D, base, 1);
-                softmax_probs(qr, kr, P, lse_row, T, D);
+                softmax_probs(qr, kr, P, lse_row, T, D, window);
 #pragma omp parallel for schedule(dynamic, 8)
                 for (int i = 0; i < T; ++i) {
                     /* o_i, Delta_i and the row of dS */
+                    const int lo = first_key(i, window);
                     double* oi = orow + (size_t)i * D;
                     const double* dOi = dO + IDX4(b, i, h, 0, T, Hq, D);
                     for (int d = 0; d < D; ++d) oi[d] = 0.0;
-                    for (int j = 0; j <= i; ++j) {
+                    for (int j = lo; j <= i; ++j) {
                         const double p = P[(size_t)i * T + j];
                         const double* vj = v + IDX4(b, j, g, 0, T, Hkv, D);
                         for (int d = 0; d < D; ++d) oi[d] += p * vj[d];
@@ -229,7 +268,8 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
                     double di = 0.0;
                     for (int d = 0; d < D; ++d) di += dOi[d] * od[d];
                     delta[i] = di;
-                    for (int j = 0; j <= i; ++j) {
+                    for (int j = 0; j < lo; ++j) dS[(size_t)i * T + j] = 0.0;
+                    for (int j = lo; j <= i; ++j) {
                         const double* vj = v + IDX4(b, j, g, 0, T, Hkv, D);
                         double dp = 0.0;
                         for (int d = 0; d < D; ++d) dp += dOi[d] * vj[d];
@@ -239,7 +279,7 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
                     /* dq'_i */
                     double* dqi = dqr + (size_t)i * D;
                     for (int d = 0; d < D; ++d) dqi[d] = 0.0;
-                    for (int j = 0; j <= i; ++j) {
+                    for (int j = lo; j <= i; ++j) {
                         const double s = dS[(size_t)i * T + j];
                         for (int d = 0; d < D; ++d) dqi[d] += s * kr[(size_t)j * D + d];
                     }
@@ -247,12 +287,13 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
                 }
                 /* dq = R^T dq' for this head */
                 rope_rows(dqr, (size_t)D, dq + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, T, D, base, -1);
-                /* column sums over the query rows i >= j, one thread per key row j */
+                /* column sums over the query rows that see key j, one thread per key row j */
 #pragma omp parallel for schedule(dynamic, 8)
                 for (int j = 0; j < T; ++j) {
                     double* dkj = dkr + (size_t)j * D;
                     double* dvj = dvg + (size_t)j * D;
-                    for (int i = j; i < T; ++i) {
+                    const int hi = last_row(j, T, window);
+                    for (int i = j; i <= hi; ++i) {
                         const double s = dS[(size_t)i * T + j] * scale;
                         const double p = P[(size_t)i * T + j];
                         const double* qi = qr + (size_t)i * D;

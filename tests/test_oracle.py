@@ -37,7 +37,7 @@ def relerr(a, b):
 # Brute force: rotations as complex multiplications, softmax as exp/sum without the max
 # shift, sums with math.fsum.  Different formulation from the oracle's real 2x2 form.
 # --------------------------------------------------------------------------------------
-def brute_fwd(q, k, v, base):
+def brute_fwd(q, k, v, base, window=0):
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
     G = Hq // Hkv
@@ -59,14 +59,15 @@ def brute_fwd(q, k, v, base):
             qs = [rot(q[b, t, h], t) for t in range(T)]
             ks = [rot(k[b, t, g], t) for t in range(T)]
             for i in range(T):
+                keys = [j for j in range(i + 1) if window <= 0 or i - j < window]
                 w = []
-                for j in range(i + 1):
+                for j in keys:
                     s = math.fsum((qs[i][p].conjugate() * ks[j][p]).real for p in range(D // 2))
                     w.append(math.exp(s / math.sqrt(D)))
                 z = math.fsum(w)
                 lse[b, h, i] = math.log(z)
                 for d in range(D):
-                    o[b, i, h, d] = math.fsum(w[j] * v[b, j, g, d] for j in range(i + 1)) / z
+                    o[b, i, h, d] = math.fsum(wj * v[b, j, g, d] for wj, j in zip(w, keys)) / z
     return o, lse
 
 
@@ -117,7 +118,7 @@ def test_bwd_matches_brute_force_finite_differences(shape, base):
 # torch float64 autograd: an independent implementation (complex RoPE via view_as_complex,
 # KV heads expanded with repeat_interleave, masked softmax, autograd for the gradients).
 # --------------------------------------------------------------------------------------
-def torch_attention(q, k, v, base):
+def torch_attention(q, k, v, base, window=0):
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
     if base > 0:
@@ -135,6 +136,8 @@ def torch_attention(q, k, v, base):
     ve = v.repeat_interleave(Hq // Hkv, dim=2)
     s = torch.einsum("bihd,bjhd->bhij", qr, kr) / math.sqrt(D)
     mask = torch.ones(T, T, dtype=torch.bool).triu(1)
+    if window > 0:  # keys more than window - 1 positions back are hidden too
+        mask |= torch.ones(T, T, dtype=torch.bool).tril(-window)
     s = s.masked_fill(mask, float("-inf"))
     lse = torch.logsumexp(s, dim=-1)
     p = torch.softmax(s, dim=-1)
@@ -434,3 +437,109 @@ def test_bwd_given_o_matches_autograd_with_delta_from_o():
     assert relerr(dq2, tq.grad.numpy()) < 1e-11
     assert relerr(dk2, tk.grad.numpy()) < 1e-11
     assert relerr(dv2, tv.grad.numpy()) < 1e-11
+
+
+# --------------------------------------------------------------------------------------
+# Sliding window (query i sees keys i - W + 1 .. i): the nanochat guide's window_pattern,
+# where "S" layers see a quarter of the context.
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("shape,window", [((1, 6, 2, 1, 4), 1), ((1, 6, 4, 2, 4), 2), ((2, 7, 2, 2, 2), 3),
+                                          ((1, 5, 3, 1, 4), 5)])
+def test_window_matches_brute_force(shape, window):
+    q, k, v, _ = case(*shape, seed=301)
+    o, lse = oracle.fwd(q, k, v, 3.0, window=window)
+    bo, blse = brute_fwd(q, k, v, 3.0, window=window)
+    assert relerr(o, bo) < 1e-13
+    assert np.max(np.abs(lse - blse)) < 1e-13
+
+
+@pytest.mark.parametrize("shape,base,window", [((2, 37, 6, 2, 16), 10000.0, 8), ((1, 64, 4, 2, 32), 10000.0, 16),
+                                               ((1, 33, 4, 4, 8), 0.0, 5), ((1, 19, 3, 1, 6), 10.0, 1)])
+def test_window_against_torch_float64_autograd(shape, base, window):
+    q, k, v, dO = case(*shape, seed=311)
+    o, lse = oracle.fwd(q, k, v, base, window=window)
+    dq, dk, dv = oracle.bwd(q, k, v, dO, base, window=window)
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    to, tlse = torch_attention(tq, tk, tv, base, window=window)
+    (to * torch.tensor(dO)).sum().backward()
+    assert relerr(o, to.detach().numpy()) < 1e-12
+    assert np.max(np.abs(lse - tlse.detach().numpy())) < 1e-12
+    assert relerr(dq, tq.grad.numpy()) < 1e-11
+    assert relerr(dk, tk.grad.numpy()) < 1e-11
+    assert relerr(dv, tv.grad.numpy()) < 1e-11
+
+
+def test_window_of_at_least_T_is_the_full_causal_prefix():
+    q, k, v, dO = case(1, 21, 4, 2, 8, seed=321)
+    full = oracle.fwd(q, k, v, 10000.0) + oracle.bwd(q, k, v, dO, 10000.0)
+    for W in (21, 22, 1000):
+        got = oracle.fwd(q, k, v, 10000.0, window=W) + oracle.bwd(q, k, v, dO, 10000.0, window=W)
+        for a, b in zip(got, full):
+            np.testing.assert_array_equal(a, b)
+
+
+def test_window_one_sees_only_itself():
+    """W = 1: o_i = v_i, lse_i = q'_i . k'_i / sqrt(D); P = 1 makes dS = 0, so dq = dk = 0."""
+    q, k, v, dO = case(1, 9, 4, 2, 8, seed=331)
+    o, lse = oracle.fwd(q, k, v, 10000.0, window=1)
+    dq, dk, dv = oracle.bwd(q, k, v, dO, 10000.0, window=1)
+    qr, kr = oracle.rope(q, 10000.0), oracle.rope(k, 10000.0)
+    for h in range(4):
+        np.testing.assert_array_equal(o[0, :, h], v[0, :, h // 2])
+        ref = np.sum(qr[0, :, h] * kr[0, :, h // 2], axis=-1) / math.sqrt(8)
+        np.testing.assert_allclose(lse[0, h], ref, rtol=0, atol=1e-13)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    np.testing.assert_allclose(dv[0, :, 0], dO[0, :, 0] + dO[0, :, 1], rtol=0, atol=1e-15)
+
+
+def test_window_zero_queries_average_the_window():
+    """q = 0: every visible key has weight 1 / min(i + 1, W)."""
+    W, T = 7, 30
+    _, k, v, dO = case(1, T, 2, 1, 16, seed=341)
+    q = np.zeros((1, T, 2, 16))
+    o, lse = oracle.fwd(q, k, v, 10000.0, window=W)
+    dq, dk, dv = oracle.bwd(q, k, v, dO, 10000.0, window=W)
+    n = np.minimum(np.arange(1, T + 1), W)
+    np.testing.assert_allclose(lse[0, 0], np.log(n), rtol=0, atol=1e-14)
+    mean = np.array([v[0, max(0, i - W + 1):i + 1, 0].mean(axis=0) for i in range(T)])
+    np.testing.assert_allclose(o[0, :, 0], mean, rtol=0, atol=1e-13)
+    # dv_j = sum over the queries i = j .. j + W - 1 that see key j of dO_i / n_i (both heads)
+    w = dO[0].sum(axis=1) / n[:, None]
+    dv_ref = np.array([w[j:min(T, j + W)].sum(axis=0) for j in range(T)])
+    np.testing.assert_allclose(dv[0, :, 0], dv_ref, rtol=0, atol=1e-13)
+    assert np.all(dk == 0)
+
+
+def test_window_keys_outside_the_window_are_invisible():
+    """Perturbing key/value j changes only the queries j .. j + W - 1, bitwise."""
+    W, T, j = 6, 25, 9
+    q, k, v, dO = case(1, T, 4, 2, 8, seed=351)
+    o, lse = oracle.fwd(q, k, v, 10000.0, window=W)
+    k2, v2 = k.copy(), v.copy()
+    k2[0, j] += 1.0
+    v2[0, j] -= 2.0
+    o2, lse2 = oracle.fwd(q, k2, v2, 10000.0, window=W)
+    outside = [i for i in range(T) if not (j <= i <= j + W - 1)]
+    np.testing.assert_array_equal(o[0, outside], o2[0, outside])
+    np.testing.assert_array_equal(lse[0, :, outside], lse2[0, :, outside])
+    inside = list(range(j, j + W))
+    assert np.all(np.any(o[0, inside] != o2[0, inside], axis=(1, 2)))
+
+
+def test_window_finite_differences_tiny():
+    q, k, v, dO = case(1, 7, 4, 2, 4, seed=361)
+    W = 3
+    dq, dk, dv = oracle.bwd(q, k, v, dO, 10000.0, window=W)
+    worst = 0.0
+    for which, a in enumerate((dq, dk, dv)):
+        arrs = [q.copy(), k.copy(), v.copy()]
+        for idx in np.ndindex(*a.shape):
+            x0 = arrs[which][idx]
+            step = 1e-5 * max(1.0, abs(x0))
+            arrs[which][idx] = x0 + step
+            lp = float(np.sum(oracle.fwd(*arrs, 10000.0, window=W)[0] * dO))
+            arrs[which][idx] = x0 - step
+            lm = float(np.sum(oracle.fwd(*arrs, 10000.0, window=W)[0] * dO))
+            arrs[which][idx] = x0
+            worst = max(worst, abs((lp - lm) / (2 * step) - a[idx]) / np.max(np.abs(a)))
+    assert worst < 1e-6

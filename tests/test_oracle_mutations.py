@@ -20,13 +20,17 @@ MUTATIONS = {
     "rope_frequency_exponent": ("pow(base, -2.0 * (double)i / (double)D)", "pow(base, -1.0 * (double)i / (double)D)"),
     "gqa_head_mapping": ("const int g = h / G;", "const int g = h % Hkv;"),
     "mask_includes_future": [
-        ("for (int j = 0; j <= i; ++j) {\n            double s = 0.0;",
-         "for (int j = 0; j < T; ++j) {\n            double s = 0.0;"),
-        ("for (int j = 0; j <= i; ++j) {\n            Pi[j] = exp(Pi[j] - m);",
-         "for (int j = 0; j < T; ++j) {\n            Pi[j] = exp(Pi[j] - m);"),
-        ("for (int j = 0; j <= i; ++j) Pi[j] /= l;", "for (int j = 0; j < T; ++j) Pi[j] /= l;"),
+        ("for (int j = lo; j <= i; ++j) {\n            double s = 0.0;",
+         "for (int j = lo; j < T; ++j) {\n            double s = 0.0;"),
+        ("for (int j = lo; j <= i; ++j) {\n            Pi[j] = exp(Pi[j] - m);",
+         "for (int j = lo; j < T; ++j) {\n            Pi[j] = exp(Pi[j] - m);"),
+        ("for (int j = lo; j <= i; ++j) Pi[j] /= l;", "for (int j = lo; j < T; ++j) Pi[j] /= l;"),
         ("for (int j = i + 1; j < T; ++j) Pi[j] = 0.0;", ""),
     ],
+    "window_off_by_one": ("return (window > 0 && i - window + 1 > 0) ? i - window + 1 : 0;",
+                          "return (window > 0 && i - window > 0) ? i - window : 0;"),
+    "window_column_short": ("return (window > 0 && j + window - 1 < T - 1) ? j + window - 1 : T - 1;",
+                            "return (window > 0 && j + window - 2 < T - 1) ? j + window - 2 : T - 1;"),
     "softmax_scale_missing": ("            s *= scale;\n", "\n"),
     "dq_scale_missing": ("for (int d = 0; d < D; ++d) dqi[d] *= scale;", ""),
     "ds_sign": ("* (dp - di);", "* (di - dp);"),
@@ -52,6 +56,8 @@ def battery():
         ("d2", pins.test_d2_rotation_by_t_radians),
         ("zero_q", pins.test_zero_queries_give_uniform_weights),
         ("single", pins.test_single_token),
+        ("window_autograd", lambda: pins.test_window_against_torch_float64_autograd((2, 37, 6, 2, 16), 10000.0, 8)),
+        ("window_zero_q", pins.test_window_zero_queries_average_the_window),
     ]
     for name, fn in checks:
         try:

@@ -20,6 +20,7 @@ STATUS = {0: "NE_OK", 1: "NE_ERR_NULL", 2: "NE_ERR_SHAPE", 3: "NE_ERR_UNSUPPORTE
 # Every symbol include/ne_rope_attn.h declares.
 EXPORTS = ("ne_rope_attn_fwd_workspace_bytes", "ne_rope_attn_bwd_workspace_bytes",
            "ne_rope_attn_fwd", "ne_rope_attn_bwd", "ne_rope_attn_fwd_timed", "ne_rope_attn_bwd_timed",
+           "ne_rope_attn_fwd_window", "ne_rope_attn_bwd_window",
            "ne_status_str", "ne_last_error", "ne_abi_version")
 
 
@@ -54,6 +55,12 @@ def lib():
     L.ne_rope_attn_fwd_timed.restype = i
     L.ne_rope_attn_bwd_timed.argtypes = L.ne_rope_attn_bwd.argtypes + [ctypes.POINTER(vp)]
     L.ne_rope_attn_bwd_timed.restype = i
+    L.ne_rope_attn_fwd_window.argtypes = ([vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, i, vp, sz, vp]
+                                          + [ctypes.POINTER(vp)])
+    L.ne_rope_attn_fwd_window.restype = i
+    L.ne_rope_attn_bwd_window.argtypes = ([vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, i, vp, sz, vp]
+                                          + [ctypes.POINTER(vp)])
+    L.ne_rope_attn_bwd_window.restype = i
     L.ne_status_str.argtypes = [i]
     L.ne_status_str.restype = ctypes.c_char_p
     L.ne_last_error.argtypes = []
@@ -129,6 +136,16 @@ def ne_rope_attn_fwd(q, k, v, rope_base, out_dtype=torch.float32, o=None, lse=No
 
     events: optional 4 torch.cuda.Event(enable_timing=True) (or None) recorded around the two
     kernels."""
+    return _fwd(q, k, v, rope_base, None, out_dtype, o, lse, workspace, events)
+
+
+def ne_rope_attn_fwd_window(q, k, v, rope_base, window, out_dtype=torch.float32, o=None, lse=None,
+                            workspace=None, events=None):
+    """Sliding-window forward: query t sees keys t - window + 1 .. t (window <= 0: causal prefix)."""
+    return _fwd(q, k, v, rope_base, int(window), out_dtype, o, lse, workspace, events)
+
+
+def _fwd(q, k, v, rope_base, window, out_dtype, o, lse, workspace, events):
     _require_gpu(q, k, v)
     B, T, Hq, Hkv, D = _dims(q, k)
     if o is None:
@@ -142,7 +159,9 @@ def ne_rope_attn_fwd(q, k, v, rope_base, out_dtype=torch.float32, o=None, lse=No
             _DT[q.dtype], _DT[o.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream())
     ev = _events_arg(events, 4)
-    if ev is None:
+    if window is not None:
+        _check(lib().ne_rope_attn_fwd_window(*args[:11], window, *args[11:], ev))
+    elif ev is None:
         _check(lib().ne_rope_attn_fwd(*args))
     else:
         _check(lib().ne_rope_attn_fwd_timed(*args, ev))
@@ -155,6 +174,16 @@ def ne_rope_attn_bwd(q, k, v, o, lse, dO, rope_base, dq=None, dk=None, dv=None, 
 
     events: optional 6 torch.cuda.Event(enable_timing=True) (or None) recorded around the three
     kernels."""
+    return _bwd(q, k, v, o, lse, dO, rope_base, None, dq, dk, dv, workspace, events)
+
+
+def ne_rope_attn_bwd_window(q, k, v, o, lse, dO, rope_base, window, dq=None, dk=None, dv=None,
+                            workspace=None, events=None):
+    """Sliding-window backward; `window` must be the one the forward used."""
+    return _bwd(q, k, v, o, lse, dO, rope_base, int(window), dq, dk, dv, workspace, events)
+
+
+def _bwd(q, k, v, o, lse, dO, rope_base, window, dq, dk, dv, workspace, events):
     _require_gpu(q, k, v, o, lse, dO)
     B, T, Hq, Hkv, D = _dims(q, k)
     if dq is None:
@@ -170,7 +199,9 @@ def ne_rope_attn_bwd(q, k, v, o, lse, dO, rope_base, dq=None, dk=None, dv=None, 
             B, T, Hq, Hkv, D, float(rope_base), _DT[q.dtype], _DT[o.dtype], _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream())
     ev = _events_arg(events, 6)
-    if ev is None:
+    if window is not None:
+        _check(lib().ne_rope_attn_bwd_window(*args[:15], window, *args[15:], ev))
+    elif ev is None:
         _check(lib().ne_rope_attn_bwd(*args))
     else:
         _check(lib().ne_rope_attn_bwd_timed(*args, ev))

@@ -73,6 +73,9 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, ne_dtype_t in) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Keys a query sees at most: the window, or the whole causal prefix when window <= 0 or >= T.
+int visible_keys(int window, int T) { return (window <= 0 || window >= T) ? T : window; }
+
 ne_status_t common_checks(int B, int T, int Hq, int Hkv, int D, ne_dtype_t in, ne_dtype_t out) {
     ne_status_t s = check_shape(B, T, Hq, Hkv, D);
     if (s != NE_OK) return s;
@@ -119,7 +122,7 @@ size_t ne_rope_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_
 namespace {
 
 ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
-                     int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                     int B, int T, int Hq, int Hkv, int head_dim, double rope_base, int window,
                      ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                      void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     if (!q || !k || !v || !o || !lse || !workspace)
@@ -145,6 +148,7 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     fa.q = q; fa.kh = pa.kh; fa.vh = pa.vh; fa.table = pa.table; fa.o = o; fa.lse = lse;
     fa.rope_base = rope_base; fa.qscale = pa.qscale;
     fa.B = B; fa.T = T; fa.Hq = Hq; fa.Hkv = Hkv; fa.G = G;
+    fa.window = visible_keys(window, T);
     fa.nrb = (int)(((int64_t)T * G + 127) / 128);
     hipError_t e = ne::launch_fwd((int)in_dtype, (int)out_dtype, head_dim, pa, fa, (hipStream_t)stream,
                                   (hipEvent_t const*)events);
@@ -154,7 +158,7 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
 
 ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* dO, void* dq, void* dk, void* dv,
-                     int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                     int B, int T, int Hq, int Hkv, int head_dim, double rope_base, int window,
                      ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                      void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
@@ -182,6 +186,7 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     ba.delta = pa.delta; ba.lse2 = pa.lse2; ba.table = pa.table;
     ba.dq = dq; ba.dk = dk; ba.dv = dv;
     ba.B = B; ba.T = T; ba.Hq = Hq; ba.Hkv = Hkv; ba.G = G;
+    ba.window = visible_keys(window, T);
     ba.nrb = (int)(((int64_t)T * G + 127) / 128);
     ba.rope_base = rope_base;
     ba.scale = (float)(1.0 / std::sqrt((double)head_dim));
@@ -199,7 +204,7 @@ ne_status_t ne_rope_attn_fwd(const void* q, const void* k, const void* v, void* 
                              int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
                              ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, out_dtype, workspace,
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, 0, in_dtype, out_dtype, workspace,
                     workspace_bytes, stream, nullptr);
 }
 
@@ -208,7 +213,7 @@ ne_status_t ne_rope_attn_bwd(const void* q, const void* k, const void* v, const 
                              int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
                              ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, out_dtype,
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, 0, in_dtype, out_dtype,
                     workspace, workspace_bytes, stream, nullptr);
 }
 
@@ -218,7 +223,7 @@ ne_status_t ne_rope_attn_fwd_timed(const void* q, const void* k, const void* v, 
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    void* const* events) {
     if (!events) return fail(NE_ERR_NULL, "ne_rope_attn_fwd_timed: events must be non-null");
-    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, out_dtype, workspace,
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, 0, in_dtype, out_dtype, workspace,
                     workspace_bytes, stream, events);
 }
 
@@ -229,8 +234,27 @@ ne_status_t ne_rope_attn_bwd_timed(const void* q, const void* k, const void* v, 
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    void* const* events) {
     if (!events) return fail(NE_ERR_NULL, "ne_rope_attn_bwd_timed: events must be non-null");
-    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, out_dtype,
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, 0, in_dtype, out_dtype,
                     workspace, workspace_bytes, stream, events);
+}
+
+ne_status_t ne_rope_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int B, int T, int Hq, int Hkv, int head_dim, double rope_base, int window,
+                                    ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    void* const* events) {
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, window, in_dtype, out_dtype,
+                    workspace, workspace_bytes, stream, events);
+}
+
+ne_status_t ne_rope_attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                                    int B, int T, int Hq, int Hkv, int head_dim, double rope_base, int window,
+                                    ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    void* const* events) {
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, window, in_dtype,
+                    out_dtype, workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"

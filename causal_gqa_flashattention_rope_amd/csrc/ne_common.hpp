@@ -31,6 +31,12 @@ typedef __attribute__((address_space(3))) fp16x4_tr* lds_tr_ptr;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Starting value of a running row maximum: finite, so exp2(-inf - kMFloor) = 0 for masked scores
+// and exp2(kMFloor - m) = 0 when a real maximum m replaces it.
+constexpr float kMFloor = -1.0e30f;
+
+// Query t sees key j iff t - W < j <= t (W = the window, 1..T; W = T is the causal prefix).
+__device__ __forceinline__ bool visible(int j, int t, int W) { return (unsigned)(t - j) < (unsigned)W; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 

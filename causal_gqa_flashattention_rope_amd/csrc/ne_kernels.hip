@@ -333,6 +333,8 @@ void fwd_kernel(FwdArgs a) {
     const int wave_tmin = Rw / G;
     const int wave_tmax = min(Rw + 31, TG - 1) / G;
     const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;
+    const int W = a.window;
+    const int j0 = max(0, R0 / G - W + 1) / BN;  // the block's first key tile
 
     const size_t grp = (size_t)wk.grp;
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
@@ -346,25 +348,28 @@ void fwd_kernel(FwdArgs a) {
         load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, a.qscale, h, rvalid);
     }
     wait_all();
-    lds_fill<OP, D, BN, NW>(lds, kg, 0, T);
-    lds_fill<OP, D, BN, NW>(lds + TILE, vg, 0, T);
+    lds_fill<OP, D, BN, NW>(lds, kg, j0 * BN, T);
+    lds_fill<OP, D, BN, NW>(lds + TILE, vg, j0 * BN, T);
 
-    float m_run = -INFINITY, l_run = 0.f;
+    // kMFloor instead of -inf: a row whose first tiles are all masked keeps p = 0 until a tile
+    // it sees raises m (the first such tile always does)
+    float m_run = kMFloor, l_run = 0.f;
     floatx16 oacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
 
-    for (int it = 0; it < ntiles; ++it) {
-        const OP* Ks = lds + (it & 1) * 2 * TILE;
+    for (int it = j0; it < ntiles; ++it) {
+        const OP* Ks = lds + ((it - j0) & 1) * 2 * TILE;
         const OP* Vs = Ks + TILE;
         lds_fill_wait();
         if (it + 1 < ntiles) {
-            OP* nxt = lds + ((it + 1) & 1) * 2 * TILE;
+            OP* nxt = lds + ((it + 1 - j0) & 1) * 2 * TILE;
             lds_fill<OP, D, BN, NW>(nxt, kg, (it + 1) * BN, T);
             lds_fill<OP, D, BN, NW>(nxt + TILE, vg, (it + 1) * BN, T);
         }
         const int n0 = it * BN;
-        if (n0 > wave_tmax) continue;  // every row of this wave precedes the whole tile
+        if (n0 > wave_tmax) continue;                 // every row of this wave precedes the tile
+        if (wave_tmin - (n0 + BN - 1) >= W) continue;  // the tile is older than every row's window
 
         floatx16 s[2];
 #pragma unroll
@@ -374,12 +379,12 @@ void fwd_kernel(FwdArgs a) {
             for (int ks = 0; ks < KS; ++ks)
                 s[mb] = M::mma(row_frag_sw<OP, D>(Ks, 32 * mb + c, ks, h), qf[ks], s[mb]);
         }
-        if (n0 + BN - 1 > wave_tmin) {  // tile crosses some row's diagonal
+        if (n0 + BN - 1 > wave_tmin || wave_tmax - n0 >= W) {  // crosses a diagonal or a window edge
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (n0 + 32 * mb + acc_row(r, h) > t_lane) s[mb][r] = -INFINITY;
+                    if (!visible(n0 + 32 * mb + acc_row(r, h), t_lane, W)) s[mb][r] = -INFINITY;
         }
         float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
@@ -489,6 +494,9 @@ void fwd_kernel_h(FwdArgs a) {
     const int wave_tmax = min(Rw + 31, TG - 1) / G;
     const int last = Rw < TG ? wave_tmax / BN : -1;           // this wave's last key tile
     const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;  // the block's
+    const int W = a.window;
+    const int j0 = max(0, R0 / G - W + 1) / BN;                // the block's first key tile
+    const int first = max(0, wave_tmin - W + 1) / BN;         // this wave's
 
     const size_t grp = (size_t)wk.grp;
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
@@ -510,26 +518,29 @@ void fwd_kernel_h(FwdArgs a) {
         load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, a.qscale, h, rvalid);
     }
     wait_all();
-    fill_k(0);
-    if (ntiles > 1) fill_k(1);
-    lds_fill_wait_keep(ntiles > 1 ? nkw : 0);  // K of tile 0
+    fill_k(j0);
+    if (ntiles > j0 + 1) fill_k(j0 + 1);
+    lds_fill_wait_keep(ntiles > j0 + 1 ? nkw : 0);  // K of tile j0
 
     floatx16 s[2];        // scores of one tile (32 keys per accumulator)
-    half8 p[2][4];        // fp16 probabilities of two consecutive tiles (index: tile parity)
+    // fp16 probabilities of two consecutive tiles (index: tile parity counted from j0); zeros
+    // until written, so the product of a wave's first active iteration adds nothing
+    half8 p[2][4] = {};
     floatx16 oacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
-    float m_run = 0.f, l_run = 0.f, apend = 1.f;
+    float m_run = kMFloor, l_run = 0.f, apend = 1.f;
     bool pend = false;
 
-    auto mask_max = [&](int j) {  // mask of tile j (if it crosses a diagonal), then the row max
+    // mask of tile j (if it crosses a diagonal or a window edge), then the row max
+    auto mask_max = [&](int j) {
         const int n0 = j * BN;
-        if (n0 + BN - 1 > wave_tmin) {
+        if (n0 + BN - 1 > wave_tmin || wave_tmax - n0 >= W) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (n0 + 32 * mb + acc_row(r, h) > t_lane) s[mb][r] = -INFINITY;
+                    if (!visible(n0 + 32 * mb + acc_row(r, h), t_lane, W)) s[mb][r] = -INFINITY;
         }
         float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
@@ -616,9 +627,11 @@ void fwd_kernel_h(FwdArgs a) {
         if (it + 3 < ntiles) fill_k(it + 3);
         if (it + 1 < ntiles) fill_v(it + 1);
     };
+    // A wave starts at its own first tile: the iterations before it are skipped, the one just
+    // before it exponentiates scores that are all -inf (p = 0, with m_run still at the floor).
     auto step = [&](int it, auto PAR) {
         sync_fill(it);
-        if (it <= last + 1) {
+        if (it >= first - 1 && it <= last + 1) {
             const float ps = phase1(it, PAR, IC<1>{});
             l_run += it <= last ? ps : 0.f;  // iteration last + 1 only finishes the product
             if (it + 1 <= last) phase2(it + 1);
@@ -633,24 +646,26 @@ void fwd_kernel_h(FwdArgs a) {
         }
     };
 
-    // iteration -1: the scores of tile 0, which every row sees, fix the first m exactly
-    if (ntiles > 2) fill_k(2);
-    fill_v(0);
+    // iteration j0 - 1: the scores of tile j0 fix the first m exactly for the rows that see it
+    // (without a window, every row); the others keep the floor until their first tile
+    if (ntiles > j0 + 2) fill_k(j0 + 2);
+    fill_v(j0);
     if (last >= 0) {
-        phase2(0);
-        m_run = mask_max(0);
+        phase2(j0);
+        m_run = fmaxf(mask_max(j0), kMFloor);
     }
-    // iteration 0: no product yet
-    sync_fill(0);
+    // iteration j0: no product yet
+    sync_fill(j0);
     if (last >= 0) {
-        l_run = phase1(0, IC<0>{}, IC<0>{});
-        if (last >= 1) {
-            phase2(1);
-            refresh(1);
+        l_run = phase1(j0, IC<0>{}, IC<0>{});
+        if (last >= j0 + 1) {
+            phase2(j0 + 1);
+            refresh(j0 + 1);
         }
     }
-    // iterations 1 .. ntiles, run by every wave (the barriers are block-wide)
-    for (int it = 1; it <= ntiles; it += 2) {
+    // iterations j0 + 1 .. ntiles, run by every wave (the barriers are block-wide); the parity of
+    // the probability buffers counts from j0
+    for (int it = j0 + 1; it <= ntiles; it += 2) {
         step(it, IC<1>{});
         if (it + 1 > ntiles) break;
         step(it + 1, IC<0>{});
@@ -747,9 +762,17 @@ void dkdv_kernel(BwdArgs a) {
         const int n0 = kb * BN + 32 * kq;                      // first key of this wave
         const int key = n0 + c;
         const bool kvalid = key < T;
-        const int keyG = key * G;              // row R sees this key iff R >= key * G
+        // flattened row R (position R / G) sees this key iff keyG <= R < keyWG
+        const int W = a.window;
+        const int keyG = key * G;
+        const int keyWG = (T - key <= W ? T : key + W) * G;
         const int rstart = (kb * BN * G) / BMR * BMR;
-        const int ntiles = (TG - rstart + BMR - 1) / BMR;
+        const int kl = kb * BN + BN - 1;                                 // the block's last key
+        const int rend = (T - kl <= W ? T : kl + W) * G;                 // rows past it see none
+        const int ntiles = (rend - rstart + BMR - 1) / BMR;
+        const int wlim = (T - (n0 + 31) <= W ? T : n0 + 31 + W) * G;    // rows from wlim see none
+        const int wedge = (T - n0 <= W ? T : n0 + W) * G;                // of this wave's keys, from
+                                                                         // wedge some are hidden
 
         // role 0 keeps K^T fragments, role 1 keeps V^T fragments (B operands, one key per lane)
         typename M::frag kvf[KS];
@@ -773,8 +796,8 @@ void dkdv_kernel(BwdArgs a) {
             lds_fill_wait_keep(per_fill * min(NST - 2, ntiles - 1 - it));
             if (it + NST - 1 < ntiles) fill((it + NST - 1) % NST, R0 + (NST - 1) * BMR);
             const int Rh = R0 + 32 * rh;                       // first row of this wave's half
-            const bool active = min(Rh + 31, TG - 1) >= n0 * G && Rh < TG;
-            const bool need_mask = Rh < (n0 + 31) * G || Rh + 32 > TG;
+            const bool active = min(Rh + 31, TG - 1) >= n0 * G && Rh < wlim;
+            const bool need_mask = Rh < (n0 + 31) * G || Rh + 32 > wedge;
             floatx16 x;                                        // role 0: S -> P, role 1: dP
             if constexpr (F16) {
                 // every LDS fragment of this tile first (one round trip), then the products
@@ -796,7 +819,7 @@ void dkdv_kernel(BwdArgs a) {
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
                                 const int row = Rh + acc_row(r, h);
-                                if (row < keyG || row >= TG) x[r] = -INFINITY;
+                                if (row < keyG || row >= keyWG) x[r] = -INFINITY;
                             }
                         }
 #pragma unroll
@@ -843,7 +866,7 @@ void dkdv_kernel(BwdArgs a) {
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
                                 const int row = Rh + acc_row(r, h);
-                                if (row < keyG || row >= TG) x[r] = -INFINITY;
+                                if (row < keyG || row >= keyWG) x[r] = -INFINITY;
                             }
                         }
 #pragma unroll
@@ -1041,17 +1064,25 @@ void dkdv_kernel_h(BwdArgs a) {
         const int n0 = kb * BN + 32 * kq;                      // first key of this wave
         const int key = n0 + c;
         const bool kvalid = key < T;
-        const int keyG = key * G;              // row R sees this key iff R >= key * G
+        // flattened row R (position R / G) sees this key iff keyG <= R < keyWG
+        const int W = a.window;
+        const int keyG = key * G;
+        const int keyWG = (T - key <= W ? T : key + W) * G;
         const int rstart = (kb * BN * G) / BMR * BMR;
-        const int ntiles = (TG - rstart + BMR - 1) / BMR;
+        const int kl = kb * BN + BN - 1;                                 // the block's last key
+        const int rend = (T - kl <= W ? T : kl + W) * G;                 // rows past it see none
+        const int ntiles = (rend - rstart + BMR - 1) / BMR;
+        const int wlim = (T - (n0 + 31) <= W ? T : n0 + 31 + W) * G;    // rows from wlim see none
+        const int wedge = (T - n0 <= W ? T : n0 + W) * G;                // of this wave's keys, from
+                                                                         // wedge some are hidden
         // does this wave's row half of tile j see any of its keys, and does it need the mask
         auto active = [&](int j) {
             const int Rh = rstart + j * BMR + 32 * rh;
-            return min(Rh + 31, TG - 1) >= n0 * G && Rh < TG;
+            return min(Rh + 31, TG - 1) >= n0 * G && Rh < wlim;
         };
         auto needs_mask = [&](int j) {
             const int Rh = rstart + j * BMR + 32 * rh;
-            return Rh < (n0 + 31) * G || Rh + 32 > TG;
+            return Rh < (n0 + 31) * G || Rh + 32 > wedge;
         };
 
         const OP* kvrow = (role == 0 ? kg : vg) + (size_t)key * D;
@@ -1083,7 +1114,7 @@ void dkdv_kernel_h(BwdArgs a) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int row = Rh + acc_row(r, h);
-                            if (row < keyG || row >= TG) x[r] = -INFINITY;
+                            if (row < keyG || row >= keyWG) x[r] = -INFINITY;
                         }
                     }
                     half8 pf[2];
@@ -1186,6 +1217,8 @@ void dq_kernel(BwdArgs a) {
     const int wave_tmin = Rw / G;
     const int wave_tmax = min(Rw + 31, TG - 1) / G;
     const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;
+    const int W = a.window;
+    const int j0 = max(0, R0 / G - W + 1) / BN;  // the block's first key tile
 
     const size_t grp = (size_t)wk.grp;
     const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
@@ -1207,25 +1240,26 @@ void dq_kernel(BwdArgs a) {
     const float L = rvalid ? a.lse2[grp * (size_t)TG + R] : INFINITY;
     const float Dl = rvalid ? a.delta[grp * (size_t)TG + R] : 0.f;
     wait_all();
-    lds_fill<OP, D, BN, NW>(lds, kg, 0, T);
-    lds_fill<OP, D, BN, NW>(lds + TILE, vg, 0, T);
+    lds_fill<OP, D, BN, NW>(lds, kg, j0 * BN, T);
+    lds_fill<OP, D, BN, NW>(lds + TILE, vg, j0 * BN, T);
 
     floatx16 dq[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[db] = floatx16{};
 
-    for (int it = 0; it < ntiles; ++it) {
-        const OP* Ks = lds + (it & 1) * 2 * TILE;
+    for (int it = j0; it < ntiles; ++it) {
+        const OP* Ks = lds + ((it - j0) & 1) * 2 * TILE;
         const OP* Vs = Ks + TILE;
         lds_fill_wait();
         if (it + 1 < ntiles) {
-            OP* nxt = lds + ((it + 1) & 1) * 2 * TILE;
+            OP* nxt = lds + ((it + 1 - j0) & 1) * 2 * TILE;
             lds_fill<OP, D, BN, NW>(nxt, kg, (it + 1) * BN, T);
             lds_fill<OP, D, BN, NW>(nxt + TILE, vg, (it + 1) * BN, T);
         }
         const int n0 = it * BN;
-        if (n0 > wave_tmax) continue;
-        const bool need_mask = n0 + BN - 1 > wave_tmin;
+        if (n0 > wave_tmax) continue;                 // every row of this wave precedes the tile
+        if (wave_tmin - (n0 + BN - 1) >= W) continue;  // the tile is older than every row's window
+        const bool need_mask = n0 + BN - 1 > wave_tmin || wave_tmax - n0 >= W;
 
         floatx16 ds[2];
 #pragma unroll
@@ -1239,7 +1273,7 @@ void dq_kernel(BwdArgs a) {
             if (need_mask) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (n0 + 32 * mb + acc_row(r, h) > t_lane) sacc[r] = -INFINITY;
+                    if (!visible(n0 + 32 * mb + acc_row(r, h), t_lane, W)) sacc[r] = -INFINITY;
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -1298,7 +1332,9 @@ void dq_kernel(BwdArgs a) {
 // chains (S^T and dP^T, two 32-key halves each) advance in turn, and every product's LDS operand
 // is read four products ahead.
 // =====================================================================================
-template <int D, typename TOUT>
+// WIN: a window shorter than T (its edge is masked too).  Without one the kernel keeps every
+// register for the causal case, where the budget is exhausted.
+template <int D, typename TOUT, bool WIN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void dq_kernel_h(BwdArgs a) {
     using OP = _Float16;
@@ -1319,6 +1355,8 @@ void dq_kernel_h(BwdArgs a) {
     const int wave_tmin = Rw / G;
     const int wave_tmax = min(Rw + 31, TG - 1) / G;
     const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;
+    const int W = WIN ? a.window : T;
+    const int j0 = WIN ? max(0, R0 / G - W + 1) / BN : 0;  // the block's first key tile
 
     const size_t grp = (size_t)wk.grp;
     const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
@@ -1338,26 +1376,28 @@ void dq_kernel_h(BwdArgs a) {
     const half8 fd = fold_frag(rvalid ? -a.delta[grp * (size_t)TG + R] : 0.f, h);
     const half8 fw = fold_weights(h);
     wait_all();
-    lds_fill<OP, D, BN, NW>(lds, kg, 0, T);
-    lds_fill<OP, D, BN, NW>(lds + TILE, vg, 0, T);
+    lds_fill<OP, D, BN, NW>(lds, kg, j0 * BN, T);
+    lds_fill<OP, D, BN, NW>(lds + TILE, vg, j0 * BN, T);
 
     floatx16 dq[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[db] = floatx16{};
 
-    for (int it = 0; it < ntiles; ++it) {
-        const OP* Ks = lds + (it & 1) * 2 * TILE;
+    for (int it = j0; it < ntiles; ++it) {
+        const OP* Ks = lds + ((it - j0) & 1) * 2 * TILE;
         const OP* Vs = Ks + TILE;
         lds_fill_wait();
         if (it + 1 < ntiles) {
-            OP* nxt = lds + ((it + 1) & 1) * 2 * TILE;
+            OP* nxt = lds + ((it + 1 - j0) & 1) * 2 * TILE;
             lds_fill<OP, D, BN, NW>(nxt, kg, (it + 1) * BN, T);
             lds_fill<OP, D, BN, NW>(nxt + TILE, vg, (it + 1) * BN, T);
         }
         const int n0 = it * BN;
-        if (n0 > wave_tmax) continue;
+        if (n0 > wave_tmax) continue;                 // every row of this wave precedes the tile
+        if (wave_tmin - (n0 + BN - 1) >= W) continue;  // the tile is older than every row's window
 
-        const bool diag = n0 + BN - 1 > wave_tmin;  // the tile crosses some row's diagonal
+        // the tile crosses some row's diagonal or window edge
+        const bool diag = n0 + BN - 1 > wave_tmin || wave_tmax - n0 >= W;
         // Per 32-key half mb: two chains, S^T - lse2 (even slots) and dP^T - Delta (odd slots),
         // operands read four products ahead, then the ALU work of the half (P, dS and their fp16
         // packing); that of half 1 runs between the first dQ products.  dQ^T += K^T dS^T reads
@@ -1375,8 +1415,10 @@ void dq_kernel_h(BwdArgs a) {
         };
         auto mask = [&](floatx16 (&x)[2], int mb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (n0 + 32 * mb + acc_row(r, h) > t_lane) x[0][r] = -INFINITY;
+            for (int r = 0; r < 16; ++r) {
+                const int key = n0 + 32 * mb + acc_row(r, h);
+                if (WIN ? !visible(key, t_lane, W) : key > t_lane) x[0][r] = -INFINITY;
+            }
         };
         // the chains of half mb into x; with WITH_PREV, half 0's ALU work (from prev) in between
         auto chains = [&](int mb, floatx16 (&x)[2], floatx16 (&prev)[2], auto WITH_PREV) {
@@ -1498,8 +1540,12 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(1));
     NE_TRY(m.before(2));
-    if constexpr (sizeof(OP) == 2)
-        hipLaunchKernelGGL((dq_kernel_h<D, TO>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
+    if constexpr (sizeof(OP) == 2) {
+        if (ba.window < ba.T)
+            hipLaunchKernelGGL((dq_kernel_h<D, TO, true>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
+        else
+            hipLaunchKernelGGL((dq_kernel_h<D, TO, false>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
+    }
     else
         hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
     NE_TRY(hipGetLastError());

@@ -22,6 +22,7 @@ struct FwdArgs {
     const float2* table;                            // cos/sin [T][D/2] (RoPE on)
     void* o; float* lse;
     int B, T, Hq, Hkv, G, nrb;
+    int window;                                     // query t sees keys t - window + 1 .. t (1..T)
     double rope_base;
     float qscale;                                   // softmax scale * log2(e)
 };
@@ -31,6 +32,7 @@ struct BwdArgs {
     const float* delta; const float* lse2; const float2* table;
     void* dq; void* dk; void* dv;
     int B, T, Hq, Hkv, G, nrb;
+    int window;                                     // query t sees keys t - window + 1 .. t (1..T)
     double rope_base;
     float scale;                                    // softmax scale 1/sqrt(D)
 };

@@ -112,6 +112,30 @@ ne_status_t ne_rope_attn_bwd_timed(const void* q, const void* k, const void* v,
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    void* const* events);
 
+/* Sliding-window attention: the same operation with each query seeing only the `window` most
+ * recent keys, its own position included -- query t sees keys t - window + 1 .. t -- as in the
+ * short-window layers of the window_pattern feature ("nanochat 全栈 LLM 训练实践指南", section
+ * 模型架构速览, where a short window is a quarter of the context).  window <= 0, or >= T, is the
+ * full causal prefix and gives the same bits as ne_rope_attn_fwd / ne_rope_attn_bwd.  The backward
+ * must be given the window the forward used (lse depends on it).  Arguments, layouts, workspace
+ * sizes and errors are those of ne_rope_attn_fwd / ne_rope_attn_bwd; `events` is NULL (untimed) or
+ * an array as for the *_timed calls (4 forward, 6 backward). */
+ne_status_t ne_rope_attn_fwd_window(const void* q, const void* k, const void* v,
+                                    void* o, float* lse,
+                                    int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                                    int window,
+                                    ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    void* const* events);
+ne_status_t ne_rope_attn_bwd_window(const void* q, const void* k, const void* v,
+                                    const void* o, const float* lse, const void* dO,
+                                    void* dq, void* dk, void* dv,
+                                    int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                                    int window,
+                                    ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    void* const* events);
+
 const char* ne_status_str(ne_status_t status);
 const char* ne_last_error(void);
 int ne_abi_version(void);

@@ -11,6 +11,10 @@ The whole-step time comes from the host clock around K synchronised steps; insid
 library records HIP events (on the stream it launches on) around the dominant kernel only, whose
 average duration gives the roofline figure.  The per-kernel breakdown comes from a separate
 pass with every launch bracketed.  Prints one JSON line.
+
+After the headline measurement the same step is measured with a sliding window of --window keys
+(default T/4, the short window of the nanochat guide's window_pattern; 0 skips it), counting the
+visible pairs N_W = W(W+1)/2 + (T-W)W per head; it is reported under "sliding_window".
 """
 import argparse
 import hashlib
@@ -126,6 +130,8 @@ def main():
                     help="after timing, run one plain device copy of this many MiB (reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--cpu-sample-batch", type=int, default=4)
+    ap.add_argument("--window", type=int, default=-1,
+                    help="window of the sliding-window measurement (-1: T/4; 0: skip it)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards over "
@@ -152,10 +158,19 @@ def main():
     wsf = binding.alloc_workspace(binding.fwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype), dev)
     wsb = binding.alloc_workspace(binding.bwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype), dev)
 
-    def step(ev_f=None, ev_b=None):
-        binding.ne_rope_attn_fwd(q, k, v, w.rope_base, o=o, lse=lse, workspace=wsf, events=ev_f)
-        binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=wsb,
-                                 events=ev_b)
+    def make_step(window):
+        if window is None:
+            def step(ev_f=None, ev_b=None):
+                binding.ne_rope_attn_fwd(q, k, v, w.rope_base, o=o, lse=lse, workspace=wsf, events=ev_f)
+                binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=wsb,
+                                         events=ev_b)
+        else:
+            def step(ev_f=None, ev_b=None):
+                binding.ne_rope_attn_fwd_window(q, k, v, w.rope_base, window, o=o, lse=lse, workspace=wsf,
+                                                events=ev_f)
+                binding.ne_rope_attn_bwd_window(q, k, v, o, lse, dO, w.rope_base, window, dq=dq, dk=dk, dv=dv,
+                                                workspace=wsb, events=ev_b)
+        return step
 
     hev = _HipEvents()
 
@@ -170,45 +185,51 @@ def main():
 
     slot = {"prep_fwd": ("f", 0), "attn_fwd": ("f", 1), "prep_bwd": ("b", 0), "attn_bwd_dkdv": ("b", 1),
             "attn_bwd_dq": ("b", 2)}
-    # warmup, every launch bracketed: picks the dominant kernel (the longest of the three attention
-    # kernels) that the timed region brackets
-    W = max(args.warmup, 1)
-    evf = [new_events(4) for _ in range(W)]
-    evb = [new_events(6) for _ in range(W)]
-    for i in range(W):
-        step(evf[i], evb[i])
-    torch.cuda.synchronize()
-    warm = per_kernel_ms(evf, evb)
-    dominant = max(["attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"], key=lambda n: warm[n])
 
-    # timed region: K steps; HIP events only around the dominant kernel (each event record costs
-    # stream time, so bracketing every launch would slow the step being measured)
+    def measure(step, warmup, K):
+        """(ms per step, dominant kernel, its average launch ms, per-kernel breakdown)"""
+        # warmup, every launch bracketed: picks the dominant kernel (the longest of the three
+        # attention kernels) that the timed region brackets
+        Wu = max(warmup, 1)
+        evf = [new_events(4) for _ in range(Wu)]
+        evb = [new_events(6) for _ in range(Wu)]
+        for i in range(Wu):
+            step(evf[i], evb[i])
+        torch.cuda.synchronize()
+        warm = per_kernel_ms(evf, evb)
+        dominant = max(["attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"], key=lambda n: warm[n])
+
+        # timed region: K steps; HIP events only around the dominant kernel (each event record
+        # costs stream time, so bracketing every launch would slow the step being measured)
+        side, idx = slot[dominant]
+        tev = [new_events(2) for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            pair = [None] * (4 if side == "f" else 6)
+            pair[2 * idx], pair[2 * idx + 1] = tev[i]
+            if side == "f":
+                step(pair, None)
+            else:
+                step(None, pair)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1e3 / K
+        dom_ms = sum(hev.elapsed_ms(a, b) for a, b in tev) / K
+
+        # per-kernel breakdown from a separate, untimed pass with every launch bracketed
+        Kb = min(K, 10)
+        evf = [new_events(4) for _ in range(Kb)]
+        evb = [new_events(6) for _ in range(Kb)]
+        torch.cuda.synchronize()
+        for i in range(Kb):
+            step(evf[i], evb[i])
+        torch.cuda.synchronize()
+        return ms_per_step, dominant, dom_ms, per_kernel_ms(evf, evb)
+
     K = args.steps
-    side, idx = slot[dominant]
-    tev = [new_events(2) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        pair = [None] * (4 if side == "f" else 6)
-        pair[2 * idx], pair[2 * idx + 1] = tev[i]
-        if side == "f":
-            step(pair, None)
-        else:
-            step(None, pair)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-    dom_ms = sum(hev.elapsed_ms(a, b) for a, b in tev) / K
-
-    # per-kernel breakdown from a separate, untimed pass with every launch bracketed
     Kb = min(K, 10)
-    evf = [new_events(4) for _ in range(Kb)]
-    evb = [new_events(6) for _ in range(Kb)]
-    torch.cuda.synchronize()
-    for i in range(Kb):
-        step(evf[i], evb[i])
-    torch.cuda.synchronize()
-    kern_ms = per_kernel_ms(evf, evb)
+    ms_per_step, dominant, dom_ms, kern_ms = measure(make_step(None), args.warmup, K)
 
     N = T * (T + 1) / 2
     unit = B * Hq * D * N
@@ -248,6 +269,22 @@ def main():
                      "flops_per_launch": kern_flops[dominant], "launch_ms": round(dom_ms, 4),
                      "launch_ms_source": "HIP events around this kernel in every timed step"},
     }
+    Wn = T // 4 if args.window < 0 else args.window
+    if 0 < Wn < T:
+        # sliding window: the same step, counting the visible pairs only
+        ms_w, dom_w, dom_ms_w, kern_w = measure(make_step(Wn), 20, K)
+        unit_w = B * Hq * D * (Wn * (Wn + 1) / 2 + (T - Wn) * Wn)
+        kf_w = {"attn_fwd": 4.0 * unit_w, "attn_bwd_dkdv": 8.0 * unit_w, "attn_bwd_dq": 6.0 * unit_w}
+        ach_w = kf_w[dom_w] / (dom_ms_w * 1e-3) / 1e12
+        result["sliding_window"] = {
+            "window": Wn, "pairs_per_head": Wn * (Wn + 1) // 2 + (T - Wn) * Wn,
+            "value": round(14.0 * unit_w / (ms_w * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(ms_w, 4), "steps": K, "warmup": 20,
+            "kernel_ms": {n: round(t, 4) for n, t in kern_w.items()},
+            "roofline": {"kernel": dom_w, "bound": "mfma", "achieved": round(ach_w, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(ach_w / peak, 4), "traffic": None,
+                         "flops_per_launch": kf_w[dom_w], "launch_ms": round(dom_ms_w, 4)},
+        }
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

@@ -12,6 +12,7 @@ import ctypes
 import numpy as np
 
 from . import build as _build
+from .decode import decode_fwd, rope_rows  # noqa: F401  (numpy oracle of the cached-decode workload)
 
 _lib = None
 

@@ -21,6 +21,8 @@ STATUS = {0: "NE_OK", 1: "NE_ERR_NULL", 2: "NE_ERR_SHAPE", 3: "NE_ERR_UNSUPPORTE
 EXPORTS = ("ne_rope_attn_fwd_workspace_bytes", "ne_rope_attn_bwd_workspace_bytes",
            "ne_rope_attn_fwd", "ne_rope_attn_bwd", "ne_rope_attn_fwd_timed", "ne_rope_attn_bwd_timed",
            "ne_rope_attn_fwd_window", "ne_rope_attn_bwd_window",
+           "ne_kv_cache_bytes", "ne_kv_cache_append", "ne_rope_attn_decode_workspace_bytes",
+           "ne_rope_attn_decode",
            "ne_status_str", "ne_last_error", "ne_abi_version")
 
 
@@ -61,6 +63,15 @@ def lib():
     L.ne_rope_attn_bwd_window.argtypes = ([vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, i, vp, sz, vp]
                                           + [ctypes.POINTER(vp)])
     L.ne_rope_attn_bwd_window.restype = i
+    L.ne_kv_cache_bytes.argtypes = [i, i, i, i, i]
+    L.ne_kv_cache_bytes.restype = sz
+    L.ne_kv_cache_append.argtypes = [vp, sz, vp, vp, vp, i, i, i, i, i, d, i, vp]
+    L.ne_kv_cache_append.restype = i
+    L.ne_rope_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.ne_rope_attn_decode_workspace_bytes.restype = sz
+    L.ne_rope_attn_decode.argtypes = ([vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, d, i, i, i, vp, sz, vp]
+                                      + [ctypes.POINTER(vp)])
+    L.ne_rope_attn_decode.restype = i
     L.ne_status_str.argtypes = [i]
     L.ne_status_str.restype = ctypes.c_char_p
     L.ne_last_error.argtypes = []
@@ -206,3 +217,63 @@ def _bwd(q, k, v, o, lse, dO, rope_base, window, dq, dk, dv, workspace, events):
     else:
         _check(lib().ne_rope_attn_bwd_timed(*args, ev))
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------------------------
+# Key/value cache: decode and chunked prefill.
+# ---------------------------------------------------------------------------------------------
+def kv_cache_bytes(B, Tcap, Hkv, D, in_dtype):
+    return int(lib().ne_kv_cache_bytes(B, Tcap, Hkv, D, _DT[in_dtype]))
+
+
+def new_kv_cache(B, Tcap, Hkv, D, in_dtype, device):
+    """A zeroed cache buffer (uint8) in the library's layout."""
+    n = kv_cache_bytes(B, Tcap, Hkv, D, in_dtype)
+    if n == 0:
+        raise ValueError("invalid cache shape")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def _lens_arg(lens, B, device):
+    if isinstance(lens, torch.Tensor):
+        if lens.dtype != torch.int32 or not lens.is_cuda or lens.numel() != B:
+            raise ValueError("cache_lens must be a device int32 tensor of B entries")
+        return lens
+    return torch.tensor(list(lens), dtype=torch.int32, device=device)
+
+
+def ne_kv_cache_append(cache, cache_lens, k_new, v_new, Tcap, rope_base):
+    """Write k_new, v_new [B, Tn, Hkv, D] at positions cache_lens[b] .. of the cache."""
+    _require_gpu(cache, k_new, v_new)
+    B, Tn, Hkv, D = k_new.shape
+    lens = _lens_arg(cache_lens, B, k_new.device)
+    _check(lib().ne_kv_cache_append(_ptr(cache), cache.numel() * cache.element_size(), _ptr(lens), _ptr(k_new),
+                                    _ptr(v_new), B, Tn, Tcap, Hkv, D, float(rope_base), _DT[k_new.dtype],
+                                    _stream()))
+    return lens
+
+
+def decode_workspace_bytes(B, Tq, Tcap, Hq, Hkv, D, in_dtype):
+    return int(lib().ne_rope_attn_decode_workspace_bytes(B, Tq, Tcap, Hq, Hkv, D, _DT[in_dtype]))
+
+
+def ne_rope_attn_decode(q, cache, cache_lens, Tcap, Hkv, rope_base, window=0, out_dtype=torch.float32,
+                        o=None, lse=None, workspace=None, events=None):
+    """o, lse for the queries q [B, Tq, Hq, D] at positions cache_lens[b] + t against the cache.
+
+    events: optional 6 events (or None entries) around the three launches."""
+    _require_gpu(q, cache)
+    B, Tq, Hq, D = q.shape
+    lens = _lens_arg(cache_lens, B, q.device)
+    if o is None:
+        o = torch.empty((B, Tq, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(decode_workspace_bytes(B, Tq, Tcap, Hq, Hkv, D, q.dtype), q.device)
+    _check(lib().ne_rope_attn_decode(_ptr(q), _ptr(cache), cache.numel() * cache.element_size(), _ptr(lens),
+                                     _ptr(o), _ptr(lse), B, Tq, Tcap, Hq, Hkv, D, float(rope_base), int(window),
+                                     _DT[q.dtype], _DT[o.dtype], _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(),
+                                     _events_arg(events, 6)))
+    return o, lse

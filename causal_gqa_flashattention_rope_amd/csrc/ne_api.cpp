@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -255,6 +256,143 @@ ne_status_t ne_rope_attn_bwd_window(const void* q, const void* k, const void* v,
                                     void* const* events) {
     return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, window, in_dtype,
                     out_dtype, workspace, workspace_bytes, stream, events);
+}
+
+}  // extern "C"
+
+// =====================================================================================
+// Key/value cache and decode.
+// =====================================================================================
+namespace {
+
+bool decode_dtype_ok(ne_dtype_t in, ne_dtype_t out) {
+    if (in == NE_BF16) return out == NE_F32 || out == NE_BF16;
+    if (in == NE_F16) return out == NE_F32 || out == NE_F16;
+    return false;
+}
+
+ne_status_t check_cache_shape(int B, int Tcap, int Hkv, int D) {
+    if (B < 1 || Hkv < 1 || Tcap < 64) return fail(NE_ERR_SHAPE, "B=%d Hkv=%d must be >= 1 and Tcap=%d >= 64", B, Hkv, Tcap);
+    if (Tcap % 64 != 0) return fail(NE_ERR_SHAPE, "Tcap=%d must be a multiple of 64", Tcap);
+    if (D != 32 && D != 64 && D != 128) return fail(NE_ERR_UNSUPPORTED, "head_dim=%d not in {32, 64, 128}", D);
+    if (B > 65535 || Hkv > 65535) return fail(NE_ERR_SHAPE, "B and Hkv must be <= 65535");
+    if ((int64_t)B * Hkv * Tcap * D > ((int64_t)1 << 44)) return fail(NE_ERR_SHAPE, "cache is too large");
+    return NE_OK;
+}
+
+// Key slices per (group, 32-row block): about four workgroups per CU overall, and no more than one
+// slice per 256 keys of the cache's capacity.
+int decode_nsplit(int B, int Hkv, int nrb, int Tcap) {
+    const int64_t blocks = (int64_t)B * Hkv * nrb;
+    int64_t ns = (1024 + blocks - 1) / blocks;
+    ns = std::min<int64_t>(ns, std::max(1, Tcap / 256));
+    return (int)std::max<int64_t>(ns, 1);
+}
+
+struct DecodeLayout {
+    size_t qh, part_o, part_ml, total;
+    int nrb, nsplit;
+};
+
+DecodeLayout decode_layout(int B, int Tq, int Tcap, int Hq, int Hkv, int D) {
+    DecodeLayout L{};
+    const int G = Hq / Hkv;
+    L.nrb = (int)(((int64_t)Tq * G + 31) / 32);
+    L.nsplit = decode_nsplit(B, Hkv, L.nrb, Tcap);
+    const size_t slots = (size_t)B * Hkv * L.nrb * L.nsplit;
+    size_t off = 0;
+    L.qh = off; off += up((size_t)B * Tq * Hq * D * 2);
+    L.part_o = off; off += up(slots * 32 * D * 4);
+    L.part_ml = off; off += up(slots * 64 * 4);
+    L.total = off;
+    return L;
+}
+
+ne_status_t check_decode(int B, int Tq, int Tcap, int Hq, int Hkv, int D) {
+    ne_status_t s = check_cache_shape(B, Tcap, Hkv, D);
+    if (s != NE_OK) return s;
+    if (Hq < 1 || Hq % Hkv != 0) return fail(NE_ERR_SHAPE, "Hq=%d is not a positive multiple of Hkv=%d", Hq, Hkv);
+    if (Tq < 1 || Tq > Tcap) return fail(NE_ERR_SHAPE, "Tq=%d must be in [1, Tcap=%d]", Tq, Tcap);
+    if ((int64_t)Tq * (Hq / Hkv) > (1 << 24)) return fail(NE_ERR_SHAPE, "Tq * Hq / Hkv is too large");
+    return NE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ne_kv_cache_bytes(int B, int Tcap, int Hkv, int head_dim, ne_dtype_t in_dtype) {
+    if (check_cache_shape(B, Tcap, Hkv, head_dim) != NE_OK) return 0;
+    if (in_dtype != NE_BF16 && in_dtype != NE_F16) return 0;
+    return 2 * (size_t)B * Hkv * Tcap * head_dim * 2;
+}
+
+ne_status_t ne_kv_cache_append(void* cache, size_t cache_bytes, const int* cache_lens, const void* k_new,
+                               const void* v_new, int B, int Tn, int Tcap, int Hkv, int head_dim, double rope_base,
+                               ne_dtype_t in_dtype, void* stream) {
+    if (!cache || !cache_lens || !k_new || !v_new)
+        return fail(NE_ERR_NULL, "ne_kv_cache_append: cache, cache_lens, k_new and v_new must be non-null");
+    ne_status_t s = check_cache_shape(B, Tcap, Hkv, head_dim);
+    if (s != NE_OK) return s;
+    if (in_dtype != NE_BF16 && in_dtype != NE_F16)
+        return fail(NE_ERR_UNSUPPORTED, "ne_kv_cache_append: in_dtype must be BF16 or F16");
+    if (Tn < 1 || Tn > Tcap) return fail(NE_ERR_SHAPE, "Tn=%d must be in [1, Tcap=%d]", Tn, Tcap);
+    if (!aligned16(cache) || !aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)cache_lens & 3u))
+        return fail(NE_ERR_ALIGN, "ne_kv_cache_append: cache, k_new, v_new must be 16-byte aligned, cache_lens 4");
+    if (!std::isfinite(rope_base)) return fail(NE_ERR_SHAPE, "rope_base must be finite");
+    if (cache_bytes < ne_kv_cache_bytes(B, Tcap, Hkv, head_dim, in_dtype))
+        return fail(NE_ERR_WORKSPACE, "cache of %zu bytes < %zu required", cache_bytes,
+                    ne_kv_cache_bytes(B, Tcap, Hkv, head_dim, in_dtype));
+    ne::AppendArgs a{};
+    a.k = k_new; a.v = v_new; a.cache = cache; a.lens = cache_lens;
+    a.B = B; a.Tn = Tn; a.Tcap = Tcap; a.Hkv = Hkv; a.rope_base = rope_base;
+    hipError_t e = ne::launch_append((int)in_dtype, head_dim, a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_kv_cache_append: launch failed: %s", hipGetErrorString(e));
+    return NE_OK;
+}
+
+size_t ne_rope_attn_decode_workspace_bytes(int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
+                                           ne_dtype_t in_dtype) {
+    if (check_decode(B, Tq, Tcap, Hq, Hkv, head_dim) != NE_OK) return 0;
+    if (in_dtype != NE_BF16 && in_dtype != NE_F16) return 0;
+    return decode_layout(B, Tq, Tcap, Hq, Hkv, head_dim).total;
+}
+
+ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_bytes, const int* cache_lens,
+                                void* o, float* lse, int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
+                                double rope_base, int window, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    if (!q || !cache || !cache_lens || !o || !lse || !workspace)
+        return fail(NE_ERR_NULL, "ne_rope_attn_decode: q, cache, cache_lens, o, lse and workspace must be non-null");
+    ne_status_t s = check_decode(B, Tq, Tcap, Hq, Hkv, head_dim);
+    if (s != NE_OK) return s;
+    if (!decode_dtype_ok(in_dtype, out_dtype))
+        return fail(NE_ERR_UNSUPPORTED, "ne_rope_attn_decode: dtype pair in=%d out=%d is not supported",
+                    (int)in_dtype, (int)out_dtype);
+    if (!aligned16(q) || !aligned16(cache) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace) ||
+        ((uintptr_t)cache_lens & 3u))
+        return fail(NE_ERR_ALIGN, "ne_rope_attn_decode: pointers must be 16-byte aligned (cache_lens 4)");
+    if (!std::isfinite(rope_base)) return fail(NE_ERR_SHAPE, "rope_base must be finite");
+    if (cache_bytes < ne_kv_cache_bytes(B, Tcap, Hkv, head_dim, in_dtype))
+        return fail(NE_ERR_WORKSPACE, "cache of %zu bytes < %zu required", cache_bytes,
+                    ne_kv_cache_bytes(B, Tcap, Hkv, head_dim, in_dtype));
+    const DecodeLayout L = decode_layout(B, Tq, Tcap, Hq, Hkv, head_dim);
+    if (workspace_bytes < L.total)
+        return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
+    char* ws = (char*)workspace;
+    ne::DecodeArgs a{};
+    a.q = q; a.cache = cache; a.lens = cache_lens;
+    a.qh = ws + L.qh; a.part_o = (float*)(ws + L.part_o); a.part_ml = (float*)(ws + L.part_ml);
+    a.o = o; a.lse = lse;
+    a.B = B; a.Tq = Tq; a.Tcap = Tcap; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+    a.nrb = L.nrb; a.nsplit = L.nsplit;
+    a.window = visible_keys(window, Tcap);
+    a.rope_base = rope_base;
+    a.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    hipError_t e = ne::launch_decode((int)in_dtype, (int)out_dtype, head_dim, a, (hipStream_t)stream,
+                                     (hipEvent_t const*)events);
+    if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_attn_decode: launch failed: %s", hipGetErrorString(e));
+    return NE_OK;
 }
 
 }  // extern "C"

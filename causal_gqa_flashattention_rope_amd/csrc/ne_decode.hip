@@ -1,0 +1,392 @@
+// ne_decode.hip -- attention of a few new tokens against a key/value cache (decode and chunked
+// prefill), 16-bit operands, gfx950.
+//
+// The cache (one caller-owned buffer, ne_kv_cache_bytes) holds, per (batch, KV head) group g:
+//   K'  [g][Tcap][D]  fp16(R_p(k)): each key rotated once, at its own absolute position p
+//   V'^T[g][D][Tcap]  fp16(v) transposed, the keys of every aligned group of 16 in the order
+//                     0-3, 8-11, 4-7, 12-15 (vt_key_of_pos)
+// so that, for a 32-key tile, both MFMA operands of a lane are single 16-byte global loads:
+// K' rows for S^T = K' Q~^T (lane c: key c, 8 consecutive d) and V'^T rows for O^T = V'^T P^T
+// (lane c: d = c, 8 consecutive keys in the order the S^T accumulator hands P over).
+//
+// Decode is bound by reading the cache, which no two workgroups share, so the kernels stream it
+// from HBM straight into registers (no LDS staging) and spread every group's keys over many
+// workgroups (split-KV); a second kernel merges the partial results by the log-sum-exp rule.
+#include <hip/hip_runtime.h>
+
+#include "ne_common.hpp"
+#include "ne_launch.hpp"
+
+namespace ne {
+
+namespace {
+
+// theta_i = base^(-2i/D) for the D/2 rotary pairs, in double precision (into LDS).
+template <int D>
+__device__ __forceinline__ void rope_theta(double* theta, double base) {
+    for (int i = threadIdx.x; i < D / 2; i += blockDim.x)
+        theta[i] = exp2(-2.0 * (double)i / (double)D * log2(base));
+}
+
+// cos and sin of p * theta: the phase is formed and reduced to [-pi, pi] in double precision
+// (two-term 2 pi), so the single-precision sincos sees a small argument at any position.
+__device__ __forceinline__ float2 rope_cs(int p, double theta) {
+    constexpr double kTwoPiHi = 6.283185307179586;
+    constexpr double kTwoPiLo = 2.4492935982947064e-16;
+    constexpr double kInvTwoPi = 0.15915494309189535;
+    const double phi = (double)p * theta;
+    const double n = rint(phi * kInvTwoPi);
+    const double r = fma(-n, kTwoPiLo, fma(-n, kTwoPiHi, phi));
+    float s, c;
+    sincosf((float)r, &s, &c);
+    return make_float2(c, s);
+}
+
+template <typename TI>
+__device__ __forceinline__ void load8_in(const TI* p, float (&x)[8]) {
+    typedef TI v8 __attribute__((ext_vector_type(8)));
+    const v8 a = *reinterpret_cast<const v8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+}
+
+// Tokens already in the cache, clamped so that the n new ones fit: [0, Tcap - n].
+__device__ __forceinline__ int cache_len(const int* lens, int b, int n, int Tcap) {
+    return min(max(lens[b], 0), Tcap - n);
+}
+
+}  // namespace
+
+// =====================================================================================
+// Append: tokens i < Tn of k_new / v_new go to positions len_b + i of their group.
+// grid (ceil(Tn / 16), B * Hkv), 256 threads.  Keys: one thread per (token, 8-element chunk),
+// rotated in fp32 with the cos/sin of the absolute position, one 16-byte store.  Values: staged
+// through LDS and written transposed, 16 consecutive tokens of one d per 16 lanes.
+// =====================================================================================
+template <typename TI, int D>
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
+    constexpr int TB = 16, CPR = D / 8;
+    __shared__ double theta[D / 2];
+    __shared__ float vs[TB][D + 1];
+    const int grp = blockIdx.y, b = grp / a.Hkv, hkv = grp % a.Hkv;
+    const int t0 = blockIdx.x * TB, Tn = a.Tn, Tcap = a.Tcap;
+    const int len = cache_len(a.lens, b, Tn, Tcap);
+    const bool rope = a.rope_base > 0.0;
+    if (rope) rope_theta<D>(theta, a.rope_base);
+    __syncthreads();
+    _Float16* kc = (_Float16*)a.cache + (size_t)grp * Tcap * D;
+    _Float16* vtc = (_Float16*)a.cache + (size_t)a.B * a.Hkv * Tcap * D + (size_t)grp * D * Tcap;
+    for (int idx = threadIdx.x; idx < TB * CPR; idx += 256) {
+        const int tl = idx / CPR, chunk = idx % CPR, t = t0 + tl;
+        if (t >= Tn) continue;
+        const size_t in_off = (((size_t)b * Tn + t) * a.Hkv + hkv) * D + chunk * 8;
+        const int p = len + t;
+        float x[8];
+        load8_in((const TI*)a.k + in_off, x);
+        if (rope) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float2 r = rope_cs(p, theta[chunk * 4 + q]);
+                const float u = x[2 * q], v = x[2 * q + 1];
+                x[2 * q] = u * r.x - v * r.y;
+                x[2 * q + 1] = u * r.y + v * r.x;
+            }
+        }
+        half8 out;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = (_Float16)x[e];
+        *reinterpret_cast<half8*>(kc + (size_t)p * D + chunk * 8) = out;
+        float y[8];
+        load8_in((const TI*)a.v + in_off, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vs[tl][chunk * 8 + e] = y[e];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < TB * D; idx += 256) {
+        const int tl = idx % TB, d = idx / TB, t = t0 + tl;
+        if (t >= Tn) continue;
+        const int p = len + t;
+        const int slot = (p & ~15) + vt_key_of_pos(p & 15);  // the order is its own inverse
+        vtc[(size_t)d * Tcap + slot] = (_Float16)vs[tl][d];
+    }
+}
+
+// =====================================================================================
+// Query preparation: q~ = fp16(R_p(q) * scale * log2 e) at p = len_b + t, as flattened rows
+// [group][t * G + hh][D] (the row order of one token's heads).  grid (Tq, B), 256 threads.
+// =====================================================================================
+template <typename TI, int D>
+__global__ __launch_bounds__(256) void decode_prep_q(DecodeArgs a) {
+    constexpr int CPR = D / 8;
+    __shared__ double theta[D / 2];
+    const int t = blockIdx.x, b = blockIdx.y;
+    const int Tq = a.Tq, Hq = a.Hq, G = a.G;
+    const int p = cache_len(a.lens, b, Tq, a.Tcap) + t;
+    const bool rope = a.rope_base > 0.0;
+    if (rope) rope_theta<D>(theta, a.rope_base);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < Hq * CPR; idx += 256) {
+        const int hq = idx / CPR, chunk = idx % CPR, g = hq / G, hh = hq % G;
+        float x[8];
+        load8_in((const TI*)a.q + (((size_t)b * Tq + t) * Hq + hq) * D + chunk * 8, x);
+        if (rope) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float2 r = rope_cs(p, theta[chunk * 4 + q]);
+                const float u = x[2 * q], v = x[2 * q + 1];
+                x[2 * q] = u * r.x - v * r.y;
+                x[2 * q + 1] = u * r.y + v * r.x;
+            }
+        }
+        half8 out;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = (_Float16)(x[e] * a.qscale);
+        const size_t row = ((size_t)b * a.Hkv + g) * ((size_t)Tq * G) + (size_t)t * G + hh;
+        *reinterpret_cast<half8*>((_Float16*)a.qh + row * D + chunk * 8) = out;
+    }
+}
+
+// =====================================================================================
+// Split-KV attention.  grid (nsplit * nrb * B * Hkv), 256 threads = 4 waves; a workgroup takes
+// one block of 32 flattened query rows of one group and one of nsplit equal slices of the key
+// range those rows see ([first key of the window of its first row, rounded down to 32], last
+// row's position]); its 4 waves take the slice's 32-key tiles in turn.  Per tile a wave loads
+// its K' and V'^T fragments from HBM into registers, computes S^T = K' Q~^T (keys on lanes,
+// one query row per lane column), masks (causal, window, cache end), updates its running max and
+// sum (log2 units), and adds V'^T P^T.  The waves merge in LDS in a fixed order and the
+// workgroup writes its partial (unnormalised O over its keys, max m, sum l) for the valid rows.
+// =====================================================================================
+template <int D>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+    using M = Mma<_Float16>;
+    constexpr int KS = D / 16, NDB = D / 32, NWV = 4;
+    __shared__ float so[32][D + 4];
+    __shared__ float sm[NWV][32];
+    __shared__ float sl[NWV][32];
+    const int nsplit = a.nsplit, nrb = a.nrb;
+    const int s = blockIdx.x % nsplit, rb = (blockIdx.x / nsplit) % nrb, g = blockIdx.x / (nsplit * nrb);
+    const int b = g / a.Hkv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int Tq = a.Tq, G = a.G, TqG = Tq * G, Tcap = a.Tcap, W = a.window;
+    const int len = cache_len(a.lens, b, Tq, Tcap), L = len + Tq;
+
+    const int R0 = rb * 32, R = R0 + c;
+    const bool rvalid = R < TqG;
+    const int p_lane = len + min(R, TqG - 1) / G;                 // this lane's query position
+    const int p_min = len + R0 / G, p_max = len + min(R0 + 31, TqG - 1) / G;
+    const int Kb = max(0, p_min - W + 1) & ~31, Ke = p_max + 1;    // key range of the row block
+    const int CH = ((Ke - Kb + nsplit - 1) / nsplit + 31) & ~31;  // keys per split
+    const int k0 = Kb + s * CH, k1 = min(Ke, k0 + CH);
+
+    const _Float16* kc = (const _Float16*)a.cache + (size_t)g * Tcap * D;
+    const _Float16* vtc = (const _Float16*)a.cache + (size_t)a.B * a.Hkv * Tcap * D + (size_t)g * D * Tcap;
+
+    half8 qf[KS];
+    {
+        const _Float16* qrow = (const _Float16*)a.qh + ((size_t)g * TqG + min(R, TqG - 1)) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = rvalid ? M::row_frag(qrow, ks, h, D) : half8{};
+    }
+    floatx16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
+    float m_run = kMFloor, l_run = 0.f;
+
+    for (int k = k0 + 32 * w; k < k1; k += 32 * NWV) {
+        // k is a multiple of 32 below k1 <= Tcap (a multiple of 64), so keys k .. k + 31 are in
+        // the cache; keys at or past L hold stale or unwritten data and are masked (V zeroed)
+        half8 kf[KS], vf[2][NDB];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const half8*>(kc + (size_t)(k + c) * D + 16 * ks + 8 * h);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                vf[kk][db] = *reinterpret_cast<const half8*>(vtc + (size_t)(32 * db + c) * Tcap + k + 16 * kk + 8 * h);
+        floatx16 sc = floatx16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sc = M::mma(kf[ks], qf[ks], sc);
+        if (k + 31 >= L) {  // the cache ends inside this tile
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (k + 16 * kk + vt_key_of_pos(8 * h + j) >= L)
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) vf[kk][db][j] = (_Float16)0.f;
+        }
+        float mx = kMFloor;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (!visible(k + acc_row(r, h), p_lane, W)) sc[r] = -INFINITY;
+            mx = fmaxf(mx, sc[r]);
+        }
+        mx = max_halves(mx);
+        if (mx > m_run) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = mx;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            sc[r] = __builtin_amdgcn_exp2f(sc[r] - m_run);
+            l_run += sc[r];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const half8 pf = pack_frag_f16(sc, kk);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] = M::mma(vf[kk][db], pf, oacc[db]);
+        }
+    }
+    l_run = sum_halves(l_run);
+
+    // merge the four waves: common max, then O and l added in wave order
+    if (h == 0) {
+        sm[w][c] = m_run;
+        sl[w][c] = l_run;
+    }
+    __syncthreads();
+    float mall = sm[0][c];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) mall = fmaxf(mall, sm[i][c]);
+    const float f = __builtin_amdgcn_exp2f(m_run - mall);  // 1 when both are the floor
+    for (int i = 0; i < NWV; ++i) {
+        if (w == i) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float* dst = &so[c][32 * db + acc_row(r, h)];
+                    *dst = (i == 0 ? 0.f : *dst) + oacc[db][r] * f;
+                }
+        }
+        __syncthreads();
+    }
+    // partials of the valid rows: O [row][D], then (m, l) per row
+    const int nvalid = min(32, TqG - R0);
+    const size_t slot = ((size_t)g * nrb + rb) * nsplit + s;
+    float* po = a.part_o + slot * 32 * D;
+    for (int idx = tid; idx < nvalid * (D / 4); idx += 256) {
+        const int row = idx / (D / 4), q4 = idx % (D / 4);
+        *reinterpret_cast<floatx4*>(po + row * D + 4 * q4) =
+            floatx4{so[row][4 * q4], so[row][4 * q4 + 1], so[row][4 * q4 + 2], so[row][4 * q4 + 3]};
+    }
+    if (tid < nvalid) {
+        float mt = sm[0][tid];
+        for (int i = 1; i < NWV; ++i) mt = fmaxf(mt, sm[i][tid]);
+        float lsum = 0.f;
+        for (int i = 0; i < NWV; ++i) lsum += sl[i][tid] * __builtin_amdgcn_exp2f(sm[i][tid] - mt);
+        a.part_ml[slot * 64 + tid] = mt;
+        a.part_ml[slot * 64 + 32 + tid] = lsum;
+    }
+}
+
+// =====================================================================================
+// Merge of the nsplit partials of every valid row: m = max m_s, l = sum l_s 2^(m_s - m),
+// o = sum O_s 2^(m_s - m) / l, lse = ln 2 (m + log2 l).  grid (nrb * B * Hkv), 256 threads, one
+// thread per (row, 4 consecutive d); splits are added in index order.
+// =====================================================================================
+template <int D, typename TOUT>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+    const int nsplit = a.nsplit, nrb = a.nrb;
+    const int rb = blockIdx.x % nrb, g = blockIdx.x / nrb;
+    const int b = g / a.Hkv, hkv = g % a.Hkv;
+    const int Tq = a.Tq, G = a.G, TqG = Tq * G;
+    const int R0 = rb * 32, nvalid = min(32, TqG - R0);
+    const size_t slot0 = ((size_t)g * nrb + rb) * nsplit;
+    for (int idx = threadIdx.x; idx < nvalid * (D / 4); idx += 256) {
+        const int row = idx / (D / 4), q4 = idx % (D / 4);
+        float m = kMFloor;
+        for (int s = 0; s < nsplit; ++s) m = fmaxf(m, a.part_ml[(slot0 + s) * 64 + row]);
+        float lsum = 0.f;
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < nsplit; ++s) {
+            const float f = __builtin_amdgcn_exp2f(a.part_ml[(slot0 + s) * 64 + row] - m);
+            lsum += a.part_ml[(slot0 + s) * 64 + 32 + row] * f;
+            const floatx4 x = *reinterpret_cast<const floatx4*>(a.part_o + ((slot0 + s) * 32 + row) * D + 4 * q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += x[e] * f;
+        }
+        const float inv = 1.f / lsum;
+        const int R = R0 + row, t = R / G, hq = hkv * G + (R - t * G);
+        store4((TOUT*)a.o + (((size_t)b * Tq + t) * a.Hq + hq) * D + 4 * q4, acc[0] * inv, acc[1] * inv,
+               acc[2] * inv, acc[3] * inv);
+        if (q4 == 0) a.lse[((size_t)b * a.Hq + hq) * Tq + t] = (m + __log2f(lsum)) * kLn2;
+    }
+}
+
+// =====================================================================================
+// Launchers.
+// =====================================================================================
+namespace {
+struct DMarks {
+    hipEvent_t const* ev;
+    hipStream_t s;
+    hipError_t rec(int j) const { return ev && ev[j] ? hipEventRecord(ev[j], s) : hipSuccess; }
+};
+#define NE_DTRY(x)                            \
+    do {                                      \
+        hipError_t e_ = (x);                  \
+        if (e_ != hipSuccess) return e_;      \
+    } while (0)
+
+template <typename TI, typename TO, int D>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t const* ev) {
+    const DMarks m{ev, s};
+    NE_DTRY(m.rec(0));
+    hipLaunchKernelGGL((decode_prep_q<TI, D>), dim3(a.Tq, a.B), dim3(256), 0, s, a);
+    NE_DTRY(hipGetLastError());
+    NE_DTRY(m.rec(1));
+    NE_DTRY(m.rec(2));
+    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(a.nsplit * a.nrb * a.B * a.Hkv), dim3(256), 0, s, a);
+    NE_DTRY(hipGetLastError());
+    NE_DTRY(m.rec(3));
+    NE_DTRY(m.rec(4));
+    hipLaunchKernelGGL((decode_combine_kernel<D, TO>), dim3(a.nrb * a.B * a.Hkv), dim3(256), 0, s, a);
+    NE_DTRY(hipGetLastError());
+    return m.rec(5);
+}
+
+template <typename TI, int D>
+hipError_t launch_append_t(const AppendArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((kv_append_kernel<TI, D>), dim3((a.Tn + 15) / 16, a.B * a.Hkv), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+}  // namespace
+
+#define NE_DDISPATCH(FN, ...)                                  \
+    switch (D) {                                               \
+        case 32: return FN<__VA_ARGS__, 32>(a, s);             \
+        case 64: return FN<__VA_ARGS__, 64>(a, s);             \
+        case 128: return FN<__VA_ARGS__, 128>(a, s);           \
+        default: return hipErrorInvalidValue;                  \
+    }
+
+hipError_t launch_append(int in_dt, int D, const AppendArgs& a, hipStream_t s) {
+    if (in_dt == 1) { NE_DDISPATCH(launch_append_t, __bf16) }
+    if (in_dt == 2) { NE_DDISPATCH(launch_append_t, _Float16) }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(int in_dt, int out_dt, int D, const DecodeArgs& a, hipStream_t s, hipEvent_t const* ev) {
+#define NE_DCASE(TI, TO)                                                   \
+    switch (D) {                                                           \
+        case 32: return launch_decode_t<TI, TO, 32>(a, s, ev);             \
+        case 64: return launch_decode_t<TI, TO, 64>(a, s, ev);             \
+        case 128: return launch_decode_t<TI, TO, 128>(a, s, ev);           \
+        default: return hipErrorInvalidValue;                              \
+    }
+    if (in_dt == 1 && out_dt == 0) { NE_DCASE(__bf16, float) }
+    if (in_dt == 1 && out_dt == 1) { NE_DCASE(__bf16, __bf16) }
+    if (in_dt == 2 && out_dt == 0) { NE_DCASE(_Float16, float) }
+    if (in_dt == 2 && out_dt == 2) { NE_DCASE(_Float16, _Float16) }
+#undef NE_DCASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ne

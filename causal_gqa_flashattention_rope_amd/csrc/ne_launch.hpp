@@ -37,6 +37,27 @@ struct BwdArgs {
     float scale;                                    // softmax scale 1/sqrt(D)
 };
 
+// Cache append (decode path): k_new / v_new [B][Tn][Hkv][D] into the cache at positions
+// lens[b] + i (clamped to fit).
+struct AppendArgs {
+    const void* k; const void* v;
+    void* cache; const int* lens;
+    int B, Tn, Tcap, Hkv;
+    double rope_base;
+};
+
+// Decode / chunked prefill: Tq new queries per sequence at positions lens[b] + t against the cache.
+struct DecodeArgs {
+    const void* q; const void* cache; const int* lens;
+    void* qh;                                       // q~ rows [B * Hkv][Tq * G][D] fp16
+    float* part_o; float* part_ml;                  // split partials
+    void* o; float* lse;
+    int B, Tq, Tcap, Hq, Hkv, G, nrb, nsplit;
+    int window;                                     // 1..Tcap (Tcap: no window)
+    double rope_base;
+    float qscale;                                   // softmax scale * log2(e)
+};
+
 // dtype codes follow ne_dtype_t: 0 = f32, 1 = bf16, 2 = f16.
 // ev (nullable): hipEvent_t pairs recorded on `s` around each kernel launch, in launch order
 // (forward: prep, fwd; backward: prep, dkdv, dq).
@@ -44,5 +65,8 @@ hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const Fw
                       hipEvent_t const* ev);
 hipError_t launch_bwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const BwdArgs& ba, hipStream_t s,
                       hipEvent_t const* ev);
+hipError_t launch_append(int in_dt, int D, const AppendArgs& a, hipStream_t s);
+// ev (nullable): pairs around the query preparation, the split kernel and the merge.
+hipError_t launch_decode(int in_dt, int out_dt, int D, const DecodeArgs& a, hipStream_t s, hipEvent_t const* ev);
 
 }  // namespace ne

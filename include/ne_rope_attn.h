@@ -136,6 +136,54 @@ ne_status_t ne_rope_attn_bwd_window(const void* q, const void* k, const void* v,
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     void* const* events);
 
+/* ---- Key/value cache: decode and chunked prefill ----------------------------------------------
+ * The second workload of the same operation: a few new tokens per sequence attend to everything
+ * before them, held in a key/value cache -- nanochat's inference stage generates with a KV cache
+ * ("nanochat 全栈 LLM 训练实践指南", sections 项目定位 and 测试体系; section 模型架构速览 notes, with its
+ * peak-bandwidth table, that decoding is bound by memory bandwidth).  The new tokens of sequence b sit at absolute positions cache_lens[b] ..
+ * cache_lens[b] + n - 1: keys are rotated at their own positions when appended, queries at theirs
+ * when attending, so the results equal the last rows of ne_rope_attn_fwd over the whole sequence
+ * (up to rounding).  Query t of sequence b sees the cached keys max(0, p - window + 1) .. p,
+ * p = cache_lens[b] + t (window <= 0 or >= Tcap: every key up to p).
+ *
+ * The cache is one caller-owned device buffer of ne_kv_cache_bytes() bytes in the library's
+ * layout (for each (b, kv head) group g = b * Hkv + h):
+ *   K' [B * Hkv][Tcap][head_dim]  fp16, keys after RoPE
+ *   V^T[B * Hkv][head_dim][Tcap]  fp16, values transposed; within every aligned run of 16
+ *                                 positions, position 16a + s is stored at 16a + s', where s'
+ *                                 swaps bits 2 and 3 of s
+ * (V follows K in the buffer).  Values are converted to fp16 (|v| must stay below 65504).
+ * Tcap, the capacity in tokens, is a multiple of 64.  cache_lens is a DEVICE array of B int32:
+ * the tokens each sequence already holds.  It is read on the device, so it cannot be checked on
+ * the host: each call uses min(max(cache_lens[b], 0), Tcap - n), n the tokens of the call, and
+ * never touches memory outside the cache.  Neither call changes cache_lens; the caller advances
+ * it after the tokens of a step are appended and attended to.  Only in_dtype BF16 and F16. */
+size_t ne_kv_cache_bytes(int B, int Tcap, int Hkv, int head_dim, ne_dtype_t in_dtype);
+
+/* Writes k_new, v_new ([B][Tn][Hkv][head_dim], in_dtype) into the cache at positions
+ * cache_lens[b] .. cache_lens[b] + Tn - 1, keys rotated at those positions. */
+ne_status_t ne_kv_cache_append(void* cache, size_t cache_bytes, const int* cache_lens,
+                               const void* k_new, const void* v_new,
+                               int B, int Tn, int Tcap, int Hkv, int head_dim, double rope_base,
+                               ne_dtype_t in_dtype, void* stream);
+
+size_t ne_rope_attn_decode_workspace_bytes(int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
+                                           ne_dtype_t in_dtype);
+
+/* o [B][Tq][Hq][head_dim] (out_dtype F32 or in_dtype), lse [B][Hq][Tq] for the queries q
+ * ([B][Tq][Hq][head_dim], in_dtype) at positions cache_lens[b] + t against the cache, whose
+ * positions up to cache_lens[b] + Tq - 1 must have been appended.  The keys are split into slices
+ * processed by separate workgroups and merged by the log-sum-exp rule in a fixed order
+ * (deterministic).  events: NULL or 6 hipEvent_t entries (pairs around the query preparation,
+ * the attention and the merge; null entries are skipped). */
+ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_bytes, const int* cache_lens,
+                                void* o, float* lse,
+                                int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
+                                double rope_base, int window,
+                                ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* events);
+
 const char* ne_status_str(ne_status_t status);
 const char* ne_last_error(void);
 int ne_abi_version(void);

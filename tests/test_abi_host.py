@@ -111,3 +111,57 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 4, 2, 32)
     with pytest.raises(RuntimeError):
         binding.ne_rope_attn_fwd(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous(), 1e4)
+
+
+# ---- window, cache and decode entry points ----------------------------------------------------
+def test_window_calls_reject_before_launch(L):
+    ev = None
+    args = [FAKE] * 5 + [1, 16, 4, 2, 64, 1e4, 8, binding.NE_BF16, binding.NE_F32, FAKE, 16, None, ev]
+    assert L.ne_rope_attn_fwd_window(*args) == 5          # workspace too small
+    args[5] = 0
+    assert L.ne_rope_attn_fwd_window(*args) == 2          # B = 0
+    bargs = [FAKE] * 9 + [1, 16, 4, 2, 64, 1e4, 8, binding.NE_BF16, binding.NE_F32, None, 1 << 30, None, ev]
+    assert L.ne_rope_attn_bwd_window(*bargs) == 1         # null workspace
+
+
+def test_cache_and_decode_sizes(L):
+    B, Tcap, Hq, Hkv, D = 8, 8192, 32, 8, 128
+    assert L.ne_kv_cache_bytes(B, Tcap, Hkv, D, binding.NE_BF16) == 2 * B * Hkv * Tcap * D * 2
+    assert L.ne_kv_cache_bytes(B, 100, Hkv, D, binding.NE_BF16) == 0      # Tcap not a multiple of 64
+    assert L.ne_kv_cache_bytes(B, Tcap, Hkv, D, binding.NE_F32) == 0      # 16-bit inputs only
+    ws = L.ne_rope_attn_decode_workspace_bytes(B, 1, Tcap, Hq, Hkv, D, binding.NE_BF16)
+    assert ws >= B * Hq * D * 2
+    assert L.ne_rope_attn_decode_workspace_bytes(B, Tcap + 1, Tcap, Hq, Hkv, D, binding.NE_BF16) == 0
+    assert L.ne_rope_attn_decode_workspace_bytes(B, 1, Tcap, 30, Hkv, D, binding.NE_BF16) == 0
+
+
+def decode_call(L, q=FAKE, cache=FAKE, cb=1 << 40, lens=FAKE, o=FAKE, lse=FAKE, B=2, Tq=1, Tcap=256, Hq=4,
+                Hkv=2, D=64, base=1e4, W=0, i=binding.NE_BF16, out=binding.NE_F32, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = L.ne_rope_attn_decode_workspace_bytes(B, Tq, Tcap, Hq, Hkv, D, i) if D in (32, 64, 128) else 1 << 20
+    return L.ne_rope_attn_decode(q, cache, cb, lens, o, lse, B, Tq, Tcap, Hq, Hkv, D, base, W, i, out, ws, wsb,
+                                 None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(lens=None), 1), (dict(cache=None), 1),
+    (dict(Tcap=100), 2), (dict(Tq=0), 2), (dict(Tq=300), 2), (dict(Hq=5), 2), (dict(B=0), 2),
+    (dict(D=96), 3), (dict(i=binding.NE_F32, out=binding.NE_F32), 3), (dict(out=binding.NE_F16), 3),
+    (dict(lens=FAKE + 2), 4), (dict(o=FAKE + 8), 4),
+    (dict(cb=16), 5), (dict(wsb=16), 5), (dict(base=float("inf")), 2),
+])
+def test_decode_rejects_before_launch(L, kw, status):
+    assert decode_call(L, **kw) == status
+    assert L.ne_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cache=None), 1), (dict(Tn=0), 2), (dict(Tcap=96), 2), (dict(i=binding.NE_F32), 3),
+    (dict(k=FAKE + 4), 4), (dict(cb=100), 5),
+])
+def test_append_rejects_before_launch(L, kw, status):
+    a = dict(cache=FAKE, cb=1 << 40, lens=FAKE, k=FAKE, v=FAKE, B=2, Tn=3, Tcap=256, Hkv=2, D=64, base=1e4,
+             i=binding.NE_BF16)
+    a.update(kw)
+    assert L.ne_kv_cache_append(a["cache"], a["cb"], a["lens"], a["k"], a["v"], a["B"], a["Tn"], a["Tcap"],
+                                a["Hkv"], a["D"], a["base"], a["i"], None) == status

@@ -15,6 +15,10 @@ pass with every launch bracketed.  Prints one JSON line.
 After the headline measurement the same step is measured with a sliding window of --window keys
 (default T/4, the short window of the nanochat guide's window_pattern; 0 skips it), counting the
 visible pairs N_W = W(W+1)/2 + (T-W)W per head; it is reported under "sliding_window".
+Then one decode step of the cached workload (--decode-batch sequences, each holding 8191 tokens of
+the long-context shape, Hq 32 / Hkv 8 / D 128, RoPE base 5e5, attending with one new token) is
+measured as HBM bandwidth: bytes = the visible cached keys and values (fp16) + q + o, reported
+under "decode"; 0 skips it.
 """
 import argparse
 import hashlib
@@ -116,6 +120,74 @@ def cpu_baseline(w, sample_B):
                       f"float64, {dt:.2f} s wall"}
 
 
+def measure_decode(Bd, K, hev, new_events):
+    """One decode step (split-KV attention with the query rotation, then the merge) of Bd sequences of the
+    long-context shape with 8191 cached tokens and one new token each."""
+    import torch
+    from causal_gqa_flashattention_rope_amd import binding, inputs
+    dev = torch.device("cuda:0")
+    Tcap, Hq, Hkv, D, base = 8192, 32, 8, 128, 5.0e5
+    L = Tcap - 1                                       # tokens already in the cache
+    cache = binding.new_kv_cache(Bd, Tcap, Hkv, D, torch.bfloat16, dev)
+    lens = torch.zeros(Bd, dtype=torch.int32, device=dev)
+    for c in range(0, Tcap, 1024):
+        kc = inputs.gaussian((Bd, 1024, Hkv, D), 801 + c, 1.0, "bf16").to(dev)
+        vc = inputs.gaussian((Bd, 1024, Hkv, D), 901 + c, 1.0, "bf16").to(dev)
+        binding.ne_kv_cache_append(cache, lens, kc, vc, Tcap, base)
+        lens += 1024
+    lens.fill_(L)
+    q = inputs.gaussian((Bd, 1, Hq, D), 990, 1.0, "bf16").to(dev)
+    o = torch.empty((Bd, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Bd, Hq, 1), dtype=torch.float32, device=dev)
+    ws = binding.alloc_workspace(binding.decode_workspace_bytes(Bd, 1, Tcap, Hq, Hkv, D, torch.bfloat16), dev)
+
+    def call(ev=None):
+        binding.ne_rope_attn_decode(q, cache, lens, Tcap, Hkv, base, 0, o=o, lse=lse, workspace=ws, events=ev)
+
+    # warm-up with every launch bracketed (per-kernel breakdown)
+    Wd = 50
+    evs = [new_events(4) for _ in range(Wd)]
+    for i in range(Wd):
+        call(evs[i])
+    torch.cuda.synchronize()
+    kern = {n: sum(hev.elapsed_ms(e[2 * i], e[2 * i + 1]) for e in evs[-10:]) / 10
+            for i, n in enumerate(["decode_split", "decode_merge"])}
+    # timed: K calls, events only around the split kernel
+    tev = [new_events(2) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        call([tev[i][0], tev[i][1], None, None])
+    torch.cuda.synchronize()
+    ms_call = (time.perf_counter() - t0) * 1e3 / K
+    split_ms = sum(hev.elapsed_ms(a, b) for a, b in tev) / K
+    # append of one token per sequence (the other half of a serving step), timed alone
+    k1 = inputs.gaussian((Bd, 1, Hkv, D), 991, 1.0, "bf16").to(dev)
+    lens_app = torch.full((Bd,), L, dtype=torch.int32, device=dev)
+    binding.ne_kv_cache_append(cache, lens_app, k1, k1, Tcap, base)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        binding.ne_kv_cache_append(cache, lens_app, k1, k1, Tcap, base)
+    torch.cuda.synchronize()
+    append_ms = (time.perf_counter() - t0) * 1e3 / K
+    kv_bytes = 2.0 * Bd * Hkv * (L + 1) * D * 2        # visible keys and values, fp16
+    io_bytes = Bd * Hq * D * 2 * 2 + Bd * Hq * 4       # q, o (bf16), lse
+    split_bytes = kv_bytes + Bd * Hq * D * 2           # the split kernel reads the cache and q~
+    return {
+        "workload": f"decode_t8192_b{Bd}", "B": Bd, "cached_tokens": L, "new_tokens": 1, "Tcap": Tcap,
+        "Hq": Hq, "Hkv": Hkv, "head_dim": D, "rope_base": base, "in_dtype": "bf16", "cache_dtype": "f16",
+        "out_dtype": "bf16", "ms_per_call": round(ms_call, 4), "tokens_per_s": round(Bd / (ms_call * 1e-3), 1),
+        "hbm_gb_s": round((kv_bytes + io_bytes) / (ms_call * 1e-3) / 1e9, 1),
+        "kernel_ms": {n: round(t, 4) for n, t in kern.items()},
+        "append_one_token_ms": round(append_ms, 4),
+        "roofline": {"kernel": "decode_split", "bound": "hbm",
+                     "achieved": round(split_bytes / (split_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK,
+                     "unit": "GB/s", "frac": round(split_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK, 4),
+                     "traffic": None, "bytes_per_launch": split_bytes, "launch_ms": round(split_ms, 4)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +204,8 @@ def main():
     ap.add_argument("--cpu-sample-batch", type=int, default=4)
     ap.add_argument("--window", type=int, default=-1,
                     help="window of the sliding-window measurement (-1: T/4; 0: skip it)")
+    ap.add_argument("--decode-batch", type=int, default=8,
+                    help="sequences of the decode measurement (0: skip it)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards over "
@@ -285,6 +359,8 @@ def main():
                          "unit": "TFLOP/s", "frac": round(ach_w / peak, 4), "traffic": None,
                          "flops_per_launch": kf_w[dom_w], "launch_ms": round(dom_ms_w, 4)},
         }
+    if args.decode_batch > 0:
+        result["decode"] = measure_decode(args.decode_batch, K, hev, new_events)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

@@ -261,7 +261,7 @@ def ne_rope_attn_decode(q, cache, cache_lens, Tcap, Hkv, rope_base, window=0, ou
                         o=None, lse=None, workspace=None, events=None):
     """o, lse for the queries q [B, Tq, Hq, D] at positions cache_lens[b] + t against the cache.
 
-    events: optional 6 events (or None entries) around the three launches."""
+    events: optional 4 events (or None entries) around the two launches."""
     _require_gpu(q, cache)
     B, Tq, Hq, D = q.shape
     lens = _lens_arg(cache_lens, B, q.device)
@@ -275,5 +275,5 @@ def ne_rope_attn_decode(q, cache, cache_lens, Tcap, Hkv, rope_base, window=0, ou
                                      _ptr(o), _ptr(lse), B, Tq, Tcap, Hq, Hkv, D, float(rope_base), int(window),
                                      _DT[q.dtype], _DT[o.dtype], _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(),
-                                     _events_arg(events, 6)))
+                                     _events_arg(events, 4)))
     return o, lse

@@ -280,17 +280,27 @@ ne_status_t check_cache_shape(int B, int Tcap, int Hkv, int D) {
     return NE_OK;
 }
 
-// Key slices per (group, 32-row block): about four workgroups per CU overall, and no more than one
-// slice per 256 keys of the cache's capacity.
+// Key slices per (group, 32-row block): at least NE_DECODE_WORKGROUPS workgroups overall (two per
+// CU), and at least one slice per NE_DECODE_SPLIT_KEYS keys of the cache's capacity (each wave
+// then streams about 8 tiles: measured best on the 8192-token cache at 8 and 32 sequences); at
+// most one slice per 32-key tile and kMaxSplits.
+#ifndef NE_DECODE_WORKGROUPS
+#define NE_DECODE_WORKGROUPS 512
+#endif
+#ifndef NE_DECODE_SPLIT_KEYS
+#define NE_DECODE_SPLIT_KEYS 1024
+#endif
 int decode_nsplit(int B, int Hkv, int nrb, int Tcap) {
     const int64_t blocks = (int64_t)B * Hkv * nrb;
-    int64_t ns = (1024 + blocks - 1) / blocks;
-    ns = std::min<int64_t>(ns, std::max(1, Tcap / 256));
+    int64_t ns = std::max<int64_t>((NE_DECODE_WORKGROUPS + blocks - 1) / blocks,
+                                   (Tcap + NE_DECODE_SPLIT_KEYS - 1) / NE_DECODE_SPLIT_KEYS);
+    ns = std::min<int64_t>(ns, std::max(1, Tcap / 32));
+    ns = std::min<int64_t>(ns, ne::kMaxSplits);
     return (int)std::max<int64_t>(ns, 1);
 }
 
 struct DecodeLayout {
-    size_t qh, part_o, part_ml, total;
+    size_t part_o, part_ml, total;
     int nrb, nsplit;
 };
 
@@ -301,7 +311,6 @@ DecodeLayout decode_layout(int B, int Tq, int Tcap, int Hq, int Hkv, int D) {
     L.nsplit = decode_nsplit(B, Hkv, L.nrb, Tcap);
     const size_t slots = (size_t)B * Hkv * L.nrb * L.nsplit;
     size_t off = 0;
-    L.qh = off; off += up((size_t)B * Tq * Hq * D * 2);
     L.part_o = off; off += up(slots * 32 * D * 4);
     L.part_ml = off; off += up(slots * 64 * 4);
     L.total = off;
@@ -346,6 +355,8 @@ ne_status_t ne_kv_cache_append(void* cache, size_t cache_bytes, const int* cache
     ne::AppendArgs a{};
     a.k = k_new; a.v = v_new; a.cache = cache; a.lens = cache_lens;
     a.B = B; a.Tn = Tn; a.Tcap = Tcap; a.Hkv = Hkv; a.rope_base = rope_base;
+    for (int i = 0; i < head_dim / 2; ++i)
+        a.theta[i] = rope_base > 0.0 ? std::pow(rope_base, -2.0 * i / head_dim) : 0.0;
     hipError_t e = ne::launch_append((int)in_dtype, head_dim, a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_kv_cache_append: launch failed: %s", hipGetErrorString(e));
     return NE_OK;
@@ -382,13 +393,15 @@ ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_b
     char* ws = (char*)workspace;
     ne::DecodeArgs a{};
     a.q = q; a.cache = cache; a.lens = cache_lens;
-    a.qh = ws + L.qh; a.part_o = (float*)(ws + L.part_o); a.part_ml = (float*)(ws + L.part_ml);
+    a.part_o = (float*)(ws + L.part_o); a.part_ml = (float*)(ws + L.part_ml);
     a.o = o; a.lse = lse;
     a.B = B; a.Tq = Tq; a.Tcap = Tcap; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
     a.nrb = L.nrb; a.nsplit = L.nsplit;
     a.window = visible_keys(window, Tcap);
     a.rope_base = rope_base;
     a.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    for (int i = 0; i < head_dim / 2; ++i)
+        a.theta[i] = rope_base > 0.0 ? std::pow(rope_base, -2.0 * i / head_dim) : 0.0;
     hipError_t e = ne::launch_decode((int)in_dtype, (int)out_dtype, head_dim, a, (hipStream_t)stream,
                                      (hipEvent_t const*)events);
     if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_attn_decode: launch failed: %s", hipGetErrorString(e));

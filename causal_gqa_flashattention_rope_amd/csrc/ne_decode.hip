@@ -21,14 +21,8 @@ namespace ne {
 
 namespace {
 
-// theta_i = base^(-2i/D) for the D/2 rotary pairs, in double precision (into LDS).
-template <int D>
-__device__ __forceinline__ void rope_theta(double* theta, double base) {
-    for (int i = threadIdx.x; i < D / 2; i += blockDim.x)
-        theta[i] = exp2(-2.0 * (double)i / (double)D * log2(base));
-}
-
-// cos and sin of p * theta: the phase is formed and reduced to [-pi, pi] in double precision
+// cos and sin of p * theta (theta_i = base^(-2i/D), computed by the host in double precision): the
+// phase is formed and reduced to [-pi, pi] in double precision
 // (two-term 2 pi), so the single-precision sincos sees a small argument at any position.
 __device__ __forceinline__ float2 rope_cs(int p, double theta) {
     constexpr double kTwoPiHi = 6.283185307179586;
@@ -66,14 +60,11 @@ __device__ __forceinline__ int cache_len(const int* lens, int b, int n, int Tcap
 template <typename TI, int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     constexpr int TB = 16, CPR = D / 8;
-    __shared__ double theta[D / 2];
     __shared__ float vs[TB][D + 1];
     const int grp = blockIdx.y, b = grp / a.Hkv, hkv = grp % a.Hkv;
     const int t0 = blockIdx.x * TB, Tn = a.Tn, Tcap = a.Tcap;
     const int len = cache_len(a.lens, b, Tn, Tcap);
     const bool rope = a.rope_base > 0.0;
-    if (rope) rope_theta<D>(theta, a.rope_base);
-    __syncthreads();
     _Float16* kc = (_Float16*)a.cache + (size_t)grp * Tcap * D;
     _Float16* vtc = (_Float16*)a.cache + (size_t)a.B * a.Hkv * Tcap * D + (size_t)grp * D * Tcap;
     for (int idx = threadIdx.x; idx < TB * CPR; idx += 256) {
@@ -86,7 +77,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
         if (rope) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float2 r = rope_cs(p, theta[chunk * 4 + q]);
+                const float2 r = rope_cs(p, a.theta[chunk * 4 + q]);
                 const float u = x[2 * q], v = x[2 * q + 1];
                 x[2 * q] = u * r.x - v * r.y;
                 x[2 * q + 1] = u * r.y + v * r.x;
@@ -112,68 +103,37 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
 }
 
 // =====================================================================================
-// Query preparation: q~ = fp16(R_p(q) * scale * log2 e) at p = len_b + t, as flattened rows
-// [group][t * G + hh][D] (the row order of one token's heads).  grid (Tq, B), 256 threads.
+// Split-KV attention.  grid (nsplit * nrb * B * Hkv), 256 threads = 4 waves; a workgroup takes
+// one block of 32 flattened query rows (row R = t * G + hh of one group: the order of one token's
+// heads) and one of nsplit equal slices of the key range those rows see ([first key of the window
+// of its first row, rounded down to 32], last row's position]); its 4 waves take the slice's
+// 32-key tiles in turn.  The workgroup first rotates its query rows at their absolute positions
+// (theta_i from the host in double precision, the phase reduced in double) and stages them in
+// LDS as fp16 times scale * log2 e.  Per tile a wave loads its K' and V'^T fragments from HBM
+// straight into registers, one tile ahead of the one it computes: S^T = K' Q~^T (keys on lanes,
+// one query row per lane column), masks (causal, window, cache end), updates its running max and
+// sum (log2 units) and adds V'^T P^T.  The waves merge in LDS in a fixed order and the workgroup
+// writes its partial (unnormalised O over its keys, max m, sum l) for the valid rows.
 // =====================================================================================
 template <typename TI, int D>
-__global__ __launch_bounds__(256) void decode_prep_q(DecodeArgs a) {
-    constexpr int CPR = D / 8;
-    __shared__ double theta[D / 2];
-    const int t = blockIdx.x, b = blockIdx.y;
-    const int Tq = a.Tq, Hq = a.Hq, G = a.G;
-    const int p = cache_len(a.lens, b, Tq, a.Tcap) + t;
-    const bool rope = a.rope_base > 0.0;
-    if (rope) rope_theta<D>(theta, a.rope_base);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < Hq * CPR; idx += 256) {
-        const int hq = idx / CPR, chunk = idx % CPR, g = hq / G, hh = hq % G;
-        float x[8];
-        load8_in((const TI*)a.q + (((size_t)b * Tq + t) * Hq + hq) * D + chunk * 8, x);
-        if (rope) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float2 r = rope_cs(p, theta[chunk * 4 + q]);
-                const float u = x[2 * q], v = x[2 * q + 1];
-                x[2 * q] = u * r.x - v * r.y;
-                x[2 * q + 1] = u * r.y + v * r.x;
-            }
-        }
-        half8 out;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = (_Float16)(x[e] * a.qscale);
-        const size_t row = ((size_t)b * a.Hkv + g) * ((size_t)Tq * G) + (size_t)t * G + hh;
-        *reinterpret_cast<half8*>((_Float16*)a.qh + row * D + chunk * 8) = out;
-    }
-}
-
-// =====================================================================================
-// Split-KV attention.  grid (nsplit * nrb * B * Hkv), 256 threads = 4 waves; a workgroup takes
-// one block of 32 flattened query rows of one group and one of nsplit equal slices of the key
-// range those rows see ([first key of the window of its first row, rounded down to 32], last
-// row's position]); its 4 waves take the slice's 32-key tiles in turn.  Per tile a wave loads
-// its K' and V'^T fragments from HBM into registers, computes S^T = K' Q~^T (keys on lanes,
-// one query row per lane column), masks (causal, window, cache end), updates its running max and
-// sum (log2 units), and adds V'^T P^T.  The waves merge in LDS in a fixed order and the
-// workgroup writes its partial (unnormalised O over its keys, max m, sum l) for the valid rows.
-// =====================================================================================
-template <int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
     using M = Mma<_Float16>;
-    constexpr int KS = D / 16, NDB = D / 32, NWV = 4;
+    constexpr int KS = D / 16, NDB = D / 32, NWV = 4, CPR = D / 8;
+    __shared__ __attribute__((aligned(16))) _Float16 sq[32][D + 8];
     __shared__ float so[32][D + 4];
     __shared__ float sm[NWV][32];
     __shared__ float sl[NWV][32];
     const int nsplit = a.nsplit, nrb = a.nrb;
     const int s = blockIdx.x % nsplit, rb = (blockIdx.x / nsplit) % nrb, g = blockIdx.x / (nsplit * nrb);
-    const int b = g / a.Hkv;
+    const int b = g / a.Hkv, hkv = g % a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
     const int Tq = a.Tq, G = a.G, TqG = Tq * G, Tcap = a.Tcap, W = a.window;
     const int len = cache_len(a.lens, b, Tq, Tcap), L = len + Tq;
 
     const int R0 = rb * 32, R = R0 + c;
-    const bool rvalid = R < TqG;
+    const int nvalid = min(32, TqG - R0);
     const int p_lane = len + min(R, TqG - 1) / G;                 // this lane's query position
-    const int p_min = len + R0 / G, p_max = len + min(R0 + 31, TqG - 1) / G;
+    const int p_min = len + R0 / G, p_max = len + (R0 + nvalid - 1) / G;
     const int Kb = max(0, p_min - W + 1) & ~31, Ke = p_max + 1;    // key range of the row block
     const int CH = ((Ke - Kb + nsplit - 1) / nsplit + 31) & ~31;  // keys per split
     const int k0 = Kb + s * CH, k1 = min(Ke, k0 + CH);
@@ -181,39 +141,74 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const _Float16* kc = (const _Float16*)a.cache + (size_t)g * Tcap * D;
     const _Float16* vtc = (const _Float16*)a.cache + (size_t)a.B * a.Hkv * Tcap * D + (size_t)g * D * Tcap;
 
-    half8 qf[KS];
-    {
-        const _Float16* qrow = (const _Float16*)a.qh + ((size_t)g * TqG + min(R, TqG - 1)) * D;
+    // first tile's loads, in flight while the queries are prepared
+    half8 kf[KS], vf[2][NDB];
+    auto load_tile = [&](int k) {
+        // k is a multiple of 32 below k1 <= Tcap (a multiple of 64): keys k .. k + 31 are in the cache
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = rvalid ? M::row_frag(qrow, ks, h, D) : half8{};
-    }
-    floatx16 oacc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
-    float m_run = kMFloor, l_run = 0.f;
-
-    for (int k = k0 + 32 * w; k < k1; k += 32 * NWV) {
-        // k is a multiple of 32 below k1 <= Tcap (a multiple of 64), so keys k .. k + 31 are in
-        // the cache; keys at or past L hold stale or unwritten data and are masked (V zeroed)
-        half8 kf[KS], vf[2][NDB];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const half8*>(kc + (size_t)(k + c) * D + 16 * ks + 8 * h);
+        for (int ks = 0; ks < KS; ++ks)
+            kf[ks] = *reinterpret_cast<const half8*>(kc + (size_t)(k + c) * D + 16 * ks + 8 * h);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
                 vf[kk][db] = *reinterpret_cast<const half8*>(vtc + (size_t)(32 * db + c) * Tcap + k + 16 * kk + 8 * h);
+    };
+    int k = k0 + 32 * w;
+    if (k < k1) load_tile(k);
+
+    // q~ rows of this block into LDS (rows past the valid ones are zeros)
+    const bool rope = a.rope_base > 0.0;
+    for (int idx = tid; idx < 32 * CPR; idx += 256) {
+        const int r = idx / CPR, chunk = idx % CPR;
+        half8 out = half8{};
+        if (r < nvalid) {
+            const int Rr = R0 + r, t = Rr / G, hq = hkv * G + (Rr - t * G);
+            float x[8];
+            load8_in((const TI*)a.q + (((size_t)b * Tq + t) * a.Hq + hq) * D + chunk * 8, x);
+            if (rope) {
+                const int p = len + t;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float2 cs = rope_cs(p, a.theta[chunk * 4 + q]);
+                    const float u = x[2 * q], v = x[2 * q + 1];
+                    x[2 * q] = u * cs.x - v * cs.y;
+                    x[2 * q + 1] = u * cs.y + v * cs.x;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[e] = (_Float16)(x[e] * a.qscale);
+        }
+        *reinterpret_cast<half8*>(&sq[r][chunk * 8]) = out;
+    }
+    __syncthreads();
+    half8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const half8*>(&sq[c][16 * ks + 8 * h]);
+
+    floatx16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
+    float m_run = kMFloor, l_run = 0.f;
+
+    for (; k < k1; k += 32 * NWV) {
         floatx16 sc = floatx16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) sc = M::mma(kf[ks], qf[ks], sc);
-        if (k + 31 >= L) {  // the cache ends inside this tile
+        half8 vc[2][NDB];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) vc[kk][db] = vf[kk][db];
+        if (k + 32 * NWV < k1) load_tile(k + 32 * NWV);   // next tile in flight during this one
+        if (k + 31 >= L) {  // the cache ends inside this tile: stale or unwritten values there
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     if (k + 16 * kk + vt_key_of_pos(8 * h + j) >= L)
 #pragma unroll
-                        for (int db = 0; db < NDB; ++db) vf[kk][db][j] = (_Float16)0.f;
+                        for (int db = 0; db < NDB; ++db) vc[kk][db][j] = (_Float16)0.f;
         }
         float mx = kMFloor;
 #pragma unroll
@@ -240,7 +235,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         for (int kk = 0; kk < 2; ++kk) {
             const half8 pf = pack_frag_f16(sc, kk);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) oacc[db] = M::mma(vf[kk][db], pf, oacc[db]);
+            for (int db = 0; db < NDB; ++db) oacc[db] = M::mma(vc[kk][db], pf, oacc[db]);
         }
     }
     l_run = sum_halves(l_run);
@@ -268,7 +263,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         __syncthreads();
     }
     // partials of the valid rows: O [row][D], then (m, l) per row
-    const int nvalid = min(32, TqG - R0);
     const size_t slot = ((size_t)g * nrb + rb) * nsplit + s;
     float* po = a.part_o + slot * 32 * D;
     for (int idx = tid; idx < nvalid * (D / 4); idx += 256) {
@@ -289,10 +283,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 // =====================================================================================
 // Merge of the nsplit partials of every valid row: m = max m_s, l = sum l_s 2^(m_s - m),
 // o = sum O_s 2^(m_s - m) / l, lse = ln 2 (m + log2 l).  grid (nrb * B * Hkv), 256 threads, one
-// thread per (row, 4 consecutive d); splits are added in index order.
+// thread per (row, 4 consecutive d).  The splits are folded in index order, 16 at a time: the
+// (m_s, l_s) and O_s of a chunk are loaded together (one memory round trip per chunk), then the
+// running (m, l, O) is rescaled to the chunk's max and the chunk added.
 // =====================================================================================
 template <int D, typename TOUT>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+    constexpr int CK = 16;
     const int nsplit = a.nsplit, nrb = a.nrb;
     const int rb = blockIdx.x % nrb, g = blockIdx.x / nrb;
     const int b = g / a.Hkv, hkv = g % a.Hkv;
@@ -301,16 +298,40 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     const size_t slot0 = ((size_t)g * nrb + rb) * nsplit;
     for (int idx = threadIdx.x; idx < nvalid * (D / 4); idx += 256) {
         const int row = idx / (D / 4), q4 = idx % (D / 4);
-        float m = kMFloor;
-        for (int s = 0; s < nsplit; ++s) m = fmaxf(m, a.part_ml[(slot0 + s) * 64 + row]);
-        float lsum = 0.f;
+        const float* ml = a.part_ml + slot0 * 64 + row;
+        const float* src = a.part_o + (slot0 * 32 + row) * D + 4 * q4;
+        float m = kMFloor, lsum = 0.f;
         floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < nsplit; ++s) {
-            const float f = __builtin_amdgcn_exp2f(a.part_ml[(slot0 + s) * 64 + row] - m);
-            lsum += a.part_ml[(slot0 + s) * 64 + 32 + row] * f;
-            const floatx4 x = *reinterpret_cast<const floatx4*>(a.part_o + ((slot0 + s) * 32 + row) * D + 4 * q4);
+        for (int s0 = 0; s0 < nsplit; s0 += CK) {
+            float ms[CK], ls[CK];
+            floatx4 xs[CK];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += x[e] * f;
+            for (int u = 0; u < CK; ++u) {
+                if (s0 + u < nsplit) {
+                    ms[u] = ml[(size_t)(s0 + u) * 64];
+                    ls[u] = ml[(size_t)(s0 + u) * 64 + 32];
+                    xs[u] = *reinterpret_cast<const floatx4*>(src + (size_t)(s0 + u) * 32 * D);
+                } else {
+                    ms[u] = kMFloor;
+                    ls[u] = 0.f;
+                    xs[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            float mc = m;
+#pragma unroll
+            for (int u = 0; u < CK; ++u) mc = fmaxf(mc, ms[u]);
+            const float fa = __builtin_amdgcn_exp2f(m - mc);
+            lsum *= fa;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] *= fa;
+#pragma unroll
+            for (int u = 0; u < CK; ++u) {
+                const float f = __builtin_amdgcn_exp2f(ms[u] - mc);
+                lsum += ls[u] * f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] += xs[u][e] * f;
+            }
+            m = mc;
         }
         const float inv = 1.f / lsum;
         const int R = R0 + row, t = R / G, hq = hkv * G + (R - t * G);
@@ -339,17 +360,13 @@ template <typename TI, typename TO, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t const* ev) {
     const DMarks m{ev, s};
     NE_DTRY(m.rec(0));
-    hipLaunchKernelGGL((decode_prep_q<TI, D>), dim3(a.Tq, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<TI, D>), dim3(a.nsplit * a.nrb * a.B * a.Hkv), dim3(256), 0, s, a);
     NE_DTRY(hipGetLastError());
     NE_DTRY(m.rec(1));
     NE_DTRY(m.rec(2));
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(a.nsplit * a.nrb * a.B * a.Hkv), dim3(256), 0, s, a);
-    NE_DTRY(hipGetLastError());
-    NE_DTRY(m.rec(3));
-    NE_DTRY(m.rec(4));
     hipLaunchKernelGGL((decode_combine_kernel<D, TO>), dim3(a.nrb * a.B * a.Hkv), dim3(256), 0, s, a);
     NE_DTRY(hipGetLastError());
-    return m.rec(5);
+    return m.rec(3);
 }
 
 template <typename TI, int D>

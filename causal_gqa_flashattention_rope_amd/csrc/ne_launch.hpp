@@ -44,18 +44,20 @@ struct AppendArgs {
     void* cache; const int* lens;
     int B, Tn, Tcap, Hkv;
     double rope_base;
+    double theta[64];                               // base^(-2i/D), i < D/2 (RoPE on)
 };
 
 // Decode / chunked prefill: Tq new queries per sequence at positions lens[b] + t against the cache.
+constexpr int kMaxSplits = 64;                      // key slices per (group, row block), at most
 struct DecodeArgs {
     const void* q; const void* cache; const int* lens;
-    void* qh;                                       // q~ rows [B * Hkv][Tq * G][D] fp16
     float* part_o; float* part_ml;                  // split partials
     void* o; float* lse;
     int B, Tq, Tcap, Hq, Hkv, G, nrb, nsplit;
     int window;                                     // 1..Tcap (Tcap: no window)
     double rope_base;
     float qscale;                                   // softmax scale * log2(e)
+    double theta[64];                               // base^(-2i/D), i < D/2 (RoPE on)
 };
 
 // dtype codes follow ne_dtype_t: 0 = f32, 1 = bf16, 2 = f16.
@@ -66,7 +68,7 @@ hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const Fw
 hipError_t launch_bwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const BwdArgs& ba, hipStream_t s,
                       hipEvent_t const* ev);
 hipError_t launch_append(int in_dt, int D, const AppendArgs& a, hipStream_t s);
-// ev (nullable): pairs around the query preparation, the split kernel and the merge.
+// ev (nullable): pairs around the split kernel and the merge (4 entries).
 hipError_t launch_decode(int in_dt, int out_dt, int D, const DecodeArgs& a, hipStream_t s, hipEvent_t const* ev);
 
 }  // namespace ne

@@ -174,8 +174,8 @@ size_t ne_rope_attn_decode_workspace_bytes(int B, int Tq, int Tcap, int Hq, int 
  * ([B][Tq][Hq][head_dim], in_dtype) at positions cache_lens[b] + t against the cache, whose
  * positions up to cache_lens[b] + Tq - 1 must have been appended.  The keys are split into slices
  * processed by separate workgroups and merged by the log-sum-exp rule in a fixed order
- * (deterministic).  events: NULL or 6 hipEvent_t entries (pairs around the query preparation,
- * the attention and the merge; null entries are skipped). */
+ * (deterministic).  events: NULL or 4 hipEvent_t entries (pairs around the attention and the
+ * merge; null entries are skipped). */
 ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_bytes, const int* cache_lens,
                                 void* o, float* lse,
                                 int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,

@@ -37,17 +37,19 @@ HBM_PEAK = 8000.0         # GB/s
 METRIC = "causal GQA attention TFLOP/s fwd+bwd (1 MI355X) + % of MFMA peak"
 KERNEL_SOURCES = ["causal_gqa_flashattention_rope_amd/csrc/ne_kernels.hip",
                   "causal_gqa_flashattention_rope_amd/csrc/ne_common.hpp"]
+DECODE_SOURCES = ["causal_gqa_flashattention_rope_amd/csrc/ne_decode.hip",
+                  "causal_gqa_flashattention_rope_amd/csrc/ne_common.hpp"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel, workload):
+def read_traffic(kernel, workload, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
     current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
@@ -59,7 +61,7 @@ def read_traffic(kernel, workload):
             m = re.match(r"^\s*([a-z_]+):\s*(\S+)\s*$", line)
             if m:
                 fields[m.group(1)] = m.group(2)
-    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -184,7 +186,8 @@ def measure_decode(Bd, K, hev, new_events):
         "roofline": {"kernel": "decode_split", "bound": "hbm",
                      "achieved": round(split_bytes / (split_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK,
                      "unit": "GB/s", "frac": round(split_bytes / (split_ms * 1e-3) / 1e9 / HBM_PEAK, 4),
-                     "traffic": None, "bytes_per_launch": split_bytes, "launch_ms": round(split_ms, 4)},
+                     "traffic": read_traffic("decode_split", f"decode_t8192_b{Bd}", DECODE_SOURCES),
+                     "bytes_per_launch": split_bytes, "launch_ms": round(split_ms, 4)},
     }
 
 

@@ -33,6 +33,11 @@ def _bind(path):
     lib.ne_oracle_bwd_w.restype = i
     lib.ne_oracle_bwd_given_o_w.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, ctypes.c_double, i, i]
     lib.ne_oracle_bwd_given_o_w.restype = i
+    d = ctypes.c_double
+    lib.ne_oracle_fwd_x.argtypes = [P, P, P, P, P, i, i, i, i, i, d, i, i, d, d, i]
+    lib.ne_oracle_fwd_x.restype = i
+    lib.ne_oracle_bwd_x.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, d, i, i, d, d, i]
+    lib.ne_oracle_bwd_x.restype = i
     lib.ne_oracle_rope.argtypes = [P, P, i, i, i, i, ctypes.c_double, i]
     lib.ne_oracle_rope.restype = i
     lib.ne_oracle_max_threads.argtypes = []
@@ -82,46 +87,53 @@ def _dims(q, k):
     return B, T, Hq, Hkv, D
 
 
-def fwd(q, k, v, rope_base, nthreads=0, window=0):
-    """Return (o, lse) in float64.  window W > 0: query i sees keys i-W+1 .. i."""
+def _qk(qk_norm):
+    """qk_norm: None (off) or (gain, eps)."""
+    if qk_norm is None:
+        return 0, 0.0, 0.0
+    gain, eps = qk_norm
+    return 1, float(gain), float(eps)
+
+
+def fwd(q, k, v, rope_base, nthreads=0, window=0, qk_norm=None):
+    """Return (o, lse) in float64.  window W > 0: query i sees keys i-W+1 .. i.
+    qk_norm (gain, eps): every row of q and k becomes gain * x / sqrt(mean(x^2) + eps) first."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, Hq, Hkv, D = _dims(q, k)
     o = np.empty_like(q)
     lse = np.empty((B, Hq, T), dtype=np.float64)
-    rc = _load().ne_oracle_fwd_w(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                 B, T, Hq, Hkv, D, float(rope_base), int(window), int(nthreads))
+    rc = _load().ne_oracle_fwd_x(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D,
+                                 float(rope_base), int(window), *_qk(qk_norm), int(nthreads))
     if rc:
         raise ValueError(f"ne_oracle_fwd rejected the arguments (rc={rc})")
     return o, lse
 
 
-def bwd(q, k, v, dO, rope_base, nthreads=0, window=0):
-    """Return (dq, dk, dv) in float64: the exact gradients of sum(o * dO)."""
+def _bwd(q, k, v, o, dO, rope_base, nthreads, window, qk_norm):
     q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
     B, T, Hq, Hkv, D = _dims(q, k)
     dq = np.empty_like(q)
     dk = np.empty_like(k)
     dv = np.empty_like(v)
-    rc = _load().ne_oracle_bwd_w(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq), _ptr(dk),
-                                 _ptr(dv), B, T, Hq, Hkv, D, float(rope_base), int(window), int(nthreads))
+    optr = None
+    if o is not None:
+        o = _f64(o)
+        optr = _ptr(o)
+    rc = _load().ne_oracle_bwd_x(_ptr(q), _ptr(k), _ptr(v), optr, _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 B, T, Hq, Hkv, D, float(rope_base), int(window), *_qk(qk_norm), int(nthreads))
     if rc:
         raise ValueError(f"ne_oracle_bwd rejected the arguments (rc={rc})")
     return dq, dk, dv
 
 
-def bwd_given_o(q, k, v, o, dO, rope_base, nthreads=0, window=0):
+def bwd(q, k, v, dO, rope_base, nthreads=0, window=0, qk_norm=None):
+    """Return (dq, dk, dv) in float64: the exact gradients of sum(o * dO)."""
+    return _bwd(q, k, v, None, dO, rope_base, nthreads, window, qk_norm)
+
+
+def bwd_given_o(q, k, v, o, dO, rope_base, nthreads=0, window=0, qk_norm=None):
     """(dq, dk, dv) with Delta = rowsum(dO * o) from the given o (e.g. o stored in bf16)."""
-    q, k, v, o, dO = _f64(q), _f64(k), _f64(v), _f64(o), _f64(dO)
-    B, T, Hq, Hkv, D = _dims(q, k)
-    dq = np.empty_like(q)
-    dk = np.empty_like(k)
-    dv = np.empty_like(v)
-    rc = _load().ne_oracle_bwd_given_o_w(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(dq),
-                                         _ptr(dk), _ptr(dv), B, T, Hq, Hkv, D, float(rope_base),
-                                         int(window), int(nthreads))
-    if rc:
-        raise ValueError(f"ne_oracle_bwd_given_o rejected the arguments (rc={rc})")
-    return dq, dk, dv
+    return _bwd(q, k, v, o, dO, rope_base, nthreads, window, qk_norm)
 
 
 def rope(x, rope_base, inverse=False):

@@ -38,11 +38,17 @@ def rope_rows(x, positions, base):
     return y
 
 
-def decode_fwd(q_new, k_seq, v_seq, lens, base, window=0):
+def qk_norm_rows(x, gain, eps):
+    """gain * x / sqrt(mean(x^2) + eps) over the last axis (the QK norm of 模型架构速览)."""
+    return gain * x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def decode_fwd(q_new, k_seq, v_seq, lens, base, window=0, qk_norm=None):
     """o [B][Tq][Hq][D], lse [B][Hq][Tq] for queries q_new [B][Tq][Hq][D] at positions lens[b] + t.
 
     k_seq[b], v_seq[b]: the raw (un-rotated) keys and values [L][Hkv][D] of sequence b at positions
-    0 .. L - 1, L >= lens[b] + Tq (positions past lens[b] + Tq - 1 are never visible)."""
+    0 .. L - 1, L >= lens[b] + Tq (positions past lens[b] + Tq - 1 are never visible).
+    qk_norm (gain, eps): rows of q and k are normalised first (rows of the cache when appended)."""
     q_new = np.asarray(q_new, dtype=np.float64)
     B, Tq, Hq, D = q_new.shape
     o = np.zeros((B, Tq, Hq, D))
@@ -56,7 +62,10 @@ def decode_fwd(q_new, k_seq, v_seq, lens, base, window=0):
         Hkv = k.shape[1]
         G = Hq // Hkv
         pos = int(lens[b]) + np.arange(Tq)
-        qr = rope_rows(q_new[b], pos, base)          # [Tq][Hq][D]
+        qb = q_new[b]
+        if qk_norm is not None:
+            qb, k = qk_norm_rows(qb, *qk_norm), qk_norm_rows(k, *qk_norm)
+        qr = rope_rows(qb, pos, base)                # [Tq][Hq][D]
         kr = rope_rows(k, np.arange(L), base)        # [L][Hkv][D]
         j = np.arange(L)
         vis = (j[None, :] <= pos[:, None])

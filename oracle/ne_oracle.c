@@ -20,6 +20,8 @@
  *     tiled kernel reaches: it DOES store the full masked T x T matrix.
  *   - Hand-written backward checked in double precision -- agentlenshq page,
  *     "验证与稳定性"; cnblogs page, section 2.1 "编译 + gradient check".
+ *   - QK norm (the *_x entry points): same guide, section 模型架构速览, the feature list entry
+ *     on QK norm (q and k normalised, then scaled up by 1.2); see qk_norm_rows below.
  *   - Sliding-window attention (the *_w entry points): "nanochat 全栈 LLM 训练实践指南"
  *     (the nanochat guide), section "模型架构速览" (architecture overview), the feature
  *     list entry on window_pattern: "S" layers see a quarter of the context, "L" layers
@@ -312,6 +314,80 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
     }
     free(qr); free(kr); free(orow); free(delta); free(lse_row); free(P); free(dS);
     free(dqr); free(dkr); free(dvg);
+    return 0;
+}
+
+/* ---- QK norm ------------------------------------------------------------------------------
+ * Every (b, t, head) row x of q and of k is replaced, before RoPE, by
+ *   x_hat = gain * x / sqrt(mean_d(x_d^2) + eps)
+ * (nanochat guide, section 模型架构速览: q and k are normalised and scaled up by 1.2).  Attention
+ * then runs on (q_hat, k_hat, v) exactly as above, and the gradients flow back through the
+ * normalisation: with rho = 1 / sqrt(mean(x^2) + eps) and dy the gradient with respect to
+ * x_hat, dx = gain * rho * (dy - x * rho^2 * (dy . x) / D).  (RoPE preserves the sum of squares
+ * of each row, so normalising before or after the rotation gives the same x_hat.) */
+static void qk_norm_rows(const double* x, double* y, size_t nrows, int D, double gain, double eps) {
+    for (size_t r = 0; r < nrows; ++r) {
+        const double* xr = x + r * D;
+        double ss = 0.0;
+        for (int d = 0; d < D; ++d) ss += xr[d] * xr[d];
+        const double rho = 1.0 / sqrt(ss / (double)D + eps);
+        for (int d = 0; d < D; ++d) y[r * D + d] = gain * xr[d] * rho;
+    }
+}
+
+static void qk_norm_rows_bwd(const double* x, double* dxy, size_t nrows, int D, double gain, double eps) {
+    /* dxy holds dy on entry and dx on return */
+    for (size_t r = 0; r < nrows; ++r) {
+        const double* xr = x + r * D;
+        double* g = dxy + r * D;
+        double ss = 0.0, dot = 0.0;
+        for (int d = 0; d < D; ++d) {
+            ss += xr[d] * xr[d];
+            dot += g[d] * xr[d];
+        }
+        const double rho = 1.0 / sqrt(ss / (double)D + eps);
+        for (int d = 0; d < D; ++d) g[d] = gain * rho * (g[d] - xr[d] * rho * rho * dot / (double)D);
+    }
+}
+
+static int qk_norm_copies(const double* q, const double* k, double** qh, double** kh, int B, int T,
+                          int Hq, int Hkv, int D, double gain, double eps) {
+    const size_t nq = (size_t)B * T * Hq, nk = (size_t)B * T * Hkv;
+    *qh = (double*)malloc(sizeof(double) * nq * D);
+    *kh = (double*)malloc(sizeof(double) * nk * D);
+    if (!*qh || !*kh) { free(*qh); free(*kh); return 2; }
+    qk_norm_rows(q, *qh, nq, D, gain, eps);
+    qk_norm_rows(k, *kh, nk, D, gain, eps);
+    return 0;
+}
+
+/* Forward with every option: window as in the header, qk_norm != 0 applies the QK norm. */
+int ne_oracle_fwd_x(const double* q, const double* k, const double* v, double* o, double* lse,
+                    int B, int T, int Hq, int Hkv, int D, double base, int window, int qk_norm,
+                    double gain, double eps, int nthreads) {
+    if (check_shape(B, T, Hq, Hkv, D, base) || (qk_norm && !(eps >= 0.0))) return 1;
+    if (!qk_norm) return ne_oracle_fwd_w(q, k, v, o, lse, B, T, Hq, Hkv, D, base, window, nthreads);
+    double *qh, *kh;
+    if (qk_norm_copies(q, k, &qh, &kh, B, T, Hq, Hkv, D, gain, eps)) return 2;
+    const int rc = ne_oracle_fwd_w(qh, kh, v, o, lse, B, T, Hq, Hkv, D, base, window, nthreads);
+    free(qh); free(kh);
+    return rc;
+}
+
+/* Backward with every option; o may be NULL (exact Delta) or the o to take Delta from. */
+int ne_oracle_bwd_x(const double* q, const double* k, const double* v, const double* o,
+                    const double* dO, double* dq, double* dk, double* dv, int B, int T, int Hq,
+                    int Hkv, int D, double base, int window, int qk_norm, double gain, double eps,
+                    int nthreads) {
+    if (check_shape(B, T, Hq, Hkv, D, base) || (qk_norm && !(eps >= 0.0))) return 1;
+    if (!qk_norm) return bwd_impl(q, k, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, window, nthreads);
+    double *qh, *kh;
+    if (qk_norm_copies(q, k, &qh, &kh, B, T, Hq, Hkv, D, gain, eps)) return 2;
+    const int rc = bwd_impl(qh, kh, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, window, nthreads);
+    free(qh); free(kh);
+    if (rc) return rc;
+    qk_norm_rows_bwd(q, dq, (size_t)B * T * Hq, D, gain, eps);
+    qk_norm_rows_bwd(k, dk, (size_t)B * T * Hkv, D, gain, eps);
     return 0;
 }
 

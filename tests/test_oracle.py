@@ -118,9 +118,13 @@ def test_bwd_matches_brute_force_finite_differences(shape, base):
 # torch float64 autograd: an independent implementation (complex RoPE via view_as_complex,
 # KV heads expanded with repeat_interleave, masked softmax, autograd for the gradients).
 # --------------------------------------------------------------------------------------
-def torch_attention(q, k, v, base, window=0):
+def torch_attention(q, k, v, base, window=0, qk_norm=None):
     B, T, Hq, D = q.shape
     Hkv = k.shape[2]
+    if qk_norm is not None:  # RMS over the head dimension of every (token, head) row, times the gain
+        gain, eps = qk_norm
+        q = gain * q / torch.sqrt((q * q).mean(dim=-1, keepdim=True) + eps)
+        k = gain * k / torch.sqrt((k * k).mean(dim=-1, keepdim=True) + eps)
     if base > 0:
         theta = base ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
         ang = torch.arange(T, dtype=torch.float64)[:, None] * theta[None, :]
@@ -543,3 +547,88 @@ def test_window_finite_differences_tiny():
             arrs[which][idx] = x0
             worst = max(worst, abs((lp - lm) / (2 * step) - a[idx]) / np.max(np.abs(a)))
     assert worst < 1e-6
+
+
+# --------------------------------------------------------------------------------------
+# QK norm (nanochat guide, 模型架构速览: q and k normalised and scaled up by 1.2).
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("shape,base,window,qkn", [((2, 37, 6, 2, 16), 10000.0, 0, (1.2, 1e-6)),
+                                                   ((1, 33, 4, 4, 8), 0.0, 0, (1.2, 0.0)),
+                                                   ((1, 50, 8, 2, 32), 5.0e5, 9, (1.2, 1e-6)),
+                                                   ((1, 19, 3, 1, 6), 10.0, 0, (0.7, 0.25))])
+def test_qk_norm_against_torch_float64_autograd(shape, base, window, qkn):
+    q, k, v, dO = case(*shape, seed=371)
+    o, lse = oracle.fwd(q, k, v, base, window=window, qk_norm=qkn)
+    dq, dk, dv = oracle.bwd(q, k, v, dO, base, window=window, qk_norm=qkn)
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    to, tlse = torch_attention(tq, tk, tv, base, window=window, qk_norm=qkn)
+    (to * torch.tensor(dO)).sum().backward()
+    assert relerr(o, to.detach().numpy()) < 1e-12
+    assert np.max(np.abs(lse - tlse.detach().numpy())) < 1e-12
+    assert relerr(dq, tq.grad.numpy()) < 1e-11
+    assert relerr(dk, tk.grad.numpy()) < 1e-11
+    assert relerr(dv, tv.grad.numpy()) < 1e-11
+
+
+def test_qk_norm_self_score_closed_form():
+    """T = 1 (R_0 = I) and k = q: the only score is |x_hat|^2 / sqrt(D) with |x_hat|^2 =
+    gain^2 * D * ms / (ms + eps), ms = mean(x^2) -- independent of the direction of x."""
+    rng = np.random.default_rng(381)
+    D, gain = 16, 1.2
+    for eps in (0.0, 1e-6, 0.5):
+        q = rng.standard_normal((1, 1, 2, D)) * rng.uniform(0.1, 3.0)
+        k = q[:, :, :1].copy()
+        q[:, :, 1] = q[:, :, 0]                 # both query heads equal the key
+        v = rng.standard_normal((1, 1, 1, D))
+        o, lse = oracle.fwd(q, k, v, 1e4, qk_norm=(gain, eps))
+        ms = float(np.mean(q[0, 0, 0] ** 2))
+        ref = gain ** 2 * D * ms / (ms + eps) / math.sqrt(D)
+        np.testing.assert_allclose(lse[0, :, 0], [ref, ref], rtol=1e-14, atol=0)
+        np.testing.assert_array_equal(o[0, 0, 0], v[0, 0, 0])
+
+
+def test_qk_norm_rescaling_rows_changes_nothing():
+    """eps = 0: scaling any q or k row by c > 0 leaves o and lse unchanged, and the gradient with
+    respect to that row scales by 1 / c (the loss is invariant along the row)."""
+    q, k, v, dO = case(1, 23, 4, 2, 8, seed=391)
+    qkn = (1.2, 0.0)
+    o, lse = oracle.fwd(q, k, v, 1e4, qk_norm=qkn)
+    dq, dk, dv = oracle.bwd(q, k, v, dO, 1e4, qk_norm=qkn)
+    c = np.random.default_rng(392).uniform(0.2, 5.0, size=(1, 23, 4, 1))
+    ck = np.random.default_rng(393).uniform(0.2, 5.0, size=(1, 23, 2, 1))
+    o2, lse2 = oracle.fwd(q * c, k * ck, v, 1e4, qk_norm=qkn)
+    dq2, dk2, dv2 = oracle.bwd(q * c, k * ck, v, dO, 1e4, qk_norm=qkn)
+    assert relerr(o2, o) < 1e-13 and np.max(np.abs(lse2 - lse)) < 1e-13
+    assert relerr(dq2 * c, dq) < 1e-12 and relerr(dk2 * ck, dk) < 1e-12 and relerr(dv2, dv) < 1e-12
+    # and the gradient is orthogonal to its row (no component along the scale direction)
+    assert np.max(np.abs(np.sum(dq * q, axis=-1))) < 1e-12 * np.max(np.abs(dq)) * np.max(np.abs(q)) * 8
+    assert np.max(np.abs(np.sum(dk * k, axis=-1))) < 1e-12 * np.max(np.abs(dk)) * np.max(np.abs(k)) * 8
+
+
+def test_qk_norm_finite_differences_tiny():
+    q, k, v, dO = case(1, 6, 4, 2, 4, seed=401)
+    qkn = (1.2, 1e-3)
+    dq, dk, dv = oracle.bwd(q, k, v, dO, 10000.0, window=4, qk_norm=qkn)
+    worst = 0.0
+    for which, a in enumerate((dq, dk, dv)):
+        arrs = [q.copy(), k.copy(), v.copy()]
+        for idx in np.ndindex(*a.shape):
+            x0 = arrs[which][idx]
+            step = 1e-5 * max(1.0, abs(x0))
+            arrs[which][idx] = x0 + step
+            lp = float(np.sum(oracle.fwd(*arrs, 10000.0, window=4, qk_norm=qkn)[0] * dO))
+            arrs[which][idx] = x0 - step
+            lm = float(np.sum(oracle.fwd(*arrs, 10000.0, window=4, qk_norm=qkn)[0] * dO))
+            arrs[which][idx] = x0
+            worst = max(worst, abs((lp - lm) / (2 * step) - a[idx]) / np.max(np.abs(a)))
+    assert worst < 1e-6
+
+
+def test_qk_norm_given_o_with_exact_o_is_the_exact_gradient():
+    q, k, v, dO = case(1, 30, 6, 2, 16, seed=411)
+    qkn = (1.2, 1e-6)
+    o, _ = oracle.fwd(q, k, v, 1e4, qk_norm=qkn)
+    a = oracle.bwd(q, k, v, dO, 1e4, qk_norm=qkn)
+    b = oracle.bwd_given_o(q, k, v, o, dO, 1e4, qk_norm=qkn)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)

@@ -44,6 +44,18 @@ def test_decode_rows_equal_full_causal_rows(L, Tq, Hq, Hkv, D, base, window):
     assert np.max(np.abs(lse[0] - flse[0, :, L - Tq:])) < 1e-12
 
 
+@pytest.mark.parametrize("window", [0, 6])
+def test_decode_qk_norm_rows_equal_full_causal_rows(window):
+    L, Tq, Hq, Hkv, D = 41, 5, 6, 2, 16
+    q, k, v = seq_case(L, Hq, Hkv, D, seed=77)
+    qkn = (1.2, 1e-6)
+    qn = q[:, L - Tq:]
+    o, lse = oracle.decode_fwd(qn, [k[0]], [v[0]], [L - Tq], 1e4, window, qk_norm=qkn)
+    fo, flse = oracle.fwd(q, k, v, 1e4, window=window, qk_norm=qkn)
+    np.testing.assert_allclose(o[0], fo[0, L - Tq:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0], flse[0, :, L - Tq:], rtol=0, atol=1e-12)
+
+
 def test_decode_ragged_batch_each_row_matches_its_own_sequence():
     Tq, Hq, Hkv, D = 3, 4, 2, 16
     lens = [0, 11, 29]

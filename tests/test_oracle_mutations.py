@@ -42,6 +42,13 @@ MUTATIONS = {
     "dk_uses_rotated_k": ("dkj[d] += s * qi[d];", "dkj[d] += s * kr[(size_t)i * D + d];"),
     "lse_without_max": ("lse_row[i] = m + log(l);", "lse_row[i] = log(l);"),
     "delta_from_value": ("di += dOi[d] * od[d];", "di += dOi[d] * od[d] * 0.5;"),
+    "qknorm_gain_once": ("y[r * D + d] = gain * xr[d] * rho;", "y[r * D + d] = xr[d] * rho;"),
+    "qknorm_sum_not_mean": ("const double rho = 1.0 / sqrt(ss / (double)D + eps);\n        for (int d = 0; d < D; ++d) y",
+                            "const double rho = 1.0 / sqrt(ss + eps);\n        for (int d = 0; d < D; ++d) y"),
+    "qknorm_bwd_projection_dropped": ("g[d] = gain * rho * (g[d] - xr[d] * rho * rho * dot / (double)D);",
+                                      "g[d] = gain * rho * g[d];"),
+    "qknorm_bwd_wrong_rho_power": ("g[d] = gain * rho * (g[d] - xr[d] * rho * rho * dot / (double)D);",
+                                   "g[d] = gain * rho * (g[d] - xr[d] * rho * dot / (double)D);"),
 }
 
 
@@ -58,6 +65,10 @@ def battery():
         ("single", pins.test_single_token),
         ("window_autograd", lambda: pins.test_window_against_torch_float64_autograd((2, 37, 6, 2, 16), 10000.0, 8)),
         ("window_zero_q", pins.test_window_zero_queries_average_the_window),
+        ("qknorm_autograd", lambda: pins.test_qk_norm_against_torch_float64_autograd((2, 37, 6, 2, 16), 10000.0, 0,
+                                                                                    (1.2, 1e-6))),
+        ("qknorm_self_score", pins.test_qk_norm_self_score_closed_form),
+        ("qknorm_invariance", pins.test_qk_norm_rescaling_rows_changes_nothing),
     ]
     for name, fn in checks:
         try:

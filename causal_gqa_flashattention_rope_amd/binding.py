@@ -22,8 +22,22 @@ EXPORTS = ("ne_rope_attn_fwd_workspace_bytes", "ne_rope_attn_bwd_workspace_bytes
            "ne_rope_attn_fwd", "ne_rope_attn_bwd", "ne_rope_attn_fwd_timed", "ne_rope_attn_bwd_timed",
            "ne_rope_attn_fwd_window", "ne_rope_attn_bwd_window",
            "ne_kv_cache_bytes", "ne_kv_cache_append", "ne_rope_attn_decode_workspace_bytes",
-           "ne_rope_attn_decode",
+           "ne_rope_attn_decode", "ne_rope_attn_fwd_ex", "ne_rope_attn_bwd_ex",
            "ne_status_str", "ne_last_error", "ne_abi_version")
+
+
+class AttnOpts(ctypes.Structure):
+    """ne_attn_opts_t: window (<= 0: causal prefix), QK norm (on, gain, eps)."""
+    _fields_ = [("window", ctypes.c_int), ("qk_norm", ctypes.c_int), ("qk_gain", ctypes.c_float),
+                ("qk_eps", ctypes.c_float)]
+
+
+def make_opts(window=0, qk_norm=None):
+    """qk_norm: None or (gain, eps)."""
+    if qk_norm is None:
+        return AttnOpts(int(window), 0, 1.0, 0.0)
+    gain, eps = qk_norm
+    return AttnOpts(int(window), 1, float(gain), float(eps))
 
 
 class NeError(RuntimeError):
@@ -65,11 +79,17 @@ def lib():
     L.ne_rope_attn_bwd_window.restype = i
     L.ne_kv_cache_bytes.argtypes = [i, i, i, i, i]
     L.ne_kv_cache_bytes.restype = sz
-    L.ne_kv_cache_append.argtypes = [vp, sz, vp, vp, vp, i, i, i, i, i, d, i, vp]
+    op = ctypes.POINTER(AttnOpts)
+    L.ne_rope_attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, d, op, i, i, vp, sz, vp, ctypes.POINTER(vp)]
+    L.ne_rope_attn_fwd_ex.restype = i
+    L.ne_rope_attn_bwd_ex.argtypes = ([vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, op, i, i, vp, sz, vp]
+                                      + [ctypes.POINTER(vp)])
+    L.ne_rope_attn_bwd_ex.restype = i
+    L.ne_kv_cache_append.argtypes = [vp, sz, vp, vp, vp, i, i, i, i, i, d, op, i, vp]
     L.ne_kv_cache_append.restype = i
     L.ne_rope_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.ne_rope_attn_decode_workspace_bytes.restype = sz
-    L.ne_rope_attn_decode.argtypes = ([vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, d, i, i, i, vp, sz, vp]
+    L.ne_rope_attn_decode.argtypes = ([vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, d, op, i, i, vp, sz, vp]
                                       + [ctypes.POINTER(vp)])
     L.ne_rope_attn_decode.restype = i
     L.ne_status_str.argtypes = [i]
@@ -150,6 +170,12 @@ def ne_rope_attn_fwd(q, k, v, rope_base, out_dtype=torch.float32, o=None, lse=No
     return _fwd(q, k, v, rope_base, None, out_dtype, o, lse, workspace, events)
 
 
+def ne_rope_attn_fwd_ex(q, k, v, rope_base, window=0, qk_norm=None, out_dtype=torch.float32, o=None, lse=None,
+                        workspace=None, events=None):
+    """Forward with every option: window (<= 0: causal prefix), qk_norm None or (gain, eps)."""
+    return _fwd(q, k, v, rope_base, make_opts(window, qk_norm), out_dtype, o, lse, workspace, events)
+
+
 def ne_rope_attn_fwd_window(q, k, v, rope_base, window, out_dtype=torch.float32, o=None, lse=None,
                             workspace=None, events=None):
     """Sliding-window forward: query t sees keys t - window + 1 .. t (window <= 0: causal prefix)."""
@@ -170,7 +196,9 @@ def _fwd(q, k, v, rope_base, window, out_dtype, o, lse, workspace, events):
             _DT[q.dtype], _DT[o.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream())
     ev = _events_arg(events, 4)
-    if window is not None:
+    if isinstance(window, AttnOpts):
+        _check(lib().ne_rope_attn_fwd_ex(*args[:11], ctypes.byref(window), *args[11:], ev))
+    elif window is not None:
         _check(lib().ne_rope_attn_fwd_window(*args[:11], window, *args[11:], ev))
     elif ev is None:
         _check(lib().ne_rope_attn_fwd(*args))
@@ -194,6 +222,12 @@ def ne_rope_attn_bwd_window(q, k, v, o, lse, dO, rope_base, window, dq=None, dk=
     return _bwd(q, k, v, o, lse, dO, rope_base, int(window), dq, dk, dv, workspace, events)
 
 
+def ne_rope_attn_bwd_ex(q, k, v, o, lse, dO, rope_base, window=0, qk_norm=None, dq=None, dk=None, dv=None,
+                        workspace=None, events=None):
+    """Backward with every option; the options must be the forward's."""
+    return _bwd(q, k, v, o, lse, dO, rope_base, make_opts(window, qk_norm), dq, dk, dv, workspace, events)
+
+
 def _bwd(q, k, v, o, lse, dO, rope_base, window, dq, dk, dv, workspace, events):
     _require_gpu(q, k, v, o, lse, dO)
     B, T, Hq, Hkv, D = _dims(q, k)
@@ -210,7 +244,9 @@ def _bwd(q, k, v, o, lse, dO, rope_base, window, dq, dk, dv, workspace, events):
             B, T, Hq, Hkv, D, float(rope_base), _DT[q.dtype], _DT[o.dtype], _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream())
     ev = _events_arg(events, 6)
-    if window is not None:
+    if isinstance(window, AttnOpts):
+        _check(lib().ne_rope_attn_bwd_ex(*args[:15], ctypes.byref(window), *args[15:], ev))
+    elif window is not None:
         _check(lib().ne_rope_attn_bwd_window(*args[:15], window, *args[15:], ev))
     elif ev is None:
         _check(lib().ne_rope_attn_bwd(*args))
@@ -242,14 +278,15 @@ def _lens_arg(lens, B, device):
     return torch.tensor(list(lens), dtype=torch.int32, device=device)
 
 
-def ne_kv_cache_append(cache, cache_lens, k_new, v_new, Tcap, rope_base):
+def ne_kv_cache_append(cache, cache_lens, k_new, v_new, Tcap, rope_base, qk_norm=None):
     """Write k_new, v_new [B, Tn, Hkv, D] at positions cache_lens[b] .. of the cache."""
     _require_gpu(cache, k_new, v_new)
     B, Tn, Hkv, D = k_new.shape
     lens = _lens_arg(cache_lens, B, k_new.device)
+    opts = make_opts(0, qk_norm)
     _check(lib().ne_kv_cache_append(_ptr(cache), cache.numel() * cache.element_size(), _ptr(lens), _ptr(k_new),
-                                    _ptr(v_new), B, Tn, Tcap, Hkv, D, float(rope_base), _DT[k_new.dtype],
-                                    _stream()))
+                                    _ptr(v_new), B, Tn, Tcap, Hkv, D, float(rope_base), ctypes.byref(opts),
+                                    _DT[k_new.dtype], _stream()))
     return lens
 
 
@@ -258,7 +295,7 @@ def decode_workspace_bytes(B, Tq, Tcap, Hq, Hkv, D, in_dtype):
 
 
 def ne_rope_attn_decode(q, cache, cache_lens, Tcap, Hkv, rope_base, window=0, out_dtype=torch.float32,
-                        o=None, lse=None, workspace=None, events=None):
+                        o=None, lse=None, workspace=None, events=None, qk_norm=None):
     """o, lse for the queries q [B, Tq, Hq, D] at positions cache_lens[b] + t against the cache.
 
     events: optional 4 events (or None entries) around the two launches."""
@@ -271,8 +308,9 @@ def ne_rope_attn_decode(q, cache, cache_lens, Tcap, Hkv, rope_base, window=0, ou
         lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = alloc_workspace(decode_workspace_bytes(B, Tq, Tcap, Hq, Hkv, D, q.dtype), q.device)
+    opts = make_opts(window, qk_norm)
     _check(lib().ne_rope_attn_decode(_ptr(q), _ptr(cache), cache.numel() * cache.element_size(), _ptr(lens),
-                                     _ptr(o), _ptr(lse), B, Tq, Tcap, Hq, Hkv, D, float(rope_base), int(window),
+                                     _ptr(o), _ptr(lse), B, Tq, Tcap, Hq, Hkv, D, float(rope_base), ctypes.byref(opts),
                                      _DT[q.dtype], _DT[o.dtype], _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(),
                                      _events_arg(events, 4)))

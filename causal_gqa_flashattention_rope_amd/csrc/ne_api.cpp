@@ -28,7 +28,7 @@ constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t qh, kh, vh, dOh, delta, lse2, table, total;
+    size_t qh, kh, vh, dOh, delta, lse2, rq, rk, table, total;
 };
 
 bool dtype_ok(ne_dtype_t in, ne_dtype_t out) {
@@ -66,6 +66,8 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, ne_dtype_t in) {
         L.dOh = off; off += up(nq * esz);
         L.delta = off; off += up((size_t)B * T * Hq * 4);
         L.lse2 = off; off += up((size_t)B * T * Hq * 4);
+        L.rq = off; off += up((size_t)B * T * Hq * 4);
+        L.rk = off; off += up((size_t)B * T * Hkv * 4);
     }
     L.table = off; off += up((size_t)T * (D / 2) * 8);
     L.total = off;
@@ -76,6 +78,17 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Keys a query sees at most: the window, or the whole causal prefix when window <= 0 or >= T.
 int visible_keys(int window, int T) { return (window <= 0 || window >= T) ? T : window; }
+
+const ne_attn_opts_t kNoOpts = {0, 0, 1.0f, 0.0f};
+
+ne_status_t check_opts(const ne_attn_opts_t* o, ne::QkNorm* qkn) {
+    qkn->on = o->qk_norm != 0;
+    qkn->gain = o->qk_gain;
+    qkn->eps = o->qk_eps;
+    if (qkn->on && (!std::isfinite(o->qk_gain) || !std::isfinite(o->qk_eps) || o->qk_eps < 0.f))
+        return fail(NE_ERR_SHAPE, "qk_gain must be finite and qk_eps finite and >= 0");
+    return NE_OK;
+}
 
 ne_status_t common_checks(int B, int T, int Hq, int Hkv, int D, ne_dtype_t in, ne_dtype_t out) {
     ne_status_t s = check_shape(B, T, Hq, Hkv, D);
@@ -123,7 +136,7 @@ size_t ne_rope_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_
 namespace {
 
 ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
-                     int B, int T, int Hq, int Hkv, int head_dim, double rope_base, int window,
+                     int B, int T, int Hq, int Hkv, int head_dim, double rope_base, const ne_attn_opts_t* opts,
                      ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                      void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     if (!q || !k || !v || !o || !lse || !workspace)
@@ -134,6 +147,9 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
         !aligned16(workspace))
         return fail(NE_ERR_ALIGN, "ne_rope_attn_fwd: every pointer must be 16-byte aligned");
     if (!std::isfinite(rope_base)) return fail(NE_ERR_SHAPE, "rope_base must be finite");
+    if (!opts) opts = &kNoOpts;
+    ne::QkNorm qkn{};
+    if ((s = check_opts(opts, &qkn)) != NE_OK) return s;
     const Layout L = layout(false, B, T, Hq, Hkv, head_dim, in_dtype);
     if (workspace_bytes < L.total)
         return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
@@ -145,11 +161,13 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     pa.B = B; pa.T = T; pa.Hq = Hq; pa.Hkv = Hkv; pa.D = head_dim;
     pa.rope_base = rope_base;
     pa.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    pa.qkn = qkn;
     ne::FwdArgs fa{};
     fa.q = q; fa.kh = pa.kh; fa.vh = pa.vh; fa.table = pa.table; fa.o = o; fa.lse = lse;
     fa.rope_base = rope_base; fa.qscale = pa.qscale;
     fa.B = B; fa.T = T; fa.Hq = Hq; fa.Hkv = Hkv; fa.G = G;
-    fa.window = visible_keys(window, T);
+    fa.window = visible_keys(opts->window, T);
+    fa.qkn = qkn;
     fa.nrb = (int)(((int64_t)T * G + 127) / 128);
     hipError_t e = ne::launch_fwd((int)in_dtype, (int)out_dtype, head_dim, pa, fa, (hipStream_t)stream,
                                   (hipEvent_t const*)events);
@@ -159,7 +177,7 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
 
 ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* dO, void* dq, void* dk, void* dv,
-                     int B, int T, int Hq, int Hkv, int head_dim, double rope_base, int window,
+                     int B, int T, int Hq, int Hkv, int head_dim, double rope_base, const ne_attn_opts_t* opts,
                      ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                      void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
@@ -170,6 +188,9 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
         !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
         return fail(NE_ERR_ALIGN, "ne_rope_attn_bwd: every pointer must be 16-byte aligned");
     if (!std::isfinite(rope_base)) return fail(NE_ERR_SHAPE, "rope_base must be finite");
+    if (!opts) opts = &kNoOpts;
+    ne::QkNorm qkn{};
+    if ((s = check_opts(opts, &qkn)) != NE_OK) return s;
     const Layout L = layout(true, B, T, Hq, Hkv, head_dim, in_dtype);
     if (workspace_bytes < L.total)
         return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
@@ -179,15 +200,20 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     pa.q = q; pa.k = k; pa.v = v; pa.o = o; pa.lse = lse; pa.dO = dO;
     pa.qh = ws + L.qh; pa.kh = ws + L.kh; pa.vh = ws + L.vh; pa.dOh = ws + L.dOh;
     pa.delta = (float*)(ws + L.delta); pa.lse2 = (float*)(ws + L.lse2); pa.table = (float2*)(ws + L.table);
+    pa.rq = (float*)(ws + L.rq); pa.rk = (float*)(ws + L.rk);
     pa.B = B; pa.T = T; pa.Hq = Hq; pa.Hkv = Hkv; pa.D = head_dim;
     pa.rope_base = rope_base;
     pa.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+    pa.qkn = qkn;
     ne::BwdArgs ba{};
     ba.qh = pa.qh; ba.kh = pa.kh; ba.vh = pa.vh; ba.dOh = pa.dOh;
     ba.delta = pa.delta; ba.lse2 = pa.lse2; ba.table = pa.table;
     ba.dq = dq; ba.dk = dk; ba.dv = dv;
     ba.B = B; ba.T = T; ba.Hq = Hq; ba.Hkv = Hkv; ba.G = G;
-    ba.window = visible_keys(window, T);
+    ba.window = visible_keys(opts->window, T);
+    ba.qkn = qkn;
+    ba.q = q; ba.k = k; ba.in_dt = (int)in_dtype;
+    ba.rq = pa.rq; ba.rk = pa.rk;
     ba.nrb = (int)(((int64_t)T * G + 127) / 128);
     ba.rope_base = rope_base;
     ba.scale = (float)(1.0 / std::sqrt((double)head_dim));
@@ -205,7 +231,7 @@ ne_status_t ne_rope_attn_fwd(const void* q, const void* k, const void* v, void* 
                              int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
                              ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, 0, in_dtype, out_dtype, workspace,
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, nullptr, in_dtype, out_dtype, workspace,
                     workspace_bytes, stream, nullptr);
 }
 
@@ -214,8 +240,8 @@ ne_status_t ne_rope_attn_bwd(const void* q, const void* k, const void* v, const 
                              int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
                              ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, 0, in_dtype, out_dtype,
-                    workspace, workspace_bytes, stream, nullptr);
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, nullptr, in_dtype,
+                    out_dtype, workspace, workspace_bytes, stream, nullptr);
 }
 
 ne_status_t ne_rope_attn_fwd_timed(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -224,7 +250,7 @@ ne_status_t ne_rope_attn_fwd_timed(const void* q, const void* k, const void* v, 
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    void* const* events) {
     if (!events) return fail(NE_ERR_NULL, "ne_rope_attn_fwd_timed: events must be non-null");
-    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, 0, in_dtype, out_dtype, workspace,
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, nullptr, in_dtype, out_dtype, workspace,
                     workspace_bytes, stream, events);
 }
 
@@ -235,8 +261,8 @@ ne_status_t ne_rope_attn_bwd_timed(const void* q, const void* k, const void* v, 
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    void* const* events) {
     if (!events) return fail(NE_ERR_NULL, "ne_rope_attn_bwd_timed: events must be non-null");
-    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, 0, in_dtype, out_dtype,
-                    workspace, workspace_bytes, stream, events);
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, nullptr, in_dtype,
+                    out_dtype, workspace, workspace_bytes, stream, events);
 }
 
 ne_status_t ne_rope_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -244,8 +270,26 @@ ne_status_t ne_rope_attn_fwd_window(const void* q, const void* k, const void* v,
                                     ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     void* const* events) {
-    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, window, in_dtype, out_dtype,
+    const ne_attn_opts_t opts = {window, 0, 1.0f, 0.0f};
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, &opts, in_dtype, out_dtype,
                     workspace, workspace_bytes, stream, events);
+}
+
+ne_status_t ne_rope_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                                const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, opts, in_dtype, out_dtype,
+                    workspace, workspace_bytes, stream, events);
+}
+
+ne_status_t ne_rope_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                const void* dO, void* dq, void* dk, void* dv,
+                                int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                                const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, opts, in_dtype,
+                    out_dtype, workspace, workspace_bytes, stream, events);
 }
 
 ne_status_t ne_rope_attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
@@ -254,7 +298,8 @@ ne_status_t ne_rope_attn_bwd_window(const void* q, const void* k, const void* v,
                                     ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     void* const* events) {
-    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, window, in_dtype,
+    const ne_attn_opts_t opts = {window, 0, 1.0f, 0.0f};
+    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, &opts, in_dtype,
                     out_dtype, workspace, workspace_bytes, stream, events);
 }
 
@@ -338,7 +383,7 @@ size_t ne_kv_cache_bytes(int B, int Tcap, int Hkv, int head_dim, ne_dtype_t in_d
 
 ne_status_t ne_kv_cache_append(void* cache, size_t cache_bytes, const int* cache_lens, const void* k_new,
                                const void* v_new, int B, int Tn, int Tcap, int Hkv, int head_dim, double rope_base,
-                               ne_dtype_t in_dtype, void* stream) {
+                               const ne_attn_opts_t* opts, ne_dtype_t in_dtype, void* stream) {
     if (!cache || !cache_lens || !k_new || !v_new)
         return fail(NE_ERR_NULL, "ne_kv_cache_append: cache, cache_lens, k_new and v_new must be non-null");
     ne_status_t s = check_cache_shape(B, Tcap, Hkv, head_dim);
@@ -352,7 +397,10 @@ ne_status_t ne_kv_cache_append(void* cache, size_t cache_bytes, const int* cache
     if (cache_bytes < ne_kv_cache_bytes(B, Tcap, Hkv, head_dim, in_dtype))
         return fail(NE_ERR_WORKSPACE, "cache of %zu bytes < %zu required", cache_bytes,
                     ne_kv_cache_bytes(B, Tcap, Hkv, head_dim, in_dtype));
+    ne::QkNorm qkn{};
+    if ((s = check_opts(opts ? opts : &kNoOpts, &qkn)) != NE_OK) return s;
     ne::AppendArgs a{};
+    a.qkn = qkn;
     a.k = k_new; a.v = v_new; a.cache = cache; a.lens = cache_lens;
     a.B = B; a.Tn = Tn; a.Tcap = Tcap; a.Hkv = Hkv; a.rope_base = rope_base;
     for (int i = 0; i < head_dim / 2; ++i)
@@ -371,7 +419,7 @@ size_t ne_rope_attn_decode_workspace_bytes(int B, int Tq, int Tcap, int Hq, int 
 
 ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_bytes, const int* cache_lens,
                                 void* o, float* lse, int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
-                                double rope_base, int window, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                double rope_base, const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                                 void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     if (!q || !cache || !cache_lens || !o || !lse || !workspace)
         return fail(NE_ERR_NULL, "ne_rope_attn_decode: q, cache, cache_lens, o, lse and workspace must be non-null");
@@ -387,6 +435,9 @@ ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_b
     if (cache_bytes < ne_kv_cache_bytes(B, Tcap, Hkv, head_dim, in_dtype))
         return fail(NE_ERR_WORKSPACE, "cache of %zu bytes < %zu required", cache_bytes,
                     ne_kv_cache_bytes(B, Tcap, Hkv, head_dim, in_dtype));
+    if (!opts) opts = &kNoOpts;
+    ne::QkNorm qkn{};
+    if ((s = check_opts(opts, &qkn)) != NE_OK) return s;
     const DecodeLayout L = decode_layout(B, Tq, Tcap, Hq, Hkv, head_dim);
     if (workspace_bytes < L.total)
         return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
@@ -397,7 +448,8 @@ ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_b
     a.o = o; a.lse = lse;
     a.B = B; a.Tq = Tq; a.Tcap = Tcap; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
     a.nrb = L.nrb; a.nsplit = L.nsplit;
-    a.window = visible_keys(window, Tcap);
+    a.window = visible_keys(opts->window, Tcap);
+    a.qkn = qkn;
     a.rope_base = rope_base;
     a.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
     for (int i = 0; i < head_dim / 2; ++i)

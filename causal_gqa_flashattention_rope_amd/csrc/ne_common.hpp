@@ -35,6 +35,35 @@ constexpr float kLn2 = 0.6931471805599453f;
 // and exp2(kMFloor - m) = 0 when a real maximum m replaces it.
 constexpr float kMFloor = -1.0e30f;
 
+// QK norm: the factor gain / sqrt(mean(x^2) + eps) of a row of D elements whose squares sum to ss.
+__device__ __forceinline__ float qk_factor(float ss, int D, float gain, float eps) {
+    return gain / sqrtf(ss / (float)D + eps);
+}
+// Sum of squares of a row of D elements (16-byte loads), read whole by the calling thread.
+template <typename TI>
+__device__ __forceinline__ float row_sumsq(const TI* row, int D) {
+    float ss = 0.f;
+    if constexpr (sizeof(TI) == 4) {
+        for (int d = 0; d < D; d += 4) {
+            const floatx4 x = *reinterpret_cast<const floatx4*>(row + d);
+            ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+        }
+    } else {
+        typedef TI v8 __attribute__((ext_vector_type(8)));
+        for (int d = 0; d < D; d += 8) {
+            const v8 x = *reinterpret_cast<const v8*>(row + d);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += (float)x[e] * (float)x[e];
+        }
+    }
+    return ss;
+}
+// Sum over the n consecutive lanes (n a power of two dividing 64) that hold one row.
+__device__ __forceinline__ float sum_lanes(float x, int n) {
+    for (int off = 1; off < n; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
 // Query t sees key j iff t - W < j <= t (W = the window, 1..T; W = T is the causal prefix).
 __device__ __forceinline__ bool visible(int j, int t, int W) { return (unsigned)(t - j) < (unsigned)W; }
 
@@ -62,6 +91,47 @@ __device__ __forceinline__ float max_halves(float x) {
 __device__ __forceinline__ float sum_halves(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Four consecutive elements base[off .. off + 3] of an array of dtype dt (0 f32, 1 bf16, 2 f16).
+__device__ __forceinline__ floatx4 load4_dt(const void* base, size_t off, int dt) {
+    if (dt == 0) return *reinterpret_cast<const floatx4*>((const float*)base + off);
+    if (dt == 1) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 v = *reinterpret_cast<const bf16x4*>((const __bf16*)base + off);
+        return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    }
+    const half4v v = *reinterpret_cast<const half4v*>((const _Float16*)base + off);
+    return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+// QK-norm backward of one row held in the 32x32 accumulator layout: lane (h, c) holds the values at
+// d = 32 db + 8 q4 + 4 h + e (the other half of the row in lane c ^ 32, which must be active too).
+// On entry y is the gradient with respect to the normalised row gain * rho * x, on return with
+// respect to x: gain * rho * (y - x * rho^2 * (y . x) / D).  x = base[off ..] in dtype dt.
+template <int NDB>
+__device__ __forceinline__ void qk_norm_bwd_row(floatx16 (&y)[NDB], const void* base, size_t off, int dt, float rho,
+                                                float gain, int h) {
+    constexpr int D = 32 * NDB;
+    float dot = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const floatx4 x = load4_dt(base, off + 32 * db + 8 * q4 + 4 * h, dt);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dot += y[db][4 * q4 + e] * x[e];
+        }
+    dot = sum_halves(dot);
+    const float c1 = gain * rho, c2 = rho * rho * dot / (float)D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const floatx4 x = load4_dt(base, off + 32 * db + 8 * q4 + 4 * h, dt);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[db][4 * q4 + e] = c1 * (y[db][4 * q4 + e] - x[e] * c2);
+        }
 }
 
 // ---- MFMA operand traits ----------------------------------------------------------------

@@ -69,11 +69,20 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     _Float16* vtc = (_Float16*)a.cache + (size_t)a.B * a.Hkv * Tcap * D + (size_t)grp * D * Tcap;
     for (int idx = threadIdx.x; idx < TB * CPR; idx += 256) {
         const int tl = idx / CPR, chunk = idx % CPR, t = t0 + tl;
-        if (t >= Tn) continue;
-        const size_t in_off = (((size_t)b * Tn + t) * a.Hkv + hkv) * D + chunk * 8;
-        const int p = len + t;
+        const size_t in_off = (((size_t)b * Tn + min(t, Tn - 1)) * a.Hkv + hkv) * D + chunk * 8;
         float x[8];
         load8_in((const TI*)a.k + in_off, x);
+        float fac = 1.f;  // QK norm of this key row (its chunks sit in consecutive lanes)
+        if (a.qkn.on) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+            fac = qk_factor(sum_lanes(ss, CPR), D, a.qkn.gain, a.qkn.eps);
+        }
+        if (t >= Tn) continue;
+        const int p = len + t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= fac;
         if (rope) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -162,10 +171,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     for (int idx = tid; idx < 32 * CPR; idx += 256) {
         const int r = idx / CPR, chunk = idx % CPR;
         half8 out = half8{};
+        const int Rr = R0 + min(r, nvalid - 1), t = Rr / G, hq = hkv * G + (Rr - t * G);
+        float x[8];
+        load8_in((const TI*)a.q + (((size_t)b * Tq + t) * a.Hq + hq) * D + chunk * 8, x);
+        float mul = a.qscale;  // times the QK norm of this query row (its chunks in consecutive lanes)
+        if (a.qkn.on) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+            mul *= qk_factor(sum_lanes(ss, CPR), D, a.qkn.gain, a.qkn.eps);
+        }
         if (r < nvalid) {
-            const int Rr = R0 + r, t = Rr / G, hq = hkv * G + (Rr - t * G);
-            float x[8];
-            load8_in((const TI*)a.q + (((size_t)b * Tq + t) * a.Hq + hq) * D + chunk * 8, x);
             if (rope) {
                 const int p = len + t;
 #pragma unroll
@@ -177,7 +193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) out[e] = (_Float16)(x[e] * a.qscale);
+            for (int e = 0; e < 8; ++e) out[e] = (_Float16)(x[e] * mul);
         }
         *reinterpret_cast<half8*>(&sq[r][chunk * 8]) = out;
     }

@@ -62,6 +62,20 @@ __device__ __forceinline__ void rope_cs_fill(float2* cs, double* theta, int t0, 
     }
 }
 
+// Eight consecutive input elements as fp32, with 16-byte loads.
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(p), b = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+}
+template <typename T16>
+__device__ __forceinline__ void load8(const T16* p, float (&x)[8]) {
+    typedef T16 v8 __attribute__((ext_vector_type(8)));
+    const v8 a = *reinterpret_cast<const v8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+}
+
 template <typename TI, typename OP, int D, bool ROT>
 __device__ __forceinline__ void convert8(const TI* src, OP* dst, const float2* cs_row, int chunk, float mul) {
     // 8 consecutive elements: chunk*8 .. chunk*8+7, pairs (2i, 2i+1) rotated by cs_row[i].
@@ -115,19 +129,40 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         const float2* csr = cs + tl * (D / 2);
         float part = 0.f;  // Delta partial (dO rows only)
         int dO_row = -1;
+        // QK norm: the factor gain / rms of this thread's q or k row (its CPR chunks sit in
+        // consecutive lanes), and 1/rms kept for the backward's epilogues
+        float fac = 1.f;
+        if (a.qkn.on) {
+            float ss = 0.f;
+            if (live && which < Hq + Hkv) {
+                const TI* src = which < Hq ? (const TI*)a.q + (((size_t)b * T + t) * Hq + which) * D
+                                           : (const TI*)a.k + (((size_t)b * T + t) * Hkv + (which - Hq)) * D;
+                float x[8];
+                load8(src + chunk * 8, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+            }
+            ss = sum_lanes(ss, CPR);
+            const float rho = 1.f / sqrtf(ss / (float)D + a.qkn.eps);
+            fac = a.qkn.gain * rho;
+            if (BWD && live && chunk == 0 && which < Hq + Hkv) {
+                if (which < Hq) a.rq[((size_t)b * Hkv + which / G) * TG + (size_t)t * G + which % G] = rho;
+                else a.rk[((size_t)b * Hkv + (which - Hq)) * T + t] = rho;
+            }
+        }
         if (live) {
             if (which < Hq) {  // q -> q~ (rotated, scaled by scale*log2e), flattened rows
                 const int hq = which, g = hq / G, hh = hq % G;
                 const TI* src = (const TI*)a.q + (((size_t)b * T + t) * Hq + hq) * D + chunk * 8;
                 OP* dst = (OP*)a.qh + (((size_t)b * Hkv + g) * TG + (size_t)t * G + hh) * D + chunk * 8;
-                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, a.qscale);
-                else convert8<TI, OP, D, false>(src, dst, csr, chunk, a.qscale);
+                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, a.qscale * fac);
+                else convert8<TI, OP, D, false>(src, dst, csr, chunk, a.qscale * fac);
             } else if (which < Hq + Hkv) {  // k -> k'
                 const int g = which - Hq;
                 const TI* src = (const TI*)a.k + (((size_t)b * T + t) * Hkv + g) * D + chunk * 8;
                 OP* dst = (OP*)a.kh + (((size_t)b * Hkv + g) * T + t) * D + chunk * 8;
-                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, 1.f);
-                else convert8<TI, OP, D, false>(src, dst, csr, chunk, 1.f);
+                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, fac);
+                else convert8<TI, OP, D, false>(src, dst, csr, chunk, fac);
             } else if (which < Hq + 2 * Hkv) {  // v -> v'
                 const int g = which - Hq - Hkv;
                 const TI* src = (const TI*)a.v + (((size_t)b * T + t) * Hkv + g) * D + chunk * 8;
@@ -162,20 +197,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
 }
 
-// Eight consecutive input elements as fp32, with 16-byte loads.
-__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
-    const floatx4 a = *reinterpret_cast<const floatx4*>(p), b = *reinterpret_cast<const floatx4*>(p + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
-}
-template <typename T16>
-__device__ __forceinline__ void load8(const T16* p, float (&x)[8]) {
-    typedef T16 v8 __attribute__((ext_vector_type(8)));
-    const v8 a = *reinterpret_cast<const v8*>(p);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
-}
-
 // Forward preparation for 16-bit operands.  grid (Tp / 64, B * Hkv), 256 threads: 64 tokens of
 // one (batch, KV head) group.  k' = fp16(R(k)) rows as [group][T][D]; v' = fp16(v) transposed to
 // [group][D][Tp] with the key order of vt_key_of_pos and zeros past T; the cos/sin table rows of
@@ -202,11 +223,21 @@ __global__ __launch_bounds__(256) void prep_fwd_h(PrepArgs a) {
     for (int idx = threadIdx.x; idx < TB * CPR; idx += 256) {
         const int tl = idx / CPR, chunk = idx % CPR, t = t0 + tl;
         float x[8];
+        float fac = 1.f;  // QK norm factor of this key row (its chunks sit in consecutive lanes)
+        if (a.qkn.on) {
+            float ss = 0.f;
+            if (t < T) {
+                load8((const TI*)a.k + (((size_t)b * T + t) * Hkv + hkv) * D + chunk * 8, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+            }
+            fac = qk_factor(sum_lanes(ss, CPR), D, a.qkn.gain, a.qkn.eps);
+        }
         if (t < T) {
             const size_t in_off = (((size_t)b * T + t) * Hkv + hkv) * D + chunk * 8;
             _Float16* kdst = (_Float16*)a.kh + ((size_t)grp * T + t) * D + chunk * 8;
-            if (rope) convert8<TI, _Float16, D, true>((const TI*)a.k + in_off, kdst, cs + tl * (D / 2), chunk, 1.f);
-            else convert8<TI, _Float16, D, false>((const TI*)a.k + in_off, kdst, cs, chunk, 1.f);
+            if (rope) convert8<TI, _Float16, D, true>((const TI*)a.k + in_off, kdst, cs + tl * (D / 2), chunk, fac);
+            else convert8<TI, _Float16, D, false>((const TI*)a.k + in_off, kdst, cs, chunk, fac);
             load8((const TI*)a.v + in_off, x);
         } else {
 #pragma unroll
@@ -345,7 +376,9 @@ void fwd_kernel(FwdArgs a) {
     {
         const int t = min(t_lane, T - 1), hh = R - t_lane * G;
         const TI* qrow = (const TI*)a.q + (((size_t)b * T + t) * a.Hq + hkv * G + hh) * D;
-        load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, a.qscale, h, rvalid);
+        float qmul = a.qscale;
+        if (a.qkn.on && rvalid) qmul *= qk_factor(row_sumsq(qrow, D), D, a.qkn.gain, a.qkn.eps);
+        load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, qmul, h, rvalid);
     }
     wait_all();
     lds_fill<OP, D, BN, NW>(lds, kg, j0 * BN, T);
@@ -515,7 +548,9 @@ void fwd_kernel_h(FwdArgs a) {
     {
         const int t = min(t_lane, T - 1), hh = R - t_lane * G;
         const TI* qrow = (const TI*)a.q + (((size_t)b * T + t) * a.Hq + hkv * G + hh) * D;
-        load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, a.qscale, h, rvalid);
+        float qmul = a.qscale;
+        if (a.qkn.on && rvalid) qmul *= qk_factor(row_sumsq(qrow, D), D, a.qkn.gain, a.qkn.eps);
+        load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, qmul, h, rvalid);
     }
     wait_all();
     fill_k(j0);
@@ -917,8 +952,8 @@ void dkdv_kernel(BwdArgs a) {
                         floatx4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
         }
         __syncthreads();
-        if (rh == 0 && kvalid) {
-            TOUT* orow = (TOUT*)(role == 0 ? a.dv : a.dk) + (((size_t)b * T + key) * a.Hkv + hkv) * D;
+        if (rh == 0 && kvalid) {  // both lanes of a key pair (c, c + 32) agree
+            const size_t koff = (((size_t)b * T + key) * a.Hkv + hkv) * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -938,8 +973,16 @@ void dkdv_kernel(BwdArgs a) {
                             x0 = y0; x1 = y1; x2 = y2; x3 = y3;
                         }
                     }
-                    store4(orow + d, x0, x1, x2, x3);
+                    acc[db][4 * q4] = x0; acc[db][4 * q4 + 1] = x1; acc[db][4 * q4 + 2] = x2; acc[db][4 * q4 + 3] = x3;
                 }
+            if (role == 1 && a.qkn.on) qk_norm_bwd_row<NDB>(acc, a.k, koff, a.in_dt, a.rk[grp * (size_t)T + key], a.qkn.gain, h);
+            TOUT* orow = (TOUT*)(role == 0 ? a.dv : a.dk) + koff;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    store4(orow + 32 * db + 8 * q4 + 4 * h, acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2],
+                           acc[db][4 * q4 + 3]);
         }
         __syncthreads();  // the staging area is refilled by the next key block
     }
@@ -1159,8 +1202,8 @@ void dkdv_kernel_h(BwdArgs a) {
                         floatx4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
         }
         __syncthreads();
-        if (rh == 0 && kvalid) {
-            TOUT* orow = (TOUT*)(role == 0 ? a.dv : a.dk) + (((size_t)b * T + key) * a.Hkv + hkv) * D;
+        if (rh == 0 && kvalid) {  // both lanes of a key pair (c, c + 32) agree
+            const size_t koff = (((size_t)b * T + key) * a.Hkv + hkv) * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1180,8 +1223,16 @@ void dkdv_kernel_h(BwdArgs a) {
                             x0 = y0; x1 = y1; x2 = y2; x3 = y3;
                         }
                     }
-                    store4(orow + d, x0, x1, x2, x3);
+                    acc[db][4 * q4] = x0; acc[db][4 * q4 + 1] = x1; acc[db][4 * q4 + 2] = x2; acc[db][4 * q4 + 3] = x3;
                 }
+            if (role == 1 && a.qkn.on) qk_norm_bwd_row<NDB>(acc, a.k, koff, a.in_dt, a.rk[grp * (size_t)T + key], a.qkn.gain, h);
+            TOUT* orow = (TOUT*)(role == 0 ? a.dv : a.dk) + koff;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    store4(orow + 32 * db + 8 * q4 + 4 * h, acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2],
+                           acc[db][4 * q4 + 3]);
         }
         __syncthreads();  // the staging area is refilled by the next key block
     }
@@ -1301,11 +1352,12 @@ void dq_kernel(BwdArgs a) {
         }
     }
 
-    if (!rvalid) return;
+    if (!rvalid) return;  // both lanes of a row pair (c, c + 32) agree
     const int t = t_lane, hh = R - t * G, hq = hkv * G + hh;
-    TOUT* dqrow = (TOUT*)a.dq + (((size_t)b * T + t) * a.Hq + hq) * D;
+    const size_t qoff = (((size_t)b * T + t) * a.Hq + hq) * D;
     const float sc = a.scale;
     const bool rope = a.rope_base > 0.0;
+    // dq = R^T (scale * dq'), in place
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1320,8 +1372,16 @@ void dq_kernel(BwdArgs a) {
                 const float y2 = x2 * r1.x + x3 * r1.y, y3 = -x2 * r1.y + x3 * r1.x;
                 x0 = y0; x1 = y1; x2 = y2; x3 = y3;
             }
-            store4(dqrow + d, x0, x1, x2, x3);
+            dq[db][4 * q4] = x0; dq[db][4 * q4 + 1] = x1; dq[db][4 * q4 + 2] = x2; dq[db][4 * q4 + 3] = x3;
         }
+    if (a.qkn.on) qk_norm_bwd_row<NDB>(dq, a.q, qoff, a.in_dt, a.rq[grp * (size_t)TG + R], a.qkn.gain, h);
+    TOUT* dqrow = (TOUT*)a.dq + qoff;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            store4(dqrow + 32 * db + 8 * q4 + 4 * h, dq[db][4 * q4], dq[db][4 * q4 + 1], dq[db][4 * q4 + 2],
+                   dq[db][4 * q4 + 3]);
 }
 
 // =====================================================================================
@@ -1332,9 +1392,10 @@ void dq_kernel(BwdArgs a) {
 // chains (S^T and dP^T, two 32-key halves each) advance in turn, and every product's LDS operand
 // is read four products ahead.
 // =====================================================================================
-// WIN: a window shorter than T (its edge is masked too).  Without one the kernel keeps every
-// register for the causal case, where the budget is exhausted.
-template <int D, typename TOUT, bool WIN>
+// EXT: a window shorter than T (its edge is masked too) and/or the QK norm (its backward in the
+// epilogue).  Without them the kernel keeps every register for the plain causal case, where the
+// budget is exhausted.
+template <int D, typename TOUT, bool EXT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void dq_kernel_h(BwdArgs a) {
     using OP = _Float16;
@@ -1355,8 +1416,8 @@ void dq_kernel_h(BwdArgs a) {
     const int wave_tmin = Rw / G;
     const int wave_tmax = min(Rw + 31, TG - 1) / G;
     const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;
-    const int W = WIN ? a.window : T;
-    const int j0 = WIN ? max(0, R0 / G - W + 1) / BN : 0;  // the block's first key tile
+    const int W = EXT ? a.window : T;
+    const int j0 = EXT ? max(0, R0 / G - W + 1) / BN : 0;  // the block's first key tile
 
     const size_t grp = (size_t)wk.grp;
     const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
@@ -1417,7 +1478,7 @@ void dq_kernel_h(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = n0 + 32 * mb + acc_row(r, h);
-                if (WIN ? !visible(key, t_lane, W) : key > t_lane) x[0][r] = -INFINITY;
+                if (EXT ? !visible(key, t_lane, W) : key > t_lane) x[0][r] = -INFINITY;
             }
         };
         // the chains of half mb into x; with WITH_PREV, half 0's ALU work (from prev) in between
@@ -1462,11 +1523,12 @@ void dq_kernel_h(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    if (!rvalid) return;
+    if (!rvalid) return;  // both lanes of a row pair (c, c + 32) agree
     const int t = t_lane, hh = R - t * G, hq = hkv * G + hh;
-    TOUT* dqrow = (TOUT*)a.dq + (((size_t)b * T + t) * a.Hq + hq) * D;
+    const size_t qoff = (((size_t)b * T + t) * a.Hq + hq) * D;
     const float sc = a.scale;
     const bool rope = a.rope_base > 0.0;
+    // dq = R^T (scale * dq'), in place
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1481,8 +1543,16 @@ void dq_kernel_h(BwdArgs a) {
                 const float y2 = x2 * r1.x + x3 * r1.y, y3 = -x2 * r1.y + x3 * r1.x;
                 x0 = y0; x1 = y1; x2 = y2; x3 = y3;
             }
-            store4(dqrow + d, x0, x1, x2, x3);
+            dq[db][4 * q4] = x0; dq[db][4 * q4 + 1] = x1; dq[db][4 * q4 + 2] = x2; dq[db][4 * q4 + 3] = x3;
         }
+    if (EXT && a.qkn.on) qk_norm_bwd_row<NDB>(dq, a.q, qoff, a.in_dt, a.rq[grp * (size_t)TG + R], a.qkn.gain, h);
+    TOUT* dqrow = (TOUT*)a.dq + qoff;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            store4(dqrow + 32 * db + 8 * q4 + 4 * h, dq[db][4 * q4], dq[db][4 * q4 + 1], dq[db][4 * q4 + 2],
+                   dq[db][4 * q4 + 3]);
 }
 
 // =====================================================================================
@@ -1541,7 +1611,7 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
     NE_TRY(m.after(1));
     NE_TRY(m.before(2));
     if constexpr (sizeof(OP) == 2) {
-        if (ba.window < ba.T)
+        if (ba.window < ba.T || ba.qkn.on)
             hipLaunchKernelGGL((dq_kernel_h<D, TO, true>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
         else
             hipLaunchKernelGGL((dq_kernel_h<D, TO, false>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);

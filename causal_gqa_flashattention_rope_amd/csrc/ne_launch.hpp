@@ -5,15 +5,24 @@
 
 namespace ne {
 
+// QK norm: every (token, head) row x of q and k becomes gain * x / sqrt(mean(x^2) + eps).
+struct QkNorm {
+    int on;
+    float gain, eps;
+};
+
 // Operand preparation: rotate/scale/convert into the workspace copies.
 struct PrepArgs {
     const void* q; const void* k; const void* v;   // in dtype, [B][T][H][D]
     const void* o; const float* lse; const void* dO;  // backward only (o in out dtype)
     void* qh; void* kh; void* vh; void* dOh;        // operand copies (fp16 or fp32)
     float* delta; float* lse2; float2* table;       // backward only
+    float* rq; float* rk;                           // backward with QK norm: 1/rms of q rows
+                                                    // (flattened, [B*Hkv][T*G]) and k rows ([B*Hkv][T])
     int B, T, Hq, Hkv, D;
     double rope_base;
     float qscale;                                   // softmax scale * log2(e)
+    QkNorm qkn;
 };
 
 struct FwdArgs {
@@ -25,16 +34,21 @@ struct FwdArgs {
     int window;                                     // query t sees keys t - window + 1 .. t (1..T)
     double rope_base;
     float qscale;                                   // softmax scale * log2(e)
+    QkNorm qkn;
 };
 
 struct BwdArgs {
     const void* qh; const void* kh; const void* vh; const void* dOh;
     const float* delta; const float* lse2; const float2* table;
     void* dq; void* dk; void* dv;
+    const void* q; const void* k;                   // raw inputs (QK norm backward), dtype in_dt
+    int in_dt;                                      // 0 f32, 1 bf16, 2 f16
+    const float* rq; const float* rk;               // 1/rms of the q and k rows (QK norm)
     int B, T, Hq, Hkv, G, nrb;
     int window;                                     // query t sees keys t - window + 1 .. t (1..T)
     double rope_base;
     float scale;                                    // softmax scale 1/sqrt(D)
+    QkNorm qkn;
 };
 
 // Cache append (decode path): k_new / v_new [B][Tn][Hkv][D] into the cache at positions
@@ -43,6 +57,7 @@ struct AppendArgs {
     const void* k; const void* v;
     void* cache; const int* lens;
     int B, Tn, Tcap, Hkv;
+    QkNorm qkn;
     double rope_base;
     double theta[64];                               // base^(-2i/D), i < D/2 (RoPE on)
 };
@@ -57,6 +72,7 @@ struct DecodeArgs {
     int window;                                     // 1..Tcap (Tcap: no window)
     double rope_base;
     float qscale;                                   // softmax scale * log2(e)
+    QkNorm qkn;
     double theta[64];                               // base^(-2i/D), i < D/2 (RoPE on)
 };
 

@@ -68,7 +68,8 @@ size_t ne_rope_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_
                                         ne_dtype_t in_dtype);
 
 /* Bytes of device workspace the backward needs (operand copies, the per-row
- * Delta = rowsum(dO * o), the log2-scaled lse and the cos/sin table). */
+ * Delta = rowsum(dO * o), the log2-scaled lse, the per-row 1/rms of q and k used by the QK norm
+ * and the cos/sin table). */
 size_t ne_rope_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim,
                                         ne_dtype_t in_dtype);
 
@@ -111,6 +112,37 @@ ne_status_t ne_rope_attn_bwd_timed(const void* q, const void* k, const void* v,
                                    ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    void* const* events);
+
+/* Options of the *_ex calls and of the cache calls (a NULL pointer means all defaults: no window,
+ * no QK norm). */
+typedef struct {
+    int window;     /* > 0: query t sees keys t - window + 1 .. t; <= 0: the whole causal prefix   */
+    int qk_norm;    /* nonzero: QK norm -- every (token, head) row x of q and of k is replaced by
+                       qk_gain * x / sqrt(mean(x^2) + qk_eps) before RoPE ("nanochat 全栈 LLM 训练实践
+                       指南", section 模型架构速览: q and k normalised and scaled up by 1.2); the
+                       backward returns gradients with respect to the raw q and k                     */
+    float qk_gain;  /* 1.2 in the guide; finite                                                       */
+    float qk_eps;   /* added to the mean square; finite, >= 0 (0 with an all-zero row: non-finite)    */
+} ne_attn_opts_t;
+
+/* The forward and backward with every option (window and QK norm).  Arguments as in
+ * ne_rope_attn_fwd / ne_rope_attn_bwd; opts may be NULL; events NULL or as for the *_timed calls.
+ * The backward must be given the options the forward used. */
+ne_status_t ne_rope_attn_fwd_ex(const void* q, const void* k, const void* v,
+                                void* o, float* lse,
+                                int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                                const ne_attn_opts_t* opts,
+                                ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* events);
+ne_status_t ne_rope_attn_bwd_ex(const void* q, const void* k, const void* v,
+                                const void* o, const float* lse, const void* dO,
+                                void* dq, void* dk, void* dv,
+                                int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                                const ne_attn_opts_t* opts,
+                                ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                void* const* events);
 
 /* Sliding-window attention: the same operation with each query seeing only the `window` most
  * recent keys, its own position included -- query t sees keys t - window + 1 .. t -- as in the
@@ -161,25 +193,27 @@ ne_status_t ne_rope_attn_bwd_window(const void* q, const void* k, const void* v,
 size_t ne_kv_cache_bytes(int B, int Tcap, int Hkv, int head_dim, ne_dtype_t in_dtype);
 
 /* Writes k_new, v_new ([B][Tn][Hkv][head_dim], in_dtype) into the cache at positions
- * cache_lens[b] .. cache_lens[b] + Tn - 1, keys rotated at those positions. */
+ * cache_lens[b] .. cache_lens[b] + Tn - 1, keys rotated at those positions (after the QK norm when
+ * opts asks for it; opts may be NULL; its window is not used here). */
 ne_status_t ne_kv_cache_append(void* cache, size_t cache_bytes, const int* cache_lens,
                                const void* k_new, const void* v_new,
                                int B, int Tn, int Tcap, int Hkv, int head_dim, double rope_base,
-                               ne_dtype_t in_dtype, void* stream);
+                               const ne_attn_opts_t* opts, ne_dtype_t in_dtype, void* stream);
 
 size_t ne_rope_attn_decode_workspace_bytes(int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
                                            ne_dtype_t in_dtype);
 
 /* o [B][Tq][Hq][head_dim] (out_dtype F32 or in_dtype), lse [B][Hq][Tq] for the queries q
  * ([B][Tq][Hq][head_dim], in_dtype) at positions cache_lens[b] + t against the cache, whose
- * positions up to cache_lens[b] + Tq - 1 must have been appended.  The keys are split into slices
+ * positions up to cache_lens[b] + Tq - 1 must have been appended (with the same QK-norm options;
+ * opts may be NULL; a window counts positions as in the *_ex calls).  The keys are split into slices
  * processed by separate workgroups and merged by the log-sum-exp rule in a fixed order
  * (deterministic).  events: NULL or 4 hipEvent_t entries (pairs around the attention and the
  * merge; null entries are skipped). */
 ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_bytes, const int* cache_lens,
                                 void* o, float* lse,
                                 int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
-                                double rope_base, int window,
+                                double rope_base, const ne_attn_opts_t* opts,
                                 ne_dtype_t in_dtype, ne_dtype_t out_dtype,
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 void* const* events);

@@ -50,7 +50,7 @@ def test_workspace_sizes(L):
     fwd = L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
     assert fwd == 2 * up(2 * nk) + table
     bwd = L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
-    assert bwd == 2 * up(2 * nq) + 2 * up(2 * nk) + 2 * up(4 * B * T * Hq) + table
+    assert bwd == 2 * up(2 * nq) + 2 * up(2 * nk) + 3 * up(4 * B * T * Hq) + up(4 * B * T * Hkv) + table
     assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_F32) == 2 * up(4 * nk) + table
     # ragged T: the forward's transposed V' copy pads every row of keys to a multiple of 64
     Tr = 100
@@ -139,8 +139,9 @@ def decode_call(L, q=FAKE, cache=FAKE, cb=1 << 40, lens=FAKE, o=FAKE, lse=FAKE, 
                 Hkv=2, D=64, base=1e4, W=0, i=binding.NE_BF16, out=binding.NE_F32, ws=FAKE, wsb=None):
     if wsb is None:
         wsb = L.ne_rope_attn_decode_workspace_bytes(B, Tq, Tcap, Hq, Hkv, D, i) if D in (32, 64, 128) else 1 << 20
-    return L.ne_rope_attn_decode(q, cache, cb, lens, o, lse, B, Tq, Tcap, Hq, Hkv, D, base, W, i, out, ws, wsb,
-                                 None, None)
+    opts = binding.make_opts(W)
+    return L.ne_rope_attn_decode(q, cache, cb, lens, o, lse, B, Tq, Tcap, Hq, Hkv, D, base, ctypes.byref(opts), i,
+                                 out, ws, wsb, None, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -164,4 +165,14 @@ def test_append_rejects_before_launch(L, kw, status):
              i=binding.NE_BF16)
     a.update(kw)
     assert L.ne_kv_cache_append(a["cache"], a["cb"], a["lens"], a["k"], a["v"], a["B"], a["Tn"], a["Tcap"],
-                                a["Hkv"], a["D"], a["base"], a["i"], None) == status
+                                a["Hkv"], a["D"], a["base"], None, a["i"], None) == status
+
+
+@pytest.mark.parametrize("qkn,status", [((float("nan"), 1e-6), 2), ((1.2, -1.0), 2), ((1.2, float("inf")), 2)])
+def test_ex_calls_reject_bad_qk_norm(L, qkn, status):
+    opts = binding.make_opts(0, qkn)
+    wsf = L.ne_rope_attn_fwd_workspace_bytes(1, 16, 4, 2, 64, binding.NE_BF16)
+    assert L.ne_rope_attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 4, 2, 64, 1e4, ctypes.byref(opts),
+                                 binding.NE_BF16, binding.NE_F32, FAKE, wsf, None, None) == status
+    assert L.ne_rope_attn_bwd_ex(*([FAKE] * 9), 1, 16, 4, 2, 64, 1e4, ctypes.byref(opts), binding.NE_BF16,
+                                 binding.NE_F32, FAKE, 1 << 30, None, None) == status

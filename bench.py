@@ -14,7 +14,8 @@ pass with every launch bracketed.  Prints one JSON line.
 
 After the headline measurement the same step is measured with a sliding window of --window keys
 (default T/4, the short window of the nanochat guide's window_pattern; 0 skips it), counting the
-visible pairs N_W = W(W+1)/2 + (T-W)W per head; it is reported under "sliding_window".
+visible pairs N_W = W(W+1)/2 + (T-W)W per head; it is reported under "sliding_window".  The causal
+step with the QK norm on (gain 1.2, eps 1e-6) is reported under "qk_norm".
 Then one decode step of the cached workload (--decode-batch sequences, each holding 8191 tokens of
 the long-context shape, Hq 32 / Hkv 8 / D 128, RoPE base 5e5, attending with one new token) is
 measured as HBM bandwidth: bytes = the visible cached keys and values (fp16) + q + o, reported
@@ -207,6 +208,7 @@ def main():
     ap.add_argument("--cpu-sample-batch", type=int, default=4)
     ap.add_argument("--window", type=int, default=-1,
                     help="window of the sliding-window measurement (-1: T/4; 0: skip it)")
+    ap.add_argument("--qk-norm", type=int, default=1, help="also measure the step with the QK norm on (0: skip)")
     ap.add_argument("--decode-batch", type=int, default=8,
                     help="sequences of the decode measurement (0: skip it)")
     args = ap.parse_args()
@@ -235,8 +237,14 @@ def main():
     wsf = binding.alloc_workspace(binding.fwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype), dev)
     wsb = binding.alloc_workspace(binding.bwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype), dev)
 
-    def make_step(window):
-        if window is None:
+    def make_step(window, qk_norm=None):
+        if qk_norm is not None:
+            def step(ev_f=None, ev_b=None):
+                binding.ne_rope_attn_fwd_ex(q, k, v, w.rope_base, window or 0, qk_norm, o=o, lse=lse, workspace=wsf,
+                                            events=ev_f)
+                binding.ne_rope_attn_bwd_ex(q, k, v, o, lse, dO, w.rope_base, window or 0, qk_norm, dq=dq, dk=dk,
+                                            dv=dv, workspace=wsb, events=ev_b)
+        elif window is None:
             def step(ev_f=None, ev_b=None):
                 binding.ne_rope_attn_fwd(q, k, v, w.rope_base, o=o, lse=lse, workspace=wsf, events=ev_f)
                 binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=wsb,
@@ -361,6 +369,14 @@ def main():
             "roofline": {"kernel": dom_w, "bound": "mfma", "achieved": round(ach_w, 2), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(ach_w / peak, 4), "traffic": None,
                          "flops_per_launch": kf_w[dom_w], "launch_ms": round(dom_ms_w, 4)},
+        }
+    if args.qk_norm:
+        # QK norm (gain 1.2, eps 1e-6): the same causal step, counting the same pairs
+        ms_q, dom_q, dom_ms_q, kern_q = measure(make_step(None, (1.2, 1e-6)), 20, K)
+        result["qk_norm"] = {
+            "gain": 1.2, "eps": 1e-6, "value": round(flops_step / (ms_q * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(ms_q, 4), "steps": K, "warmup": 20,
+            "kernel_ms": {n: round(t, 4) for n, t in kern_q.items()},
         }
     if args.decode_batch > 0:
         result["decode"] = measure_decode(args.decode_batch, K, hev, new_events)

@@ -13,6 +13,7 @@ import numpy as np
 
 from . import build as _build
 from .decode import decode_fwd, rope_rows  # noqa: F401  (numpy oracle of the cached-decode workload)
+from .qkv import qkv_rope_proj  # noqa: F401  (numpy oracle of the QKV projection with RoPE epilogue)
 
 _lib = None
 

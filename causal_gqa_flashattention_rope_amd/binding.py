@@ -23,6 +23,7 @@ EXPORTS = ("ne_rope_attn_fwd_workspace_bytes", "ne_rope_attn_bwd_workspace_bytes
            "ne_rope_attn_fwd_window", "ne_rope_attn_bwd_window",
            "ne_kv_cache_bytes", "ne_kv_cache_append", "ne_rope_attn_decode_workspace_bytes",
            "ne_rope_attn_decode", "ne_rope_attn_fwd_ex", "ne_rope_attn_bwd_ex",
+           "ne_qkv_rope_workspace_bytes", "ne_qkv_rope_proj",
            "ne_status_str", "ne_last_error", "ne_abi_version")
 
 
@@ -92,6 +93,10 @@ def lib():
     L.ne_rope_attn_decode.argtypes = ([vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, d, op, i, i, vp, sz, vp]
                                       + [ctypes.POINTER(vp)])
     L.ne_rope_attn_decode.restype = i
+    L.ne_qkv_rope_workspace_bytes.argtypes = [i, i]
+    L.ne_qkv_rope_workspace_bytes.restype = sz
+    L.ne_qkv_rope_proj.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, d, op, i, i, vp, sz, vp, ctypes.POINTER(vp)]
+    L.ne_qkv_rope_proj.restype = i
     L.ne_status_str.argtypes = [i]
     L.ne_status_str.restype = ctypes.c_char_p
     L.ne_last_error.argtypes = []
@@ -315,3 +320,31 @@ def ne_rope_attn_decode(q, cache, cache_lens, Tcap, Hkv, rope_base, window=0, ou
                                      workspace.numel() * workspace.element_size(), _stream(),
                                      _events_arg(events, 4)))
     return o, lse
+
+
+# ---------------------------------------------------------------------------------------------
+# QKV projection with the RoPE epilogue.
+# ---------------------------------------------------------------------------------------------
+def ne_qkv_rope_proj(x, w, Hq, Hkv, rope_base, qk_norm=None, out_dtype=torch.float32, q=None, k=None, v=None,
+                     workspace=None, events=None):
+    """q', k', v from x [B, T, C] and w [(Hq + 2 Hkv) D, C]: y = x w^T, RoPE (after the optional QK norm)
+    applied to the query and key heads in the product's epilogue."""
+    _require_gpu(x, w)
+    B, T, C = x.shape
+    N = w.shape[0]
+    D = N // (Hq + 2 * Hkv)
+    if w.shape[1] != C or D * (Hq + 2 * Hkv) != N:
+        raise ValueError("weight shape does not match C, Hq, Hkv")
+    if q is None:
+        q = torch.empty((B, T, Hq, D), dtype=out_dtype, device=x.device)
+    if k is None:
+        k = torch.empty((B, T, Hkv, D), dtype=out_dtype, device=x.device)
+    if v is None:
+        v = torch.empty((B, T, Hkv, D), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(int(lib().ne_qkv_rope_workspace_bytes(T, D)), x.device)
+    opts = make_opts(0, qk_norm)
+    _check(lib().ne_qkv_rope_proj(_ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v), B, T, C, Hq, Hkv, D, float(rope_base),
+                                  ctypes.byref(opts), _DT[x.dtype], _DT[q.dtype], _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(), _events_arg(events, 4)))
+    return q, k, v

@@ -461,3 +461,54 @@ ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_b
 }
 
 }  // extern "C"
+
+// =====================================================================================
+// QKV projection with the RoPE epilogue.
+// =====================================================================================
+extern "C" {
+
+size_t ne_qkv_rope_workspace_bytes(int T, int head_dim) {
+    if (T < 1 || (head_dim != 32 && head_dim != 64 && head_dim != 128)) return 0;
+    return up((size_t)T * (head_dim / 2) * 8);
+}
+
+ne_status_t ne_qkv_rope_proj(const void* x, const void* w, void* q, void* k, void* v,
+                             int B, int T, int C, int Hq, int Hkv, int head_dim, double rope_base,
+                             const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    if (!x || !w || !q || !k || !v || !workspace)
+        return fail(NE_ERR_NULL, "ne_qkv_rope_proj: x, w, q, k, v and workspace must be non-null");
+    if (B < 1 || T < 1 || C < 64 || Hq < 1 || Hkv < 1)
+        return fail(NE_ERR_SHAPE, "B=%d T=%d Hq=%d Hkv=%d must be >= 1 and C=%d >= 64", B, T, Hq, Hkv, C);
+    if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+        return fail(NE_ERR_UNSUPPORTED, "head_dim=%d not in {32, 64, 128}", head_dim);
+    if (C % 64 != 0) return fail(NE_ERR_SHAPE, "C=%d must be a multiple of 64", C);
+    const int64_t N = (int64_t)(Hq + 2 * Hkv) * head_dim, M = (int64_t)B * T;
+    if (N % 128 != 0) return fail(NE_ERR_SHAPE, "(Hq + 2 Hkv) * head_dim = %lld must be a multiple of 128", (long long)N);
+    if (std::max(M, N) * C * 2 >= ((int64_t)1 << 31))
+        return fail(NE_ERR_SHAPE, "B*T*C and N*C must stay below 2^30 elements");
+    if (!decode_dtype_ok(in_dtype, out_dtype))
+        return fail(NE_ERR_UNSUPPORTED, "ne_qkv_rope_proj: dtype pair in=%d out=%d is not supported",
+                    (int)in_dtype, (int)out_dtype);
+    if (!aligned16(x) || !aligned16(w) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(workspace))
+        return fail(NE_ERR_ALIGN, "ne_qkv_rope_proj: every pointer must be 16-byte aligned");
+    if (!std::isfinite(rope_base)) return fail(NE_ERR_SHAPE, "rope_base must be finite");
+    if (workspace_bytes < ne_qkv_rope_workspace_bytes(T, head_dim))
+        return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes,
+                    ne_qkv_rope_workspace_bytes(T, head_dim));
+    ne::QkNorm qkn{};
+    ne_status_t s = check_opts(opts ? opts : &kNoOpts, &qkn);
+    if (s != NE_OK) return s;
+    ne::QkvArgs a{};
+    a.x = x; a.w = w; a.q = q; a.k = k; a.v = v; a.table = (float2*)workspace;
+    a.M = (int)M; a.C = C; a.N = (int)N; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.D = head_dim;
+    a.rope_base = rope_base; a.qkn = qkn;
+    for (int i = 0; i < head_dim / 2; ++i)
+        a.theta[i] = rope_base > 0.0 ? std::pow(rope_base, -2.0 * i / head_dim) : 0.0;
+    hipError_t e = ne::launch_qkv((int)in_dtype, (int)out_dtype, head_dim, a, (hipStream_t)stream,
+                                  (hipEvent_t const*)events);
+    if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_qkv_rope_proj: launch failed: %s", hipGetErrorString(e));
+    return NE_OK;
+}
+
+}  // extern "C"

@@ -76,6 +76,17 @@ struct DecodeArgs {
     double theta[64];                               // base^(-2i/D), i < D/2 (RoPE on)
 };
 
+// QKV projection with the rotation (and QK norm) in the epilogue.
+struct QkvArgs {
+    const void* x; const void* w;                   // [M][C], [N][C] (in dtype)
+    void* q; void* k; void* v;                      // [M][H][D] (out dtype)
+    float2* table;                                  // cos/sin [T][D/2] (workspace)
+    int M, C, N, T, Hq, Hkv, D;
+    double rope_base;
+    QkNorm qkn;
+    double theta[64];                               // base^(-2i/D), i < D/2 (RoPE on)
+};
+
 // dtype codes follow ne_dtype_t: 0 = f32, 1 = bf16, 2 = f16.
 // ev (nullable): hipEvent_t pairs recorded on `s` around each kernel launch, in launch order
 // (forward: prep, fwd; backward: prep, dkdv, dq).
@@ -84,6 +95,8 @@ hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const Fw
 hipError_t launch_bwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const BwdArgs& ba, hipStream_t s,
                       hipEvent_t const* ev);
 hipError_t launch_append(int in_dt, int D, const AppendArgs& a, hipStream_t s);
+// ev (nullable): pairs around the cos/sin table and the product (4 entries).
+hipError_t launch_qkv(int in_dt, int out_dt, int D, const QkvArgs& a, hipStream_t s, hipEvent_t const* ev);
 // ev (nullable): pairs around the split kernel and the merge (4 entries).
 hipError_t launch_decode(int in_dt, int out_dt, int D, const DecodeArgs& a, hipStream_t s, hipEvent_t const* ev);
 

@@ -218,6 +218,26 @@ ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_b
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 void* const* events);
 
+/* ---- QKV projection with the RoPE epilogue ----------------------------------------------------
+ * The step before attention: y = x W^T for every token, then RoPE on the query and key heads --
+ * on the pages a tensor-core matrix product followed by a RoPE kernel of its own ("NanoEuler: 使用
+ * C 和 CUDA 从零开始构建的 GPT-2 规模 LLM", 内核实现; the cnblogs walkthrough §3.4 counts the cost
+ * of such separate passes).  Here the rotation (and, with opts->qk_norm, the QK norm before it)
+ * is applied to the product's accumulators before they are stored, so q' and k' leave rotated:
+ *   x [B][T][C] (in_dtype BF16 or F16), w [(Hq + 2 Hkv) * head_dim][C] (in_dtype; rows: the Hq
+ *   query heads, then the Hkv key heads, then the Hkv value heads, head_dim features each),
+ *   q [B][T][Hq][head_dim] = R_t(norm(x W_q^T)), k [B][T][Hkv][head_dim] = R_t(norm(x W_k^T)),
+ *   v [B][T][Hkv][head_dim] = x W_v^T, in out_dtype (F32 or in_dtype); t the token's position.
+ * Feeding q, k, v to ne_rope_attn_fwd with rope_base <= 0 (and no QK norm) gives attention with
+ * RoPE.  Requires C % 64 == 0 and (Hq + 2 Hkv) * head_dim % 128 == 0.  Products run on bf16/fp16
+ * MFMA with fp32 accumulation.  The workspace holds the cos/sin table of the T positions.
+ * events: NULL or 4 entries (pairs around the table and the product). */
+size_t ne_qkv_rope_workspace_bytes(int T, int head_dim);
+ne_status_t ne_qkv_rope_proj(const void* x, const void* w, void* q, void* k, void* v,
+                             int B, int T, int C, int Hq, int Hkv, int head_dim, double rope_base,
+                             const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
 const char* ne_status_str(ne_status_t status);
 const char* ne_last_error(void);
 int ne_abi_version(void);

@@ -1,0 +1,98 @@
+"""GPU parity of the QKV projection with the RoPE epilogue (ne_qkv_rope_proj) against the oracle
+(oracle/qkv.py).  Products of bf16/fp16 inputs are exact in fp32 and accumulate in fp32, so the bar
+is 1e-4 of each output's scale (fp32 outputs); 16-bit outputs add half an ulp of their format.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from causal_gqa_flashattention_rope_amd import binding, inputs
+from tests.test_gpu_parity import DEV, check, f64
+
+pytestmark = pytest.mark.gpu
+
+_NAME = {torch.bfloat16: "bf16", torch.float16: "f16"}
+
+
+def check_qkv(name, got, ref, out_dt):
+    got = got.double().numpy()
+    scale = float(np.max(np.abs(ref)))
+    assert np.all(np.isfinite(got)), name
+    if out_dt == torch.float32:
+        err = float(np.max(np.abs(got - ref)) / scale)
+        assert err <= 1e-4, f"{name}: rel err {err:.3e}"
+        return
+    mant = 8 if out_dt == torch.bfloat16 else 11
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - (mant - 1))
+    excess = np.abs(got - ref) - (1e-4 * scale + 0.5 * ulp)
+    assert np.max(excess) <= 0, f"{name}: exceeds bar by {np.max(excess):.3e}"
+
+
+def make(B, T, C, Hq, Hkv, D, seed, dtype):
+    x = inputs.gaussian((B, T, C), seed, 1.0, dtype)
+    w = inputs.gaussian(((Hq + 2 * Hkv) * D, C), seed + 1, 1.0 / np.sqrt(C), dtype)
+    return x, w
+
+
+@pytest.mark.parametrize("shape", [(2, 100, 128, 4, 2, 32), (1, 300, 256, 6, 1, 64), (2, 129, 192, 4, 2, 128),
+                                   (1, 1, 64, 2, 1, 128)])
+@pytest.mark.parametrize("in_dt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("variant", ["rope", "rope_qknorm", "plain"])
+def test_qkv_parity(shape, in_dt, variant):
+    B, T, C, Hq, Hkv, D = shape
+    x, w = make(B, T, C, Hq, Hkv, D, 5000 + T, _NAME[in_dt])
+    base = 0.0 if variant == "plain" else 1e4
+    qkn = (1.2, 1e-6) if variant == "rope_qknorm" else None
+    q, k, v = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), Hq, Hkv, base, qk_norm=qkn)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_rope_proj(f64(x), f64(w), Hq, Hkv, base, qk_norm=qkn)
+    for nm, g, r in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        check_qkv(nm, g.cpu(), r, torch.float32)
+
+
+@pytest.mark.parametrize("in_dt", [torch.bfloat16, torch.float16])
+def test_qkv_16bit_outputs(in_dt):
+    x, w = make(2, 200, 256, 8, 2, 64, 5100, _NAME[in_dt])
+    q, k, v = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), 8, 2, 5e5, out_dtype=in_dt)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_rope_proj(f64(x), f64(w), 8, 2, 5e5)
+    for nm, g, r in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        check_qkv(nm, g.cpu(), r, in_dt)
+
+
+def test_qkv_workload_projection_sampled_tokens():
+    """The projection of the wide GQA layer (B4 T2048, C = Hq D = 1536, Hq 12 / Hkv 4, D 128):
+    full-size GPU run, oracle on sampled tokens at their positions."""
+    B, T, Hq, Hkv, D = 4, 2048, 12, 4, 128
+    C = Hq * D
+    x, w = make(B, T, C, Hq, Hkv, D, 5200, "bf16")
+    q, k, v = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), Hq, Hkv, 1e4)
+    torch.cuda.synchronize()
+    idx = np.array([0, 1, 255, 256, 1000, 2047])
+    for b in (0, 3):
+        rq, rk, rv = oracle.qkv_rope_proj(f64(x[b:b + 1, idx]), f64(w), Hq, Hkv, 1e4, positions=idx)
+        for nm, g, r in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+            check_qkv(nm, g[b:b + 1, idx].cpu(), r, torch.float32)
+
+
+def test_qkv_then_attention_without_rope_equals_attention_with_rope():
+    B, T, C, Hq, Hkv, D = 1, 200, 256, 8, 2, 64
+    x, w = make(B, T, C, Hq, Hkv, D, 5300, "bf16")
+    xd, wd = x.to(DEV), w.to(DEV)
+    q1, k1, v1 = binding.ne_qkv_rope_proj(xd, wd, Hq, Hkv, 1e4, out_dtype=torch.bfloat16)
+    o1, l1 = binding.ne_rope_attn_fwd(q1, k1, v1, 0.0)
+    q0, k0, v0 = binding.ne_qkv_rope_proj(xd, wd, Hq, Hkv, 0.0, out_dtype=torch.bfloat16)
+    o2, l2 = binding.ne_rope_attn_fwd(q0, k0, v0, 1e4)
+    torch.cuda.synchronize()
+    assert float((o1 - o2).abs().max()) <= 4e-3 * float(o2.abs().max())
+    assert float((l1 - l2).abs().max()) <= 4e-3 * float(l2.abs().max())
+
+
+def test_qkv_is_bitwise_deterministic():
+    x, w = make(2, 300, 256, 6, 1, 64, 5400, "bf16")
+    a = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), 6, 1, 1e4)
+    a = [t.clone() for t in a]
+    b = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), 6, 1, 1e4)
+    for s, t in zip(a, b):
+        assert torch.equal(s, t)

@@ -33,6 +33,16 @@ def test_brute_force_sums_without_rope():
             assert abs(ref - s) < 1e-13
 
 
+def test_sampled_positions_equal_the_full_sequence_rows():
+    B, T, C, Hq, Hkv, D = 1, 50, 16, 2, 1, 8
+    x, w = case(B, T, C, Hq, Hkv, D, 4)
+    full = oracle.qkv_rope_proj(x, w, Hq, Hkv, 1e4)
+    idx = np.array([0, 7, 31, 49])
+    part = oracle.qkv_rope_proj(x[:, idx], w, Hq, Hkv, 1e4, positions=idx)
+    for a, b in zip(full, part):
+        np.testing.assert_array_equal(a[:, idx], b)
+
+
 def test_rotation_equals_the_c_oracle_rotation():
     B, T, C, Hq, Hkv, D = 2, 40, 32, 4, 2, 16
     x, w = case(B, T, C, Hq, Hkv, D, 2)
@@ -58,7 +68,7 @@ def test_projection_then_attention_without_rope_equals_attention_with_rope(qkn):
 MUTATIONS = {
     "weight_read_as_c_by_n": ("y = x @ w.T", "y = x @ w.reshape(w.shape[1], w.shape[0])"),
     "k_before_q": ("q = y[..., :Hq * D].reshape(B, T, Hq, D)", "q = y[..., Hkv * D:(Hq + Hkv) * D].reshape(B, T, Hq, D)"),
-    "positions_from_one": ("pos = np.arange(T)", "pos = np.arange(1, T + 1)"),
+    "positions_from_one": ("pos = np.arange(T) if positions is None", "pos = np.arange(1, T + 1) if positions is None"),
     "v_rotated": ("v = y[..., (Hq + Hkv) * D:].reshape(B, T, Hkv, D).copy()",
                   "v = np.stack([rope_rows(y[..., (Hq + Hkv) * D:].reshape(B, T, Hkv, D)[b], np.arange(T), base) for b in range(B)])"),
     "norm_after_k_only": ("q, k = qk_norm_rows(q, *qk_norm), qk_norm_rows(k, *qk_norm)", "k = qk_norm_rows(k, *qk_norm)"),

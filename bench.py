@@ -15,7 +15,8 @@ pass with every launch bracketed.  Prints one JSON line.
 After the headline measurement the same step is measured with a sliding window of --window keys
 (default T/4, the short window of the nanochat guide's window_pattern; 0 skips it), counting the
 visible pairs N_W = W(W+1)/2 + (T-W)W per head; it is reported under "sliding_window".  The causal
-step with the QK norm on (gain 1.2, eps 1e-6) is reported under "qk_norm".
+step with the QK norm on (gain 1.2, eps 1e-6) is reported under "qk_norm", and the workload layer's
+QKV projection with the RoPE epilogue (2 M N C flops) under "qkv_projection".
 Then one decode step of the cached workload (--decode-batch sequences, each holding 8191 tokens of
 the long-context shape, Hq 32 / Hkv 8 / D 128, RoPE base 5e5, attending with one new token) is
 measured as HBM bandwidth: bytes = the visible cached keys and values (fp16) + q + o, reported
@@ -40,6 +41,8 @@ KERNEL_SOURCES = ["causal_gqa_flashattention_rope_amd/csrc/ne_kernels.hip",
                   "causal_gqa_flashattention_rope_amd/csrc/ne_common.hpp"]
 DECODE_SOURCES = ["causal_gqa_flashattention_rope_amd/csrc/ne_decode.hip",
                   "causal_gqa_flashattention_rope_amd/csrc/ne_common.hpp"]
+QKV_SOURCES = ["causal_gqa_flashattention_rope_amd/csrc/ne_qkv.hip",
+               "causal_gqa_flashattention_rope_amd/csrc/ne_common.hpp"]
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES):
@@ -192,6 +195,50 @@ def measure_decode(Bd, K, hev, new_events):
     }
 
 
+def measure_qkv(w, K, hev, new_events, peak):
+    """The QKV projection of the workload's layer (C = Hq D, weight [(Hq + 2 Hkv) D][C]) with the RoPE
+    epilogue: 2 M N C flops per call, M = B T."""
+    import torch
+    from causal_gqa_flashattention_rope_amd import binding, inputs
+    dev = torch.device("cuda:0")
+    B, T, Hq, Hkv, D = w.B, w.T, w.Hq, w.Hkv, w.D
+    C = Hq * D
+    N = (Hq + 2 * Hkv) * D
+    x = inputs.gaussian((B, T, C), 1101, 1.0, "bf16").to(dev)
+    wt = inputs.gaussian((N, C), 1102, C ** -0.5, "bf16").to(dev)
+    q = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((B, T, Hkv, D), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((B, T, Hkv, D), dtype=torch.bfloat16, device=dev)
+    ws = binding.alloc_workspace(int(binding.lib().ne_qkv_rope_workspace_bytes(T, D)), dev)
+
+    def call(ev=None):
+        binding.ne_qkv_rope_proj(x, wt, Hq, Hkv, w.rope_base, q=q, k=k, v=v, workspace=ws, events=ev)
+
+    evs = [new_events(4) for _ in range(50)]
+    for i in range(50):
+        call(evs[i])
+    torch.cuda.synchronize()
+    table_ms = sum(hev.elapsed_ms(e[0], e[1]) for e in evs[-10:]) / 10
+    tev = [new_events(2) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        call([None, None, tev[i][0], tev[i][1]])
+    torch.cuda.synchronize()
+    ms_call = (time.perf_counter() - t0) * 1e3 / K
+    gemm_ms = sum(hev.elapsed_ms(a, b) for a, b in tev) / K
+    flops = 2.0 * B * T * N * C
+    ach = flops / (gemm_ms * 1e-3) / 1e12
+    return {"workload": f"qkv_proj_b{B}_t{T}_c{C}_n{N}", "M": B * T, "N": N, "C": C, "in_dtype": "bf16",
+            "out_dtype": "bf16", "epilogue": "rope", "ms_per_call": round(ms_call, 4),
+            "value": round(flops / (ms_call * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "kernel_ms": {"qkv_rope_table": round(table_ms, 4), "qkv_rope_gemm": round(gemm_ms, 4)},
+            "roofline": {"kernel": "qkv_rope_gemm", "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                         "traffic": read_traffic("qkv_rope_gemm", f"qkv_proj_b{B}_t{T}_c{C}_n{N}", QKV_SOURCES),
+                         "flops_per_launch": flops, "launch_ms": round(gemm_ms, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +255,7 @@ def main():
     ap.add_argument("--cpu-sample-batch", type=int, default=4)
     ap.add_argument("--window", type=int, default=-1,
                     help="window of the sliding-window measurement (-1: T/4; 0: skip it)")
+    ap.add_argument("--qkv", type=int, default=1, help="also measure the QKV projection with the RoPE epilogue")
     ap.add_argument("--qk-norm", type=int, default=1, help="also measure the step with the QK norm on (0: skip)")
     ap.add_argument("--decode-batch", type=int, default=8,
                     help="sequences of the decode measurement (0: skip it)")
@@ -378,6 +426,8 @@ def main():
             "ms_per_step": round(ms_q, 4), "steps": K, "warmup": 20,
             "kernel_ms": {n: round(t, 4) for n, t in kern_q.items()},
         }
+    if args.qkv:
+        result["qkv_projection"] = measure_qkv(w, K, hev, new_events, MFMA_PEAK_F16)
     if args.decode_batch > 0:
         result["decode"] = measure_decode(args.decode_batch, K, hev, new_events)
     if args.copy_calibration_mib:

@@ -1464,6 +1464,9 @@ void dq_kernel_h(BwdArgs a) {
         // packing); that of half 1 runs between the first dQ products.  dQ^T += K^T dS^T reads
         // its K^T fragments four products ahead.
         constexpr int NC = 2 * KS, NQ = 4 * NDB;
+        // operand look-ahead: four products; two in the option instantiation, whose masks need the
+        // registers (no spills; within noise of three or four on the window and QK-norm steps)
+        constexpr int AHD = EXT ? 2 : 4;
         auto rd = [&](int mb, int i) {
             return row_frag_sw<OP, D>((i & 1) ? Vs : Ks, 32 * mb + c, i >> 1, h);
         };
@@ -1485,14 +1488,14 @@ void dq_kernel_h(BwdArgs a) {
         auto chains = [&](int mb, floatx16 (&x)[2], floatx16 (&prev)[2], auto WITH_PREV) {
             half8 fr[NC];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fr[i] = rd(mb, i);
+            for (int i = 0; i < AHD; ++i) fr[i] = rd(mb, i);
             x[0] = M::mma(fw, fl, floatx16{});
             x[1] = M::mma(fw, fd, floatx16{});
 #pragma unroll
             for (int i = 0; i < NC; ++i) {
                 __builtin_amdgcn_sched_barrier(0);
                 x[i & 1] = M::mma(fr[i], (i & 1) ? of[i >> 1] : qf[i >> 1], x[i & 1]);
-                if (i + 4 < NC) fr[i + 4] = rd(mb, i + 4);
+                if (i + AHD < NC) fr[i + AHD] = rd(mb, i + AHD);
                 if constexpr (decltype(WITH_PREV)::value) {
 #pragma unroll
                     for (int e = 16 * i / NC; e < 16 * (i + 1) / NC; ++e) elem(prev, 0, e);
@@ -1509,7 +1512,7 @@ void dq_kernel_h(BwdArgs a) {
         if (diag) mask(x1, 1);
         half8 kt[NQ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kt[i] = rk(i);
+        for (int i = 0; i < AHD; ++i) kt[i] = rk(i);
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             __builtin_amdgcn_sched_barrier(0);
@@ -1518,7 +1521,7 @@ void dq_kernel_h(BwdArgs a) {
                 for (int e = 32 * i / NQ; e < 32 * (i + 1) / NQ; ++e) elem(x1, 1, e);
             }
             dq[i % NDB] = M::mma(kt[i], dsf[i / NDB], dq[i % NDB]);
-            if (i + 4 < NQ) kt[i + 4] = rk(i + 4);
+            if (i + AHD < NQ) kt[i + AHD] = rk(i + AHD);
         }
         __builtin_amdgcn_sched_barrier(0);
     }

@@ -54,6 +54,24 @@ __device__ __forceinline__ void fill_rows(OP* tile, const OP* src, int row0, int
     }
 }
 
+// Same, with the tile given as a wave-uniform 32-bit LDS byte address.
+template <typename OP, int BK, int ROWS, int NW>
+__device__ __forceinline__ void fill_rows_at(unsigned tile, const OP* src, int row0, int nrows, int ld, int k0) {
+    using TL = Tile<OP, BK>;
+    constexpr int WL = ROWS * TL::CPR / 64;
+    static_assert(ROWS * TL::CPR % 64 == 0 && WL % NW == 0, "whole wave loads per wave");
+    const int l = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < WL / NW; ++i) {
+        const int j = i * NW + w;
+        const int q = 64 * j + l;
+        const int r = q / TL::CPR, p = q % TL::CPR;
+        const int gr = min(row0 + r, nrows - 1);
+        const unsigned off = (unsigned)(((size_t)gr * ld + k0 + (p ^ TL::swz(r)) * TL::EPC) * sizeof(OP));
+        dma16_s(off, src, __builtin_amdgcn_readfirstlane(tile + 1024u * (unsigned)j));
+    }
+}
+
 template <typename TI>
 __device__ __forceinline__ floatx16 mma16(half8 a, half8 b, floatx16 c) {
     if constexpr (sizeof(TI) == 2 && __is_same(TI, __bf16)) {
@@ -68,6 +86,7 @@ __device__ __forceinline__ floatx16 mma16(half8 a, half8 b, floatx16 c) {
 }  // namespace
 
 // =====================================================================================
+// Narrow tiles, for projections too small to fill the chip with the wide tiles below.
 // grid (ceil(M / 256) * N / 128), 256 threads = 4 waves.  A workgroup computes 256 tokens x 128
 // features; wave w takes tokens [64 w, 64 w + 64) (two 32-token blocks) against all 128 features
 // (four 32-feature blocks): 8 accumulators.  W and x tiles of BK columns go through a 2-stage LDS
@@ -201,7 +220,183 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_QKV_WPE)
     }
 }
 
+// =====================================================================================
+// Wide tiles (B4 T2048 C1536 N2560 projection: 86 us against 95 us with the narrow tiles, whose 640
+// workgroups take three rounds of the 256 compute units).
+// grid (ceil(M / 128) * ceil(N / 640)), 512 threads = 8 waves, two per SIMD.  A
+// workgroup computes 128 tokens x 640 features (640 / D whole heads); wave w takes features
+// [160 (w / 2), 160 (w / 2) + 160) (five 32-feature blocks) against tokens [64 (w % 2), 64 (w % 2)
+// + 64) (two 32-token blocks): 10 accumulators, and each fragment read from LDS feeds two or five
+// products.
+// 32-column steps of W and x go through a 3-stage LDS ring by direct loads issued three steps
+// ahead (a stage is refilled as soon as every wave has read it); the fragments of each 16-column
+// half-step are read while the products of the previous one run, and the one barrier per step
+// sits between the two halves.  Epilogue per block: QK
+// norm (a head's sum of squares gathered across the waves through LDS), rotation, and four
+// consecutive features per lane stored directly.  Features past N (a partial last tile of heads)
+// are computed from repeated rows of W and not stored.
+// =====================================================================================
+template <typename TI, typename TOUT, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void qkv_wide_kernel(QkvArgs a) {
+    constexpr int BM = 128, BN = 640, NW = 8, BK = 32, TB = 2, FB = 5, NST = 3;
+    constexpr int ATILE = BN * BK, BTILE = BM * BK, STAGE = ATILE + BTILE;   // 16-bit elements
+    constexpr int LOADS = (BN + BM) * (BK * 2 / 16) / 64 / NW;              // direct loads per wave per step
+    static_assert(LOADS == 6 && 2 * TB * 32 == BM && 4 * FB * 32 == BN, "tile shape");
+    __shared__ __attribute__((aligned(1024))) _Float16 lds[NST * STAGE];
+    auto As = [&](int st) { return lds + st * STAGE; };
+    auto Bs = [&](int st) { return lds + st * STAGE + ATILE; };
+
+    const int M = a.M, C = a.C, N = a.N;
+    const int NB = (N + BN - 1) / BN, MB = (M + BM - 1) / BM;
+    int mb, nb;
+    {
+        const int i = blockIdx.x;
+        if ((MB & 7) == 0) {  // XCD i % 8 takes the 128-token blocks congruent to it
+            const int x = i & 7, k = i >> 3;
+            nb = k % NB;
+            mb = x + 8 * (k / NB);
+        } else {
+            nb = i % NB;
+            mb = i / NB;
+        }
+    }
+    const int m0 = mb * BM, n0 = nb * BN;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int wt_ = w & 1, wf = w >> 1;         // token half, feature quarter
+    const _Float16* x = (const _Float16*)a.x;   // 16-bit words; the MFMA reinterprets them as TI
+    const _Float16* wt = (const _Float16*)a.w;
+
+    floatx16 acc[TB][FB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) acc[tb][fb] = floatx16{};
+
+    const int nk = C / BK;
+    const unsigned lds0 = lds_addr(lds);
+    auto fill = [&](int st, int kstep) {
+        const unsigned sa = lds0 + (unsigned)(st * STAGE * 2);
+        fill_rows_at<_Float16, BK, BN, NW>(sa, wt, n0, N, C, kstep * BK);
+        fill_rows_at<_Float16, BK, BM, NW>(sa + ATILE * 2, x, m0, M, C, kstep * BK);
+    };
+    half8 af[2][FB], bf[2][TB];
+    auto frags = [&](int st, int ks, half8 (&fa)[FB], half8 (&fb_)[TB]) {
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) fa[fb] = row_frag_sw<_Float16, BK>(As(st), 160 * wf + 32 * fb + c, ks, h);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) fb_[tb] = row_frag_sw<_Float16, BK>(Bs(st), 64 * wt_ + 32 * tb + c, ks, h);
+    };
+    auto products = [&](const half8 (&fa)[FB], const half8 (&fb_)[TB]) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb) acc[tb][fb] = mma16<TI>(fa[fb], fb_[tb], acc[tb][fb]);
+    };
+
+    __builtin_assume(nk >= 2);  // C >= 64
+    const int pre = nk < NST ? nk : NST;
+    for (int st = 0; st < pre; ++st) fill(st, st);
+    lds_fill_wait_keep((pre - 1) * LOADS);  // step 0 has landed
+    frags(0, 0, af[0], bf[0]);
+    for (int it = 0; it < nk - 1; ++it) {
+        frags(it % NST, 1, af[1], bf[1]);
+        products(af[0], bf[0]);
+        // step it + 1 has landed for every wave (step it + 2 may still be in flight), and every
+        // wave has read all of step it, whose stage the fill of step it + 3 reuses
+        lds_fill_wait_keep(it + 2 < nk ? LOADS : 0);
+        if (it + 3 < nk) fill(it % NST, it + 3);
+        frags((it + 1) % NST, 0, af[0], bf[0]);
+        products(af[1], bf[1]);
+    }
+    frags((nk - 1) % NST, 1, af[1], bf[1]);
+    products(af[0], bf[0]);
+    products(af[1], bf[1]);
+    __syncthreads();  // the ring becomes the sum-of-squares scratch
+
+    const bool rope = a.rope_base > 0.0;
+    const int H3 = a.Hq + 2 * a.Hkv, Hqk = a.Hq + a.Hkv;
+    // QK norm factor of each block's head (1 for v heads and without the norm); the accumulators
+    // are only read inside the branch and scaled in the store loop
+    float fac[TB][FB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) fac[tb][fb] = 1.f;
+    if (a.qkn.on) {
+        // per token and 32-feature block of the tile: sum of squares, [BM][BN / 32]
+        float* ssq = reinterpret_cast<float*>(lds);
+        const int row = 64 * wt_ + c;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb) {
+                float ss = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ss += acc[tb][fb][r] * acc[tb][fb][r];
+                ss = sum_halves(ss);
+                if (h == 0) ssq[(row + 32 * tb) * (BN / 32) + FB * wf + fb] = ss;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb) {
+                const int f0 = n0 + 160 * wf + 32 * fb, head = f0 / D;
+                const int b0 = FB * wf + fb - (f0 % D) / 32;  // the head's first block in the tile
+                float ss = 0.f;
+#pragma unroll
+                for (int j = 0; j < D / 32; ++j) ss += ssq[(row + 32 * tb) * (BN / 32) + b0 + j];
+                if (head < Hqk) fac[tb][fb] = qk_factor(ss, D, a.qkn.gain, a.qkn.eps);
+            }
+    }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const int m = m0 + 64 * wt_ + 32 * tb + c;
+        const int t = (m < M ? m : M - 1) % a.T;
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) {
+            const int f0 = n0 + 160 * wf + 32 * fb, head = f0 / D, dh0 = f0 % D;
+            const bool qk = head < Hqk, isq = head < a.Hq;
+            TOUT* const base = (TOUT*)(isq ? a.q : qk ? a.k : a.v);
+            const int H = isq ? a.Hq : a.Hkv, hd = isq ? head : qk ? head - a.Hq : head - Hqk;
+            TOUT* row = base + ((size_t)m * H + hd) * D;
+            const bool st = m < M && head < H3;
+            const bool rot = qk && rope;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d = dh0 + 8 * q4 + 4 * h;   // features d .. d + 3 of this lane
+                const float f = fac[tb][fb];
+                float y0 = acc[tb][fb][4 * q4] * f, y1 = acc[tb][fb][4 * q4 + 1] * f;
+                float y2 = acc[tb][fb][4 * q4 + 2] * f, y3 = acc[tb][fb][4 * q4 + 3] * f;
+                if (rot) {
+                    const floatx4 r01 = *reinterpret_cast<const floatx4*>(a.table + (size_t)t * (D / 2) + d / 2);
+                    const float u0 = y0, v0 = y1, u1 = y2, v1 = y3;
+                    y0 = u0 * r01[0] - v0 * r01[1];
+                    y1 = u0 * r01[1] + v0 * r01[0];
+                    y2 = u1 * r01[2] - v1 * r01[3];
+                    y3 = u1 * r01[3] + v1 * r01[2];
+                }
+                if (st) store4(row + d, y0, y1, y2, y3);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one block at a time: its registers die here
+        }
+    }
+}
+
 namespace {
+// compute units of the current device (cached per device)
+int cu_count() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <typename TI, typename TO, int D>
 hipError_t launch_qkv_t(const QkvArgs& a, hipStream_t s, hipEvent_t const* ev) {
     auto rec = [&](int j) { return ev && ev[j] ? hipEventRecord(ev[j], s) : hipSuccess; };
@@ -213,8 +408,15 @@ hipError_t launch_qkv_t(const QkvArgs& a, hipStream_t s, hipEvent_t const* ev) {
     }
     if ((e = rec(1)) != hipSuccess) return e;
     if ((e = rec(2)) != hipSuccess) return e;
-    const int grid = (a.M + 255) / 256 * (a.N / 128);
-    hipLaunchKernelGGL((qkv_rope_kernel<TI, TO, D, NE_QKV_BK>), dim3(grid), dim3(256), 0, s, a);
+    // wide tiles when they fill at least three quarters of the compute units in one round (their
+    // per-flop cost is lower; with fewer tiles the narrow kernel spreads the work wider)
+    const int wide_tiles = (a.M + 127) / 128 * ((a.N + 639) / 640);
+    if (4 * wide_tiles >= 3 * cu_count()) {
+        hipLaunchKernelGGL((qkv_wide_kernel<TI, TO, D>), dim3(wide_tiles), dim3(512), 0, s, a);
+    } else {
+        const int grid = (a.M + 255) / 256 * (a.N / 128);
+        hipLaunchKernelGGL((qkv_rope_kernel<TI, TO, D, NE_QKV_BK>), dim3(grid), dim3(256), 0, s, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return rec(3);
 }

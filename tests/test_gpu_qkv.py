@@ -51,6 +51,45 @@ def test_qkv_parity(shape, in_dt, variant):
         check_qkv(nm, g.cpu(), r, torch.float32)
 
 
+# Shapes whose 128-token x 640-feature tiles fill at least three quarters of the 256 compute units, so
+# the wide-tile kernel runs: ragged token counts, a partial last tile of heads (N = 1536), head sizes
+# 32 / 64 / 128, and C from the two-step minimum to several passes of the 3-stage ring.
+WIDE = [(1, 8100, 64, 12, 4, 128), (2, 4100, 320, 8, 2, 128), (1, 6200, 128, 16, 8, 64), (3, 4100, 192, 24, 8, 32)]
+
+
+def test_wide_shapes_select_the_wide_kernel():
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for B, T, C, Hq, Hkv, D in WIDE:
+        tiles = -(-B * T // 128) * -(-(Hq + 2 * Hkv) * D // 640)
+        assert 4 * tiles >= 3 * cus, (B, T, C, Hq, Hkv, D)
+
+
+@pytest.mark.parametrize("shape", WIDE)
+@pytest.mark.parametrize("variant", ["rope", "rope_qknorm", "plain"])
+def test_qkv_wide_tiles_parity(shape, variant):
+    B, T, C, Hq, Hkv, D = shape
+    x, w = make(B, T, C, Hq, Hkv, D, 5500 + T + C, "bf16")
+    base = 0.0 if variant == "plain" else 1e4
+    qkn = (0.8, 1e-5) if variant == "rope_qknorm" else None
+    q, k, v = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), Hq, Hkv, base, qk_norm=qkn)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_rope_proj(f64(x), f64(w), Hq, Hkv, base, qk_norm=qkn)
+    for nm, g, r in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        check_qkv(nm, g.cpu(), r, torch.float32)
+
+
+@pytest.mark.parametrize("out_dt", [torch.bfloat16, torch.float16])
+def test_qkv_wide_tiles_16bit(out_dt):
+    B, T, C, Hq, Hkv, D = WIDE[0]
+    name = _NAME[out_dt]
+    x, w = make(B, T, C, Hq, Hkv, D, 5600, name)
+    q, k, v = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), Hq, Hkv, 5e5, qk_norm=(1.1, 1e-6), out_dtype=out_dt)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_rope_proj(f64(x), f64(w), Hq, Hkv, 5e5, qk_norm=(1.1, 1e-6))
+    for nm, g, r in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        check_qkv(nm, g.cpu(), r, out_dt)
+
+
 @pytest.mark.parametrize("in_dt", [torch.bfloat16, torch.float16])
 def test_qkv_16bit_outputs(in_dt):
     x, w = make(2, 200, 256, 8, 2, 64, 5100, _NAME[in_dt])
@@ -89,10 +128,12 @@ def test_qkv_then_attention_without_rope_equals_attention_with_rope():
     assert float((l1 - l2).abs().max()) <= 4e-3 * float(l2.abs().max())
 
 
-def test_qkv_is_bitwise_deterministic():
-    x, w = make(2, 300, 256, 6, 1, 64, 5400, "bf16")
-    a = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), 6, 1, 1e4)
+@pytest.mark.parametrize("shape", [(2, 300, 256, 6, 1, 64), WIDE[1]])
+def test_qkv_is_bitwise_deterministic(shape):
+    B, T, C, Hq, Hkv, D = shape
+    x, w = make(B, T, C, Hq, Hkv, D, 5400, "bf16")
+    a = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), Hq, Hkv, 1e4, qk_norm=(1.0, 1e-6))
     a = [t.clone() for t in a]
-    b = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), 6, 1, 1e4)
+    b = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), Hq, Hkv, 1e4, qk_norm=(1.0, 1e-6))
     for s, t in zip(a, b):
         assert torch.equal(s, t)

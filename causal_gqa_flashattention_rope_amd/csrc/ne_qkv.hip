@@ -221,27 +221,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_QKV_WPE)
 }
 
 // =====================================================================================
-// Wide tiles (B4 T2048 C1536 N2560 projection: 86 us against 95 us with the narrow tiles, whose 640
-// workgroups take three rounds of the 256 compute units).
-// grid (ceil(M / 128) * ceil(N / 640)), 512 threads = 8 waves, two per SIMD.  A
-// workgroup computes 128 tokens x 640 features (640 / D whole heads); wave w takes features
-// [160 (w / 2), 160 (w / 2) + 160) (five 32-feature blocks) against tokens [64 (w % 2), 64 (w % 2)
-// + 64) (two 32-token blocks): 10 accumulators, and each fragment read from LDS feeds two or five
-// products.
-// 32-column steps of W and x go through a 3-stage LDS ring by direct loads issued three steps
-// ahead (a stage is refilled as soon as every wave has read it); the fragments of each 16-column
-// half-step are read while the products of the previous one run, and the one barrier per step
-// sits between the two halves.  Epilogue per block: QK
-// norm (a head's sum of squares gathered across the waves through LDS), rotation, and four
-// consecutive features per lane stored directly.  Features past N (a partial last tile of heads)
-// are computed from repeated rows of W and not stored.
+// Wide tiles, for projections that fill the chip in one round.  grid (ceil(M / BM) * ceil(N / BN)),
+// 512 threads = 8 waves, two per SIMD, in a WT x (8 / WT) grid over tokens x features: each wave
+// computes 64 tokens (two 32-token blocks) x 160 features (five 32-feature blocks), 10
+// accumulators, so every fragment read from LDS feeds two or five products.  Workgroup tile
+// BM = 64 WT tokens x BN = 1280 / WT features:
+//   WT = 4: 256 x 320, 64-column steps (whole 128-byte rows per direct load) in a 2-stage ring;
+//           heads of 128 features straddle tiles, so it runs without the QK norm or with D <= 64;
+//   WT = 2: 128 x 640 (640 / D whole heads), 32-column steps in a 3-stage ring.
+// B4 T2048 C1536 N2560 projection (256 tiles either way): see the host selection below.
+// Stage s + NST reuses the stage of step s, refilled right after the mid-step barrier that shows
+// every wave has read it, so loads are issued NST steps ahead and each wait keeps the newer fills
+// in flight; the fragments of each 16-column k-step are read while the products of the previous
+// one run.  Epilogue per block: QK norm (a head's sum of squares gathered across the waves through
+// LDS), rotation, and four consecutive features per lane stored directly.  Features past N (a
+// partial last tile of heads) are computed from repeated rows of W and not stored.
 // =====================================================================================
-template <typename TI, typename TOUT, int D>
+template <typename TI, typename TOUT, int D, int WT, int BK, int NST>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void qkv_wide_kernel(QkvArgs a) {
-    constexpr int BM = 128, BN = 640, NW = 8, BK = 32, TB = 2, FB = 5, NST = 3;
+    constexpr int NW = 8, WF = NW / WT, BM = 64 * WT, BN = 160 * WF, TB = 2, FB = 5, KS = BK / 16;
     constexpr int ATILE = BN * BK, BTILE = BM * BK, STAGE = ATILE + BTILE;   // 16-bit elements
     constexpr int LOADS = (BN + BM) * (BK * 2 / 16) / 64 / NW;              // direct loads per wave per step
-    static_assert(LOADS == 6 && 2 * TB * 32 == BM && 4 * FB * 32 == BN, "tile shape");
+    static_assert(KS % 2 == 0 && (NST - 2) * LOADS <= 12 && (NST - 1) * LOADS <= 12, "pipeline shape");
     __shared__ __attribute__((aligned(1024))) _Float16 lds[NST * STAGE];
     auto As = [&](int st) { return lds + st * STAGE; };
     auto Bs = [&](int st) { return lds + st * STAGE + ATILE; };
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void q
     int mb, nb;
     {
         const int i = blockIdx.x;
-        if ((MB & 7) == 0) {  // XCD i % 8 takes the 128-token blocks congruent to it
+        if ((MB & 7) == 0) {  // XCD i % 8 takes the token blocks congruent to it
             const int x = i & 7, k = i >> 3;
             nb = k % NB;
             mb = x + 8 * (k / NB);
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void q
     }
     const int m0 = mb * BM, n0 = nb * BN;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
-    const int wt_ = w & 1, wf = w >> 1;         // token half, feature quarter
+    const int wt_ = w % WT, wf = w / WT;        // token block of 64, feature block of 160
     const _Float16* x = (const _Float16*)a.x;   // 16-bit words; the MFMA reinterprets them as TI
     const _Float16* wt = (const _Float16*)a.w;
 
@@ -292,24 +293,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void q
 #pragma unroll
             for (int fb = 0; fb < FB; ++fb) acc[tb][fb] = mma16<TI>(fa[fb], fb_[tb], acc[tb][fb]);
     };
+    // the k-steps of step it but the last, each reading the next one's fragments first
+    auto body = [&](int it) {
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks) {
+            frags(it % NST, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+            products(af[ks & 1], bf[ks & 1]);
+        }
+    };
 
-    __builtin_assume(nk >= 2);  // C >= 64
+    __builtin_assume(nk >= 64 / BK);  // C >= 64
     const int pre = nk < NST ? nk : NST;
     for (int st = 0; st < pre; ++st) fill(st, st);
     lds_fill_wait_keep((pre - 1) * LOADS);  // step 0 has landed
     frags(0, 0, af[0], bf[0]);
     for (int it = 0; it < nk - 1; ++it) {
-        frags(it % NST, 1, af[1], bf[1]);
-        products(af[0], bf[0]);
-        // step it + 1 has landed for every wave (step it + 2 may still be in flight), and every
-        // wave has read all of step it, whose stage the fill of step it + 3 reuses
-        lds_fill_wait_keep(it + 2 < nk ? LOADS : 0);
-        if (it + 3 < nk) fill(it % NST, it + 3);
+        body(it);
+        // step it + 1 has landed for every wave (later steps may still be in flight), and every
+        // wave has read all of step it, whose stage the fill of step it + NST reuses
+        lds_fill_wait_keep(it + 2 < nk ? (NST - 2) * LOADS : 0);
+        if (it + NST < nk) fill(it % NST, it + NST);
         frags((it + 1) % NST, 0, af[0], bf[0]);
         products(af[1], bf[1]);
     }
-    frags((nk - 1) % NST, 1, af[1], bf[1]);
-    products(af[0], bf[0]);
+    body(nk - 1);
     products(af[1], bf[1]);
     __syncthreads();  // the ring becomes the sum-of-squares scratch
 
@@ -322,7 +329,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void q
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb) fac[tb][fb] = 1.f;
-    if (a.qkn.on) {
+    if (BN % D == 0 && a.qkn.on) {  // the host never asks for the norm with heads straddling tiles
         // per token and 32-feature block of the tile: sum of squares, [BM][BN / 32]
         float* ssq = reinterpret_cast<float*>(lds);
         const int row = 64 * wt_ + c;
@@ -408,11 +415,17 @@ hipError_t launch_qkv_t(const QkvArgs& a, hipStream_t s, hipEvent_t const* ev) {
     }
     if ((e = rec(1)) != hipSuccess) return e;
     if ((e = rec(2)) != hipSuccess) return e;
-    // wide tiles when they fill at least three quarters of the compute units in one round (their
-    // per-flop cost is lower; with fewer tiles the narrow kernel spreads the work wider)
-    const int wide_tiles = (a.M + 127) / 128 * ((a.N + 639) / 640);
-    if (4 * wide_tiles >= 3 * cu_count()) {
-        hipLaunchKernelGGL((qkv_wide_kernel<TI, TO, D>), dim3(wide_tiles), dim3(512), 0, s, a);
+    // Tilings by preference: 256 x 320 (least operand traffic per flop, whole-line loads), then
+    // 128 x 640, each when its tiles cover at least three quarters of the compute units in one
+    // round; below that the narrow kernel spreads the work wider.  B4 T2048 C1536 N2560: 256 x 320
+    // 77 us, 128 x 640 85 us, narrow 95 us; 64-byte row segments (32-column steps) stream into LDS at
+    // half the rate of whole 128-byte rows.
+    const int cus3 = 3 * cu_count();
+    const int t320 = (a.M + 255) / 256 * ((a.N + 319) / 320), t640 = (a.M + 127) / 128 * ((a.N + 639) / 640);
+    if ((!a.qkn.on || 320 % D == 0) && 4 * t320 >= cus3) {
+        hipLaunchKernelGGL((qkv_wide_kernel<TI, TO, D, 4, 64, 2>), dim3(t320), dim3(512), 0, s, a);
+    } else if (4 * t640 >= cus3) {
+        hipLaunchKernelGGL((qkv_wide_kernel<TI, TO, D, 2, 32, 3>), dim3(t640), dim3(512), 0, s, a);
     } else {
         const int grid = (a.M + 255) / 256 * (a.N / 128);
         hipLaunchKernelGGL((qkv_rope_kernel<TI, TO, D, NE_QKV_BK>), dim3(grid), dim3(256), 0, s, a);

@@ -51,21 +51,39 @@ def test_qkv_parity(shape, in_dt, variant):
         check_qkv(nm, g.cpu(), r, torch.float32)
 
 
-# Shapes whose 128-token x 640-feature tiles fill at least three quarters of the 256 compute units, so
-# the wide-tile kernel runs: ragged token counts, a partial last tile of heads (N = 1536), head sizes
-# 32 / 64 / 128, and C from the two-step minimum to several passes of the 3-stage ring.
-WIDE = [(1, 8100, 64, 12, 4, 128), (2, 4100, 320, 8, 2, 128), (1, 6200, 128, 16, 8, 64), (3, 4100, 192, 24, 8, 32)]
+# Shapes that select the wide-tile kernel: its 256-token x 320-feature tiling (without the QK norm,
+# or with it for D <= 64) or its 128 x 640 tiling, each when the tiles cover at least three
+# quarters of the compute units.  Ragged token counts, partial last tiles of heads, head sizes
+# 32 / 64 / 128, and C from the minimum step count to several passes of the ring.
+WIDE = [(1, 8100, 64, 12, 4, 128), (2, 4100, 320, 8, 2, 128), (1, 6200, 128, 16, 8, 64), (3, 4100, 192, 24, 8, 32),
+        (2, 5000, 128, 16, 8, 64)]
+VARIANTS = ["rope", "rope_qknorm", "plain"]
 
 
-def test_wide_shapes_select_the_wide_kernel():
+def tiling(B, T, Hq, Hkv, D, qk_norm, cus):
+    """The host's choice in ne_qkv_rope_proj, restated."""
+    M, N = B * T, (Hq + 2 * Hkv) * D
+    t320 = -(-M // 256) * -(-N // 320)
+    t640 = -(-M // 128) * -(-N // 640)
+    if (not qk_norm or 320 % D == 0) and 4 * t320 >= 3 * cus:
+        return "256x320"
+    return "128x640" if 4 * t640 >= 3 * cus else "narrow"
+
+
+def test_wide_shapes_cover_both_wide_tilings():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    seen = {}
     for B, T, C, Hq, Hkv, D in WIDE:
-        tiles = -(-B * T // 128) * -(-(Hq + 2 * Hkv) * D // 640)
-        assert 4 * tiles >= 3 * cus, (B, T, C, Hq, Hkv, D)
+        for v in VARIANTS:
+            t = tiling(B, T, Hq, Hkv, D, v == "rope_qknorm", cus)
+            assert t != "narrow", (B, T, C, Hq, Hkv, D, v)
+            seen.setdefault(t, set()).add((D, v))
+    assert {(128, "rope"), (32, "rope_qknorm"), (64, "rope_qknorm"), (32, "plain")} <= seen["256x320"]
+    assert {(128, "rope_qknorm"), (64, "rope"), (128, "plain")} <= seen["128x640"]
 
 
 @pytest.mark.parametrize("shape", WIDE)
-@pytest.mark.parametrize("variant", ["rope", "rope_qknorm", "plain"])
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_qkv_wide_tiles_parity(shape, variant):
     B, T, C, Hq, Hkv, D = shape
     x, w = make(B, T, C, Hq, Hkv, D, 5500 + T + C, "bf16")
@@ -79,13 +97,14 @@ def test_qkv_wide_tiles_parity(shape, variant):
 
 
 @pytest.mark.parametrize("out_dt", [torch.bfloat16, torch.float16])
-def test_qkv_wide_tiles_16bit(out_dt):
+@pytest.mark.parametrize("qk_norm", [None, (1.1, 1e-6)])   # D 128: 256 x 320 without, 128 x 640 with
+def test_qkv_wide_tiles_16bit(out_dt, qk_norm):
     B, T, C, Hq, Hkv, D = WIDE[0]
     name = _NAME[out_dt]
     x, w = make(B, T, C, Hq, Hkv, D, 5600, name)
-    q, k, v = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), Hq, Hkv, 5e5, qk_norm=(1.1, 1e-6), out_dtype=out_dt)
+    q, k, v = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), Hq, Hkv, 5e5, qk_norm=qk_norm, out_dtype=out_dt)
     torch.cuda.synchronize()
-    rq, rk, rv = oracle.qkv_rope_proj(f64(x), f64(w), Hq, Hkv, 5e5, qk_norm=(1.1, 1e-6))
+    rq, rk, rv = oracle.qkv_rope_proj(f64(x), f64(w), Hq, Hkv, 5e5, qk_norm=qk_norm)
     for nm, g, r in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
         check_qkv(nm, g.cpu(), r, out_dt)
 
@@ -128,7 +147,7 @@ def test_qkv_then_attention_without_rope_equals_attention_with_rope():
     assert float((l1 - l2).abs().max()) <= 4e-3 * float(l2.abs().max())
 
 
-@pytest.mark.parametrize("shape", [(2, 300, 256, 6, 1, 64), WIDE[1]])
+@pytest.mark.parametrize("shape", [(2, 300, 256, 6, 1, 64), WIDE[1], WIDE[4]])
 def test_qkv_is_bitwise_deterministic(shape):
     B, T, C, Hq, Hkv, D = shape
     x, w = make(B, T, C, Hq, Hkv, D, 5400, "bf16")

@@ -62,7 +62,7 @@ def read_traffic(kernel, workload, sources=KERNEL_SOURCES):
     fields = {}
     with open(path) as f:
         for line in f:
-            m = re.match(r"^\s*([a-z_]+):\s*(\S+)\s*$", line)
+            m = re.match(r"^\s*([a-z0-9_]+):\s*(\S+)\s*$", line)
             if m:
                 fields[m.group(1)] = m.group(2)
     if fields.get("kernel_source_sha256_16") != kernel_source_hash(sources):
@@ -91,6 +91,7 @@ class _HipEvents:
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         out = []
@@ -101,6 +102,11 @@ class _HipEvents:
                 raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
             out.append(h.value)
         return out
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, a, b):
         ms = self.ct.c_float()
@@ -124,6 +130,76 @@ def cpu_baseline(w, sample_B):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"fwd+bwd of batch elements 0..{sample_B - 1} of {w.B} (all {w.Hq} heads), "
                       f"float64, {dt:.2f} s wall"}
+
+
+def measure_configs(skip, hev, new_events):
+    """Every other workload of the table: fwd, bwd and fwd+bwd times (median and min over the reps,
+    HIP events around each call on the current stream), with fp32 outputs (the fp32 path for the fp32
+    workload).  The two smaller, HBM-relevant workloads also get a cold fwd+bwd number: 1 GiB is
+    written between reps, which evicts the 256 MB last-level cache."""
+    import statistics
+    import torch
+    from causal_gqa_flashattention_rope_amd import binding, inputs
+    dev = torch.device("cuda:0")
+    out = {}
+    scrub = None
+    for name, w in inputs.WORKLOADS.items():
+        if name == skip:
+            continue
+        q, k, v, dO = (t.to(dev) for t in inputs.make_inputs(w))
+        B, T, Hq, Hkv, D = w.B, w.T, w.Hq, w.Hkv, w.D
+        o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+        dq = torch.empty_like(o)
+        dk = torch.empty((B, T, Hkv, D), dtype=torch.float32, device=dev)
+        dv = torch.empty_like(dk)
+        wsf = binding.alloc_workspace(binding.fwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype), dev)
+        wsb = binding.alloc_workspace(binding.bwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype), dev)
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def call(ev=None):
+            if ev:
+                hev.record(ev[0], stream)
+            binding.ne_rope_attn_fwd(q, k, v, w.rope_base, o=o, lse=lse, workspace=wsf)
+            if ev:
+                hev.record(ev[1], stream)
+            binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=wsb)
+            if ev:
+                hev.record(ev[2], stream)
+
+        reps = 20 if T >= 8192 else 50
+        for _ in range(10):
+            call()
+        evs = [new_events(3) for _ in range(reps)]
+        for e in evs:
+            call(e)
+        torch.cuda.synchronize()
+        f = [hev.elapsed_ms(e[0], e[1]) for e in evs]
+        b = [hev.elapsed_ms(e[1], e[2]) for e in evs]
+        fb = [x + y for x, y in zip(f, b)]
+        unit = B * Hq * D * T * (T + 1) / 2
+        rec = {"shape": f"B{B} T{T} Hq{Hq} Hkv{Hkv} D{D}", "rope_base": w.rope_base, "in_dtype": w.dtype,
+               "out_dtype": "f32", "reps": reps,
+               "fwd_ms": {"median": round(statistics.median(f), 4), "min": round(min(f), 4)},
+               "bwd_ms": {"median": round(statistics.median(b), 4), "min": round(min(b), 4)},
+               "fwd_bwd_ms": {"median": round(statistics.median(fb), 4), "min": round(min(fb), 4)},
+               "fwd_bwd_tflops_median": round(14.0 * unit / (statistics.median(fb) * 1e-3) / 1e12, 2)}
+        if name in ("nanoeuler_gpu_layer", "gpt2_small_mha"):
+            if scrub is None:
+                scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+            cold = []
+            for _ in range(10):
+                scrub.fill_(1.0)
+                e = new_events(3)
+                call(e)
+                torch.cuda.synchronize()
+                cold.append(hev.elapsed_ms(e[0], e[2]))
+            rec["cold_fwd_bwd_ms"] = {"median": round(statistics.median(cold), 4), "min": round(min(cold), 4),
+                                      "reps": 10}
+        out[name] = rec
+        del q, k, v, dO, o, lse, dq, dk, dv, wsf, wsb
+        torch.cuda.empty_cache()
+    return out
 
 
 def measure_decode(Bd, K, hev, new_events):
@@ -257,6 +333,8 @@ def main():
                     help="window of the sliding-window measurement (-1: T/4; 0: skip it)")
     ap.add_argument("--qkv", type=int, default=1, help="also measure the QKV projection with the RoPE epilogue")
     ap.add_argument("--qk-norm", type=int, default=1, help="also measure the step with the QK norm on (0: skip)")
+    ap.add_argument("--configs", type=int, default=1,
+                    help="also time fwd / bwd of every other workload of the table (0: skip)")
     ap.add_argument("--decode-batch", type=int, default=8,
                     help="sequences of the decode measurement (0: skip it)")
     args = ap.parse_args()
@@ -430,6 +508,8 @@ def main():
         result["qkv_projection"] = measure_qkv(w, K, hev, new_events, MFMA_PEAK_F16)
     if args.decode_batch > 0:
         result["decode"] = measure_decode(args.decode_batch, K, hev, new_events)
+    if args.configs:
+        result["configs"] = measure_configs(args.workload, hev, new_events)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

@@ -38,7 +38,9 @@ bool dtype_ok(ne_dtype_t in, ne_dtype_t out) {
     return false;
 }
 
-ne_status_t check_shape(int B, int T, int Hq, int Hkv, int D) {
+// esz: bytes of a kernel operand element (4 on the fp32 path, 2 otherwise).  The direct LDS loads
+// address a (batch, KV head) group's T G rows with 32-bit byte offsets, so T G D esz stays below 2^31.
+ne_status_t check_shape(int B, int T, int Hq, int Hkv, int D, int esz) {
     if (B < 1 || T < 1 || Hq < 1 || Hkv < 1)
         return fail(NE_ERR_SHAPE, "B=%d T=%d Hq=%d Hkv=%d must all be >= 1", B, T, Hq, Hkv);
     if (Hq % Hkv != 0) return fail(NE_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
@@ -47,6 +49,9 @@ ne_status_t check_shape(int B, int T, int Hq, int Hkv, int D) {
     if (B > 65535 || Hkv > 65535) return fail(NE_ERR_SHAPE, "B and Hkv must be <= 65535");
     const int64_t TG = (int64_t)T * (Hq / Hkv);
     if (TG + 128 > INT32_MAX) return fail(NE_ERR_SHAPE, "T * Hq / Hkv = %lld is too large", (long long)TG);
+    if ((TG + 128) * D * esz > INT32_MAX)
+        return fail(NE_ERR_SHAPE, "T * Hq / Hkv * head_dim = %lld is too large for 32-bit row offsets",
+                    (long long)(TG * D));
     const int64_t n = (int64_t)B * T * Hq * D;
     if (n > ((int64_t)1 << 46)) return fail(NE_ERR_SHAPE, "tensor of %lld elements is too large", (long long)n);
     return NE_OK;
@@ -91,7 +96,7 @@ ne_status_t check_opts(const ne_attn_opts_t* o, ne::QkNorm* qkn) {
 }
 
 ne_status_t common_checks(int B, int T, int Hq, int Hkv, int D, ne_dtype_t in, ne_dtype_t out) {
-    ne_status_t s = check_shape(B, T, Hq, Hkv, D);
+    ne_status_t s = check_shape(B, T, Hq, Hkv, D, in == NE_F32 ? 4 : 2);
     if (s != NE_OK) return s;
     if (!dtype_ok(in, out))
         return fail(NE_ERR_UNSUPPORTED, "dtype pair in=%d out=%d is not supported", (int)in, (int)out);
@@ -120,14 +125,14 @@ const char* ne_status_str(ne_status_t s) {
 }
 
 size_t ne_rope_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim, ne_dtype_t in_dtype) {
-    if (check_shape(B, T, Hq, Hkv, head_dim) != NE_OK) return 0;
     if (in_dtype != NE_F32 && in_dtype != NE_BF16 && in_dtype != NE_F16) return 0;
+    if (check_shape(B, T, Hq, Hkv, head_dim, in_dtype == NE_F32 ? 4 : 2) != NE_OK) return 0;
     return layout(false, B, T, Hq, Hkv, head_dim, in_dtype).total;
 }
 
 size_t ne_rope_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim, ne_dtype_t in_dtype) {
-    if (check_shape(B, T, Hq, Hkv, head_dim) != NE_OK) return 0;
     if (in_dtype != NE_F32 && in_dtype != NE_BF16 && in_dtype != NE_F16) return 0;
+    if (check_shape(B, T, Hq, Hkv, head_dim, in_dtype == NE_F32 ? 4 : 2) != NE_OK) return 0;
     return layout(true, B, T, Hq, Hkv, head_dim, in_dtype).total;
 }
 

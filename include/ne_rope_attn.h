@@ -50,7 +50,10 @@ typedef enum { NE_F32 = 0, NE_BF16 = 1, NE_F16 = 2 } ne_dtype_t;
 typedef enum {
     NE_OK = 0,
     NE_ERR_NULL = 1,        /* a required pointer is NULL                                   */
-    NE_ERR_SHAPE = 2,       /* B, T, Hq, Hkv < 1, Hq % Hkv != 0, or sizes overflow            */
+    NE_ERR_SHAPE = 2,       /* B, T, Hq, Hkv < 1, Hq % Hkv != 0, or sizes overflow (for the
+                               attention calls: T * (Hq / Hkv) * head_dim * e >= 2^31, e = 4
+                               for fp32 inputs, else 2 -- a KV group's rows are addressed with
+                               32-bit byte offsets)                                           */
     NE_ERR_UNSUPPORTED = 3, /* head_dim not in {32, 64, 128}, or dtype pair not supported     */
     NE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                               */
     NE_ERR_WORKSPACE = 5,   /* workspace_bytes smaller than the matching *_workspace_bytes()  */

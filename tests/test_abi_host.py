@@ -61,6 +61,21 @@ def test_workspace_sizes(L):
     assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, 96, binding.NE_BF16) == 0
 
 
+def test_group_rows_beyond_32_bit_offsets_are_rejected(L):
+    """A (batch, KV head) group's T G rows of head_dim operand elements are addressed with 32-bit byte
+    offsets: T G D times 2 (16-bit operands) or 4 (fp32 path) must stay below 2^31."""
+    bf, f32 = binding.NE_BF16, binding.NE_F32
+    # T G D = 2^29: fine with 16-bit operands, too large on the fp32 path
+    assert L.ne_rope_attn_bwd_workspace_bytes(1, 1 << 20, 4, 1, 128, bf) > 0
+    assert L.ne_rope_attn_bwd_workspace_bytes(1, 1 << 20, 4, 1, 128, f32) == 0
+    assert L.ne_rope_attn_fwd_workspace_bytes(1, 1 << 20, 4, 1, 128, f32) == 0
+    # T G D = 2^31 / 2: too large for 16-bit operands as well
+    assert L.ne_rope_attn_fwd_workspace_bytes(1, 1 << 21, 8, 1, 64, bf) == 0
+    assert L.ne_rope_attn_fwd_workspace_bytes(1, 1 << 20, 8, 1, 64, bf) > 0
+    # the same limit through an entry point (validation fails before any launch)
+    assert fwd_call(L, T=1 << 21, Hq=8, Hkv=1, D=64, wsb=1 << 40) == 2   # NE_ERR_SHAPE
+
+
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
 
 

@@ -362,6 +362,41 @@ __device__ __forceinline__ void lds_fill_vt(_Float16* tile, const _Float16* src,
     }
 }
 
+// lds_fill and lds_fill_vt with the tile given as a wave-uniform 32-bit LDS byte address (no
+// generic-pointer round trip per load).
+template <typename OP, int D, int ROWS, int NW>
+__device__ __forceinline__ void lds_fill_at(unsigned tile, const OP* src, int n0, int nrows) {
+    using TL = Tile<OP, D>;
+    constexpr int CHUNKS = ROWS * TL::CPR;
+    constexpr int WL = CHUNKS / 64;
+    static_assert(CHUNKS % 64 == 0, "tile must be a whole number of wave loads");
+    const int l = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < (WL + NW - 1) / NW; ++i) {
+        const int j = i * NW + w;
+        if (WL % NW != 0 && j >= WL) break;
+        const int q = 64 * j + l;
+        const int r = q / TL::CPR, p = q % TL::CPR;
+        const int gr = min(n0 + r, nrows - 1);
+        const unsigned off = (unsigned)((gr * D + (p ^ TL::swz(r)) * TL::EPC) * (int)sizeof(OP));
+        dma16_s(off, src, __builtin_amdgcn_readfirstlane(tile + 1024u * (unsigned)j));
+    }
+}
+template <int D, int BN, int NW>
+__device__ __forceinline__ void lds_fill_vt_at(unsigned tile, const _Float16* src, int n0, int Tp) {
+    constexpr int CPR = BN / 8, WL = D * CPR / 64;
+    const int l = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < (WL + NW - 1) / NW; ++i) {
+        const int j = i * NW + w;
+        if (WL % NW != 0 && j >= WL) break;
+        const int q = 64 * j + l;
+        const int r = q / CPR, sl = q % CPR;
+        const _Float16* g = src + (size_t)r * Tp + n0 + 8 * VtTile<BN>::slot(r, sl);
+        dma16(g, __builtin_amdgcn_readfirstlane(tile + 1024u * (unsigned)j));
+    }
+}
+
 // Row fragment from a swizzled tile (k-step ks of row r), both operand types.
 template <typename OP, int D>
 __device__ __forceinline__ typename Mma<OP>::frag row_frag_sw(const OP* tile, int r, int ks, int h) {

@@ -535,10 +535,15 @@ void fwd_kernel_h(FwdArgs a) {
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
     const OP* vtg = (const OP*)a.vh + grp * (size_t)D * Tp;
     const bool rope = a.rope_base > 0.0;
-    auto kst = [&](int j) { return lds + (j % NST) * TILE; };
-    auto vst = [&](int j) { return lds + (NST + j % NST) * TILE; };
-    auto fill_k = [&](int j) { lds_fill<OP, D, BN, NW>(kst(j), kg, j * BN, T); };
-    auto fill_v = [&](int j) { lds_fill_vt<D, BN, NW>(vst(j), vtg, j * BN, Tp); };
+    // ring stage of tile j: (j - j0) % NST, a compile-time constant in the unrolled main loop, so
+    // the stage offsets fold into the LDS instructions' immediate offsets
+    const unsigned lds0 = lds_addr(lds);
+    auto kst = [&](int s) { return lds + s * TILE; };
+    auto vst = [&](int s) { return lds + (NST + s) * TILE; };
+    auto fill_k = [&](int j, int s) { lds_fill_at<OP, D, BN, NW>(lds0 + (unsigned)(s * TILE * 2), kg, j * BN, T); };
+    auto fill_v = [&](int j, int s) {
+        lds_fill_vt_at<D, BN, NW>(lds0 + (unsigned)((NST + s) * TILE * 2), vtg, j * BN, Tp);
+    };
     const int nkw = lds_fill_count<OP, D, BN, NW>(w), nvw = lds_fill_vt_count<D, BN, NW>(w);
     auto kept = [&](int it) {  // loads this wave issued in iteration it - 1 (K of it + 2, V of it)
         return (it + 2 < ntiles ? nkw : 0) + (it < ntiles ? nvw : 0);
@@ -553,8 +558,8 @@ void fwd_kernel_h(FwdArgs a) {
         load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, qmul, h, rvalid);
     }
     wait_all();
-    fill_k(j0);
-    if (ntiles > j0 + 1) fill_k(j0 + 1);
+    fill_k(j0, 0);
+    if (ntiles > j0 + 1) fill_k(j0 + 1, 1);
     lds_fill_wait_keep(ntiles > j0 + 1 ? nkw : 0);  // K of tile j0
 
     floatx16 s[2];        // scores of one tile (32 keys per accumulator)
@@ -585,8 +590,8 @@ void fwd_kernel_h(FwdArgs a) {
         return max_halves(mx);
     };
     // phase 2: scores of tile j, products alternating between the two 32-key accumulators
-    auto phase2 = [&](int j) {
-        const OP* Ks = kst(j);
+    auto phase2 = [&](int j, auto SK) {
+        const OP* Ks = kst(decltype(SK)::value);
         constexpr int AH = N2 < 4 ? N2 : 4;
         half8 fr[N2];
 #pragma unroll
@@ -603,12 +608,12 @@ void fwd_kernel_h(FwdArgs a) {
     };
     // phase 1 of iteration j: O^T += V^T P^T for tile j - 1 (when PV) and the probabilities of
     // tile j (parity C), whose sum is returned; the 32 exponentials are spread over the products
-    auto phase1 = [&](int j, auto PAR, auto PV) -> float {
+    auto phase1 = [&](int j, auto PAR, auto PV, auto SV) -> float {
         constexpr int C = decltype(PAR)::value, NP = C ^ 1;
         constexpr bool DO_PV = decltype(PV)::value;
         constexpr int NS = DO_PV ? N1 : 1;              // issue slots
         constexpr int AH = N1 < 4 ? N1 : 4;
-        const OP* Vs = vst(j - 1);
+        const OP* Vs = vst(decltype(SV)::value);
         auto rd = [&](int i) { return vt_frag<BN>(Vs, 32 * (i % NDB) + c, i / NDB, h); };
         half8 fr[N1];
         half2v hp[16];
@@ -654,22 +659,24 @@ void fwd_kernel_h(FwdArgs a) {
             pend = true;
         }
     };
-    auto sync_fill = [&](int it) {
+    auto sync_fill = [&](int it, auto S) {
         // K of tile it + 1 and V of tile it - 1 have landed (K of it + 2 and V of it may still be
         // in flight); every wave is done with the stages the new loads overwrite (K of tile it,
-        // V of tile it - 2)
+        // V of tile it - 2); S = stage of tile it
+        constexpr int s = decltype(S)::value;
         lds_fill_wait_keep(kept(it));
-        if (it + 3 < ntiles) fill_k(it + 3);
-        if (it + 1 < ntiles) fill_v(it + 1);
+        if (it + 3 < ntiles) fill_k(it + 3, s);
+        if (it + 1 < ntiles) fill_v(it + 1, (s + 1) % NST);
     };
     // A wave starts at its own first tile: the iterations before it are skipped, the one just
     // before it exponentiates scores that are all -inf (p = 0, with m_run still at the floor).
-    auto step = [&](int it, auto PAR) {
-        sync_fill(it);
+    auto step = [&](int it, auto PAR, auto S) {
+        constexpr int s = decltype(S)::value;
+        sync_fill(it, S);
         if (it >= first - 1 && it <= last + 1) {
-            const float ps = phase1(it, PAR, IC<1>{});
+            const float ps = phase1(it, PAR, IC<1>{}, IC<(s + 2) % NST>{});
             l_run += it <= last ? ps : 0.f;  // iteration last + 1 only finishes the product
-            if (it + 1 <= last) phase2(it + 1);
+            if (it + 1 <= last) phase2(it + 1, IC<(s + 1) % NST>{});
             if (pend) {  // O now holds every tile whose probabilities used the old m
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
@@ -683,27 +690,36 @@ void fwd_kernel_h(FwdArgs a) {
 
     // iteration j0 - 1: the scores of tile j0 fix the first m exactly for the rows that see it
     // (without a window, every row); the others keep the floor until their first tile
-    if (ntiles > j0 + 2) fill_k(j0 + 2);
-    fill_v(j0);
+    if (ntiles > j0 + 2) fill_k(j0 + 2, 2);
+    fill_v(j0, 0);
     if (last >= 0) {
-        phase2(j0);
+        phase2(j0, IC<0>{});
         m_run = fmaxf(mask_max(j0), kMFloor);
     }
     // iteration j0: no product yet
-    sync_fill(j0);
+    sync_fill(j0, IC<0>{});
     if (last >= 0) {
-        l_run = phase1(j0, IC<0>{}, IC<0>{});
+        l_run = phase1(j0, IC<0>{}, IC<0>{}, IC<0>{});
         if (last >= j0 + 1) {
-            phase2(j0 + 1);
+            phase2(j0 + 1, IC<1>{});
             refresh(j0 + 1);
         }
     }
     // iterations j0 + 1 .. ntiles, run by every wave (the barriers are block-wide); the parity of
     // the probability buffers counts from j0
-    for (int it = j0 + 1; it <= ntiles; it += 2) {
-        step(it, IC<1>{});
+    // unrolled by six: probability parity (it - j0) % 2 and ring stage (it - j0) % 3
+    for (int it = j0 + 1; it <= ntiles; it += 6) {
+        step(it, IC<1>{}, IC<1>{});
         if (it + 1 > ntiles) break;
-        step(it + 1, IC<0>{});
+        step(it + 1, IC<0>{}, IC<2>{});
+        if (it + 2 > ntiles) break;
+        step(it + 2, IC<1>{}, IC<0>{});
+        if (it + 3 > ntiles) break;
+        step(it + 3, IC<0>{}, IC<1>{});
+        if (it + 4 > ntiles) break;
+        step(it + 4, IC<1>{}, IC<2>{});
+        if (it + 5 > ntiles) break;
+        step(it + 5, IC<0>{}, IC<0>{});
     }
 
     const float l_tot = sum_halves(l_run);
@@ -1051,10 +1067,11 @@ void dkdv_kernel_h(BwdArgs a) {
 
     // Q and dO rows, lse2 (wave 0) and Delta (wave 1) of rows [R0, R0 + 64), all by direct loads;
     // rows past TG are copies of row TG - 1 and are masked out (P = 0) below.
-    auto fill = [&](int stage, int R0) {
-        OP* dst = lds + stage * 2 * TILE;
-        lds_fill<OP, D, BMR, NW>(dst, qg, R0, TG);
-        lds_fill<OP, D, BMR, NW>(dst + TILE, og, R0, TG);
+    const unsigned lds0 = lds_addr(lds);
+    auto fill = [&](int stage, int R0) {   // 32-bit LDS bases: no generic-pointer round trip
+        const unsigned dst = lds0 + (unsigned)(stage * 2 * TILE * 2);
+        lds_fill_at<OP, D, BMR, NW>(dst, qg, R0, TG);
+        lds_fill_at<OP, D, BMR, NW>(dst + TILE * 2, og, R0, TG);
         if (w < 2) {
             const float* src = (w == 0 ? lse2g : delg) + min(R0 + l, TG - 1);
             dma4(src, lds_addr(&rowv[stage][w][0]));
@@ -1437,8 +1454,12 @@ void dq_kernel_h(BwdArgs a) {
     const half8 fd = fold_frag(rvalid ? -a.delta[grp * (size_t)TG + R] : 0.f, h);
     const half8 fw = fold_weights(h);
     wait_all();
-    lds_fill<OP, D, BN, NW>(lds, kg, j0 * BN, T);
-    lds_fill<OP, D, BN, NW>(lds + TILE, vg, j0 * BN, T);
+    const unsigned lds0 = lds_addr(lds);
+    auto fill = [&](int j, int st) {   // K and V of tile j into ring stage st (32-bit LDS bases)
+        lds_fill_at<OP, D, BN, NW>(lds0 + (unsigned)(st * 2 * TILE * 2), kg, j * BN, T);
+        lds_fill_at<OP, D, BN, NW>(lds0 + (unsigned)((st * 2 + 1) * TILE * 2), vg, j * BN, T);
+    };
+    fill(j0, 0);
 
     floatx16 dq[NDB];
 #pragma unroll
@@ -1448,11 +1469,7 @@ void dq_kernel_h(BwdArgs a) {
         const OP* Ks = lds + ((it - j0) & 1) * 2 * TILE;
         const OP* Vs = Ks + TILE;
         lds_fill_wait();
-        if (it + 1 < ntiles) {
-            OP* nxt = lds + ((it + 1 - j0) & 1) * 2 * TILE;
-            lds_fill<OP, D, BN, NW>(nxt, kg, (it + 1) * BN, T);
-            lds_fill<OP, D, BN, NW>(nxt + TILE, vg, (it + 1) * BN, T);
-        }
+        if (it + 1 < ntiles) fill(it + 1, (it + 1 - j0) & 1);
         const int n0 = it * BN;
         if (n0 > wave_tmax) continue;                 // every row of this wave precedes the tile
         if (wave_tmin - (n0 + BN - 1) >= W) continue;  // the tile is older than every row's window

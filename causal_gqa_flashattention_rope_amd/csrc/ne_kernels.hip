@@ -499,6 +499,35 @@ void fwd_kernel(FwdArgs a) {
 // =====================================================================================
 template <int V> struct IC { static constexpr int value = V; };
 
+// =====================================================================================
+// Backward dK/dV, 16-bit operands.  Same work split as dkdv_kernel (8 waves: row half, 32-key
+// sub-block, role; mirrored 64-key block pairs), but the two roles work one row tile apart, so
+// a step needs one barrier: at step s the role-0 wave computes S and P of tile s, hands P to its
+// role-1 partner through an LDS buffer of step parity s & 1 and adds dO^T P to dV^T, while the
+// role-1 wave computes dP of tile s - 1, dS with the P handed over one step earlier and adds
+// Q^T dS to dK^T.  The shifts by lse2 and by Delta ride on one extra k-step of the S and dP
+// products: the A operand carries three fp16 terms of -lse2 (or -Delta) of the lane's row
+// (fold_frag) against B = (256, 1, 1), so the accumulators come out as S - lse2 and
+// dP - Delta with fp32 accuracy and no per-element subtraction.  Row tiles go through a 4-stage
+// ring filled two steps ahead.
+// =====================================================================================
+// Three fp16 terms with 256 a + b + c = x to about 2^-33 |x| (|x| < 2^24): lane half 0 of the
+// A operand of an extra k-step (k = 0, 1, 2); lane half 1 holds zeros.
+__device__ __forceinline__ half8 fold_frag(float x, int h) {
+    const _Float16 a = (_Float16)(x * (1.f / 256.f));
+    const float r1 = x - 256.f * (float)a;
+    const _Float16 b = (_Float16)r1;
+    const _Float16 c = (_Float16)(r1 - (float)b);
+    const _Float16 z = (_Float16)0.f;
+    return h == 0 ? half8{a, b, c, z, z, z, z, z} : half8{z, z, z, z, z, z, z, z};
+}
+// The matching B operand (k = 0, 1, 2 weighted 256, 1, 1 for every column).
+__device__ __forceinline__ half8 fold_weights(int h) {
+    const _Float16 z = (_Float16)0.f;
+    return h == 0 ? half8{(_Float16)256.f, (_Float16)1.f, (_Float16)1.f, z, z, z, z, z} : half8{z, z, z, z, z, z, z, z};
+}
+
+
 template <typename TI, int D, typename TOUT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel_h(FwdArgs a) {
@@ -570,8 +599,24 @@ void fwd_kernel_h(FwdArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = floatx16{};
     float m_run = kMFloor, l_run = 0.f, apend = 1.f;
+    // The score products start from -mf (an extra k-step: fold weights x the split of -mf), so the
+    // accumulators hold S - mf and the exponentials need no subtraction; mf = m_run once the row
+    // has seen a key (0 before, when m_run is the floor), and a refresh rebases the current tile.
+    float mf = 0.f;
+    const half8 fw = fold_weights(h);
+    half8 fmf = fold_frag(0.f, h);
     bool pend = false;
 
+    // scores of the current tile from S - mf to S - m_run, and the fold to the new m_run
+    auto rebase = [&]() {
+        const float dl = m_run - mf;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[mb][r] -= dl;
+        mf = m_run > 0.5f * kMFloor ? m_run : 0.f;
+        fmf = fold_frag(-mf, h);
+    };
     // mask of tile j (if it crosses a diagonal or a window edge), then the row max
     auto mask_max = [&](int j) {
         const int n0 = j * BN;
@@ -596,8 +641,8 @@ void fwd_kernel_h(FwdArgs a) {
         half8 fr[N2];
 #pragma unroll
         for (int i = 0; i < AH; ++i) fr[i] = row_frag_sw<OP, D>(Ks, 32 * (i & 1) + c, i >> 1, h);
-        s[0] = floatx16{};
-        s[1] = floatx16{};
+        s[0] = M::mma(fw, fmf, floatx16{});
+        s[1] = s[0];
 #pragma unroll
         for (int i = 0; i < N2; ++i) {
             __builtin_amdgcn_sched_barrier(0);
@@ -631,7 +676,7 @@ void fwd_kernel_h(FwdArgs a) {
             }
 #pragma unroll
             for (int e = 32 * i / NS; e < 32 * (i + 1) / NS; ++e) {
-                const float x = __builtin_amdgcn_exp2f(s[e >> 4][e & 15] - m_run);
+                const float x = __builtin_amdgcn_exp2f(s[e >> 4][e & 15]);
                 if (e & 1) {
                     hp[e >> 1][1] = (_Float16)x;
                     ps = __builtin_amdgcn_fdot2(hp[e >> 1], half2v{1, 1}, ps, false);
@@ -651,10 +696,11 @@ void fwd_kernel_h(FwdArgs a) {
     // after the scores of tile j are in s: mask, max and the (rare) refresh of m
     auto refresh = [&](int j) {
         const float mx = mask_max(j);
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + TAU) != 0) {  // raise m to this tile's max
-            const float m_new = fmaxf(m_run, mx);
+        if (__builtin_amdgcn_ballot_w64(mf + mx > m_run + TAU) != 0) {  // raise m to this tile's max
+            const float m_new = fmaxf(m_run, mf + mx);
             apend = __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
+            rebase();
             l_run *= apend;
             pend = true;
         }
@@ -695,6 +741,7 @@ void fwd_kernel_h(FwdArgs a) {
     if (last >= 0) {
         phase2(j0, IC<0>{});
         m_run = fmaxf(mask_max(j0), kMFloor);
+        rebase();
     }
     // iteration j0: no product yet
     sync_fill(j0, IC<0>{});
@@ -1004,33 +1051,6 @@ void dkdv_kernel(BwdArgs a) {
     }
 }
 
-// =====================================================================================
-// Backward dK/dV, 16-bit operands.  Same work split as dkdv_kernel (8 waves: row half, 32-key
-// sub-block, role; mirrored 64-key block pairs), but the two roles work one row tile apart, so
-// a step needs one barrier: at step s the role-0 wave computes S and P of tile s, hands P to its
-// role-1 partner through an LDS buffer of step parity s & 1 and adds dO^T P to dV^T, while the
-// role-1 wave computes dP of tile s - 1, dS with the P handed over one step earlier and adds
-// Q^T dS to dK^T.  The shifts by lse2 and by Delta ride on one extra k-step of the S and dP
-// products: the A operand carries three fp16 terms of -lse2 (or -Delta) of the lane's row
-// (fold_frag) against B = (256, 1, 1), so the accumulators come out as S - lse2 and
-// dP - Delta with fp32 accuracy and no per-element subtraction.  Row tiles go through a 4-stage
-// ring filled two steps ahead.
-// =====================================================================================
-// Three fp16 terms with 256 a + b + c = x to about 2^-33 |x| (|x| < 2^24): lane half 0 of the
-// A operand of an extra k-step (k = 0, 1, 2); lane half 1 holds zeros.
-__device__ __forceinline__ half8 fold_frag(float x, int h) {
-    const _Float16 a = (_Float16)(x * (1.f / 256.f));
-    const float r1 = x - 256.f * (float)a;
-    const _Float16 b = (_Float16)r1;
-    const _Float16 c = (_Float16)(r1 - (float)b);
-    const _Float16 z = (_Float16)0.f;
-    return h == 0 ? half8{a, b, c, z, z, z, z, z} : half8{z, z, z, z, z, z, z, z};
-}
-// The matching B operand (k = 0, 1, 2 weighted 256, 1, 1 for every column).
-__device__ __forceinline__ half8 fold_weights(int h) {
-    const _Float16 z = (_Float16)0.f;
-    return h == 0 ? half8{(_Float16)256.f, (_Float16)1.f, (_Float16)1.f, z, z, z, z, z} : half8{z, z, z, z, z, z, z, z};
-}
 
 template <int D, typename TOUT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))

@@ -493,26 +493,20 @@ void fwd_kernel(FwdArgs a) {
 //   then its mask (diagonal tiles only), row max and the rare refresh of the reference max m.
 // A refresh rescales the row sum at once and O after the next phase 1, which adds the last
 // probabilities that still use the old m.  The row sums are packed dot products of the fp16
-// probabilities that the product consumes.  V arrives transposed (vt_frag), so both operand
-// streams are plain 16-byte LDS reads, four products ahead of their use.  K and V^T tiles go
-// through 3-stage LDS rings filled two iterations ahead by direct loads.
+// probabilities that the product consumes.  The score products start from -m (one fold k-step
+// per 32-key accumulator), so the exponentials take the accumulators as they are; a refresh
+// rebases the tile in hand.  V arrives transposed (vt_frag), so both operand streams are plain
+// 16-byte LDS reads, four products ahead of their use.  K and V^T tiles go through 3-stage LDS
+// rings filled two iterations ahead by direct loads; the main loop is unrolled by six, so ring
+// stages and probability buffers are compile-time and their offsets fold into the LDS
+// instructions.
 // =====================================================================================
 template <int V> struct IC { static constexpr int value = V; };
 
-// =====================================================================================
-// Backward dK/dV, 16-bit operands.  Same work split as dkdv_kernel (8 waves: row half, 32-key
-// sub-block, role; mirrored 64-key block pairs), but the two roles work one row tile apart, so
-// a step needs one barrier: at step s the role-0 wave computes S and P of tile s, hands P to its
-// role-1 partner through an LDS buffer of step parity s & 1 and adds dO^T P to dV^T, while the
-// role-1 wave computes dP of tile s - 1, dS with the P handed over one step earlier and adds
-// Q^T dS to dK^T.  The shifts by lse2 and by Delta ride on one extra k-step of the S and dP
-// products: the A operand carries three fp16 terms of -lse2 (or -Delta) of the lane's row
-// (fold_frag) against B = (256, 1, 1), so the accumulators come out as S - lse2 and
-// dP - Delta with fp32 accuracy and no per-element subtraction.  Row tiles go through a 4-stage
-// ring filled two steps ahead.
-// =====================================================================================
-// Three fp16 terms with 256 a + b + c = x to about 2^-33 |x| (|x| < 2^24): lane half 0 of the
-// A operand of an extra k-step (k = 0, 1, 2); lane half 1 holds zeros.
+// Shifts that ride on one extra k-step of a product: three fp16 terms with 256 a + b + c = x to
+// about 2^-33 |x| (|x| < 2^24) in lane half 0 of one operand (k = 0, 1, 2; lane half 1 holds
+// zeros), against fold_weights (256, 1, 1) in the other, add x to every accumulator element of
+// the lane's row or column with fp32 accuracy and no per-element arithmetic.
 __device__ __forceinline__ half8 fold_frag(float x, int h) {
     const _Float16 a = (_Float16)(x * (1.f / 256.f));
     const float r1 = x - 256.f * (float)a;
@@ -521,7 +515,7 @@ __device__ __forceinline__ half8 fold_frag(float x, int h) {
     const _Float16 z = (_Float16)0.f;
     return h == 0 ? half8{a, b, c, z, z, z, z, z} : half8{z, z, z, z, z, z, z, z};
 }
-// The matching B operand (k = 0, 1, 2 weighted 256, 1, 1 for every column).
+// The matching operand (k = 0, 1, 2 weighted 256, 1, 1 for every row or column).
 __device__ __forceinline__ half8 fold_weights(int h) {
     const _Float16 z = (_Float16)0.f;
     return h == 0 ? half8{(_Float16)256.f, (_Float16)1.f, (_Float16)1.f, z, z, z, z, z} : half8{z, z, z, z, z, z, z, z};
@@ -1052,6 +1046,18 @@ void dkdv_kernel(BwdArgs a) {
 }
 
 
+// =====================================================================================
+// Backward dK/dV, 16-bit operands.  Same work split as dkdv_kernel (8 waves: row half, 32-key
+// sub-block, role; mirrored 64-key block pairs), but the two roles work one row tile apart, so
+// a step needs one barrier: at step s the role-0 wave computes S and P of tile s, hands P to its
+// role-1 partner through an LDS buffer of step parity s & 1 and adds dO^T P to dV^T, while the
+// role-1 wave computes dP of tile s - 1, dS with the P handed over one step earlier and adds
+// Q^T dS to dK^T.  The shifts by lse2 and by Delta ride on one extra k-step of the S and dP
+// products: the A operand carries three fp16 terms of -lse2 (or -Delta) of the lane's row
+// (fold_frag) against B = (256, 1, 1), so the accumulators come out as S - lse2 and
+// dP - Delta with fp32 accuracy and no per-element subtraction.  Row tiles go through a 4-stage
+// ring filled two steps ahead.
+// =====================================================================================
 template <int D, typename TOUT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void dkdv_kernel_h(BwdArgs a) {

@@ -52,6 +52,10 @@ WORKLOADS = {
     "long_ctx_t8192": Workload(
         "long_ctx_t8192", 1, 8192, 32, 8, 128, 5.0e5, 1.0, (501, 502, 503, 504), "bf16",
         "Long-context stress: B1 T8192 Hq32 Hkv8 D128, RoPE base 5e5, bf16 in"),
+    "long_ctx_t8192_shard8": Workload(
+        "long_ctx_t8192_shard8", 1, 8192, 4, 1, 128, 5.0e5, 1.0, (511, 512, 513, 514), "bf16",
+        "One GPU's share of the long-context layer split over 8 GPUs by KV head: B1 T8192 Hq4 Hkv1 "
+        "D128 (one KV group), RoPE base 5e5, bf16 in"),
 }
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}

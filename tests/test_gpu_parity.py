@@ -156,6 +156,24 @@ def test_workload_long_ctx_bf16():
     workload_parity("long_ctx_t8192", [(0, 5)])
 
 
+def test_one_kv_group_alone_equals_its_slice_of_the_full_run_bitwise():
+    """The long-context layer sharded by KV head (one group per GPU, no exchange): a group run on
+    its own, as one GPU of 8 would, gives exactly the bits of that group in the full run."""
+    w = inputs.WORKLOADS["long_ctx_t8192"]
+    q, k, v, dO = inputs.make_inputs(w)
+    full = run_gpu(q, k, v, dO, w.rope_base, torch.float32)
+    G = w.G
+    for g in (0, 5):
+        qs, dOs = slice_group(q, 0, g, G), slice_group(dO, 0, g, G)
+        ks, vs = slice_group(k, 0, g, 0), slice_group(v, 0, g, 0)
+        o, lse, dq, dk, dv = run_gpu(qs, ks, vs, dOs, w.rope_base, torch.float32)
+        assert torch.equal(o.cpu(), slice_group(full[0], 0, g, G).cpu())
+        assert torch.equal(lse.cpu(), full[1][:, g * G:(g + 1) * G].cpu())
+        assert torch.equal(dq.cpu(), slice_group(full[2], 0, g, G).cpu())
+        assert torch.equal(dk.cpu(), slice_group(full[3], 0, g, 0).cpu())
+        assert torch.equal(dv.cpu(), slice_group(full[4], 0, g, 0).cpu())
+
+
 # ---------------------------------------------------------------------------------------
 # Properties checked on the GPU outputs themselves.
 # ---------------------------------------------------------------------------------------

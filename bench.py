@@ -45,6 +45,25 @@ QKV_SOURCES = ["causal_gqa_flashattention_rope_amd/csrc/ne_qkv.hip",
                "causal_gqa_flashattention_rope_amd/csrc/ne_common.hpp"]
 
 
+def dq_flops_per_pair_over_d(B, T, Hq, Hkv, D, dtype):
+    """Executed MFMA work of the dQ pass per (query, key) pair and head, in units of D: 2 when it
+    reads the dS the dK/dV pass stores (the 16-bit path while that buffer fits its cap), 6 when it
+    recomputes S and dP.  The stored dS shows as extra backward workspace."""
+    from causal_gqa_flashattention_rope_amd import binding
+    key = "NE_ROPE_ATTN_DS_MAX_BYTES"
+    with_ds = binding.bwd_workspace_bytes(B, T, Hq, Hkv, D, dtype)
+    old = os.environ.get(key)
+    os.environ[key] = "0"
+    try:
+        without = binding.bwd_workspace_bytes(B, T, Hq, Hkv, D, dtype)
+    finally:
+        if old is None:
+            os.environ.pop(key, None)
+        else:
+            os.environ[key] = old
+    return 2.0 if with_ds > without else 6.0
+
+
 def kernel_source_hash(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
     for rel in sources:
@@ -446,8 +465,9 @@ def main():
     unit = B * Hq * D * N
     flops_step = 14.0 * unit
     value = flops_step / (ms_per_step * 1e-3) / 1e12
-    # executed-useful MFMA work per launch (the deterministic dQ pass recomputes S and dP)
-    kern_flops = {"attn_fwd": 4.0 * unit, "attn_bwd_dkdv": 8.0 * unit, "attn_bwd_dq": 6.0 * unit}
+    # executed MFMA work per launch (dQ: from the stored dS, or recomputing S and dP)
+    dqf = dq_flops_per_pair_over_d(B, T, Hq, Hkv, D, q.dtype)
+    kern_flops = {"attn_fwd": 4.0 * unit, "attn_bwd_dkdv": 8.0 * unit, "attn_bwd_dq": dqf * unit}
     peak = MFMA_PEAK_F16 if q.dtype != torch.float32 else MFMA_PEAK_F32
     achieved = kern_flops[dominant] / (dom_ms * 1e-3) / 1e12
     traffic = read_traffic(dominant, args.workload)
@@ -485,7 +505,7 @@ def main():
         # sliding window: the same step, counting the visible pairs only
         ms_w, dom_w, dom_ms_w, kern_w = measure(make_step(Wn), 20, K)
         unit_w = B * Hq * D * (Wn * (Wn + 1) / 2 + (T - Wn) * Wn)
-        kf_w = {"attn_fwd": 4.0 * unit_w, "attn_bwd_dkdv": 8.0 * unit_w, "attn_bwd_dq": 6.0 * unit_w}
+        kf_w = {"attn_fwd": 4.0 * unit_w, "attn_bwd_dkdv": 8.0 * unit_w, "attn_bwd_dq": dqf * unit_w}
         ach_w = kf_w[dom_w] / (dom_ms_w * 1e-3) / 1e12
         result["sliding_window"] = {
             "window": Wn, "pairs_per_head": Wn * (Wn + 1) // 2 + (T - Wn) * Wn,

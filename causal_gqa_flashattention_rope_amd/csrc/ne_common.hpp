@@ -223,6 +223,11 @@ __device__ __forceinline__ void dma16_s(unsigned voff, const void* sbase, unsign
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase),
                  "s"(lds_base) : "memory", "m0");
 }
+// Same for data read exactly once (non-temporal: it should not displace reused data in the caches).
+__device__ __forceinline__ void dma16_s_nt(unsigned voff, const void* sbase, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" :: "v"(voff), "s"(sbase),
+                 "s"(lds_base) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* g, unsigned lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(g), "s"(lds_base)
                  : "memory", "m0");

@@ -1058,7 +1058,7 @@ void dkdv_kernel(BwdArgs a) {
 // dP - Delta with fp32 accuracy and no per-element subtraction.  Row tiles go through a 4-stage
 // ring filled two steps ahead.
 // =====================================================================================
-template <int D, typename TOUT>
+template <int D, typename TOUT, bool DS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void dkdv_kernel_h(BwdArgs a) {
     using OP = _Float16;
@@ -1090,6 +1090,16 @@ void dkdv_kernel_h(BwdArgs a) {
     const float* delg = a.delta + grp * (size_t)TG;
     const bool rope = a.rope_base > 0.0;
     const half8 fw = fold_weights(h);
+    // DS: the dS tiles of this group (ds_tile_index), 512 fragments of 16 bytes each, in 1 KiB
+    // blocks (2 kq + rh) * 2 + cc written whole by one store; in a block, lane (h, c) takes slot
+    // 32 h + (c ^ (4 h + 8 cc)), which keeps the dQ pass's transposed reads free of bank conflicts
+    half8* dsg = nullptr;
+    int ds0 = 0, ds1 = 0;
+    if constexpr (DS) {
+        dsg = (half8*)a.ds + grp * ds_tiles_per_group((TG + 63) / 64, (T + 63) / 64, G) * 512 + (kq * 2 + rh) * 128;
+        ds0 = 32 * h + (c ^ (4 * h));
+        ds1 = 64 + 32 * h + (c ^ (4 * h + 8));
+    }
 
     // Q and dO rows, lse2 (wave 0) and Delta (wave 1) of rows [R0, R0 + 64), all by direct loads;
     // rows past TG are copies of row TG - 1 and are masked out (P = 0) below.
@@ -1158,6 +1168,8 @@ void dkdv_kernel_h(BwdArgs a) {
         const int kl = kb * BN + BN - 1;                                 // the block's last key
         const int rend = (T - kl <= W ? T : kl + W) * G;                 // rows past it see none
         const int ntiles = (rend - rstart + BMR - 1) / BMR;
+        // DS: tile s of this key block (row tile kb G + s) is stored at index dsb + s
+        const size_t dsb = DS ? ds_tile_index(kb, kb * G, (TG + 63) / 64, G) : 0;
         const int wlim = (T - (n0 + 31) <= W ? T : n0 + 31 + W) * G;    // rows from wlim see none
         const int wedge = (T - n0 <= W ? T : n0 + W) * G;                // of this wave's keys, from
                                                                          // wedge some are hidden
@@ -1184,7 +1196,8 @@ void dkdv_kernel_h(BwdArgs a) {
         for (int s = 0; s <= ntiles; ++s) {
             // tile s has landed (tile s + 1 may still be in flight); the P of tile s - 1 is in
             // pbuf[(s - 1) & 1]; every wave is done with tile s - 2 and with pbuf[s & 1]
-            lds_fill_wait_keep(s + 1 < ntiles ? per_fill : 0);
+            // (with DS, role 1's two dS stores of the previous step are its most recent operations)
+            lds_fill_wait_keep((s + 1 < ntiles ? per_fill : 0) + (DS && role == 1 && s >= 2 ? 2 : 0));
             if (s + 2 < ntiles) fill((s + 2) % NST, rstart + (s + 2) * BMR);
             if (role == 0) {
                 if (s < ntiles && active(s)) {
@@ -1213,6 +1226,10 @@ void dkdv_kernel_h(BwdArgs a) {
                     product2(Os, tf0, pf, acc);
                 }
             } else {
+                if (DS && s >= 1 && !active(s - 1)) {  // a stored tile is complete: zeros here
+                    __builtin_nontemporal_store(half8{}, &dsg[(dsb + s - 1) * 512 + ds0]);
+                    __builtin_nontemporal_store(half8{}, &dsg[(dsb + s - 1) * 512 + ds1]);
+                }
                 if (s >= 1 && active(s - 1)) {
                     const int st = (s - 1) % NST;
                     const OP* Qs = lds + st * 2 * TILE;
@@ -1227,6 +1244,10 @@ void dkdv_kernel_h(BwdArgs a) {
                         const half8 pv = pbuf[(s - 1) & 1][kq][rh][cc][l];
 #pragma unroll
                         for (int j = 0; j < 8; ++j) dsf[cc][j] = (_Float16)((float)pv[j] * y[8 * cc + j]);
+                    }
+                    if constexpr (DS) {
+                        __builtin_nontemporal_store(dsf[0], &dsg[(dsb + s - 1) * 512 + ds0]);
+                        __builtin_nontemporal_store(dsf[1], &dsg[(dsb + s - 1) * 512 + ds1]);
                     }
                     product2(Qs, tf0, dsf, acc);
                 }
@@ -1602,6 +1623,157 @@ void dq_kernel_h(BwdArgs a) {
 }
 
 // =====================================================================================
+// Backward dQ from the stored dS, 16-bit operands (deterministic, no atomics).  The dK/dV pass
+// leaves dS of every tile of 64 flattened rows x 64 keys it visits in the workspace, as its lanes
+// hold it: lane (h, c) of the wave for row half rh and key half kq has, for k-step cc, the 8 rows
+// 32 rh + 16 cc + 8 (j / 4) + 4 h + j % 4 (j < 8) of key 32 kq + c, stored in 1 KiB block
+// (2 kq + rh) * 2 + cc at slot 32 h + (c ^ (4 h + 8 cc)).  Here dQ^T += K^T dS^T: tiles are copied
+// whole into LDS, and both operands are transposed reads (ds_read_tr16_b64), dS^T addressed
+// through that layout as rows of keys and columns of positions p = 32 rh + 16 cc + 8 h + j, so
+// the contraction order of the two operands is the same j order; the epilogue maps positions
+// back to rows.  No S, P or dP is recomputed.
+// grid (ceil(nrt / RT) * B * Hkv), 128 RT threads: a block takes RT row tiles, wave w positions
+// 32 (w & 1) .. 32 (w & 1) + 31 of tile w >> 1 and all D columns of dQ; 64-key steps through a
+// 3-stage ring [K tile | the RT dS tiles] filled two steps ahead.
+// =====================================================================================
+// B operand of dQ^T += K^T dS^T for k-step kk and positions col0 .. col0 + 31 of a stored tile
+// in LDS (the same lane pattern as tr_frag_f16_sw).
+__device__ __forceinline__ half8 ds_tr_frag(const _Float16* tile, int kk, int col0) {
+    const int l = lane_id();
+    const int g = l >> 4, s = l & 15, h = l >> 5;
+    const int pos = col0 + 16 * (g & 1) + 4 * (s & 3), ch = pos >> 3;
+    const int key = 16 * kk + 4 * h + (s >> 2);                    // and key + 8 (same key half)
+    const int cc = (ch >> 1) & 1, hh = ch & 1, c = key & 31;
+    const int blk = ((key >> 5) * 2 + (ch >> 2)) * 2 + cc;
+    const int lo = (blk * 64 + 32 * hh + (c ^ (4 * hh + 8 * cc))) * 16 + (pos & 7) * 2;
+    const int hi = (blk * 64 + 32 * hh + ((c + 8) ^ (4 * hh + 8 * cc))) * 16 + (pos & 7) * 2;
+    const char* t = reinterpret_cast<const char*>(tile);
+    fp16x4_tr a = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr_ptr)(t + lo));
+    fp16x4_tr b = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr_ptr)(t + hi));
+    half8 f;
+    half4v x = __builtin_bit_cast(half4v, a), y = __builtin_bit_cast(half4v, b);
+    f[0] = x[0]; f[1] = x[1]; f[2] = x[2]; f[3] = x[3];
+    f[4] = y[0]; f[5] = y[1]; f[6] = y[2]; f[7] = y[3];
+    return f;
+}
+
+#ifndef NE_DQ_RT
+#define NE_DQ_RT 4
+#endif
+template <int D, typename TOUT, int RT>
+__global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
+    using OP = _Float16;
+    using M = Mma<OP>;
+    constexpr int BN = 64, NW = 2 * RT, NST = 3, NDB = D / 32;
+    constexpr int KT = BN * D, DT = BN * 64;           // elements of a K tile and of a dS^T tile
+    constexpr int STG = KT + RT * DT;                  // elements per ring stage
+    __shared__ __attribute__((aligned(1024))) OP lds[NST * STG];
+
+    const int T = a.T, G = a.G, TG = T * G;
+    const int nrt = (TG + 63) / 64, nkb = (T + 63) / 64;
+    const Work wk = map_block((nrt + RT - 1) / RT, a.B * a.Hkv, true);
+    const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int rt0 = RT * wk.blk;
+    const int W = a.window;
+    const size_t grp = (size_t)wk.grp;
+    const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
+    const OP* dsg = (const OP*)a.ds + grp * ds_tiles_per_group(nrt, nkb, G) * 4096;
+
+    // key blocks with a stored tile for row tile rt: kb G <= rt, and the rows that see some key
+    // of the block extend past 64 rt: min(T, 64 kb + 63 + W) G > 64 rt
+    auto kb_hi = [&](int rt) { return min(nkb - 1, rt / G); };
+    auto kb_lo = [&](int rt) {
+        const int a0 = T - 63 - W;                                   // 64 kb >= a0: reaches T
+        const int la = a0 <= 0 ? 0 : (a0 + 63) / 64;
+        const int y = (int)((int64_t)64 * rt / G) - 63 - W;           // 64 kb > y
+        const int lb = y < 0 ? 0 : y / 64 + 1;
+        return min(la, lb);
+    };
+    const int lo = kb_lo(rt0), hi = kb_hi(min(rt0 + RT - 1, nrt - 1));
+    const int rt = rt0 + (w >> 1), pb = w & 1;          // this wave's row tile and positions
+    const bool wact = rt < nrt;
+    const int wlo = wact ? kb_lo(rt) : 1, whi = wact ? kb_hi(rt) : 0;
+
+    const unsigned lds0 = lds_addr(lds);
+    // K tile kb and the stored dS tiles of row tiles rt0 .. rt0 + RT - 1 into stage st (a row
+    // tile without a stored tile for kb copies tile 0 of the group instead, which it does not use)
+    auto fill = [&](int kb, int st) {
+        const unsigned base = lds0 + (unsigned)(st * STG * 2);
+        lds_fill_at<OP, D, BN, NW>(base, kg, kb * BN, T);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int rtx = rt0 + r;
+            const bool ok = rtx < nrt && kb >= kb_lo(rtx) && kb <= kb_hi(rtx);
+            const OP* src = dsg + (ok ? ds_tile_index(kb, rtx, nrt, G) : 0) * 4096;
+#pragma unroll
+            for (int i = 0; i < 8 / NW; ++i) {
+                const int j = w + NW * i;                    // 1 KiB block j of the tile
+                dma16_s_nt((unsigned)(1024 * j + 16 * l), src,
+                        __builtin_amdgcn_readfirstlane(base + (unsigned)((KT + r * DT) * 2) + 1024u * (unsigned)j));
+            }
+        }
+    };
+    static_assert(8 % NW == 0, "whole 1 KiB blocks per wave");
+    const int per_fill = lds_fill_count<OP, D, BN, NW>(w) + RT * (8 / NW);
+
+    floatx16 dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = floatx16{};
+    if (lo <= hi) fill(lo, 0);    // (never empty: every row tile sees its own diagonal block)
+    if (lo + 1 <= hi) fill(lo + 1, 1);
+    for (int kb = lo; kb <= hi; ++kb) {
+        const int st = (kb - lo) % NST;
+        lds_fill_wait_keep(kb + 1 <= hi ? per_fill : 0);
+        if (kb + 2 <= hi) fill(kb + 2, (kb + 2 - lo) % NST);
+        if (kb < wlo || kb > whi) continue;
+        const _Float16* Ks = lds + st * STG;
+        const _Float16* Ds = Ks + KT + (w >> 1) * DT;
+        half8 df[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) df[ks] = ds_tr_frag(Ds, ks, 32 * pb);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) dq[db] = M::mma(tr_frag_f16_sw<D>(Ks, ks, 32 * db), df[ks], dq[db]);
+    }
+
+    if (!wact) return;
+    // the row of this lane's position c (both lanes of the pair c, c + 32 agree)
+    const int R = 64 * rt + 32 * pb + 16 * (c >> 4) + 8 * ((c & 7) >> 2) + 4 * ((c >> 3) & 1) + (c & 3);
+    if (R >= TG) return;
+    const int t = R / G, hh = R - t * G, hq = hkv * G + hh;
+    const size_t qoff = (((size_t)b * T + t) * a.Hq + hq) * D;
+    const float sc = a.scale;
+    const bool rope = a.rope_base > 0.0;
+    // dq = R^T (scale * dq'), in place
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d = 32 * db + 8 * q4 + 4 * h;
+            float x0 = dq[db][4 * q4] * sc, x1 = dq[db][4 * q4 + 1] * sc;
+            float x2 = dq[db][4 * q4 + 2] * sc, x3 = dq[db][4 * q4 + 3] * sc;
+            if (rope) {
+                const float2 r0 = a.table[(size_t)t * (D / 2) + d / 2];
+                const float2 r1 = a.table[(size_t)t * (D / 2) + d / 2 + 1];
+                const float y0 = x0 * r0.x + x1 * r0.y, y1 = -x0 * r0.y + x1 * r0.x;
+                const float y2 = x2 * r1.x + x3 * r1.y, y3 = -x2 * r1.y + x3 * r1.x;
+                x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+            }
+            dq[db][4 * q4] = x0; dq[db][4 * q4 + 1] = x1; dq[db][4 * q4 + 2] = x2; dq[db][4 * q4 + 3] = x3;
+        }
+    if (a.qkn.on) qk_norm_bwd_row<NDB>(dq, a.q, qoff, a.in_dt, a.rq[grp * (size_t)TG + R], a.qkn.gain, h);
+    TOUT* dqrow = (TOUT*)a.dq + qoff;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            store4(dqrow + 32 * db + 8 * q4 + 4 * h, dq[db][4 * q4], dq[db][4 * q4 + 1], dq[db][4 * q4 + 2],
+                   dq[db][4 * q4 + 3]);
+}
+
+// =====================================================================================
 // Launchers.
 // =====================================================================================
 // Records ev[2i] / ev[2i + 1] around launch i when events are given (null entries skipped).
@@ -1649,15 +1821,23 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(0));
     NE_TRY(m.before(1));
-    if constexpr (sizeof(OP) == 2)
-        hipLaunchKernelGGL((dkdv_kernel_h<D, TO>), dim3(((ba.T + 63) / 64 + 1) / 2 * ba.Hkv * ba.B), dim3(512), 0, s, ba);
+    if constexpr (sizeof(OP) == 2) {
+        const dim3 grid(((ba.T + 63) / 64 + 1) / 2 * ba.Hkv * ba.B);
+        if (ba.ds) hipLaunchKernelGGL((dkdv_kernel_h<D, TO, true>), grid, dim3(512), 0, s, ba);
+        else hipLaunchKernelGGL((dkdv_kernel_h<D, TO, false>), grid, dim3(512), 0, s, ba);
+    }
     else
         hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3(((ba.T + 63) / 64 + 1) / 2 * ba.Hkv * ba.B), dim3(512), 0, s, ba);
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(1));
     NE_TRY(m.before(2));
     if constexpr (sizeof(OP) == 2) {
-        if (ba.window < ba.T || ba.qkn.on)
+        if (ba.ds) {
+            const int nrt = (int)(((int64_t)ba.T * ba.G + 63) / 64);
+            hipLaunchKernelGGL((dq_ds_kernel<D, TO, NE_DQ_RT>), dim3((nrt + NE_DQ_RT - 1) / NE_DQ_RT * ba.Hkv * ba.B),
+                               dim3(128 * NE_DQ_RT), 0, s, ba);
+        }
+        else if (ba.window < ba.T || ba.qkn.on)
             hipLaunchKernelGGL((dq_kernel_h<D, TO, true>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
         else
             hipLaunchKernelGGL((dq_kernel_h<D, TO, false>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);

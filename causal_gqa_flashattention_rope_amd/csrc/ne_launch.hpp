@@ -5,6 +5,16 @@
 
 namespace ne {
 
+// Stored dS (16-bit backward): one tile of 64 flattened rows x 64 keys (8 KiB of fp16) for every
+// row tile rt < nrt = ceil(T G / 64) and key block kb < nkb = ceil(T / 64) with rt >= kb G -- the
+// row tiles the dK/dV pass visits for that key block -- stored by key block, then row tile.
+__host__ __device__ inline size_t ds_tiles_per_group(int nrt, int nkb, int G) {
+    return (size_t)nkb * nrt - (size_t)G * ((size_t)nkb * (nkb - 1) / 2);
+}
+__host__ __device__ inline size_t ds_tile_index(int kb, int rt, int nrt, int G) {
+    return (size_t)kb * nrt - (size_t)G * ((size_t)kb * (kb - 1) / 2) + (size_t)(rt - kb * G);
+}
+
 // QK norm: every (token, head) row x of q and k becomes gain * x / sqrt(mean(x^2) + eps).
 struct QkNorm {
     int on;
@@ -44,6 +54,8 @@ struct BwdArgs {
     const void* q; const void* k;                   // raw inputs (QK norm backward), dtype in_dt
     int in_dt;                                      // 0 f32, 1 bf16, 2 f16
     const float* rq; const float* rk;               // 1/rms of the q and k rows (QK norm)
+    void* ds;                                       // stored dS tiles (16-bit operands), or null:
+                                                    // dQ then recomputes S and dP
     int B, T, Hq, Hkv, G, nrb;
     int window;                                     // query t sees keys t - window + 1 .. t (1..T)
     double rope_base;

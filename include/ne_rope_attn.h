@@ -71,8 +71,13 @@ size_t ne_rope_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_
                                         ne_dtype_t in_dtype);
 
 /* Bytes of device workspace the backward needs (operand copies, the per-row
- * Delta = rowsum(dO * o), the log2-scaled lse, the per-row 1/rms of q and k used by the QK norm
- * and the cos/sin table). */
+ * Delta = rowsum(dO * o), the log2-scaled lse, the per-row 1/rms of q and k used by the QK norm,
+ * the cos/sin table and, for 16-bit inputs, the fp16 dS of every 64-row x 64-key tile of the
+ * causal band: 8 KiB per tile, about B * Hkv * T * T * (Hq / Hkv) bytes).  The dS buffer is used
+ * while it is at most 4 GiB, or at most the byte count in the environment variable
+ * NE_ROPE_ATTN_DS_MAX_BYTES (0: never); above it dQ recomputes S and dP and the workspace omits
+ * it.  The variable is read by this call and by ne_rope_attn_bwd*: keep it unchanged between
+ * them.  Results agree within rounding either way; each choice is bit-reproducible. */
 size_t ne_rope_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim,
                                         ne_dtype_t in_dtype);
 

@@ -49,8 +49,28 @@ def test_workspace_sizes(L):
     table = up(T * (D // 2) * 8)
     fwd = L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
     assert fwd == 2 * up(2 * nk) + table
+    # 16-bit backward: plus 8 KiB of stored dS per (64-row tile, 64-key block) pair that dK/dV
+    # visits, i.e. key block kb with row tiles kb G .. ceil(T G / 64) - 1, for every group
+    G = Hq // Hkv
+    nrt, nkb = -(-T * G // 64), -(-T // 64)
+    tiles = sum(1 for kb in range(nkb) for rt in range(nrt) if rt >= kb * G)
+    base = 2 * up(2 * nq) + 2 * up(2 * nk) + 3 * up(4 * B * T * Hq) + up(4 * B * T * Hkv) + table
     bwd = L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
-    assert bwd == 2 * up(2 * nq) + 2 * up(2 * nk) + 3 * up(4 * B * T * Hq) + up(4 * B * T * Hkv) + table
+    assert bwd == base + up(B * Hkv * tiles * 8192)
+    old = os.environ.get("NE_ROPE_ATTN_DS_MAX_BYTES")
+    try:  # the cap: 0 turns the stored dS off, a cap at its exact size keeps it
+        os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = "0"
+        assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16) == base
+        os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = str(B * Hkv * tiles * 8192)
+        assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16) == bwd
+    finally:
+        if old is None:
+            os.environ.pop("NE_ROPE_ATTN_DS_MAX_BYTES", None)
+        else:
+            os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = old
+    # the fp32 path recomputes in dQ and stores no dS
+    assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_F32) == \
+        2 * up(4 * nq) + 2 * up(4 * nk) + 3 * up(4 * B * T * Hq) + up(4 * B * T * Hkv) + table
     assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_F32) == 2 * up(4 * nk) + table
     # ragged T: the forward's transposed V' copy pads every row of keys to a multiple of 64
     Tr = 100

@@ -12,7 +12,9 @@ With 16-bit outputs the backward is handed the forward's rounded o, and Delta = 
 is computed from it (as the ABI states), so its reference is the oracle backward with Delta from
 that same o (oracle.bwd_given_o); with fp32 outputs the reference is the exact gradient.
 """
+import contextlib
 import math
+import os
 
 import numpy as np
 import pytest
@@ -97,6 +99,43 @@ def test_parity_small(shape, dtypes, base):
     q, k, v, dO = inputs.random_case(B, T, Hq, Hkv, D, seed=1000 + T, dtype={torch.bfloat16: "bf16",
                                      torch.float32: "f32", torch.float16: "f16"}[in_dt])
     parity(q, k, v, dO, base, out_dt, in_dt)
+
+
+@contextlib.contextmanager
+def recompute_dq():
+    """The 16-bit backward as it runs above its stored-dS cap: the dQ pass recomputes S and dP
+    instead of reading dS stored by the dK/dV pass (the cap is read at every call)."""
+    old = os.environ.get("NE_ROPE_ATTN_DS_MAX_BYTES")
+    os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = "0"
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("NE_ROPE_ATTN_DS_MAX_BYTES", None)
+        else:
+            os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = old
+
+
+@pytest.mark.parametrize("shape", SHAPES[2:])
+@pytest.mark.parametrize("in_dt", [torch.bfloat16, torch.float16])
+def test_parity_small_recompute_dq(shape, in_dt):
+    B, T, Hq, Hkv, D = shape
+    q, k, v, dO = inputs.random_case(B, T, Hq, Hkv, D, seed=1000 + T, dtype="bf16" if in_dt == torch.bfloat16 else "f16")
+    with recompute_dq():
+        parity(q, k, v, dO, 1.0e4, torch.float32, in_dt)
+
+
+def test_stored_ds_and_recompute_dq_agree():
+    """Storing dS leaves the dK/dV pass's arithmetic unchanged (o, lse, dk, dv bitwise equal); the two
+    dQ passes use the same dS up to where its fp16 rounding happens."""
+    w = inputs.WORKLOADS["wide_gqa_t2048_d128"]
+    q, k, v, dO = inputs.make_inputs(w, B=1)
+    stored = run_gpu(q, k, v, dO, w.rope_base, torch.float32)
+    with recompute_dq():
+        again = run_gpu(q, k, v, dO, w.rope_base, torch.float32)
+    for i in (0, 1, 3, 4):
+        assert torch.equal(stored[i], again[i])
+    assert float((stored[2] - again[2]).abs().max() / again[2].abs().max()) < 2e-3
 
 
 @pytest.mark.parametrize("in_dt,out_dt", [(torch.bfloat16, torch.bfloat16), (torch.float16, torch.float16)])

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from causal_gqa_flashattention_rope_amd import binding, inputs
-from tests.test_gpu_parity import DEV, check, f64, slice_group
+from tests.test_gpu_parity import DEV, check, f64, recompute_dq, slice_group
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,15 @@ def test_qk_norm_parity_small(shape, in_dt, window):
     B, T, Hq, Hkv, D = shape
     q, k, v, dO = inputs.random_case(B, T, Hq, Hkv, D, seed=3000 + T, dtype=_NAME[in_dt])
     ex_parity(q, k, v, dO, 1.0e4, window, QKN, torch.float32, in_dt)
+
+
+@pytest.mark.parametrize("shape", [(2, 100, 6, 2, 64), (2, 257, 3, 3, 128), (1, 200, 8, 2, 32)])
+@pytest.mark.parametrize("window", [0, 37])
+def test_qk_norm_parity_small_recompute_dq(shape, window):
+    B, T, Hq, Hkv, D = shape
+    q, k, v, dO = inputs.random_case(B, T, Hq, Hkv, D, seed=3000 + T, dtype="bf16")
+    with recompute_dq():
+        ex_parity(q, k, v, dO, 1.0e4, window, QKN, torch.float32, torch.bfloat16)
 
 
 @pytest.mark.parametrize("in_dt", [torch.bfloat16, torch.float16])

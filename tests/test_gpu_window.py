@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from causal_gqa_flashattention_rope_amd import binding, inputs
-from tests.test_gpu_parity import DEV, check, f64, slice_group
+from tests.test_gpu_parity import DEV, check, f64, recompute_dq, slice_group
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +61,15 @@ def test_window_parity_small(shape, window, in_dt):
     B, T, Hq, Hkv, D = shape
     q, k, v, dO = inputs.random_case(B, T, Hq, Hkv, D, seed=2000 + window, dtype=_NAME[in_dt])
     window_parity(q, k, v, dO, 1.0e4, window, torch.float32, in_dt)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("window", [5, 65])
+def test_window_parity_small_recompute_dq(shape, window):
+    B, T, Hq, Hkv, D = shape
+    q, k, v, dO = inputs.random_case(B, T, Hq, Hkv, D, seed=2000 + window, dtype="bf16")
+    with recompute_dq():
+        window_parity(q, k, v, dO, 1.0e4, window, torch.float32, torch.bfloat16)
 
 
 @pytest.mark.parametrize("in_dt", [torch.bfloat16, torch.float16])

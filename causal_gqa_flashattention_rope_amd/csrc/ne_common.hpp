@@ -134,6 +134,42 @@ __device__ __forceinline__ void qk_norm_bwd_row(floatx16 (&y)[NDB], const void* 
         }
 }
 
+// The same with the row's values already loaded: xr[db][q4] holds the 16-bit elements
+// d = 32 db + 8 q4 + 4 h .. + 3 (dt 1 bf16, 2 f16) as raw bits.
+template <int NDB>
+__device__ __forceinline__ void qk_norm_bwd_row_raw16(floatx16 (&y)[NDB], const uint2 (&xr)[NDB][4], int dt, float rho,
+                                                      float gain) {
+    constexpr int D = 32 * NDB;
+    auto x4 = [&](int db, int q4) {
+        if (dt == 1) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            const bf16x4 v = __builtin_bit_cast(bf16x4, xr[db][q4]);
+            return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+        }
+        const half4v v = __builtin_bit_cast(half4v, xr[db][q4]);
+        return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    };
+    float dot = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const floatx4 x = x4(db, q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dot += y[db][4 * q4 + e] * x[e];
+        }
+    dot = sum_halves(dot);
+    const float c1 = gain * rho, c2 = rho * rho * dot / (float)D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const floatx4 x = x4(db, q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[db][4 * q4 + e] = c1 * (y[db][4 * q4 + e] - x[e] * c2);
+        }
+}
+
 // ---- MFMA operand traits ----------------------------------------------------------------
 template <typename OP> struct Mma;
 

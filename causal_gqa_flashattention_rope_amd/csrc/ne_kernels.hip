@@ -1660,7 +1660,9 @@ __device__ __forceinline__ half8 ds_tr_frag(const _Float16* tile, int kk, int co
 #ifndef NE_DQ_RT
 #define NE_DQ_RT 4
 #endif
-template <int D, typename TOUT, int RT>
+// QKN: the QK norm is on (its backward in the epilogue, the raw q values fetched up front); a
+// separate instantiation, so that the plain kernel keeps its registers.
+template <int D, typename TOUT, int RT, bool QKN>
 __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
     using OP = _Float16;
     using M = Mma<OP>;
@@ -1717,6 +1719,24 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
     static_assert(8 % NW == 0, "whole 1 KiB blocks per wave");
     const int per_fill = lds_fill_count<OP, D, BN, NW>(w) + RT * (8 / NW);
 
+    // the row of this lane's position c (both lanes of the pair c, c + 32 agree)
+    const int R = 64 * rt + 32 * pb + 16 * (c >> 4) + 8 * ((c & 7) >> 2) + 4 * ((c >> 3) & 1) + (c & 3);
+    const bool rvalid = wact && R < TG;
+    const int t = R / G, hh = R - t * G, hq = hkv * G + hh;
+    const size_t qoff = (((size_t)b * T + t) * a.Hq + hq) * D;
+    // QK norm: the raw (16-bit) q values and 1/rms of the row, fetched now so that the epilogue
+    // does not wait for them
+    uint2 xr[NDB][4];
+    float rho = 0.f;
+    if (QKN && rvalid) {
+        rho = a.rq[grp * (size_t)TG + R];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                xr[db][q4] = *reinterpret_cast<const uint2*>((const char*)a.q + (qoff + 32 * db + 8 * q4 + 4 * h) * 2);
+    }
+
     floatx16 dq[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[db] = floatx16{};
@@ -1738,12 +1758,7 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
             for (int db = 0; db < NDB; ++db) dq[db] = M::mma(tr_frag_f16_sw<D>(Ks, ks, 32 * db), df[ks], dq[db]);
     }
 
-    if (!wact) return;
-    // the row of this lane's position c (both lanes of the pair c, c + 32 agree)
-    const int R = 64 * rt + 32 * pb + 16 * (c >> 4) + 8 * ((c & 7) >> 2) + 4 * ((c >> 3) & 1) + (c & 3);
-    if (R >= TG) return;
-    const int t = R / G, hh = R - t * G, hq = hkv * G + hh;
-    const size_t qoff = (((size_t)b * T + t) * a.Hq + hq) * D;
+    if (!rvalid) return;
     const float sc = a.scale;
     const bool rope = a.rope_base > 0.0;
     // dq = R^T (scale * dq'), in place
@@ -1763,7 +1778,7 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
             }
             dq[db][4 * q4] = x0; dq[db][4 * q4 + 1] = x1; dq[db][4 * q4 + 2] = x2; dq[db][4 * q4 + 3] = x3;
         }
-    if (a.qkn.on) qk_norm_bwd_row<NDB>(dq, a.q, qoff, a.in_dt, a.rq[grp * (size_t)TG + R], a.qkn.gain, h);
+    if constexpr (QKN) qk_norm_bwd_row_raw16<NDB>(dq, xr, a.in_dt, rho, a.qkn.gain);
     TOUT* dqrow = (TOUT*)a.dq + qoff;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -1834,8 +1849,9 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
     if constexpr (sizeof(OP) == 2) {
         if (ba.ds) {
             const int nrt = (int)(((int64_t)ba.T * ba.G + 63) / 64);
-            hipLaunchKernelGGL((dq_ds_kernel<D, TO, NE_DQ_RT>), dim3((nrt + NE_DQ_RT - 1) / NE_DQ_RT * ba.Hkv * ba.B),
-                               dim3(128 * NE_DQ_RT), 0, s, ba);
+            const dim3 grid((nrt + NE_DQ_RT - 1) / NE_DQ_RT * ba.Hkv * ba.B);
+            if (ba.qkn.on) hipLaunchKernelGGL((dq_ds_kernel<D, TO, NE_DQ_RT, true>), grid, dim3(128 * NE_DQ_RT), 0, s, ba);
+            else hipLaunchKernelGGL((dq_ds_kernel<D, TO, NE_DQ_RT, false>), grid, dim3(128 * NE_DQ_RT), 0, s, ba);
         }
         else if (ba.window < ba.T || ba.qkn.on)
             hipLaunchKernelGGL((dq_kernel_h<D, TO, true>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);

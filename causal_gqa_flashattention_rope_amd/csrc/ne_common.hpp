@@ -209,6 +209,17 @@ __device__ __forceinline__ half8 pack_frag_f16(const floatx16& acc, int c) {
     return f;
 }
 
+// A wave-uniform global pointer moved into SGPRs: readfirstlane of each 32-bit half.  The builtin
+// returns int, so each half is widened as unsigned (a sign-extended low half would corrupt the
+// upper half of the address).
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* sgpr_global_ptr(const void* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)v);
+    const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+    return (__attribute__((address_space(1))) T*)((hi << 32) | lo);
+}
+
 // ---- swizzled LDS tiles --------------------------------------------------------------------
 // A tile of rows x D elements is stored densely (row = D * sizeof(OP) bytes) with the 16-byte
 // chunks of row r permuted: chunk c lives in slot c ^ swz(r).  The permutations are chosen so
@@ -257,11 +268,6 @@ __device__ __forceinline__ void dma16(const void* g, unsigned lds_base) {
 // 32-bit byte offset (one VGPR instead of a 64-bit address per load).
 __device__ __forceinline__ void dma16_s(unsigned voff, const void* sbase, unsigned lds_base) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase),
-                 "s"(lds_base) : "memory", "m0");
-}
-// Same for data read exactly once (non-temporal: it should not displace reused data in the caches).
-__device__ __forceinline__ void dma16_s_nt(unsigned voff, const void* sbase, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" :: "v"(voff), "s"(sbase),
                  "s"(lds_base) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, unsigned lds_base) {

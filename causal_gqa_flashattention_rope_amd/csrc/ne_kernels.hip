@@ -1632,9 +1632,10 @@ void dq_kernel_h(BwdArgs a) {
 // through that layout as rows of keys and columns of positions p = 32 rh + 16 cc + 8 h + j, so
 // the contraction order of the two operands is the same j order; the epilogue maps positions
 // back to rows.  No S, P or dP is recomputed.
-// grid (ceil(nrt / RT) * B * Hkv), 128 RT threads: a block takes RT row tiles, wave w positions
-// 32 (w & 1) .. 32 (w & 1) + 31 of tile w >> 1 and all D columns of dQ; 64-key steps through a
-// 3-stage ring [K tile | the RT dS tiles] filled two steps ahead.
+// grid (ceil(nrt / 4) * B * Hkv), 512 threads: a block takes 4 row tiles, wave w positions
+// 32 (w & 1) .. 32 (w & 1) + 31 of tile w >> 1 and all D columns of dQ; per 64-key step the K tile
+// and the 4 dS tiles come global -> registers four steps ahead (non-temporal loads for dS, which is
+// read once), then registers -> a 2-stage LDS ring one step ahead.
 // =====================================================================================
 // B operand of dQ^T += K^T dS^T for k-step kk and positions col0 .. col0 + 31 of a stored tile
 // in LDS (the same lane pattern as tr_frag_f16_sw).
@@ -1666,9 +1667,13 @@ template <int D, typename TOUT, int RT, bool QKN>
 __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
     using OP = _Float16;
     using M = Mma<OP>;
-    constexpr int BN = 64, NW = 2 * RT, NST = 3, NDB = D / 32;
+    static_assert(RT == 4, "512 threads: one 16-byte unit of each dS tile per thread");
+    constexpr int BN = 64, NST = 2, NDB = D / 32;
+    constexpr int PF = QKN && D == 128 ? 3 : 4;          // register slots (the QK norm needs 32 VGPRs more)
     constexpr int KT = BN * D, DT = BN * 64;           // elements of a K tile and of a dS^T tile
-    constexpr int STG = KT + RT * DT;                  // elements per ring stage
+    constexpr int STG = KT + RT * DT;                  // elements per LDS stage
+    constexpr int CPR = D / 8, KCH = BN * CPR;         // 16-byte chunks per K row, per K tile
+    constexpr int KPT = (KCH + 511) / 512;             // K chunks per thread
     __shared__ __attribute__((aligned(1024))) OP lds[NST * STG];
 
     const int T = a.T, G = a.G, TG = T * G;
@@ -1697,27 +1702,48 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
     const bool wact = rt < nrt;
     const int wlo = wact ? kb_lo(rt) : 1, whi = wact ? kb_hi(rt) : 0;
 
-    const unsigned lds0 = lds_addr(lds);
-    // K tile kb and the stored dS tiles of row tiles rt0 .. rt0 + RT - 1 into stage st (a row
-    // tile without a stored tile for kb copies tile 0 of the group instead, which it does not use)
-    auto fill = [&](int kb, int st) {
-        const unsigned base = lds0 + (unsigned)(st * STG * 2);
-        lds_fill_at<OP, D, BN, NW>(base, kg, kb * BN, T);
+    // Step kb's K tile and RT dS tiles travel global -> registers PF steps ahead (slot
+    // (kb - lo) % PF), then registers -> LDS stage (kb - lo) & 1 one step ahead.  Every step issues
+    // the same loads (past hi, or for a row tile without a stored tile, from a valid tile that is
+    // not used), so the waits before each register -> LDS copy keep the later steps' loads in flight.
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+    u32x4 kr[PF][KPT], dr[PF][RT];
+    int rlo[RT], rhi[RT];                              // key blocks of each row tile (uniform)
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int rtx = rt0 + r;
+        rlo[r] = __builtin_amdgcn_readfirstlane(rtx < nrt ? kb_lo(rtx) : 1);
+        rhi[r] = __builtin_amdgcn_readfirstlane(rtx < nrt ? kb_hi(rtx) : 0);
+    }
+    auto issue = [&](int kb, auto SLOT) {
+        constexpr int sl = decltype(SLOT)::value;
+        const int kc = min(kb, hi);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int q = (tid + 512 * i) % KCH, r = q / CPR;
+            kr[sl][i] = *reinterpret_cast<const u32x4*>(kg + (size_t)min(kc * BN + r, T - 1) * D + (q % CPR) * 8);
+        }
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
-            const int rtx = rt0 + r;
-            const bool ok = rtx < nrt && kb >= kb_lo(rtx) && kb <= kb_hi(rtx);
-            const OP* src = dsg + (ok ? ds_tile_index(kb, rtx, nrt, G) : 0) * 4096;
-#pragma unroll
-            for (int i = 0; i < 8 / NW; ++i) {
-                const int j = w + NW * i;                    // 1 KiB block j of the tile
-                dma16_s_nt((unsigned)(1024 * j + 16 * l), src,
-                        __builtin_amdgcn_readfirstlane(base + (unsigned)((KT + r * DT) * 2) + 1024u * (unsigned)j));
-            }
+            const bool ok = kc >= rlo[r] && kc <= rhi[r];
+            gu32x4* src = sgpr_global_ptr<const u32x4>(dsg + (ok ? ds_tile_index(kc, rt0 + r, nrt, G) : 0) * 4096);
+            dr[sl][r] = __builtin_nontemporal_load(src + tid);
         }
     };
-    static_assert(8 % NW == 0, "whole 1 KiB blocks per wave");
-    const int per_fill = lds_fill_count<OP, D, BN, NW>(w) + RT * (8 / NW);
+    auto commit = [&](int kb, auto SLOT) {
+        constexpr int sl = decltype(SLOT)::value;
+        if (kb > hi) return;
+        char* st = reinterpret_cast<char*>(lds + ((kb - lo) & 1) * STG);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int q = tid + 512 * i, r = q / CPR;
+            if (KCH % 512 == 0 || q < KCH)
+                *reinterpret_cast<u32x4*>(st + r * (D * 2) + (((q % CPR) ^ Tile<OP, D>::swz(r)) << 4)) = kr[sl][i];
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) *reinterpret_cast<u32x4*>(st + (KT + r * DT) * 2 + tid * 16) = dr[sl][r];
+    };
 
     // the row of this lane's position c (both lanes of the pair c, c + 32 agree)
     const int R = 64 * rt + 32 * pb + 16 * (c >> 4) + 8 * ((c & 7) >> 2) + 4 * ((c >> 3) & 1) + (c & 3);
@@ -1740,14 +1766,8 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
     floatx16 dq[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[db] = floatx16{};
-    if (lo <= hi) fill(lo, 0);    // (never empty: every row tile sees its own diagonal block)
-    if (lo + 1 <= hi) fill(lo + 1, 1);
-    for (int kb = lo; kb <= hi; ++kb) {
-        const int st = (kb - lo) % NST;
-        lds_fill_wait_keep(kb + 1 <= hi ? per_fill : 0);
-        if (kb + 2 <= hi) fill(kb + 2, (kb + 2 - lo) % NST);
-        if (kb < wlo || kb > whi) continue;
-        const _Float16* Ks = lds + st * STG;
+    auto compute = [&](int kb) {
+        const _Float16* Ks = lds + ((kb - lo) & 1) * STG;
         const _Float16* Ds = Ks + KT + (w >> 1) * DT;
         half8 df[4];
 #pragma unroll
@@ -1756,6 +1776,31 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) dq[db] = M::mma(tr_frag_f16_sw<D>(Ks, ks, 32 * db), df[ks], dq[db]);
+    };
+    auto body = [&](int kb, auto SLOT) {
+        constexpr int sl = decltype(SLOT)::value;
+        commit(kb + 1, IC<(sl + 1) % PF>{});
+        issue(kb + PF, SLOT);
+        if (kb >= wlo && kb <= whi) compute(kb);
+        __syncthreads();
+    };
+    // (lo <= hi always: every row tile sees its own diagonal block)
+    issue(lo, IC<0>{});
+    issue(lo + 1, IC<1>{});
+    issue(lo + 2, IC<2>{});
+    if constexpr (PF == 4) issue(lo + 3, IC<3>{});
+    commit(lo, IC<0>{});
+    __syncthreads();
+    for (int kb = lo; kb <= hi; kb += PF) {
+        body(kb, IC<0>{});
+        if (kb + 1 > hi) break;
+        body(kb + 1, IC<1>{});
+        if (kb + 2 > hi) break;
+        body(kb + 2, IC<2>{});
+        if constexpr (PF == 4) {
+            if (kb + 3 > hi) break;
+            body(kb + 3, IC<3>{});
+        }
     }
 
     if (!rvalid) return;

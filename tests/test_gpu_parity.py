@@ -240,6 +240,27 @@ def test_backward_is_bitwise_deterministic():
             assert torch.equal(a, b)
 
 
+def test_backward_is_the_same_wherever_the_workspace_lies():
+    """The stored-dS tile addresses are moved into scalar registers as two 32-bit halves; a workspace
+    whose address has the low half at or above 2^31 (where a sign-extended half would corrupt the
+    address) gives the same bits as one with the low half below 2^31."""
+    B, T, Hq, Hkv, D = 1, 300, 6, 2, 128
+    q, k, v, dO = (t.to(DEV) for t in inputs.random_case(B, T, Hq, Hkv, D, seed=31, dtype="bf16"))
+    o, lse = binding.ne_rope_attn_fwd(q, k, v, 1e4)
+    n = binding.bwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype)
+    buf = torch.empty((1 << 32) + n + 512, dtype=torch.uint8, device=DEV)
+    base = buf.data_ptr()
+    outs = []
+    for start in (0, 1 << 31):   # the low 32 address bits of the workspace
+        off = ((start - (base & 0xFFFFFFFF)) % (1 << 32) + 255) // 256 * 256
+        low = (base + off) & 0xFFFFFFFF
+        assert (low >= 1 << 31) == (start > 0) and (low + n < 1 << 32)
+        outs.append([t.clone() for t in binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, 1e4, workspace=buf[off:off + n])])
+    del buf
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_gqa_matches_replicated_kv_mha():
     q, k, v, dO = inputs.random_case(1, 130, 8, 2, 64, seed=9, dtype="bf16")
     G = 4

@@ -30,7 +30,7 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t qh, kh, vh, dOh, delta, lse2, rq, rk, table, ds, total;
-    bool has_ds;
+    int ds_groups;  // groups per stored-dS batch (0: none)
 };
 
 bool dtype_ok(ne_dtype_t in, ne_dtype_t out) {
@@ -59,22 +59,23 @@ ne_status_t check_shape(int B, int T, int Hq, int Hkv, int D, int esz) {
     return NE_OK;
 }
 
-// Bytes of stored dS for the 16-bit backward: 8 KiB per tile of 64 flattened rows x 64 keys that
-// the dK/dV pass visits (ne::ds_tiles_per_group per (batch, KV head) group).
-size_t ds_bytes(int B, int T, int Hq, int Hkv) {
+// Bytes of stored dS of one (batch, KV head) group for the 16-bit backward: 8 KiB per tile of 64
+// flattened rows x 64 keys that the dK/dV pass visits (ne::ds_tiles_per_group).
+size_t ds_group_bytes(int T, int Hq, int Hkv) {
     const int G = Hq / Hkv;
     const int nrt = (int)(((int64_t)T * G + 63) / 64), nkb = (T + 63) / 64;
-    return (size_t)B * Hkv * ne::ds_tiles_per_group(nrt, nkb, G) * 8192;
+    return ne::ds_tiles_per_group(nrt, nkb, G) * 8192;
 }
 
-// The 16-bit backward stores dS for the dQ pass when that buffer is at most 4 GiB, or at most the
-// byte count in the environment variable NE_ROPE_ATTN_DS_MAX_BYTES (read at every call; 0 turns
-// it off); otherwise dQ recomputes S and dP.
-bool use_stored_ds(int B, int T, int Hq, int Hkv, ne_dtype_t in) {
-    if (in == NE_F32) return false;
+// Groups whose dS the 16-bit backward's buffer holds at once: as many as fit 4 GiB, or the byte
+// count in the environment variable NE_ROPE_ATTN_DS_MAX_BYTES (read at every call; 0 turns the
+// stored dS off), at most B * Hkv; the dK/dV and dQ passes run once per batch of that many groups.
+// 0 (fp32 path, or a single group's dS above the cap): dQ recomputes S and dP instead.
+int ds_batch_groups(int B, int T, int Hq, int Hkv, ne_dtype_t in) {
+    if (in == NE_F32) return 0;
     size_t cap = (size_t)4 << 30;
     if (const char* e = std::getenv("NE_ROPE_ATTN_DS_MAX_BYTES"); e && *e) cap = (size_t)std::strtoull(e, nullptr, 10);
-    return ds_bytes(B, T, Hq, Hkv) <= cap;
+    return (int)std::min<size_t>((size_t)B * Hkv, cap / ds_group_bytes(T, Hq, Hkv));
 }
 
 Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, ne_dtype_t in) {
@@ -95,8 +96,8 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, ne_dtype_t in) {
         L.rk = off; off += up((size_t)B * T * Hkv * 4);
     }
     L.table = off; off += up((size_t)T * (D / 2) * 8);
-    L.has_ds = bwd && use_stored_ds(B, T, Hq, Hkv, in);
-    if (L.has_ds) { L.ds = off; off += up(ds_bytes(B, T, Hq, Hkv)); }
+    L.ds_groups = bwd ? ds_batch_groups(B, T, Hq, Hkv, in) : 0;
+    if (L.ds_groups > 0) { L.ds = off; off += up((size_t)L.ds_groups * ds_group_bytes(T, Hq, Hkv)); }
     L.total = off;
     return L;
 }
@@ -241,7 +242,10 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     ba.qkn = qkn;
     ba.q = q; ba.k = k; ba.in_dt = (int)in_dtype;
     ba.rq = pa.rq; ba.rk = pa.rk;
-    ba.ds = L.has_ds ? ws + L.ds : nullptr;
+    ba.ds = L.ds_groups > 0 ? ws + L.ds : nullptr;
+    ba.ds_groups = L.ds_groups;
+    ba.grp0 = 0;
+    ba.ngrp = B * Hkv;
     ba.nrb = (int)(((int64_t)T * G + 127) / 128);
     ba.rope_base = rope_base;
     ba.scale = (float)(1.0 / std::sqrt((double)head_dim));

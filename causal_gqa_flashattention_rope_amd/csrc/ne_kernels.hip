@@ -1074,14 +1074,15 @@ void dkdv_kernel_h(BwdArgs a) {
     const int T = a.T, G = a.G, TG = T * G;
     const int nkb = (T + BN - 1) / BN;
     const int npair = (nkb + 1) / 2;
-    const Work wk = map_block(npair, a.B * a.Hkv, false);
-    const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
+    const Work wk = map_block(npair, a.ngrp, false);
+    const int gg = a.grp0 + wk.grp;                   // the (batch, KV head) group
+    const int hkv = gg % a.Hkv, b = gg / a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
     // waves w and w + 4 (same row half and key sub-block, the two roles) share a SIMD
     const int rh = w & 1, kq = (w >> 1) & 1, role = w >> 2;
     const int per_fill = 2 * lds_fill_count<OP, D, BMR, NW>(w) + (w < 2 ? 1 : 0);  // loads per fill
 
-    const size_t grp = (size_t)wk.grp;
+    const size_t grp = (size_t)gg;
     const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
     const OP* og = (const OP*)a.dOh + grp * (size_t)TG * D;
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
@@ -1096,7 +1097,7 @@ void dkdv_kernel_h(BwdArgs a) {
     half8* dsg = nullptr;
     int ds0 = 0, ds1 = 0;
     if constexpr (DS) {
-        dsg = (half8*)a.ds + grp * ds_tiles_per_group((TG + 63) / 64, (T + 63) / 64, G) * 512 + (kq * 2 + rh) * 128;
+        dsg = (half8*)a.ds + (size_t)wk.grp * ds_tiles_per_group((TG + 63) / 64, (T + 63) / 64, G) * 512 + (kq * 2 + rh) * 128;
         ds0 = 32 * h + (c ^ (4 * h));
         ds1 = 64 + 32 * h + (c ^ (4 * h + 8));
     }
@@ -1678,14 +1679,15 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
 
     const int T = a.T, G = a.G, TG = T * G;
     const int nrt = (TG + 63) / 64, nkb = (T + 63) / 64;
-    const Work wk = map_block((nrt + RT - 1) / RT, a.B * a.Hkv, true);
-    const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
+    const Work wk = map_block((nrt + RT - 1) / RT, a.ngrp, true);
+    const int gg = a.grp0 + wk.grp;                   // the (batch, KV head) group
+    const int hkv = gg % a.Hkv, b = gg / a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
     const int rt0 = RT * wk.blk;
     const int W = a.window;
-    const size_t grp = (size_t)wk.grp;
+    const size_t grp = (size_t)gg;
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
-    const OP* dsg = (const OP*)a.ds + grp * ds_tiles_per_group(nrt, nkb, G) * 4096;
+    const OP* dsg = (const OP*)a.ds + (size_t)wk.grp * ds_tiles_per_group(nrt, nkb, G) * 4096;
 
     // key blocks with a stored tile for row tile rt: kb G <= rt, and the rows that see some key
     // of the block extend past 64 rt: min(T, 64 kb + 63 + W) G > 64 rt
@@ -1880,31 +1882,48 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
     hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, true>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(0));
-    NE_TRY(m.before(1));
+    const int ngroups = ba.B * ba.Hkv, npair = ((ba.T + 63) / 64 + 1) / 2;
     if constexpr (sizeof(OP) == 2) {
-        const dim3 grid(((ba.T + 63) / 64 + 1) / 2 * ba.Hkv * ba.B);
-        if (ba.ds) hipLaunchKernelGGL((dkdv_kernel_h<D, TO, true>), grid, dim3(512), 0, s, ba);
-        else hipLaunchKernelGGL((dkdv_kernel_h<D, TO, false>), grid, dim3(512), 0, s, ba);
+        if (ba.ds) {
+            // stored dS: dK/dV, then dQ, for each batch of ds_groups groups (a single batch unless the
+            // dS of every group would exceed the buffer); with several batches the second marked
+            // interval covers all but the last dQ launch as well
+            const int nrt = (int)(((int64_t)ba.T * ba.G + 63) / 64);
+            NE_TRY(m.before(1));
+            for (int g0 = 0; g0 < ngroups; g0 += ba.ds_groups) {
+                BwdArgs bb = ba;
+                bb.grp0 = g0;
+                bb.ngrp = min(ba.ds_groups, ngroups - g0);
+                hipLaunchKernelGGL((dkdv_kernel_h<D, TO, true>), dim3(npair * bb.ngrp), dim3(512), 0, s, bb);
+                NE_TRY(hipGetLastError());
+                if (g0 + bb.ngrp >= ngroups) {
+                    NE_TRY(m.after(1));
+                    NE_TRY(m.before(2));
+                }
+                const dim3 grid((nrt + NE_DQ_RT - 1) / NE_DQ_RT * bb.ngrp);
+                if (ba.qkn.on) hipLaunchKernelGGL((dq_ds_kernel<D, TO, NE_DQ_RT, true>), grid, dim3(128 * NE_DQ_RT), 0, s, bb);
+                else hipLaunchKernelGGL((dq_ds_kernel<D, TO, NE_DQ_RT, false>), grid, dim3(128 * NE_DQ_RT), 0, s, bb);
+                NE_TRY(hipGetLastError());
+            }
+            return m.after(2);
+        }
     }
+    NE_TRY(m.before(1));
+    if constexpr (sizeof(OP) == 2)
+        hipLaunchKernelGGL((dkdv_kernel_h<D, TO, false>), dim3(npair * ngroups), dim3(512), 0, s, ba);
     else
-        hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3(((ba.T + 63) / 64 + 1) / 2 * ba.Hkv * ba.B), dim3(512), 0, s, ba);
+        hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3(npair * ngroups), dim3(512), 0, s, ba);
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(1));
     NE_TRY(m.before(2));
     if constexpr (sizeof(OP) == 2) {
-        if (ba.ds) {
-            const int nrt = (int)(((int64_t)ba.T * ba.G + 63) / 64);
-            const dim3 grid((nrt + NE_DQ_RT - 1) / NE_DQ_RT * ba.Hkv * ba.B);
-            if (ba.qkn.on) hipLaunchKernelGGL((dq_ds_kernel<D, TO, NE_DQ_RT, true>), grid, dim3(128 * NE_DQ_RT), 0, s, ba);
-            else hipLaunchKernelGGL((dq_ds_kernel<D, TO, NE_DQ_RT, false>), grid, dim3(128 * NE_DQ_RT), 0, s, ba);
-        }
-        else if (ba.window < ba.T || ba.qkn.on)
-            hipLaunchKernelGGL((dq_kernel_h<D, TO, true>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
+        if (ba.window < ba.T || ba.qkn.on)
+            hipLaunchKernelGGL((dq_kernel_h<D, TO, true>), dim3(ba.nrb * ngroups), dim3(256), 0, s, ba);
         else
-            hipLaunchKernelGGL((dq_kernel_h<D, TO, false>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
+            hipLaunchKernelGGL((dq_kernel_h<D, TO, false>), dim3(ba.nrb * ngroups), dim3(256), 0, s, ba);
     }
     else
-        hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb * ba.Hkv * ba.B), dim3(256), 0, s, ba);
+        hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb * ngroups), dim3(256), 0, s, ba);
     NE_TRY(hipGetLastError());
     return m.after(2);
 }

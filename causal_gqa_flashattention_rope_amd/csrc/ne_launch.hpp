@@ -56,6 +56,9 @@ struct BwdArgs {
     const float* rq; const float* rk;               // 1/rms of the q and k rows (QK norm)
     void* ds;                                       // stored dS tiles (16-bit operands), or null:
                                                     // dQ then recomputes S and dP
+    int ds_groups;                                  // groups whose dS the buffer holds at once
+    int grp0, ngrp;                                 // the (batch, KV head) groups of one launch of
+                                                    // the stored-dS pair (else 0 and B * Hkv)
     int B, T, Hq, Hkv, G, nrb;
     int window;                                     // query t sees keys t - window + 1 .. t (1..T)
     double rope_base;

@@ -73,11 +73,13 @@ size_t ne_rope_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_
 /* Bytes of device workspace the backward needs (operand copies, the per-row
  * Delta = rowsum(dO * o), the log2-scaled lse, the per-row 1/rms of q and k used by the QK norm,
  * the cos/sin table and, for 16-bit inputs, the fp16 dS of every 64-row x 64-key tile of the
- * causal band: 8 KiB per tile, about B * Hkv * T * T * (Hq / Hkv) bytes).  The dS buffer is used
- * while it is at most 4 GiB, or at most the byte count in the environment variable
- * NE_ROPE_ATTN_DS_MAX_BYTES (0: never); above it dQ recomputes S and dP and the workspace omits
- * it.  The variable is read by this call and by ne_rope_attn_bwd*: keep it unchanged between
- * them.  Results agree within rounding either way; each choice is bit-reproducible. */
+ * causal band: 8 KiB per tile, about T * T * (Hq / Hkv) bytes per (batch, KV head) group).  The
+ * dS buffer holds as many groups as fit 4 GiB, or the byte count in the environment variable
+ * NE_ROPE_ATTN_DS_MAX_BYTES (0: none), and the dK/dV and dQ passes run once per batch of that many
+ * groups; when not even one group fits, dQ recomputes S and dP and the workspace omits the
+ * buffer.  The variable is read by this call and by ne_rope_attn_bwd*: keep it unchanged between
+ * them.  Results agree within rounding either way, and are bitwise the same for every batch size;
+ * each choice is bit-reproducible. */
 size_t ne_rope_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim,
                                         ne_dtype_t in_dtype);
 
@@ -104,7 +106,9 @@ ne_status_t ne_rope_attn_bwd(const void* q, const void* k, const void* v,
 /* Instrumented variants for measurement: identical work, plus hipEvent_t records on `stream`
  * around each kernel launch -- events[2i] before and events[2i+1] after launch i.  Forward:
  * i = 0 operand preparation, 1 attention (an array of 4).  Backward: i = 0 preparation with
- * Delta, 1 dK/dV, 2 dQ (an array of 6).  The array must be non-null; a null entry skips that
+ * Delta, 1 dK/dV, 2 dQ (an array of 6; when the stored dS is processed in several group batches,
+ * interval 1 spans every batch's dK/dV and all but the last dQ, interval 2 the last dQ).  The
+ * array must be non-null; a null entry skips that
  * record (a record costs microseconds of stream time, so a measurement brackets only the
  * launches it needs).  The events are created and owned by the caller. */
 ne_status_t ne_rope_attn_fwd_timed(const void* q, const void* k, const void* v,

@@ -58,11 +58,17 @@ def test_workspace_sizes(L):
     bwd = L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
     assert bwd == base + up(B * Hkv * tiles * 8192)
     old = os.environ.get("NE_ROPE_ATTN_DS_MAX_BYTES")
-    try:  # the cap: 0 turns the stored dS off, a cap at its exact size keeps it
+    try:  # the cap: the buffer holds the dS of as many whole groups as fit (0: none)
         os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = "0"
         assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16) == base
         os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = str(B * Hkv * tiles * 8192)
         assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16) == bwd
+        os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = str(tiles * 8192 - 1)
+        assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16) == base
+        for groups in (1, 3, 5):
+            os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = str(groups * tiles * 8192 + 4095)
+            assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16) == \
+                base + up(groups * tiles * 8192)
     finally:
         if old is None:
             os.environ.pop("NE_ROPE_ATTN_DS_MAX_BYTES", None)

@@ -102,11 +102,12 @@ def test_parity_small(shape, dtypes, base):
 
 
 @contextlib.contextmanager
-def recompute_dq():
-    """The 16-bit backward as it runs above its stored-dS cap: the dQ pass recomputes S and dP
-    instead of reading dS stored by the dK/dV pass (the cap is read at every call)."""
+def ds_cap(nbytes):
+    """Cap of the 16-bit backward's stored-dS buffer (read at every call): it holds the dS of as many
+    (batch, KV head) groups as fit, and the dK/dV and dQ passes run once per such batch; below one
+    group the dQ pass recomputes S and dP instead."""
     old = os.environ.get("NE_ROPE_ATTN_DS_MAX_BYTES")
-    os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = "0"
+    os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = str(int(nbytes))
     try:
         yield
     finally:
@@ -114,6 +115,29 @@ def recompute_dq():
             os.environ.pop("NE_ROPE_ATTN_DS_MAX_BYTES", None)
         else:
             os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = old
+
+
+def recompute_dq():
+    """The 16-bit backward as it runs when one group's dS exceeds the cap."""
+    return ds_cap(0)
+
+
+def ds_group_bytes(T, G):
+    nrt, nkb = -(-T * G // 64), -(-T // 64)
+    return sum(1 for kb in range(nkb) for rt in range(nrt) if rt >= kb * G) * 8192
+
+
+def test_stored_ds_in_group_batches_is_bitwise_the_single_batch_run():
+    """A dS buffer smaller than every group's dS: the passes run per batch of groups (one group at a
+    time; 3 + 1), with the same bits as the single batch."""
+    w = inputs.WORKLOADS["wide_gqa_t2048_d128"]
+    q, k, v, dO = inputs.make_inputs(w, B=1)      # 4 groups
+    one = run_gpu(q, k, v, dO, w.rope_base, torch.float32)
+    for groups in (1, 3):
+        with ds_cap(groups * ds_group_bytes(w.T, w.G)):
+            again = run_gpu(q, k, v, dO, w.rope_base, torch.float32)
+        for a, b in zip(one, again):
+            assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("shape", SHAPES[2:])

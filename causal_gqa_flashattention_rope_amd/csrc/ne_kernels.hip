@@ -1635,7 +1635,7 @@ void dq_kernel_h(BwdArgs a) {
 // back to rows.  No S, P or dP is recomputed.
 // grid (ceil(nrt / 4) * B * Hkv), 512 threads: a block takes 4 row tiles, wave w positions
 // 32 (w & 1) .. 32 (w & 1) + 31 of tile w >> 1 and all D columns of dQ; per 64-key step the K tile
-// and the 4 dS tiles come global -> registers four steps ahead (non-temporal loads for dS, which is
+// and the 4 dS tiles come global -> registers two steps ahead (non-temporal loads for dS, which is
 // read once), then registers -> a 2-stage LDS ring one step ahead.
 // =====================================================================================
 // B operand of dQ^T += K^T dS^T for k-step kk and positions col0 .. col0 + 31 of a stored tile
@@ -1670,7 +1670,7 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
     using M = Mma<OP>;
     static_assert(RT == 4, "512 threads: one 16-byte unit of each dS tile per thread");
     constexpr int BN = 64, NST = 2, NDB = D / 32;
-    constexpr int PF = QKN && D == 128 ? 3 : 4;          // register slots (the QK norm needs 32 VGPRs more)
+    constexpr int PF = 2;                              // register slots (two: 54 us; four: 56 us)
     constexpr int KT = BN * D, DT = BN * 64;           // elements of a K tile and of a dS^T tile
     constexpr int STG = KT + RT * DT;                  // elements per LDS stage
     constexpr int CPR = D / 8, KCH = BN * CPR;         // 16-byte chunks per K row, per K tile
@@ -1705,7 +1705,8 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
     const int wlo = wact ? kb_lo(rt) : 1, whi = wact ? kb_hi(rt) : 0;
 
     // Step kb's K tile and RT dS tiles travel global -> registers PF steps ahead (slot
-    // (kb - lo) % PF), then registers -> LDS stage (kb - lo) & 1 one step ahead.  Every step issues
+    // (kb - lo) % PF), then registers -> LDS stage (kb - lo) & 1 one step ahead (with the LDS
+    // stage, three steps of loads are in flight; deeper register rings measured no faster).  Every step issues
     // the same loads (past hi, or for a row tile without a stored tile, from a valid tile that is
     // not used), so the waits before each register -> LDS copy keep the later steps' loads in flight.
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -1789,20 +1790,12 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
     // (lo <= hi always: every row tile sees its own diagonal block)
     issue(lo, IC<0>{});
     issue(lo + 1, IC<1>{});
-    issue(lo + 2, IC<2>{});
-    if constexpr (PF == 4) issue(lo + 3, IC<3>{});
     commit(lo, IC<0>{});
     __syncthreads();
     for (int kb = lo; kb <= hi; kb += PF) {
         body(kb, IC<0>{});
         if (kb + 1 > hi) break;
         body(kb + 1, IC<1>{});
-        if (kb + 2 > hi) break;
-        body(kb + 2, IC<2>{});
-        if constexpr (PF == 4) {
-            if (kb + 3 > hi) break;
-            body(kb + 3, IC<3>{});
-        }
     }
 
     if (!rvalid) return;

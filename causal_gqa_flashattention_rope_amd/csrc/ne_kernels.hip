@@ -18,9 +18,11 @@
 //  backward: prep  -> q~, k', v', dO' and Delta = rowsum(dO * o), lse2 = lse * log2 e, cos/sin table
 //            dkdv  -> per pair of mirrored 64-key blocks of one KV head: dK, dV accumulated over
 //                     every query row of the group (all G heads), written once; inverse RoPE in
-//                     the epilogue.
-//            dq    -> per 128 flattened rows: dQ accumulated over the visible key tiles, written
-//                     once; inverse RoPE in the epilogue.  No atomics: bit-reproducible.
+//                     the epilogue; the fp16 dS of every 64 x 64 tile stored in the workspace.
+//            dq    -> per 256 flattened rows: dQ = dS K over the stored tiles of the visible key
+//                     blocks, written once; inverse RoPE in the epilogue.  (Per batch of (batch,
+//                     KV head) groups whose dS fits the buffer; when one group's dS does not, dq
+//                     recomputes S and dP per 128 rows instead.)  No atomics: bit-reproducible.
 //
 // Flattened rows: within a (batch, KV head) group the G query heads are interleaved with the
 // tokens, row R = t * G + hh (hh = head within the group).  In the [B][T][Hq][D] input these

@@ -1,13 +1,15 @@
 // ne_decode.hip -- attention of a few new tokens against a key/value cache (decode and chunked
 // prefill), 16-bit operands, gfx950.
 //
-// The cache (one caller-owned buffer, ne_kv_cache_bytes) holds, per (batch, KV head) group g:
-//   K'  [g][Tcap][D]  fp16(R_p(k)): each key rotated once, at its own absolute position p
-//   V'^T[g][D][Tcap]  fp16(v) transposed, the keys of every aligned group of 16 in the order
-//                     0-3, 8-11, 4-7, 12-15 (vt_key_of_pos)
-// so that, for a 32-key tile, both MFMA operands of a lane are single 16-byte global loads:
-// K' rows for S^T = K' Q~^T (lane c: key c, 8 consecutive d) and V'^T rows for O^T = V'^T P^T
-// (lane c: d = c, 8 consecutive keys in the order the S^T accumulator hands P over).
+// The cache (one caller-owned buffer, ne_kv_cache_bytes) holds, per (batch, KV head) group g, its
+// Tcap / 32 tiles of 32 keys, each 128 D bytes in the order one wave loads them (CacheTile):
+//   K' block: for load ks < D / 16 and lane l < 64, 16 bytes: fp16(R_p(k)) of key l % 32 of the
+//             tile, elements d = 16 ks + 8 (l / 32) .. + 7 (each key rotated once, at its own
+//             absolute position p): the A operand of S^T = K' Q~^T for k-step ks;
+//   V' block: for load (kk < 2, db < D / 32) and lane l, 16 bytes: fp16(v) at d = 32 db + l % 32 of
+//             the 8 keys 16 kk + vt_key_of_pos(8 (l / 32) + j), j < 8: the A operand of
+//             O^T += V'^T P^T for k-step kk, in the order the S^T accumulator hands P over.
+// Every 16-byte load of the decode kernel is thus one lane's part of a contiguous 1 KiB.
 //
 // Decode is bound by reading the cache, which no two workgroups share, so the kernels stream it
 // from HBM straight into registers (no LDS staging) and spread every group's keys over many
@@ -36,6 +38,19 @@ __device__ __forceinline__ float2 rope_cs(int p, double theta) {
     return make_float2(c, s);
 }
 
+// Offsets (in fp16 elements) inside a group's cache of the 16-byte unit a lane loads.
+template <int D>
+struct CacheTile {
+    static constexpr int KS = D / 16, NDB = D / 32;
+    static constexpr size_t ELEMS = (size_t)64 * D;    // elements per 32-key tile (K' and V' blocks)
+    __device__ __forceinline__ static size_t k_unit(int tile, int ks, int lane) {
+        return tile * ELEMS + (size_t)(ks * 64 + lane) * 8;
+    }
+    __device__ __forceinline__ static size_t v_unit(int tile, int kk, int db, int lane) {
+        return tile * ELEMS + (size_t)32 * D + (size_t)((kk * NDB + db) * 64 + lane) * 8;
+    }
+};
+
 template <typename TI>
 __device__ __forceinline__ void load8_in(const TI* p, float (&x)[8]) {
     typedef TI v8 __attribute__((ext_vector_type(8)));
@@ -55,7 +70,7 @@ __device__ __forceinline__ int cache_len(const int* lens, int b, int n, int Tcap
 // Append: tokens i < Tn of k_new / v_new go to positions len_b + i of their group.
 // grid (ceil(Tn / 16), B * Hkv), 256 threads.  Keys: one thread per (token, 8-element chunk),
 // rotated in fp32 with the cos/sin of the absolute position, one 16-byte store.  Values: staged
-// through LDS and written transposed, 16 consecutive tokens of one d per 16 lanes.
+// through LDS and written in the tile order, one fp16 element per thread.
 // =====================================================================================
 template <typename TI, int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
@@ -65,8 +80,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     const int t0 = blockIdx.x * TB, Tn = a.Tn, Tcap = a.Tcap;
     const int len = cache_len(a.lens, b, Tn, Tcap);
     const bool rope = a.rope_base > 0.0;
-    _Float16* kc = (_Float16*)a.cache + (size_t)grp * Tcap * D;
-    _Float16* vtc = (_Float16*)a.cache + (size_t)a.B * a.Hkv * Tcap * D + (size_t)grp * D * Tcap;
+    using CT = CacheTile<D>;
+    _Float16* gc = (_Float16*)a.cache + (size_t)grp * Tcap * D * 2;   // this group's tiles
     for (int idx = threadIdx.x; idx < TB * CPR; idx += 256) {
         const int tl = idx / CPR, chunk = idx % CPR, t = t0 + tl;
         const size_t in_off = (((size_t)b * Tn + min(t, Tn - 1)) * a.Hkv + hkv) * D + chunk * 8;
@@ -95,7 +110,8 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
         half8 out;
 #pragma unroll
         for (int e = 0; e < 8; ++e) out[e] = (_Float16)x[e];
-        *reinterpret_cast<half8*>(kc + (size_t)p * D + chunk * 8) = out;
+        // elements 8 chunk .. 8 chunk + 7 of key p: load ks = chunk / 2 of lane 32 (chunk & 1) + p % 32
+        *reinterpret_cast<half8*>(gc + CT::k_unit(p >> 5, chunk >> 1, 32 * (chunk & 1) + (p & 31))) = out;
         float y[8];
         load8_in((const TI*)a.v + in_off, y);
 #pragma unroll
@@ -106,8 +122,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
         const int tl = idx % TB, d = idx / TB, t = t0 + tl;
         if (t >= Tn) continue;
         const int p = len + t;
-        const int slot = (p & ~15) + vt_key_of_pos(p & 15);  // the order is its own inverse
-        vtc[(size_t)d * Tcap + slot] = (_Float16)vs[tl][d];
+        // key p of its tile sits at position pos = vt_key_of_pos(p % 16) of k-step (p % 32) / 16
+        // (the order is its own inverse): lane 32 (pos / 8) + d % 32, element pos % 8
+        const int pos = vt_key_of_pos(p & 15);
+        gc[CT::v_unit(p >> 5, (p >> 4) & 1, d >> 5, 32 * (pos >> 3) + (d & 31)) + (pos & 7)] = (_Float16)vs[tl][d];
     }
 }
 
@@ -147,21 +165,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int CH = ((Ke - Kb + nsplit - 1) / nsplit + 31) & ~31;  // keys per split
     const int k0 = Kb + s * CH, k1 = min(Ke, k0 + CH);
 
-    const _Float16* kc = (const _Float16*)a.cache + (size_t)g * Tcap * D;
-    const _Float16* vtc = (const _Float16*)a.cache + (size_t)a.B * a.Hkv * Tcap * D + (size_t)g * D * Tcap;
+    using CT = CacheTile<D>;
+    const _Float16* gc = (const _Float16*)a.cache + (size_t)g * Tcap * D * 2;   // this group's tiles
 
     // first tile's loads, in flight while the queries are prepared
     half8 kf[KS], vf[2][NDB];
     auto load_tile = [&](int k) {
         // k is a multiple of 32 below k1 <= Tcap (a multiple of 64): keys k .. k + 31 are in the cache
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            kf[ks] = *reinterpret_cast<const half8*>(kc + (size_t)(k + c) * D + 16 * ks + 8 * h);
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = *reinterpret_cast<const half8*>(gc + CT::k_unit(k >> 5, ks, l));
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                vf[kk][db] = *reinterpret_cast<const half8*>(vtc + (size_t)(32 * db + c) * Tcap + k + 16 * kk + 8 * h);
+            for (int db = 0; db < NDB; ++db) vf[kk][db] = *reinterpret_cast<const half8*>(gc + CT::v_unit(k >> 5, kk, db, l));
     };
     int k = k0 + 32 * w;
     if (k < k1) load_tile(k);

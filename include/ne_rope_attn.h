@@ -191,12 +191,15 @@ ne_status_t ne_rope_attn_bwd_window(const void* q, const void* k, const void* v,
  * p = cache_lens[b] + t (window <= 0 or >= Tcap: every key up to p).
  *
  * The cache is one caller-owned device buffer of ne_kv_cache_bytes() bytes in the library's
- * layout (for each (b, kv head) group g = b * Hkv + h):
- *   K' [B * Hkv][Tcap][head_dim]  fp16, keys after RoPE
- *   V^T[B * Hkv][head_dim][Tcap]  fp16, values transposed; within every aligned run of 16
- *                                 positions, position 16a + s is stored at 16a + s', where s'
- *                                 swaps bits 2 and 3 of s
- * (V follows K in the buffer).  Values are converted to fp16 (|v| must stay below 65504).
+ * layout: for each (b, kv head) group g = b * Hkv + h, its Tcap / 32 tiles of 32 positions, tile i
+ * at element offset (g * Tcap / 32 + i) * 64 * head_dim, each holding
+ *   keys after RoPE (fp16): for u < head_dim / 16 and lane l < 64, 8 elements: key i * 32 + l % 32,
+ *     dimensions 16 u + 8 (l / 32) .. + 7, at element (u * 64 + l) * 8 of the tile;
+ *   values (fp16), from element 32 * head_dim of the tile: for kk < 2, db < head_dim / 32 and lane
+ *     l, 8 elements: dimension 32 db + l % 32 of the keys i * 32 + 16 kk + s(8 (l / 32) + j),
+ *     j < 8, at element ((kk * head_dim / 32 + db) * 64 + l) * 8 + j, where s swaps bits 2 and 3
+ * (the order of the decode kernel's 16-byte loads).  Values are converted to fp16 (|v| must stay
+ * below 65504).
  * Tcap, the capacity in tokens, is a multiple of 64.  cache_lens is a DEVICE array of B int32:
  * the tokens each sequence already holds.  It is read on the device, so it cannot be checked on
  * the host: each call uses min(max(cache_lens[b], 0), Tcap - n), n the tokens of the call, and

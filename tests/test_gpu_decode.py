@@ -24,6 +24,22 @@ def seqs(B, P, Hq, Hkv, D, seed, dtype):
             inputs.gaussian((B, P, Hkv, D), seed + 2, 1.0, dtype))
 
 
+def unpack_cache(half, B, Hkv, Tcap, D):
+    """Keys and values [B][Hkv][Tcap][D] from the cache layout of include/ne_rope_attn.h: per group,
+    tiles of 32 positions; in a tile the key block (unit u, lane l: key l % 32, dimensions
+    16u + 8(l / 32) + e) and then the value block (unit (kk, db), lane l, element j: dimension
+    32db + l % 32 of key 16kk + s(8(l / 32) + j), s swapping bits 2 and 3)."""
+    t = half.reshape(B, Hkv, Tcap // 32, 64 * D)
+    kb = t[..., :32 * D].reshape(B, Hkv, Tcap // 32, D // 16, 2, 32, 8)       # [u][l / 32][l % 32][e]
+    keys = kb.transpose(0, 1, 2, 5, 3, 4, 6).reshape(B, Hkv, Tcap, D)
+    vb = t[..., 32 * D:].reshape(B, Hkv, Tcap // 32, 2, D // 32, 2, 32, 8)     # [kk][db][l / 32][l % 32][j]
+    vb = vb.transpose(0, 1, 2, 3, 5, 7, 4, 6).reshape(B, Hkv, Tcap // 32, 32, D)  # [16kk + 8(l / 32) + j][d]
+    pos = np.arange(32)
+    swap = (pos & ~15) + 8 * ((pos >> 2) & 1) + 4 * ((pos >> 3) & 1) + (pos & 3)   # its own inverse
+    vals = vb[:, :, :, swap, :].reshape(B, Hkv, Tcap, D)
+    return keys, vals
+
+
 def fill_cache(k, v, Tcap, base, chunks):
     """Append positions 0 .. P-1 of every sequence in chunks of the given sizes; returns the cache."""
     B, P, Hkv, D = k.shape
@@ -81,18 +97,14 @@ def test_append_writes_rotated_keys_and_transposed_values(base):
     B, P, Hkv, D, Tcap = 2, 150, 2, 64, 192
     _, k, v = seqs(B, P, 2, Hkv, D, 700, "bf16")
     cache = fill_cache(k, v, Tcap, base, (10, 1, 50, 89)).cpu()
-    half = cache.view(torch.float16).double().numpy()
-    kc = half[: B * Hkv * Tcap * D].reshape(B, Hkv, Tcap, D)
-    vt = half[B * Hkv * Tcap * D:].reshape(B, Hkv, D, Tcap)
+    kc, vc = unpack_cache(cache.view(torch.float16).double().numpy(), B, Hkv, Tcap, D)
     ref_k = np.stack([oracle.rope_rows(f64(k[b]), np.arange(P), base) for b in range(B)])   # [B][P][Hkv][D]
     for b in range(B):
         for g in range(Hkv):
             rk = ref_k[b, :, g]
             assert np.all(np.abs(kc[b, g, :P] - rk) <= 2.0 ** -11 * np.abs(rk) + 1e-6)
-            pos = np.arange(P)
-            slot = (pos & ~15) + 8 * ((pos >> 2) & 1) + 4 * ((pos >> 3) & 1) + (pos & 3)
-            np.testing.assert_array_equal(vt[b, g][:, slot].T, f64(v[b, :, g]).astype(np.float16).astype(np.float64))
-    assert np.all(kc[:, :, P:] == 0) and np.all(vt[:, :, :, 160:] == 0)
+            np.testing.assert_array_equal(vc[b, g, :P], f64(v[b, :, g]).astype(np.float16).astype(np.float64))
+    assert np.all(kc[:, :, P:] == 0) and np.all(vc[:, :, P:] == 0)
 
 
 def test_decode_token_by_token_loop():

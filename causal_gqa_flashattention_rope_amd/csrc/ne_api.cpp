@@ -86,8 +86,10 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, ne_dtype_t in) {
     if (bwd) { L.qh = off; off += up(nq * esz); }
     // the forward keeps V'^T as [B * Hkv][D][Tp], Tp = T rounded up to 64 (zeros past T)
     const size_t nv = bwd ? nk : (size_t)B * Hkv * D * (((size_t)T + 63) / 64 * 64);
+    L.ds_groups = bwd ? ds_batch_groups(B, T, Hq, Hkv, in) : 0;
     L.kh = off; off += up(nk * esz);
-    L.vh = off; off += up(nv * esz);
+    L.vh = off;
+    if (L.ds_groups == 0) off += up(nv * esz);  // the stored-dS backward reads v itself
     if (bwd) {
         L.dOh = off; off += up(nq * esz);
         L.delta = off; off += up((size_t)B * T * Hq * 4);
@@ -96,7 +98,6 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, ne_dtype_t in) {
         L.rk = off; off += up((size_t)B * T * Hkv * 4);
     }
     L.table = off; off += up((size_t)T * (D / 2) * 8);
-    L.ds_groups = bwd ? ds_batch_groups(B, T, Hq, Hkv, in) : 0;
     if (L.ds_groups > 0) { L.ds = off; off += up((size_t)L.ds_groups * ds_group_bytes(T, Hq, Hkv)); }
     L.total = off;
     return L;
@@ -243,6 +244,8 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     ba.q = q; ba.k = k; ba.in_dt = (int)in_dtype;
     ba.rq = pa.rq; ba.rk = pa.rk;
     ba.ds = L.ds_groups > 0 ? ws + L.ds : nullptr;
+    pa.skip_v = L.ds_groups > 0 ? 1 : 0;
+    ba.v = v;
     ba.ds_groups = L.ds_groups;
     ba.grp0 = 0;
     ba.ngrp = B * Hkv;

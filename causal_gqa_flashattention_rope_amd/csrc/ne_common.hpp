@@ -105,6 +105,19 @@ __device__ __forceinline__ floatx4 load4_dt(const void* base, size_t off, int dt
     return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 
+// Eight consecutive elements base[off .. off + 7] of a 16-bit array (dt 1 bf16, 2 f16) as fp16.
+__device__ __forceinline__ half8 load8_f16(const void* base, size_t off, int dt) {
+    if (dt == 1) {
+        typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>((const __bf16*)base + off);
+        half8 r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = (_Float16)(float)v[e];
+        return r;
+    }
+    return *reinterpret_cast<const half8*>((const _Float16*)base + off);
+}
+
 // QK-norm backward of one row held in the 32x32 accumulator layout: lane (h, c) holds the values at
 // d = 32 db + 8 q4 + 4 h + e (the other half of the row in lane c ^ 32, which must be active too).
 // On entry y is the gradient with respect to the normalised row gain * rho * x, on return with

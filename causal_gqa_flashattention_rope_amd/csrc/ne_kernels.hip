@@ -117,7 +117,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         }
     }
     const int qrows = BWD ? Hq : 0;  // the forward rotates q inside the attention kernel
-    const int rows_per_tok = qrows + 2 * Hkv + (BWD ? Hq : 0);
+    const int skip_v = BWD && a.skip_v ? Hkv : 0;  // rows of v not copied
+    const int rows_per_tok = qrows + 2 * Hkv - skip_v + (BWD ? Hq : 0);
     const int items = TT * rows_per_tok * CPR;
     const int items_pad = (items + 255) / 256 * 256;  // whole waves iterate together
     const size_t TG = (size_t)T * G;
@@ -125,7 +126,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         const int chunk = idx % CPR;
         const int rowid = idx / CPR;
         const int tl = rowid / rows_per_tok;
-        const int which = rowid % rows_per_tok + (BWD ? 0 : Hq);  // forward: skip the q rows
+        int which = rowid % rows_per_tok + (BWD ? 0 : Hq);  // forward: skip the q rows
+        if (which >= Hq + Hkv) which += skip_v;
         const int t = t0 + tl;
         const bool live = idx < items && t < T;
         const float2* csr = cs + tl * (D / 2);
@@ -1187,8 +1189,14 @@ void dkdv_kernel_h(BwdArgs a) {
         };
 
         const OP* kvrow = (role == 0 ? kg : vg) + (size_t)key * D;
+        if (DS && role == 1) {  // fp16(v) straight from the input: no v' copy on this path
+            const size_t voff = (((size_t)b * T + min(key, T - 1)) * a.Hkv + hkv) * D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kvf[ks] = kvalid ? M::row_frag(kvrow, ks, h, D) : half8{};
+            for (int ks = 0; ks < KS; ++ks) kvf[ks] = kvalid ? load8_f16(a.v, voff + 16 * ks + 8 * h, a.in_dt) : half8{};
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kvf[ks] = kvalid ? M::row_frag(kvrow, ks, h, D) : half8{};
+        }
         floatx16 acc[NDB];  // role 0: dV^T, role 1: dK^T (d rows, this lane's key column)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[db] = floatx16{};

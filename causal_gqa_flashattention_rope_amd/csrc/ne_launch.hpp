@@ -33,6 +33,7 @@ struct PrepArgs {
     double rope_base;
     float qscale;                                   // softmax scale * log2(e)
     QkNorm qkn;
+    int skip_v;                                     // backward: no v' copy (the dK/dV pass reads v)
 };
 
 struct FwdArgs {
@@ -51,7 +52,8 @@ struct BwdArgs {
     const void* qh; const void* kh; const void* vh; const void* dOh;
     const float* delta; const float* lse2; const float2* table;
     void* dq; void* dk; void* dv;
-    const void* q; const void* k;                   // raw inputs (QK norm backward), dtype in_dt
+    const void* q; const void* k; const void* v;    // raw inputs (QK norm backward; v for dK/dV
+                                                    // on the stored-dS path), dtype in_dt
     int in_dt;                                      // 0 f32, 1 bf16, 2 f16
     const float* rq; const float* rk;               // 1/rms of the q and k rows (QK norm)
     void* ds;                                       // stored dS tiles (16-bit operands), or null:

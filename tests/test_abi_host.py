@@ -56,7 +56,8 @@ def test_workspace_sizes(L):
     tiles = sum(1 for kb in range(nkb) for rt in range(nrt) if rt >= kb * G)
     base = 2 * up(2 * nq) + 2 * up(2 * nk) + 3 * up(4 * B * T * Hq) + up(4 * B * T * Hkv) + table
     bwd = L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
-    assert bwd == base + up(B * Hkv * tiles * 8192)
+    # with the stored dS the dK/dV pass reads v itself: no v' copy
+    assert bwd == base - up(2 * nk) + up(B * Hkv * tiles * 8192)
     old = os.environ.get("NE_ROPE_ATTN_DS_MAX_BYTES")
     try:  # the cap: the buffer holds the dS of as many whole groups as fit (0: none)
         os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = "0"
@@ -68,7 +69,7 @@ def test_workspace_sizes(L):
         for groups in (1, 3, 5):
             os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = str(groups * tiles * 8192 + 4095)
             assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16) == \
-                base + up(groups * tiles * 8192)
+                base - up(2 * nk) + up(groups * tiles * 8192)
     finally:
         if old is None:
             os.environ.pop("NE_ROPE_ATTN_DS_MAX_BYTES", None)

@@ -1669,9 +1669,7 @@ __device__ __forceinline__ half8 ds_tr_frag(const _Float16* tile, int kk, int co
     return f;
 }
 
-#ifndef NE_DQ_RT
-#define NE_DQ_RT 4
-#endif
+constexpr int kDqRowTiles = 4;  // row tiles (64 flattened rows each) per dq_ds_kernel block
 // QKN: the QK norm is on (its backward in the epilogue, the raw q values fetched up front); a
 // separate instantiation, so that the plain kernel keeps its registers.
 template <int D, typename TOUT, int RT, bool QKN>
@@ -1903,9 +1901,9 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
                     NE_TRY(m.after(1));
                     NE_TRY(m.before(2));
                 }
-                const dim3 grid((nrt + NE_DQ_RT - 1) / NE_DQ_RT * bb.ngrp);
-                if (ba.qkn.on) hipLaunchKernelGGL((dq_ds_kernel<D, TO, NE_DQ_RT, true>), grid, dim3(128 * NE_DQ_RT), 0, s, bb);
-                else hipLaunchKernelGGL((dq_ds_kernel<D, TO, NE_DQ_RT, false>), grid, dim3(128 * NE_DQ_RT), 0, s, bb);
+                const dim3 grid((nrt + kDqRowTiles - 1) / kDqRowTiles * bb.ngrp);
+                if (ba.qkn.on) hipLaunchKernelGGL((dq_ds_kernel<D, TO, kDqRowTiles, true>), grid, dim3(128 * kDqRowTiles), 0, s, bb);
+                else hipLaunchKernelGGL((dq_ds_kernel<D, TO, kDqRowTiles, false>), grid, dim3(128 * kDqRowTiles), 0, s, bb);
                 NE_TRY(hipGetLastError());
             }
             return m.after(2);

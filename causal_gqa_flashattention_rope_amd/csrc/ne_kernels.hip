@@ -1643,7 +1643,8 @@ void dq_kernel_h(BwdArgs a) {
 // through that layout as rows of keys and columns of positions p = 32 rh + 16 cc + 8 h + j, so
 // the contraction order of the two operands is the same j order; the epilogue maps positions
 // back to rows.  No S, P or dP is recomputed.
-// grid (ceil(nrt / 4) * B * Hkv), 512 threads: a block takes 4 row tiles, wave w positions
+// grid (ceil(nrt / 4) * ngrp), the groups grp0 .. grp0 + ngrp - 1 of one batch, 512 threads: a
+// block takes 4 row tiles, wave w positions
 // 32 (w & 1) .. 32 (w & 1) + 31 of tile w >> 1 and all D columns of dQ; per 64-key step the K tile
 // and the 4 dS tiles come global -> registers two steps ahead (non-temporal loads for dS, which is
 // read once), then registers -> a 2-stage LDS ring one step ahead.

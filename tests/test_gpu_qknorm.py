@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from causal_gqa_flashattention_rope_amd import binding, inputs
-from tests.test_gpu_parity import DEV, check, f64, recompute_dq, slice_group
+from tests.test_gpu_parity import DEV, check, ds_cap, ds_group_bytes, f64, recompute_dq, slice_group
 
 pytestmark = pytest.mark.gpu
 
@@ -131,3 +131,15 @@ def test_qk_norm_decode_parity():
                                      1e4, window, qk_norm=QKN)
         check("o", o.cpu(), ro, torch.bfloat16, torch.float32)
         check("lse", lse.cpu(), rlse, torch.bfloat16, torch.float32)
+
+
+def test_window_and_qk_norm_in_group_batches_are_bitwise_the_single_batch_run():
+    """The stored dS processed one (batch, KV head) group at a time, with a window and the QK norm,
+    gives the bits of the single batch."""
+    B, T, Hq, Hkv, D = 2, 300, 6, 2, 128
+    q, k, v, dO = inputs.random_case(B, T, Hq, Hkv, D, seed=41, dtype="bf16")
+    one = run_ex(q, k, v, dO, 1.0e4, 100, QKN, torch.float32)
+    with ds_cap(ds_group_bytes(T, Hq // Hkv)):
+        again = run_ex(q, k, v, dO, 1.0e4, 100, QKN, torch.float32)
+    for a, b in zip(one, again):
+        assert torch.equal(a, b)

@@ -201,10 +201,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     }
 }
 
-// Forward preparation for 16-bit operands.  grid (Tp / 64, B * Hkv), 256 threads: 64 tokens of
-// one (batch, KV head) group.  k' = fp16(R(k)) rows as [group][T][D]; v' = fp16(v) transposed to
-// [group][D][Tp] with the key order of vt_key_of_pos and zeros past T; the cos/sin table rows of
-// these tokens (written by the group-0 blocks).
+// Forward preparation for 16-bit operands.  grid (Tp / 64, B * Hkv, 2), 256 threads: 64 tokens of
+// one (batch, KV head) group; z = 0: k' = fp16(R(k)) rows as [group][T][D] and the cos/sin table
+// rows of these tokens (group 0); z = 1: v' = fp16(v) transposed to [group][D][Tp] with the key
+// order of vt_key_of_pos and zeros past T.
 template <typename TI, int D>
 __global__ __launch_bounds__(256) void prep_fwd_h(PrepArgs a) {
     constexpr int TB = 64, CPR = D / 8;
@@ -214,35 +214,43 @@ __global__ __launch_bounds__(256) void prep_fwd_h(PrepArgs a) {
     const int t0 = blockIdx.x * TB, grp = blockIdx.y;
     const int T = a.T, Hkv = a.Hkv, b = grp / Hkv, hkv = grp % Hkv;
     const int Tp = (T + TB - 1) / TB * TB;
-    const bool rope = a.rope_base > 0.0;
-    if (rope) {
-        rope_cs_fill<D>(cs, theta, t0, TB, T, a.rope_base);
-        __syncthreads();
-        if (grp == 0)
-            for (int idx = threadIdx.x; idx < TB * (D / 2); idx += 256) {
-                const int t = t0 + idx / (D / 2);
-                if (t < T) a.table[(size_t)t * (D / 2) + idx % (D / 2)] = cs[idx];
+    if (blockIdx.z == 0) {
+        const bool rope = a.rope_base > 0.0;
+        if (rope) {
+            rope_cs_fill<D>(cs, theta, t0, TB, T, a.rope_base);
+            __syncthreads();
+            if (grp == 0)
+                for (int idx = threadIdx.x; idx < TB * (D / 2); idx += 256) {
+                    const int t = t0 + idx / (D / 2);
+                    if (t < T) a.table[(size_t)t * (D / 2) + idx % (D / 2)] = cs[idx];
+                }
+        }
+        for (int idx = threadIdx.x; idx < TB * CPR; idx += 256) {
+            const int tl = idx / CPR, chunk = idx % CPR, t = t0 + tl;
+            float fac = 1.f;  // QK norm factor of this key row (its chunks sit in consecutive lanes)
+            if (a.qkn.on) {
+                float x[8], ss = 0.f;
+                if (t < T) {
+                    load8((const TI*)a.k + (((size_t)b * T + t) * Hkv + hkv) * D + chunk * 8, x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+                }
+                fac = qk_factor(sum_lanes(ss, CPR), D, a.qkn.gain, a.qkn.eps);
             }
+            if (t < T) {
+                const size_t in_off = (((size_t)b * T + t) * Hkv + hkv) * D + chunk * 8;
+                _Float16* kdst = (_Float16*)a.kh + ((size_t)grp * T + t) * D + chunk * 8;
+                if (rope) convert8<TI, _Float16, D, true>((const TI*)a.k + in_off, kdst, cs + tl * (D / 2), chunk, fac);
+                else convert8<TI, _Float16, D, false>((const TI*)a.k + in_off, kdst, cs, chunk, fac);
+            }
+        }
+        return;
     }
     for (int idx = threadIdx.x; idx < TB * CPR; idx += 256) {
         const int tl = idx / CPR, chunk = idx % CPR, t = t0 + tl;
         float x[8];
-        float fac = 1.f;  // QK norm factor of this key row (its chunks sit in consecutive lanes)
-        if (a.qkn.on) {
-            float ss = 0.f;
-            if (t < T) {
-                load8((const TI*)a.k + (((size_t)b * T + t) * Hkv + hkv) * D + chunk * 8, x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-            }
-            fac = qk_factor(sum_lanes(ss, CPR), D, a.qkn.gain, a.qkn.eps);
-        }
         if (t < T) {
-            const size_t in_off = (((size_t)b * T + t) * Hkv + hkv) * D + chunk * 8;
-            _Float16* kdst = (_Float16*)a.kh + ((size_t)grp * T + t) * D + chunk * 8;
-            if (rope) convert8<TI, _Float16, D, true>((const TI*)a.k + in_off, kdst, cs + tl * (D / 2), chunk, fac);
-            else convert8<TI, _Float16, D, false>((const TI*)a.k + in_off, kdst, cs, chunk, fac);
-            load8((const TI*)a.v + in_off, x);
+            load8((const TI*)a.v + (((size_t)b * T + t) * Hkv + hkv) * D + chunk * 8, x);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -1860,7 +1868,7 @@ static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, hipStream_
     const Marks m{ev, s};
     NE_TRY(m.before(0));
     if constexpr (sizeof(OP) == 2)
-        hipLaunchKernelGGL((prep_fwd_h<TI, D>), dim3((pa.T + 63) / 64, pa.B * pa.Hkv), dim3(256), 0, s, pa);
+        hipLaunchKernelGGL((prep_fwd_h<TI, D>), dim3((pa.T + 63) / 64, pa.B * pa.Hkv, 2), dim3(256), 0, s, pa);
     else
         hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, false>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);
     NE_TRY(hipGetLastError());

@@ -40,27 +40,26 @@ namespace ne {
 // theta_i and the phase t * theta_i are formed in double precision and the phase is reduced to
 // [-pi, pi] there (two-term 2 pi), so the single-precision sincos sees a small argument and the
 // table entries are within a few fp32 ulps of the exactly rounded values at any position.
+__device__ __forceinline__ float2 rope_cs_at(int t, double theta) {
+    constexpr double kTwoPiHi = 6.283185307179586;        // 2 pi rounded to double
+    constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2 pi - kTwoPiHi
+    constexpr double kInvTwoPi = 0.15915494309189535;
+    const double phi = (double)t * theta;
+    const double n = rint(phi * kInvTwoPi);
+    const double r = fma(-n, kTwoPiLo, fma(-n, kTwoPiHi, phi));
+    float sv, cv;
+    sincosf((float)r, &sv, &cv);
+    return make_float2(cv, sv);
+}
 template <int D>
 __device__ __forceinline__ void rope_cs_fill(float2* cs, double* theta, int t0, int TT, int T, double base) {
     for (int i = threadIdx.x; i < D / 2; i += blockDim.x)
         theta[i] = base > 0.0 ? exp2(-2.0 * (double)i / (double)D * log2(base)) : 0.0;
     __syncthreads();
-    constexpr double kTwoPiHi = 6.283185307179586;        // 2 pi rounded to double
-    constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2 pi - kTwoPiHi
-    constexpr double kInvTwoPi = 0.15915494309189535;
     for (int idx = threadIdx.x; idx < TT * (D / 2); idx += blockDim.x) {
         const int tl = idx / (D / 2), i = idx % (D / 2);
         const int t = t0 + tl;
-        float2 v = make_float2(1.f, 0.f);
-        if (base > 0.0 && t < T) {
-            const double phi = (double)t * theta[i];
-            const double n = rint(phi * kInvTwoPi);
-            const double r = fma(-n, kTwoPiLo, fma(-n, kTwoPiHi, phi));
-            float sv, cv;
-            sincosf((float)r, &sv, &cv);
-            v = make_float2(cv, sv);
-        }
-        cs[idx] = v;
+        cs[idx] = base > 0.0 && t < T ? rope_cs_at(t, theta[i]) : make_float2(1.f, 0.f);
     }
 }
 
@@ -217,7 +216,28 @@ __global__ __launch_bounds__(256) void prep_fwd_h(PrepArgs a) {
     if (blockIdx.z == 0) {
         const bool rope = a.rope_base > 0.0;
         if (rope) {
-            rope_cs_fill<D>(cs, theta, t0, TB, T, a.rope_base);
+            // cos/sin of tokens t0 + 8u and of offsets v (u, v < 8) directly, then every row of the 64
+            // as a product, cs(t0 + 8u + v) = cs(t0 + 8u) cs(v): a quarter of the sincos evaluations,
+            // each product within a few fp32 ulps of the directly computed entry
+            for (int i = threadIdx.x; i < D / 2; i += 256)
+                theta[i] = exp2(-2.0 * (double)i / (double)D * log2(a.rope_base));
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < 16 * (D / 2); idx += 256) {
+                const int r = idx / (D / 2);
+                cs[idx] = rope_cs_at(r < 8 ? t0 + 8 * r : r - 8, theta[idx % (D / 2)]);
+            }
+            __syncthreads();
+            constexpr int PT = TB * (D / 2) / 256;   // entries per thread
+            float2 ra[PT];
+#pragma unroll
+            for (int it = 0; it < PT; ++it) {
+                const int idx = threadIdx.x + 256 * it, tl = idx / (D / 2), i = idx % (D / 2);
+                const float2 u = cs[(tl >> 3) * (D / 2) + i], v = cs[(8 + (tl & 7)) * (D / 2) + i];
+                ra[it] = make_float2(u.x * v.x - u.y * v.y, u.y * v.x + u.x * v.y);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < PT; ++it) cs[threadIdx.x + 256 * it] = ra[it];
             __syncthreads();
             if (grp == 0)
                 for (int idx = threadIdx.x; idx < TB * (D / 2); idx += 256) {

@@ -1767,7 +1767,9 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             const bool ok = kc >= rlo[r] && kc <= rhi[r];
-            gu32x4* src = sgpr_global_ptr<const u32x4>(dsg + (ok ? ds_tile_index(kc, rt0 + r, nrt, G) : 0) * 4096);
+            // past hi the loads are not used: read the K tile of hi again (L2-resident) instead of dS
+            gu32x4* src = sgpr_global_ptr<const u32x4>(kb > hi ? kg + (size_t)kc * BN * D
+                                                               : dsg + (ok ? ds_tile_index(kc, rt0 + r, nrt, G) : 0) * 4096);
             dr[sl][r] = __builtin_nontemporal_load(src + tid);
         }
     };

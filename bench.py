@@ -489,6 +489,7 @@ def main():
         "config": {"workload": w.name, "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "head_dim": D,
                    "rope_base": w.rope_base, "in_dtype": w.dtype, "mfma_operands": "f16",
                    "accumulate": "f32", "out_dtype": args.out_dtype, "backward": "deterministic",
+                   "dq_pass": "stored_ds" if dqf == 2.0 else "recompute",
                    "step": "fwd+bwd", "global_batch": B, "seq_len": T, "parallelism": "none"},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
         "fwd_tflops": round(4.0 * unit / (fwd_ms * 1e-3) / 1e12, 2),

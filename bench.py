@@ -3,24 +3,31 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = one forward call (operand preparation + attention) and one backward call
-(preparation with Delta + dK/dV + dQ) over one batch of synthetic inputs already resident in
-HBM.  Throughput counts algorithmic causal FLOPs only (unmasked (query, key) pairs,
-N = T(T+1)/2 per head): forward 4*B*Hq*D*N, backward 10*B*Hq*D*N, step 14*B*Hq*D*N.
-The whole-step time comes from the host clock around K synchronised steps; inside them the
-library records HIP events (on the stream it launches on) around the dominant kernel only, whose
-average duration gives the roofline figure.  The per-kernel breakdown comes from a separate
-pass with every launch bracketed.  Prints one JSON line.
+One step = one forward call (operand preparation + attention) and one backward call (dO scale,
+preparation with Delta, dK/dV, dQ) over one batch of synthetic inputs already resident in HBM.  The
+headline runs the default backward: deterministic, O(T) workspace, the dQ pass recomputing S and dP.
+Throughput counts algorithmic causal FLOPs only (unmasked (query, key) pairs, N = T(T+1)/2 per head):
+forward 4*B*Hq*D*N, backward 10*B*Hq*D*N, step 14*B*Hq*D*N.  The RoPE table is built once per
+workspace (ne_rope_table_init) before the warmup, outside the timed steps, and timed on its own.
+The whole-step time comes from the host clock around K synchronised steps; inside them the library
+records HIP events (on the stream it launches on) around the dominant kernel only, whose average
+duration gives the roofline figure.  The per-kernel breakdown comes from a separate pass with every
+launch bracketed, the fwd / bwd / fwd+bwd medians and minima from another pass with events between
+the calls, and the GPU clock under load from amdsmi samples taken while the same step runs for about
+a second.  Prints one JSON line.
 
-After the headline measurement the same step is measured with a sliding window of --window keys
-(default T/4, the short window of the nanochat guide's window_pattern; 0 skips it), counting the
-visible pairs N_W = W(W+1)/2 + (T-W)W per head; it is reported under "sliding_window".  The causal
-step with the QK norm on (gain 1.2, eps 1e-6) is reported under "qk_norm", and the workload layer's
-QKV projection with the RoPE epilogue (2 M N C flops) under "qkv_projection".
-Then one decode step of the cached workload (--decode-batch sequences, each holding 8191 tokens of
-the long-context shape, Hq 32 / Hkv 8 / D 128, RoPE base 5e5, attending with one new token) is
-measured as HBM bandwidth: bytes = the visible cached keys and values (fp16) + q + o, reported
-under "decode"; 0 skips it.
+The other measurements run first (each with its own warmup), the headline last:
+  * the same step with the backward's other designs: the stored dS (NE_FLAG_STORE_DS, under
+    "stored_ds") and dQ added with atomics in the dK/dV pass (NE_FLAG_NONDETERMINISTIC, "atomic_dq");
+  * a sliding window of --window keys (default T/4, the short window of the nanochat guide's
+    window_pattern; 0 skips it), counting the visible pairs N_W = W(W+1)/2 + (T-W)W per head;
+  * the causal step with the QK norm on (gain 1.2, eps 1e-6), under "qk_norm";
+  * the workload layer's QKV projection with the RoPE epilogue (2 M N C flops), "qkv_projection";
+  * one decode step of the cached workload (--decode-batch sequences, each holding 8191 tokens of the
+    long-context shape, Hq 32 / Hkv 8 / D 128, RoPE base 5e5, attending with one new token) as HBM
+    bandwidth: bytes = the visible cached keys and values (fp16) + q + o, under "decode";
+  * fwd / bwd of every other workload of the table (the fp32 path of the NanoEuler layer too),
+    under "configs".
 """
 import argparse
 import hashlib
@@ -45,23 +52,61 @@ QKV_SOURCES = ["causal_gqa_flashattention_rope_amd/csrc/ne_qkv.hip",
                "causal_gqa_flashattention_rope_amd/csrc/ne_common.hpp"]
 
 
-def dq_flops_per_pair_over_d(B, T, Hq, Hkv, D, dtype):
-    """Executed MFMA work of the dQ pass per (query, key) pair and head, in units of D: 2 when it
-    reads the dS the dK/dV pass stores (the 16-bit path while that buffer fits its cap), 6 when it
-    recomputes S and dP.  The stored dS shows as extra backward workspace."""
-    from causal_gqa_flashattention_rope_amd import binding
-    key = "NE_ROPE_ATTN_DS_MAX_BYTES"
-    with_ds = binding.bwd_workspace_bytes(B, T, Hq, Hkv, D, dtype)
-    old = os.environ.get(key)
-    os.environ[key] = "0"
-    try:
-        without = binding.bwd_workspace_bytes(B, T, Hq, Hkv, D, dtype)
-    finally:
-        if old is None:
-            os.environ.pop(key, None)
-        else:
-            os.environ[key] = old
-    return 2.0 if with_ds > without else 6.0
+# Executed MFMA work of each kernel per (query, key) pair and head, in units of D, for each backward
+# design: the dQ pass recomputes S and dP (6 D), or reads the stored dS (2 D); with atomic dQ the
+# dK/dV pass carries the dQ product (8 D + 2 D) and the dQ launch only converts the accumulator.
+KERNEL_FLOPS_OVER_D = {
+    "recompute": {"attn_fwd": 4.0, "attn_bwd_dkdv": 8.0, "attn_bwd_dq": 6.0},
+    "stored_ds": {"attn_fwd": 4.0, "attn_bwd_dkdv": 8.0, "attn_bwd_dq": 2.0},
+    "atomic": {"attn_fwd": 4.0, "attn_bwd_dkdv": 10.0, "attn_bwd_dq": 0.0},
+}
+
+
+class ClockSampler:
+    """The GPU's current graphics clock (MHz), sampled from a background thread with amdsmi while the
+    GPU runs a workload; None if amdsmi cannot be used."""
+
+    def __init__(self):
+        self.ok = False
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.smi = amdsmi
+            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self.read()
+            self.ok = True
+        except Exception:
+            self.ok = False
+
+    def read(self):
+        info = self.smi.amdsmi_get_clock_info(self.handle, self.smi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def sample_while(self, fn):
+        import threading
+        samples, stop = [], threading.Event()
+
+        def loop():
+            while not stop.is_set():
+                try:
+                    samples.append(self.read())
+                except Exception:
+                    pass
+                time.sleep(0.002)
+        th = threading.Thread(target=loop, daemon=True)
+        if self.ok:
+            th.start()
+        try:
+            fn()
+        finally:
+            stop.set()
+            if self.ok:
+                th.join()
+        if not samples:
+            return None
+        samples.sort()
+        return {"median": samples[len(samples) // 2], "min": samples[0], "max": samples[-1],
+                "samples": len(samples), "unit": "MHz"}
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES):
@@ -154,35 +199,35 @@ def cpu_baseline(w, sample_B):
 def measure_configs(skip, hev, new_events):
     """Every other workload of the table: fwd, bwd and fwd+bwd times (median and min over the reps,
     HIP events around each call on the current stream), with fp32 outputs (the fp32 path for the fp32
-    workload).  The two smaller, HBM-relevant workloads also get a cold fwd+bwd number: 1 GiB is
-    written between reps, which evicts the 256 MB last-level cache."""
+    workload, and the NanoEuler layer on the fp32 path as well, against the fp32 MFMA peak).  The two
+    smaller, HBM-relevant workloads also get a cold fwd+bwd number: 1 GiB is written between reps,
+    which evicts the 256 MB last-level cache."""
     import statistics
     import torch
     from causal_gqa_flashattention_rope_amd import binding, inputs
     dev = torch.device("cuda:0")
     out = {}
     scrub = None
-    for name, w in inputs.WORKLOADS.items():
-        if name == skip:
-            continue
-        q, k, v, dO = (t.to(dev) for t in inputs.make_inputs(w))
+    runs = [(name, w, None) for name, w in inputs.WORKLOADS.items() if name != skip]
+    runs.insert(2, ("nanoeuler_gpu_layer_f32", inputs.WORKLOADS["nanoeuler_gpu_layer"], "f32"))
+    for name, w, dt in runs:
+        q, k, v, dO = (t.to(dev) for t in inputs.make_inputs(w, dtype=dt))
         B, T, Hq, Hkv, D = w.B, w.T, w.Hq, w.Hkv, w.D
         o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
         dq = torch.empty_like(o)
         dk = torch.empty((B, T, Hkv, D), dtype=torch.float32, device=dev)
         dv = torch.empty_like(dk)
-        wsf = binding.alloc_workspace(binding.fwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype), dev)
-        wsb = binding.alloc_workspace(binding.bwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype), dev)
+        ws = binding.new_workspace(True, q, k, w.rope_base)   # serves the forward too
         stream = torch.cuda.current_stream().cuda_stream
 
         def call(ev=None):
             if ev:
                 hev.record(ev[0], stream)
-            binding.ne_rope_attn_fwd(q, k, v, w.rope_base, o=o, lse=lse, workspace=wsf)
+            binding.ne_rope_attn_fwd(q, k, v, w.rope_base, o=o, lse=lse, workspace=ws)
             if ev:
                 hev.record(ev[1], stream)
-            binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=wsb)
+            binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws)
             if ev:
                 hev.record(ev[2], stream)
 
@@ -197,12 +242,15 @@ def measure_configs(skip, hev, new_events):
         b = [hev.elapsed_ms(e[1], e[2]) for e in evs]
         fb = [x + y for x, y in zip(f, b)]
         unit = B * Hq * D * T * (T + 1) / 2
-        rec = {"shape": f"B{B} T{T} Hq{Hq} Hkv{Hkv} D{D}", "rope_base": w.rope_base, "in_dtype": w.dtype,
-               "out_dtype": "f32", "reps": reps,
+        peak = MFMA_PEAK_F32 if q.dtype == torch.float32 else MFMA_PEAK_F16
+        tf = 14.0 * unit / (statistics.median(fb) * 1e-3) / 1e12
+        rec = {"shape": f"B{B} T{T} Hq{Hq} Hkv{Hkv} D{D}", "rope_base": w.rope_base,
+               "in_dtype": dt or w.dtype, "out_dtype": "f32", "reps": reps,
                "fwd_ms": {"median": round(statistics.median(f), 4), "min": round(min(f), 4)},
                "bwd_ms": {"median": round(statistics.median(b), 4), "min": round(min(b), 4)},
                "fwd_bwd_ms": {"median": round(statistics.median(fb), 4), "min": round(min(fb), 4)},
-               "fwd_bwd_tflops_median": round(14.0 * unit / (statistics.median(fb) * 1e-3) / 1e12, 2)}
+               "fwd_bwd_tflops_median": round(tf, 2), "mfma_peak": peak,
+               "frac_of_peak": round(tf / peak, 4)}
         if name in ("nanoeuler_gpu_layer", "gpt2_small_mha"):
             if scrub is None:
                 scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
@@ -216,7 +264,7 @@ def measure_configs(skip, hev, new_events):
             rec["cold_fwd_bwd_ms"] = {"median": round(statistics.median(cold), 4), "min": round(min(cold), 4),
                                       "reps": 10}
         out[name] = rec
-        del q, k, v, dO, o, lse, dq, dk, dv, wsf, wsb
+        del q, k, v, dO, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
     return out
 
@@ -338,8 +386,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100,
-                    help="untimed steps first (the GPU clocks settle over the first ~50 steps)")
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps before the timed ones")
     ap.add_argument("--workload", default="wide_gqa_t2048_d128")
     ap.add_argument("--out-dtype", default="bf16", choices=["f32", "bf16"],
                     help="dtype of o, dq, dk, dv (the inputs are bf16)")
@@ -352,10 +399,15 @@ def main():
                     help="window of the sliding-window measurement (-1: T/4; 0: skip it)")
     ap.add_argument("--qkv", type=int, default=1, help="also measure the QKV projection with the RoPE epilogue")
     ap.add_argument("--qk-norm", type=int, default=1, help="also measure the step with the QK norm on (0: skip)")
+    ap.add_argument("--other-backwards", type=int, default=1,
+                    help="also measure the step with the stored dS and with the atomic dQ (0: skip)")
     ap.add_argument("--configs", type=int, default=1,
                     help="also time fwd / bwd of every other workload of the table (0: skip)")
     ap.add_argument("--decode-batch", type=int, default=8,
                     help="sequences of the decode measurement (0: skip it)")
+    ap.add_argument("--clock", type=int, default=1, help="sample the GPU clock under load (0: skip)")
+    ap.add_argument("--flags", type=int, default=0,
+                    help="backward flags of the headline step (0: the default, deterministic O(T) backward)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards over "
@@ -363,6 +415,7 @@ def main():
               "own groups).", file=sys.stderr)
         sys.exit(2)
 
+    import statistics
     import torch
     from causal_gqa_flashattention_rope_amd import binding, inputs
 
@@ -379,33 +432,30 @@ def main():
     dq = torch.empty((B, T, Hq, D), dtype=out_dt, device=dev)
     dk = torch.empty((B, T, Hkv, D), dtype=out_dt, device=dev)
     dv = torch.empty((B, T, Hkv, D), dtype=out_dt, device=dev)
-    wsf = binding.alloc_workspace(binding.fwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype), dev)
-    wsb = binding.alloc_workspace(binding.bwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype), dev)
-
-    def make_step(window, qk_norm=None):
-        if qk_norm is not None:
-            def step(ev_f=None, ev_b=None):
-                binding.ne_rope_attn_fwd_ex(q, k, v, w.rope_base, window or 0, qk_norm, o=o, lse=lse, workspace=wsf,
-                                            events=ev_f)
-                binding.ne_rope_attn_bwd_ex(q, k, v, o, lse, dO, w.rope_base, window or 0, qk_norm, dq=dq, dk=dk,
-                                            dv=dv, workspace=wsb, events=ev_b)
-        elif window is None:
-            def step(ev_f=None, ev_b=None):
-                binding.ne_rope_attn_fwd(q, k, v, w.rope_base, o=o, lse=lse, workspace=wsf, events=ev_f)
-                binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=wsb,
-                                         events=ev_b)
-        else:
-            def step(ev_f=None, ev_b=None):
-                binding.ne_rope_attn_fwd_window(q, k, v, w.rope_base, window, o=o, lse=lse, workspace=wsf,
-                                                events=ev_f)
-                binding.ne_rope_attn_bwd_window(q, k, v, o, lse, dO, w.rope_base, window, dq=dq, dk=dk, dv=dv,
-                                                workspace=wsb, events=ev_b)
-        return step
-
     hev = _HipEvents()
 
     def new_events(n):              # created outside any timed region
         return hev.create(n)
+
+    wss = {}
+
+    def workspace(flags):
+        """One backward workspace per flag set (it serves the forward too), its table built once."""
+        if flags not in wss:
+            n = binding.workspace_bytes(True, B, T, Hq, Hkv, D, w.rope_base, q.dtype, flags)
+            wss[flags] = binding.alloc_workspace(n, dev)
+            binding.ne_rope_table_init(wss[flags], T, D, w.rope_base)
+        return wss[flags]
+
+    def make_step(window=0, qk_norm=None, flags=0):
+        ws = workspace(flags)
+
+        def step(ev_f=None, ev_b=None):
+            binding.ne_rope_attn_fwd(q, k, v, w.rope_base, o=o, lse=lse, workspace=ws, window=window,
+                                     qk_norm=qk_norm, events=ev_f)
+            binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws,
+                                     flags=flags, window=window, qk_norm=qk_norm, events=ev_b)
+        return step
 
     def per_kernel_ms(evf, evb):
         def avg(evs, i):
@@ -417,7 +467,7 @@ def main():
             "attn_bwd_dq": ("b", 2)}
 
     def measure(step, warmup, K):
-        """(ms per step, dominant kernel, its average launch ms, per-kernel breakdown)"""
+        """(ms per step, dominant kernel, its launch ms (mean, min, max), per-kernel breakdown)"""
         # warmup, every launch bracketed: picks the dominant kernel (the longest of the three
         # attention kernels) that the timed region brackets
         Wu = max(warmup, 1)
@@ -445,7 +495,7 @@ def main():
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         ms_per_step = (t1 - t0) * 1e3 / K
-        dom_ms = sum(hev.elapsed_ms(a, b) for a, b in tev) / K
+        dl = [hev.elapsed_ms(a, b) for a, b in tev]
 
         # per-kernel breakdown from a separate, untimed pass with every launch bracketed
         Kb = min(K, 10)
@@ -455,24 +505,103 @@ def main():
         for i in range(Kb):
             step(evf[i], evb[i])
         torch.cuda.synchronize()
-        return ms_per_step, dominant, dom_ms, per_kernel_ms(evf, evb)
-
-    K = args.steps
-    Kb = min(K, 10)
-    ms_per_step, dominant, dom_ms, kern_ms = measure(make_step(None), args.warmup, K)
+        return ms_per_step, dominant, (sum(dl) / K, min(dl), max(dl)), per_kernel_ms(evf, evb)
 
     N = T * (T + 1) / 2
     unit = B * Hq * D * N
     flops_step = 14.0 * unit
-    value = flops_step / (ms_per_step * 1e-3) / 1e12
-    # executed MFMA work per launch (dQ: from the stored dS, or recomputing S and dP)
-    dqf = dq_flops_per_pair_over_d(B, T, Hq, Hkv, D, q.dtype)
-    kern_flops = {"attn_fwd": 4.0 * unit, "attn_bwd_dkdv": 8.0 * unit, "attn_bwd_dq": dqf * unit}
     peak = MFMA_PEAK_F16 if q.dtype != torch.float32 else MFMA_PEAK_F32
-    achieved = kern_flops[dominant] / (dom_ms * 1e-3) / 1e12
-    traffic = read_traffic(dominant, args.workload)
-    fwd_ms = kern_ms["prep_fwd"] + kern_ms["attn_fwd"]
-    bwd_ms = kern_ms["prep_bwd"] + kern_ms["attn_bwd_dkdv"] + kern_ms["attn_bwd_dq"]
+
+    def roofline(design, dominant, dom, flops_unit, traffic_key=None):
+        kf = KERNEL_FLOPS_OVER_D[design][dominant] * flops_unit
+        ach = kf / (dom[0] * 1e-3) / 1e12
+        return {"kernel": dominant, "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4),
+                "traffic": read_traffic(dominant, traffic_key) if traffic_key else None,
+                "flops_per_launch": kf, "launch_ms": round(dom[0], 4),
+                "launch_ms_min": round(dom[1], 4), "launch_ms_max": round(dom[2], 4),
+                "launch_ms_source": "HIP events around this kernel in every timed step"}
+
+    def side_line(step, design, flops_unit, K):
+        ms, dom_k, dom, kern = measure(step, 20, K)
+        return {"value": round(14.0 * flops_unit / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "ms_per_step": round(ms, 4), "steps": K, "warmup": 20,
+                "kernel_ms": {n: round(t, 4) for n, t in kern.items()},
+                "roofline": roofline(design, dom_k, dom, flops_unit)}
+
+    result = {}
+    K = args.steps
+    # ---- the other measurements first (each with its own warmup), the headline last ----
+    if args.other_backwards and q.dtype != torch.float32:
+        result["stored_ds"] = dict(side_line(make_step(flags=binding.NE_FLAG_STORE_DS), "stored_ds", unit, K),
+                                   flags="NE_FLAG_STORE_DS", dq_pass="stored_ds", deterministic=True,
+                                   workspace_bytes=binding.workspace_bytes(True, B, T, Hq, Hkv, D, w.rope_base,
+                                                                           q.dtype, binding.NE_FLAG_STORE_DS))
+        result["atomic_dq"] = dict(side_line(make_step(flags=binding.NE_FLAG_NONDETERMINISTIC), "atomic", unit, K),
+                                   flags="NE_FLAG_NONDETERMINISTIC", dq_pass="atomic adds in dK/dV",
+                                   deterministic=False,
+                                   workspace_bytes=binding.workspace_bytes(True, B, T, Hq, Hkv, D, w.rope_base,
+                                                                           q.dtype, binding.NE_FLAG_NONDETERMINISTIC))
+    Wn = T // 4 if args.window < 0 else args.window
+    if 0 < Wn < T:
+        unit_w = B * Hq * D * (Wn * (Wn + 1) / 2 + (T - Wn) * Wn)
+        result["sliding_window"] = dict(window=Wn, pairs_per_head=Wn * (Wn + 1) // 2 + (T - Wn) * Wn,
+                                        **side_line(make_step(window=Wn), "recompute", unit_w, K))
+    if args.qk_norm:
+        result["qk_norm"] = dict(gain=1.2, eps=1e-6, **side_line(make_step(qk_norm=(1.2, 1e-6)), "recompute", unit, K))
+    if args.qkv:
+        result["qkv_projection"] = measure_qkv(w, K, hev, new_events, MFMA_PEAK_F16)
+    if args.decode_batch > 0:
+        result["decode"] = measure_decode(args.decode_batch, K, hev, new_events)
+    if args.configs:
+        result["configs"] = measure_configs(args.workload, hev, new_events)
+
+    # ---- the headline: the default backward (or --flags) ----
+    design = ("atomic" if args.flags & binding.NE_FLAG_NONDETERMINISTIC else
+              "stored_ds" if args.flags & binding.NE_FLAG_STORE_DS else "recompute")
+    step = make_step(flags=args.flags)
+    # the RoPE table, built once per workspace outside the timed steps, timed on its own
+    tbl = new_events(2)
+    torch.cuda.synchronize()
+    hev.record(tbl[0], torch.cuda.current_stream().cuda_stream)
+    binding.ne_rope_table_init(wss[args.flags], T, D, w.rope_base)
+    hev.record(tbl[1], torch.cuda.current_stream().cuda_stream)
+    ms_per_step, dominant, dom, kern_ms = measure(step, args.warmup, K)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    # fwd / bwd / fwd+bwd medians and minima (events between the calls), then the clock under load
+    stream = torch.cuda.current_stream().cuda_stream
+    Ks = 50
+    sev = [new_events(3) for _ in range(Ks)]
+    for e in sev:
+        hev.record(e[0], stream)
+        binding.ne_rope_attn_fwd(q, k, v, w.rope_base, o=o, lse=lse, workspace=wss[args.flags])
+        hev.record(e[1], stream)
+        binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=wss[args.flags],
+                                 flags=args.flags)
+        hev.record(e[2], stream)
+    torch.cuda.synchronize()
+    fl = [hev.elapsed_ms(e[0], e[1]) for e in sev]
+    bl = [hev.elapsed_ms(e[1], e[2]) for e in sev]
+    fbl = [a + b for a, b in zip(fl, bl)]
+
+    def med_min(x, flops):
+        return {"median_ms": round(statistics.median(x), 4), "min_ms": round(min(x), 4),
+                "tflops_median": round(flops / (statistics.median(x) * 1e-3) / 1e12, 2),
+                "tflops_max": round(flops / (min(x) * 1e-3) / 1e12, 2)}
+    clock = None
+    if args.clock:
+        sampler = ClockSampler()
+
+        def load():
+            t_end = time.perf_counter() + 1.0
+            while time.perf_counter() < t_end:
+                for _ in range(20):
+                    step()
+                torch.cuda.synchronize()
+        clock = sampler.sample_while(load)
+
+    traffic_key = args.workload if design == "recompute" and args.out_dtype == "bf16" else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -488,49 +617,26 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "head_dim": D,
                    "rope_base": w.rope_base, "in_dtype": w.dtype, "mfma_operands": "f16",
-                   "accumulate": "f32", "out_dtype": args.out_dtype, "backward": "deterministic",
-                   "dq_pass": "stored_ds" if dqf == 2.0 else "recompute",
+                   "accumulate": "f32", "out_dtype": args.out_dtype, "flags": args.flags,
+                   "backward": "deterministic" if design != "atomic" else "atomic dQ (not bit-reproducible)",
+                   "dq_pass": design, "workspace": "O(T)" if design == "recompute" else "O(T^2) stored dS"
+                   if design == "stored_ds" else "O(T) + fp32 dQ accumulator",
                    "step": "fwd+bwd", "global_batch": B, "seq_len": T, "parallelism": "none"},
         "pct_of_mfma_peak": round(100.0 * value / peak, 2),
-        "fwd_tflops": round(4.0 * unit / (fwd_ms * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(10.0 * unit / (bwd_ms * 1e-3) / 1e12, 2),
+        "fwd_tflops": round(4.0 * unit / ((kern_ms["prep_fwd"] + kern_ms["attn_fwd"]) * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(10.0 * unit / ((kern_ms["prep_bwd"] + kern_ms["attn_bwd_dkdv"] + kern_ms["attn_bwd_dq"])
+                                           * 1e-3) / 1e12, 2),
+        "spread": {"fwd": med_min(fl, 4.0 * unit), "bwd": med_min(bl, 10.0 * unit),
+                   "fwd_bwd": med_min(fbl, flops_step), "reps": Ks,
+                   "note": "HIP events between the calls of separate steps after the timed region"},
+        "gpu_clock_under_load": clock,
+        "rope_table_init_ms": round(hev.elapsed_ms(*tbl), 4),
         "kernel_ms": {n: round(t, 4) for n, t in kern_ms.items()},
-        "kernel_ms_note": f"separate pass of {Kb} steps with every launch bracketed by HIP events",
-        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "flops_per_launch": kern_flops[dominant], "launch_ms": round(dom_ms, 4),
-                     "launch_ms_source": "HIP events around this kernel in every timed step"},
+        "kernel_ms_note": f"separate pass of {min(K, 10)} steps with every launch bracketed by HIP events "
+                          "(prep_bwd includes the dO scale pass)",
+        "roofline": roofline(design, dominant, dom, unit, traffic_key),
+        **result,
     }
-    Wn = T // 4 if args.window < 0 else args.window
-    if 0 < Wn < T:
-        # sliding window: the same step, counting the visible pairs only
-        ms_w, dom_w, dom_ms_w, kern_w = measure(make_step(Wn), 20, K)
-        unit_w = B * Hq * D * (Wn * (Wn + 1) / 2 + (T - Wn) * Wn)
-        kf_w = {"attn_fwd": 4.0 * unit_w, "attn_bwd_dkdv": 8.0 * unit_w, "attn_bwd_dq": dqf * unit_w}
-        ach_w = kf_w[dom_w] / (dom_ms_w * 1e-3) / 1e12
-        result["sliding_window"] = {
-            "window": Wn, "pairs_per_head": Wn * (Wn + 1) // 2 + (T - Wn) * Wn,
-            "value": round(14.0 * unit_w / (ms_w * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(ms_w, 4), "steps": K, "warmup": 20,
-            "kernel_ms": {n: round(t, 4) for n, t in kern_w.items()},
-            "roofline": {"kernel": dom_w, "bound": "mfma", "achieved": round(ach_w, 2), "peak": peak,
-                         "unit": "TFLOP/s", "frac": round(ach_w / peak, 4), "traffic": None,
-                         "flops_per_launch": kf_w[dom_w], "launch_ms": round(dom_ms_w, 4)},
-        }
-    if args.qk_norm:
-        # QK norm (gain 1.2, eps 1e-6): the same causal step, counting the same pairs
-        ms_q, dom_q, dom_ms_q, kern_q = measure(make_step(None, (1.2, 1e-6)), 20, K)
-        result["qk_norm"] = {
-            "gain": 1.2, "eps": 1e-6, "value": round(flops_step / (ms_q * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(ms_q, 4), "steps": K, "warmup": 20,
-            "kernel_ms": {n: round(t, 4) for n, t in kern_q.items()},
-        }
-    if args.qkv:
-        result["qkv_projection"] = measure_qkv(w, K, hev, new_events, MFMA_PEAK_F16)
-    if args.decode_batch > 0:
-        result["decode"] = measure_decode(args.decode_batch, K, hev, new_events)
-    if args.configs:
-        result["configs"] = measure_configs(args.workload, hev, new_events)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

@@ -15,15 +15,17 @@ LIB_PATH = os.path.join(_HERE, "libne_rope_attn.so")
 NE_F32, NE_BF16, NE_F16 = 0, 1, 2
 _DT = {torch.float32: NE_F32, torch.bfloat16: NE_BF16, torch.float16: NE_F16}
 STATUS = {0: "NE_OK", 1: "NE_ERR_NULL", 2: "NE_ERR_SHAPE", 3: "NE_ERR_UNSUPPORTED",
-          4: "NE_ERR_ALIGN", 5: "NE_ERR_WORKSPACE", 6: "NE_ERR_HIP"}
+          4: "NE_ERR_ALIGN", 5: "NE_ERR_WORKSPACE", 6: "NE_ERR_NO_ROPE_TABLE", 7: "NE_ERR_HIP"}
+NE_FLAG_NONDETERMINISTIC = 0x1
+NE_FLAG_BF16_OPERANDS = 0x2
+NE_FLAG_ROPE_HALF_SPLIT = 0x4
+NE_FLAG_STORE_DS = 0x8
 
 # Every symbol include/ne_rope_attn.h declares.
-EXPORTS = ("ne_rope_attn_fwd_workspace_bytes", "ne_rope_attn_bwd_workspace_bytes",
-           "ne_rope_attn_fwd", "ne_rope_attn_bwd", "ne_rope_attn_fwd_timed", "ne_rope_attn_bwd_timed",
-           "ne_rope_attn_fwd_window", "ne_rope_attn_bwd_window",
+EXPORTS = ("ne_rope_attn_workspace_bytes", "ne_rope_table_init", "ne_rope_table_check",
+           "ne_rope_attn_fwd", "ne_rope_attn_bwd", "ne_rope_attn_fwd_ex", "ne_rope_attn_bwd_ex",
            "ne_kv_cache_bytes", "ne_kv_cache_append", "ne_rope_attn_decode_workspace_bytes",
-           "ne_rope_attn_decode", "ne_rope_attn_fwd_ex", "ne_rope_attn_bwd_ex",
-           "ne_qkv_rope_workspace_bytes", "ne_qkv_rope_proj",
+           "ne_rope_attn_decode", "ne_qkv_rope_workspace_bytes", "ne_qkv_rope_proj",
            "ne_status_str", "ne_last_error", "ne_abi_version")
 
 
@@ -59,43 +61,34 @@ def lib():
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m causal_gqa_flashattention_rope_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
-    vp, i, sz, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
-    L.ne_rope_attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
-    L.ne_rope_attn_fwd_workspace_bytes.restype = sz
-    L.ne_rope_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
-    L.ne_rope_attn_bwd_workspace_bytes.restype = sz
-    L.ne_rope_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp, sz, vp]
+    vp, i, sz, d, u = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double, ctypes.c_uint
+    op = ctypes.POINTER(AttnOpts)
+    evp = ctypes.POINTER(vp)
+    L.ne_rope_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, d, i, u]
+    L.ne_rope_attn_workspace_bytes.restype = sz
+    L.ne_rope_table_init.argtypes = [vp, sz, i, i, d, vp]
+    L.ne_rope_table_init.restype = i
+    L.ne_rope_table_check.argtypes = [vp, sz, i, i, d, vp]
+    L.ne_rope_table_check.restype = i
+    L.ne_rope_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, u, vp, sz, vp]
     L.ne_rope_attn_fwd.restype = i
-    L.ne_rope_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, vp, sz, vp]
+    L.ne_rope_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, u, vp, sz, vp]
     L.ne_rope_attn_bwd.restype = i
-    L.ne_rope_attn_fwd_timed.argtypes = L.ne_rope_attn_fwd.argtypes + [ctypes.POINTER(vp)]
-    L.ne_rope_attn_fwd_timed.restype = i
-    L.ne_rope_attn_bwd_timed.argtypes = L.ne_rope_attn_bwd.argtypes + [ctypes.POINTER(vp)]
-    L.ne_rope_attn_bwd_timed.restype = i
-    L.ne_rope_attn_fwd_window.argtypes = ([vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, i, vp, sz, vp]
-                                          + [ctypes.POINTER(vp)])
-    L.ne_rope_attn_fwd_window.restype = i
-    L.ne_rope_attn_bwd_window.argtypes = ([vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, i, i, i, vp, sz, vp]
-                                          + [ctypes.POINTER(vp)])
-    L.ne_rope_attn_bwd_window.restype = i
+    L.ne_rope_attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, d, op, i, i, u, vp, sz, vp, evp]
+    L.ne_rope_attn_fwd_ex.restype = i
+    L.ne_rope_attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, op, i, i, u, vp, sz, vp, evp]
+    L.ne_rope_attn_bwd_ex.restype = i
     L.ne_kv_cache_bytes.argtypes = [i, i, i, i, i]
     L.ne_kv_cache_bytes.restype = sz
-    op = ctypes.POINTER(AttnOpts)
-    L.ne_rope_attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, d, op, i, i, vp, sz, vp, ctypes.POINTER(vp)]
-    L.ne_rope_attn_fwd_ex.restype = i
-    L.ne_rope_attn_bwd_ex.argtypes = ([vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, d, op, i, i, vp, sz, vp]
-                                      + [ctypes.POINTER(vp)])
-    L.ne_rope_attn_bwd_ex.restype = i
     L.ne_kv_cache_append.argtypes = [vp, sz, vp, vp, vp, i, i, i, i, i, d, op, i, vp]
     L.ne_kv_cache_append.restype = i
     L.ne_rope_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.ne_rope_attn_decode_workspace_bytes.restype = sz
-    L.ne_rope_attn_decode.argtypes = ([vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, d, op, i, i, vp, sz, vp]
-                                      + [ctypes.POINTER(vp)])
+    L.ne_rope_attn_decode.argtypes = [vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, d, op, i, i, vp, sz, vp, evp]
     L.ne_rope_attn_decode.restype = i
     L.ne_qkv_rope_workspace_bytes.argtypes = [i, i]
     L.ne_qkv_rope_workspace_bytes.restype = sz
-    L.ne_qkv_rope_proj.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, d, op, i, i, vp, sz, vp, ctypes.POINTER(vp)]
+    L.ne_qkv_rope_proj.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, d, op, i, i, vp, sz, vp, evp]
     L.ne_qkv_rope_proj.restype = i
     L.ne_status_str.argtypes = [i]
     L.ne_status_str.restype = ctypes.c_char_p
@@ -136,16 +129,38 @@ def _require_gpu(*ts):
             raise ValueError("tensors must be contiguous [B, T, H, D]")
 
 
-def fwd_workspace_bytes(B, T, Hq, Hkv, D, in_dtype):
-    return int(lib().ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, _DT[in_dtype]))
+def _nbytes(t):
+    return t.numel() * t.element_size()
 
 
-def bwd_workspace_bytes(B, T, Hq, Hkv, D, in_dtype):
-    return int(lib().ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, _DT[in_dtype]))
+def workspace_bytes(is_bwd, B, T, Hq, Hkv, D, rope_base, in_dtype, flags=0):
+    return int(lib().ne_rope_attn_workspace_bytes(int(bool(is_bwd)), B, T, Hq, Hkv, D, float(rope_base),
+                                                  _DT[in_dtype], int(flags)))
 
 
 def alloc_workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def ne_rope_table_init(workspace, T, D, rope_base):
+    """Build the RoPE table of T positions in the workspace (once per workspace and arguments)."""
+    _require_gpu(workspace)
+    _check(lib().ne_rope_table_init(_ptr(workspace), _nbytes(workspace), T, D, float(rope_base), _stream()))
+    return workspace
+
+
+def ne_rope_table_check(workspace, T, D, rope_base):
+    """The status of the workspace's table for (T, D, rope_base): 0 (NE_OK) or 6 (NE_ERR_NO_ROPE_TABLE).
+    Synchronises the current stream."""
+    _require_gpu(workspace)
+    return int(lib().ne_rope_table_check(_ptr(workspace), _nbytes(workspace), T, D, float(rope_base), _stream()))
+
+
+def new_workspace(is_bwd, q, k, rope_base, flags=0):
+    """A workspace for these tensors with its RoPE table built."""
+    B, T, Hq, Hkv, D = _dims(q, k)
+    ws = alloc_workspace(workspace_bytes(is_bwd, B, T, Hq, Hkv, D, rope_base, q.dtype, flags), q.device)
+    return ne_rope_table_init(ws, T, D, rope_base)
 
 
 def _events_arg(events, n):
@@ -166,74 +181,41 @@ def _events_arg(events, n):
     return (ctypes.c_void_p * n)(*handles)
 
 
-def ne_rope_attn_fwd(q, k, v, rope_base, out_dtype=torch.float32, o=None, lse=None, workspace=None,
-                     events=None):
+def ne_rope_attn_fwd(q, k, v, rope_base, out_dtype=torch.float32, o=None, lse=None, workspace=None, flags=0,
+                     window=0, qk_norm=None, events=None):
     """o, lse = attention forward.  q [B,T,Hq,D], k/v [B,T,Hkv,D] of one dtype.
 
-    events: optional 4 torch.cuda.Event(enable_timing=True) (or None) recorded around the two
-    kernels."""
-    return _fwd(q, k, v, rope_base, None, out_dtype, o, lse, workspace, events)
-
-
-def ne_rope_attn_fwd_ex(q, k, v, rope_base, window=0, qk_norm=None, out_dtype=torch.float32, o=None, lse=None,
-                        workspace=None, events=None):
-    """Forward with every option: window (<= 0: causal prefix), qk_norm None or (gain, eps)."""
-    return _fwd(q, k, v, rope_base, make_opts(window, qk_norm), out_dtype, o, lse, workspace, events)
-
-
-def ne_rope_attn_fwd_window(q, k, v, rope_base, window, out_dtype=torch.float32, o=None, lse=None,
-                            workspace=None, events=None):
-    """Sliding-window forward: query t sees keys t - window + 1 .. t (window <= 0: causal prefix)."""
-    return _fwd(q, k, v, rope_base, int(window), out_dtype, o, lse, workspace, events)
-
-
-def _fwd(q, k, v, rope_base, window, out_dtype, o, lse, workspace, events):
+    workspace: None (a new one, its table built here) or one whose table ne_rope_table_init built.
+    window / qk_norm / events select ne_rope_attn_fwd_ex (events: 4 torch.cuda.Event or None)."""
     _require_gpu(q, k, v)
     B, T, Hq, Hkv, D = _dims(q, k)
     if o is None:
         o = torch.empty((B, T, Hq, D), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
-    need = fwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype)
     if workspace is None:
-        workspace = alloc_workspace(need, q.device)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D, float(rope_base),
-            _DT[q.dtype], _DT[o.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
-            _stream())
-    ev = _events_arg(events, 4)
-    if isinstance(window, AttnOpts):
-        _check(lib().ne_rope_attn_fwd_ex(*args[:11], ctypes.byref(window), *args[11:], ev))
-    elif window is not None:
-        _check(lib().ne_rope_attn_fwd_window(*args[:11], window, *args[11:], ev))
-    elif ev is None:
-        _check(lib().ne_rope_attn_fwd(*args))
+        workspace = new_workspace(False, q, k, rope_base, flags)
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D, float(rope_base))
+    tail = (_DT[q.dtype], _DT[o.dtype], int(flags), _ptr(workspace), _nbytes(workspace), _stream())
+    if window or qk_norm is not None or events is not None:
+        opts = make_opts(window, qk_norm)
+        _check(lib().ne_rope_attn_fwd_ex(*head, ctypes.byref(opts), *tail, _events_arg(events, 4)))
     else:
-        _check(lib().ne_rope_attn_fwd_timed(*args, ev))
+        _check(lib().ne_rope_attn_fwd(*head, *tail))
     return o, lse
 
 
-def ne_rope_attn_bwd(q, k, v, o, lse, dO, rope_base, dq=None, dk=None, dv=None, workspace=None,
-                     events=None):
-    """dq, dk, dv = attention backward (out dtype = o's dtype).
-
-    events: optional 6 torch.cuda.Event(enable_timing=True) (or None) recorded around the three
-    kernels."""
-    return _bwd(q, k, v, o, lse, dO, rope_base, None, dq, dk, dv, workspace, events)
+def ne_rope_attn_fwd_ex(q, k, v, rope_base, window=0, qk_norm=None, **kw):
+    """Forward with every option: window (<= 0: causal prefix), qk_norm None or (gain, eps)."""
+    return ne_rope_attn_fwd(q, k, v, rope_base, window=window, qk_norm=qk_norm, **kw)
 
 
-def ne_rope_attn_bwd_window(q, k, v, o, lse, dO, rope_base, window, dq=None, dk=None, dv=None,
-                            workspace=None, events=None):
-    """Sliding-window backward; `window` must be the one the forward used."""
-    return _bwd(q, k, v, o, lse, dO, rope_base, int(window), dq, dk, dv, workspace, events)
+def ne_rope_attn_bwd(q, k, v, o, lse, dO, rope_base, dq=None, dk=None, dv=None, workspace=None, flags=0,
+                     window=0, qk_norm=None, events=None):
+    """dq, dk, dv = attention backward (out dtype = o's dtype); window / qk_norm must be the forward's.
 
-
-def ne_rope_attn_bwd_ex(q, k, v, o, lse, dO, rope_base, window=0, qk_norm=None, dq=None, dk=None, dv=None,
-                        workspace=None, events=None):
-    """Backward with every option; the options must be the forward's."""
-    return _bwd(q, k, v, o, lse, dO, rope_base, make_opts(window, qk_norm), dq, dk, dv, workspace, events)
-
-
-def _bwd(q, k, v, o, lse, dO, rope_base, window, dq, dk, dv, workspace, events):
+    workspace: None (a new one sized for `flags`, its table built here) or one sized with the same flags
+    whose table ne_rope_table_init built.  events: 6 torch.cuda.Event or None."""
     _require_gpu(q, k, v, o, lse, dO)
     B, T, Hq, Hkv, D = _dims(q, k)
     if dq is None:
@@ -242,22 +224,22 @@ def _bwd(q, k, v, o, lse, dO, rope_base, window, dq, dk, dv, workspace, events):
         dk = torch.empty((B, T, Hkv, D), dtype=o.dtype, device=q.device)
     if dv is None:
         dv = torch.empty((B, T, Hkv, D), dtype=o.dtype, device=q.device)
-    need = bwd_workspace_bytes(B, T, Hq, Hkv, D, q.dtype)
     if workspace is None:
-        workspace = alloc_workspace(need, q.device)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
-            B, T, Hq, Hkv, D, float(rope_base), _DT[q.dtype], _DT[o.dtype], _ptr(workspace),
-            workspace.numel() * workspace.element_size(), _stream())
-    ev = _events_arg(events, 6)
-    if isinstance(window, AttnOpts):
-        _check(lib().ne_rope_attn_bwd_ex(*args[:15], ctypes.byref(window), *args[15:], ev))
-    elif window is not None:
-        _check(lib().ne_rope_attn_bwd_window(*args[:15], window, *args[15:], ev))
-    elif ev is None:
-        _check(lib().ne_rope_attn_bwd(*args))
+        workspace = new_workspace(True, q, k, rope_base, flags)
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, T, Hq, Hkv, D, float(rope_base))
+    tail = (_DT[q.dtype], _DT[o.dtype], int(flags), _ptr(workspace), _nbytes(workspace), _stream())
+    if window or qk_norm is not None or events is not None:
+        opts = make_opts(window, qk_norm)
+        _check(lib().ne_rope_attn_bwd_ex(*head, ctypes.byref(opts), *tail, _events_arg(events, 6)))
     else:
-        _check(lib().ne_rope_attn_bwd_timed(*args, ev))
+        _check(lib().ne_rope_attn_bwd(*head, *tail))
     return dq, dk, dv
+
+
+def ne_rope_attn_bwd_ex(q, k, v, o, lse, dO, rope_base, window=0, qk_norm=None, **kw):
+    """Backward with every option; the options must be the forward's."""
+    return ne_rope_attn_bwd(q, k, v, o, lse, dO, rope_base, window=window, qk_norm=qk_norm, **kw)
 
 
 # ---------------------------------------------------------------------------------------------

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <initializer_list>
 
 #include "ne_launch.hpp"
 
@@ -29,8 +30,10 @@ constexpr size_t kAlign = 256;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t qh, kh, vh, dOh, delta, lse2, rq, rk, table, ds, total;
-    int ds_groups;  // groups per stored-dS batch (0: none)
+    size_t table, qh, kh, vh, dOh, delta, lse2, rq, rk, dsc, amax, dqacc, ds, total;
+    int mode;       // ne::kBwdRecompute, kBwdStoredDs or kBwdAtomic (backward)
+    int ds_groups;  // stored dS: groups whose dS the workspace holds at once
+    int nparts;     // partial maxima of |dO| per group (16-bit backward)
 };
 
 bool dtype_ok(ne_dtype_t in, ne_dtype_t out) {
@@ -38,6 +41,18 @@ bool dtype_ok(ne_dtype_t in, ne_dtype_t out) {
     if (in == NE_BF16) return out == NE_F32 || out == NE_BF16;
     if (in == NE_F16) return out == NE_F32 || out == NE_F16;
     return false;
+}
+
+constexpr unsigned kKnownFlags = NE_FLAG_NONDETERMINISTIC | NE_FLAG_BF16_OPERANDS | NE_FLAG_ROPE_HALF_SPLIT |
+                                 NE_FLAG_STORE_DS;
+
+ne_status_t check_flags(unsigned flags) {
+    if (flags & ~kKnownFlags) return fail(NE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+    if (flags & NE_FLAG_BF16_OPERANDS)
+        return fail(NE_ERR_UNSUPPORTED, "NE_FLAG_BF16_OPERANDS is reserved and not implemented (fp16 operands only)");
+    if (flags & NE_FLAG_ROPE_HALF_SPLIT)
+        return fail(NE_ERR_UNSUPPORTED, "NE_FLAG_ROPE_HALF_SPLIT is reserved and not implemented (adjacent pairs only)");
+    return NE_OK;
 }
 
 // esz: bytes of a kernel operand element (4 on the fp32 path, 2 otherwise).  The direct LDS loads
@@ -66,39 +81,59 @@ size_t ds_group_bytes(int T, int Hq, int Hkv) {
     const int nrt = (int)(((int64_t)T * G + 63) / 64), nkb = (T + 63) / 64;
     return ne::ds_tiles_per_group(nrt, nkb, G) * 8192;
 }
+constexpr size_t kDsCap = (size_t)4 << 30;   // the stored dS buffer holds at most 4 GiB
 
-// Groups whose dS the 16-bit backward's buffer holds at once: as many as fit 4 GiB, or the byte
-// count in the environment variable NE_ROPE_ATTN_DS_MAX_BYTES (read at every call; 0 turns the
-// stored dS off), at most B * Hkv; the dK/dV and dQ passes run once per batch of that many groups.
-// 0 (fp32 path, or a single group's dS above the cap): dQ recomputes S and dP instead.
-int ds_batch_groups(int B, int T, int Hq, int Hkv, ne_dtype_t in) {
-    if (in == NE_F32) return 0;
-    size_t cap = (size_t)4 << 30;
-    if (const char* e = std::getenv("NE_ROPE_ATTN_DS_MAX_BYTES"); e && *e) cap = (size_t)std::strtoull(e, nullptr, 10);
-    return (int)std::min<size_t>((size_t)B * Hkv, cap / ds_group_bytes(T, Hq, Hkv));
+// Partial maxima of |dO| per group: enough parts for about 512 workgroups, at most 64 and T.
+int amax_parts(int B, int T, int Hkv) {
+    const int64_t g = (int64_t)B * Hkv;
+    return (int)std::max<int64_t>(1, std::min<int64_t>({64, (int64_t)T, std::max<int64_t>(16, (512 + g - 1) / g)}));
 }
 
-Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, ne_dtype_t in) {
+int bwd_mode(ne_dtype_t in, unsigned flags, int T, int Hq, int Hkv) {
+    if (in == NE_F32) return ne::kBwdRecompute;
+    if (flags & NE_FLAG_NONDETERMINISTIC) return ne::kBwdAtomic;
+    if ((flags & NE_FLAG_STORE_DS) && ds_group_bytes(T, Hq, Hkv) <= kDsCap) return ne::kBwdStoredDs;
+    return ne::kBwdRecompute;
+}
+
+// The workspace regions.  ds_bytes: bytes available for the stored dS (stored-dS mode), or
+// SIZE_MAX to size it for every group (up to the cap).
+Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, double base, ne_dtype_t in, unsigned flags,
+              size_t ws_bytes = SIZE_MAX) {
     const size_t esz = in == NE_F32 ? 4 : 2;
     const size_t nq = (size_t)B * T * Hq * D, nk = (size_t)B * T * Hkv * D;
     Layout L{};
-    size_t off = 0;
+    L.mode = bwd ? bwd_mode(in, flags, T, Hq, Hkv) : ne::kBwdRecompute;
+    size_t off = ne::kTableHdrBytes;
+    L.table = off;
+    if (base > 0.0) off += up((size_t)T * (D / 2) * 8);
     if (bwd) { L.qh = off; off += up(nq * esz); }
     // the forward keeps V'^T as [B * Hkv][D][Tp], Tp = T rounded up to 64 (zeros past T)
     const size_t nv = bwd ? nk : (size_t)B * Hkv * D * (((size_t)T + 63) / 64 * 64);
-    L.ds_groups = bwd ? ds_batch_groups(B, T, Hq, Hkv, in) : 0;
     L.kh = off; off += up(nk * esz);
     L.vh = off;
-    if (L.ds_groups == 0) off += up(nv * esz);  // the stored-dS backward reads v itself
+    if (!bwd || L.mode == ne::kBwdRecompute) off += up(nv * esz);  // the other backwards read v directly
     if (bwd) {
+        const size_t ngrp = (size_t)B * Hkv;
+        L.nparts = amax_parts(B, T, Hkv);
         L.dOh = off; off += up(nq * esz);
         L.delta = off; off += up((size_t)B * T * Hq * 4);
         L.lse2 = off; off += up((size_t)B * T * Hq * 4);
         L.rq = off; off += up((size_t)B * T * Hq * 4);
         L.rk = off; off += up((size_t)B * T * Hkv * 4);
+        L.dsc = off; off += up(ngrp * 4);
+        L.amax = off; off += up(ngrp * L.nparts * 4);
+        // the atomic dQ accumulator, plus 64 rows past the last group that the dK/dV pass may add zeros to
+        if (L.mode == ne::kBwdAtomic) { L.dqacc = off; off += up((nq + (size_t)64 * D) * 4); }
+        if (L.mode == ne::kBwdStoredDs) {
+            const size_t gb = ds_group_bytes(T, Hq, Hkv);
+            size_t cap = kDsCap;
+            if (ws_bytes != SIZE_MAX) cap = std::min(cap, ws_bytes > off ? (ws_bytes - off) / 256 * 256 : 0);
+            L.ds_groups = (int)std::min<size_t>(ngrp, cap / gb);
+            L.ds = off;
+            off += up((size_t)std::max(L.ds_groups, 1) * gb);
+        }
     }
-    L.table = off; off += up((size_t)T * (D / 2) * 8);
-    if (L.ds_groups > 0) { L.ds = off; off += up((size_t)L.ds_groups * ds_group_bytes(T, Hq, Hkv)); }
     L.total = off;
     return L;
 }
@@ -119,12 +154,12 @@ ne_status_t check_opts(const ne_attn_opts_t* o, ne::QkNorm* qkn) {
     return NE_OK;
 }
 
-ne_status_t common_checks(int B, int T, int Hq, int Hkv, int D, ne_dtype_t in, ne_dtype_t out) {
+ne_status_t common_checks(int B, int T, int Hq, int Hkv, int D, ne_dtype_t in, ne_dtype_t out, unsigned flags) {
     ne_status_t s = check_shape(B, T, Hq, Hkv, D, in == NE_F32 ? 4 : 2);
     if (s != NE_OK) return s;
     if (!dtype_ok(in, out))
         return fail(NE_ERR_UNSUPPORTED, "dtype pair in=%d out=%d is not supported", (int)in, (int)out);
-    return NE_OK;
+    return check_flags(flags);
 }
 
 }  // namespace
@@ -140,24 +175,58 @@ const char* ne_status_str(ne_status_t s) {
         case NE_OK: return "ok";
         case NE_ERR_NULL: return "null pointer";
         case NE_ERR_SHAPE: return "invalid shape";
-        case NE_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+        case NE_ERR_UNSUPPORTED: return "unsupported head_dim, dtype or flag";
         case NE_ERR_ALIGN: return "pointer not 16-byte aligned";
         case NE_ERR_WORKSPACE: return "workspace too small";
+        case NE_ERR_NO_ROPE_TABLE: return "no RoPE table for these arguments in the workspace";
         case NE_ERR_HIP: return "HIP runtime error";
     }
     return "unknown status";
 }
 
-size_t ne_rope_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim, ne_dtype_t in_dtype) {
+size_t ne_rope_attn_workspace_bytes(int is_bwd, int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
+                                    ne_dtype_t in_dtype, unsigned flags) {
     if (in_dtype != NE_F32 && in_dtype != NE_BF16 && in_dtype != NE_F16) return 0;
     if (check_shape(B, T, Hq, Hkv, head_dim, in_dtype == NE_F32 ? 4 : 2) != NE_OK) return 0;
-    return layout(false, B, T, Hq, Hkv, head_dim, in_dtype).total;
+    if (check_flags(flags) != NE_OK || !std::isfinite(rope_base)) return 0;
+    return layout(is_bwd != 0, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, flags).total;
 }
 
-size_t ne_rope_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim, ne_dtype_t in_dtype) {
-    if (in_dtype != NE_F32 && in_dtype != NE_BF16 && in_dtype != NE_F16) return 0;
-    if (check_shape(B, T, Hq, Hkv, head_dim, in_dtype == NE_F32 ? 4 : 2) != NE_OK) return 0;
-    return layout(true, B, T, Hq, Hkv, head_dim, in_dtype).total;
+ne_status_t ne_rope_table_init(void* workspace, size_t workspace_bytes, int T, int head_dim, double rope_base,
+                               void* stream) {
+    if (!std::isfinite(rope_base)) return fail(NE_ERR_SHAPE, "rope_base must be finite");
+    if (!(rope_base > 0.0)) return NE_OK;
+    if (!workspace) return fail(NE_ERR_NULL, "ne_rope_table_init: workspace must be non-null");
+    if (!aligned16(workspace)) return fail(NE_ERR_ALIGN, "ne_rope_table_init: workspace must be 16-byte aligned");
+    if (T < 1 || T > (1 << 30)) return fail(NE_ERR_SHAPE, "T=%d must be in [1, 2^30]", T);
+    if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+        return fail(NE_ERR_UNSUPPORTED, "head_dim=%d not in {32, 64, 128}", head_dim);
+    const size_t need = ne::kTableHdrBytes + (size_t)T * (head_dim / 2) * 8;
+    if (workspace_bytes < need)
+        return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes < %zu for the table", workspace_bytes, need);
+    ne::TableArgs a{};
+    a.hdr = (ne::TableHdr*)workspace;
+    a.table = (float2*)((char*)workspace + ne::kTableHdrBytes);
+    a.T = T; a.D = head_dim; a.base = rope_base;
+    hipError_t e = ne::launch_table(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_table_init: launch failed: %s", hipGetErrorString(e));
+    return NE_OK;
+}
+
+ne_status_t ne_rope_table_check(const void* workspace, size_t workspace_bytes, int T, int head_dim, double rope_base,
+                                void* stream) {
+    if (!(rope_base > 0.0)) return NE_OK;
+    if (!workspace) return fail(NE_ERR_NULL, "ne_rope_table_check: workspace must be non-null");
+    if (workspace_bytes < ne::kTableHdrBytes)
+        return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes holds no table header", workspace_bytes);
+    ne::TableHdr h{};
+    hipError_t e = hipMemcpyAsync(&h, workspace, sizeof(h), hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_table_check: copy failed: %s", hipGetErrorString(e));
+    if (!ne::table_matches(h, T, head_dim, rope_base))
+        return fail(NE_ERR_NO_ROPE_TABLE, "the workspace table is not built for T=%d head_dim=%d rope_base=%g", T,
+                    head_dim, rope_base);
+    return NE_OK;
 }
 
 }  // extern "C"
@@ -166,11 +235,11 @@ namespace {
 
 ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int T, int Hq, int Hkv, int head_dim, double rope_base, const ne_attn_opts_t* opts,
-                     ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                     ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                      void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     if (!q || !k || !v || !o || !lse || !workspace)
         return fail(NE_ERR_NULL, "ne_rope_attn_fwd: q, k, v, o, lse and workspace must be non-null");
-    ne_status_t s = common_checks(B, T, Hq, Hkv, head_dim, in_dtype, out_dtype);
+    ne_status_t s = common_checks(B, T, Hq, Hkv, head_dim, in_dtype, out_dtype, flags);
     if (s != NE_OK) return s;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
         !aligned16(workspace))
@@ -179,7 +248,7 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     if (!opts) opts = &kNoOpts;
     ne::QkNorm qkn{};
     if ((s = check_opts(opts, &qkn)) != NE_OK) return s;
-    const Layout L = layout(false, B, T, Hq, Hkv, head_dim, in_dtype);
+    const Layout L = layout(false, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, flags);
     if (workspace_bytes < L.total)
         return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
     char* ws = (char*)workspace;
@@ -187,6 +256,7 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     ne::PrepArgs pa{};
     pa.q = q; pa.k = k; pa.v = v;
     pa.kh = ws + L.kh; pa.vh = ws + L.vh; pa.table = (float2*)(ws + L.table);
+    pa.hdr = (const ne::TableHdr*)ws;
     pa.B = B; pa.T = T; pa.Hq = Hq; pa.Hkv = Hkv; pa.D = head_dim;
     pa.rope_base = rope_base;
     pa.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
@@ -207,11 +277,11 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
 ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* dO, void* dq, void* dk, void* dv,
                      int B, int T, int Hq, int Hkv, int head_dim, double rope_base, const ne_attn_opts_t* opts,
-                     ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                     ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                      void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
         return fail(NE_ERR_NULL, "ne_rope_attn_bwd: every tensor pointer and the workspace must be non-null");
-    ne_status_t s = common_checks(B, T, Hq, Hkv, head_dim, in_dtype, out_dtype);
+    ne_status_t s = common_checks(B, T, Hq, Hkv, head_dim, in_dtype, out_dtype, flags);
     if (s != NE_OK) return s;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
         !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
@@ -220,20 +290,34 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     if (!opts) opts = &kNoOpts;
     ne::QkNorm qkn{};
     if ((s = check_opts(opts, &qkn)) != NE_OK) return s;
-    const Layout L = layout(true, B, T, Hq, Hkv, head_dim, in_dtype);
+    const Layout L = layout(true, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, flags, workspace_bytes);
+    if (L.mode == ne::kBwdStoredDs && L.ds_groups < 1)
+        return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes holds the stored dS of no group (%zu required)",
+                    workspace_bytes, L.total);
     if (workspace_bytes < L.total)
         return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
     char* ws = (char*)workspace;
     const int G = Hq / Hkv;
+    const bool h16 = in_dtype != NE_F32;
     ne::PrepArgs pa{};
     pa.q = q; pa.k = k; pa.v = v; pa.o = o; pa.lse = lse; pa.dO = dO;
     pa.qh = ws + L.qh; pa.kh = ws + L.kh; pa.vh = ws + L.vh; pa.dOh = ws + L.dOh;
     pa.delta = (float*)(ws + L.delta); pa.lse2 = (float*)(ws + L.lse2); pa.table = (float2*)(ws + L.table);
     pa.rq = (float*)(ws + L.rq); pa.rk = (float*)(ws + L.rk);
+    pa.hdr = (const ne::TableHdr*)ws;
     pa.B = B; pa.T = T; pa.Hq = Hq; pa.Hkv = Hkv; pa.D = head_dim;
     pa.rope_base = rope_base;
     pa.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
     pa.qkn = qkn;
+    pa.skip_v = L.mode != ne::kBwdRecompute ? 1 : 0;
+    pa.amax_part = (const float*)(ws + L.amax);
+    pa.nparts = L.nparts;
+    pa.dsc = h16 ? (float*)(ws + L.dsc) : nullptr;
+    pa.dq_acc = L.mode == ne::kBwdAtomic ? (float*)(ws + L.dqacc) : nullptr;
+    ne::AmaxArgs am{};
+    am.dO = dO; am.part = (float*)(ws + L.amax);
+    am.B = B; am.T = T; am.Hq = Hq; am.Hkv = Hkv; am.nparts = L.nparts;
+    am.tpp = (T + L.nparts - 1) / L.nparts;
     ne::BwdArgs ba{};
     ba.qh = pa.qh; ba.kh = pa.kh; ba.vh = pa.vh; ba.dOh = pa.dOh;
     ba.delta = pa.delta; ba.lse2 = pa.lse2; ba.table = pa.table;
@@ -243,8 +327,9 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     ba.qkn = qkn;
     ba.q = q; ba.k = k; ba.in_dt = (int)in_dtype;
     ba.rq = pa.rq; ba.rk = pa.rk;
-    ba.ds = L.ds_groups > 0 ? ws + L.ds : nullptr;
-    pa.skip_v = L.ds_groups > 0 ? 1 : 0;
+    ba.ds = L.mode == ne::kBwdStoredDs ? ws + L.ds : nullptr;
+    ba.dsc = pa.dsc;
+    ba.dq_acc = pa.dq_acc;
     ba.v = v;
     ba.ds_groups = L.ds_groups;
     ba.grp0 = 0;
@@ -252,7 +337,7 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     ba.nrb = (int)(((int64_t)T * G + 127) / 128);
     ba.rope_base = rope_base;
     ba.scale = (float)(1.0 / std::sqrt((double)head_dim));
-    hipError_t e = ne::launch_bwd((int)in_dtype, (int)out_dtype, head_dim, pa, ba, (hipStream_t)stream,
+    hipError_t e = ne::launch_bwd((int)in_dtype, (int)out_dtype, head_dim, L.mode, pa, am, ba, (hipStream_t)stream,
                                   (hipEvent_t const*)events);
     if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_attn_bwd: launch failed: %s", hipGetErrorString(e));
     return NE_OK;
@@ -264,78 +349,36 @@ extern "C" {
 
 ne_status_t ne_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                              int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, nullptr, in_dtype, out_dtype, workspace,
-                    workspace_bytes, stream, nullptr);
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, nullptr, in_dtype, out_dtype, flags,
+                    workspace, workspace_bytes, stream, nullptr);
 }
 
 ne_status_t ne_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                              const void* dO, void* dq, void* dk, void* dv,
                              int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                              void* workspace, size_t workspace_bytes, void* stream) {
     return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, nullptr, in_dtype,
-                    out_dtype, workspace, workspace_bytes, stream, nullptr);
-}
-
-ne_status_t ne_rope_attn_fwd_timed(const void* q, const void* k, const void* v, void* o, float* lse,
-                                   int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                                   ne_dtype_t in_dtype, ne_dtype_t out_dtype,
-                                   void* workspace, size_t workspace_bytes, void* stream,
-                                   void* const* events) {
-    if (!events) return fail(NE_ERR_NULL, "ne_rope_attn_fwd_timed: events must be non-null");
-    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, nullptr, in_dtype, out_dtype, workspace,
-                    workspace_bytes, stream, events);
-}
-
-ne_status_t ne_rope_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                                   const void* dO, void* dq, void* dk, void* dv,
-                                   int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                                   ne_dtype_t in_dtype, ne_dtype_t out_dtype,
-                                   void* workspace, size_t workspace_bytes, void* stream,
-                                   void* const* events) {
-    if (!events) return fail(NE_ERR_NULL, "ne_rope_attn_bwd_timed: events must be non-null");
-    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, nullptr, in_dtype,
-                    out_dtype, workspace, workspace_bytes, stream, events);
-}
-
-ne_status_t ne_rope_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
-                                    int B, int T, int Hq, int Hkv, int head_dim, double rope_base, int window,
-                                    ne_dtype_t in_dtype, ne_dtype_t out_dtype,
-                                    void* workspace, size_t workspace_bytes, void* stream,
-                                    void* const* events) {
-    const ne_attn_opts_t opts = {window, 0, 1.0f, 0.0f};
-    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, &opts, in_dtype, out_dtype,
-                    workspace, workspace_bytes, stream, events);
+                    out_dtype, flags, workspace, workspace_bytes, stream, nullptr);
 }
 
 ne_status_t ne_rope_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                                const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                                 void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
-    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, opts, in_dtype, out_dtype,
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, opts, in_dtype, out_dtype, flags,
                     workspace, workspace_bytes, stream, events);
 }
 
 ne_status_t ne_rope_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                 const void* dO, void* dq, void* dk, void* dv,
                                 int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                                const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                                 void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, opts, in_dtype,
-                    out_dtype, workspace, workspace_bytes, stream, events);
-}
-
-ne_status_t ne_rope_attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
-                                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                                    int B, int T, int Hq, int Hkv, int head_dim, double rope_base, int window,
-                                    ne_dtype_t in_dtype, ne_dtype_t out_dtype,
-                                    void* workspace, size_t workspace_bytes, void* stream,
-                                    void* const* events) {
-    const ne_attn_opts_t opts = {window, 0, 1.0f, 0.0f};
-    return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, &opts, in_dtype,
-                    out_dtype, workspace, workspace_bytes, stream, events);
+                    out_dtype, flags, workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -357,6 +357,15 @@ __device__ __forceinline__ void lds_fill_wait_keep(int n) {
     __syncthreads();
 }
 
+// The same for a wave that issued n = 0, 16 or 32 other vector-memory operations (atomic adds)
+// after its share of the fill being waited for.
+__device__ __forceinline__ void lds_fill_wait_keep_atomics(int n) {
+    if (n == 32) wait_vmcnt<32>();
+    else if (n == 16) wait_vmcnt<16>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+}
+
 // Transposed f16 fragment from a swizzled tile (same meaning as tr_frag_f16).
 template <int D>
 __device__ __forceinline__ half8 tr_frag_f16_sw(const _Float16* tile, int kk, int col0) {

@@ -51,16 +51,28 @@ __device__ __forceinline__ float2 rope_cs_at(int t, double theta) {
     sincosf((float)r, &sv, &cv);
     return make_float2(cv, sv);
 }
-template <int D>
-__device__ __forceinline__ void rope_cs_fill(float2* cs, double* theta, int t0, int TT, int T, double base) {
-    for (int i = threadIdx.x; i < D / 2; i += blockDim.x)
-        theta[i] = base > 0.0 ? exp2(-2.0 * (double)i / (double)D * log2(base)) : 0.0;
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < TT * (D / 2); idx += blockDim.x) {
-        const int tl = idx / (D / 2), i = idx % (D / 2);
-        const int t = t0 + tl;
-        cs[idx] = base > 0.0 && t < T ? rope_cs_at(t, theta[i]) : make_float2(1.f, 0.f);
+// The RoPE table of positions 0 .. T-1, each entry evaluated directly, and its header.
+// grid ceil(T D / 2 / 256), 256 threads.
+__global__ __launch_bounds__(256) void rope_table_kernel(TableArgs a) {
+    const int half = a.D / 2;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx < a.T * half) {
+        const int t = idx / half, i = idx % half;
+        const double theta = exp2(-2.0 * (double)i / (double)a.D * log2(a.base));
+        a.table[idx] = rope_cs_at(t, theta);
     }
+    if (idx == 0) {
+        TableHdr h{};
+        h.magic = kTableMagic; h.T = a.T; h.D = a.D; h.pad = 0; h.base = a.base;
+        *a.hdr = h;
+    }
+}
+
+// 1 when the workspace's table was built for this call's (T, D, base) or RoPE is off, else NaN: the
+// preparation kernels multiply their rotated copies by it, so a missing table shows as NaN outputs.
+__device__ __forceinline__ float table_guard(const PrepArgs& a) {
+    if (!(a.rope_base > 0.0)) return 1.f;
+    return table_matches(*a.hdr, a.T, a.D, a.rope_base) ? 1.f : __builtin_nanf("");
 }
 
 // Eight consecutive input elements as fp32, with 16-byte loads.
@@ -75,6 +87,40 @@ __device__ __forceinline__ void load8(const T16* p, float (&x)[8]) {
     const v8 a = *reinterpret_cast<const v8*>(p);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+}
+
+// Partial maxima of |dO| for the per-group scale of dO (16-bit operands).  grid (nparts, B * Hkv),
+// 256 threads: block (p, g) reads tokens [p tpp, (p + 1) tpp) of the G heads of group g.
+template <typename TI, int D>
+__global__ __launch_bounds__(256) void dO_amax_kernel(AmaxArgs a) {
+    __shared__ float red[4];
+    const int g = blockIdx.y, p = blockIdx.x;
+    const int b = g / a.Hkv, hkv = g % a.Hkv, G = a.Hq / a.Hkv;
+    const int t0 = p * a.tpp, t1 = min(a.T, t0 + a.tpp);
+    constexpr int CPR = D / 8;
+    const int rows = max(0, t1 - t0) * G;
+    float m = 0.f;
+    for (int idx = threadIdx.x; idx < rows * CPR; idx += 256) {
+        const int r = idx / CPR, ch = idx % CPR;
+        const int t = t0 + r / G, hq = hkv * G + r % G;
+        float x[8];
+        load8((const TI*)a.dO + (((size_t)b * a.T + t) * a.Hq + hq) * D + ch * 8, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) a.part[(size_t)g * a.nparts + p] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// The power of two s that brings a group's max |dO| into [4, 8) (1 for an all-zero or non-finite
+// maximum): s dO is exact in fp32 and its fp16 rounding keeps the relative precision of every
+// normal element; gradients are linear in dO and are multiplied by 1 / s at the end.
+__device__ __forceinline__ float dO_scale(float amax) {
+    if (!(amax > 0.f) || !(amax < INFINITY)) return 1.f;
+    const int e = min(120, max(-120, 2 - ilogbf(amax)));
+    return ldexpf(1.f, e);
 }
 
 template <typename TI, typename OP, int D, bool ROT>
@@ -103,18 +149,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     constexpr int TT = 8;
     constexpr int CPR = D / 8;  // 8-element chunks per row
     __shared__ float2 cs[TT * (D / 2)];
-    __shared__ double theta[D / 2];
     const int t0 = blockIdx.x * TT, b = blockIdx.y;
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
     const bool rope = a.rope_base > 0.0;
-    rope_cs_fill<D>(cs, theta, t0, TT, T, a.rope_base);
-    __syncthreads();
-    if (b == 0 && rope) {
-        for (int idx = threadIdx.x; idx < TT * (D / 2); idx += blockDim.x) {
-            const int t = t0 + idx / (D / 2);
-            if (t < T) a.table[(size_t)t * (D / 2) + idx % (D / 2)] = cs[idx];
-        }
+    for (int idx = threadIdx.x; idx < TT * (D / 2); idx += blockDim.x) {
+        const int t = t0 + idx / (D / 2);
+        cs[idx] = rope && t < T ? a.table[(size_t)t * (D / 2) + idx % (D / 2)] : make_float2(1.f, 0.f);
     }
+    const float guard = table_guard(a);
+    __syncthreads();
     const int qrows = BWD ? Hq : 0;  // the forward rotates q inside the attention kernel
     const int skip_v = BWD && a.skip_v ? Hkv : 0;  // rows of v not copied
     const int rows_per_tok = qrows + 2 * Hkv - skip_v + (BWD ? Hq : 0);
@@ -132,6 +175,18 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         const float2* csr = cs + tl * (D / 2);
         float part = 0.f;  // Delta partial (dO rows only)
         int dO_row = -1;
+        // 16-bit operands: the power-of-two scale of this dO row's group, from the group's partial
+        // maxima (read by the row's CPR lanes together)
+        float sdo = 1.f;
+        if constexpr (BWD && sizeof(OP) == 2) {
+            float m = 0.f;
+            if (live && which >= Hq + 2 * Hkv) {
+                const size_t grp = (size_t)b * Hkv + (which - Hq - 2 * Hkv) / G;
+                for (int j = chunk; j < a.nparts; j += CPR) m = fmaxf(m, a.amax_part[grp * a.nparts + j]);
+            }
+            for (int off = 1; off < CPR; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            sdo = dO_scale(m);
+        }
         // QK norm: the factor gain / rms of this thread's q or k row (its CPR chunks sit in
         // consecutive lanes), and 1/rms kept for the backward's epilogues
         float fac = 1.f;
@@ -158,13 +213,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                 const int hq = which, g = hq / G, hh = hq % G;
                 const TI* src = (const TI*)a.q + (((size_t)b * T + t) * Hq + hq) * D + chunk * 8;
                 OP* dst = (OP*)a.qh + (((size_t)b * Hkv + g) * TG + (size_t)t * G + hh) * D + chunk * 8;
-                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, a.qscale * fac);
+                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, a.qscale * fac * guard);
                 else convert8<TI, OP, D, false>(src, dst, csr, chunk, a.qscale * fac);
             } else if (which < Hq + Hkv) {  // k -> k'
                 const int g = which - Hq;
                 const TI* src = (const TI*)a.k + (((size_t)b * T + t) * Hkv + g) * D + chunk * 8;
                 OP* dst = (OP*)a.kh + (((size_t)b * Hkv + g) * T + t) * D + chunk * 8;
-                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, fac);
+                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, fac * guard);
                 else convert8<TI, OP, D, false>(src, dst, csr, chunk, fac);
             } else if (which < Hq + 2 * Hkv) {  // v -> v'
                 const int g = which - Hq - Hkv;
@@ -182,8 +237,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
                 for (int e = 0; e < 8; ++e) {
                     const float x = to_f32(src[e]);
                     part += x * to_f32(osrc[e]);
-                    dst[e] = from_f32<OP>(x);
+                    dst[e] = from_f32<OP>(x * sdo);
                 }
+                if (a.dq_acc) {   // the atomic dQ accumulator starts at zero
+                    floatx4* acc = reinterpret_cast<floatx4*>(a.dq_acc + frow * D + chunk * 8);
+                    acc[0] = floatx4{};
+                    acc[1] = floatx4{};
+                }
+                if (a.dsc && t == 0 && hh == 0 && chunk == 0) a.dsc[(size_t)b * Hkv + g] = 1.f / sdo;
                 dO_row = (int)hq;
                 if (chunk == 0) a.lse2[frow] = a.lse[((size_t)b * Hq + hq) * T + t] * kLog2e;
             }
@@ -194,60 +255,29 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
             for (int off = 1; off < CPR; off <<= 1) part += __shfl_xor(part, off, 64);
             if (live && dO_row >= 0 && chunk == 0) {
                 const int g = dO_row / G, hh = dO_row % G;
-                a.delta[((size_t)b * Hkv + g) * TG + (size_t)t * G + hh] = part;
+                a.delta[((size_t)b * Hkv + g) * TG + (size_t)t * G + hh] = part * sdo;
             }
         }
     }
 }
 
 // Forward preparation for 16-bit operands.  grid (Tp / 64, B * Hkv, 2), 256 threads: 64 tokens of
-// one (batch, KV head) group; z = 0: k' = fp16(R(k)) rows as [group][T][D] and the cos/sin table
-// rows of these tokens (group 0); z = 1: v' = fp16(v) transposed to [group][D][Tp] with the key
+// one (batch, KV head) group; z = 0: k' = fp16(R(k)) rows as [group][T][D] with the cos/sin rows
+// of the workspace table; z = 1: v' = fp16(v) transposed to [group][D][Tp] with the key
 // order of vt_key_of_pos and zeros past T.
 template <typename TI, int D>
 __global__ __launch_bounds__(256) void prep_fwd_h(PrepArgs a) {
     constexpr int TB = 64, CPR = D / 8;
-    __shared__ float2 cs[TB * (D / 2)];
-    __shared__ double theta[D / 2];
     __shared__ _Float16 vts[D][TB + 8];                // v'^T of the 64 tokens (144-byte rows)
     const int t0 = blockIdx.x * TB, grp = blockIdx.y;
     const int T = a.T, Hkv = a.Hkv, b = grp / Hkv, hkv = grp % Hkv;
     const int Tp = (T + TB - 1) / TB * TB;
     if (blockIdx.z == 0) {
         const bool rope = a.rope_base > 0.0;
-        if (rope) {
-            // cos/sin of tokens t0 + 8u and of offsets v (u, v < 8) directly, then every row of the 64
-            // as a product, cs(t0 + 8u + v) = cs(t0 + 8u) cs(v): a quarter of the sincos evaluations,
-            // each product within a few fp32 ulps of the directly computed entry
-            for (int i = threadIdx.x; i < D / 2; i += 256)
-                theta[i] = exp2(-2.0 * (double)i / (double)D * log2(a.rope_base));
-            __syncthreads();
-            for (int idx = threadIdx.x; idx < 16 * (D / 2); idx += 256) {
-                const int r = idx / (D / 2);
-                cs[idx] = rope_cs_at(r < 8 ? t0 + 8 * r : r - 8, theta[idx % (D / 2)]);
-            }
-            __syncthreads();
-            constexpr int PT = TB * (D / 2) / 256;   // entries per thread
-            float2 ra[PT];
-#pragma unroll
-            for (int it = 0; it < PT; ++it) {
-                const int idx = threadIdx.x + 256 * it, tl = idx / (D / 2), i = idx % (D / 2);
-                const float2 u = cs[(tl >> 3) * (D / 2) + i], v = cs[(8 + (tl & 7)) * (D / 2) + i];
-                ra[it] = make_float2(u.x * v.x - u.y * v.y, u.y * v.x + u.x * v.y);
-            }
-            __syncthreads();
-#pragma unroll
-            for (int it = 0; it < PT; ++it) cs[threadIdx.x + 256 * it] = ra[it];
-            __syncthreads();
-            if (grp == 0)
-                for (int idx = threadIdx.x; idx < TB * (D / 2); idx += 256) {
-                    const int t = t0 + idx / (D / 2);
-                    if (t < T) a.table[(size_t)t * (D / 2) + idx % (D / 2)] = cs[idx];
-                }
-        }
+        const float guard = table_guard(a);
         for (int idx = threadIdx.x; idx < TB * CPR; idx += 256) {
             const int tl = idx / CPR, chunk = idx % CPR, t = t0 + tl;
-            float fac = 1.f;  // QK norm factor of this key row (its chunks sit in consecutive lanes)
+            float fac = guard;  // times the QK norm factor of this key row (its chunks sit in consecutive lanes)
             if (a.qkn.on) {
                 float x[8], ss = 0.f;
                 if (t < T) {
@@ -255,13 +285,14 @@ __global__ __launch_bounds__(256) void prep_fwd_h(PrepArgs a) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
                 }
-                fac = qk_factor(sum_lanes(ss, CPR), D, a.qkn.gain, a.qkn.eps);
+                fac *= qk_factor(sum_lanes(ss, CPR), D, a.qkn.gain, a.qkn.eps);
             }
             if (t < T) {
                 const size_t in_off = (((size_t)b * T + t) * Hkv + hkv) * D + chunk * 8;
                 _Float16* kdst = (_Float16*)a.kh + ((size_t)grp * T + t) * D + chunk * 8;
-                if (rope) convert8<TI, _Float16, D, true>((const TI*)a.k + in_off, kdst, cs + tl * (D / 2), chunk, fac);
-                else convert8<TI, _Float16, D, false>((const TI*)a.k + in_off, kdst, cs, chunk, fac);
+                if (rope) convert8<TI, _Float16, D, true>((const TI*)a.k + in_off, kdst, a.table + (size_t)t * (D / 2),
+                                                          chunk, fac);
+                else convert8<TI, _Float16, D, false>((const TI*)a.k + in_off, kdst, nullptr, chunk, fac);
             }
         }
         return;
@@ -1090,18 +1121,28 @@ void dkdv_kernel(BwdArgs a) {
 // dP - Delta with fp32 accuracy and no per-element subtraction.  Row tiles go through a 4-stage
 // ring filled two steps ahead.
 // =====================================================================================
-template <int D, typename TOUT, bool DS>
+// MODE 0: dQ is a separate pass; 1: also store dS for the dQ pass (DS); 2: atomic dQ (AT) -- the
+// role-1 waves leave dS^T of each tile in LDS, and one step later the role-0 waves multiply it by
+// the key block's K' (kept in LDS) and add dQ of their 32 rows x D/2 columns into an fp32
+// accumulator with atomic adds (not bit-reproducible: the order of the adds varies).  With AT the
+// row-tile ring has three stages filled one step ahead, to leave LDS for K' and dS^T.
+template <int D, typename TOUT, int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void dkdv_kernel_h(BwdArgs a) {
     using OP = _Float16;
     using M = Mma<OP>;
-    constexpr int KSUB = 2, BN = 32 * KSUB, BMR = 64, NW = 8, NST = 4;
+    constexpr bool DS = MODE == 1, AT = MODE == 2;
+    constexpr int KSUB = 2, BN = 32 * KSUB, BMR = 64, NW = 8, NST = AT ? 3 : 4, AHEAD = AT ? 1 : 2;
     constexpr int KS = D / 16, NDB = D / 32, TILE = BMR * D;
+    // AT: the D / 32 column blocks of dQ split between the two key sub-block waves of a row half
+    constexpr int NDQ = NDB >= 2 ? NDB / 2 : 1, NATOM = 16 * NDQ;
     static_assert(NST * 2 * TILE * sizeof(OP) >= KSUB * 2 * NDB * 16 * 64 * sizeof(float),
                   "the ring holds the partials of the final reduction");
     __shared__ __attribute__((aligned(1024))) OP lds[NST * 2 * TILE];     // [stage][Q~ | dO'] row tiles
     __shared__ __attribute__((aligned(16))) half8 pbuf[2][KSUB][2][2][64];  // [s & 1][kq][rh][cc][lane]
     __shared__ __attribute__((aligned(16))) float rowv[NST][2][BMR];       // [stage][lse2 | delta][row]
+    __shared__ __attribute__((aligned(1024))) OP ktile[AT ? BN * D : 8];   // AT: K' of the key block
+    __shared__ __attribute__((aligned(1024))) OP dstile[AT ? 2 * BN * BMR : 8];  // AT: [s & 1] dS^T [key][row]
 
     const int T = a.T, G = a.G, TG = T * G;
     const int nkb = (T + BN - 1) / BN;
@@ -1149,7 +1190,10 @@ void dkdv_kernel_h(BwdArgs a) {
 
     half8 kvf[KS];  // role 0: K^T fragments, role 1: V^T fragments (B operands, one key per lane)
     // x = rows(this wave's half of `rows`) . kvf over D, the row fragments read four products ahead
-    auto chain = [&](const OP* rows) {
+    // (KT: the key fragments from the block's K' tile in LDS instead of kvf -- role 0 with AT, whose
+    // registers the dQ product needs)
+    auto chain = [&](const OP* rows, auto KT) {
+        constexpr bool FROM_TILE = decltype(KT)::value;
         constexpr int AH = KS < 4 ? KS : 4;
         half8 fr[KS];
 #pragma unroll
@@ -1158,7 +1202,8 @@ void dkdv_kernel_h(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
             __builtin_amdgcn_sched_barrier(0);
-            x = M::mma(fr[i], kvf[i], x);
+            if constexpr (FROM_TILE) x = M::mma(fr[i], row_frag_sw<OP, D>(ktile, 32 * kq + c, i, h), x);
+            else x = M::mma(fr[i], kvf[i], x);
             if (i + AH < KS) fr[i + AH] = row_frag_sw<OP, D>(rows, 32 * rh + c, i + AH, h);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1217,11 +1262,11 @@ void dkdv_kernel_h(BwdArgs a) {
         };
 
         const OP* kvrow = (role == 0 ? kg : vg) + (size_t)key * D;
-        if (DS && role == 1) {  // fp16(v) straight from the input: no v' copy on this path
+        if ((DS || AT) && role == 1) {  // fp16(v) straight from the input: no v' copy on these paths
             const size_t voff = (((size_t)b * T + min(key, T - 1)) * a.Hkv + hkv) * D;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) kvf[ks] = kvalid ? load8_f16(a.v, voff + 16 * ks + 8 * h, a.in_dt) : half8{};
-        } else {
+        } else if (!AT) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) kvf[ks] = kvalid ? M::row_frag(kvrow, ks, h, D) : half8{};
         }
@@ -1230,21 +1275,67 @@ void dkdv_kernel_h(BwdArgs a) {
         for (int db = 0; db < NDB; ++db) acc[db] = floatx16{};
         wait_all();
 
+        if constexpr (AT) lds_fill_at<OP, D, BN, NW>(lds_addr(ktile), kg, kb * BN, T);
         fill(0, rstart);
-        if (ntiles > 1) fill(1, rstart + BMR);
-        for (int s = 0; s <= ntiles; ++s) {
+        if (AHEAD == 2 && ntiles > 1) fill(1, rstart + BMR);
+        // AT: rows of this wave's half of tile j see a key of sub-block kq_
+        auto active_kq = [&](int j, int kq_) {
+            const int m0 = kb * BN + 32 * kq_;
+            const int lim = (T - (m0 + 31) <= W ? T : m0 + 31 + W) * G;
+            const int Rh = rstart + j * BMR + 32 * rh;
+            return min(Rh + 31, TG - 1) >= m0 * G && Rh < lim;
+        };
+        // The step loop is instantiated once per role (each wave runs one copy; both copies reach
+        // the same barriers), so each role's registers are allocated for its own work only.
+        auto steps = [&](auto ROLE) {
+        constexpr int RL = decltype(ROLE)::value;
+        int natom = 0;  // AT: atomic adds this wave issued after its share of the latest fill
+        for (int s = 0; s <= ntiles + (AT ? 1 : 0); ++s) {
             // tile s has landed (tile s + 1 may still be in flight); the P of tile s - 1 is in
             // pbuf[(s - 1) & 1]; every wave is done with tile s - 2 and with pbuf[s & 1]
-            // (with DS, role 1's two dS stores of the previous step are its most recent operations)
-            lds_fill_wait_keep((s + 1 < ntiles ? per_fill : 0) + (DS && role == 1 && s >= 2 ? 2 : 0));
-            if (s + 2 < ntiles) fill((s + 2) % NST, rstart + (s + 2) * BMR);
-            if (role == 0) {
+            // (with DS, role 1's two dS stores of the previous step are its most recent operations;
+            // with AT, the fill is one step ahead and role 0's atomic adds of the previous step were
+            // issued after it: vector memory operations complete in order)
+            if constexpr (AT) lds_fill_wait_keep_atomics(natom);
+            else lds_fill_wait_keep((s + 1 < ntiles ? per_fill : 0) + (DS && RL == 1 && s >= 2 ? 2 : 0));
+            natom = 0;
+            if (s + AHEAD < ntiles) fill((s + AHEAD) % NST, rstart + (s + AHEAD) * BMR);
+            if constexpr (RL == 0) {
+                if constexpr (AT) {
+                    // dQ of this wave's 32 rows of tile s - 2 (whose dS^T the role-1 waves left in
+                    // dstile[s & 1]) over the block's 64 keys, columns 32 db .. + 31 for the NDQ
+                    // column blocks db of this key sub-block wave; every wave issues the same
+                    // number of atomic adds (rows past TG add 0 to row TG - 1), so the wait count
+                    // above is exact
+                    const int j = s - 2;
+                    if (j >= 0 && j < ntiles && (NDB >= 2 || kq == 0) && (active_kq(j, 0) || active_kq(j, 1))) {
+                        const OP* dt = dstile + (s & 1) * (BN * BMR);
+                        half8 af[4];
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) af[kk] = tr_frag_f16_sw<64>((const _Float16*)dt, kk, 32 * rh);
+                        // rows past TG (their dS rows are zero) land in the next group's rows or in the
+                        // 64 rows of padding after the last group: adding 0 changes nothing
+                        const int Rh = rstart + j * BMR + 32 * rh;
+                        float* dst = a.dq_acc + grp * (size_t)TG * D + (size_t)(Rh + 4 * h) * D + c;
+#pragma unroll
+                        for (int i = 0; i < NDQ; ++i) {   // one column block at a time (registers)
+                            floatx16 qa = floatx16{};
+#pragma unroll
+                            for (int kk = 0; kk < 4; ++kk)
+                                qa = M::mma(af[kk], tr_frag_f16_sw<D>((const _Float16*)ktile, kk, 32 * (kq * NDQ + i)), qa);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D + 32 * (kq * NDQ + i), qa[r]);
+                        }
+                        natom = NATOM;
+                    }
+                }
                 if (s < ntiles && active(s)) {
                     const int st = s % NST;
                     const OP* Qs = lds + st * 2 * TILE;
                     const OP* Os = Qs + TILE;
                     const int Rh = rstart + s * BMR + 32 * rh;
-                    floatx16 x = chain(Qs);
+                    floatx16 x = chain(Qs, IC<AT ? 1 : 0>{});
                     x = M::mma(fold_frag(-rowv[st][0][32 * rh + c], h), fw, x);  // S - lse2
                     half8 tf0[NDB];
                     tr_frags0(Os, tf0);  // in flight during the exponentials
@@ -1265,6 +1356,15 @@ void dkdv_kernel_h(BwdArgs a) {
                     product2(Os, tf0, pf, acc);
                 }
             } else {
+                if (AT && s >= 1 && !active(s - 1)) {  // this quadrant of dS^T is zero
+                    char* dt = reinterpret_cast<char*>(dstile + ((s - 1) & 1) * (BN * BMR));
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                        for (int j4 = 0; j4 < 2; ++j4)
+                            *reinterpret_cast<uint2*>(dt + Tile<_Float16, 64>::off(32 * kq + c, 32 * rh + 16 * cc + 8 * j4 + 4 * h)) =
+                                uint2{0u, 0u};
+                }
                 if (DS && s >= 1 && !active(s - 1)) {  // a stored tile is complete: zeros here
                     __builtin_nontemporal_store(half8{}, &dsg[(dsb + s - 1) * 512 + ds0]);
                     __builtin_nontemporal_store(half8{}, &dsg[(dsb + s - 1) * 512 + ds1]);
@@ -1273,7 +1373,7 @@ void dkdv_kernel_h(BwdArgs a) {
                     const int st = (s - 1) % NST;
                     const OP* Qs = lds + st * 2 * TILE;
                     const OP* Os = Qs + TILE;
-                    floatx16 y = chain(Os);
+                    floatx16 y = chain(Os, IC<0>{});
                     y = M::mma(fold_frag(-rowv[st][1][32 * rh + c], h), fw, y);  // dP - Delta
                     half8 tf0[NDB];
                     tr_frags0(Qs, tf0);  // in flight during dS
@@ -1288,10 +1388,24 @@ void dkdv_kernel_h(BwdArgs a) {
                         __builtin_nontemporal_store(dsf[0], &dsg[(dsb + s - 1) * 512 + ds0]);
                         __builtin_nontemporal_store(dsf[1], &dsg[(dsb + s - 1) * 512 + ds1]);
                     }
+                    if constexpr (AT) {
+                        // dS^T as [key][row] (swizzled 64 x 64 tile): lane (h, c) holds key 32 kq + c and,
+                        // per k-step cc, the rows 32 rh + 16 cc + 8 (j / 4) + 4 h + j % 4
+                        char* dt = reinterpret_cast<char*>(dstile + ((s - 1) & 1) * (BN * BMR));
+#pragma unroll
+                        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                            for (int j4 = 0; j4 < 2; ++j4)
+                                *reinterpret_cast<half4v*>(dt + Tile<_Float16, 64>::off(32 * kq + c, 32 * rh + 16 * cc + 8 * j4 + 4 * h)) =
+                                    half4v{dsf[cc][4 * j4], dsf[cc][4 * j4 + 1], dsf[cc][4 * j4 + 2], dsf[cc][4 * j4 + 3]};
+                    }
                     product2(Qs, tf0, dsf, acc);
                 }
             }
         }
+        };
+        if (role == 0) steps(IC<0>{});
+        else steps(IC<1>{});
 
         // add the two row halves in a fixed order (half 0 + half 1) through the staging area
         __syncthreads();
@@ -1307,6 +1421,7 @@ void dkdv_kernel_h(BwdArgs a) {
         __syncthreads();
         if (rh == 0 && kvalid) {  // both lanes of a key pair (c, c + 32) agree
             const size_t koff = (((size_t)b * T + key) * a.Hkv + hkv) * D;
+            const float us = a.dsc ? a.dsc[grp] : 1.f;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1315,9 +1430,12 @@ void dkdv_kernel_h(BwdArgs a) {
                     const int d = 32 * db + 8 * q4 + 4 * h;
                     float x0 = acc[db][4 * q4] + o1[0], x1 = acc[db][4 * q4 + 1] + o1[1];
                     float x2 = acc[db][4 * q4 + 2] + o1[2], x3 = acc[db][4 * q4 + 3] + o1[3];
-                    if (role == 1) {
-                        // dk' = ln2 * sum dS q~ (q~ carries scale * log2 e), then dk = R^T dk'
-                        x0 *= kLn2; x1 *= kLn2; x2 *= kLn2; x3 *= kLn2;
+                    if (role == 0) {
+                        x0 *= us; x1 *= us; x2 *= us; x3 *= us;
+                    } else {
+                        // dk' = ln2 * sum dS q~ (q~ carries scale * log2 e), then dk = R^T dk'; both
+                        // gradients carry the dO scale, undone by us
+                        x0 *= kLn2 * us; x1 *= kLn2 * us; x2 *= kLn2 * us; x3 *= kLn2 * us;
                         if (rope) {
                             const float2 r0 = a.table[(size_t)key * (D / 2) + d / 2];
                             const float2 r1 = a.table[(size_t)key * (D / 2) + d / 2 + 1];
@@ -1339,6 +1457,44 @@ void dkdv_kernel_h(BwdArgs a) {
         }
         __syncthreads();  // the staging area is refilled by the next key block
     }
+}
+
+// =====================================================================================
+// Atomic dQ: the fp32 accumulator [group][T G][D] (flattened rows) that the dK/dV pass added into,
+// scaled by softmax scale / (dO scale), rotated back (R^T), QK-norm backward, written as dq.
+// grid ceil(rows D / 1024), 256 threads: D / 4 lanes per row, four consecutive columns per lane.
+// =====================================================================================
+template <int D, typename TOUT>
+__global__ __launch_bounds__(256) void dq_acc_convert_kernel(BwdArgs a) {
+    constexpr int LPR = D / 4, RPB = 256 / LPR;
+    const int TG = a.T * a.G;
+    const int64_t nrows = (int64_t)a.B * a.Hkv * TG;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int lane = threadIdx.x % LPR, d = 4 * lane;
+    const bool valid = row < nrows;
+    const int64_t rr = valid ? row : nrows - 1;
+    const int grp = (int)(rr / TG), R = (int)(rr % TG);
+    const int t = R / a.G, hq = (grp % a.Hkv) * a.G + R % a.G, b = grp / a.Hkv;
+    const floatx4 v = *reinterpret_cast<const floatx4*>(a.dq_acc + rr * D + d);
+    const float sc = a.scale * a.dsc[grp];
+    float x0 = v[0] * sc, x1 = v[1] * sc, x2 = v[2] * sc, x3 = v[3] * sc;
+    if (a.rope_base > 0.0) {
+        const float2 r0 = a.table[(size_t)t * (D / 2) + d / 2];
+        const float2 r1 = a.table[(size_t)t * (D / 2) + d / 2 + 1];
+        const float y0 = x0 * r0.x + x1 * r0.y, y1 = -x0 * r0.y + x1 * r0.x;
+        const float y2 = x2 * r1.x + x3 * r1.y, y3 = -x2 * r1.y + x3 * r1.x;
+        x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+    }
+    const size_t qoff = (((size_t)b * a.T + t) * a.Hq + hq) * D;
+    if (a.qkn.on) {  // dx = gain rho (y - x rho^2 (y . x) / D), x the raw q row
+        const floatx4 xr = load4_dt(a.q, qoff + d, a.in_dt);
+        const float rho = a.rq[(size_t)grp * TG + R];
+        const float dot = sum_lanes(x0 * xr[0] + x1 * xr[1] + x2 * xr[2] + x3 * xr[3], LPR);
+        const float c1 = a.qkn.gain * rho, c2 = rho * rho * dot / (float)D;
+        x0 = c1 * (x0 - xr[0] * c2); x1 = c1 * (x1 - xr[1] * c2);
+        x2 = c1 * (x2 - xr[2] * c2); x3 = c1 * (x3 - xr[3] * c2);
+    }
+    if (valid) store4((TOUT*)a.dq + qoff + d, x0, x1, x2, x3);
 }
 
 // =====================================================================================
@@ -1458,7 +1614,7 @@ void dq_kernel(BwdArgs a) {
     if (!rvalid) return;  // both lanes of a row pair (c, c + 32) agree
     const int t = t_lane, hh = R - t * G, hq = hkv * G + hh;
     const size_t qoff = (((size_t)b * T + t) * a.Hq + hq) * D;
-    const float sc = a.scale;
+    const float sc = a.scale * (a.dsc ? a.dsc[grp] : 1.f);   // the dO scale undone as well
     const bool rope = a.rope_base > 0.0;
     // dq = R^T (scale * dq'), in place
 #pragma unroll
@@ -1632,7 +1788,7 @@ void dq_kernel_h(BwdArgs a) {
     if (!rvalid) return;  // both lanes of a row pair (c, c + 32) agree
     const int t = t_lane, hh = R - t * G, hq = hkv * G + hh;
     const size_t qoff = (((size_t)b * T + t) * a.Hq + hq) * D;
-    const float sc = a.scale;
+    const float sc = a.scale * (a.dsc ? a.dsc[grp] : 1.f);   // the dO scale undone as well
     const bool rope = a.rope_base > 0.0;
     // dq = R^T (scale * dq'), in place
 #pragma unroll
@@ -1838,7 +1994,7 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
     }
 
     if (!rvalid) return;
-    const float sc = a.scale;
+    const float sc = a.scale * (a.dsc ? a.dsc[grp] : 1.f);   // the dO scale undone as well
     const bool rope = a.rope_base > 0.0;
     // dq = R^T (scale * dq'), in place
 #pragma unroll
@@ -1908,15 +2064,20 @@ static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, hipStream_
 }
 
 template <typename TI, typename TO, typename OP, int D>
-static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_t s, hipEvent_t const* ev) {
+static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am, const BwdArgs& ba, hipStream_t s,
+                               hipEvent_t const* ev) {
     const Marks m{ev, s};
     NE_TRY(m.before(0));
+    if constexpr (sizeof(OP) == 2) {
+        hipLaunchKernelGGL((dO_amax_kernel<TI, D>), dim3(am.nparts, ba.B * ba.Hkv), dim3(256), 0, s, am);
+        NE_TRY(hipGetLastError());
+    }
     hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, true>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(0));
     const int ngroups = ba.B * ba.Hkv, npair = ((ba.T + 63) / 64 + 1) / 2;
     if constexpr (sizeof(OP) == 2) {
-        if (ba.ds) {
+        if (mode == kBwdStoredDs) {
             // stored dS: dK/dV, then dQ, for each batch of ds_groups groups (a single batch unless the
             // dS of every group would exceed the buffer); with several batches the second marked
             // interval covers all but the last dQ launch as well
@@ -1926,7 +2087,7 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
                 BwdArgs bb = ba;
                 bb.grp0 = g0;
                 bb.ngrp = min(ba.ds_groups, ngroups - g0);
-                hipLaunchKernelGGL((dkdv_kernel_h<D, TO, true>), dim3(npair * bb.ngrp), dim3(512), 0, s, bb);
+                hipLaunchKernelGGL((dkdv_kernel_h<D, TO, 1>), dim3(npair * bb.ngrp), dim3(512), 0, s, bb);
                 NE_TRY(hipGetLastError());
                 if (g0 + bb.ngrp >= ngroups) {
                     NE_TRY(m.after(1));
@@ -1939,10 +2100,22 @@ static hipError_t launch_bwd_t(const PrepArgs& pa, const BwdArgs& ba, hipStream_
             }
             return m.after(2);
         }
+        if (mode == kBwdAtomic) {
+            NE_TRY(m.before(1));
+            hipLaunchKernelGGL((dkdv_kernel_h<D, TO, 2>), dim3(npair * ngroups), dim3(512), 0, s, ba);
+            NE_TRY(hipGetLastError());
+            NE_TRY(m.after(1));
+            NE_TRY(m.before(2));
+            const int64_t rows = (int64_t)ngroups * ba.T * ba.G;
+            hipLaunchKernelGGL((dq_acc_convert_kernel<D, TO>), dim3((unsigned)((rows * D / 4 + 255) / 256)), dim3(256), 0,
+                               s, ba);
+            NE_TRY(hipGetLastError());
+            return m.after(2);
+        }
     }
     NE_TRY(m.before(1));
     if constexpr (sizeof(OP) == 2)
-        hipLaunchKernelGGL((dkdv_kernel_h<D, TO, false>), dim3(npair * ngroups), dim3(512), 0, s, ba);
+        hipLaunchKernelGGL((dkdv_kernel_h<D, TO, 0>), dim3(npair * ngroups), dim3(512), 0, s, ba);
     else
         hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3(npair * ngroups), dim3(512), 0, s, ba);
     NE_TRY(hipGetLastError());
@@ -1978,14 +2151,20 @@ hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const Fw
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const BwdArgs& ba, hipStream_t s,
-                      hipEvent_t const* ev) {
-    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, float, float, float, D, pa, ba, s, ev) }
-    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, __bf16, float, _Float16, D, pa, ba, s, ev) }
-    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_bwd_t, __bf16, __bf16, _Float16, D, pa, ba, s, ev) }
-    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, _Float16, float, _Float16, D, pa, ba, s, ev) }
-    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_bwd_t, _Float16, _Float16, _Float16, D, pa, ba, s, ev) }
+hipError_t launch_bwd(int in_dt, int out_dt, int D, int mode, const PrepArgs& pa, const AmaxArgs& am,
+                      const BwdArgs& ba, hipStream_t s, hipEvent_t const* ev) {
+    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, float, float, float, D, mode, pa, am, ba, s, ev) }
+    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, __bf16, float, _Float16, D, mode, pa, am, ba, s, ev) }
+    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_bwd_t, __bf16, __bf16, _Float16, D, mode, pa, am, ba, s, ev) }
+    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, _Float16, float, _Float16, D, mode, pa, am, ba, s, ev) }
+    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_bwd_t, _Float16, _Float16, _Float16, D, mode, pa, am, ba, s, ev) }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_table(const TableArgs& a, hipStream_t s) {
+    const int64_t n = (int64_t)a.T * (a.D / 2);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace ne

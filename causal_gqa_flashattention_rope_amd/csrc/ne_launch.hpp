@@ -15,6 +15,20 @@ __host__ __device__ inline size_t ds_tile_index(int kb, int rt, int nrt, int G) 
     return (size_t)kb * nrt - (size_t)G * ((size_t)kb * (kb - 1) / 2) + (size_t)(rt - kb * G);
 }
 
+// Header of the RoPE table at the start of an attention workspace (the table follows at byte 256):
+// the arguments it was built for.  The preparation kernels compare it with the call's arguments on
+// the device and make their operand copies NaN when it does not match.
+constexpr unsigned kTableMagic = 0x52504e45u;
+constexpr size_t kTableHdrBytes = 256;
+struct TableHdr {
+    unsigned magic;
+    int T, D, pad;
+    double base;
+};
+__host__ __device__ inline bool table_matches(const TableHdr& h, int T, int D, double base) {
+    return h.magic == kTableMagic && h.T == T && h.D == D && h.base == base;
+}
+
 // QK norm: every (token, head) row x of q and k becomes gain * x / sqrt(mean(x^2) + eps).
 struct QkNorm {
     int on;
@@ -34,6 +48,26 @@ struct PrepArgs {
     float qscale;                                   // softmax scale * log2(e)
     QkNorm qkn;
     int skip_v;                                     // backward: no v' copy (the dK/dV pass reads v)
+    const TableHdr* hdr;                            // the table's header (RoPE on)
+    // backward, 16-bit operands: dO' = s dO with s a power of two per (batch, KV head) group chosen
+    // from the group's max |dO| (amax_part: nparts partial maxima per group); dsc[group] = 1 / s
+    const float* amax_part; int nparts; float* dsc;
+    float* dq_acc;                                  // atomic dQ accumulator to clear (or null)
+};
+
+// Partial maxima of |dO| per (batch, KV head) group: part p of group g covers tokens
+// [p * tpp, (p + 1) * tpp) of the group's G heads.
+struct AmaxArgs {
+    const void* dO;
+    float* part;
+    int B, T, Hq, Hkv, nparts, tpp;
+};
+
+// RoPE table of T positions into the workspace, plus its header.
+struct TableArgs {
+    TableHdr* hdr; float2* table;
+    int T, D;
+    double base;
 };
 
 struct FwdArgs {
@@ -58,6 +92,8 @@ struct BwdArgs {
     const float* rq; const float* rk;               // 1/rms of the q and k rows (QK norm)
     void* ds;                                       // stored dS tiles (16-bit operands), or null:
                                                     // dQ then recomputes S and dP
+    const float* dsc;                               // 1 / (dO scale) per group (16-bit operands), or null
+    float* dq_acc;                                  // atomic dQ: fp32 accumulator [group][T G][D]
     int ds_groups;                                  // groups whose dS the buffer holds at once
     int grp0, ngrp;                                 // the (batch, KV head) groups of one launch of
                                                     // the stored-dS pair (else 0 and B * Hkv)
@@ -107,10 +143,13 @@ struct QkvArgs {
 // dtype codes follow ne_dtype_t: 0 = f32, 1 = bf16, 2 = f16.
 // ev (nullable): hipEvent_t pairs recorded on `s` around each kernel launch, in launch order
 // (forward: prep, fwd; backward: prep, dkdv, dq).
+hipError_t launch_table(const TableArgs& a, hipStream_t s);
 hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, hipStream_t s,
                       hipEvent_t const* ev);
-hipError_t launch_bwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const BwdArgs& ba, hipStream_t s,
-                      hipEvent_t const* ev);
+// mode: 0 dQ recomputes S and dP, 1 dQ reads the stored dS, 2 atomic dQ in the dK/dV pass
+enum { kBwdRecompute = 0, kBwdStoredDs = 1, kBwdAtomic = 2 };
+hipError_t launch_bwd(int in_dt, int out_dt, int D, int mode, const PrepArgs& pa, const AmaxArgs& am,
+                      const BwdArgs& ba, hipStream_t s, hipEvent_t const* ev);
 hipError_t launch_append(int in_dt, int D, const AppendArgs& a, hipStream_t s);
 // ev (nullable): pairs around the cos/sin table and the product (4 entries).
 hipError_t launch_qkv(int in_dt, int out_dt, int D, const QkvArgs& a, hipStream_t s, hipEvent_t const* ev);

@@ -23,13 +23,17 @@
  *   lse          : [B][Hq][T], always float32
  *
  * Ownership: every tensor pointer and the workspace are DEVICE pointers allocated and owned by
- * the caller.  The library never allocates, frees, synchronises or prints on the compute calls.
+ * the caller.  The library never allocates, frees, synchronises or prints on the compute calls
+ * (ne_rope_table_check, a diagnostic, is the one call that waits for its stream).
  * Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs asynchronously;
  * device-side faults surface at the caller's next synchronisation.
  *
  * Errors: arguments are validated on the host before anything is enqueued; on failure the call
  * returns a non-zero ne_status_t, enqueues nothing, and ne_last_error() gives a thread-local
  * message.  NE_ERR_HIP means a launch was rejected by the HIP runtime (hipGetLastError).
+ * The one condition the host cannot see is a workspace whose RoPE table was never built for the
+ * call's (T, head_dim, rope_base): the kernels detect it on the device and make the outputs NaN
+ * (ne_rope_table_init, ne_rope_table_check).
  *
  * Thread safety: calls are re-entrant; the only mutable library state is the thread-local error
  * message.  Two calls that share a workspace must be ordered on one stream.
@@ -43,92 +47,126 @@
 extern "C" {
 #endif
 
-#define NE_ABI_VERSION 1
+#define NE_ABI_VERSION 2
 
 typedef enum { NE_F32 = 0, NE_BF16 = 1, NE_F16 = 2 } ne_dtype_t;
 
 typedef enum {
     NE_OK = 0,
-    NE_ERR_NULL = 1,        /* a required pointer is NULL                                   */
-    NE_ERR_SHAPE = 2,       /* B, T, Hq, Hkv < 1, Hq % Hkv != 0, or sizes overflow (for the
-                               attention calls: T * (Hq / Hkv) * head_dim * e >= 2^31, e = 4
-                               for fp32 inputs, else 2 -- a KV group's rows are addressed with
-                               32-bit byte offsets)                                           */
-    NE_ERR_UNSUPPORTED = 3, /* head_dim not in {32, 64, 128}, or dtype pair not supported     */
-    NE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                               */
-    NE_ERR_WORKSPACE = 5,   /* workspace_bytes smaller than the matching *_workspace_bytes()  */
-    NE_ERR_HIP = 6          /* the HIP runtime rejected a launch                              */
+    NE_ERR_NULL = 1,          /* a required pointer is NULL                                 */
+    NE_ERR_SHAPE = 2,         /* B, T, Hq, Hkv < 1, Hq % Hkv != 0, or sizes overflow (for the
+                                 attention calls: T * (Hq / Hkv) * head_dim * e >= 2^31, e = 4
+                                 for fp32 inputs, else 2 -- a KV group's rows are addressed
+                                 with 32-bit byte offsets)                                   */
+    NE_ERR_UNSUPPORTED = 3,   /* head_dim not in {32, 64, 128}, dtype pair not supported, or a
+                                 flag this build does not implement                         */
+    NE_ERR_ALIGN = 4,         /* a pointer is not 16-byte aligned                             */
+    NE_ERR_WORKSPACE = 5,     /* workspace_bytes smaller than ne_rope_attn_workspace_bytes()  */
+    NE_ERR_NO_ROPE_TABLE = 6, /* the workspace holds no cos/sin table for (T, head_dim,
+                                 rope_base): returned by ne_rope_table_check; see the
+                                 table notes below for what fwd / bwd do instead             */
+    NE_ERR_HIP = 7            /* the HIP runtime rejected a launch or a copy                  */
 } ne_status_t;
+
+/* Flags (bitwise OR; 0 = the defaults).
+ *   NE_FLAG_NONDETERMINISTIC  backward: dQ is accumulated in the dK/dV pass with fp32 atomic adds
+ *                             into a workspace buffer and converted by a small pass, instead of a
+ *                             separate pass that recomputes S and dP.  Results meet the same error
+ *                             bound but their low bits may differ from call to call.  Without the
+ *                             flag every output is written once by one thread in a fixed order and
+ *                             repeated calls give identical bits.  (16-bit inputs; the fp32 path
+ *                             ignores the flag and stays deterministic.)
+ *   NE_FLAG_STORE_DS          backward: the dK/dV pass also stores the fp16 dS of every 64 x 64
+ *                             tile of the causal band in the workspace (about T * T * Hq / Hkv bytes
+ *                             per (batch, KV head) group) and the dQ pass reads it instead of
+ *                             recomputing S and dP: this gives up the O(T) memory of the default
+ *                             backward for fewer products.  The workspace query sizes the buffer for
+ *                             every group (at most 4 GiB); a smaller workspace that still holds one
+ *                             group's dS makes the two passes run once per batch of as many groups
+ *                             as it holds, with the same bits.  Deterministic; 16-bit inputs only.
+ *                             Ignored together with NE_FLAG_NONDETERMINISTIC.
+ *   NE_FLAG_BF16_OPERANDS     reserved: bf16 MFMA operands.  Not implemented: NE_ERR_UNSUPPORTED.
+ *   NE_FLAG_ROPE_HALF_SPLIT   reserved: rotate the pairs (i, i + D/2) instead of (2i, 2i + 1).
+ *                             Not implemented: NE_ERR_UNSUPPORTED. */
+#define NE_FLAG_NONDETERMINISTIC 0x1u
+#define NE_FLAG_BF16_OPERANDS 0x2u
+#define NE_FLAG_ROPE_HALF_SPLIT 0x4u
+#define NE_FLAG_STORE_DS 0x8u
 
 /* Supported (in_dtype -> out_dtype) pairs: F32->F32 (fp32 operands on fp32 MFMA),
  * BF16->F32, BF16->BF16, F16->F32, F16->F16 (fp16 MFMA operands, fp32 accumulation).
- * q, k, v and dO are in_dtype; o, dq, dk and dv are out_dtype. */
+ * q, k, v and dO are in_dtype; o, dq, dk and dv are out_dtype.
+ * Range of 16-bit inputs: k and v become fp16 MFMA operands, so |k|, |v| must stay below 65504
+ * (values under 2^-14 lose relative precision as fp16 subnormals).  dO is scaled per (batch, KV
+ * head) group by a power of two before its conversion to fp16 and the gradients are scaled back, so
+ * any finite dO is supported. */
 
-/* Bytes of device workspace the forward needs (256-byte aligned base recommended; 16 is
- * required).  Holds the rotated, scaled, converted operand copies.  Returns 0 for invalid
- * arguments. */
-size_t ne_rope_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim,
-                                        ne_dtype_t in_dtype);
+/* Bytes of device workspace a forward (is_bwd = 0) or backward (is_bwd != 0) call needs for these
+ * arguments and flags (256-byte aligned base recommended; 16 is required).  0 for invalid
+ * arguments.  Layout, all caller-owned:
+ *   [0, 256)                 table header (T, head_dim, rope_base of the table below)
+ *   then, when rope_base > 0, the cos/sin table [T][head_dim / 2] of float2 (ne_rope_table_init);
+ *   forward:  the rotated fp16 keys and transposed fp16 values (fp32 copies on the fp32 path);
+ *   backward: the rotated, scaled copies of q, k, dO (and v), Delta = rowsum(dO * o), the
+ *             log2-scaled lse, the per-row 1/rms of the QK norm, the dO scales; with
+ *             NE_FLAG_NONDETERMINISTIC the fp32 dQ accumulator [B][Hq][T][head_dim]; with
+ *             NE_FLAG_STORE_DS the stored dS.
+ * A backward workspace is also a valid forward workspace for the same arguments: the table sits at
+ * the same place, so one ne_rope_table_init serves both calls. */
+size_t ne_rope_attn_workspace_bytes(int is_bwd, int B, int T, int Hq, int Hkv, int head_dim,
+                                    double rope_base, ne_dtype_t in_dtype, unsigned flags);
 
-/* Bytes of device workspace the backward needs (operand copies, the per-row
- * Delta = rowsum(dO * o), the log2-scaled lse, the per-row 1/rms of q and k used by the QK norm,
- * the cos/sin table and, for 16-bit inputs, the fp16 dS of every 64-row x 64-key tile of the
- * causal band: 8 KiB per tile, about T * T * (Hq / Hkv) bytes per (batch, KV head) group).  The
- * dS buffer holds as many groups as fit 4 GiB, or the byte count in the environment variable
- * NE_ROPE_ATTN_DS_MAX_BYTES (0: none), and the dK/dV and dQ passes run once per batch of that many
- * groups; when not even one group fits, dQ recomputes S and dP and the workspace omits the
- * buffer.  The variable is read by this call and by ne_rope_attn_bwd*: keep it unchanged between
- * them.  Results agree within rounding either way, and are bitwise the same for every batch size;
- * each choice is bit-reproducible. */
-size_t ne_rope_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim,
-                                        ne_dtype_t in_dtype);
+/* Builds the RoPE cos/sin table of positions 0 .. T-1 in the workspace and records (T, head_dim,
+ * rope_base) in its header: c = cos(t theta_i), s = sin(t theta_i), theta_i = rope_base^(-2i/D)
+ * (RoPE on queries and keys: "NanoEuler: 使用 C 和 CUDA 从零开始构建的 GPT-2 规模 LLM", 技术规格),
+ * the phase formed and reduced to [-pi, pi] in double precision, then rounded to fp32.  Once per
+ * workspace and (T, head_dim, rope_base): every forward and backward call with that workspace and
+ * those arguments reads it.  rope_base <= 0: nothing to build (NE_OK).  Asynchronous on `stream`.
+ * Table notes: the calls cannot read device memory without synchronising, so they do not check the
+ * header on the host; their first kernel checks it on the device and, when it does not match the
+ * call's (T, head_dim, rope_base), makes every output NaN.  ne_rope_table_check reports the state
+ * explicitly. */
+ne_status_t ne_rope_table_init(void* workspace, size_t workspace_bytes, int T, int head_dim,
+                               double rope_base, void* stream);
 
-/* Forward: o = softmax(mask(R(q) R(k)^T / sqrt(D))) v, lse = log-sum-exp of each score row.
- * rope_base <= 0 disables the rotation. */
+/* NE_OK when the workspace's table header matches (T, head_dim, rope_base) (or rope_base <= 0),
+ * NE_ERR_NO_ROPE_TABLE otherwise.  Copies the 256-byte header to the host and waits for `stream`:
+ * the one call of this library that synchronises (a diagnostic, not for the hot path). */
+ne_status_t ne_rope_table_check(const void* workspace, size_t workspace_bytes, int T, int head_dim,
+                                double rope_base, void* stream);
+
+/* Forward: o = softmax(mask(R(q) R(k)^T / sqrt(D))) v, lse = log-sum-exp of each score row, computed
+ * over 64-key tiles with an online softmax so no T x T matrix is stored ("NanoEuler: 使用 C 和 CUDA
+ * 从零开始构建的 GPT-2 规模 LLM", 内核实现; "用 100KB C/CUDA 单文件复刻 GPT-2:NanoEuler 116M 单卡可跑的
+ * 全流程拆解", §3.4).  rope_base <= 0 disables the rotation.  flags: 0 (the backward flags are
+ * accepted and have no effect here). */
 ne_status_t ne_rope_attn_fwd(const void* q, const void* k, const void* v,
                              void* o, float* lse,
                              int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward: given q, k, v, the forward's o (out_dtype) and lse, and dO (in_dtype), writes the
- * gradients of sum(o * dO): dq (w.r.t. the un-rotated q), dk (un-rotated k, summed over the
- * query heads of each group) and dv.  Deterministic: every output element is written once by
- * one thread in a fixed order (no atomics), so repeated calls give identical bits.
- * Delta = rowsum(dO * o) is computed from the o passed in. */
+/* Backward (the hand-written backward of the same pages, 验证与稳定性): given q, k, v, the forward's
+ * o (out_dtype) and lse, and dO (in_dtype), writes the gradients of sum(o * dO): dq (w.r.t. the
+ * un-rotated q), dk (un-rotated k, summed over the query heads of each group) and dv.
+ * Delta = rowsum(dO * o) is computed from the o passed in.  By default dK/dV and dQ are separate
+ * passes, dQ recomputing S and dP: the workspace is O(T) and every output element is written once
+ * (bit-reproducible).  NE_FLAG_STORE_DS and NE_FLAG_NONDETERMINISTIC select the other two backward
+ * designs (see the flags); the workspace must be sized with the same flags. */
 ne_status_t ne_rope_attn_bwd(const void* q, const void* k, const void* v,
                              const void* o, const float* lse, const void* dO,
                              void* dq, void* dk, void* dv,
                              int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                             ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                             ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                              void* workspace, size_t workspace_bytes, void* stream);
-
-/* Instrumented variants for measurement: identical work, plus hipEvent_t records on `stream`
- * around each kernel launch -- events[2i] before and events[2i+1] after launch i.  Forward:
- * i = 0 operand preparation, 1 attention (an array of 4).  Backward: i = 0 preparation with
- * Delta, 1 dK/dV, 2 dQ (an array of 6; when the stored dS is processed in several group batches,
- * interval 1 spans every batch's dK/dV and all but the last dQ, interval 2 the last dQ).  The
- * array must be non-null; a null entry skips that
- * record (a record costs microseconds of stream time, so a measurement brackets only the
- * launches it needs).  The events are created and owned by the caller. */
-ne_status_t ne_rope_attn_fwd_timed(const void* q, const void* k, const void* v,
-                                   void* o, float* lse,
-                                   int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                                   ne_dtype_t in_dtype, ne_dtype_t out_dtype,
-                                   void* workspace, size_t workspace_bytes, void* stream,
-                                   void* const* events);
-ne_status_t ne_rope_attn_bwd_timed(const void* q, const void* k, const void* v,
-                                   const void* o, const float* lse, const void* dO,
-                                   void* dq, void* dk, void* dv,
-                                   int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                                   ne_dtype_t in_dtype, ne_dtype_t out_dtype,
-                                   void* workspace, size_t workspace_bytes, void* stream,
-                                   void* const* events);
 
 /* Options of the *_ex calls and of the cache calls (a NULL pointer means all defaults: no window,
  * no QK norm). */
 typedef struct {
-    int window;     /* > 0: query t sees keys t - window + 1 .. t; <= 0: the whole causal prefix   */
+    int window;     /* > 0: query t sees keys t - window + 1 .. t, its own position included, as in
+                       the short-window layers of the window_pattern feature ("nanochat 全栈 LLM 训练
+                       实践指南", 模型架构速览, where a short window is a quarter of the context);
+                       <= 0 or >= T: the whole causal prefix (the same bits as no window)            */
     int qk_norm;    /* nonzero: QK norm -- every (token, head) row x of q and of k is replaced by
                        qk_gain * x / sqrt(mean(x^2) + qk_eps) before RoPE ("nanochat 全栈 LLM 训练实践
                        指南", section 模型架构速览: q and k normalised and scaled up by 1.2); the
@@ -137,14 +175,21 @@ typedef struct {
     float qk_eps;   /* added to the mean square; finite, >= 0 (0 with an all-zero row: non-finite)    */
 } ne_attn_opts_t;
 
-/* The forward and backward with every option (window and QK norm).  Arguments as in
- * ne_rope_attn_fwd / ne_rope_attn_bwd; opts may be NULL; events NULL or as for the *_timed calls.
- * The backward must be given the options the forward used. */
+/* The forward and backward with every option (window and QK norm) and, for measurement, HIP events:
+ * arguments as in ne_rope_attn_fwd / ne_rope_attn_bwd; opts may be NULL; the backward must be given
+ * the options the forward used (lse depends on them).  events: NULL, or an array of hipEvent_t
+ * recorded on `stream` around each kernel launch -- events[2i] before and events[2i+1] after launch
+ * i; a NULL entry skips that record (a record costs stream time, so a measurement brackets only the
+ * launches it needs).  Forward: i = 0 operand preparation, 1 attention (4 entries).  Backward: i = 0
+ * preparation with Delta (and the dO scales), 1 dK/dV, 2 dQ (the dQ pass, or with
+ * NE_FLAG_NONDETERMINISTIC the conversion of the accumulated dQ) (6 entries; with NE_FLAG_STORE_DS
+ * run in several group batches, interval 1 spans every batch's dK/dV and all but the last dQ,
+ * interval 2 the last dQ).  The events are created and owned by the caller. */
 ne_status_t ne_rope_attn_fwd_ex(const void* q, const void* k, const void* v,
                                 void* o, float* lse,
                                 int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
                                 const ne_attn_opts_t* opts,
-                                ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 void* const* events);
 ne_status_t ne_rope_attn_bwd_ex(const void* q, const void* k, const void* v,
@@ -152,33 +197,9 @@ ne_status_t ne_rope_attn_bwd_ex(const void* q, const void* k, const void* v,
                                 void* dq, void* dk, void* dv,
                                 int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
                                 const ne_attn_opts_t* opts,
-                                ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 void* const* events);
-
-/* Sliding-window attention: the same operation with each query seeing only the `window` most
- * recent keys, its own position included -- query t sees keys t - window + 1 .. t -- as in the
- * short-window layers of the window_pattern feature ("nanochat 全栈 LLM 训练实践指南", section
- * 模型架构速览, where a short window is a quarter of the context).  window <= 0, or >= T, is the
- * full causal prefix and gives the same bits as ne_rope_attn_fwd / ne_rope_attn_bwd.  The backward
- * must be given the window the forward used (lse depends on it).  Arguments, layouts, workspace
- * sizes and errors are those of ne_rope_attn_fwd / ne_rope_attn_bwd; `events` is NULL (untimed) or
- * an array as for the *_timed calls (4 forward, 6 backward). */
-ne_status_t ne_rope_attn_fwd_window(const void* q, const void* k, const void* v,
-                                    void* o, float* lse,
-                                    int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                                    int window,
-                                    ne_dtype_t in_dtype, ne_dtype_t out_dtype,
-                                    void* workspace, size_t workspace_bytes, void* stream,
-                                    void* const* events);
-ne_status_t ne_rope_attn_bwd_window(const void* q, const void* k, const void* v,
-                                    const void* o, const float* lse, const void* dO,
-                                    void* dq, void* dk, void* dv,
-                                    int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
-                                    int window,
-                                    ne_dtype_t in_dtype, ne_dtype_t out_dtype,
-                                    void* workspace, size_t workspace_bytes, void* stream,
-                                    void* const* events);
 
 /* ---- Key/value cache: decode and chunked prefill ----------------------------------------------
  * The second workload of the same operation: a few new tokens per sequence attend to everything

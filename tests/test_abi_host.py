@@ -34,58 +34,76 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.ne_abi_version() == 1
-    for s in range(7):
-        assert L.ne_status_str(s)
+    assert L.ne_abi_version() == 2
+    names = [L.ne_status_str(st) for st in range(8)]
+    assert len(set(names)) == 8 and all(names)
+    assert b"table" in names[6] and b"HIP" in names[7]
     assert L.ne_status_str(99) == b"unknown status"
+    assert set(binding.STATUS) == set(range(8))
+
+
+def up(x):
+    return (x + 255) // 256 * 256
+
+
+def ds_tiles(T, G):
+    nrt, nkb = -(-T * G // 64), -(-T // 64)
+    return sum(1 for kb in range(nkb) for rt in range(nrt) if rt >= kb * G)
+
+
+def amax_parts(B, T, Hkv):
+    g = B * Hkv
+    return max(1, min(64, T, max(16, -(-512 // g))))
+
+
+def sizes(B, T, Hq, Hkv, D, esz, base=1e4):
+    """(header + table, forward, backward base without the optional regions, v' copy)"""
+    nq, nk = B * T * Hq * D, B * T * Hkv * D
+    head = 256 + (up(T * (D // 2) * 8) if base > 0 else 0)
+    Tp = -(-T // 64) * 64
+    fwd = head + up(esz * nk) + up(esz * (B * Hkv * D * Tp if esz == 2 else nk))
+    bwd = head + 2 * up(esz * nq) + up(esz * nk) + 3 * up(4 * B * T * Hq) + up(4 * B * T * Hkv) + \
+        up(4 * B * Hkv) + up(4 * B * Hkv * amax_parts(B, T, Hkv))
+    return head, fwd, bwd, up(esz * nk)
+
+
+def wsb(L, is_bwd, B, T, Hq, Hkv, D, base=1e4, dt=binding.NE_BF16, flags=0):
+    return L.ne_rope_attn_workspace_bytes(is_bwd, B, T, Hq, Hkv, D, base, dt, flags)
 
 
 def test_workspace_sizes(L):
     B, T, Hq, Hkv, D = 4, 2048, 12, 4, 128
-
-    def up(x):
-        return (x + 255) // 256 * 256
-    nq, nk = B * T * Hq * D, B * T * Hkv * D
-    table = up(T * (D // 2) * 8)
-    fwd = L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
-    assert fwd == 2 * up(2 * nk) + table
-    # 16-bit backward: plus 8 KiB of stored dS per (64-row tile, 64-key block) pair that dK/dV
-    # visits, i.e. key block kb with row tiles kb G .. ceil(T G / 64) - 1, for every group
+    head, fwd, bwd, vcopy = sizes(B, T, Hq, Hkv, D, 2)
+    assert wsb(L, 0, B, T, Hq, Hkv, D) == fwd
+    # default backward: O(T) -- operand copies (v' included, the dQ pass recomputes from it), no dS
+    assert wsb(L, 1, B, T, Hq, Hkv, D) == bwd + vcopy
+    # stored dS: 8 KiB per (64-row tile, 64-key block) pair that dK/dV visits, for every group; no v' copy
     G = Hq // Hkv
-    nrt, nkb = -(-T * G // 64), -(-T // 64)
-    tiles = sum(1 for kb in range(nkb) for rt in range(nrt) if rt >= kb * G)
-    base = 2 * up(2 * nq) + 2 * up(2 * nk) + 3 * up(4 * B * T * Hq) + up(4 * B * T * Hkv) + table
-    bwd = L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16)
-    # with the stored dS the dK/dV pass reads v itself: no v' copy
-    assert bwd == base - up(2 * nk) + up(B * Hkv * tiles * 8192)
-    old = os.environ.get("NE_ROPE_ATTN_DS_MAX_BYTES")
-    try:  # the cap: the buffer holds the dS of as many whole groups as fit (0: none)
-        os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = "0"
-        assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16) == base
-        os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = str(B * Hkv * tiles * 8192)
-        assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16) == bwd
-        os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = str(tiles * 8192 - 1)
-        assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16) == base
-        for groups in (1, 3, 5):
-            os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = str(groups * tiles * 8192 + 4095)
-            assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_BF16) == \
-                base - up(2 * nk) + up(groups * tiles * 8192)
-    finally:
-        if old is None:
-            os.environ.pop("NE_ROPE_ATTN_DS_MAX_BYTES", None)
-        else:
-            os.environ["NE_ROPE_ATTN_DS_MAX_BYTES"] = old
-    # the fp32 path recomputes in dQ and stores no dS
-    assert L.ne_rope_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_F32) == \
-        2 * up(4 * nq) + 2 * up(4 * nk) + 3 * up(4 * B * T * Hq) + up(4 * B * T * Hkv) + table
-    assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, binding.NE_F32) == 2 * up(4 * nk) + table
+    assert wsb(L, 1, B, T, Hq, Hkv, D, flags=binding.NE_FLAG_STORE_DS) == \
+        bwd + up(B * Hkv * ds_tiles(T, G) * 8192)
+    # atomic dQ: the fp32 accumulator (plus 64 padding rows); no v' copy
+    assert wsb(L, 1, B, T, Hq, Hkv, D, flags=binding.NE_FLAG_NONDETERMINISTIC) == \
+        bwd + up(4 * (B * T * Hq * D + 64 * D))
+    # both: the atomic path
+    assert wsb(L, 1, B, T, Hq, Hkv, D, flags=binding.NE_FLAG_NONDETERMINISTIC | binding.NE_FLAG_STORE_DS) == \
+        wsb(L, 1, B, T, Hq, Hkv, D, flags=binding.NE_FLAG_NONDETERMINISTIC)
+    # the fp32 path always recomputes (flags have no effect on its layout)
+    h4, f4, b4, v4 = sizes(B, T, Hq, Hkv, D, 4)
+    assert wsb(L, 0, B, T, Hq, Hkv, D, dt=binding.NE_F32) == f4
+    for fl in (0, binding.NE_FLAG_STORE_DS, binding.NE_FLAG_NONDETERMINISTIC):
+        assert wsb(L, 1, B, T, Hq, Hkv, D, dt=binding.NE_F32, flags=fl) == b4 + v4
+    # no RoPE: no table after the header
+    assert wsb(L, 0, B, T, Hq, Hkv, D, base=0.0) == sizes(B, T, Hq, Hkv, D, 2, base=0.0)[1]
+    # a backward workspace also serves the forward (the table sits at the same place)
+    assert wsb(L, 1, B, T, Hq, Hkv, D) >= wsb(L, 0, B, T, Hq, Hkv, D)
     # ragged T: the forward's transposed V' copy pads every row of keys to a multiple of 64
-    Tr = 100
-    nkr, Tp = B * Tr * Hkv * D, 128
-    assert L.ne_rope_attn_fwd_workspace_bytes(B, Tr, Hq, Hkv, D, binding.NE_BF16) == \
-        up(2 * nkr) + up(2 * B * Hkv * D * Tp) + up(Tr * (D // 2) * 8)
-    assert L.ne_rope_attn_fwd_workspace_bytes(B, T, 12, 5, D, binding.NE_BF16) == 0
-    assert L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, 96, binding.NE_BF16) == 0
+    assert wsb(L, 0, B, 100, Hq, Hkv, D) == sizes(B, 100, Hq, Hkv, D, 2)[1]
+    # invalid arguments: 0
+    assert wsb(L, 0, B, T, 12, 5, D) == 0
+    assert wsb(L, 0, B, T, Hq, Hkv, 96) == 0
+    assert wsb(L, 0, B, T, Hq, Hkv, D, base=float("nan")) == 0
+    assert wsb(L, 1, B, T, Hq, Hkv, D, flags=binding.NE_FLAG_BF16_OPERANDS) == 0
+    assert wsb(L, 1, B, T, Hq, Hkv, D, flags=0x100) == 0
 
 
 def test_group_rows_beyond_32_bit_offsets_are_rejected(L):
@@ -93,12 +111,12 @@ def test_group_rows_beyond_32_bit_offsets_are_rejected(L):
     offsets: T G D times 2 (16-bit operands) or 4 (fp32 path) must stay below 2^31."""
     bf, f32 = binding.NE_BF16, binding.NE_F32
     # T G D = 2^29: fine with 16-bit operands, too large on the fp32 path
-    assert L.ne_rope_attn_bwd_workspace_bytes(1, 1 << 20, 4, 1, 128, bf) > 0
-    assert L.ne_rope_attn_bwd_workspace_bytes(1, 1 << 20, 4, 1, 128, f32) == 0
-    assert L.ne_rope_attn_fwd_workspace_bytes(1, 1 << 20, 4, 1, 128, f32) == 0
+    assert wsb(L, 1, 1, 1 << 20, 4, 1, 128) > 0
+    assert wsb(L, 1, 1, 1 << 20, 4, 1, 128, dt=f32) == 0
+    assert wsb(L, 0, 1, 1 << 20, 4, 1, 128, dt=f32) == 0
     # T G D = 2^31 / 2: too large for 16-bit operands as well
-    assert L.ne_rope_attn_fwd_workspace_bytes(1, 1 << 21, 8, 1, 64, bf) == 0
-    assert L.ne_rope_attn_fwd_workspace_bytes(1, 1 << 20, 8, 1, 64, bf) > 0
+    assert wsb(L, 0, 1, 1 << 21, 8, 1, 64, dt=bf) == 0
+    assert wsb(L, 0, 1, 1 << 20, 8, 1, 64, dt=bf) > 0
     # the same limit through an entry point (validation fails before any launch)
     assert fwd_call(L, T=1 << 21, Hq=8, Hkv=1, D=64, wsb=1 << 40) == 2   # NE_ERR_SHAPE
 
@@ -107,16 +125,16 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 
 
 def fwd_call(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, T=16, Hq=4, Hkv=2, D=64, base=1e4,
-             i=binding.NE_BF16, out=binding.NE_F32, ws=FAKE, wsb=None):
+             i=binding.NE_BF16, out=binding.NE_F32, flags=0, ws=FAKE, wsb=None):
     if wsb is None:
-        wsb = L.ne_rope_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D, i) if D in (32, 64, 128) else 1 << 20
-    return L.ne_rope_attn_fwd(q, k, v, o, lse, B, T, Hq, Hkv, D, base, i, out, ws, wsb, None)
+        wsb = L.ne_rope_attn_workspace_bytes(0, B, T, Hq, Hkv, D, base, i, 0) if D in (32, 64, 128) else 1 << 20
+    return L.ne_rope_attn_fwd(q, k, v, o, lse, B, T, Hq, Hkv, D, base, i, out, flags, ws, wsb, None)
 
 
 def bwd_call(L, ptrs=None, B=1, T=16, Hq=4, Hkv=2, D=64, base=1e4, i=binding.NE_BF16,
-             out=binding.NE_F32, ws=FAKE, wsb=1 << 30):
+             out=binding.NE_F32, flags=0, ws=FAKE, wsb=1 << 30):
     p = [FAKE] * 9 if ptrs is None else ptrs
-    return L.ne_rope_attn_bwd(*p, B, T, Hq, Hkv, D, base, i, out, ws, wsb, None)
+    return L.ne_rope_attn_bwd(*p, B, T, Hq, Hkv, D, base, i, out, flags, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -124,6 +142,8 @@ def bwd_call(L, ptrs=None, B=1, T=16, Hq=4, Hkv=2, D=64, base=1e4, i=binding.NE_
     (dict(B=0), 2), (dict(T=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(Hq=6, Hkv=4), 2),
     (dict(D=96), 3), (dict(D=16), 3), (dict(i=binding.NE_F32, out=binding.NE_BF16), 3),
     (dict(i=binding.NE_BF16, out=binding.NE_F16), 3), (dict(i=7), 3),
+    (dict(flags=binding.NE_FLAG_BF16_OPERANDS), 3), (dict(flags=binding.NE_FLAG_ROPE_HALF_SPLIT), 3),
+    (dict(flags=0x10), 3),
     (dict(q=FAKE + 8), 4), (dict(ws=FAKE + 4), 4),
     (dict(wsb=16), 5),
     (dict(base=float("nan")), 2),
@@ -140,12 +160,45 @@ def test_bwd_rejects_null(L, idx, status):
     assert bwd_call(L, ptrs=p) == status
 
 
-def test_bwd_rejects_misaligned_and_small_workspace(L):
+def test_bwd_rejects_misaligned_small_workspace_and_flags(L):
     p = [FAKE] * 9
     p[6] = FAKE + 2
     assert bwd_call(L, ptrs=p) == 4
     assert bwd_call(L, wsb=100) == 5
     assert bwd_call(L, Hq=5, Hkv=2) == 2
+    assert bwd_call(L, flags=binding.NE_FLAG_BF16_OPERANDS) == 3
+    assert bwd_call(L, flags=binding.NE_FLAG_ROPE_HALF_SPLIT | binding.NE_FLAG_STORE_DS) == 3
+    assert bwd_call(L, flags=1 << 31) == 3
+    # the atomic dQ needs its accumulator: a workspace one region short is rejected (the stored dS
+    # is covered below: a smaller buffer is valid down to one group)
+    nf = L.ne_rope_attn_workspace_bytes(1, 1, 16, 4, 2, 64, 1e4, binding.NE_BF16, binding.NE_FLAG_NONDETERMINISTIC)
+    assert bwd_call(L, flags=binding.NE_FLAG_NONDETERMINISTIC, wsb=nf - 256) == 5
+
+
+def test_stored_ds_workspace_below_one_group_is_rejected(L):
+    """With NE_FLAG_STORE_DS the workspace must hold at least one group's dS; the passes then run once
+    per batch of as many groups as it holds."""
+    B, T, Hq, Hkv, D = 2, 300, 6, 2, 64
+    full = L.ne_rope_attn_workspace_bytes(1, B, T, Hq, Hkv, D, 1e4, binding.NE_BF16, binding.NE_FLAG_STORE_DS)
+    one = ds_tiles(T, Hq // Hkv) * 8192
+    base = full - up(B * Hkv * one)
+    assert bwd_call(L, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, flags=binding.NE_FLAG_STORE_DS, wsb=base + one - 1) == 5
+    assert b"stored dS" in L.ne_last_error()
+
+
+def test_table_init_and_check_reject_before_touching_memory(L):
+    # rope_base <= 0: nothing to build or check
+    assert L.ne_rope_table_init(None, 0, 16, 64, 0.0, None) == 0
+    assert L.ne_rope_table_check(None, 0, 16, 64, -1.0, None) == 0
+    assert L.ne_rope_table_init(None, 1 << 20, 16, 64, 1e4, None) == 1
+    assert L.ne_rope_table_init(FAKE + 4, 1 << 20, 16, 64, 1e4, None) == 4
+    assert L.ne_rope_table_init(FAKE, 1 << 20, 0, 64, 1e4, None) == 2
+    assert L.ne_rope_table_init(FAKE, 1 << 20, 16, 48, 1e4, None) == 3
+    assert L.ne_rope_table_init(FAKE, 1 << 20, 16, 64, float("inf"), None) == 2
+    need = 256 + 16 * 32 * 8
+    assert L.ne_rope_table_init(FAKE, need - 1, 16, 64, 1e4, None) == 5
+    assert L.ne_rope_table_check(None, 1 << 20, 16, 64, 1e4, None) == 1
+    assert L.ne_rope_table_check(FAKE, 100, 16, 64, 1e4, None) == 5
 
 
 def test_binding_refuses_cpu_tensors():
@@ -156,14 +209,16 @@ def test_binding_refuses_cpu_tensors():
 
 
 # ---- window, cache and decode entry points ----------------------------------------------------
-def test_window_calls_reject_before_launch(L):
-    ev = None
-    args = [FAKE] * 5 + [1, 16, 4, 2, 64, 1e4, 8, binding.NE_BF16, binding.NE_F32, FAKE, 16, None, ev]
-    assert L.ne_rope_attn_fwd_window(*args) == 5          # workspace too small
+def test_ex_calls_reject_before_launch(L):
+    opts = binding.make_opts(8)
+    args = [FAKE] * 5 + [1, 16, 4, 2, 64, 1e4, ctypes.byref(opts), binding.NE_BF16, binding.NE_F32, 0, FAKE, 16, None,
+                         None]
+    assert L.ne_rope_attn_fwd_ex(*args) == 5          # workspace too small
     args[5] = 0
-    assert L.ne_rope_attn_fwd_window(*args) == 2          # B = 0
-    bargs = [FAKE] * 9 + [1, 16, 4, 2, 64, 1e4, 8, binding.NE_BF16, binding.NE_F32, None, 1 << 30, None, ev]
-    assert L.ne_rope_attn_bwd_window(*bargs) == 1         # null workspace
+    assert L.ne_rope_attn_fwd_ex(*args) == 2          # B = 0
+    bargs = [FAKE] * 9 + [1, 16, 4, 2, 64, 1e4, ctypes.byref(opts), binding.NE_BF16, binding.NE_F32, 0, None, 1 << 30,
+                          None, None]
+    assert L.ne_rope_attn_bwd_ex(*bargs) == 1         # null workspace
 
 
 def test_cache_and_decode_sizes(L):
@@ -213,8 +268,8 @@ def test_append_rejects_before_launch(L, kw, status):
 @pytest.mark.parametrize("qkn,status", [((float("nan"), 1e-6), 2), ((1.2, -1.0), 2), ((1.2, float("inf")), 2)])
 def test_ex_calls_reject_bad_qk_norm(L, qkn, status):
     opts = binding.make_opts(0, qkn)
-    wsf = L.ne_rope_attn_fwd_workspace_bytes(1, 16, 4, 2, 64, binding.NE_BF16)
+    wsf = L.ne_rope_attn_workspace_bytes(0, 1, 16, 4, 2, 64, 1e4, binding.NE_BF16, 0)
     assert L.ne_rope_attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 16, 4, 2, 64, 1e4, ctypes.byref(opts),
-                                 binding.NE_BF16, binding.NE_F32, FAKE, wsf, None, None) == status
+                                 binding.NE_BF16, binding.NE_F32, 0, FAKE, wsf, None, None) == status
     assert L.ne_rope_attn_bwd_ex(*([FAKE] * 9), 1, 16, 4, 2, 64, 1e4, ctypes.byref(opts), binding.NE_BF16,
-                                 binding.NE_F32, FAKE, 1 << 30, None, None) == status
+                                 binding.NE_F32, 0, FAKE, 1 << 30, None, None) == status

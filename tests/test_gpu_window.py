@@ -12,17 +12,18 @@ import torch
 
 import oracle
 from causal_gqa_flashattention_rope_amd import binding, inputs
-from tests.test_gpu_parity import DEV, check, f64, recompute_dq, slice_group
+from tests.test_gpu_parity import BWD_FLAGS, BWD_IDS, DEV, STORE_DS, bwd_workspace, check, f64, slice_group, zero_ref_scale
 
 pytestmark = pytest.mark.gpu
 
 _NAME = {torch.bfloat16: "bf16", torch.float32: "f32", torch.float16: "f16"}
 
 
-def run_gpu_window(q, k, v, dO, base, window, out_dtype):
+def run_gpu_window(q, k, v, dO, base, window, out_dtype, flags=0):
     qd, kd, vd, dOd = (t.to(DEV) for t in (q, k, v, dO))
-    o, lse = binding.ne_rope_attn_fwd_window(qd, kd, vd, base, window, out_dtype=out_dtype)
-    dq, dk, dv = binding.ne_rope_attn_bwd_window(qd, kd, vd, o, lse, dOd, base, window)
+    o, lse = binding.ne_rope_attn_fwd(qd, kd, vd, base, out_dtype=out_dtype, window=window)
+    ws = bwd_workspace(qd, kd, base, flags)
+    dq, dk, dv = binding.ne_rope_attn_bwd(qd, kd, vd, o, lse, dOd, base, workspace=ws, flags=flags, window=window)
     torch.cuda.synchronize()
     return [t.cpu() for t in (o, lse, dq, dk, dv)]
 
@@ -36,13 +37,12 @@ def ref_window(q, k, v, dO, o_gpu, base, window, out_dtype):
     return (ro, rlse) + tuple(grads)
 
 
-def window_parity(q, k, v, dO, base, window, out_dtype, in_dtype):
-    got = run_gpu_window(q, k, v, dO, base, window, out_dtype)
+def window_parity(q, k, v, dO, base, window, out_dtype, in_dtype, flags=0):
+    got = run_gpu_window(q, k, v, dO, base, window, out_dtype, flags)
     ref = ref_window(q, k, v, dO, got[0], base, window, out_dtype)
     # with W = 1 the exact dq and dk are zero (P = 1, and dS = dP - Delta cancels up to the rounding
-    # of two D-term dot products), so their error is measured against the largest reference
-    # gradient of the call, as the single-token closed-form test does
-    gscale = max(float(np.max(np.abs(x))) for x in ref[2:])
+    # of two D-term dot products): the zero-reference scale of test_gpu_parity.py
+    gscale = zero_ref_scale(in_dtype, ref[2:])
     for name, g, r in zip(("o", "lse", "dq", "dk", "dv"), got, ref):
         check(name, g, r, in_dtype, out_dtype, zero_scale=gscale)
 
@@ -64,12 +64,12 @@ def test_window_parity_small(shape, window, in_dt):
 
 
 @pytest.mark.parametrize("shape", SHAPES)
-@pytest.mark.parametrize("window", [5, 65])
-def test_window_parity_small_recompute_dq(shape, window):
+@pytest.mark.parametrize("window", [1, 5, 65])
+@pytest.mark.parametrize("flags", BWD_FLAGS[1:], ids=BWD_IDS[1:])
+def test_window_parity_small_other_backwards(shape, window, flags):
     B, T, Hq, Hkv, D = shape
     q, k, v, dO = inputs.random_case(B, T, Hq, Hkv, D, seed=2000 + window, dtype="bf16")
-    with recompute_dq():
-        window_parity(q, k, v, dO, 1.0e4, window, torch.float32, torch.bfloat16)
+    window_parity(q, k, v, dO, 1.0e4, window, torch.float32, torch.bfloat16, flags=flags)
 
 
 @pytest.mark.parametrize("in_dt", [torch.bfloat16, torch.float16])
@@ -83,8 +83,8 @@ def test_window_of_T_or_more_equals_the_causal_call_bitwise():
     o, lse = binding.ne_rope_attn_fwd(q, k, v, 1e4)
     ref = (o, lse) + tuple(binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, 1e4))
     for W in (0, -3, 190, 191, 10 ** 6):
-        ow, lw = binding.ne_rope_attn_fwd_window(q, k, v, 1e4, W)
-        got = (ow, lw) + tuple(binding.ne_rope_attn_bwd_window(q, k, v, ow, lw, dO, 1e4, W))
+        ow, lw = binding.ne_rope_attn_fwd(q, k, v, 1e4, window=W)
+        got = (ow, lw) + tuple(binding.ne_rope_attn_bwd(q, k, v, ow, lw, dO, 1e4, window=W))
         for a, b in zip(got, ref):
             assert torch.equal(a, b), W
 
@@ -104,20 +104,23 @@ def test_window_keys_outside_are_bitwise_invisible():
     assert not torch.equal(o1[:, j:j + W], o2[:, j:j + W])
 
 
-def test_window_backward_is_bitwise_deterministic():
+@pytest.mark.parametrize("flags", BWD_FLAGS[:2], ids=BWD_IDS[:2])
+def test_window_backward_is_bitwise_deterministic(flags):
     q, k, v, dO = (t.to(DEV) for t in inputs.random_case(2, 700, 12, 4, 128, seed=17, dtype="bf16"))
-    o, lse = binding.ne_rope_attn_fwd_window(q, k, v, 1e4, 175)
-    first = [t.clone() for t in binding.ne_rope_attn_bwd_window(q, k, v, o, lse, dO, 1e4, 175)]
-    again = binding.ne_rope_attn_bwd_window(q, k, v, o, lse, dO, 1e4, 175)
+    o, lse = binding.ne_rope_attn_fwd(q, k, v, 1e4, window=175)
+    ws = bwd_workspace(q, k, 1e4, flags)
+    first = [t.clone() for t in binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, 1e4, window=175, workspace=ws,
+                                                         flags=flags)]
+    again = binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, 1e4, window=175, workspace=ws, flags=flags)
     for a, b in zip(first, again):
         assert torch.equal(a, b)
 
 
-def workload_window_parity(name, window, groups, out_dtype=torch.float32):
+def workload_window_parity(name, window, groups, out_dtype=torch.float32, flags=0):
     """Full-size GPU run with a window; compare the (batch, KV group) slices the oracle recomputes."""
     w = inputs.WORKLOADS[name]
     q, k, v, dO = inputs.make_inputs(w)
-    got = run_gpu_window(q, k, v, dO, w.rope_base, window, out_dtype)
+    got = run_gpu_window(q, k, v, dO, w.rope_base, window, out_dtype, flags)
     o, lse, dq, dk, dv = got
     G = w.G
     for b, g in groups:
@@ -130,8 +133,9 @@ def workload_window_parity(name, window, groups, out_dtype=torch.float32):
             check(nm, gpart, r, q.dtype, out_dtype)
 
 
-def test_window_workload_wide_gqa_quarter_context():
-    workload_window_parity("wide_gqa_t2048_d128", 512, [(0, 0), (3, 2)])
+@pytest.mark.parametrize("flags", BWD_FLAGS, ids=BWD_IDS)
+def test_window_workload_wide_gqa_quarter_context(flags):
+    workload_window_parity("wide_gqa_t2048_d128", 512, [(0, 0), (3, 2)], flags=flags)
 
 
 def test_window_workload_wide_gqa_quarter_context_bf16_out():

@@ -25,7 +25,7 @@ NE_FLAG_STORE_DS = 0x8
 EXPORTS = ("ne_rope_attn_workspace_bytes", "ne_rope_table_init", "ne_rope_table_check",
            "ne_rope_attn_fwd", "ne_rope_attn_bwd", "ne_rope_attn_fwd_ex", "ne_rope_attn_bwd_ex",
            "ne_kv_cache_bytes", "ne_kv_cache_append", "ne_rope_attn_decode_workspace_bytes",
-           "ne_rope_attn_decode", "ne_qkv_rope_workspace_bytes", "ne_qkv_rope_proj",
+           "ne_rope_attn_decode", "ne_rope_attn_decode_noalloc", "ne_qkv_rope_workspace_bytes", "ne_qkv_rope_proj",
            "ne_status_str", "ne_last_error", "ne_abi_version")
 
 
@@ -86,6 +86,8 @@ def lib():
     L.ne_rope_attn_decode_workspace_bytes.restype = sz
     L.ne_rope_attn_decode.argtypes = [vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, d, op, i, i, vp, sz, vp, evp]
     L.ne_rope_attn_decode.restype = i
+    L.ne_rope_attn_decode_noalloc.argtypes = [vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, d, op, i, i, vp]
+    L.ne_rope_attn_decode_noalloc.restype = i
     L.ne_qkv_rope_workspace_bytes.argtypes = [i, i]
     L.ne_qkv_rope_workspace_bytes.restype = sz
     L.ne_qkv_rope_proj.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, d, op, i, i, vp, sz, vp, evp]
@@ -301,6 +303,28 @@ def ne_rope_attn_decode(q, cache, cache_lens, Tcap, Hkv, rope_base, window=0, ou
                                      _DT[q.dtype], _DT[o.dtype], _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(),
                                      _events_arg(events, 4)))
+    return o, lse
+
+
+DECODE_SCRATCH_BYTES = 64 << 20
+
+
+def ne_rope_attn_decode_noalloc(q, cache, cache_lens, Tcap, Hkv, rope_base, window=0, out_dtype=torch.float32,
+                                o=None, lse=None, qk_norm=None):
+    """ne_rope_attn_decode without a workspace: the split partials go to the library's own scratch
+    (DECODE_SCRATCH_BYTES per GPU); shapes that need more are rejected.  Pass o and lse to make the
+    call allocate nothing at all."""
+    _require_gpu(q, cache)
+    B, Tq, Hq, D = q.shape
+    lens = _lens_arg(cache_lens, B, q.device)
+    if o is None:
+        o = torch.empty((B, Tq, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    opts = make_opts(window, qk_norm)
+    _check(lib().ne_rope_attn_decode_noalloc(_ptr(q), _ptr(cache), _nbytes(cache), _ptr(lens), _ptr(o), _ptr(lse),
+                                             B, Tq, Tcap, Hq, Hkv, D, float(rope_base), ctypes.byref(opts),
+                                             _DT[q.dtype], _DT[o.dtype], _stream()))
     return o, lse
 
 

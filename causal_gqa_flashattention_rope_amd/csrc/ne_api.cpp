@@ -27,6 +27,7 @@ ne_status_t fail(ne_status_t s, const char* fmt, ...) {
 }
 
 constexpr size_t kAlign = 256;
+static_assert(ne::kDecodeScratchBytes == NE_DECODE_SCRATCH_BYTES, "the header states the scratch size");
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
@@ -495,18 +496,23 @@ size_t ne_rope_attn_decode_workspace_bytes(int B, int Tq, int Tcap, int Hq, int 
     return decode_layout(B, Tq, Tcap, Hq, Hkv, head_dim).total;
 }
 
-ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_bytes, const int* cache_lens,
-                                void* o, float* lse, int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
-                                double rope_base, const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
-                                void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
-    if (!q || !cache || !cache_lens || !o || !lse || !workspace)
+}  // extern "C"
+
+namespace {
+
+// workspace == nullptr with noalloc: the library's file-scope scratch (ne::decode_scratch).
+ne_status_t decode_impl(const void* q, const void* cache, size_t cache_bytes, const int* cache_lens,
+                        void* o, float* lse, int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
+                        double rope_base, const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                        void* workspace, size_t workspace_bytes, bool noalloc, void* stream, void* const* events) {
+    if (!q || !cache || !cache_lens || !o || !lse || (!workspace && !noalloc))
         return fail(NE_ERR_NULL, "ne_rope_attn_decode: q, cache, cache_lens, o, lse and workspace must be non-null");
     ne_status_t s = check_decode(B, Tq, Tcap, Hq, Hkv, head_dim);
     if (s != NE_OK) return s;
     if (!decode_dtype_ok(in_dtype, out_dtype))
         return fail(NE_ERR_UNSUPPORTED, "ne_rope_attn_decode: dtype pair in=%d out=%d is not supported",
                     (int)in_dtype, (int)out_dtype);
-    if (!aligned16(q) || !aligned16(cache) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace) ||
+    if (!aligned16(q) || !aligned16(cache) || !aligned16(o) || !aligned16(lse) || (!noalloc && !aligned16(workspace)) ||
         ((uintptr_t)cache_lens & 3u))
         return fail(NE_ERR_ALIGN, "ne_rope_attn_decode: pointers must be 16-byte aligned (cache_lens 4)");
     if (!std::isfinite(rope_base)) return fail(NE_ERR_SHAPE, "rope_base must be finite");
@@ -517,8 +523,19 @@ ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_b
     ne::QkNorm qkn{};
     if ((s = check_opts(opts, &qkn)) != NE_OK) return s;
     const DecodeLayout L = decode_layout(B, Tq, Tcap, Hq, Hkv, head_dim);
-    if (workspace_bytes < L.total)
+    if (noalloc) {
+        if (L.total > ne::kDecodeScratchBytes)
+            return fail(NE_ERR_WORKSPACE,
+                        "ne_rope_attn_decode_noalloc: the split partials need %zu bytes, more than the %zu bytes of "
+                        "the library's scratch (use ne_rope_attn_decode with a workspace)", L.total,
+                        ne::kDecodeScratchBytes);
+        hipError_t e = ne::decode_scratch(&workspace);
+        if (e != hipSuccess)
+            return fail(NE_ERR_HIP, "ne_rope_attn_decode_noalloc: no scratch address on this device: %s",
+                        hipGetErrorString(e));
+    } else if (workspace_bytes < L.total) {
         return fail(NE_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
+    }
     char* ws = (char*)workspace;
     ne::DecodeArgs a{};
     a.q = q; a.cache = cache; a.lens = cache_lens;
@@ -536,6 +553,26 @@ ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_b
                                      (hipEvent_t const*)events);
     if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_attn_decode: launch failed: %s", hipGetErrorString(e));
     return NE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_bytes, const int* cache_lens,
+                                void* o, float* lse, int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
+                                double rope_base, const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype,
+                                void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    return decode_impl(q, cache, cache_bytes, cache_lens, o, lse, B, Tq, Tcap, Hq, Hkv, head_dim, rope_base, opts,
+                       in_dtype, out_dtype, workspace, workspace_bytes, false, stream, events);
+}
+
+ne_status_t ne_rope_attn_decode_noalloc(const void* q, const void* cache, size_t cache_bytes, const int* cache_lens,
+                                        void* o, float* lse, int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
+                                        double rope_base, const ne_attn_opts_t* opts, ne_dtype_t in_dtype,
+                                        ne_dtype_t out_dtype, void* stream) {
+    return decode_impl(q, cache, cache_bytes, cache_lens, o, lse, B, Tq, Tcap, Hq, Hkv, head_dim, rope_base, opts,
+                       in_dtype, out_dtype, nullptr, 0, true, stream, nullptr);
 }
 
 }  // extern "C"

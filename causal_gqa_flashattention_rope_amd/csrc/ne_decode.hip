@@ -16,6 +16,8 @@
 // workgroups (split-KV); a second kernel merges the partial results by the log-sum-exp rule.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "ne_common.hpp"
 #include "ne_launch.hpp"
 
@@ -420,6 +422,34 @@ hipError_t launch_append(int in_dt, int D, const AppendArgs& a, hipStream_t s) {
     if (in_dt == 1) { NE_DDISPATCH(launch_append_t, __bf16) }
     if (in_dt == 2) { NE_DDISPATCH(launch_append_t, _Float16) }
     return hipErrorInvalidValue;
+}
+
+// ---- the decode without a caller workspace ---------------------------------------------------
+// A file-scope device array holds the split partials for callers that cannot allocate.  Its name is
+// a host-side stand-in: host code uses only the address hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode(int in_dt, int out_dt, int D, const DecodeArgs& a, hipStream_t s, hipEvent_t const* ev) {

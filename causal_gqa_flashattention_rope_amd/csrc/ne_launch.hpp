@@ -155,5 +155,10 @@ hipError_t launch_append(int in_dt, int D, const AppendArgs& a, hipStream_t s);
 hipError_t launch_qkv(int in_dt, int out_dt, int D, const QkvArgs& a, hipStream_t s, hipEvent_t const* ev);
 // ev (nullable): pairs around the split kernel and the merge (4 entries).
 hipError_t launch_decode(int in_dt, int out_dt, int D, const DecodeArgs& a, hipStream_t s, hipEvent_t const* ev);
+// The decode's split partials without a caller workspace: a file-scope device array of this many
+// bytes, shared by every call on a device (calls that overlap on one device race).  decode_scratch
+// gives its address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+hipError_t decode_scratch(void** out);
 
 }  // namespace ne

@@ -254,6 +254,23 @@ ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_b
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 void* const* events);
 
+/* The same decode for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): no workspace argument.  The split partials live in a
+ * scratch array inside the library, NE_DECODE_SCRATCH_BYTES (64 MiB) per GPU, held until the process
+ * ends; its address on the current device is looked up on the first call there and kept (the one
+ * piece of library state besides the error message).  Shapes whose partials
+ * (ne_rope_attn_decode_workspace_bytes) exceed it are rejected with NE_ERR_WORKSPACE before anything
+ * is enqueued.  Nothing is allocated or freed.  Every call on a device shares that device's array, so
+ * calls that overlap on one device (different streams, or threads) race: order them on one stream.
+ * Each call writes every partial it reads, so no state carries over between calls.  Same arguments,
+ * results (bitwise) and errors as ne_rope_attn_decode otherwise. */
+#define NE_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+ne_status_t ne_rope_attn_decode_noalloc(const void* q, const void* cache, size_t cache_bytes,
+                                        const int* cache_lens, void* o, float* lse,
+                                        int B, int Tq, int Tcap, int Hq, int Hkv, int head_dim,
+                                        double rope_base, const ne_attn_opts_t* opts,
+                                        ne_dtype_t in_dtype, ne_dtype_t out_dtype, void* stream);
+
 /* ---- QKV projection with the RoPE epilogue ----------------------------------------------------
  * The step before attention: y = x W^T for every token, then RoPE on the query and key heads --
  * on the pages a tensor-core matrix product followed by a RoPE kernel of its own ("NanoEuler: 使用

@@ -273,3 +273,18 @@ def test_ex_calls_reject_bad_qk_norm(L, qkn, status):
                                  binding.NE_BF16, binding.NE_F32, 0, FAKE, wsf, None, None) == status
     assert L.ne_rope_attn_bwd_ex(*([FAKE] * 9), 1, 16, 4, 2, 64, 1e4, ctypes.byref(opts), binding.NE_BF16,
                                  binding.NE_F32, 0, FAKE, 1 << 30, None, None) == status
+
+
+def test_noalloc_decode_rejects_before_touching_the_device(L):
+    """The scratch holds NE_DECODE_SCRATCH_BYTES; larger partials fail validation before any HIP call."""
+    B, Tq, Tcap, Hq, Hkv, D = 64, 1, 8192, 32, 8, 128
+    assert L.ne_rope_attn_decode_workspace_bytes(B, Tq, Tcap, Hq, Hkv, D, binding.NE_BF16) > 64 << 20
+    opts = binding.make_opts(0)
+    st = L.ne_rope_attn_decode_noalloc(FAKE, FAKE, 1 << 40, FAKE, FAKE, FAKE, B, Tq, Tcap, Hq, Hkv, D, 1e4,
+                                       ctypes.byref(opts), binding.NE_BF16, binding.NE_F32, None)
+    assert st == 5 and b"scratch" in L.ne_last_error()
+    assert L.ne_rope_attn_decode_noalloc(None, FAKE, 1 << 40, FAKE, FAKE, FAKE, 2, 1, 256, 4, 2, 64, 1e4,
+                                         ctypes.byref(opts), binding.NE_BF16, binding.NE_F32, None) == 1
+    assert L.ne_rope_attn_decode_noalloc(FAKE, FAKE, 1 << 40, FAKE, FAKE, FAKE, 2, 1, 100, 4, 2, 64, 1e4,
+                                         ctypes.byref(opts), binding.NE_BF16, binding.NE_F32, None) == 2
+

@@ -84,10 +84,12 @@ size_t ds_group_bytes(int T, int Hq, int Hkv) {
 }
 constexpr size_t kDsCap = (size_t)4 << 30;   // the stored dS buffer holds at most 4 GiB
 
-// Partial maxima of |dO| per group: enough parts for about 512 workgroups, at most 64 and T.
+// Partial maxima of |dO| per group: one per block of the max pass, which reads whole tokens of one
+// batch element -- enough blocks for about 512 workgroups, each at least 8 tokens, at most 1024.
 int amax_parts(int B, int T, int Hkv) {
-    const int64_t g = (int64_t)B * Hkv;
-    return (int)std::max<int64_t>(1, std::min<int64_t>({64, (int64_t)T, std::max<int64_t>(16, (512 + g - 1) / g)}));
+    (void)Hkv;
+    const int64_t want = std::max<int64_t>(1, (512 + B - 1) / B);
+    return (int)std::max<int64_t>(1, std::min<int64_t>({want, (T + 7) / 8, 1024}));
 }
 
 int bwd_mode(ne_dtype_t in, unsigned flags, int T, int Hq, int Hkv) {

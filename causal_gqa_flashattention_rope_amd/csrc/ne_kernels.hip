@@ -89,30 +89,44 @@ __device__ __forceinline__ void load8(const T16* p, float (&x)[8]) {
     for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
 }
 
-// Partial maxima of |dO| for the per-group scale of dO (16-bit operands).  grid (nparts, B * Hkv),
-// 256 threads: block (p, g) reads tokens [p tpp, (p + 1) tpp) of the G heads of group g.
+// Partial maxima of |dO| for the per-group scale of dO (16-bit operands).  grid (nparts, B), 256
+// threads: block (p, b) reads tokens [p tpp, (p + 1) tpp) of batch b, all Hq heads (contiguous
+// rows), and writes the max of each of its KV groups to part[(b Hkv + g) nparts + p].  Groups are
+// reduced in LDS (max of non-negative floats = max of their bit patterns as unsigned), up to
+// kAmaxGroups per block; more groups are covered in passes over the rows.
+constexpr int kAmaxGroups = 256;
 template <typename TI, int D>
 __global__ __launch_bounds__(256) void dO_amax_kernel(AmaxArgs a) {
-    __shared__ float red[4];
-    const int g = blockIdx.y, p = blockIdx.x;
-    const int b = g / a.Hkv, hkv = g % a.Hkv, G = a.Hq / a.Hkv;
-    const int t0 = p * a.tpp, t1 = min(a.T, t0 + a.tpp);
+    __shared__ unsigned smax[kAmaxGroups];
     constexpr int CPR = D / 8;
-    const int rows = max(0, t1 - t0) * G;
-    float m = 0.f;
-    for (int idx = threadIdx.x; idx < rows * CPR; idx += 256) {
-        const int r = idx / CPR, ch = idx % CPR;
-        const int t = t0 + r / G, hq = hkv * G + r % G;
-        float x[8];
-        load8((const TI*)a.dO + (((size_t)b * a.T + t) * a.Hq + hq) * D + ch * 8, x);
+    const int p = blockIdx.x, b = blockIdx.y;
+    const int G = a.Hq / a.Hkv;
+    const int t0 = p * a.tpp, t1 = min(a.T, t0 + a.tpp);
+    const int rows = max(0, t1 - t0) * a.Hq;                      // (token, head) rows, contiguous
+    const TI* base = (const TI*)a.dO + ((size_t)b * a.T + t0) * a.Hq * D;
+    for (int g0 = 0; g0 < a.Hkv; g0 += kAmaxGroups) {
+        const int ng = min(kAmaxGroups, a.Hkv - g0);
+        for (int i = threadIdx.x; i < ng; i += 256) smax[i] = 0u;
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < rows * CPR; idx += 256) {
+            const int r = idx / CPR, g = (r % a.Hq) / G - g0;
+            if (g < 0 || g >= ng) continue;
+            float x[8];
+            load8(base + (size_t)r * D + (idx % CPR) * 8, x);
+            float m = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+            // (fmaxf skips a NaN element here; it still reaches the gradients through dO itself)
+            atomicMax(&smax[g], __float_as_uint(m));
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < ng; i += 256)
+            a.part[((size_t)b * a.Hkv + g0 + i) * a.nparts + p] = __uint_as_float(smax[i]);
+        __syncthreads();
     }
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) a.part[(size_t)g * a.nparts + p] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
+
+constexpr int kPrepScales = 256;   // groups per batch element whose dO scales a preparation block keeps
 
 // The power of two s that brings a group's max |dO| into [4, 8) (1 for an all-zero or non-finite
 // maximum): s dO is exact in fp32 and its fp16 rounding keeps the relative precision of every
@@ -149,12 +163,25 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     constexpr int TT = 8;
     constexpr int CPR = D / 8;  // 8-element chunks per row
     __shared__ float2 cs[TT * (D / 2)];
+    __shared__ unsigned gmax[BWD ? kPrepScales : 1];   // backward: max |dO| of each group of batch b
+    __shared__ float gsc[BWD ? kPrepScales : 1];       // and its power-of-two scale
     const int t0 = blockIdx.x * TT, b = blockIdx.y;
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
     const bool rope = a.rope_base > 0.0;
     for (int idx = threadIdx.x; idx < TT * (D / 2); idx += blockDim.x) {
         const int t = t0 + idx / (D / 2);
         cs[idx] = rope && t < T ? a.table[(size_t)t * (D / 2) + idx % (D / 2)] : make_float2(1.f, 0.f);
+    }
+    if constexpr (BWD && sizeof(OP) == 2) {
+        if (Hkv <= kPrepScales) {   // the groups of batch b: their partial maxima reduced once per block
+            for (int g = threadIdx.x; g < Hkv; g += blockDim.x) gmax[g] = 0u;
+            __syncthreads();
+            const int n = Hkv * a.nparts;
+            for (int i = threadIdx.x; i < n; i += blockDim.x)
+                atomicMax(&gmax[i / a.nparts], __float_as_uint(a.amax_part[(size_t)b * Hkv * a.nparts + i]));
+            __syncthreads();
+            for (int g = threadIdx.x; g < Hkv; g += blockDim.x) gsc[g] = dO_scale(__uint_as_float(gmax[g]));
+        }
     }
     const float guard = table_guard(a);
     __syncthreads();
@@ -175,17 +202,20 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         const float2* csr = cs + tl * (D / 2);
         float part = 0.f;  // Delta partial (dO rows only)
         int dO_row = -1;
-        // 16-bit operands: the power-of-two scale of this dO row's group, from the group's partial
-        // maxima (read by the row's CPR lanes together)
+        // 16-bit operands: the power-of-two scale of this dO row's group
         float sdo = 1.f;
         if constexpr (BWD && sizeof(OP) == 2) {
-            float m = 0.f;
-            if (live && which >= Hq + 2 * Hkv) {
-                const size_t grp = (size_t)b * Hkv + (which - Hq - 2 * Hkv) / G;
-                for (int j = chunk; j < a.nparts; j += CPR) m = fmaxf(m, a.amax_part[grp * a.nparts + j]);
+            if (which >= Hq + 2 * Hkv) {
+                const int g = (which - Hq - 2 * Hkv) / G;
+                if (Hkv <= kPrepScales) {
+                    sdo = gsc[g];
+                } else {  // more groups than the block keeps: reduce this group's partial maxima here
+                    const float* pp = a.amax_part + ((size_t)b * Hkv + g) * a.nparts;
+                    float m = 0.f;
+                    for (int j = 0; j < a.nparts; ++j) m = fmaxf(m, pp[j]);
+                    sdo = dO_scale(m);
+                }
             }
-            for (int off = 1; off < CPR; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-            sdo = dO_scale(m);
         }
         // QK norm: the factor gain / rms of this thread's q or k row (its CPR chunks sit in
         // consecutive lanes), and 1/rms kept for the backward's epilogues
@@ -1335,8 +1365,9 @@ void dkdv_kernel_h(BwdArgs a) {
                     const OP* Qs = lds + st * 2 * TILE;
                     const OP* Os = Qs + TILE;
                     const int Rh = rstart + s * BMR + 32 * rh;
+                    const half8 fl = fold_frag(-rowv[st][0][32 * rh + c], h);  // ahead of the chain
                     floatx16 x = chain(Qs, IC<AT ? 1 : 0>{});
-                    x = M::mma(fold_frag(-rowv[st][0][32 * rh + c], h), fw, x);  // S - lse2
+                    x = M::mma(fl, fw, x);  // S - lse2
                     half8 tf0[NDB];
                     tr_frags0(Os, tf0);  // in flight during the exponentials
                     if (needs_mask(s)) {
@@ -1373,8 +1404,9 @@ void dkdv_kernel_h(BwdArgs a) {
                     const int st = (s - 1) % NST;
                     const OP* Qs = lds + st * 2 * TILE;
                     const OP* Os = Qs + TILE;
+                    const half8 fd = fold_frag(-rowv[st][1][32 * rh + c], h);  // ahead of the chain
                     floatx16 y = chain(Os, IC<0>{});
-                    y = M::mma(fold_frag(-rowv[st][1][32 * rh + c], h), fw, y);  // dP - Delta
+                    y = M::mma(fd, fw, y);  // dP - Delta
                     half8 tf0[NDB];
                     tr_frags0(Qs, tf0);  // in flight during dS
                     half8 dsf[2];
@@ -2069,7 +2101,7 @@ static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am,
     const Marks m{ev, s};
     NE_TRY(m.before(0));
     if constexpr (sizeof(OP) == 2) {
-        hipLaunchKernelGGL((dO_amax_kernel<TI, D>), dim3(am.nparts, ba.B * ba.Hkv), dim3(256), 0, s, am);
+        hipLaunchKernelGGL((dO_amax_kernel<TI, D>), dim3(am.nparts, ba.B), dim3(256), 0, s, am);
         NE_TRY(hipGetLastError());
     }
     hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, true>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);

@@ -52,8 +52,7 @@ def ds_tiles(T, G):
 
 
 def amax_parts(B, T, Hkv):
-    g = B * Hkv
-    return max(1, min(64, T, max(16, -(-512 // g))))
+    return max(1, min(-(-512 // B), -(-T // 8), 1024))
 
 
 def sizes(B, T, Hq, Hkv, D, esz, base=1e4):

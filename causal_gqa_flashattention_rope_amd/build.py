@@ -14,7 +14,7 @@ BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["ne_kernels.hip", "ne_decode.hip", "ne_qkv.hip", "ne_api.cpp"]
+SOURCES = ["ne_kernels.hip", "ne_decode.hip", "ne_qkv.hip", "ne_api.cpp", "ne_split.cpp"]
 HEADERS = ["ne_common.hpp", "ne_launch.hpp", os.path.join("..", "..", "include", "ne_rope_attn.h")]
 
 FLAGS = [

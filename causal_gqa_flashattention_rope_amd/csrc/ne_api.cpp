@@ -31,7 +31,7 @@ static_assert(ne::kDecodeScratchBytes == NE_DECODE_SCRATCH_BYTES, "the header st
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t table, qh, kh, vh, dOh, delta, lse2, rq, rk, dsc, amax, dqacc, ds, total;
+    size_t table, qh, kh, vh, dOh, delta, lse2, rq, rk, dsc, amax, dqacc, ds, spart, scnt, total;
     int mode;       // ne::kBwdRecompute, kBwdStoredDs or kBwdAtomic (backward)
     int ds_groups;  // stored dS: groups whose dS the workspace holds at once
     int nparts;     // partial maxima of |dO| per group (16-bit backward)
@@ -99,6 +99,16 @@ int bwd_mode(ne_dtype_t in, unsigned flags, int T, int Hq, int Hkv) {
     return ne::kBwdRecompute;
 }
 
+// Split plan of the 16-bit forward (256-row blocks, one workgroup per CU, up to 4 pieces) or of
+// the recomputing dQ pass (128-row blocks, two per CU, 2 pieces: its registers are all taken).  The plan struct is large: one per thread, reused.
+ne::SplitPlan* split_scratch() {
+    thread_local ne::SplitPlan sp;
+    return &sp;
+}
+void plan_for(bool bwd, int T, int G, int ngrp, ne::SplitPlan* sp) {
+    ne::split_plan(T, G, ngrp, bwd ? 128 : 256, bwd ? 2 : 1, bwd ? 2 : 4, sp);
+}
+
 // The workspace regions.  ds_bytes: bytes available for the stored dS (stored-dS mode), or
 // SIZE_MAX to size it for every group (up to the cap).
 Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, double base, ne_dtype_t in, unsigned flags,
@@ -135,6 +145,18 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, double base, ne_dt
             L.ds_groups = (int)std::min<size_t>(ngrp, cap / gb);
             L.ds = off;
             off += up((size_t)std::max(L.ds_groups, 1) * gb);
+        }
+    }
+    // partial results and counters of the split row blocks: forward (16-bit operands), or the
+    // recomputing dQ pass; sized for the plan without a window (a window turns the split off)
+    if (in != NE_F32 && (!bwd || L.mode == ne::kBwdRecompute)) {
+        ne::SplitPlan* sp = split_scratch();
+        plan_for(bwd, T, Hq / Hkv, B * Hkv, sp);
+        if (sp->njobs) {
+            const size_t nsb = (size_t)B * Hkv * (sp->nrb - sp->rs);
+            const size_t slot = bwd ? ne::split_slot_floats_dq(D) : ne::split_slot_floats_fwd(D);
+            L.spart = off; off += up(nsb * sp->np * slot * 4);
+            L.scnt = off; off += up(nsb * 2 * 4);
         }
     }
     L.total = off;
@@ -192,7 +214,9 @@ size_t ne_rope_attn_workspace_bytes(int is_bwd, int B, int T, int Hq, int Hkv, i
     if (in_dtype != NE_F32 && in_dtype != NE_BF16 && in_dtype != NE_F16) return 0;
     if (check_shape(B, T, Hq, Hkv, head_dim, in_dtype == NE_F32 ? 4 : 2) != NE_OK) return 0;
     if (check_flags(flags) != NE_OK || !std::isfinite(rope_base)) return 0;
-    return layout(is_bwd != 0, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, flags).total;
+    const size_t fwd = layout(false, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, flags).total;
+    // a backward workspace of this size also serves the forward of the same arguments
+    return is_bwd ? std::max(fwd, layout(true, B, T, Hq, Hkv, head_dim, rope_base, in_dtype, flags).total) : fwd;
 }
 
 ne_status_t ne_rope_table_init(void* workspace, size_t workspace_bytes, int T, int head_dim, double rope_base,
@@ -271,7 +295,18 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     fa.window = visible_keys(opts->window, T);
     fa.qkn = qkn;
     fa.nrb = (int)(((int64_t)T * G + 127) / 128);
-    hipError_t e = ne::launch_fwd((int)in_dtype, (int)out_dtype, head_dim, pa, fa, (hipStream_t)stream,
+    ne::SplitPlan* sp = split_scratch();
+    sp->njobs = 0;
+    if (in_dtype != NE_F32 && fa.window >= T) {
+        plan_for(false, T, G, B * Hkv, sp);
+        if (sp->njobs) {
+            sp->part = (float*)(ws + L.spart);
+            sp->cnt = (unsigned*)(ws + L.scnt);
+            pa.split_cnt = sp->cnt;
+            pa.nsplit_cnt = 2 * B * Hkv * (sp->nrb - sp->rs);
+        }
+    }
+    hipError_t e = ne::launch_fwd((int)in_dtype, (int)out_dtype, head_dim, pa, fa, *sp, (hipStream_t)stream,
                                   (hipEvent_t const*)events);
     if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_attn_fwd: launch failed: %s", hipGetErrorString(e));
     return NE_OK;
@@ -340,8 +375,19 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     ba.nrb = (int)(((int64_t)T * G + 127) / 128);
     ba.rope_base = rope_base;
     ba.scale = (float)(1.0 / std::sqrt((double)head_dim));
-    hipError_t e = ne::launch_bwd((int)in_dtype, (int)out_dtype, head_dim, L.mode, pa, am, ba, (hipStream_t)stream,
-                                  (hipEvent_t const*)events);
+    ne::SplitPlan* sp = split_scratch();
+    sp->njobs = 0;
+    if (h16 && L.mode == ne::kBwdRecompute && ba.window >= T && !qkn.on) {
+        plan_for(true, T, G, B * Hkv, sp);
+        if (sp->njobs) {
+            sp->part = (float*)(ws + L.spart);
+            sp->cnt = (unsigned*)(ws + L.scnt);
+            pa.split_cnt = sp->cnt;
+            pa.nsplit_cnt = 2 * B * Hkv * (sp->nrb - sp->rs);
+        }
+    }
+    hipError_t e = ne::launch_bwd((int)in_dtype, (int)out_dtype, head_dim, L.mode, pa, am, ba, *sp,
+                                  (hipStream_t)stream, (hipEvent_t const*)events);
     if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_attn_bwd: launch failed: %s", hipGetErrorString(e));
     return NE_OK;
 }

@@ -513,6 +513,42 @@ __device__ __forceinline__ void store_rows(const floatx16 (&acc)[D / 32], float 
     }
 }
 
+// ---- hand-off between the workgroups of one split row block --------------------------------
+// Every piece of a split block counts itself in cnt[0] when its products are done; the pieces
+// that arrive before the last leave their partial result in the workspace, then count it in
+// cnt[1] (after an agent-scope release: the partial is visible to every XCD).  The last piece
+// to arrive waits until cnt[1] shows the others' partials (they arrived before it, so they are
+// running and only have stores left; the wait is bounded anyway) and acquires them.  Every
+// thread of the workgroup makes the calls; sh: two words of LDS.
+__device__ __forceinline__ unsigned split_arrive(unsigned* cnt, unsigned* sh) {
+    if (threadIdx.x == 0) *sh = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    return *sh;
+}
+__device__ __forceinline__ void split_publish(unsigned* cnt) {
+    wait_all();             // this wave's partial stores are done
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+// true when all n partials were seen (false after 2^20 polls, well under a second: the caller poisons its output)
+__device__ __forceinline__ bool split_collect(unsigned* cnt, unsigned n, unsigned* sh) {
+    if (threadIdx.x == 0) {
+        unsigned it = 0;
+        bool ok = true;
+        while (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++it >= (1u << 20)) { ok = false; break; }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        sh[1] = ok ? 1u : 0u;
+    }
+    __syncthreads();
+    return sh[1] != 0u;
+}
+
 // ---- small vector stores of four consecutive output elements -----------------------------
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<floatx4*>(p) = floatx4{a, b, c, d};

@@ -158,6 +158,13 @@ __device__ __forceinline__ void convert8(const TI* src, OP* dst, const float2* c
 
 // grid (ceil(T / TT), B), 256 threads.  Forward: k, v and the cos/sin table.  Backward: q, k, v,
 // dO, Delta, lse2 and the table.
+// The hand-off counters of the split row blocks of the attention pass that follows start at zero.
+__device__ __forceinline__ void clear_split_counters(const PrepArgs& a) {
+    if (!a.split_cnt) return;
+    const int nthr = gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+    const int i0 = ((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    for (int i = i0; i < a.nsplit_cnt; i += nthr) a.split_cnt[i] = 0u;
+}
 template <typename TI, typename TO, typename OP, int D, bool BWD>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     constexpr int TT = 8;
@@ -168,6 +175,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const int t0 = blockIdx.x * TT, b = blockIdx.y;
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
     const bool rope = a.rope_base > 0.0;
+    clear_split_counters(a);
     for (int idx = threadIdx.x; idx < TT * (D / 2); idx += blockDim.x) {
         const int t = t0 + idx / (D / 2);
         cs[idx] = rope && t < T ? a.table[(size_t)t * (D / 2) + idx % (D / 2)] : make_float2(1.f, 0.f);
@@ -298,6 +306,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 template <typename TI, int D>
 __global__ __launch_bounds__(256) void prep_fwd_h(PrepArgs a) {
     constexpr int TB = 64, CPR = D / 8;
+    clear_split_counters(a);
     __shared__ _Float16 vts[D][TB + 8];                // v'^T of the 64 tokens (144-byte rows)
     const int t0 = blockIdx.x * TB, grp = blockIdx.y;
     const int T = a.T, Hkv = a.Hkv, b = grp / Hkv, hkv = grp % Hkv;
@@ -371,6 +380,24 @@ __device__ __forceinline__ Work map_block(int nblk, int ngrp, bool longest_last)
     }
     return Work{longest_last ? nblk - 1 - j : j, g};
 }
+
+// The job of this workgroup under a split plan: row block, piece and piece count (np = 1: the
+// block's whole key range), and its group.  Without a plan, blocks go longest-first as above.
+struct RowJob {
+    int rb, piece, np, grp;
+};
+__device__ __forceinline__ RowJob map_row_job(const SplitPlan& sp, int nrb, int ngrp) {
+    if (sp.njobs == 0) {
+        const Work w = map_block(nrb, ngrp, true);
+        return RowJob{w.blk, 0, 1, w.grp};
+    }
+    const Work w = map_block(sp.njobs, ngrp, false);
+    const unsigned e = sp.job[w.blk];
+    const int rb = (int)(e >> 2);
+    return RowJob{rb, (int)(e & 3u), rb >= sp.rs ? sp.np : 1, w.grp};
+}
+// Key tiles [lo, hi) of piece p of np of the range [j0, j1).
+__device__ __forceinline__ int piece_lo(int j0, int j1, int p, int np) { return j0 + (j1 - j0) * p / np; }
 
 // =====================================================================================
 // Forward.  grid (nrb * B * Hkv), 256 threads = 4 waves x 32 flattened rows.
@@ -617,7 +644,7 @@ __device__ __forceinline__ half8 fold_weights(int h) {
 
 template <typename TI, int D, typename TOUT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void fwd_kernel_h(FwdArgs a) {
+void fwd_kernel_h(FwdArgs a, SplitPlan sp) {
     using OP = _Float16;
     using M = Mma<OP>;
     typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -630,9 +657,9 @@ void fwd_kernel_h(FwdArgs a) {
     OP* const lds = reinterpret_cast<OP*>(lds_raw);    // K stages 0..2, then V^T stages 0..2
 
     const int T = a.T, G = a.G, TG = T * G, Tp = (T + 63) / 64 * 64;
-    const Work wk = map_block(a.nrb, a.B * a.Hkv, true);
-    const int rb = wk.blk;
-    const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
+    const RowJob job = map_row_job(sp, a.nrb, a.B * a.Hkv);
+    const int rb = job.rb;
+    const int hkv = job.grp % a.Hkv, b = job.grp / a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
     const int R0 = rb * BM;
     const int Rw = R0 + 32 * w;
@@ -641,13 +668,17 @@ void fwd_kernel_h(FwdArgs a) {
     const int t_lane = R / G;
     const int wave_tmin = Rw / G;
     const int wave_tmax = min(Rw + 31, TG - 1) / G;
-    const int last = Rw < TG ? wave_tmax / BN : -1;           // this wave's last key tile
-    const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;  // the block's
     const int W = a.window;
-    const int j0 = max(0, R0 / G - W + 1) / BN;                // the block's first key tile
-    const int first = max(0, wave_tmin - W + 1) / BN;         // this wave's
+    // the block's key tiles are [jb0, jb1); this job runs piece job.piece of them, [j0, ntiles)
+    const int jb0 = max(0, R0 / G - W + 1) / BN, jb1 = min(R0 + BM - 1, TG - 1) / G / BN + 1;
+    const int j0 = piece_lo(jb0, jb1, job.piece, job.np);
+    const int ntiles = piece_lo(jb0, jb1, job.piece + 1, job.np);
+    // this wave's last key tile in the piece (-1: none, the wave only joins the loads and barriers)
+    const int wlast = Rw < TG ? wave_tmax / BN : -1;
+    const int last = wlast >= j0 ? min(wlast, ntiles - 1) : -1;
+    const int first = max(max(0, wave_tmin - W + 1) / BN, j0);  // this wave's first
 
-    const size_t grp = (size_t)wk.grp;
+    const size_t grp = (size_t)job.grp;
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
     const OP* vtg = (const OP*)a.vh + grp * (size_t)D * Tp;
     const bool rope = a.rope_base > 0.0;
@@ -856,7 +887,71 @@ void fwd_kernel_h(FwdArgs a) {
         step(it + 5, IC<0>{}, IC<0>{});
     }
 
-    const float l_tot = sum_halves(l_run);
+    float l_tot = sum_halves(l_run);
+    if (job.np > 1) {
+        // split block: the pieces before the last leave m, l and O (unnormalised, relative to m)
+        // in their slot; the last combines all pieces in piece order and writes the output
+        __shared__ unsigned sh[2];
+        constexpr int NF = NDB * 16;                       // O floats per lane
+        const size_t sb = (size_t)job.grp * (a.nrb - sp.rs) + (rb - sp.rs);
+        unsigned* cnt = sp.cnt + 2 * sb;
+        float* slots = sp.part + sb * job.np * (size_t)(NW * 64 * (NF + 2));
+        auto o_at = [&](int p) { return slots + (size_t)p * (NW * 64 * (NF + 2)) + (size_t)w * 64 * NF; };
+        auto ml_at = [&](int p) { return slots + (size_t)p * (NW * 64 * (NF + 2)) + (size_t)NW * 64 * NF + (w * 64 + l) * 2; };
+        const unsigned ord = split_arrive(cnt, sh);
+        if ((int)ord + 1 < job.np) {
+            float* op = o_at(job.piece);
+#pragma unroll
+            for (int i = 0; i < NF / 4; ++i)
+                *reinterpret_cast<floatx4*>(op + (i * 64 + l) * 4) =
+                    floatx4{oacc[i / 4][4 * (i % 4)], oacc[i / 4][4 * (i % 4) + 1], oacc[i / 4][4 * (i % 4) + 2],
+                            oacc[i / 4][4 * (i % 4) + 3]};
+            *reinterpret_cast<float2*>(ml_at(job.piece)) = make_float2(m_run, l_tot);
+            split_publish(cnt);
+            return;
+        }
+        const bool ok = split_collect(cnt, (unsigned)job.np - 1, sh);
+        // (the same operations in the same order whichever piece is last: deterministic)
+        float mp[4], lp[4];
+        float mx = m_run;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            if (p >= job.np) break;
+            if (p == job.piece) { mp[p] = m_run; lp[p] = l_tot; continue; }
+            const float2 ml = *reinterpret_cast<const float2*>(ml_at(p));
+            mp[p] = ml.x; lp[p] = ml.y;
+            mx = fmaxf(mx, ml.x);
+        }
+        floatx16 acc[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = floatx16{};
+        float lsum = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            if (p >= job.np) break;
+            const float f = __builtin_amdgcn_exp2f(mp[p] - mx);
+            lsum = __builtin_fmaf(lp[p], f, lsum);
+            if (p == job.piece) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[db][r] = __builtin_fmaf(oacc[db][r], f, acc[db][r]);
+            } else {
+                const float* op = o_at(p);
+#pragma unroll
+                for (int i = 0; i < NF / 4; ++i) {
+                    const floatx4 x = *reinterpret_cast<const floatx4*>(op + (i * 64 + l) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i / 4][4 * (i % 4) + e] = __builtin_fmaf(x[e], f, acc[i / 4][4 * (i % 4) + e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] = acc[db];
+        m_run = mx;
+        l_tot = ok ? lsum : __builtin_nanf("");
+    }
     const float inv = 1.f / l_tot;
     if (rvalid && h == 0) {
         const int t = t_lane, hq = hkv * G + (R - t * G);
@@ -1688,16 +1783,16 @@ void dq_kernel(BwdArgs a) {
 // budget is exhausted.
 template <int D, typename TOUT, bool EXT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void dq_kernel_h(BwdArgs a) {
+void dq_kernel_h(BwdArgs a, SplitPlan sp) {
     using OP = _Float16;
     using M = Mma<OP>;
     constexpr int BM = 128, BN = 64, NW = 4, KS = D / 16, NDB = D / 32, TILE = BN * D;
     __shared__ __attribute__((aligned(1024))) OP lds[2 * 2 * TILE];  // [stage][K | V]
 
     const int T = a.T, G = a.G, TG = T * G;
-    const Work wk = map_block(a.nrb, a.B * a.Hkv, true);
-    const int rb = wk.blk;
-    const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
+    const RowJob job = map_row_job(sp, a.nrb, a.B * a.Hkv);
+    const int rb = job.rb;
+    const int hkv = job.grp % a.Hkv, b = job.grp / a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
     const int R0 = rb * BM;
     const int Rw = R0 + 32 * w;
@@ -1706,11 +1801,13 @@ void dq_kernel_h(BwdArgs a) {
     const int t_lane = R / G;
     const int wave_tmin = Rw / G;
     const int wave_tmax = min(Rw + 31, TG - 1) / G;
-    const int ntiles = min(R0 + BM - 1, TG - 1) / G / BN + 1;
     const int W = EXT ? a.window : T;
-    const int j0 = EXT ? max(0, R0 / G - W + 1) / BN : 0;  // the block's first key tile
+    // the block's key tiles [jb0, jb1); this job runs piece job.piece of them, [j0, ntiles)
+    const int jb0 = EXT ? max(0, R0 / G - W + 1) / BN : 0, jb1 = min(R0 + BM - 1, TG - 1) / G / BN + 1;
+    const int j0 = piece_lo(jb0, jb1, job.piece, job.np);
+    const int ntiles = piece_lo(jb0, jb1, job.piece + 1, job.np);
 
-    const size_t grp = (size_t)wk.grp;
+    const size_t grp = (size_t)job.grp;
     const OP* qg = (const OP*)a.qh + grp * (size_t)TG * D;
     const OP* og = (const OP*)a.dOh + grp * (size_t)TG * D;
     const OP* kg = (const OP*)a.kh + grp * (size_t)T * D;
@@ -1815,6 +1912,35 @@ void dq_kernel_h(BwdArgs a) {
             if (i + AHD < NQ) kt[i + AHD] = rk(i + AHD);
         }
         __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if (job.np > 1) {
+        // split block (two pieces): the first to finish leaves its dQ sums in its slot; the other
+        // adds them to its own (one addition per element: the same result whichever is last)
+        __shared__ unsigned sh[2];
+        constexpr int NF = NDB * 16;
+        const size_t sb = (size_t)job.grp * (a.nrb - sp.rs) + (rb - sp.rs);
+        unsigned* cnt = sp.cnt + 2 * sb;
+        float* slots = sp.part + sb * 2 * (size_t)(NW * 64 * NF);
+        auto at = [&](int p) { return slots + (size_t)p * (NW * 64 * NF) + (size_t)w * 64 * NF; };
+        if (split_arrive(cnt, sh) == 0u) {
+            float* op = at(job.piece);
+#pragma unroll
+            for (int i = 0; i < NF / 4; ++i)
+                *reinterpret_cast<floatx4*>(op + (i * 64 + l) * 4) =
+                    floatx4{dq[i / 4][4 * (i % 4)], dq[i / 4][4 * (i % 4) + 1], dq[i / 4][4 * (i % 4) + 2],
+                            dq[i / 4][4 * (i % 4) + 3]};
+            split_publish(cnt);
+            return;
+        }
+        const float poison = split_collect(cnt, 1u, sh) ? 0.f : __builtin_nanf("");
+        const float* op = at(job.piece ^ 1);
+#pragma unroll
+        for (int i = 0; i < NF / 4; ++i) {
+            const floatx4 x = *reinterpret_cast<const floatx4*>(op + (i * 64 + l) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dq[i / 4][4 * (i % 4) + e] += x[e] + poison;
+        }
     }
 
     if (!rvalid) return;  // both lanes of a row pair (c, c + 32) agree
@@ -2074,7 +2200,8 @@ struct Marks {
     } while (0)
 
 template <typename TI, typename TO, typename OP, int D>
-static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, hipStream_t s, hipEvent_t const* ev) {
+static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, const SplitPlan& sp, hipStream_t s,
+                               hipEvent_t const* ev) {
     const Marks m{ev, s};
     NE_TRY(m.before(0));
     if constexpr (sizeof(OP) == 2)
@@ -2087,7 +2214,8 @@ static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, hipStream_
     if constexpr (sizeof(OP) == 2) {
         FwdArgs f2 = fa;
         f2.nrb = (int)(((int64_t)fa.T * fa.G + 255) / 256);
-        hipLaunchKernelGGL((fwd_kernel_h<TI, D, TO>), dim3(f2.nrb * fa.Hkv * fa.B), dim3(512), 0, s, f2);
+        const int njobs = sp.njobs ? sp.njobs : f2.nrb;
+        hipLaunchKernelGGL((fwd_kernel_h<TI, D, TO>), dim3(njobs * fa.Hkv * fa.B), dim3(512), 0, s, f2, sp);
     }
     else
         hipLaunchKernelGGL((fwd_kernel<TI, OP, D, TO>), dim3(fa.nrb * fa.Hkv * fa.B), dim3(256), 0, s, fa);
@@ -2096,8 +2224,8 @@ static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, hipStream_
 }
 
 template <typename TI, typename TO, typename OP, int D>
-static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am, const BwdArgs& ba, hipStream_t s,
-                               hipEvent_t const* ev) {
+static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am, const BwdArgs& ba,
+                               const SplitPlan& sp, hipStream_t s, hipEvent_t const* ev) {
     const Marks m{ev, s};
     NE_TRY(m.before(0));
     if constexpr (sizeof(OP) == 2) {
@@ -2154,10 +2282,11 @@ static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am,
     NE_TRY(m.after(1));
     NE_TRY(m.before(2));
     if constexpr (sizeof(OP) == 2) {
+        const int njobs = sp.njobs ? sp.njobs : ba.nrb;
         if (ba.window < ba.T || ba.qkn.on)
-            hipLaunchKernelGGL((dq_kernel_h<D, TO, true>), dim3(ba.nrb * ngroups), dim3(256), 0, s, ba);
+            hipLaunchKernelGGL((dq_kernel_h<D, TO, true>), dim3(njobs * ngroups), dim3(256), 0, s, ba, sp);
         else
-            hipLaunchKernelGGL((dq_kernel_h<D, TO, false>), dim3(ba.nrb * ngroups), dim3(256), 0, s, ba);
+            hipLaunchKernelGGL((dq_kernel_h<D, TO, false>), dim3(njobs * ngroups), dim3(256), 0, s, ba, sp);
     }
     else
         hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb * ngroups), dim3(256), 0, s, ba);
@@ -2173,23 +2302,23 @@ static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am,
         default: return hipErrorInvalidValue;                      \
     }
 
-hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, hipStream_t s,
-                      hipEvent_t const* ev) {
-    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, float, float, float, D, pa, fa, s, ev) }
-    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, __bf16, float, _Float16, D, pa, fa, s, ev) }
-    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_fwd_t, __bf16, __bf16, _Float16, D, pa, fa, s, ev) }
-    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, _Float16, float, _Float16, D, pa, fa, s, ev) }
-    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_fwd_t, _Float16, _Float16, _Float16, D, pa, fa, s, ev) }
+hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, const SplitPlan& sp,
+                      hipStream_t s, hipEvent_t const* ev) {
+    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, float, float, float, D, pa, fa, sp, s, ev) }
+    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, __bf16, float, _Float16, D, pa, fa, sp, s, ev) }
+    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_fwd_t, __bf16, __bf16, _Float16, D, pa, fa, sp, s, ev) }
+    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_fwd_t, _Float16, float, _Float16, D, pa, fa, sp, s, ev) }
+    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_fwd_t, _Float16, _Float16, _Float16, D, pa, fa, sp, s, ev) }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd(int in_dt, int out_dt, int D, int mode, const PrepArgs& pa, const AmaxArgs& am,
-                      const BwdArgs& ba, hipStream_t s, hipEvent_t const* ev) {
-    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, float, float, float, D, mode, pa, am, ba, s, ev) }
-    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, __bf16, float, _Float16, D, mode, pa, am, ba, s, ev) }
-    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_bwd_t, __bf16, __bf16, _Float16, D, mode, pa, am, ba, s, ev) }
-    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, _Float16, float, _Float16, D, mode, pa, am, ba, s, ev) }
-    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_bwd_t, _Float16, _Float16, _Float16, D, mode, pa, am, ba, s, ev) }
+                      const BwdArgs& ba, const SplitPlan& sp, hipStream_t s, hipEvent_t const* ev) {
+    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, float, float, float, D, mode, pa, am, ba, sp, s, ev) }
+    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, __bf16, float, _Float16, D, mode, pa, am, ba, sp, s, ev) }
+    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_bwd_t, __bf16, __bf16, _Float16, D, mode, pa, am, ba, sp, s, ev) }
+    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, _Float16, float, _Float16, D, mode, pa, am, ba, sp, s, ev) }
+    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_bwd_t, _Float16, _Float16, _Float16, D, mode, pa, am, ba, sp, s, ev) }
     return hipErrorInvalidValue;
 }
 

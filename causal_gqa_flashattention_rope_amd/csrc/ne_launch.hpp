@@ -53,6 +53,7 @@ struct PrepArgs {
     // from the group's max |dO| (amax_part: nparts partial maxima per group); dsc[group] = 1 / s
     const float* amax_part; int nparts; float* dsc;
     float* dq_acc;                                  // atomic dQ accumulator to clear (or null)
+    unsigned* split_cnt; int nsplit_cnt;            // counters of the split row blocks, cleared here
 };
 
 // Partial maxima of |dO| per (batch, KV head) group: part p of group g covers tokens
@@ -69,6 +70,28 @@ struct TableArgs {
     int T, D;
     double base;
 };
+
+// Key-range split of the longest row blocks.  Causal work per row block grows with its position,
+// so when a launch has few blocks per CU the longest ones set the time.  Row blocks rb >= rs are
+// cut into np contiguous ranges of their key tiles ("pieces"), each run by its own workgroup; the
+// last piece of a block to finish combines the others' partial results (read back in piece
+// order, so the sum does not depend on the arrival order) and writes the output.  job[] lists the
+// pieces and unsplit blocks of one group longest-first (rb << 2 | piece); workgroup i takes job
+// rank i / ngrp (XCD-interleaved as for unsplit launches).  njobs == 0: no split.
+constexpr int kMaxSplitJobs = 1024;
+struct SplitPlan {
+    int njobs, rs, np, nrb;
+    float* part;                                    // [split block][piece][slot floats]
+    unsigned* cnt;                                  // [split block][arrived, written]
+    unsigned short job[kMaxSplitJobs];
+};
+// The host's plan for a launch of BM-row blocks, at most max_np (<= 4) pieces per block: fills
+// njobs, rs, np, nrb and job (not part and cnt).  It depends only on the causal tile counts of the row blocks (tiles of 64 keys, no
+// window), the number of groups and the workgroups the chip runs at once (256 CUs x wg_per_cu).
+void split_plan(int T, int G, int ngrp, int BM, int wg_per_cu, int max_np, SplitPlan* out);
+// floats of the partial-result slot of one piece (forward: O, m and l of 8 waves; dQ: 4 waves)
+inline size_t split_slot_floats_fwd(int D) { return (size_t)8 * 64 * (D / 2 + 2); }
+inline size_t split_slot_floats_dq(int D) { return (size_t)4 * 64 * (D / 2); }
 
 struct FwdArgs {
     const void* q;                                  // raw queries (in dtype), rotated in the kernel
@@ -144,12 +167,14 @@ struct QkvArgs {
 // ev (nullable): hipEvent_t pairs recorded on `s` around each kernel launch, in launch order
 // (forward: prep, fwd; backward: prep, dkdv, dq).
 hipError_t launch_table(const TableArgs& a, hipStream_t s);
-hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, hipStream_t s,
-                      hipEvent_t const* ev);
+// sp: the split plan of the 16-bit forward (forward) or of the recomputing dQ pass (backward);
+// njobs == 0 for none.
+hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, const SplitPlan& sp,
+                      hipStream_t s, hipEvent_t const* ev);
 // mode: 0 dQ recomputes S and dP, 1 dQ reads the stored dS, 2 atomic dQ in the dK/dV pass
 enum { kBwdRecompute = 0, kBwdStoredDs = 1, kBwdAtomic = 2 };
 hipError_t launch_bwd(int in_dt, int out_dt, int D, int mode, const PrepArgs& pa, const AmaxArgs& am,
-                      const BwdArgs& ba, hipStream_t s, hipEvent_t const* ev);
+                      const BwdArgs& ba, const SplitPlan& sp, hipStream_t s, hipEvent_t const* ev);
 hipError_t launch_append(int in_dt, int D, const AppendArgs& a, hipStream_t s);
 // ev (nullable): pairs around the cos/sin table and the product (4 entries).
 hipError_t launch_qkv(int in_dt, int out_dt, int D, const QkvArgs& a, hipStream_t s, hipEvent_t const* ev);

@@ -107,12 +107,19 @@ typedef enum {
  *   [0, 256)                 table header (T, head_dim, rope_base of the table below)
  *   then, when rope_base > 0, the cos/sin table [T][head_dim / 2] of float2 (ne_rope_table_init);
  *   forward:  the rotated fp16 keys and transposed fp16 values (fp32 copies on the fp32 path);
+ *             16-bit path: the partial results and counters of the split row blocks (below);
  *   backward: the rotated, scaled copies of q, k, dO (and v), Delta = rowsum(dO * o), the
  *             log2-scaled lse, the per-row 1/rms of the QK norm, the dO scales; with
  *             NE_FLAG_NONDETERMINISTIC the fp32 dQ accumulator [B][Hq][T][head_dim]; with
- *             NE_FLAG_STORE_DS the stored dS.
- * A backward workspace is also a valid forward workspace for the same arguments: the table sits at
- * the same place, so one ne_rope_table_init serves both calls. */
+ *             NE_FLAG_STORE_DS the stored dS; otherwise (16-bit) the split regions of the dQ pass.
+ * Split row blocks: when a call has few causal row blocks per CU, the longest blocks of the forward
+ * and of the recomputing dQ pass are cut into 2-4 ranges of keys run by separate workgroups; the
+ * last to finish combines the others' partial results in a fixed order (the result does not depend
+ * on which finishes last).  The plan depends only on the shape; a window shorter than T or the QK
+ * norm (dQ pass) turns it off.
+ * For is_bwd != 0 the size returned is at least the forward's, so a backward workspace of that size
+ * is also a valid forward workspace for the same arguments: the table sits at the same place, so
+ * one ne_rope_table_init serves both calls. */
 size_t ne_rope_attn_workspace_bytes(int is_bwd, int B, int T, int Hq, int Hkv, int head_dim,
                                     double rope_base, ne_dtype_t in_dtype, unsigned flags);
 

@@ -1,5 +1,6 @@
 """Host-side checks of the C ABI (no GPU needed): the library loads, exports every symbol the
 header declares, sizes workspaces, and rejects invalid arguments before launching anything."""
+import heapq
 import ctypes
 import os
 import re
@@ -55,15 +56,92 @@ def amax_parts(B, T, Hkv):
     return max(1, min(-(-512 // B), -(-T // 8), 1024))
 
 
+def split_plan(T, G, ngrp, BM, wg, maxp):
+    """(rs, np) of the key-range split of the longest causal row blocks, or None: the greedy
+    dispatch of the longest-first job list (each job to the slot that frees first) over 256 CUs x
+    wg slots, cost = key tiles + 1 per job + 4 per piece of a split block; the earliest end
+    wins if it is below 0.8 of the unsplit order's."""
+    TG = T * G
+    nrb = -(-TG // BM)
+    slots = 256 * wg
+    if nrb > 16383 or ngrp * nrb > 4 * slots:
+        return None
+    tiles = [min(rb * BM + BM - 1, TG - 1) // G // 64 + 1 for rb in range(nrb)]
+
+    def end(rs, np_):
+        jobs = []
+        for rb in range(nrb):
+            if rb >= rs:
+                n = tiles[rb]
+                jobs += [(n * (p + 1) // np_ - n * p // np_) + 5.0 for p in range(np_)]
+            else:
+                jobs.append(tiles[rb] + 1.0)
+        h = [0.0] * slots
+        last = 0.0
+        for c in sorted(jobs, reverse=True):
+            for _ in range(ngrp):
+                t = heapq.heappop(h) + c
+                heapq.heappush(h, t)
+                last = max(last, t)
+        return last
+
+    best = base = end(nrb, 1)
+    choice = None
+    step = max(1, nrb // 32)
+    for np_ in range(2, maxp + 1):
+        for rs in range(nrb - 1, -1, -step):
+            if tiles[rs] < 2 * np_ or rs + (nrb - rs) * np_ > 1024:
+                break
+            m = end(rs, np_)
+            if m < best:
+                best, choice = m, (rs, np_)
+    if choice is None or best > 0.8 * base:
+        return None
+    return choice
+
+
+def split_bytes(B, T, Hq, Hkv, D, bwd):
+    """Workspace of the split row blocks: per split block, a slot per piece (forward: O, m, l of
+    8 waves x 64 lanes; dQ: dQ of 4 waves x 64 lanes, fp32) and two counters."""
+    G = Hq // Hkv
+    plan = split_plan(T, G, B * Hkv, 128 if bwd else 256, 2 if bwd else 1, 2 if bwd else 4)
+    if plan is None:
+        return 0
+    rs, np_ = plan
+    nsb = B * Hkv * (-(-T * G // (128 if bwd else 256)) - rs)
+    slot = 4 * 64 * (D // 2) if bwd else 8 * 64 * (D // 2 + 2)
+    return up(nsb * np_ * slot * 4) + up(nsb * 2 * 4)
+
+
 def sizes(B, T, Hq, Hkv, D, esz, base=1e4):
-    """(header + table, forward, backward base without the optional regions, v' copy)"""
+    """(header + table, forward, backward base without the optional regions, v' copy); the 16-bit
+    forward includes its split regions"""
     nq, nk = B * T * Hq * D, B * T * Hkv * D
     head = 256 + (up(T * (D // 2) * 8) if base > 0 else 0)
     Tp = -(-T // 64) * 64
     fwd = head + up(esz * nk) + up(esz * (B * Hkv * D * Tp if esz == 2 else nk))
+    if esz == 2:
+        fwd += split_bytes(B, T, Hq, Hkv, D, False)
     bwd = head + 2 * up(esz * nq) + up(esz * nk) + 3 * up(4 * B * T * Hq) + up(4 * B * T * Hkv) + \
         up(4 * B * Hkv) + up(4 * B * Hkv * amax_parts(B, T, Hkv))
     return head, fwd, bwd, up(esz * nk)
+
+
+def test_split_plans_of_the_parity_shapes():
+    """The GPU parity shapes meant to cover the split row blocks are split: forward into 4 pieces,
+    the dQ pass into 2 (not the third shape's); the workloads of the benchmark keep their blocks."""
+    fwd = [split_plan(T, Hq // Hkv, B * Hkv, 256, 1, 4) for B, T, Hq, Hkv, D in
+           [(1, 1000, 4, 1, 128), (1, 1200, 4, 2, 64), (1, 777, 2, 1, 32)]]
+    dq = [split_plan(T, Hq // Hkv, B * Hkv, 128, 2, 2) for B, T, Hq, Hkv, D in
+          [(1, 1000, 4, 1, 128), (1, 1200, 4, 2, 64), (1, 777, 2, 1, 32)]]
+    assert all(p is not None and p[1] == 4 for p in fwd)
+    assert dq[0] is not None and dq[1] is not None and dq[2] is None
+    assert all(p[1] == 2 for p in dq[:2])
+    for B, T, Hq, Hkv in ((4, 2048, 12, 4), (8, 512, 12, 4), (16, 1024, 12, 12), (1, 8192, 32, 8)):
+        assert split_plan(T, Hq // Hkv, B * Hkv, 256, 1, 4) is None
+        assert split_plan(T, Hq // Hkv, B * Hkv, 128, 2, 2) is None
+    # one GPU's share of the 8192-token layer (one group) is split in both passes
+    assert split_plan(8192, 4, 1, 256, 1, 4) is not None and split_plan(8192, 4, 1, 128, 2, 2) is not None
 
 
 def wsb(L, is_bwd, B, T, Hq, Hkv, D, base=1e4, dt=binding.NE_BF16, flags=0):
@@ -74,8 +152,16 @@ def test_workspace_sizes(L):
     B, T, Hq, Hkv, D = 4, 2048, 12, 4, 128
     head, fwd, bwd, vcopy = sizes(B, T, Hq, Hkv, D, 2)
     assert wsb(L, 0, B, T, Hq, Hkv, D) == fwd
-    # default backward: O(T) -- operand copies (v' included, the dQ pass recomputes from it), no dS
-    assert wsb(L, 1, B, T, Hq, Hkv, D) == bwd + vcopy
+    # this shape keeps its row blocks whole; one group alone (B = 1, Hkv = 1) splits them, in the
+    # forward and in the dQ pass
+    assert split_bytes(B, T, Hq, Hkv, D, False) == 0 and split_bytes(B, T, Hq, Hkv, D, True) == 0
+    assert split_bytes(1, T, 3, 1, D, False) > 0 and split_bytes(1, T, 3, 1, D, True) > 0
+    assert wsb(L, 0, 1, T, 3, 1, D) == sizes(1, T, 3, 1, D, 2)[1]
+    h1, f1, b1, v1 = sizes(1, T, 3, 1, D, 2)
+    assert wsb(L, 1, 1, T, 3, 1, D) == max(f1, b1 + v1 + split_bytes(1, T, 3, 1, D, True))
+    # default backward: O(T) -- operand copies (v' included, the dQ pass recomputes from it) and
+    # the dQ pass's split regions, no dS
+    assert wsb(L, 1, B, T, Hq, Hkv, D) == bwd + vcopy + split_bytes(B, T, Hq, Hkv, D, True)
     # stored dS: 8 KiB per (64-row tile, 64-key block) pair that dK/dV visits, for every group; no v' copy
     G = Hq // Hkv
     assert wsb(L, 1, B, T, Hq, Hkv, D, flags=binding.NE_FLAG_STORE_DS) == \

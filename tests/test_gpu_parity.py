@@ -129,6 +129,29 @@ def test_parity_small(shape, dtypes, base):
     parity(q, k, v, dO, base, out_dt, in_dt)
 
 
+# One or two (batch, KV head) groups: the launch is short of row blocks, so the forward cuts its
+# longest 256-row blocks into 4 key ranges and the dQ pass its longest 128-row blocks into 2 (the
+# third: forward only), each block finished by the last of its workgroups (the plans are checked
+# on the CPU in test_abi_host.test_split_plans_of_the_parity_shapes).
+SPLIT_SHAPES = [(1, 1000, 4, 1, 128), (1, 1200, 4, 2, 64), (1, 777, 2, 1, 32)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES)
+@pytest.mark.parametrize("dtypes", [(torch.bfloat16, torch.float32), (torch.float16, torch.float32),
+                                    (torch.bfloat16, torch.bfloat16)])
+def test_parity_split_row_blocks(shape, dtypes):
+    in_dt, out_dt = dtypes
+    B, T, Hq, Hkv, D = shape
+    q, k, v, dO = inputs.random_case(B, T, Hq, Hkv, D, seed=3000 + T,
+                                     dtype="bf16" if in_dt == torch.bfloat16 else "f16")
+    parity(q, k, v, dO, 1.0e4, out_dt, in_dt)
+    # the combined blocks do not depend on which workgroup finishes last: bitwise repeatable
+    first = run_gpu(q, k, v, dO, 1.0e4, out_dt)
+    again = run_gpu(q, k, v, dO, 1.0e4, out_dt)
+    for a, b in zip(first, again):
+        assert torch.equal(a, b)
+
+
 def ds_group_bytes(T, G):
     nrt, nkb = -(-T * G // 64), -(-T // 64)
     return sum(1 for kb in range(nkb) for rt in range(nrt) if rt >= kb * G) * 8192
@@ -227,9 +250,12 @@ def test_workload_long_ctx_bf16(flags):
     workload_parity("long_ctx_t8192", [(0, 5)], flags=flags)
 
 
-def test_one_kv_group_alone_equals_its_slice_of_the_full_run_bitwise():
+def test_one_kv_group_alone_equals_its_slice_of_the_full_run():
     """The long-context layer sharded by KV head (one group per GPU, no exchange): a group run on
-    its own, as one GPU of 8 would, gives exactly the bits of that group in the full run."""
+    its own, as one GPU of 8 would, gives the values of that group in the full run.  Not bitwise:
+    with one group the launch is short of row blocks, so the longest ones are split over several
+    workgroups and their partial results added (in a fixed order), while the 8-group run keeps
+    them whole; only the order of fp32 sums differs."""
     w = inputs.WORKLOADS["long_ctx_t8192"]
     q, k, v, dO = inputs.make_inputs(w)
     full = run_gpu(q, k, v, dO, w.rope_base, torch.float32)
@@ -237,12 +263,14 @@ def test_one_kv_group_alone_equals_its_slice_of_the_full_run_bitwise():
     for g in (0, 5):
         qs, dOs = slice_group(q, 0, g, G), slice_group(dO, 0, g, G)
         ks, vs = slice_group(k, 0, g, 0), slice_group(v, 0, g, 0)
-        o, lse, dq, dk, dv = run_gpu(qs, ks, vs, dOs, w.rope_base, torch.float32)
-        assert torch.equal(o.cpu(), slice_group(full[0], 0, g, G).cpu())
-        assert torch.equal(lse.cpu(), full[1][:, g * G:(g + 1) * G].cpu())
-        assert torch.equal(dq.cpu(), slice_group(full[2], 0, g, G).cpu())
-        assert torch.equal(dk.cpu(), slice_group(full[3], 0, g, 0).cpu())
-        assert torch.equal(dv.cpu(), slice_group(full[4], 0, g, 0).cpu())
+        got = run_gpu(qs, ks, vs, dOs, w.rope_base, torch.float32)
+        want = [slice_group(full[0], 0, g, G), full[1][:, g * G:(g + 1) * G], slice_group(full[2], 0, g, G),
+                slice_group(full[3], 0, g, 0), slice_group(full[4], 0, g, 0)]
+        for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), got, want):
+            # fp32 reassociation of sums of up to 8192 terms, plus the fp16 rounding of P and dS it
+            # can flip: far below the 16-bit operand error the parity tests allow
+            err = (a.double() - b.double()).abs().max().item()
+            assert err <= 2e-4 * b.double().abs().max().item() + 1e-6, (g, name, err)
 
 
 # ---------------------------------------------------------------------------------------

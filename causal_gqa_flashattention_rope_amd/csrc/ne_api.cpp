@@ -31,7 +31,12 @@ static_assert(ne::kDecodeScratchBytes == NE_DECODE_SCRATCH_BYTES, "the header st
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t table, qh, kh, vh, dOh, delta, lse2, rq, rk, dsc, amax, dqacc, ds, spart, scnt, total;
+    size_t table, qh, kh, vh, dOh, delta, lse2, rq, rk, dsc, amax, dqacc, ds, total;
+    // split row / key blocks: partial results and counters of the forward (fwd, 16-bit) or of the
+    // dQ pass (q) and the dK/dV pass (k) of the recomputing 16-bit backward; counters of one call
+    // are contiguous (one clearing range), the dQ pass's first
+    size_t fpart, qpart, kpart, cnt;
+    size_t ncnt_q, ncnt_k;  // counters (unsigned) of the dQ / dK/dV pass (forward: ncnt_q)
     int mode;       // ne::kBwdRecompute, kBwdStoredDs or kBwdAtomic (backward)
     int ds_groups;  // stored dS: groups whose dS the workspace holds at once
     int nparts;     // partial maxima of |dO| per group (16-bit backward)
@@ -99,14 +104,20 @@ int bwd_mode(ne_dtype_t in, unsigned flags, int T, int Hq, int Hkv) {
     return ne::kBwdRecompute;
 }
 
-// Split plan of the 16-bit forward (256-row blocks, one workgroup per CU, up to 4 pieces) or of
-// the recomputing dQ pass (128-row blocks, two per CU, 2 pieces: its registers are all taken).  The plan struct is large: one per thread, reused.
-ne::SplitPlan* split_scratch() {
-    thread_local ne::SplitPlan sp;
-    return &sp;
+// The plan of one pass (ne::kSplitFwd, kSplitDq, kSplitDkdv).  The plan struct is large: one
+// per thread and pass, reused.
+ne::SplitPlan* split_scratch(int kind) {
+    thread_local ne::SplitPlan sp[3];
+    return &sp[kind];
 }
-void plan_for(bool bwd, int T, int G, int ngrp, ne::SplitPlan* sp) {
-    ne::split_plan(T, G, ngrp, bwd ? 128 : 256, bwd ? 2 : 1, bwd ? 2 : 4, sp);
+ne::SplitPlan* plan_for(int kind, int T, int G, int ngrp) {
+    ne::SplitPlan* sp = split_scratch(kind);
+    ne::split_plan(kind, T, G, ngrp, sp);
+    return sp;
+}
+// split blocks of a plan (0 without one)
+size_t split_blocks(const ne::SplitPlan& sp, int ngrp) {
+    return sp.njobs ? (size_t)ngrp * (sp.nrb - sp.rs) : 0;
 }
 
 // The workspace regions.  ds_bytes: bytes available for the stored dS (stored-dS mode), or
@@ -147,17 +158,25 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, double base, ne_dt
             off += up((size_t)std::max(L.ds_groups, 1) * gb);
         }
     }
-    // partial results and counters of the split row blocks: forward (16-bit operands), or the
-    // recomputing dQ pass; sized for the plan without a window (a window turns the split off)
+    // the split blocks' regions, sized for the plans without a window (a window turns them off)
     if (in != NE_F32 && (!bwd || L.mode == ne::kBwdRecompute)) {
-        ne::SplitPlan* sp = split_scratch();
-        plan_for(bwd, T, Hq / Hkv, B * Hkv, sp);
-        if (sp->njobs) {
-            const size_t nsb = (size_t)B * Hkv * (sp->nrb - sp->rs);
-            const size_t slot = bwd ? ne::split_slot_floats_dq(D) : ne::split_slot_floats_fwd(D);
-            L.spart = off; off += up(nsb * sp->np * slot * 4);
-            L.scnt = off; off += up(nsb * 2 * 4);
+        const int ngrp = B * Hkv, G = Hq / Hkv;
+        if (!bwd) {
+            const ne::SplitPlan* f = plan_for(ne::kSplitFwd, T, G, ngrp);
+            const size_t n = split_blocks(*f, ngrp);
+            L.fpart = off; off += up(n * f->np * ne::split_slot_floats_fwd(D) * 4);
+            L.ncnt_q = 2 * n;
+        } else {
+            const ne::SplitPlan* q = plan_for(ne::kSplitDq, T, G, ngrp);
+            const size_t nq = split_blocks(*q, ngrp);
+            L.qpart = off; off += up(nq * q->np * ne::split_slot_floats_dq(D) * 4);
+            const ne::SplitPlan* k = plan_for(ne::kSplitDkdv, T, G, ngrp);
+            const size_t nk = split_blocks(*k, ngrp);
+            L.kpart = off; off += up(nk * k->np * ne::split_slot_floats_dkdv(D) * 4);
+            L.ncnt_q = 2 * nq;
+            L.ncnt_k = 2 * nk;
         }
+        L.cnt = off; off += up((L.ncnt_q + L.ncnt_k) * 4);
     }
     L.total = off;
     return L;
@@ -295,15 +314,15 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     fa.window = visible_keys(opts->window, T);
     fa.qkn = qkn;
     fa.nrb = (int)(((int64_t)T * G + 127) / 128);
-    ne::SplitPlan* sp = split_scratch();
+    ne::SplitPlan* sp = split_scratch(ne::kSplitFwd);
     sp->njobs = 0;
     if (in_dtype != NE_F32 && fa.window >= T) {
-        plan_for(false, T, G, B * Hkv, sp);
+        plan_for(ne::kSplitFwd, T, G, B * Hkv);
         if (sp->njobs) {
-            sp->part = (float*)(ws + L.spart);
-            sp->cnt = (unsigned*)(ws + L.scnt);
+            sp->part = (float*)(ws + L.fpart);
+            sp->cnt = (unsigned*)(ws + L.cnt);
             pa.split_cnt = sp->cnt;
-            pa.nsplit_cnt = 2 * B * Hkv * (sp->nrb - sp->rs);
+            pa.nsplit_cnt = (int)L.ncnt_q;
         }
     }
     hipError_t e = ne::launch_fwd((int)in_dtype, (int)out_dtype, head_dim, pa, fa, *sp, (hipStream_t)stream,
@@ -375,18 +394,22 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     ba.nrb = (int)(((int64_t)T * G + 127) / 128);
     ba.rope_base = rope_base;
     ba.scale = (float)(1.0 / std::sqrt((double)head_dim));
-    ne::SplitPlan* sp = split_scratch();
-    sp->njobs = 0;
-    if (h16 && L.mode == ne::kBwdRecompute && ba.window >= T && !qkn.on) {
-        plan_for(true, T, G, B * Hkv, sp);
-        if (sp->njobs) {
-            sp->part = (float*)(ws + L.spart);
-            sp->cnt = (unsigned*)(ws + L.scnt);
-            pa.split_cnt = sp->cnt;
-            pa.nsplit_cnt = 2 * B * Hkv * (sp->nrb - sp->rs);
+    ne::SplitPlan* spq = split_scratch(ne::kSplitDq);
+    ne::SplitPlan* spk = split_scratch(ne::kSplitDkdv);
+    spq->njobs = spk->njobs = 0;
+    if (h16 && L.mode == ne::kBwdRecompute && ba.window >= T) {
+        if (!qkn.on) plan_for(ne::kSplitDq, T, G, B * Hkv);
+        plan_for(ne::kSplitDkdv, T, G, B * Hkv);
+        spq->part = (float*)(ws + L.qpart);
+        spq->cnt = (unsigned*)(ws + L.cnt);
+        spk->part = (float*)(ws + L.kpart);
+        spk->cnt = (unsigned*)(ws + L.cnt) + L.ncnt_q;
+        if (spq->njobs || spk->njobs) {
+            pa.split_cnt = spq->cnt;
+            pa.nsplit_cnt = (int)(L.ncnt_q + L.ncnt_k);
         }
     }
-    hipError_t e = ne::launch_bwd((int)in_dtype, (int)out_dtype, head_dim, L.mode, pa, am, ba, *sp,
+    hipError_t e = ne::launch_bwd((int)in_dtype, (int)out_dtype, head_dim, L.mode, pa, am, ba, *spq, *spk,
                                   (hipStream_t)stream, (hipEvent_t const*)events);
     if (e != hipSuccess) return fail(NE_ERR_HIP, "ne_rope_attn_bwd: launch failed: %s", hipGetErrorString(e));
     return NE_OK;

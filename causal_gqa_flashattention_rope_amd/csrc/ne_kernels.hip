@@ -381,20 +381,23 @@ __device__ __forceinline__ Work map_block(int nblk, int ngrp, bool longest_last)
     return Work{longest_last ? nblk - 1 - j : j, g};
 }
 
-// The job of this workgroup under a split plan: row block, piece and piece count (np = 1: the
-// block's whole key range), and its group.  Without a plan, blocks go longest-first as above.
+// The job of this workgroup under a split plan (SPLIT): row block, piece and piece count (np = 1:
+// the block's whole key range), and its group.  Without one, blocks go longest-first as above.
+// The split variants are instantiations of their own, so the plain kernels keep their registers.
 struct RowJob {
     int rb, piece, np, grp;
 };
+template <bool SPLIT>
 __device__ __forceinline__ RowJob map_row_job(const SplitPlan& sp, int nrb, int ngrp) {
-    if (sp.njobs == 0) {
+    if constexpr (!SPLIT) {
         const Work w = map_block(nrb, ngrp, true);
         return RowJob{w.blk, 0, 1, w.grp};
+    } else {
+        const Work w = map_block(sp.njobs, ngrp, false);
+        const unsigned e = sp.job[w.blk];
+        const int rb = (int)(e >> 2);
+        return RowJob{rb, (int)(e & 3u), rb >= sp.rs ? sp.np : 1, w.grp};
     }
-    const Work w = map_block(sp.njobs, ngrp, false);
-    const unsigned e = sp.job[w.blk];
-    const int rb = (int)(e >> 2);
-    return RowJob{rb, (int)(e & 3u), rb >= sp.rs ? sp.np : 1, w.grp};
 }
 // Key tiles [lo, hi) of piece p of np of the range [j0, j1).
 __device__ __forceinline__ int piece_lo(int j0, int j1, int p, int np) { return j0 + (j1 - j0) * p / np; }
@@ -642,7 +645,7 @@ __device__ __forceinline__ half8 fold_weights(int h) {
 }
 
 
-template <typename TI, int D, typename TOUT>
+template <typename TI, int D, typename TOUT, bool SPLIT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel_h(FwdArgs a, SplitPlan sp) {
     using OP = _Float16;
@@ -657,7 +660,7 @@ void fwd_kernel_h(FwdArgs a, SplitPlan sp) {
     OP* const lds = reinterpret_cast<OP*>(lds_raw);    // K stages 0..2, then V^T stages 0..2
 
     const int T = a.T, G = a.G, TG = T * G, Tp = (T + 63) / 64 * 64;
-    const RowJob job = map_row_job(sp, a.nrb, a.B * a.Hkv);
+    const RowJob job = map_row_job<SPLIT>(sp, a.nrb, a.B * a.Hkv);
     const int rb = job.rb;
     const int hkv = job.grp % a.Hkv, b = job.grp / a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
@@ -888,7 +891,7 @@ void fwd_kernel_h(FwdArgs a, SplitPlan sp) {
     }
 
     float l_tot = sum_halves(l_run);
-    if (job.np > 1) {
+    if (SPLIT && job.np > 1) {
         // split block: the pieces before the last leave m, l and O (unnormalised, relative to m)
         // in their slot; the last combines all pieces in piece order and writes the output
         __shared__ unsigned sh[2];
@@ -1251,9 +1254,9 @@ void dkdv_kernel(BwdArgs a) {
 // the key block's K' (kept in LDS) and add dQ of their 32 rows x D/2 columns into an fp32
 // accumulator with atomic adds (not bit-reproducible: the order of the adds varies).  With AT the
 // row-tile ring has three stages filled one step ahead, to leave LDS for K' and dS^T.
-template <int D, typename TOUT, int MODE>
+template <int D, typename TOUT, int MODE, bool SPLIT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void dkdv_kernel_h(BwdArgs a) {
+void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
     using OP = _Float16;
     using M = Mma<OP>;
     constexpr bool DS = MODE == 1, AT = MODE == 2;
@@ -1272,7 +1275,20 @@ void dkdv_kernel_h(BwdArgs a) {
     const int T = a.T, G = a.G, TG = T * G;
     const int nkb = (T + BN - 1) / BN;
     const int npair = (nkb + 1) / 2;
-    const Work wk = map_block(npair, a.ngrp, false);
+    // the job: a mirrored pair of key blocks (wk.blk and nkb - 1 - wk.blk), or, under a split
+    // plan, one key block (wk.blk) or piece `piece` of its row tiles
+    Work wk;
+    int piece = 0, np = 1, jrb = 0;
+    if constexpr (SPLIT) {
+        wk = map_block(sp.njobs, a.ngrp, false);
+        const unsigned e = sp.job[wk.blk];
+        jrb = (int)(e >> 2);
+        piece = (int)(e & 3u);
+        np = jrb >= sp.rs ? sp.np : 1;
+        wk.blk = nkb - 1 - jrb;
+    } else {
+        wk = map_block(npair, a.ngrp, false);
+    }
     const int gg = a.grp0 + wk.grp;                   // the (batch, KV head) group
     const int hkv = gg % a.Hkv, b = gg / a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
@@ -1359,7 +1375,7 @@ void dkdv_kernel_h(BwdArgs a) {
 
     for (int pass = 0; pass < 2; ++pass) {
         const int kb = pass == 0 ? wk.blk : nkb - 1 - wk.blk;
-        if (pass == 1 && kb == wk.blk) break;  // odd nkb: the middle block has no mirror
+        if (pass == 1 && (kb == wk.blk || SPLIT)) break;  // odd nkb: the middle block has no mirror
         const int n0 = kb * BN + 32 * kq;                      // first key of this wave
         const int key = n0 + c;
         const bool kvalid = key < T;
@@ -1367,10 +1383,13 @@ void dkdv_kernel_h(BwdArgs a) {
         const int W = a.window;
         const int keyG = key * G;
         const int keyWG = (T - key <= W ? T : key + W) * G;
-        const int rstart = (kb * BN * G) / BMR * BMR;
         const int kl = kb * BN + BN - 1;                                 // the block's last key
         const int rend = (T - kl <= W ? T : kl + W) * G;                 // rows past it see none
-        const int ntiles = (rend - rstart + BMR - 1) / BMR;
+        const int r0 = (kb * BN * G) / BMR * BMR;
+        const int nt0 = (rend - r0 + BMR - 1) / BMR;
+        // this job's row tiles: all of them, or piece `piece` of np
+        const int rstart = r0 + nt0 * piece / np * BMR;
+        const int ntiles = nt0 * (piece + 1) / np - nt0 * piece / np;
         // DS: tile s of this key block (row tile kb G + s) is stored at index dsb + s
         const size_t dsb = DS ? ds_tile_index(kb, kb * G, (TG + 63) / 64, G) : 0;
         const int wlim = (T - (n0 + 31) <= W ? T : n0 + 31 + W) * G;    // rows from wlim see none
@@ -1546,6 +1565,68 @@ void dkdv_kernel_h(BwdArgs a) {
                         floatx4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
         }
         __syncthreads();
+        if (rh == 0) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const floatx4 o1 = *reinterpret_cast<const floatx4*>(&part[((db * 4 + q4) * 64 + l) * 4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[db][4 * q4 + e] += o1[e];
+                }
+        }
+        if (SPLIT && np > 1) {
+            // split block: the pieces before the last leave their sums (the row-half-0 waves' dV^T
+            // / dK^T) in their slot; the last adds all pieces in piece order (deterministic)
+            __shared__ unsigned sh[2];
+            constexpr int NF = NDB * 16;
+            const size_t sb = (size_t)wk.grp * (nkb - sp.rs) + (jrb - sp.rs);
+            unsigned* cnt = sp.cnt + 2 * sb;
+            float* slots = sp.part + sb * np * (size_t)(4 * 64 * NF);
+            auto at = [&](int p) { return slots + (size_t)p * (4 * 64 * NF) + (size_t)(w >> 1) * 64 * NF; };
+            const unsigned ord = split_arrive(cnt, sh);
+            if ((int)ord + 1 < np) {
+                if (rh == 0) {
+                    float* op = at(piece);
+#pragma unroll
+                    for (int i = 0; i < NF / 4; ++i)
+                        *reinterpret_cast<floatx4*>(op + (i * 64 + l) * 4) =
+                            floatx4{acc[i / 4][4 * (i % 4)], acc[i / 4][4 * (i % 4) + 1], acc[i / 4][4 * (i % 4) + 2],
+                                    acc[i / 4][4 * (i % 4) + 3]};
+                }
+                split_publish(cnt);
+                return;
+            }
+            const bool ok = split_collect(cnt, (unsigned)np - 1, sh);
+            if (rh == 0) {
+                floatx16 sum[NDB];
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) sum[db] = floatx16{};
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    if (p >= np) break;
+                    if (p == piece) {
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) sum[db][r] += acc[db][r];
+                    } else {
+                        const float* op = at(p);
+#pragma unroll
+                        for (int i = 0; i < NF / 4; ++i) {
+                            const floatx4 x = *reinterpret_cast<const floatx4*>(op + (i * 64 + l) * 4);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) sum[i / 4][4 * (i % 4) + e] += x[e];
+                        }
+                    }
+                }
+                const float poison = ok ? 1.f : __builtin_nanf("");
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[db][r] = sum[db][r] * poison;
+            }
+        }
         if (rh == 0 && kvalid) {  // both lanes of a key pair (c, c + 32) agree
             const size_t koff = (((size_t)b * T + key) * a.Hkv + hkv) * D;
             const float us = a.dsc ? a.dsc[grp] : 1.f;
@@ -1553,10 +1634,9 @@ void dkdv_kernel_h(BwdArgs a) {
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const floatx4 o1 = *reinterpret_cast<const floatx4*>(&part[((db * 4 + q4) * 64 + l) * 4]);
                     const int d = 32 * db + 8 * q4 + 4 * h;
-                    float x0 = acc[db][4 * q4] + o1[0], x1 = acc[db][4 * q4 + 1] + o1[1];
-                    float x2 = acc[db][4 * q4 + 2] + o1[2], x3 = acc[db][4 * q4 + 3] + o1[3];
+                    float x0 = acc[db][4 * q4], x1 = acc[db][4 * q4 + 1];
+                    float x2 = acc[db][4 * q4 + 2], x3 = acc[db][4 * q4 + 3];
                     if (role == 0) {
                         x0 *= us; x1 *= us; x2 *= us; x3 *= us;
                     } else {
@@ -1781,7 +1861,7 @@ void dq_kernel(BwdArgs a) {
 // EXT: a window shorter than T (its edge is masked too) and/or the QK norm (its backward in the
 // epilogue).  Without them the kernel keeps every register for the plain causal case, where the
 // budget is exhausted.
-template <int D, typename TOUT, bool EXT>
+template <int D, typename TOUT, bool EXT, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void dq_kernel_h(BwdArgs a, SplitPlan sp) {
     using OP = _Float16;
@@ -1790,7 +1870,7 @@ void dq_kernel_h(BwdArgs a, SplitPlan sp) {
     __shared__ __attribute__((aligned(1024))) OP lds[2 * 2 * TILE];  // [stage][K | V]
 
     const int T = a.T, G = a.G, TG = T * G;
-    const RowJob job = map_row_job(sp, a.nrb, a.B * a.Hkv);
+    const RowJob job = map_row_job<SPLIT>(sp, a.nrb, a.B * a.Hkv);
     const int rb = job.rb;
     const int hkv = job.grp % a.Hkv, b = job.grp / a.Hkv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
@@ -1914,7 +1994,7 @@ void dq_kernel_h(BwdArgs a, SplitPlan sp) {
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    if (job.np > 1) {
+    if (SPLIT && job.np > 1) {
         // split block (two pieces): the first to finish leaves its dQ sums in its slot; the other
         // adds them to its own (one addition per element: the same result whichever is last)
         __shared__ unsigned sh[2];
@@ -2215,7 +2295,10 @@ static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, const Spli
         FwdArgs f2 = fa;
         f2.nrb = (int)(((int64_t)fa.T * fa.G + 255) / 256);
         const int njobs = sp.njobs ? sp.njobs : f2.nrb;
-        hipLaunchKernelGGL((fwd_kernel_h<TI, D, TO>), dim3(njobs * fa.Hkv * fa.B), dim3(512), 0, s, f2, sp);
+        if (sp.njobs)
+            hipLaunchKernelGGL((fwd_kernel_h<TI, D, TO, true>), dim3(njobs * fa.Hkv * fa.B), dim3(512), 0, s, f2, sp);
+        else
+            hipLaunchKernelGGL((fwd_kernel_h<TI, D, TO, false>), dim3(njobs * fa.Hkv * fa.B), dim3(512), 0, s, f2, sp);
     }
     else
         hipLaunchKernelGGL((fwd_kernel<TI, OP, D, TO>), dim3(fa.nrb * fa.Hkv * fa.B), dim3(256), 0, s, fa);
@@ -2225,7 +2308,7 @@ static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, const Spli
 
 template <typename TI, typename TO, typename OP, int D>
 static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am, const BwdArgs& ba,
-                               const SplitPlan& sp, hipStream_t s, hipEvent_t const* ev) {
+                               const SplitPlan& sp, const SplitPlan& spk, hipStream_t s, hipEvent_t const* ev) {
     const Marks m{ev, s};
     NE_TRY(m.before(0));
     if constexpr (sizeof(OP) == 2) {
@@ -2247,7 +2330,7 @@ static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am,
                 BwdArgs bb = ba;
                 bb.grp0 = g0;
                 bb.ngrp = min(ba.ds_groups, ngroups - g0);
-                hipLaunchKernelGGL((dkdv_kernel_h<D, TO, 1>), dim3(npair * bb.ngrp), dim3(512), 0, s, bb);
+                hipLaunchKernelGGL((dkdv_kernel_h<D, TO, 1, false>), dim3(npair * bb.ngrp), dim3(512), 0, s, bb, spk);
                 NE_TRY(hipGetLastError());
                 if (g0 + bb.ngrp >= ngroups) {
                     NE_TRY(m.after(1));
@@ -2262,7 +2345,7 @@ static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am,
         }
         if (mode == kBwdAtomic) {
             NE_TRY(m.before(1));
-            hipLaunchKernelGGL((dkdv_kernel_h<D, TO, 2>), dim3(npair * ngroups), dim3(512), 0, s, ba);
+            hipLaunchKernelGGL((dkdv_kernel_h<D, TO, 2, false>), dim3(npair * ngroups), dim3(512), 0, s, ba, spk);
             NE_TRY(hipGetLastError());
             NE_TRY(m.after(1));
             NE_TRY(m.before(2));
@@ -2275,18 +2358,22 @@ static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am,
     }
     NE_TRY(m.before(1));
     if constexpr (sizeof(OP) == 2)
-        hipLaunchKernelGGL((dkdv_kernel_h<D, TO, 0>), dim3(npair * ngroups), dim3(512), 0, s, ba);
+        if (spk.njobs)
+            hipLaunchKernelGGL((dkdv_kernel_h<D, TO, 0, true>), dim3(spk.njobs * ngroups), dim3(512), 0, s, ba, spk);
+        else
+            hipLaunchKernelGGL((dkdv_kernel_h<D, TO, 0, false>), dim3(npair * ngroups), dim3(512), 0, s, ba, spk);
     else
         hipLaunchKernelGGL((dkdv_kernel<OP, D, TO>), dim3(npair * ngroups), dim3(512), 0, s, ba);
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(1));
     NE_TRY(m.before(2));
     if constexpr (sizeof(OP) == 2) {
-        const int njobs = sp.njobs ? sp.njobs : ba.nrb;
         if (ba.window < ba.T || ba.qkn.on)
-            hipLaunchKernelGGL((dq_kernel_h<D, TO, true>), dim3(njobs * ngroups), dim3(256), 0, s, ba, sp);
+            hipLaunchKernelGGL((dq_kernel_h<D, TO, true, false>), dim3(ba.nrb * ngroups), dim3(256), 0, s, ba, sp);
+        else if (sp.njobs)
+            hipLaunchKernelGGL((dq_kernel_h<D, TO, false, true>), dim3(sp.njobs * ngroups), dim3(256), 0, s, ba, sp);
         else
-            hipLaunchKernelGGL((dq_kernel_h<D, TO, false>), dim3(njobs * ngroups), dim3(256), 0, s, ba, sp);
+            hipLaunchKernelGGL((dq_kernel_h<D, TO, false, false>), dim3(ba.nrb * ngroups), dim3(256), 0, s, ba, sp);
     }
     else
         hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb * ngroups), dim3(256), 0, s, ba);
@@ -2313,12 +2400,13 @@ hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const Fw
 }
 
 hipError_t launch_bwd(int in_dt, int out_dt, int D, int mode, const PrepArgs& pa, const AmaxArgs& am,
-                      const BwdArgs& ba, const SplitPlan& sp, hipStream_t s, hipEvent_t const* ev) {
-    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, float, float, float, D, mode, pa, am, ba, sp, s, ev) }
-    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, __bf16, float, _Float16, D, mode, pa, am, ba, sp, s, ev) }
-    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_bwd_t, __bf16, __bf16, _Float16, D, mode, pa, am, ba, sp, s, ev) }
-    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, _Float16, float, _Float16, D, mode, pa, am, ba, sp, s, ev) }
-    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_bwd_t, _Float16, _Float16, _Float16, D, mode, pa, am, ba, sp, s, ev) }
+                      const BwdArgs& ba, const SplitPlan& spq, const SplitPlan& spk, hipStream_t s,
+                      hipEvent_t const* ev) {
+    if (in_dt == 0 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, float, float, float, D, mode, pa, am, ba, spq, spk, s, ev) }
+    if (in_dt == 1 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, __bf16, float, _Float16, D, mode, pa, am, ba, spq, spk, s, ev) }
+    if (in_dt == 1 && out_dt == 1) { NE_DISPATCH_D(launch_bwd_t, __bf16, __bf16, _Float16, D, mode, pa, am, ba, spq, spk, s, ev) }
+    if (in_dt == 2 && out_dt == 0) { NE_DISPATCH_D(launch_bwd_t, _Float16, float, _Float16, D, mode, pa, am, ba, spq, spk, s, ev) }
+    if (in_dt == 2 && out_dt == 2) { NE_DISPATCH_D(launch_bwd_t, _Float16, _Float16, _Float16, D, mode, pa, am, ba, spq, spk, s, ev) }
     return hipErrorInvalidValue;
 }
 

@@ -85,13 +85,19 @@ struct SplitPlan {
     unsigned* cnt;                                  // [split block][arrived, written]
     unsigned short job[kMaxSplitJobs];
 };
-// The host's plan for a launch of BM-row blocks, at most max_np (<= 4) pieces per block: fills
-// njobs, rs, np, nrb and job (not part and cnt).  It depends only on the causal tile counts of the row blocks (tiles of 64 keys, no
-// window), the number of groups and the workgroups the chip runs at once (256 CUs x wg_per_cu).
-void split_plan(int T, int G, int ngrp, int BM, int wg_per_cu, int max_np, SplitPlan* out);
-// floats of the partial-result slot of one piece (forward: O, m and l of 8 waves; dQ: 4 waves)
+// The host's plan of one pass: fills njobs, rs, np, nrb and job (not part and cnt).  It depends
+// only on the causal step counts of the blocks (no window), the number of groups and the
+// workgroups the chip runs at once (256 CUs).  Forward: 256-row blocks, up to 4 pieces; dQ:
+// 128-row blocks (two workgroups per CU), 2 pieces; dK/dV: 64-key blocks, up to 4 pieces, job
+// index rb meaning key block nkb - 1 - rb -- a dK/dV plan replaces the mirrored pairs, and may
+// split nothing (rs = nrb, np = 1: single blocks longest-first fill the CUs the pairs leave idle).
+enum { kSplitFwd = 0, kSplitDq = 1, kSplitDkdv = 2 };
+void split_plan(int kind, int T, int G, int ngrp, SplitPlan* out);
+// floats of the partial-result slot of one piece (forward: O, m and l of 8 waves; dQ: 4 waves;
+// dK/dV: the 4 waves that hold the block's dV^T and dK^T after the row halves are added)
 inline size_t split_slot_floats_fwd(int D) { return (size_t)8 * 64 * (D / 2 + 2); }
 inline size_t split_slot_floats_dq(int D) { return (size_t)4 * 64 * (D / 2); }
+inline size_t split_slot_floats_dkdv(int D) { return (size_t)4 * 64 * (D / 2); }
 
 struct FwdArgs {
     const void* q;                                  // raw queries (in dtype), rotated in the kernel
@@ -167,14 +173,15 @@ struct QkvArgs {
 // ev (nullable): hipEvent_t pairs recorded on `s` around each kernel launch, in launch order
 // (forward: prep, fwd; backward: prep, dkdv, dq).
 hipError_t launch_table(const TableArgs& a, hipStream_t s);
-// sp: the split plan of the 16-bit forward (forward) or of the recomputing dQ pass (backward);
-// njobs == 0 for none.
+// sp / spq / spk: the split plans of the 16-bit forward, of the recomputing dQ pass and of its
+// dK/dV pass (njobs == 0: none).
 hipError_t launch_fwd(int in_dt, int out_dt, int D, const PrepArgs& pa, const FwdArgs& fa, const SplitPlan& sp,
                       hipStream_t s, hipEvent_t const* ev);
 // mode: 0 dQ recomputes S and dP, 1 dQ reads the stored dS, 2 atomic dQ in the dK/dV pass
 enum { kBwdRecompute = 0, kBwdStoredDs = 1, kBwdAtomic = 2 };
 hipError_t launch_bwd(int in_dt, int out_dt, int D, int mode, const PrepArgs& pa, const AmaxArgs& am,
-                      const BwdArgs& ba, const SplitPlan& sp, hipStream_t s, hipEvent_t const* ev);
+                      const BwdArgs& ba, const SplitPlan& spq, const SplitPlan& spk, hipStream_t s,
+                      hipEvent_t const* ev);
 hipError_t launch_append(int in_dt, int D, const AppendArgs& a, hipStream_t s);
 // ev (nullable): pairs around the cos/sin table and the product (4 entries).
 hipError_t launch_qkv(int in_dt, int out_dt, int D, const QkvArgs& a, hipStream_t s, hipEvent_t const* ev);

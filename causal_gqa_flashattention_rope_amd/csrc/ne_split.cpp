@@ -20,16 +20,26 @@ namespace ne {
 namespace {
 
 constexpr int kCus = 256;            // CUs of the chip the plan is made for
-constexpr double kJobCost = 1.0;     // per job, in key tiles
-// extra per piece of a split block, in key tiles: the hand-off (partial result through memory,
-// agent-scope release / acquire, which write back and invalidate the XCD's L2 and so also cost
-// the other workgroups there) measured at several tiles' time -- splitting pays only where the
-// unsplit order leaves most CUs idle (a group or two per launch), not for a 20% imbalance
-constexpr double kPieceCost = 4.0;
 constexpr double kMinGain = 0.8;     // split only if the simulated end drops below this fraction
 
+// Per pass: rows per job, workgroups per CU, most pieces per block, and the costs in steps of
+// that pass (one 64-key tile of the block's rows): per job (operand loads, epilogue) and per
+// piece of a split block -- the hand-off (partial result through memory, agent-scope release /
+// acquire, which write back and invalidate the XCD's L2 and so also cost the other workgroups
+// there) measured at several steps' time, so splitting pays only where the unsplit order leaves
+// most CUs idle (a group or two per launch), not for a 20% imbalance.
+struct Kind {
+    int BM, wg, maxp;
+    double job, piece;
+};
+constexpr Kind kKinds[3] = {
+    {256, 1, 4, 1.0, 4.0},   // forward: 256 rows x 64 keys per step
+    {128, 2, 2, 1.0, 4.0},   // dQ: 128 rows x 64 keys
+    {64, 1, 4, 2.0, 8.0},    // dK/dV: 64 keys x 64 rows (four products, about half a forward step)
+};
+
 struct Entry {
-    int T, G, ngrp, BM, wg, maxp;
+    int kind, T, G, ngrp;
     int njobs, rs, np, nrb;
     std::vector<unsigned short> job;
 };
@@ -54,16 +64,16 @@ struct Job {
 };
 
 // jobs of one group for (rs, np), longest first (ties: later block first, then piece order)
-std::vector<Job> jobs_for(const std::vector<int>& tiles, int rs, int np) {
+std::vector<Job> jobs_for(const std::vector<int>& tiles, int rs, int np, const Kind& k) {
     std::vector<Job> j;
     const int nrb = (int)tiles.size();
     for (int rb = 0; rb < nrb; ++rb) {
         if (rb >= rs) {
             const int n = tiles[rb];
             for (int p = 0; p < np; ++p)
-                j.push_back({(double)(n * (p + 1) / np - n * p / np) + kJobCost + kPieceCost, rb, p});
+                j.push_back({(double)(n * (p + 1) / np - n * p / np) + k.job + k.piece, rb, p});
         } else {
-            j.push_back({(double)tiles[rb] + kJobCost, rb, 0});
+            j.push_back({(double)tiles[rb] + k.job, rb, 0});
         }
     }
     std::stable_sort(j.begin(), j.end(), [](const Job& a, const Job& b) {
@@ -74,37 +84,75 @@ std::vector<Job> jobs_for(const std::vector<int>& tiles, int rs, int np) {
     return j;
 }
 
-Entry make_plan(int T, int G, int ngrp, int BM, int wg, int maxp) {
-    Entry e{T, G, ngrp, BM, wg, maxp, 0, 0, 1, 0, {}};
+// Steps of each block, indexed so that they grow with the index: forward and dQ, row block rb
+// (its causal keys); dK/dV, key block nkb - 1 - rb (its rows from the diagonal on).
+std::vector<int> block_steps(int kind, int64_t TG, int T, int G, int nrb) {
+    std::vector<int> tiles(nrb);
+    for (int rb = 0; rb < nrb; ++rb) {
+        if (kind == kSplitDkdv) {
+            const int64_t kb = nrb - 1 - rb;
+            tiles[rb] = (int)((TG - kb * 64 * G + 63) / 64);
+        } else {
+            const int BM = kKinds[kind].BM;
+            tiles[rb] = (int)(std::min<int64_t>((int64_t)rb * BM + BM - 1, TG - 1) / G / 64 + 1);
+        }
+    }
+    (void)T;
+    return tiles;
+}
+
+Entry make_plan(int kind, int T, int G, int ngrp) {
+    const Kind& k = kKinds[kind];
+    Entry e{kind, T, G, ngrp, 0, 0, 1, 0, {}};
     const int64_t TG = (int64_t)T * G;
-    const int64_t nrb64 = (TG + BM - 1) / BM;
+    const int64_t nrb64 = kind == kSplitDkdv ? ((int64_t)T + 63) / 64 : (TG + k.BM - 1) / k.BM;
     e.nrb = (int)std::min<int64_t>(nrb64, INT32_MAX);
-    const int slots = kCus * wg;
+    const int slots = kCus * k.wg;
     // enough blocks per slot, or too many to list: the longest-first order balances by itself
     if (nrb64 > 16383 || (int64_t)ngrp * nrb64 > (int64_t)4 * slots) return e;
-    std::vector<int> tiles(e.nrb);
-    for (int rb = 0; rb < e.nrb; ++rb)
-        tiles[rb] = (int)(std::min<int64_t>((int64_t)rb * BM + BM - 1, TG - 1) / G / 64 + 1);
+    const std::vector<int> tiles = block_steps(kind, TG, T, G, e.nrb);
     std::vector<double> cost;
     auto eval = [&](const std::vector<Job>& j) {
         cost.clear();
         for (const Job& x : j) cost.push_back(x.cost);
         return simulate(cost, ngrp, slots);
     };
-    double best = eval(jobs_for(tiles, e.nrb, 1));
-    const double base = best;
+    // dK/dV without a plan runs mirrored pairs of key blocks: equal work per workgroup
+    double base;
+    if (kind == kSplitDkdv) {
+        const int npair = (e.nrb + 1) / 2;
+        cost.assign(npair, 0.0);
+        for (int i = 0; i < npair; ++i)
+            cost[i] = tiles[e.nrb - 1 - i] + (i != e.nrb - 1 - i ? tiles[i] + k.job : 0.0) + k.job;
+        base = simulate(cost, ngrp, slots);
+    } else {
+        base = eval(jobs_for(tiles, e.nrb, 1, k));
+    }
+    // dK/dV: single key blocks longest-first, none split, need no hand-off -- the first choice when
+    // the pairs leave CUs idle
+    double ref = base;
+    bool single = false;
+    if (kind == kSplitDkdv) {
+        const double m = eval(jobs_for(tiles, e.nrb, 1, k));
+        if (m < 0.97 * base) { ref = m; single = true; }
+    }
+    double best = ref;
     int brs = e.nrb, bnp = 1;
     // candidate first split blocks: every block for short lists, else 32 evenly spaced ones
     const int step = std::max(1, e.nrb / 32);
-    for (int np = 2; np <= std::min(maxp, 4); ++np)
+    for (int np = 2; np <= k.maxp; ++np)
         for (int rs = e.nrb - 1; rs >= 0; rs -= step) {
             if (tiles[rs] < 2 * np) break;  // tiles grow with rb: smaller rs only shortens pieces
             if ((int64_t)rs + (int64_t)(e.nrb - rs) * np > kMaxSplitJobs) break;
-            const double m = eval(jobs_for(tiles, rs, np));
+            const double m = eval(jobs_for(tiles, rs, np, k));
             if (m < best) { best = m; brs = rs; bnp = np; }
         }
-    if (bnp == 1 || best > kMinGain * base) return e;  // not worth the hand-off
-    const std::vector<Job> j = jobs_for(tiles, brs, bnp);
+    if (bnp == 1 || best > kMinGain * ref) {  // not worth the hand-off
+        if (!single) return e;
+        brs = e.nrb;
+        bnp = 1;
+    }
+    const std::vector<Job> j = jobs_for(tiles, brs, bnp, k);
     e.njobs = (int)j.size();
     e.rs = brs;
     e.np = bnp;
@@ -117,15 +165,15 @@ std::vector<Entry>* g_cache = nullptr;
 
 }  // namespace
 
-void split_plan(int T, int G, int ngrp, int BM, int wg_per_cu, int max_np, SplitPlan* out) {
+void split_plan(int kind, int T, int G, int ngrp, SplitPlan* out) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (!g_cache) g_cache = new std::vector<Entry>();  // kept for the process (entries are small)
     const Entry* hit = nullptr;
     for (const Entry& e : *g_cache)
-        if (e.T == T && e.G == G && e.ngrp == ngrp && e.BM == BM && e.wg == wg_per_cu && e.maxp == max_np) hit = &e;
+        if (e.kind == kind && e.T == T && e.G == G && e.ngrp == ngrp) hit = &e;
     if (!hit) {
         if (g_cache->size() >= 256) g_cache->erase(g_cache->begin());
-        g_cache->push_back(make_plan(T, G, ngrp, BM, wg_per_cu, max_np));
+        g_cache->push_back(make_plan(kind, T, G, ngrp));
         hit = &g_cache->back();
     }
     out->njobs = hit->njobs;

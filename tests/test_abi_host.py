@@ -56,37 +56,59 @@ def amax_parts(B, T, Hkv):
     return max(1, min(-(-512 // B), -(-T // 8), 1024))
 
 
-def split_plan(T, G, ngrp, BM, wg, maxp):
-    """(rs, np) of the key-range split of the longest causal row blocks, or None: the greedy
-    dispatch of the longest-first job list (each job to the slot that frees first) over 256 CUs x
-    wg slots, cost = key tiles + 1 per job + 4 per piece of a split block; the earliest end
-    wins if it is below 0.8 of the unsplit order's."""
+KINDS = {  # pass: rows per job, workgroups per CU, most pieces, cost per job, cost per piece
+    "fwd": (256, 1, 4, 1.0, 4.0), "dq": (128, 2, 2, 1.0, 4.0), "dkdv": (64, 1, 4, 2.0, 8.0)}
+
+
+def split_plan(kind, T, G, ngrp):
+    """(rs, np) of the split of the longest causal blocks of one pass, or None.  Steps per block
+    (growing with the index): forward / dQ row block rb, its causal 64-key tiles; dK/dV key block
+    nkb - 1 - rb, its 64-row tiles from the diagonal on.  The greedy dispatch of the longest-first
+    job list (each job to the slot that frees first) over 256 CUs x wg slots, cost = steps + per
+    job + per piece of a split block; the unsplit dK/dV runs mirrored pairs.  The earliest end
+    wins if it is below 0.8 of the unsplit one."""
+    BM, wg, maxp, cjob, cpiece = KINDS[kind]
     TG = T * G
-    nrb = -(-TG // BM)
+    nrb = -(-T // 64) if kind == "dkdv" else -(-TG // BM)
     slots = 256 * wg
     if nrb > 16383 or ngrp * nrb > 4 * slots:
         return None
-    tiles = [min(rb * BM + BM - 1, TG - 1) // G // 64 + 1 for rb in range(nrb)]
+    if kind == "dkdv":
+        tiles = [-(-(TG - (nrb - 1 - rb) * 64 * G) // 64) for rb in range(nrb)]
+    else:
+        tiles = [min(rb * BM + BM - 1, TG - 1) // G // 64 + 1 for rb in range(nrb)]
 
-    def end(rs, np_):
-        jobs = []
-        for rb in range(nrb):
-            if rb >= rs:
-                n = tiles[rb]
-                jobs += [(n * (p + 1) // np_ - n * p // np_) + 5.0 for p in range(np_)]
-            else:
-                jobs.append(tiles[rb] + 1.0)
+    def dispatch(costs):
         h = [0.0] * slots
         last = 0.0
-        for c in sorted(jobs, reverse=True):
+        for c in costs:
             for _ in range(ngrp):
                 t = heapq.heappop(h) + c
                 heapq.heappush(h, t)
                 last = max(last, t)
         return last
 
-    best = base = end(nrb, 1)
-    choice = None
+    def end(rs, np_):
+        jobs = []
+        for rb in range(nrb):
+            if rb >= rs:
+                n = tiles[rb]
+                jobs += [(n * (p + 1) // np_ - n * p // np_) + cjob + cpiece for p in range(np_)]
+            else:
+                jobs.append(tiles[rb] + cjob)
+        return dispatch(sorted(jobs, reverse=True))
+
+    ref, single = None, False
+    if kind == "dkdv":
+        npair = (nrb + 1) // 2
+        ref = dispatch([tiles[nrb - 1 - i] + (tiles[i] + cjob if i != nrb - 1 - i else 0.0) + cjob
+                        for i in range(npair)])
+        m = end(nrb, 1)        # single key blocks, none split
+        if m < 0.97 * ref:
+            ref, single = m, True
+    else:
+        ref = end(nrb, 1)
+    best, choice = ref, None
     step = max(1, nrb // 32)
     for np_ in range(2, maxp + 1):
         for rs in range(nrb - 1, -1, -step):
@@ -95,22 +117,28 @@ def split_plan(T, G, ngrp, BM, wg, maxp):
             m = end(rs, np_)
             if m < best:
                 best, choice = m, (rs, np_)
-    if choice is None or best > 0.8 * base:
-        return None
+    if choice is None or best > 0.8 * ref:
+        return (nrb, 1) if single else None
     return choice
 
 
 def split_bytes(B, T, Hq, Hkv, D, bwd):
-    """Workspace of the split row blocks: per split block, a slot per piece (forward: O, m, l of
-    8 waves x 64 lanes; dQ: dQ of 4 waves x 64 lanes, fp32) and two counters."""
-    G = Hq // Hkv
-    plan = split_plan(T, G, B * Hkv, 128 if bwd else 256, 2 if bwd else 1, 2 if bwd else 4)
-    if plan is None:
-        return 0
-    rs, np_ = plan
-    nsb = B * Hkv * (-(-T * G // (128 if bwd else 256)) - rs)
-    slot = 4 * 64 * (D // 2) if bwd else 8 * 64 * (D // 2 + 2)
-    return up(nsb * np_ * slot * 4) + up(nsb * 2 * 4)
+    """Workspace of the split blocks: per split block, a slot per piece (forward: O, m, l of 8
+    waves x 64 lanes; dQ and dK/dV: 4 waves x 64 lanes of D / 2 floats) and two counters, the
+    counters of a call together; the backward's are those of its dQ and dK/dV passes."""
+    G, ngrp = Hq // Hkv, B * Hkv
+    regions, ncnt = [], 0
+    for kind in (("dq", "dkdv") if bwd else ("fwd",)):
+        plan = split_plan(kind, T, G, ngrp)
+        n, np_ = 0, 1
+        if plan is not None:
+            rs, np_ = plan
+            nrb = -(-T // 64) if kind == "dkdv" else -(-T * G // KINDS[kind][0])
+            n = ngrp * (nrb - rs)
+        slot = 8 * 64 * (D // 2 + 2) if kind == "fwd" else 4 * 64 * (D // 2)
+        regions.append(up(n * np_ * slot * 4))
+        ncnt += 2 * n
+    return sum(regions) + up(ncnt * 4)
 
 
 def sizes(B, T, Hq, Hkv, D, esz, base=1e4):
@@ -128,20 +156,26 @@ def sizes(B, T, Hq, Hkv, D, esz, base=1e4):
 
 
 def test_split_plans_of_the_parity_shapes():
-    """The GPU parity shapes meant to cover the split row blocks are split: forward into 4 pieces,
-    the dQ pass into 2 (not the third shape's); the workloads of the benchmark keep their blocks."""
-    fwd = [split_plan(T, Hq // Hkv, B * Hkv, 256, 1, 4) for B, T, Hq, Hkv, D in
-           [(1, 1000, 4, 1, 128), (1, 1200, 4, 2, 64), (1, 777, 2, 1, 32)]]
-    dq = [split_plan(T, Hq // Hkv, B * Hkv, 128, 2, 2) for B, T, Hq, Hkv, D in
-          [(1, 1000, 4, 1, 128), (1, 1200, 4, 2, 64), (1, 777, 2, 1, 32)]]
+    """The GPU parity shapes meant to cover the split blocks are split: forward into 4 pieces, the
+    dQ pass into 2 (not the third shape's), dK/dV into 2-4; the benchmark's workloads keep their
+    blocks whole, one GPU's share of the 8192-token layer (one group) splits all three passes."""
+    shapes = [(1, 1000, 4, 1, 128), (1, 1200, 4, 2, 64), (1, 777, 2, 1, 32)]
+    fwd = [split_plan("fwd", T, Hq // Hkv, B * Hkv) for B, T, Hq, Hkv, D in shapes]
+    dq = [split_plan("dq", T, Hq // Hkv, B * Hkv) for B, T, Hq, Hkv, D in shapes]
+    kv = [split_plan("dkdv", T, Hq // Hkv, B * Hkv) for B, T, Hq, Hkv, D in shapes]
     assert all(p is not None and p[1] == 4 for p in fwd)
     assert dq[0] is not None and dq[1] is not None and dq[2] is None
     assert all(p[1] == 2 for p in dq[:2])
-    for B, T, Hq, Hkv in ((4, 2048, 12, 4), (8, 512, 12, 4), (16, 1024, 12, 12), (1, 8192, 32, 8)):
-        assert split_plan(T, Hq // Hkv, B * Hkv, 256, 1, 4) is None
-        assert split_plan(T, Hq // Hkv, B * Hkv, 128, 2, 2) is None
-    # one GPU's share of the 8192-token layer (one group) is split in both passes
-    assert split_plan(8192, 4, 1, 256, 1, 4) is not None and split_plan(8192, 4, 1, 128, 2, 2) is not None
+    assert all(p is not None and p[1] >= 2 for p in kv)
+    for B, T, Hq, Hkv in ((4, 2048, 12, 4), (16, 1024, 12, 12), (1, 8192, 32, 8)):
+        for kind in KINDS:
+            assert split_plan(kind, T, Hq // Hkv, B * Hkv) is None, (kind, T)
+    # the 512-token layer: its 128 mirrored pairs of key blocks fill half the CUs; single key
+    # blocks, none split, fill them all
+    assert split_plan("fwd", 512, 3, 32) is None and split_plan("dq", 512, 3, 32) is None
+    assert split_plan("dkdv", 512, 3, 32) == (8, 1)
+    for kind in KINDS:
+        assert split_plan(kind, 8192, 4, 1)[1] > 1
 
 
 def wsb(L, is_bwd, B, T, Hq, Hkv, D, base=1e4, dt=binding.NE_BF16, flags=0):

@@ -180,9 +180,11 @@ def test_parity_small_other_backwards(shape, in_dt, flags):
 
 def test_the_three_backwards_agree():
     """The dK/dV pass's arithmetic is the same in all three designs (o, lse, dk, dv bitwise equal); the
-    dQ passes use the same dS up to where its fp16 rounding and the order of the sums happen."""
+    dQ passes use the same dS up to where its fp16 rounding and the order of the sums happen.  At the
+    full batch of 4: with fewer groups the default backward's dK/dV pass splits its longest key
+    blocks (the same sums in another order) while the other two keep the mirrored pairs."""
     w = inputs.WORKLOADS["wide_gqa_t2048_d128"]
-    q, k, v, dO = inputs.make_inputs(w, B=1)
+    q, k, v, dO = inputs.make_inputs(w)
     ref = run_gpu(q, k, v, dO, w.rope_base, torch.float32)
     for flags in BWD_FLAGS[1:]:
         again = run_gpu(q, k, v, dO, w.rope_base, torch.float32, flags=flags)

@@ -110,9 +110,9 @@ ne::SplitPlan* split_scratch(int kind) {
     thread_local ne::SplitPlan sp[3];
     return &sp[kind];
 }
-ne::SplitPlan* plan_for(int kind, int T, int G, int ngrp) {
+ne::SplitPlan* plan_for(int kind, int T, int G, int ngrp, int D) {
     ne::SplitPlan* sp = split_scratch(kind);
-    ne::split_plan(kind, T, G, ngrp, sp);
+    ne::split_plan(kind, T, G, ngrp, D, sp);
     return sp;
 }
 // split blocks of a plan (0 without one)
@@ -162,15 +162,15 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, double base, ne_dt
     if (in != NE_F32 && (!bwd || L.mode == ne::kBwdRecompute)) {
         const int ngrp = B * Hkv, G = Hq / Hkv;
         if (!bwd) {
-            const ne::SplitPlan* f = plan_for(ne::kSplitFwd, T, G, ngrp);
+            const ne::SplitPlan* f = plan_for(ne::kSplitFwd, T, G, ngrp, D);
             const size_t n = split_blocks(*f, ngrp);
             L.fpart = off; off += up(n * f->np * ne::split_slot_floats_fwd(D) * 4);
             L.ncnt_q = 2 * n;
         } else {
-            const ne::SplitPlan* q = plan_for(ne::kSplitDq, T, G, ngrp);
+            const ne::SplitPlan* q = plan_for(ne::kSplitDq, T, G, ngrp, D);
             const size_t nq = split_blocks(*q, ngrp);
             L.qpart = off; off += up(nq * q->np * ne::split_slot_floats_dq(D) * 4);
-            const ne::SplitPlan* k = plan_for(ne::kSplitDkdv, T, G, ngrp);
+            const ne::SplitPlan* k = plan_for(ne::kSplitDkdv, T, G, ngrp, D);
             const size_t nk = split_blocks(*k, ngrp);
             L.kpart = off; off += up(nk * k->np * ne::split_slot_floats_dkdv(D) * 4);
             L.ncnt_q = 2 * nq;
@@ -317,7 +317,7 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     ne::SplitPlan* sp = split_scratch(ne::kSplitFwd);
     sp->njobs = 0;
     if (in_dtype != NE_F32 && fa.window >= T) {
-        plan_for(ne::kSplitFwd, T, G, B * Hkv);
+        plan_for(ne::kSplitFwd, T, G, B * Hkv, head_dim);
         if (sp->njobs) {
             sp->part = (float*)(ws + L.fpart);
             sp->cnt = (unsigned*)(ws + L.cnt);
@@ -398,8 +398,8 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     ne::SplitPlan* spk = split_scratch(ne::kSplitDkdv);
     spq->njobs = spk->njobs = 0;
     if (h16 && L.mode == ne::kBwdRecompute && ba.window >= T) {
-        if (!qkn.on) plan_for(ne::kSplitDq, T, G, B * Hkv);
-        plan_for(ne::kSplitDkdv, T, G, B * Hkv);
+        if (!qkn.on) plan_for(ne::kSplitDq, T, G, B * Hkv, head_dim);
+        plan_for(ne::kSplitDkdv, T, G, B * Hkv, head_dim);
         spq->part = (float*)(ws + L.qpart);
         spq->cnt = (unsigned*)(ws + L.cnt);
         spk->part = (float*)(ws + L.kpart);

@@ -1254,13 +1254,22 @@ void dkdv_kernel(BwdArgs a) {
 // the key block's K' (kept in LDS) and add dQ of their 32 rows x D/2 columns into an fp32
 // accumulator with atomic adds (not bit-reproducible: the order of the adds varies).  With AT the
 // row-tile ring has three stages filled one step ahead, to leave LDS for K' and dS^T.
+// W4: head_dim <= 64, the plain-causal design under a plan (single key blocks or pieces): two
+// workgroups per CU (four waves per SIMD, 128 VGPRs), a 3-stage ring filled one tile ahead and
+// operands read two products ahead, which fits without spills; at D = 64 a 64-row step carries
+// half the products of D = 128 for the same chain of dependent steps, so the second workgroup's
+// waves are what hides it (the 12-head, 1024-token MHA layer: dK/dV 134 -> 92 us).
+template <int D, int MODE, bool SPLIT>
+struct DkdvShape {
+    static constexpr bool W4 = D <= 64 && MODE == 0 && SPLIT;
+};
 template <int D, typename TOUT, int MODE, bool SPLIT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(DkdvShape<D, MODE, SPLIT>::W4 ? 4 : 2)))
 void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
     using OP = _Float16;
     using M = Mma<OP>;
-    constexpr bool DS = MODE == 1, AT = MODE == 2;
-    constexpr int KSUB = 2, BN = 32 * KSUB, BMR = 64, NW = 8, NST = AT ? 3 : 4, AHEAD = AT ? 1 : 2;
+    constexpr bool DS = MODE == 1, AT = MODE == 2, W4 = DkdvShape<D, MODE, SPLIT>::W4;
+    constexpr int KSUB = 2, BN = 32 * KSUB, BMR = 64, NW = 8, NST = AT || W4 ? 3 : 4, AHEAD = AT || W4 ? 1 : 2;
     constexpr int KS = D / 16, NDB = D / 32, TILE = BMR * D;
     // AT: the D / 32 column blocks of dQ split between the two key sub-block waves of a row half
     constexpr int NDQ = NDB >= 2 ? NDB / 2 : 1, NATOM = 16 * NDQ;
@@ -1335,7 +1344,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
     // registers the dQ product needs)
     auto chain = [&](const OP* rows, auto KT) {
         constexpr bool FROM_TILE = decltype(KT)::value;
-        constexpr int AH = KS < 4 ? KS : 4;
+        constexpr int AH = W4 ? 2 : (KS < 4 ? KS : 4);
         half8 fr[KS];
 #pragma unroll
         for (int i = 0; i < AH; ++i) fr[i] = row_frag_sw<OP, D>(rows, 32 * rh + c, i, h);
@@ -1441,7 +1450,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
             // with AT, the fill is one step ahead and role 0's atomic adds of the previous step were
             // issued after it: vector memory operations complete in order)
             if constexpr (AT) lds_fill_wait_keep_atomics(natom);
-            else lds_fill_wait_keep((s + 1 < ntiles ? per_fill : 0) + (DS && RL == 1 && s >= 2 ? 2 : 0));
+            else lds_fill_wait_keep((AHEAD == 2 && s + 1 < ntiles ? per_fill : 0) + (DS && RL == 1 && s >= 2 ? 2 : 0));
             natom = 0;
             if (s + AHEAD < ntiles) fill((s + AHEAD) % NST, rstart + (s + AHEAD) * BMR);
             if constexpr (RL == 0) {
@@ -2150,6 +2159,8 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
         rlo[r] = __builtin_amdgcn_readfirstlane(rtx < nrt ? kb_lo(rtx) : 1);
         rhi[r] = __builtin_amdgcn_readfirstlane(rtx < nrt ? kb_hi(rtx) : 0);
     }
+    // start (in elements) of the 8 KiB that the loads past hi read from the group's K' rows
+    const int64_t kdummy = (int64_t)T * D >= 4096 ? min((int64_t)hi * BN * D, (int64_t)T * D - 4096) : -1;
     auto issue = [&](int kb, auto SLOT) {
         constexpr int sl = decltype(SLOT)::value;
         const int kc = min(kb, hi);
@@ -2161,9 +2172,13 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             const bool ok = kc >= rlo[r] && kc <= rhi[r];
-            // past hi the loads are not used: read the K tile of hi again (L2-resident) instead of dS
-            gu32x4* src = sgpr_global_ptr<const u32x4>(kb > hi ? kg + (size_t)kc * BN * D
-                                                               : dsg + (ok ? ds_tile_index(kc, rt0 + r, nrt, G) : 0) * 4096);
+            // past hi the loads are not used: read 8 KiB of the group's K' rows again (L2-resident)
+            // instead of dS, ending at the group's last row at most (a K tile holds only 4 KiB at
+            // D = 32, and a ragged last tile less); a group with fewer than 8 KiB of K' reads its
+            // first dS tile instead (a whole 8 KiB tile of its own)
+            gu32x4* src = sgpr_global_ptr<const u32x4>(
+                kb > hi ? (kdummy >= 0 ? kg + kdummy : dsg)
+                        : dsg + (ok ? ds_tile_index(kc, rt0 + r, nrt, G) : 0) * 4096);
             dr[sl][r] = __builtin_nontemporal_load(src + tid);
         }
     };

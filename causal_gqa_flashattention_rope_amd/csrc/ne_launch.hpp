@@ -91,8 +91,10 @@ struct SplitPlan {
 // 128-row blocks (two workgroups per CU), 2 pieces; dK/dV: 64-key blocks, up to 4 pieces, job
 // index rb meaning key block nkb - 1 - rb -- a dK/dV plan replaces the mirrored pairs, and may
 // split nothing (rs = nrb, np = 1: single blocks longest-first fill the CUs the pairs leave idle).
+// At head_dim <= 64 the dK/dV pass always has a plan (up to 1024 key blocks): its planned variant
+// runs two workgroups per CU.
 enum { kSplitFwd = 0, kSplitDq = 1, kSplitDkdv = 2 };
-void split_plan(int kind, int T, int G, int ngrp, SplitPlan* out);
+void split_plan(int kind, int T, int G, int ngrp, int D, SplitPlan* out);
 // floats of the partial-result slot of one piece (forward: O, m and l of 8 waves; dQ: 4 waves;
 // dK/dV: the 4 waves that hold the block's dV^T and dK^T after the row halves are added)
 inline size_t split_slot_floats_fwd(int D) { return (size_t)8 * 64 * (D / 2 + 2); }

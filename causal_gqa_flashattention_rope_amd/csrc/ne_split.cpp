@@ -35,11 +35,13 @@ struct Kind {
 constexpr Kind kKinds[3] = {
     {256, 1, 4, 1.0, 4.0},   // forward: 256 rows x 64 keys per step
     {128, 2, 2, 1.0, 4.0},   // dQ: 128 rows x 64 keys
-    {64, 1, 4, 2.0, 8.0},    // dK/dV: 64 keys x 64 rows (four products, about half a forward step)
+    {64, 1, 4, 2.0, 16.0},   // dK/dV: 64 keys x 64 rows (four products, about half a forward step);
+                             // a 4-way split of the 512-token layer's longest key blocks measured
+                             // 28.3 against 24.5 us for single blocks
 };
 
 struct Entry {
-    int kind, T, G, ngrp;
+    int kind, T, G, ngrp, D;
     int njobs, rs, np, nrb;
     std::vector<unsigned short> job;
 };
@@ -101,15 +103,27 @@ std::vector<int> block_steps(int kind, int64_t TG, int T, int G, int nrb) {
     return tiles;
 }
 
-Entry make_plan(int kind, int T, int G, int ngrp) {
+Entry make_plan(int kind, int T, int G, int ngrp, int D) {
     const Kind& k = kKinds[kind];
-    Entry e{kind, T, G, ngrp, 0, 0, 1, 0, {}};
+    Entry e{kind, T, G, ngrp, D, 0, 0, 1, 0, {}};
     const int64_t TG = (int64_t)T * G;
     const int64_t nrb64 = kind == kSplitDkdv ? ((int64_t)T + 63) / 64 : (TG + k.BM - 1) / k.BM;
     e.nrb = (int)std::min<int64_t>(nrb64, INT32_MAX);
-    const int slots = kCus * k.wg;
-    // enough blocks per slot, or too many to list: the longest-first order balances by itself
-    if (nrb64 > 16383 || (int64_t)ngrp * nrb64 > (int64_t)4 * slots) return e;
+    // dK/dV at head_dim <= 64: its planned variant (two workgroups per CU) is always the one to run,
+    // with single key blocks unless a split pays
+    const bool w4 = kind == kSplitDkdv && D <= 64;
+    const int slots = kCus * (w4 ? 2 : k.wg);
+    if (nrb64 > 16383 || (w4 && nrb64 > kMaxSplitJobs)) return e;
+    auto singles = [&]() {
+        e.njobs = e.nrb;
+        e.rs = e.nrb;
+        e.np = 1;
+        e.job.clear();
+        for (int rb = e.nrb - 1; rb >= 0; --rb) e.job.push_back((unsigned short)(rb << 2));
+        return e;
+    };
+    // enough blocks per slot: the longest-first order balances by itself
+    if ((int64_t)ngrp * nrb64 > (int64_t)4 * slots) return w4 ? singles() : e;
     const std::vector<int> tiles = block_steps(kind, TG, T, G, e.nrb);
     std::vector<double> cost;
     auto eval = [&](const std::vector<Job>& j) {
@@ -134,7 +148,7 @@ Entry make_plan(int kind, int T, int G, int ngrp) {
     bool single = false;
     if (kind == kSplitDkdv) {
         const double m = eval(jobs_for(tiles, e.nrb, 1, k));
-        if (m < 0.97 * base) { ref = m; single = true; }
+        if (w4 || m < 0.97 * base) { ref = m; single = true; }
     }
     double best = ref;
     int brs = e.nrb, bnp = 1;
@@ -147,11 +161,8 @@ Entry make_plan(int kind, int T, int G, int ngrp) {
             const double m = eval(jobs_for(tiles, rs, np, k));
             if (m < best) { best = m; brs = rs; bnp = np; }
         }
-    if (bnp == 1 || best > kMinGain * ref) {  // not worth the hand-off
-        if (!single) return e;
-        brs = e.nrb;
-        bnp = 1;
-    }
+    if (bnp == 1 || best > kMinGain * ref)  // not worth the hand-off
+        return single ? singles() : e;
     const std::vector<Job> j = jobs_for(tiles, brs, bnp, k);
     e.njobs = (int)j.size();
     e.rs = brs;
@@ -165,15 +176,16 @@ std::vector<Entry>* g_cache = nullptr;
 
 }  // namespace
 
-void split_plan(int kind, int T, int G, int ngrp, SplitPlan* out) {
+void split_plan(int kind, int T, int G, int ngrp, int D, SplitPlan* out) {
+    if (kind != kSplitDkdv) D = 0;   // only the dK/dV plan depends on head_dim
     std::lock_guard<std::mutex> lk(g_mu);
     if (!g_cache) g_cache = new std::vector<Entry>();  // kept for the process (entries are small)
     const Entry* hit = nullptr;
     for (const Entry& e : *g_cache)
-        if (e.kind == kind && e.T == T && e.G == G && e.ngrp == ngrp) hit = &e;
+        if (e.kind == kind && e.T == T && e.G == G && e.ngrp == ngrp && (e.D <= 64) == (D <= 64)) hit = &e;
     if (!hit) {
         if (g_cache->size() >= 256) g_cache->erase(g_cache->begin());
-        g_cache->push_back(make_plan(kind, T, G, ngrp));
+        g_cache->push_back(make_plan(kind, T, G, ngrp, D));
         hit = &g_cache->back();
     }
     out->njobs = hit->njobs;

@@ -57,22 +57,28 @@ def amax_parts(B, T, Hkv):
 
 
 KINDS = {  # pass: rows per job, workgroups per CU, most pieces, cost per job, cost per piece
-    "fwd": (256, 1, 4, 1.0, 4.0), "dq": (128, 2, 2, 1.0, 4.0), "dkdv": (64, 1, 4, 2.0, 8.0)}
+    "fwd": (256, 1, 4, 1.0, 4.0), "dq": (128, 2, 2, 1.0, 4.0), "dkdv": (64, 1, 4, 2.0, 16.0)}
 
 
-def split_plan(kind, T, G, ngrp):
+def split_plan(kind, T, G, ngrp, D=128):
     """(rs, np) of the split of the longest causal blocks of one pass, or None.  Steps per block
     (growing with the index): forward / dQ row block rb, its causal 64-key tiles; dK/dV key block
     nkb - 1 - rb, its 64-row tiles from the diagonal on.  The greedy dispatch of the longest-first
     job list (each job to the slot that frees first) over 256 CUs x wg slots, cost = steps + per
     job + per piece of a split block; the unsplit dK/dV runs mirrored pairs.  The earliest end
-    wins if it is below 0.8 of the unsplit one."""
+    wins if it is below 0.8 of the unsplit one.  (rs, 1) with rs = nrb: single dK/dV key blocks,
+    none split.  dK/dV at D <= 64 always has a plan (two workgroups per CU; up to 1024 blocks)."""
     BM, wg, maxp, cjob, cpiece = KINDS[kind]
+    w4 = kind == "dkdv" and D <= 64
+    if w4:
+        wg = 2
     TG = T * G
     nrb = -(-T // 64) if kind == "dkdv" else -(-TG // BM)
     slots = 256 * wg
-    if nrb > 16383 or ngrp * nrb > 4 * slots:
+    if nrb > 16383 or (w4 and nrb > 1024):
         return None
+    if ngrp * nrb > 4 * slots:
+        return (nrb, 1) if w4 else None
     if kind == "dkdv":
         tiles = [-(-(TG - (nrb - 1 - rb) * 64 * G) // 64) for rb in range(nrb)]
     else:
@@ -104,7 +110,7 @@ def split_plan(kind, T, G, ngrp):
         ref = dispatch([tiles[nrb - 1 - i] + (tiles[i] + cjob if i != nrb - 1 - i else 0.0) + cjob
                         for i in range(npair)])
         m = end(nrb, 1)        # single key blocks, none split
-        if m < 0.97 * ref:
+        if w4 or m < 0.97 * ref:
             ref, single = m, True
     else:
         ref = end(nrb, 1)
@@ -129,7 +135,7 @@ def split_bytes(B, T, Hq, Hkv, D, bwd):
     G, ngrp = Hq // Hkv, B * Hkv
     regions, ncnt = [], 0
     for kind in (("dq", "dkdv") if bwd else ("fwd",)):
-        plan = split_plan(kind, T, G, ngrp)
+        plan = split_plan(kind, T, G, ngrp, D)
         n, np_ = 0, 1
         if plan is not None:
             rs, np_ = plan
@@ -157,25 +163,28 @@ def sizes(B, T, Hq, Hkv, D, esz, base=1e4):
 
 def test_split_plans_of_the_parity_shapes():
     """The GPU parity shapes meant to cover the split blocks are split: forward into 4 pieces, the
-    dQ pass into 2 (not the third shape's), dK/dV into 2-4; the benchmark's workloads keep their
-    blocks whole, one GPU's share of the 8192-token layer (one group) splits all three passes."""
+    dQ pass into 2 (not the third shape's), dK/dV into 2-4 (the third: single key blocks, the D <= 64
+    variant at two workgroups per CU); the benchmark's D = 128 workloads keep
+    their blocks whole, one GPU's share of the 8192-token layer (one group) splits all three passes;
+    at D = 64 the dK/dV pass always has a plan (single key blocks at least)."""
     shapes = [(1, 1000, 4, 1, 128), (1, 1200, 4, 2, 64), (1, 777, 2, 1, 32)]
-    fwd = [split_plan("fwd", T, Hq // Hkv, B * Hkv) for B, T, Hq, Hkv, D in shapes]
-    dq = [split_plan("dq", T, Hq // Hkv, B * Hkv) for B, T, Hq, Hkv, D in shapes]
-    kv = [split_plan("dkdv", T, Hq // Hkv, B * Hkv) for B, T, Hq, Hkv, D in shapes]
+    fwd = [split_plan("fwd", T, Hq // Hkv, B * Hkv, D) for B, T, Hq, Hkv, D in shapes]
+    dq = [split_plan("dq", T, Hq // Hkv, B * Hkv, D) for B, T, Hq, Hkv, D in shapes]
+    kv = [split_plan("dkdv", T, Hq // Hkv, B * Hkv, D) for B, T, Hq, Hkv, D in shapes]
     assert all(p is not None and p[1] == 4 for p in fwd)
     assert dq[0] is not None and dq[1] is not None and dq[2] is None
     assert all(p[1] == 2 for p in dq[:2])
-    assert all(p is not None and p[1] >= 2 for p in kv)
-    for B, T, Hq, Hkv in ((4, 2048, 12, 4), (16, 1024, 12, 12), (1, 8192, 32, 8)):
+    assert kv[0][1] >= 2 and kv[1][1] >= 2 and kv[2] == (-(-777 // 64), 1)   # the third: single blocks
+    for B, T, Hq, Hkv in ((4, 2048, 12, 4), (1, 8192, 32, 8)):
         for kind in KINDS:
-            assert split_plan(kind, T, Hq // Hkv, B * Hkv) is None, (kind, T)
-    # the 512-token layer: its 128 mirrored pairs of key blocks fill half the CUs; single key
-    # blocks, none split, fill them all
-    assert split_plan("fwd", 512, 3, 32) is None and split_plan("dq", 512, 3, 32) is None
-    assert split_plan("dkdv", 512, 3, 32) == (8, 1)
+            assert split_plan(kind, T, Hq // Hkv, B * Hkv, 128) is None, (kind, T)
+    # D = 64 layers: forward and dQ keep their blocks; dK/dV runs single key blocks
+    for B, T, Hq, Hkv in ((8, 512, 12, 4), (16, 1024, 12, 12)):
+        assert split_plan("fwd", T, Hq // Hkv, B * Hkv, 64) is None
+        assert split_plan("dq", T, Hq // Hkv, B * Hkv, 64) is None
+        assert split_plan("dkdv", T, Hq // Hkv, B * Hkv, 64) == (-(-T // 64), 1)
     for kind in KINDS:
-        assert split_plan(kind, 8192, 4, 1)[1] > 1
+        assert split_plan(kind, 8192, 4, 1, 128)[1] > 1
 
 
 def wsb(L, is_bwd, B, T, Hq, Hkv, D, base=1e4, dt=binding.NE_BF16, flags=0):

@@ -129,10 +129,11 @@ def test_parity_small(shape, dtypes, base):
     parity(q, k, v, dO, base, out_dt, in_dt)
 
 
-# One or two (batch, KV head) groups: the launch is short of row blocks, so the forward cuts its
-# longest 256-row blocks into 4 key ranges and the dQ pass its longest 128-row blocks into 2 (the
-# third: forward only), each block finished by the last of its workgroups (the plans are checked
-# on the CPU in test_abi_host.test_split_plans_of_the_parity_shapes).
+# One or two (batch, KV head) groups: the launch is short of blocks, so the forward cuts its
+# longest 256-row blocks into 4 key ranges, the dQ pass its longest 128-row blocks into 2 and the
+# dK/dV pass its longest key blocks' rows into 4 (the third shape: forward only; its dK/dV runs
+# single key blocks), each block finished by the last of its workgroups (the plans are checked on
+# the CPU in test_abi_host.test_split_plans_of_the_parity_shapes).
 SPLIT_SHAPES = [(1, 1000, 4, 1, 128), (1, 1200, 4, 2, 64), (1, 777, 2, 1, 32)]
 
 

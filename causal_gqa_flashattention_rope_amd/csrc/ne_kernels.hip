@@ -90,10 +90,11 @@ __device__ __forceinline__ void load8(const T16* p, float (&x)[8]) {
 }
 
 // Partial maxima of |dO| for the per-group scale of dO (16-bit operands).  grid (nparts, B), 256
-// threads: block (p, b) reads tokens [p tpp, (p + 1) tpp) of batch b, all Hq heads (contiguous
-// rows), and writes the max of each of its KV groups to part[(b Hkv + g) nparts + p].  Groups are
-// reduced in LDS (max of non-negative floats = max of their bit patterns as unsigned), up to
-// kAmaxGroups per block; more groups are covered in passes over the rows.
+// threads: block (p, b) reads tokens [p tpp, (p + 1) tpp) of batch b, all Hq heads (a token's rows
+// are contiguous), and writes the max of each of its KV groups to part[(b Hkv + g) nparts + p].
+// Each thread owns fixed 16-byte chunks of a token's rows (so a fixed group) and walks the block's
+// tokens with a running max, several loads in flight; groups are then reduced in LDS (max of
+// non-negative floats = max of their bit patterns as unsigned), kAmaxGroups per pass.
 constexpr int kAmaxGroups = 256;
 template <typename TI, int D>
 __global__ __launch_bounds__(256) void dO_amax_kernel(AmaxArgs a) {
@@ -102,22 +103,33 @@ __global__ __launch_bounds__(256) void dO_amax_kernel(AmaxArgs a) {
     const int p = blockIdx.x, b = blockIdx.y;
     const int G = a.Hq / a.Hkv;
     const int t0 = p * a.tpp, t1 = min(a.T, t0 + a.tpp);
-    const int rows = max(0, t1 - t0) * a.Hq;                      // (token, head) rows, contiguous
-    const TI* base = (const TI*)a.dO + ((size_t)b * a.T + t0) * a.Hq * D;
+    const int rowlen = a.Hq * CPR;                               // 16-byte chunks per token
+    const size_t tok = (size_t)a.Hq * D;                         // elements per token
+    // rowlen < 256: 256 / rowlen sets of threads take every sets-th token; else one set
+    const int sets = rowlen < 256 ? 256 / rowlen : 1;
+    const int set = rowlen < 256 ? (int)threadIdx.x / rowlen : 0;
+    const int q0 = rowlen < 256 ? (int)threadIdx.x % rowlen : (int)threadIdx.x;
+    const TI* base = (const TI*)a.dO + ((size_t)b * a.T + t0) * tok;
     for (int g0 = 0; g0 < a.Hkv; g0 += kAmaxGroups) {
         const int ng = min(kAmaxGroups, a.Hkv - g0);
         for (int i = threadIdx.x; i < ng; i += 256) smax[i] = 0u;
         __syncthreads();
-        for (int idx = threadIdx.x; idx < rows * CPR; idx += 256) {
-            const int r = idx / CPR, g = (r % a.Hq) / G - g0;
-            if (g < 0 || g >= ng) continue;
-            float x[8];
-            load8(base + (size_t)r * D + (idx % CPR) * 8, x);
-            float m = 0.f;
+        if (set < sets) {
+            for (int q = q0; q < rowlen; q += 256) {
+                const int g = (q / CPR) / G - g0;
+                if (g < 0 || g >= ng) continue;
+                const TI* src = base + (size_t)set * tok + (size_t)q * 8;
+                float m = 0.f;
+#pragma unroll 4
+                for (int t = t0 + set; t < t1; t += sets, src += (size_t)sets * tok) {
+                    float x[8];
+                    load8(src, x);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
-            // (fmaxf skips a NaN element here; it still reaches the gradients through dO itself)
-            atomicMax(&smax[g], __float_as_uint(m));
+                    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+                }
+                // (fmaxf skips a NaN element here; it still reaches the gradients through dO itself)
+                atomicMax(&smax[g], __float_as_uint(m));
+            }
         }
         __syncthreads();
         for (int i = threadIdx.x; i < ng; i += 256)

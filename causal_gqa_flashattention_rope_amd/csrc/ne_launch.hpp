@@ -87,7 +87,8 @@ struct SplitPlan {
 };
 // The host's plan of one pass: fills njobs, rs, np, nrb and job (not part and cnt).  It depends
 // only on the causal step counts of the blocks (no window), the number of groups and the
-// workgroups the chip runs at once (256 CUs).  Forward: 256-row blocks, up to 4 pieces; dQ:
+// workgroups the chip runs at once (256 CUs).  Forward: 256-row blocks (128 rows, three workgroups
+// per CU at head_dim <= 64), up to 4 pieces; dQ:
 // 128-row blocks (two workgroups per CU), 2 pieces; dK/dV: 64-key blocks, up to 4 pieces, job
 // index rb meaning key block nkb - 1 - rb -- a dK/dV plan replaces the mirrored pairs, and may
 // split nothing (rs = nrb, np = 1: single blocks longest-first fill the CUs the pairs leave idle).
@@ -95,9 +96,10 @@ struct SplitPlan {
 // runs two workgroups per CU.
 enum { kSplitFwd = 0, kSplitDq = 1, kSplitDkdv = 2 };
 void split_plan(int kind, int T, int G, int ngrp, int D, SplitPlan* out);
-// floats of the partial-result slot of one piece (forward: O, m and l of 8 waves; dQ: 4 waves;
+// floats of the partial-result slot of one piece (forward: O, m and l of its 8 waves, 4 at
+// head_dim <= 64; dQ: 4 waves;
 // dK/dV: the 4 waves that hold the block's dV^T and dK^T after the row halves are added)
-inline size_t split_slot_floats_fwd(int D) { return (size_t)8 * 64 * (D / 2 + 2); }
+inline size_t split_slot_floats_fwd(int D) { return (size_t)(D <= 64 ? 4 : 8) * 64 * (D / 2 + 2); }
 inline size_t split_slot_floats_dq(int D) { return (size_t)4 * 64 * (D / 2); }
 inline size_t split_slot_floats_dkdv(int D) { return (size_t)4 * 64 * (D / 2); }
 

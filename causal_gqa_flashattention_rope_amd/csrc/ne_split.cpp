@@ -88,14 +88,13 @@ std::vector<Job> jobs_for(const std::vector<int>& tiles, int rs, int np, const K
 
 // Steps of each block, indexed so that they grow with the index: forward and dQ, row block rb
 // (its causal keys); dK/dV, key block nkb - 1 - rb (its rows from the diagonal on).
-std::vector<int> block_steps(int kind, int64_t TG, int T, int G, int nrb) {
+std::vector<int> block_steps(int kind, int BM, int64_t TG, int T, int G, int nrb) {
     std::vector<int> tiles(nrb);
     for (int rb = 0; rb < nrb; ++rb) {
         if (kind == kSplitDkdv) {
             const int64_t kb = nrb - 1 - rb;
             tiles[rb] = (int)((TG - kb * 64 * G + 63) / 64);
         } else {
-            const int BM = kKinds[kind].BM;
             tiles[rb] = (int)(std::min<int64_t>((int64_t)rb * BM + BM - 1, TG - 1) / G / 64 + 1);
         }
     }
@@ -104,7 +103,8 @@ std::vector<int> block_steps(int kind, int64_t TG, int T, int G, int nrb) {
 }
 
 Entry make_plan(int kind, int T, int G, int ngrp, int D) {
-    const Kind& k = kKinds[kind];
+    Kind k = kKinds[kind];
+    if (kind == kSplitFwd && D <= 64) { k.BM = 128; k.wg = 3; }   // the forward's D <= 64 variant
     Entry e{kind, T, G, ngrp, D, 0, 0, 1, 0, {}};
     const int64_t TG = (int64_t)T * G;
     const int64_t nrb64 = kind == kSplitDkdv ? ((int64_t)T + 63) / 64 : (TG + k.BM - 1) / k.BM;
@@ -124,7 +124,7 @@ Entry make_plan(int kind, int T, int G, int ngrp, int D) {
     };
     // enough blocks per slot: the longest-first order balances by itself
     if ((int64_t)ngrp * nrb64 > (int64_t)4 * slots) return w4 ? singles() : e;
-    const std::vector<int> tiles = block_steps(kind, TG, T, G, e.nrb);
+    const std::vector<int> tiles = block_steps(kind, k.BM, TG, T, G, e.nrb);
     std::vector<double> cost;
     auto eval = [&](const std::vector<Job>& j) {
         cost.clear();
@@ -177,7 +177,7 @@ std::vector<Entry>* g_cache = nullptr;
 }  // namespace
 
 void split_plan(int kind, int T, int G, int ngrp, int D, SplitPlan* out) {
-    if (kind != kSplitDkdv) D = 0;   // only the dK/dV plan depends on head_dim
+    if (kind == kSplitDq) D = 0;   // the forward and dK/dV plans depend on head_dim (<= 64 or not)
     std::lock_guard<std::mutex> lk(g_mu);
     if (!g_cache) g_cache = new std::vector<Entry>();  // kept for the process (entries are small)
     const Entry* hit = nullptr;

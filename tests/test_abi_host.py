@@ -67,11 +67,14 @@ def split_plan(kind, T, G, ngrp, D=128):
     job list (each job to the slot that frees first) over 256 CUs x wg slots, cost = steps + per
     job + per piece of a split block; the unsplit dK/dV runs mirrored pairs.  The earliest end
     wins if it is below 0.8 of the unsplit one.  (rs, 1) with rs = nrb: single dK/dV key blocks,
-    none split.  dK/dV at D <= 64 always has a plan (two workgroups per CU; up to 1024 blocks)."""
+    none split.  dK/dV at D <= 64 always has a plan (two workgroups per CU; up to 1024 blocks); the
+    forward at D <= 64 has 128-row blocks, three workgroups per CU."""
     BM, wg, maxp, cjob, cpiece = KINDS[kind]
     w4 = kind == "dkdv" and D <= 64
     if w4:
         wg = 2
+    if kind == "fwd" and D <= 64:      # the forward's D <= 64 variant: 128 rows, 3 workgroups per CU
+        BM, wg = 128, 3
     TG = T * G
     nrb = -(-T // 64) if kind == "dkdv" else -(-TG // BM)
     slots = 256 * wg
@@ -139,9 +142,10 @@ def split_bytes(B, T, Hq, Hkv, D, bwd):
         n, np_ = 0, 1
         if plan is not None:
             rs, np_ = plan
-            nrb = -(-T // 64) if kind == "dkdv" else -(-T * G // KINDS[kind][0])
+            BM = 128 if kind == "fwd" and D <= 64 else KINDS[kind][0]
+            nrb = -(-T // 64) if kind == "dkdv" else -(-T * G // BM)
             n = ngrp * (nrb - rs)
-        slot = 8 * 64 * (D // 2 + 2) if kind == "fwd" else 4 * 64 * (D // 2)
+        slot = (4 if D <= 64 else 8) * 64 * (D // 2 + 2) if kind == "fwd" else 4 * 64 * (D // 2)
         regions.append(up(n * np_ * slot * 4))
         ncnt += 2 * n
     return sum(regions) + up(ncnt * 4)

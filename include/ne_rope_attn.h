@@ -35,8 +35,10 @@
  * call's (T, head_dim, rope_base): the kernels detect it on the device and make the outputs NaN
  * (ne_rope_table_init, ne_rope_table_check).
  *
- * Thread safety: calls are re-entrant; the only mutable library state is the thread-local error
- * message.  Two calls that share a workspace must be ordered on one stream.
+ * Thread safety: calls are re-entrant.  Mutable library state: the thread-local error message, a
+ * host cache of the split plans (one per shape, behind a mutex; a plan depends only on the shape)
+ * and the device scratch of ne_rope_attn_decode_noalloc.  Two calls that share a workspace must be
+ * ordered on one stream.
  */
 #ifndef NE_ROPE_ATTN_H
 #define NE_ROPE_ATTN_H

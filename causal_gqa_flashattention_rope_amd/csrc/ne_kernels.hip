@@ -9,21 +9,26 @@
 //    query/key/value staged in on-chip shared memory; each separate pass such as RoPE costs a
 //    launch and memory traffic, which is why RoPE is folded into the operand preparation here).
 //
-// Pipeline of one call (all stream-ordered, no host synchronisation):
-//  forward : prep  -> k' = fp16(R(k)) rows, v' = fp16(v) transposed (16-bit operands), cos/sin
-//                     table (workspace)
-//            fwd   -> per 256 (16-bit operands; 128 for fp32) flattened (token, head) rows of one
-//                     KV group: q~ = fp16(R(q) * scale * log2 e) in registers, online softmax over
-//                     64-key tiles staged once in LDS for all query heads of the group; o, lse.
-//  backward: prep  -> q~, k', v', dO' and Delta = rowsum(dO * o), lse2 = lse * log2 e, cos/sin table
-//            dkdv  -> per pair of mirrored 64-key blocks of one KV head: dK, dV accumulated over
-//                     every query row of the group (all G heads), written once; inverse RoPE in
-//                     the epilogue; the fp16 dS of every 64 x 64 tile stored in the workspace.
-//            dq    -> per 256 flattened rows: dQ = dS K over the stored tiles of the visible key
-//                     blocks, written once; inverse RoPE in the epilogue.  (Per batch of (batch,
-//                     KV head) groups whose dS fits the buffer; when one group's dS does not, dq
-//                     recomputes S and dP per 128 rows instead.)  No atomics: bit-reproducible.
-//
+// The RoPE table (cos/sin of every position, built once per workspace by rope_table_kernel) is
+// read by every call.  Pipeline of one call (all stream-ordered, no host synchronisation):
+//  forward : prep  -> k' = fp16(R(k)) rows, v' = fp16(v) transposed (16-bit operands).
+//            fwd   -> per 256 flattened (token, head) rows of one KV group (128 at head_dim <= 64
+//                     and on the fp32 path): q~ = fp16(R(q) * scale * log2 e) in registers, online
+//                     softmax over 64-key tiles staged once in LDS for all query heads of the
+//                     group; o, lse.
+//  backward: max   -> the largest |dO| of each (batch, KV head) group (its fp16 scale).
+//            prep  -> q~, k', v', dO' = fp16(s dO) and Delta = s rowsum(dO * o), lse2 = lse log2 e.
+//            dkdv  -> per pair of mirrored 64-key blocks of one KV head (or, under a plan, per key
+//                     block or piece of one): dK, dV accumulated over every query row of the group
+//                     (all G heads), written once; inverse RoPE in the epilogue.
+//            dq    -> per 128 flattened rows: recomputes S and dP and adds dS K, written once;
+//                     inverse RoPE in the epilogue.  No atomics: bit-reproducible.
+//          (opt-in: the dK/dV pass stores the fp16 dS tiles and dq_ds_kernel reads them; or it
+//           adds dQ with atomics into an fp32 accumulator, converted by dq_acc_convert_kernel.)
+// A plan made on the host (ne_split.cpp) may cut the longest causal blocks of a launch with few
+// blocks per CU over several workgroups; the last of them combines the partial results in a fixed
+// order.
+
 // Flattened rows: within a (batch, KV head) group the G query heads are interleaved with the
 // tokens, row R = t * G + hh (hh = head within the group).  In the [B][T][Hq][D] input these
 // rows are exactly the memory order of one token's heads, and the causal mask depends only on
@@ -1264,7 +1269,8 @@ void dkdv_kernel(BwdArgs a) {
 // products: the A operand carries three fp16 terms of -lse2 (or -Delta) of the lane's row
 // (fold_frag) against B = (256, 1, 1), so the accumulators come out as S - lse2 and
 // dP - Delta with fp32 accuracy and no per-element subtraction.  Row tiles go through a 4-stage
-// ring filled two steps ahead.
+// ring filled two steps ahead.  SPLIT: a host plan replaces the pairs with single key blocks,
+// longest first, or with pieces of a key block's row tiles whose sums the last piece combines.
 // =====================================================================================
 // MODE 0: dQ is a separate pass; 1: also store dS for the dQ pass (DS); 2: atomic dQ (AT) -- the
 // role-1 waves leave dS^T of each tile in LDS, and one step later the role-0 waves multiply it by

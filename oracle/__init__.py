@@ -35,11 +35,11 @@ def _bind(path):
     lib.ne_oracle_bwd_given_o_w.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, ctypes.c_double, i, i]
     lib.ne_oracle_bwd_given_o_w.restype = i
     d = ctypes.c_double
-    lib.ne_oracle_fwd_x.argtypes = [P, P, P, P, P, i, i, i, i, i, d, i, i, d, d, i]
+    lib.ne_oracle_fwd_x.argtypes = [P, P, P, P, P, i, i, i, i, i, d, i, i, d, d, i, i]
     lib.ne_oracle_fwd_x.restype = i
-    lib.ne_oracle_bwd_x.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, d, i, i, d, d, i]
+    lib.ne_oracle_bwd_x.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, d, i, i, d, d, i, i]
     lib.ne_oracle_bwd_x.restype = i
-    lib.ne_oracle_rope.argtypes = [P, P, i, i, i, i, ctypes.c_double, i]
+    lib.ne_oracle_rope.argtypes = [P, P, i, i, i, i, ctypes.c_double, i, i]
     lib.ne_oracle_rope.restype = i
     lib.ne_oracle_max_threads.argtypes = []
     lib.ne_oracle_max_threads.restype = i
@@ -96,21 +96,22 @@ def _qk(qk_norm):
     return 1, float(gain), float(eps)
 
 
-def fwd(q, k, v, rope_base, nthreads=0, window=0, qk_norm=None):
+def fwd(q, k, v, rope_base, nthreads=0, window=0, qk_norm=None, half_split=False):
     """Return (o, lse) in float64.  window W > 0: query i sees keys i-W+1 .. i.
-    qk_norm (gain, eps): every row of q and k becomes gain * x / sqrt(mean(x^2) + eps) first."""
+    qk_norm (gain, eps): every row of q and k becomes gain * x / sqrt(mean(x^2) + eps) first.
+    half_split: the rotation pairs element i with element i + D/2 instead of (2i, 2i+1)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, Hq, Hkv, D = _dims(q, k)
     o = np.empty_like(q)
     lse = np.empty((B, Hq, T), dtype=np.float64)
     rc = _load().ne_oracle_fwd_x(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D,
-                                 float(rope_base), int(window), *_qk(qk_norm), int(nthreads))
+                                 float(rope_base), int(window), *_qk(qk_norm), int(bool(half_split)), int(nthreads))
     if rc:
         raise ValueError(f"ne_oracle_fwd rejected the arguments (rc={rc})")
     return o, lse
 
 
-def _bwd(q, k, v, o, dO, rope_base, nthreads, window, qk_norm):
+def _bwd(q, k, v, o, dO, rope_base, nthreads, window, qk_norm, half_split):
     q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
     B, T, Hq, Hkv, D = _dims(q, k)
     dq = np.empty_like(q)
@@ -121,28 +122,30 @@ def _bwd(q, k, v, o, dO, rope_base, nthreads, window, qk_norm):
         o = _f64(o)
         optr = _ptr(o)
     rc = _load().ne_oracle_bwd_x(_ptr(q), _ptr(k), _ptr(v), optr, _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
-                                 B, T, Hq, Hkv, D, float(rope_base), int(window), *_qk(qk_norm), int(nthreads))
+                                 B, T, Hq, Hkv, D, float(rope_base), int(window), *_qk(qk_norm), int(bool(half_split)),
+                                 int(nthreads))
     if rc:
         raise ValueError(f"ne_oracle_bwd rejected the arguments (rc={rc})")
     return dq, dk, dv
 
 
-def bwd(q, k, v, dO, rope_base, nthreads=0, window=0, qk_norm=None):
+def bwd(q, k, v, dO, rope_base, nthreads=0, window=0, qk_norm=None, half_split=False):
     """Return (dq, dk, dv) in float64: the exact gradients of sum(o * dO)."""
-    return _bwd(q, k, v, None, dO, rope_base, nthreads, window, qk_norm)
+    return _bwd(q, k, v, None, dO, rope_base, nthreads, window, qk_norm, half_split)
 
 
-def bwd_given_o(q, k, v, o, dO, rope_base, nthreads=0, window=0, qk_norm=None):
+def bwd_given_o(q, k, v, o, dO, rope_base, nthreads=0, window=0, qk_norm=None, half_split=False):
     """(dq, dk, dv) with Delta = rowsum(dO * o) from the given o (e.g. o stored in bf16)."""
-    return _bwd(q, k, v, o, dO, rope_base, nthreads, window, qk_norm)
+    return _bwd(q, k, v, o, dO, rope_base, nthreads, window, qk_norm, half_split)
 
 
-def rope(x, rope_base, inverse=False):
-    """Rotate x [B,T,H,D] by R_t (or R_t^T when inverse)."""
+def rope(x, rope_base, inverse=False, half_split=False):
+    """Rotate x [B,T,H,D] by R_t (or R_t^T when inverse); half_split: pairs (i, i + D/2)."""
     x = _f64(x)
     B, T, H, D = x.shape
     y = np.empty_like(x)
-    rc = _load().ne_oracle_rope(_ptr(x), _ptr(y), B, T, H, D, float(rope_base), int(bool(inverse)))
+    rc = _load().ne_oracle_rope(_ptr(x), _ptr(y), B, T, H, D, float(rope_base), int(bool(inverse)),
+                                int(bool(half_split)))
     if rc:
         raise ValueError("ne_oracle_rope rejected the arguments")
     return y

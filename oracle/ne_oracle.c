@@ -36,6 +36,9 @@
  *   returned with respect to the un-rotated q and k (inverse rotation R^T).
  *   A window of W > 0 keys means query i sees keys i - W + 1 .. i (its own position
  *   and the W - 1 before it); W <= 0 is the full causal prefix.
+ *   The *_x entry points and ne_oracle_rope also take the other common pairing, the
+ *   "half-split" one: element i is rotated with element i + D/2 by t*theta_i (same
+ *   frequencies, same positions), i = 0..D/2-1.
  *
  * Layouts: q, o, dO, dq are [B][T][Hq][D]; k, v, dk, dv are [B][T][Hkv][D];
  * lse is [B][Hq][T].  All arrays are dense row-major doubles owned by the caller.
@@ -79,9 +82,10 @@ static void set_threads(int nthreads) {
 
 /* Rotate one head's rows: y[t][:] = R_t x[t][:] (sign = +1) or R_t^T x[t][:]
  * (sign = -1).  x and y are [T][D] with row stride `stride` doubles.  With
- * base <= 0 the rotation is the identity.  cos/sin come from libm in double. */
+ * base <= 0 the rotation is the identity.  cos/sin come from libm in double.
+ * Rotary pair i is (2i, 2i+1), or (i, i + D/2) when half != 0. */
 static void rope_rows(const double* x, size_t xstride, double* y, size_t ystride,
-                      int T, int D, double base, int sign) {
+                      int T, int D, double base, int sign, int half) {
     for (int t = 0; t < T; ++t) {
         const double* xr = x + (size_t)t * xstride;
         double* yr = y + (size_t)t * ystride;
@@ -93,23 +97,25 @@ static void rope_rows(const double* x, size_t xstride, double* y, size_t ystride
             double theta = pow(base, -2.0 * (double)i / (double)D);
             double phi = (double)t * theta;
             double c = cos(phi), s = sin(phi) * (double)sign;
-            double a = xr[2 * i], b = xr[2 * i + 1];
-            yr[2 * i] = a * c - b * s;
-            yr[2 * i + 1] = a * s + b * c;
+            const int i0 = half ? i : 2 * i, i1 = half ? i + D / 2 : 2 * i + 1;
+            double a = xr[i0], b = xr[i1];
+            yr[i0] = a * c - b * s;
+            yr[i1] = a * s + b * c;
         }
     }
 }
 
 /* Public helper so the tests can check the rotation on its own:
- * y = R x (inverse = 0) or y = R^T x (inverse = 1), x and y [B][T][H][D]. */
+ * y = R x (inverse = 0) or y = R^T x (inverse = 1), x and y [B][T][H][D];
+ * half_split selects the pairing (i, i + D/2). */
 int ne_oracle_rope(const double* x, double* y, int B, int T, int H, int D,
-                   double base, int inverse) {
+                   double base, int inverse, int half_split) {
     if (B < 1 || T < 1 || H < 1 || D < 1 || (base > 0.0 && D % 2)) return 1;
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < H; ++h)
             rope_rows(x + IDX4(b, 0, h, 0, T, H, D), (size_t)H * D,
                       y + IDX4(b, 0, h, 0, T, H, D), (size_t)H * D, T, D, base,
-                      inverse ? -1 : 1);
+                      inverse ? -1 : 1, half_split);
     return 0;
 }
 
@@ -146,9 +152,9 @@ static void softmax_probs(const double* qr, const double* kr, double* P,
 
 /* Forward: o = softmax(mask(q' k'^T / sqrt(D))) v, lse as above; window W as in
  * the header (W <= 0: full causal prefix). */
-int ne_oracle_fwd_w(const double* q, const double* k, const double* v, double* o,
+static int fwd_impl(const double* q, const double* k, const double* v, double* o,
                     double* lse, int B, int T, int Hq, int Hkv, int D, double base,
-                    int window, int nthreads) {
+                    int window, int half, int nthreads) {
     if (check_shape(B, T, Hq, Hkv, D, base)) return 1;
     set_threads(nthreads);
     const int G = Hq / Hkv;
@@ -159,8 +165,8 @@ int ne_oracle_fwd_w(const double* q, const double* k, const double* v, double* o
     for (int b = 0; b < B; ++b) {
         for (int h = 0; h < Hq; ++h) {
             const int g = h / G;  /* GQA: KV head shared by G consecutive query heads */
-            rope_rows(q + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, qr, (size_t)D, T, D, base, 1);
-            rope_rows(k + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, kr, (size_t)D, T, D, base, 1);
+            rope_rows(q + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, qr, (size_t)D, T, D, base, 1, half);
+            rope_rows(k + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, kr, (size_t)D, T, D, base, 1, half);
             softmax_probs(qr, kr, P, lse + ((size_t)b * Hq + h) * T, T, D, window);
 #pragma omp parallel for schedule(static)
             for (int i = 0; i < T; ++i) {
@@ -178,6 +184,12 @@ int ne_oracle_fwd_w(const double* q, const double* k, const double* v, double* o
     return 0;
 }
 
+int ne_oracle_fwd_w(const double* q, const double* k, const double* v, double* o,
+                    double* lse, int B, int T, int Hq, int Hkv, int D, double base,
+                    int window, int nthreads) {
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, D, base, window, 0, nthreads);
+}
+
 int ne_oracle_fwd(const double* q, const double* k, const double* v, double* o,
                   double* lse, int B, int T, int Hq, int Hkv, int D, double base,
                   int nthreads) {
@@ -193,18 +205,18 @@ int ne_oracle_fwd(const double* q, const double* k, const double* v, double* o,
  * The heads of a group are accumulated in ascending order. */
 static int bwd_impl(const double* q, const double* k, const double* v, const double* dO,
                     const double* o_given, double* dq, double* dk, double* dv, int B, int T,
-                    int Hq, int Hkv, int D, double base, int window, int nthreads);
+                    int Hq, int Hkv, int D, double base, int window, int half, int nthreads);
 
 int ne_oracle_bwd(const double* q, const double* k, const double* v, const double* dO,
                   double* dq, double* dk, double* dv, int B, int T, int Hq, int Hkv,
                   int D, double base, int nthreads) {
-    return bwd_impl(q, k, v, dO, NULL, dq, dk, dv, B, T, Hq, Hkv, D, base, 0, nthreads);
+    return bwd_impl(q, k, v, dO, NULL, dq, dk, dv, B, T, Hq, Hkv, D, base, 0, 0, nthreads);
 }
 
 int ne_oracle_bwd_w(const double* q, const double* k, const double* v, const double* dO,
                     double* dq, double* dk, double* dv, int B, int T, int Hq, int Hkv,
                     int D, double base, int window, int nthreads) {
-    return bwd_impl(q, k, v, dO, NULL, dq, dk, dv, B, T, Hq, Hkv, D, base, window, nthreads);
+    return bwd_impl(q, k, v, dO, NULL, dq, dk, dv, B, T, Hq, Hkv, D, base, window, 0, nthreads);
 }
 
 /* The same backward with Delta_i = dO_i . o_i taken from a caller-supplied o ([B][T][Hq][D])
@@ -214,19 +226,19 @@ int ne_oracle_bwd_given_o(const double* q, const double* k, const double* v, con
                           const double* dO, double* dq, double* dk, double* dv, int B, int T,
                           int Hq, int Hkv, int D, double base, int nthreads) {
     if (!o) return 1;
-    return bwd_impl(q, k, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, 0, nthreads);
+    return bwd_impl(q, k, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, 0, 0, nthreads);
 }
 
 int ne_oracle_bwd_given_o_w(const double* q, const double* k, const double* v, const double* o,
                             const double* dO, double* dq, double* dk, double* dv, int B, int T,
                             int Hq, int Hkv, int D, double base, int window, int nthreads) {
     if (!o) return 1;
-    return bwd_impl(q, k, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, window, nthreads);
+    return bwd_impl(q, k, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, window, 0, nthreads);
 }
 
 static int bwd_impl(const double* q, const double* k, const double* v, const double* dO,
                     const double* o_given, double* dq, double* dk, double* dv, int B, int T,
-                    int Hq, int Hkv, int D, double base, int window, int nthreads) {
+                    int Hq, int Hkv, int D, double base, int window, int half, int nthreads) {
     if (check_shape(B, T, Hq, Hkv, D, base)) return 1;
     set_threads(nthreads);
     const int G = Hq / Hkv;
@@ -248,11 +260,11 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
     }
     for (int b = 0; b < B; ++b) {
         for (int g = 0; g < Hkv; ++g) {
-            rope_rows(k + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, kr, (size_t)D, T, D, base, 1);
+            rope_rows(k + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, kr, (size_t)D, T, D, base, 1, half);
             memset(dkr, 0, sizeof(double) * (size_t)T * D);
             memset(dvg, 0, sizeof(double) * (size_t)T * D);
             for (int h = g * G; h < (g + 1) * G; ++h) {
-                rope_rows(q + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, qr, (size_t)D, T, D, base, 1);
+                rope_rows(q + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, qr, (size_t)D, T, D, base, 1, half);
                 softmax_probs(qr, kr, P, lse_row, T, D, window);
 #pragma omp parallel for schedule(dynamic, 8)
                 for (int i = 0; i < T; ++i) {
@@ -288,7 +300,7 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
                     for (int d = 0; d < D; ++d) dqi[d] *= scale;
                 }
                 /* dq = R^T dq' for this head */
-                rope_rows(dqr, (size_t)D, dq + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, T, D, base, -1);
+                rope_rows(dqr, (size_t)D, dq + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, T, D, base, -1, half);
                 /* column sums over the query rows that see key j, one thread per key row j */
 #pragma omp parallel for schedule(dynamic, 8)
                 for (int j = 0; j < T; ++j) {
@@ -307,7 +319,7 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
                     }
                 }
             }
-            rope_rows(dkr, (size_t)D, dk + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, T, D, base, -1);
+            rope_rows(dkr, (size_t)D, dk + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, T, D, base, -1, half);
             for (int t = 0; t < T; ++t)
                 memcpy(dv + IDX4(b, t, g, 0, T, Hkv, D), dvg + (size_t)t * D, sizeof(double) * D);
         }
@@ -361,29 +373,32 @@ static int qk_norm_copies(const double* q, const double* k, double** qh, double*
     return 0;
 }
 
-/* Forward with every option: window as in the header, qk_norm != 0 applies the QK norm. */
+/* Forward with every option: window as in the header, qk_norm != 0 applies the QK norm,
+ * half_split != 0 pairs element i with element i + D/2 in the rotation. */
 int ne_oracle_fwd_x(const double* q, const double* k, const double* v, double* o, double* lse,
                     int B, int T, int Hq, int Hkv, int D, double base, int window, int qk_norm,
-                    double gain, double eps, int nthreads) {
+                    double gain, double eps, int half_split, int nthreads) {
     if (check_shape(B, T, Hq, Hkv, D, base) || (qk_norm && !(eps >= 0.0))) return 1;
-    if (!qk_norm) return ne_oracle_fwd_w(q, k, v, o, lse, B, T, Hq, Hkv, D, base, window, nthreads);
+    if (!qk_norm) return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, D, base, window, half_split, nthreads);
     double *qh, *kh;
     if (qk_norm_copies(q, k, &qh, &kh, B, T, Hq, Hkv, D, gain, eps)) return 2;
-    const int rc = ne_oracle_fwd_w(qh, kh, v, o, lse, B, T, Hq, Hkv, D, base, window, nthreads);
+    const int rc = fwd_impl(qh, kh, v, o, lse, B, T, Hq, Hkv, D, base, window, half_split, nthreads);
     free(qh); free(kh);
     return rc;
 }
 
-/* Backward with every option; o may be NULL (exact Delta) or the o to take Delta from. */
+/* Backward with every option; o may be NULL (exact Delta) or the o to take Delta from;
+ * half_split as in ne_oracle_fwd_x. */
 int ne_oracle_bwd_x(const double* q, const double* k, const double* v, const double* o,
                     const double* dO, double* dq, double* dk, double* dv, int B, int T, int Hq,
                     int Hkv, int D, double base, int window, int qk_norm, double gain, double eps,
-                    int nthreads) {
+                    int half_split, int nthreads) {
     if (check_shape(B, T, Hq, Hkv, D, base) || (qk_norm && !(eps >= 0.0))) return 1;
-    if (!qk_norm) return bwd_impl(q, k, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, window, nthreads);
+    if (!qk_norm)
+        return bwd_impl(q, k, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, window, half_split, nthreads);
     double *qh, *kh;
     if (qk_norm_copies(q, k, &qh, &kh, B, T, Hq, Hkv, D, gain, eps)) return 2;
-    const int rc = bwd_impl(qh, kh, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, window, nthreads);
+    const int rc = bwd_impl(qh, kh, v, dO, o, dq, dk, dv, B, T, Hq, Hkv, D, base, window, half_split, nthreads);
     free(qh); free(kh);
     if (rc) return rc;
     qk_norm_rows_bwd(q, dq, (size_t)B * T * Hq, D, gain, eps);

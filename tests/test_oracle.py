@@ -181,8 +181,8 @@ def test_no_rope_mha_equals_sdpa():
 # Central finite differences on the oracle's own forward, in double precision, as the
 # pages' gradient check does (pass bar there: max rel err < 1e-2; ours is 1e-6).
 # --------------------------------------------------------------------------------------
-def fd_check(q, k, v, dO, base, entries=None, h=1e-5):
-    dq, dk, dv = oracle.bwd(q, k, v, dO, base)
+def fd_check(q, k, v, dO, base, entries=None, h=1e-5, half_split=False):
+    dq, dk, dv = oracle.bwd(q, k, v, dO, base, half_split=half_split)
     analytic = [dq, dk, dv]
     worst = 0.0
     for which in range(3):
@@ -195,9 +195,9 @@ def fd_check(q, k, v, dO, base, entries=None, h=1e-5):
             x0 = arrs[which][idx]
             step = h * max(1.0, abs(x0))
             arrs[which][idx] = x0 + step
-            lp = float(np.sum(oracle.fwd(*arrs, base)[0] * dO))
+            lp = float(np.sum(oracle.fwd(*arrs, base, half_split=half_split)[0] * dO))
             arrs[which][idx] = x0 - step
-            lm = float(np.sum(oracle.fwd(*arrs, base)[0] * dO))
+            lm = float(np.sum(oracle.fwd(*arrs, base, half_split=half_split)[0] * dO))
             arrs[which][idx] = x0
             num[n] = (lp - lm) / (2 * step)
             ana[n] = a[idx]
@@ -385,6 +385,70 @@ def test_rope_scores_depend_only_on_relative_position():
         for n in range(T):
             ref = np.sum((np.conj(ac) * bc * np.exp(1j * (n - m) * theta)).real)
             assert abs(S[m, n] - ref) < 1e-12
+
+
+# --------------------------------------------------------------------------------------
+# The half-split pairing (element i rotated with element i + D/2).  Scores are dot products
+# over the head dimension, so permuting q and k alike changes nothing: the half-split path is
+# the interleaved path (pinned above) on inputs whose dimensions are reordered i -> 2i,
+# i + D/2 -> 2i + 1, and its gradients are the interleaved ones reordered back.
+# --------------------------------------------------------------------------------------
+def to_interleaved(x):
+    """[..., D] -> the same vector with element i at 2i and element i + D/2 at 2i + 1."""
+    D = x.shape[-1]
+    y = np.empty_like(x)
+    y[..., 0::2], y[..., 1::2] = x[..., :D // 2], x[..., D // 2:]
+    return y
+
+
+def from_interleaved(y):
+    return np.concatenate([y[..., 0::2], y[..., 1::2]], axis=-1)
+
+
+def test_half_split_rope_is_the_interleaved_rotation_of_reordered_dimensions():
+    x = rnd((2, 23, 3, 16), 151)
+    for inv in (False, True):
+        ref = from_interleaved(oracle.rope(to_interleaved(x), 10000.0, inverse=inv))
+        np.testing.assert_array_equal(oracle.rope(x, 10000.0, inverse=inv, half_split=True), ref)
+    np.testing.assert_array_equal(oracle.rope(x, 0.0, half_split=True), x)
+
+
+def test_half_split_scores_depend_only_on_relative_position():
+    """The closed form of test_rope_scores_depend_only_on_relative_position with the complex
+    pairs a_i + i a_{i + D/2}."""
+    T, D, base = 33, 16, 500.0
+    a, b = rnd((D,), 161), rnd((D,), 162)
+    A = oracle.rope(np.broadcast_to(a, (1, T, 1, D)).copy(), base, half_split=True)[0, :, 0]
+    Bm = oracle.rope(np.broadcast_to(b, (1, T, 1, D)).copy(), base, half_split=True)[0, :, 0]
+    S = A @ Bm.T
+    ac = a[:D // 2] + 1j * a[D // 2:]
+    bc = b[:D // 2] + 1j * b[D // 2:]
+    theta = base ** (-np.arange(0, D, 2) / D)
+    for m in range(T):
+        for n in range(T):
+            ref = np.sum((np.conj(ac) * bc * np.exp(1j * (n - m) * theta)).real)
+            assert abs(S[m, n] - ref) < 1e-12
+
+
+@pytest.mark.parametrize("window,qk", [(0, None), (7, None), (0, (1.2, 1e-6))])
+def test_half_split_attention_is_interleaved_attention_of_reordered_q_and_k(window, qk):
+    q, k, v, dO = case(2, 29, 6, 2, 16, seed=171)
+    o, lse = oracle.fwd(q, k, v, 10000.0, window=window, qk_norm=qk, half_split=True)
+    dq, dk, dv = oracle.bwd(q, k, v, dO, 10000.0, window=window, qk_norm=qk, half_split=True)
+    qi, ki = to_interleaved(q), to_interleaved(k)
+    ro, rlse = oracle.fwd(qi, ki, v, 10000.0, window=window, qk_norm=qk)
+    rq, rk, rv = oracle.bwd(qi, ki, v, dO, 10000.0, window=window, qk_norm=qk)
+    assert relerr(o, ro) < 1e-14 and np.max(np.abs(lse - rlse)) < 1e-13
+    assert relerr(dq, from_interleaved(rq)) < 1e-13
+    assert relerr(dk, from_interleaved(rk)) < 1e-13
+    assert relerr(dv, rv) < 1e-13
+    # and the pairing matters: the interleaved path on the same inputs gives other scores
+    assert relerr(o, oracle.fwd(q, k, v, 10000.0, window=window, qk_norm=qk)[0]) > 1e-3
+
+
+def test_half_split_finite_differences_every_entry_tiny():
+    q, k, v, dO = case(1, 5, 4, 2, 4, seed=43)
+    assert fd_check(q, k, v, dO, 10000.0, half_split=True) < 1e-6
 
 
 def test_rejects_bad_shapes():

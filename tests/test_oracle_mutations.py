@@ -16,7 +16,10 @@ from tests import test_oracle as pins
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "ne_oracle.c")
 
 MUTATIONS = {
-    "rope_rotation_sign": ("yr[2 * i + 1] = a * s + b * c;", "yr[2 * i + 1] = a * s - b * c;"),
+    "rope_rotation_sign": ("yr[i1] = a * s + b * c;", "yr[i1] = a * s - b * c;"),
+    "rope_half_split_partner": ("i1 = half ? i + D / 2 : 2 * i + 1;", "i1 = half ? D - 1 - i : 2 * i + 1;"),
+    "rope_half_split_ignored_in_backward": ("dq + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, T, D, base, -1, half);",
+                                            "dq + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, T, D, base, -1, 0);"),
     "rope_frequency_exponent": ("pow(base, -2.0 * (double)i / (double)D)", "pow(base, -1.0 * (double)i / (double)D)"),
     "gqa_head_mapping": ("const int g = h / G;", "const int g = h % Hkv;"),
     "mask_includes_future": [
@@ -34,10 +37,10 @@ MUTATIONS = {
     "softmax_scale_missing": ("            s *= scale;\n", "\n"),
     "dq_scale_missing": ("for (int d = 0; d < D; ++d) dqi[d] *= scale;", ""),
     "ds_sign": ("* (dp - di);", "* (di - dp);"),
-    "dq_forward_rotation": ("dq + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, T, D, base, -1);",
-                            "dq + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, T, D, base, 1);"),
-    "dk_forward_rotation": ("dk + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, T, D, base, -1);",
-                            "dk + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, T, D, base, 1);"),
+    "dq_forward_rotation": ("dq + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, T, D, base, -1, half);",
+                            "dq + IDX4(b, 0, h, 0, T, Hq, D), (size_t)Hq * D, T, D, base, 1, half);"),
+    "dk_forward_rotation": ("dk + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, T, D, base, -1, half);",
+                            "dk + IDX4(b, 0, g, 0, T, Hkv, D), (size_t)Hkv * D, T, D, base, 1, half);"),
     "dv_uses_ds": ("dvj[d] += p * dOi[d];", "dvj[d] += s * dOi[d];"),
     "dk_uses_rotated_k": ("dkj[d] += s * qi[d];", "dkj[d] += s * kr[(size_t)i * D + d];"),
     "lse_without_max": ("lse_row[i] = m + log(l);", "lse_row[i] = log(l);"),
@@ -69,6 +72,9 @@ def battery():
                                                                                     (1.2, 1e-6))),
         ("qknorm_self_score", pins.test_qk_norm_self_score_closed_form),
         ("qknorm_invariance", pins.test_qk_norm_rescaling_rows_changes_nothing),
+        ("half_split_rope", pins.test_half_split_rope_is_the_interleaved_rotation_of_reordered_dimensions),
+        ("half_split_relative", pins.test_half_split_scores_depend_only_on_relative_position),
+        ("half_split_fd", pins.test_half_split_finite_differences_every_entry_tiny),
     ]
     for name, fn in checks:
         try:

@@ -32,6 +32,8 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t table, qh, kh, vh, dOh, delta, lse2, rq, rk, dsc, amax, dqacc, ds, total;
+    size_t qs, ks;  // backward, half-split pairs with RoPE: slot-ordered raw q and k (QK norm backward)
+    bool half;      // half-split pairs with RoPE on
     // split row / key blocks: partial results and counters of the forward (fwd, 16-bit) or of the
     // dQ pass (q) and the dK/dV pass (k) of the recomputing 16-bit backward; counters of one call
     // are contiguous (one clearing range), the dQ pass's first
@@ -56,8 +58,6 @@ ne_status_t check_flags(unsigned flags) {
     if (flags & ~kKnownFlags) return fail(NE_ERR_UNSUPPORTED, "unknown flag bits 0x%x", flags & ~kKnownFlags);
     if (flags & NE_FLAG_BF16_OPERANDS)
         return fail(NE_ERR_UNSUPPORTED, "NE_FLAG_BF16_OPERANDS is reserved and not implemented (fp16 operands only)");
-    if (flags & NE_FLAG_ROPE_HALF_SPLIT)
-        return fail(NE_ERR_UNSUPPORTED, "NE_FLAG_ROPE_HALF_SPLIT is reserved and not implemented (adjacent pairs only)");
     return NE_OK;
 }
 
@@ -128,6 +128,7 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, double base, ne_dt
     const size_t nq = (size_t)B * T * Hq * D, nk = (size_t)B * T * Hkv * D;
     Layout L{};
     L.mode = bwd ? bwd_mode(in, flags, T, Hq, Hkv) : ne::kBwdRecompute;
+    L.half = (flags & NE_FLAG_ROPE_HALF_SPLIT) && base > 0.0;
     size_t off = ne::kTableHdrBytes;
     L.table = off;
     if (base > 0.0) off += up((size_t)T * (D / 2) * 8);
@@ -147,6 +148,11 @@ Layout layout(bool bwd, int B, int T, int Hq, int Hkv, int D, double base, ne_dt
         L.rk = off; off += up((size_t)B * T * Hkv * 4);
         L.dsc = off; off += up(ngrp * 4);
         L.amax = off; off += up(ngrp * L.nparts * 4);
+        // the size query sees no options, so the raw copies are kept whether or not the QK norm is on
+        if (L.half) {
+            L.qs = off; off += up(nq * esz);
+            L.ks = off; off += up(nk * esz);
+        }
         // the atomic dQ accumulator, plus 64 rows past the last group that the dK/dV pass may add zeros to
         if (L.mode == ne::kBwdAtomic) { L.dqacc = off; off += up((nq + (size_t)64 * D) * 4); }
         if (L.mode == ne::kBwdStoredDs) {
@@ -307,12 +313,14 @@ ne_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
     pa.rope_base = rope_base;
     pa.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
     pa.qkn = qkn;
+    pa.half = L.half ? 1 : 0;
     ne::FwdArgs fa{};
     fa.q = q; fa.kh = pa.kh; fa.vh = pa.vh; fa.table = pa.table; fa.o = o; fa.lse = lse;
     fa.rope_base = rope_base; fa.qscale = pa.qscale;
     fa.B = B; fa.T = T; fa.Hq = Hq; fa.Hkv = Hkv; fa.G = G;
     fa.window = visible_keys(opts->window, T);
     fa.qkn = qkn;
+    fa.half = pa.half;
     fa.nrb = (int)(((int64_t)T * G + 127) / 128);
     ne::SplitPlan* sp = split_scratch(ne::kSplitFwd);
     sp->njobs = 0;
@@ -366,6 +374,8 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     pa.rope_base = rope_base;
     pa.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
     pa.qkn = qkn;
+    pa.half = L.half ? 1 : 0;
+    if (L.half && qkn.on) { pa.qs = ws + L.qs; pa.ks = ws + L.ks; }
     pa.skip_v = L.mode != ne::kBwdRecompute ? 1 : 0;
     pa.amax_part = (const float*)(ws + L.amax);
     pa.nparts = L.nparts;
@@ -382,7 +392,9 @@ ne_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
     ba.B = B; ba.T = T; ba.Hq = Hq; ba.Hkv = Hkv; ba.G = G;
     ba.window = visible_keys(opts->window, T);
     ba.qkn = qkn;
-    ba.q = q; ba.k = k; ba.in_dt = (int)in_dtype;
+    ba.half = pa.half;
+    // the QK norm backward reads raw q and k in the slot order of the kernels
+    ba.q = pa.qs ? pa.qs : q; ba.k = pa.ks ? pa.ks : k; ba.in_dt = (int)in_dtype;
     ba.rq = pa.rq; ba.rk = pa.rk;
     ba.ds = L.mode == ne::kBwdStoredDs ? ws + L.ds : nullptr;
     ba.dsc = pa.dsc;

@@ -155,11 +155,28 @@ __device__ __forceinline__ float dO_scale(float amax) {
 }
 
 template <typename TI, typename OP, int D, bool ROT>
-__device__ __forceinline__ void convert8(const TI* src, OP* dst, const float2* cs_row, int chunk, float mul) {
-    // 8 consecutive elements: chunk*8 .. chunk*8+7, pairs (2i, 2i+1) rotated by cs_row[i].
+__device__ __forceinline__ void convert8(const TI* src, OP* dst, const float2* cs_row, int chunk, float mul,
+                                         bool half = false, TI* raw = nullptr) {
+    // 8 consecutive slots chunk*8 .. chunk*8+7 (src and dst point at slot chunk*8 of their rows),
+    // pairs (2i, 2i+1) rotated by cs_row[i].  half (ROT only): the half-split pairing, slot 2i takes
+    // element i and slot 2i+1 element i + D/2 of the source row, and raw (or null) receives the
+    // slots unrotated.
     float x[8];
+    if (ROT && half) {
+        const TI* row = src - chunk * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = to_f32(src[e]);
+        for (int p = 0; p < 4; ++p) {
+            x[2 * p] = to_f32(row[chunk * 4 + p]);
+            x[2 * p + 1] = to_f32(row[D / 2 + chunk * 4 + p]);
+        }
+        if (raw) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) raw[e] = from_f32<TI>(x[e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = to_f32(src[e]);
+    }
     if (ROT) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -266,15 +283,19 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
         if (live) {
             if (which < Hq) {  // q -> q~ (rotated, scaled by scale*log2e), flattened rows
                 const int hq = which, g = hq / G, hh = hq % G;
-                const TI* src = (const TI*)a.q + (((size_t)b * T + t) * Hq + hq) * D + chunk * 8;
+                const size_t in_off = (((size_t)b * T + t) * Hq + hq) * D + chunk * 8;
+                const TI* src = (const TI*)a.q + in_off;
                 OP* dst = (OP*)a.qh + (((size_t)b * Hkv + g) * TG + (size_t)t * G + hh) * D + chunk * 8;
-                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, a.qscale * fac * guard);
+                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, a.qscale * fac * guard, a.half,
+                                                    a.qs ? (TI*)a.qs + in_off : nullptr);
                 else convert8<TI, OP, D, false>(src, dst, csr, chunk, a.qscale * fac);
             } else if (which < Hq + Hkv) {  // k -> k'
                 const int g = which - Hq;
-                const TI* src = (const TI*)a.k + (((size_t)b * T + t) * Hkv + g) * D + chunk * 8;
+                const size_t in_off = (((size_t)b * T + t) * Hkv + g) * D + chunk * 8;
+                const TI* src = (const TI*)a.k + in_off;
                 OP* dst = (OP*)a.kh + (((size_t)b * Hkv + g) * T + t) * D + chunk * 8;
-                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, fac * guard);
+                if (rope) convert8<TI, OP, D, true>(src, dst, csr, chunk, fac * guard, a.half,
+                                                    a.ks ? (TI*)a.ks + in_off : nullptr);
                 else convert8<TI, OP, D, false>(src, dst, csr, chunk, fac);
             } else if (which < Hq + 2 * Hkv) {  // v -> v'
                 const int g = which - Hq - Hkv;
@@ -347,7 +368,7 @@ __global__ __launch_bounds__(256) void prep_fwd_h(PrepArgs a) {
                 const size_t in_off = (((size_t)b * T + t) * Hkv + hkv) * D + chunk * 8;
                 _Float16* kdst = (_Float16*)a.kh + ((size_t)grp * T + t) * D + chunk * 8;
                 if (rope) convert8<TI, _Float16, D, true>((const TI*)a.k + in_off, kdst, a.table + (size_t)t * (D / 2),
-                                                          chunk, fac);
+                                                          chunk, fac, a.half);
                 else convert8<TI, _Float16, D, false>((const TI*)a.k + in_off, kdst, nullptr, chunk, fac);
             }
         }
@@ -430,9 +451,11 @@ __device__ __forceinline__ int piece_lo(int j0, int j1, int p, int np) { return 
 // below 256 in between), so the rescale of O is rare.
 // =====================================================================================
 // Query fragments (B operand of S^T = K Q^T) of one row, rotated, scaled and converted.
+// half (with cs): the half-split pairing, slot 2i takes element i of the row and slot 2i + 1
+// element i + D/2.
 template <typename TI, typename OP, int D>
 __device__ __forceinline__ void load_q_frags(typename Mma<OP>::frag (&qf)[D / Mma<OP>::K], const TI* row,
-                                             const float2* cs, float mul, int h, bool valid) {
+                                             const float2* cs, float mul, int h, bool valid, bool half) {
     constexpr int KS = D / Mma<OP>::K;
     if constexpr (sizeof(OP) == 2) {
 #pragma unroll
@@ -440,7 +463,15 @@ __device__ __forceinline__ void load_q_frags(typename Mma<OP>::frag (&qf)[D / Mm
             float x[8];
             if (valid) {
                 const int e0 = 16 * ks + 8 * h;
-                load8(row + e0, x);
+                if (cs && half) {
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        x[2 * p] = to_f32(row[e0 / 2 + p]);
+                        x[2 * p + 1] = to_f32(row[D / 2 + e0 / 2 + p]);
+                    }
+                } else {
+                    load8(row + e0, x);
+                }
                 if (cs) {
                     const floatx4 c01 = *reinterpret_cast<const floatx4*>(cs + e0 / 2);
                     const floatx4 c23 = *reinterpret_cast<const floatx4*>(cs + e0 / 2 + 2);
@@ -466,7 +497,8 @@ __device__ __forceinline__ void load_q_frags(typename Mma<OP>::frag (&qf)[D / Mm
         for (int ks = 0; ks < KS; ++ks) {
             float val = 0.f;
             if (valid) {
-                const float u = to_f32(row[2 * ks]), v = to_f32(row[2 * ks + 1]);
+                const bool hs = cs && half;
+                const float u = to_f32(row[hs ? ks : 2 * ks]), v = to_f32(row[hs ? D / 2 + ks : 2 * ks + 1]);
                 val = h == 0 ? u : v;
                 if (cs) {
                     const float2 r = cs[ks];
@@ -518,7 +550,7 @@ void fwd_kernel(FwdArgs a) {
         const TI* qrow = (const TI*)a.q + (((size_t)b * T + t) * a.Hq + hkv * G + hh) * D;
         float qmul = a.qscale;
         if (a.qkn.on && rvalid) qmul *= qk_factor(row_sumsq(qrow, D), D, a.qkn.gain, a.qkn.eps);
-        load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, qmul, h, rvalid);
+        load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, qmul, h, rvalid, a.half);
     }
     wait_all();
     lds_fill<OP, D, BN, NW>(lds, kg, j0 * BN, T);
@@ -725,7 +757,7 @@ void fwd_kernel_h(FwdArgs a, SplitPlan sp) {
         const TI* qrow = (const TI*)a.q + (((size_t)b * T + t) * a.Hq + hkv * G + hh) * D;
         float qmul = a.qscale;
         if (a.qkn.on && rvalid) qmul *= qk_factor(row_sumsq(qrow, D), D, a.qkn.gain, a.qkn.eps);
-        load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, qmul, h, rvalid);
+        load_q_frags<TI, OP, D>(qf, qrow, rope ? a.table + (size_t)t * (D / 2) : nullptr, qmul, h, rvalid, a.half);
     }
     wait_all();
     fill_k(j0, 0);
@@ -2348,9 +2380,39 @@ static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, const Spli
     return m.after(1);
 }
 
+// =====================================================================================
+// Half-split rotary pairs: rows that the backward wrote in slot order (element i in slot 2i,
+// element i + D/2 in slot 2i + 1) put back in element order, in place.  grid ceil(nrows / RPB),
+// 256 threads: RPB = 256 / (D / 4) whole rows per workgroup staged through LDS, so every load of
+// the workgroup has landed before any store; each thread then writes four consecutive elements.
+// =====================================================================================
+template <typename T, int D>
+__global__ __launch_bounds__(256) void slots_to_elems_kernel(T* rows, int64_t nrows) {
+    constexpr int TPR = D / 4, RPB = 256 / TPR;
+    __shared__ float buf[RPB][D];
+    const int rl = threadIdx.x / TPR, d = 4 * (threadIdx.x % TPR);
+    const int64_t row = (int64_t)blockIdx.x * RPB + rl;
+    const bool ok = row < nrows;
+    T* r = rows + (ok ? row : 0) * D;
+    if (ok) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) buf[rl][d + e] = to_f32(r[d + e]);
+    }
+    __syncthreads();
+    if (ok) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = d + e;
+            x[e] = buf[rl][i < D / 2 ? 2 * i : 2 * (i - D / 2) + 1];
+        }
+        store4(r + d, x[0], x[1], x[2], x[3]);
+    }
+}
+
 template <typename TI, typename TO, typename OP, int D>
-static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am, const BwdArgs& ba,
-                               const SplitPlan& sp, const SplitPlan& spk, hipStream_t s, hipEvent_t const* ev) {
+static hipError_t launch_bwd_passes(int mode, const PrepArgs& pa, const AmaxArgs& am, const BwdArgs& ba,
+                                    const SplitPlan& sp, const SplitPlan& spk, hipStream_t s, hipEvent_t const* ev) {
     const Marks m{ev, s};
     NE_TRY(m.before(0));
     if constexpr (sizeof(OP) == 2) {
@@ -2421,6 +2483,23 @@ static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am,
         hipLaunchKernelGGL((dq_kernel<OP, D, TO>), dim3(ba.nrb * ngroups), dim3(256), 0, s, ba);
     NE_TRY(hipGetLastError());
     return m.after(2);
+}
+
+// The backward's passes, then (half-split pairing) dq and dk back to element order; the marked
+// intervals cover the passes.
+template <typename TI, typename TO, typename OP, int D>
+static hipError_t launch_bwd_t(int mode, const PrepArgs& pa, const AmaxArgs& am, const BwdArgs& ba,
+                               const SplitPlan& sp, const SplitPlan& spk, hipStream_t s, hipEvent_t const* ev) {
+    NE_TRY((launch_bwd_passes<TI, TO, OP, D>(mode, pa, am, ba, sp, spk, s, ev)));
+    if (!ba.half) return hipSuccess;
+    constexpr int RPB = 256 / (D / 4);
+    const int64_t nq = (int64_t)ba.B * ba.T * ba.Hq, nk = (int64_t)ba.B * ba.T * ba.Hkv;
+    hipLaunchKernelGGL((slots_to_elems_kernel<TO, D>), dim3((unsigned)((nq + RPB - 1) / RPB)), dim3(256), 0, s,
+                       (TO*)ba.dq, nq);
+    NE_TRY(hipGetLastError());
+    hipLaunchKernelGGL((slots_to_elems_kernel<TO, D>), dim3((unsigned)((nk + RPB - 1) / RPB)), dim3(256), 0, s,
+                       (TO*)ba.dk, nk);
+    return hipGetLastError();
 }
 
 #define NE_DISPATCH_D(FN, TI, TO, OP, D, ...)                       \

@@ -47,6 +47,13 @@ struct PrepArgs {
     double rope_base;
     float qscale;                                   // softmax scale * log2(e)
     QkNorm qkn;
+    // half-split rotary pairs: the kernels rotate adjacent slots (2i, 2i + 1); with the pairing
+    // (i, i + D/2) element i of a raw q or k row goes to slot 2i and element i + D/2 to slot 2i + 1
+    // (scores are sums over slots), dq and dk leave the backward in slot order and a last pass puts
+    // them back in element order; qs / ks (or null): slot-ordered raw copies of q and k for the QK
+    // norm backward
+    int half;
+    void* qs; void* ks;
     int skip_v;                                     // backward: no v' copy (the dK/dV pass reads v)
     const TableHdr* hdr;                            // the table's header (RoPE on)
     // backward, 16-bit operands: dO' = s dO with s a power of two per (batch, KV head) group chosen
@@ -113,6 +120,7 @@ struct FwdArgs {
     double rope_base;
     float qscale;                                   // softmax scale * log2(e)
     QkNorm qkn;
+    int half;                                       // half-split rotary pairs (as in PrepArgs)
 };
 
 struct BwdArgs {
@@ -135,6 +143,7 @@ struct BwdArgs {
     double rope_base;
     float scale;                                    // softmax scale 1/sqrt(D)
     QkNorm qkn;
+    int half;                                       // half-split rotary pairs (as in PrepArgs)
 };
 
 // Cache append (decode path): k_new / v_new [B][Tn][Hkv][D] into the cache at positions

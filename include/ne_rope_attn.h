@@ -88,8 +88,14 @@ typedef enum {
  *                             as it holds, with the same bits.  Deterministic; 16-bit inputs only.
  *                             Ignored together with NE_FLAG_NONDETERMINISTIC.
  *   NE_FLAG_BF16_OPERANDS     reserved: bf16 MFMA operands.  Not implemented: NE_ERR_UNSUPPORTED.
- *   NE_FLAG_ROPE_HALF_SPLIT   reserved: rotate the pairs (i, i + D/2) instead of (2i, 2i + 1).
- *                             Not implemented: NE_ERR_UNSUPPORTED. */
+ *   NE_FLAG_ROPE_HALF_SPLIT   fwd, bwd, their _ex forms and the workspace query: RoPE rotates
+ *                             element i with element i + head_dim/2 by t * theta_i (the other
+ *                             common pairing; the frequencies and positions are unchanged) instead
+ *                             of the adjacent pair (2i, 2i + 1).  Pass the same flag to the forward
+ *                             and to the backward (and to the backward's workspace query: it adds
+ *                             slot-ordered copies of q and k, read by the QK-norm backward).  No
+ *                             effect with rope_base <= 0.  The KV-cache, decode and QKV-projection
+ *                             calls take no flags and use adjacent pairs. */
 #define NE_FLAG_NONDETERMINISTIC 0x1u
 #define NE_FLAG_BF16_OPERANDS 0x2u
 #define NE_FLAG_ROPE_HALF_SPLIT 0x4u
@@ -113,7 +119,8 @@ typedef enum {
  *   backward: the rotated, scaled copies of q, k, dO (and v), Delta = rowsum(dO * o), the
  *             log2-scaled lse, the per-row 1/rms of the QK norm, the dO scales; with
  *             NE_FLAG_NONDETERMINISTIC the fp32 dQ accumulator [B][Hq][T][head_dim]; with
- *             NE_FLAG_STORE_DS the stored dS; otherwise (16-bit) the split regions of the dQ pass.
+ *             NE_FLAG_STORE_DS the stored dS; otherwise (16-bit) the split regions of the dQ pass;
+ *             with NE_FLAG_ROPE_HALF_SPLIT and rope_base > 0 copies of q and k in in_dtype.
  * Split row blocks: when a call has few causal row blocks per CU, the longest blocks of the forward
  * and of the recomputing dQ pass are cut into 2-4 ranges of keys run by separate workgroups; the
  * last to finish combines the others' partial results in a fixed order (the result does not depend

@@ -230,6 +230,16 @@ def test_workspace_sizes(L):
     assert wsb(L, 1, B, T, Hq, Hkv, D) >= wsb(L, 0, B, T, Hq, Hkv, D)
     # ragged T: the forward's transposed V' copy pads every row of keys to a multiple of 64
     assert wsb(L, 0, B, 100, Hq, Hkv, D) == sizes(B, 100, Hq, Hkv, D, 2)[1]
+    # half-split pairs: the backward keeps slot-ordered copies of raw q and k (read by the QK-norm
+    # backward); the forward and calls without RoPE need nothing more
+    HALF = binding.NE_FLAG_ROPE_HALF_SPLIT
+    nq, nk = B * T * Hq * D, B * T * Hkv * D
+    assert wsb(L, 0, B, T, Hq, Hkv, D, flags=HALF) == wsb(L, 0, B, T, Hq, Hkv, D)
+    for fl in (0, binding.NE_FLAG_STORE_DS, binding.NE_FLAG_NONDETERMINISTIC):
+        assert wsb(L, 1, B, T, Hq, Hkv, D, flags=HALF | fl) == wsb(L, 1, B, T, Hq, Hkv, D, flags=fl) + \
+            up(2 * nq) + up(2 * nk)
+        assert wsb(L, 1, B, T, Hq, Hkv, D, base=0.0, flags=HALF | fl) == wsb(L, 1, B, T, Hq, Hkv, D, base=0.0, flags=fl)
+    assert wsb(L, 1, B, T, Hq, Hkv, D, dt=binding.NE_F32, flags=HALF) == b4 + v4 + up(4 * nq) + up(4 * nk)
     # invalid arguments: 0
     assert wsb(L, 0, B, T, 12, 5, D) == 0
     assert wsb(L, 0, B, T, Hq, Hkv, 96) == 0
@@ -274,7 +284,8 @@ def bwd_call(L, ptrs=None, B=1, T=16, Hq=4, Hkv=2, D=64, base=1e4, i=binding.NE_
     (dict(B=0), 2), (dict(T=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(Hq=6, Hkv=4), 2),
     (dict(D=96), 3), (dict(D=16), 3), (dict(i=binding.NE_F32, out=binding.NE_BF16), 3),
     (dict(i=binding.NE_BF16, out=binding.NE_F16), 3), (dict(i=7), 3),
-    (dict(flags=binding.NE_FLAG_BF16_OPERANDS), 3), (dict(flags=binding.NE_FLAG_ROPE_HALF_SPLIT), 3),
+    (dict(flags=binding.NE_FLAG_BF16_OPERANDS), 3),
+    (dict(flags=binding.NE_FLAG_ROPE_HALF_SPLIT, wsb=16), 5),   # the pairing flag is accepted
     (dict(flags=0x10), 3),
     (dict(q=FAKE + 8), 4), (dict(ws=FAKE + 4), 4),
     (dict(wsb=16), 5),
@@ -299,7 +310,8 @@ def test_bwd_rejects_misaligned_small_workspace_and_flags(L):
     assert bwd_call(L, wsb=100) == 5
     assert bwd_call(L, Hq=5, Hkv=2) == 2
     assert bwd_call(L, flags=binding.NE_FLAG_BF16_OPERANDS) == 3
-    assert bwd_call(L, flags=binding.NE_FLAG_ROPE_HALF_SPLIT | binding.NE_FLAG_STORE_DS) == 3
+    assert bwd_call(L, flags=binding.NE_FLAG_ROPE_HALF_SPLIT | binding.NE_FLAG_BF16_OPERANDS) == 3
+    assert bwd_call(L, flags=binding.NE_FLAG_ROPE_HALF_SPLIT | binding.NE_FLAG_STORE_DS, wsb=100) == 5
     assert bwd_call(L, flags=1 << 31) == 3
     # the atomic dQ needs its accumulator: a workspace one region short is rejected (the stored dS
     # is covered below: a smaller buffer is valid down to one group)

@@ -22,6 +22,7 @@ The other measurements run first (each with its own warmup), the headline last:
   * a sliding window of --window keys (default T/4, the short window of the nanochat guide's
     window_pattern; 0 skips it), counting the visible pairs N_W = W(W+1)/2 + (T-W)W per head;
   * the causal step with the QK norm on (gain 1.2, eps 1e-6), under "qk_norm";
+  * the causal step with the half-split rotary pairing (NE_FLAG_ROPE_HALF_SPLIT), under "half_split";
   * the workload layer's QKV projection with the RoPE epilogue (2 M N C flops), "qkv_projection";
   * one decode step of the cached workload (--decode-batch sequences, each holding 8191 tokens of the
     long-context shape, Hq 32 / Hkv 8 / D 128, RoPE base 5e5, attending with one new token) as HBM
@@ -399,6 +400,8 @@ def main():
                     help="window of the sliding-window measurement (-1: T/4; 0: skip it)")
     ap.add_argument("--qkv", type=int, default=1, help="also measure the QKV projection with the RoPE epilogue")
     ap.add_argument("--qk-norm", type=int, default=1, help="also measure the step with the QK norm on (0: skip)")
+    ap.add_argument("--half-split", type=int, default=1,
+                    help="also measure the step with the half-split rotary pairing (0: skip)")
     ap.add_argument("--other-backwards", type=int, default=1,
                     help="also measure the step with the stored dS and with the atomic dQ (0: skip)")
     ap.add_argument("--configs", type=int, default=1,
@@ -452,7 +455,7 @@ def main():
 
         def step(ev_f=None, ev_b=None):
             binding.ne_rope_attn_fwd(q, k, v, w.rope_base, o=o, lse=lse, workspace=ws, window=window,
-                                     qk_norm=qk_norm, events=ev_f)
+                                     qk_norm=qk_norm, events=ev_f, flags=flags & binding.NE_FLAG_ROPE_HALF_SPLIT)
             binding.ne_rope_attn_bwd(q, k, v, o, lse, dO, w.rope_base, dq=dq, dk=dk, dv=dv, workspace=ws,
                                      flags=flags, window=window, qk_norm=qk_norm, events=ev_b)
         return step
@@ -549,6 +552,9 @@ def main():
                                         **side_line(make_step(window=Wn), "recompute", unit_w, K))
     if args.qk_norm:
         result["qk_norm"] = dict(gain=1.2, eps=1e-6, **side_line(make_step(qk_norm=(1.2, 1e-6)), "recompute", unit, K))
+    if args.half_split and w.rope_base > 0:
+        result["half_split"] = dict(flags="NE_FLAG_ROPE_HALF_SPLIT", pairs="(i, i + D/2)",
+                                    **side_line(make_step(flags=binding.NE_FLAG_ROPE_HALF_SPLIT), "recompute", unit, K))
     if args.qkv:
         result["qkv_projection"] = measure_qkv(w, K, hev, new_events, MFMA_PEAK_F16)
     if args.decode_batch > 0:

@@ -33,6 +33,8 @@
 // tokens, row R = t * G + hh (hh = head within the group).  In the [B][T][Hq][D] input these
 // rows are exactly the memory order of one token's heads, and the causal mask depends only on
 // t = R / G, so any G packs into fixed 128-row blocks that share one K/V tile.
+#include <algorithm>
+
 #include "ne_common.hpp"
 #include "ne_launch.hpp"
 
@@ -190,8 +192,10 @@ __device__ __forceinline__ void convert8(const TI* src, OP* dst, const float2* c
     for (int e = 0; e < 8; ++e) dst[e] = from_f32<OP>(x[e] * mul);
 }
 
-// grid (ceil(T / TT), B), 256 threads.  Forward: k, v and the cos/sin table.  Backward: q, k, v,
-// dO, Delta, lse2 and the table.
+// grid (ceil(T / TT), B, Z), 256 threads.  Forward: k, v and the cos/sin table.  Backward: q, k, v,
+// dO, Delta, lse2 and the table.  The rows of a token (q heads, k, v, dO heads) are cut into Z equal
+// ranges, one per blockIdx.z, so that a small call still launches enough workgroups to keep many
+// loads in flight.
 // The hand-off counters of the split row blocks of the attention pass that follows start at zero.
 __device__ __forceinline__ void clear_split_counters(const PrepArgs& a) {
     if (!a.split_cnt) return;
@@ -230,14 +234,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const int qrows = BWD ? Hq : 0;  // the forward rotates q inside the attention kernel
     const int skip_v = BWD && a.skip_v ? Hkv : 0;  // rows of v not copied
     const int rows_per_tok = qrows + 2 * Hkv - skip_v + (BWD ? Hq : 0);
-    const int items = TT * rows_per_tok * CPR;
+    const int zr0 = rows_per_tok * blockIdx.z / gridDim.z, zr1 = rows_per_tok * (blockIdx.z + 1) / gridDim.z;
+    const int zrows = zr1 - zr0;   // this block's rows of each token
+    const int items = TT * zrows * CPR;
     const int items_pad = (items + 255) / 256 * 256;  // whole waves iterate together
     const size_t TG = (size_t)T * G;
     for (int idx = threadIdx.x; idx < items_pad; idx += 256) {
         const int chunk = idx % CPR;
         const int rowid = idx / CPR;
-        const int tl = rowid / rows_per_tok;
-        int which = rowid % rows_per_tok + (BWD ? 0 : Hq);  // forward: skip the q rows
+        const int tl = rowid / zrows;
+        int which = zr0 + rowid % zrows + (BWD ? 0 : Hq);  // forward: skip the q rows
         if (which >= Hq + Hkv) which += skip_v;
         const int t = t0 + tl;
         const bool live = idx < items && t < T;
@@ -2352,6 +2358,18 @@ struct Marks {
         if (e_ != hipSuccess) return e_;      \
     } while (0)
 
+// Grid of prep_kernel: 8 tokens of one batch element per workgroup, and, when that gives fewer than
+// 1024 workgroups (a small call, bound by loads in flight rather than bandwidth), the rows of each
+// token cut into up to 4 ranges.  The NanoEuler layer (B8 T512 Hq12 Hkv4 D64: 512 workgroups) runs
+// its backward preparation 3.5 us faster cut in 4; at 1024 workgroups (B4 T2048) a cut in 2 was
+// 2.7 us slower.
+static dim3 prep_grid(const PrepArgs& pa, bool bwd) {
+    const int nb = (pa.T + 7) / 8 * pa.B;
+    const int rows = bwd ? 2 * pa.Hq + 2 * pa.Hkv - (pa.skip_v ? pa.Hkv : 0) : 2 * pa.Hkv;
+    const int z = nb >= 1024 ? 1 : std::max(1, std::min({4, rows, (2048 + nb - 1) / nb}));
+    return dim3((pa.T + 7) / 8, pa.B, z);
+}
+
 template <typename TI, typename TO, typename OP, int D>
 static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, const SplitPlan& sp, hipStream_t s,
                                hipEvent_t const* ev) {
@@ -2360,7 +2378,7 @@ static hipError_t launch_fwd_t(const PrepArgs& pa, const FwdArgs& fa, const Spli
     if constexpr (sizeof(OP) == 2)
         hipLaunchKernelGGL((prep_fwd_h<TI, D>), dim3((pa.T + 63) / 64, pa.B * pa.Hkv, 2), dim3(256), 0, s, pa);
     else
-        hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, false>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);
+        hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, false>), prep_grid(pa, false), dim3(256), 0, s, pa);
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(0));
     NE_TRY(m.before(1));
@@ -2419,7 +2437,7 @@ static hipError_t launch_bwd_passes(int mode, const PrepArgs& pa, const AmaxArgs
         hipLaunchKernelGGL((dO_amax_kernel<TI, D>), dim3(am.nparts, ba.B), dim3(256), 0, s, am);
         NE_TRY(hipGetLastError());
     }
-    hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, true>), dim3((pa.T + 7) / 8, pa.B), dim3(256), 0, s, pa);
+    hipLaunchKernelGGL((prep_kernel<TI, TO, OP, D, true>), prep_grid(pa, true), dim3(256), 0, s, pa);
     NE_TRY(hipGetLastError());
     NE_TRY(m.after(0));
     const int ngroups = ba.B * ba.Hkv, npair = ((ba.T + 63) / 64 + 1) / 2;

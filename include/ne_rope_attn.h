@@ -200,7 +200,8 @@ typedef struct {
  * preparation with Delta (and the dO scales), 1 dK/dV, 2 dQ (the dQ pass, or with
  * NE_FLAG_NONDETERMINISTIC the conversion of the accumulated dQ) (6 entries; with NE_FLAG_STORE_DS
  * run in several group batches, interval 1 spans every batch's dK/dV and all but the last dQ,
- * interval 2 the last dQ).  The events are created and owned by the caller. */
+ * interval 2 the last dQ; with NE_FLAG_ROPE_HALF_SPLIT the two small launches that put dq and dk back
+ * in element order follow the last interval).  The events are created and owned by the caller. */
 ne_status_t ne_rope_attn_fwd_ex(const void* q, const void* k, const void* v,
                                 void* o, float* lse,
                                 int B, int T, int Hq, int Hkv, int head_dim, double rope_base,

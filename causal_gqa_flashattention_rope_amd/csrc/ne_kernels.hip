@@ -1300,10 +1300,11 @@ void dkdv_kernel(BwdArgs a) {
 // =====================================================================================
 // Backward dK/dV, 16-bit operands.  Same work split as dkdv_kernel (8 waves: row half, 32-key
 // sub-block, role; mirrored 64-key block pairs), but the two roles work one row tile apart, so
-// a step needs one barrier: at step s the role-0 wave computes S and P of tile s, hands P to its
-// role-1 partner through an LDS buffer of step parity s & 1 and adds dO^T P to dV^T, while the
-// role-1 wave computes dP of tile s - 1, dS with the P handed over one step earlier and adds
-// Q^T dS to dK^T.  The shifts by lse2 and by Delta ride on one extra k-step of the S and dP
+// a step needs one barrier: at step s the role-0 wave adds dO^T P of tile s - 1 to dV^T (P kept
+// in registers since the previous step), then computes S and P of tile s and hands P to its role-1
+// partner through an LDS buffer of step parity s & 1 -- its exponentials come last, while the
+// partner runs products -- and the role-1 wave computes dP of tile s - 1, dS with the P handed
+// over one step earlier and adds Q^T dS to dK^T.  The shifts by lse2 and by Delta ride on one extra k-step of the S and dP
 // products: the A operand carries three fp16 terms of -lse2 (or -Delta) of the lane's row
 // (fold_frag) against B = (256, 1, 1), so the accumulators come out as S - lse2 and
 // dP - Delta with fp32 accuracy and no per-element subtraction.  Row tiles go through a 4-stage
@@ -1504,6 +1505,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
         auto steps = [&](auto ROLE) {
         constexpr int RL = decltype(ROLE)::value;
         int natom = 0;  // AT: atomic adds this wave issued after its share of the latest fill
+        half8 pcar[2] = {};  // role 0: P of tile s, formed in step s, multiplied into dV^T in step s + 1
         for (int s = 0; s <= ntiles + (AT ? 1 : 0); ++s) {
             // tile s has landed (tile s + 1 may still be in flight); the P of tile s - 1 is in
             // pbuf[(s - 1) & 1]; every wave is done with tile s - 2 and with pbuf[s & 1]
@@ -1544,16 +1546,21 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
                         natom = NATOM;
                     }
                 }
+                // dV^T += dO^T P of tile s - 1 (P kept from the previous step), then S and P of tile s:
+                // the exponentials come last, while role 1 runs its products
+                if (s >= 1 && active(s - 1)) {
+                    const OP* Os1 = lds + ((s - 1) % NST) * 2 * TILE + TILE;
+                    half8 tf0[NDB];
+                    tr_frags0(Os1, tf0);
+                    product2(Os1, tf0, pcar, acc);
+                }
                 if (s < ntiles && active(s)) {
                     const int st = s % NST;
                     const OP* Qs = lds + st * 2 * TILE;
-                    const OP* Os = Qs + TILE;
                     const int Rh = rstart + s * BMR + 32 * rh;
                     const half8 fl = fold_frag(-rowv[st][0][32 * rh + c], h);  // ahead of the chain
                     floatx16 x = chain(Qs, IC<AT ? 1 : 0>{});
                     x = M::mma(fl, fw, x);  // S - lse2
-                    half8 tf0[NDB];
-                    tr_frags0(Os, tf0);  // in flight during the exponentials
                     if (needs_mask(s)) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
@@ -1561,14 +1568,12 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
                             if (row < keyG || row >= keyWG) x[r] = -INFINITY;
                         }
                     }
-                    half8 pf[2];
 #pragma unroll
                     for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) pf[cc][j] = (_Float16)__builtin_amdgcn_exp2f(x[8 * cc + j]);
-                        pbuf[s & 1][kq][rh][cc][l] = pf[cc];
+                        for (int j = 0; j < 8; ++j) pcar[cc][j] = (_Float16)__builtin_amdgcn_exp2f(x[8 * cc + j]);
+                        pbuf[s & 1][kq][rh][cc][l] = pcar[cc];
                     }
-                    product2(Os, tf0, pf, acc);
                 }
             } else {
                 if (AT && s >= 1 && !active(s - 1)) {  // this quadrant of dS^T is zero

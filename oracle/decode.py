@@ -14,14 +14,16 @@ max(0, p - W + 1) .. p (W <= 0: all of 0 .. p).  This is exactly row p of full c
 over the L_b + Tq tokens, which the tests use as one pin.
 
 Readings (as in ne_oracle.c): RoPE rotates adjacent pairs (2i, 2i+1) by +p*theta_i,
-theta_i = base^(-2i/D), base <= 0 disables it; scale 1/sqrt(D) after RoPE; query head h reads KV
+theta_i = base^(-2i/D), base <= 0 disables it (half_split: the pairs (i, i + D/2) instead, at the
+same angles); scale 1/sqrt(D) after RoPE; query head h reads KV
 head h // (Hq/Hkv); lse is the natural-log log-sum-exp of the scaled scores.
 """
 import numpy as np
 
 
-def rope_rows(x, positions, base):
-    """Rotate x[..., P, H, D] (P positions along axis -3) pairwise by positions * theta_i."""
+def rope_rows(x, positions, base, half_split=False):
+    """Rotate x[..., P, H, D] (P positions along axis -3) pairwise by positions * theta_i: pairs
+    (2i, 2i+1), or (i, i + D/2) with half_split."""
     x = np.asarray(x, dtype=np.float64)
     if base <= 0.0:
         return x.copy()
@@ -31,6 +33,9 @@ def rope_rows(x, positions, base):
     ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]   # [P, D/2]
     c = np.cos(ang)[:, None, :]                                               # [P, 1, D/2]
     s = np.sin(ang)[:, None, :]
+    if half_split:
+        a, b = x[..., :D // 2], x[..., D // 2:]
+        return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
     a, b = x[..., 0::2], x[..., 1::2]
     y = np.empty_like(x)
     y[..., 0::2] = a * c - b * s
@@ -43,12 +48,13 @@ def qk_norm_rows(x, gain, eps):
     return gain * x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
 
 
-def decode_fwd(q_new, k_seq, v_seq, lens, base, window=0, qk_norm=None):
+def decode_fwd(q_new, k_seq, v_seq, lens, base, window=0, qk_norm=None, half_split=False):
     """o [B][Tq][Hq][D], lse [B][Hq][Tq] for queries q_new [B][Tq][Hq][D] at positions lens[b] + t.
 
     k_seq[b], v_seq[b]: the raw (un-rotated) keys and values [L][Hkv][D] of sequence b at positions
     0 .. L - 1, L >= lens[b] + Tq (positions past lens[b] + Tq - 1 are never visible).
-    qk_norm (gain, eps): rows of q and k are normalised first (rows of the cache when appended)."""
+    qk_norm (gain, eps): rows of q and k are normalised first (rows of the cache when appended).
+    half_split: the rotation pairs (i, i + D/2)."""
     q_new = np.asarray(q_new, dtype=np.float64)
     B, Tq, Hq, D = q_new.shape
     o = np.zeros((B, Tq, Hq, D))
@@ -65,8 +71,8 @@ def decode_fwd(q_new, k_seq, v_seq, lens, base, window=0, qk_norm=None):
         qb = q_new[b]
         if qk_norm is not None:
             qb, k = qk_norm_rows(qb, *qk_norm), qk_norm_rows(k, *qk_norm)
-        qr = rope_rows(qb, pos, base)                # [Tq][Hq][D]
-        kr = rope_rows(k, np.arange(L), base)        # [L][Hkv][D]
+        qr = rope_rows(qb, pos, base, half_split)                # [Tq][Hq][D]
+        kr = rope_rows(k, np.arange(L), base, half_split)        # [L][Hkv][D]
         j = np.arange(L)
         vis = (j[None, :] <= pos[:, None])
         if window > 0:

@@ -21,9 +21,10 @@ import numpy as np
 from .decode import qk_norm_rows, rope_rows
 
 
-def qkv_rope_proj(x, w, Hq, Hkv, base, qk_norm=None, positions=None):
+def qkv_rope_proj(x, w, Hq, Hkv, base, qk_norm=None, positions=None, half_split=False):
     """Return (q', k', v) as float64 arrays [B][T][H][D]; positions (default 0 .. T-1) are those of
-    the T tokens given (a sample of a longer sequence may be checked by passing its positions)."""
+    the T tokens given (a sample of a longer sequence may be checked by passing its positions);
+    half_split: the rotation pairs (i, i + D/2) instead of (2i, 2i+1)."""
     x = np.asarray(x, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
     B, T, C = x.shape
@@ -38,6 +39,6 @@ def qkv_rope_proj(x, w, Hq, Hkv, base, qk_norm=None, positions=None):
     if qk_norm is not None:
         q, k = qk_norm_rows(q, *qk_norm), qk_norm_rows(k, *qk_norm)
     pos = np.arange(T) if positions is None else np.asarray(positions)
-    qr = np.stack([rope_rows(q[b], pos, base) for b in range(B)])
-    kr = np.stack([rope_rows(k[b], pos, base) for b in range(B)])
+    qr = np.stack([rope_rows(q[b], pos, base, half_split) for b in range(B)])
+    kr = np.stack([rope_rows(k[b], pos, base, half_split) for b in range(B)])
     return qr, kr, v

@@ -117,12 +117,28 @@ def test_rope_rows_matches_c_oracle_rotation():
     x = rng.standard_normal((1, 50, 3, 16))
     np.testing.assert_allclose(oracle.rope_rows(x[0], np.arange(50), 5e5)[None], oracle.rope(x, 5e5), rtol=0,
                                atol=1e-13)
+    np.testing.assert_allclose(oracle.rope_rows(x[0], np.arange(50), 5e5, half_split=True)[None],
+                               oracle.rope(x, 5e5, half_split=True), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("window,qkn", [(0, None), (6, None), (0, (1.2, 1e-6))])
+def test_half_split_decode_rows_equal_the_c_oracles_half_split_rows(window, qkn):
+    """The half-split pairing (i, i + D/2) in decode against the C oracle's full causal half-split
+    attention (pinned in test_oracle)."""
+    L, Tq, Hq, Hkv, D = 45, 4, 6, 2, 16
+    q, k, v = seq_case(L, Hq, Hkv, D, seed=91)
+    o, lse = oracle.decode_fwd(q[:, L - Tq:], [k[0]], [v[0]], [L - Tq], 1e4, window, qk_norm=qkn, half_split=True)
+    fo, flse = oracle.fwd(q, k, v, 1e4, window=window, qk_norm=qkn, half_split=True)
+    np.testing.assert_allclose(o[0], fo[0, L - Tq:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0], flse[0, :, L - Tq:], rtol=0, atol=1e-12)
 
 
 # ---- planted mistakes in a copy of oracle/decode.py --------------------------------------------
 MUTATIONS = {
     "query_position_not_offset": ("pos = int(lens[b]) + np.arange(Tq)", "pos = np.arange(Tq)"),
-    "keys_rotated_by_query_positions": ("kr = rope_rows(k, np.arange(L), base)", "kr = rope_rows(k, L - 1 - np.arange(L), base)"),
+    "keys_rotated_by_query_positions": ("kr = rope_rows(k, np.arange(L), base, half_split)",
+                                        "kr = rope_rows(k, L - 1 - np.arange(L), base, half_split)"),
+    "half_split_halves_swapped": ("a, b = x[..., :D // 2], x[..., D // 2:]", "a, b = x[..., D // 2:], x[..., :D // 2]"),
     "window_off_by_one": ("(pos[:, None] - j[None, :]) < window", "(pos[:, None] - j[None, :]) <= window"),
     "causal_mask_dropped": ("vis = (j[None, :] <= pos[:, None])", "vis = (j[None, :] <= 0 * pos[:, None] + L - 1)"),
     "rotation_sign": ("y[..., 1::2] = a * s + b * c", "y[..., 1::2] = -a * s + b * c"),
@@ -148,6 +164,12 @@ def decode_battery(fn):
         fo, flse = oracle.fwd(q, k, v, base, window=window)
         if not (np.max(np.abs(o[0] - fo[0, L - Tq:])) < 1e-10 and np.max(np.abs(lse[0] - flse[0, :, L - Tq:])) < 1e-10):
             failed += 1
+    # the half-split pairing against the C oracle's
+    q, k, v = seq_case(44, 4, 2, 16, seed=44)
+    o, lse = fn(q[:, 40:], [k[0]], [v[0]], [40], 1e4, 0, half_split=True)
+    fo, flse = oracle.fwd(q, k, v, 1e4, half_split=True)
+    if not (np.max(np.abs(o[0] - fo[0, 40:])) < 1e-10 and np.max(np.abs(lse[0] - flse[0, :, 40:])) < 1e-10):
+        failed += 1
     return failed
 
 

@@ -51,6 +51,10 @@ def test_rotation_equals_the_c_oracle_rotation():
     np.testing.assert_allclose(q, oracle.rope(q0, 5e5), rtol=0, atol=1e-12)
     np.testing.assert_allclose(k, oracle.rope(k0, 5e5), rtol=0, atol=1e-12)
     np.testing.assert_array_equal(v, v0)
+    qh, kh, vh = oracle.qkv_rope_proj(x, w, Hq, Hkv, 5e5, half_split=True)
+    np.testing.assert_allclose(qh, oracle.rope(q0, 5e5, half_split=True), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(kh, oracle.rope(k0, 5e5, half_split=True), rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(vh, v0)
 
 
 @pytest.mark.parametrize("qkn", [None, (1.2, 1e-6)])

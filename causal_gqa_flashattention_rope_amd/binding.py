@@ -32,15 +32,15 @@ EXPORTS = ("ne_rope_attn_workspace_bytes", "ne_rope_table_init", "ne_rope_table_
 class AttnOpts(ctypes.Structure):
     """ne_attn_opts_t: window (<= 0: causal prefix), QK norm (on, gain, eps)."""
     _fields_ = [("window", ctypes.c_int), ("qk_norm", ctypes.c_int), ("qk_gain", ctypes.c_float),
-                ("qk_eps", ctypes.c_float)]
+                ("qk_eps", ctypes.c_float), ("rope_half_split", ctypes.c_int)]
 
 
-def make_opts(window=0, qk_norm=None):
-    """qk_norm: None or (gain, eps)."""
+def make_opts(window=0, qk_norm=None, rope_half_split=False):
+    """qk_norm: None or (gain, eps); rope_half_split: RoPE pairs (i, i + D/2)."""
     if qk_norm is None:
-        return AttnOpts(int(window), 0, 1.0, 0.0)
+        return AttnOpts(int(window), 0, 1.0, 0.0, int(bool(rope_half_split)))
     gain, eps = qk_norm
-    return AttnOpts(int(window), 1, float(gain), float(eps))
+    return AttnOpts(int(window), 1, float(gain), float(eps), int(bool(rope_half_split)))
 
 
 class NeError(RuntimeError):
@@ -267,12 +267,12 @@ def _lens_arg(lens, B, device):
     return torch.tensor(list(lens), dtype=torch.int32, device=device)
 
 
-def ne_kv_cache_append(cache, cache_lens, k_new, v_new, Tcap, rope_base, qk_norm=None):
+def ne_kv_cache_append(cache, cache_lens, k_new, v_new, Tcap, rope_base, qk_norm=None, rope_half_split=False):
     """Write k_new, v_new [B, Tn, Hkv, D] at positions cache_lens[b] .. of the cache."""
     _require_gpu(cache, k_new, v_new)
     B, Tn, Hkv, D = k_new.shape
     lens = _lens_arg(cache_lens, B, k_new.device)
-    opts = make_opts(0, qk_norm)
+    opts = make_opts(0, qk_norm, rope_half_split)
     _check(lib().ne_kv_cache_append(_ptr(cache), cache.numel() * cache.element_size(), _ptr(lens), _ptr(k_new),
                                     _ptr(v_new), B, Tn, Tcap, Hkv, D, float(rope_base), ctypes.byref(opts),
                                     _DT[k_new.dtype], _stream()))
@@ -284,7 +284,7 @@ def decode_workspace_bytes(B, Tq, Tcap, Hq, Hkv, D, in_dtype):
 
 
 def ne_rope_attn_decode(q, cache, cache_lens, Tcap, Hkv, rope_base, window=0, out_dtype=torch.float32,
-                        o=None, lse=None, workspace=None, events=None, qk_norm=None):
+                        o=None, lse=None, workspace=None, events=None, qk_norm=None, rope_half_split=False):
     """o, lse for the queries q [B, Tq, Hq, D] at positions cache_lens[b] + t against the cache.
 
     events: optional 4 events (or None entries) around the two launches."""
@@ -297,7 +297,7 @@ def ne_rope_attn_decode(q, cache, cache_lens, Tcap, Hkv, rope_base, window=0, ou
         lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = alloc_workspace(decode_workspace_bytes(B, Tq, Tcap, Hq, Hkv, D, q.dtype), q.device)
-    opts = make_opts(window, qk_norm)
+    opts = make_opts(window, qk_norm, rope_half_split)
     _check(lib().ne_rope_attn_decode(_ptr(q), _ptr(cache), cache.numel() * cache.element_size(), _ptr(lens),
                                      _ptr(o), _ptr(lse), B, Tq, Tcap, Hq, Hkv, D, float(rope_base), ctypes.byref(opts),
                                      _DT[q.dtype], _DT[o.dtype], _ptr(workspace),
@@ -310,7 +310,7 @@ DECODE_SCRATCH_BYTES = 64 << 20
 
 
 def ne_rope_attn_decode_noalloc(q, cache, cache_lens, Tcap, Hkv, rope_base, window=0, out_dtype=torch.float32,
-                                o=None, lse=None, qk_norm=None):
+                                o=None, lse=None, qk_norm=None, rope_half_split=False):
     """ne_rope_attn_decode without a workspace: the split partials go to the library's own scratch
     (DECODE_SCRATCH_BYTES per GPU); shapes that need more are rejected.  Pass o and lse to make the
     call allocate nothing at all."""
@@ -321,7 +321,7 @@ def ne_rope_attn_decode_noalloc(q, cache, cache_lens, Tcap, Hkv, rope_base, wind
         o = torch.empty((B, Tq, Hq, D), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
-    opts = make_opts(window, qk_norm)
+    opts = make_opts(window, qk_norm, rope_half_split)
     _check(lib().ne_rope_attn_decode_noalloc(_ptr(q), _ptr(cache), _nbytes(cache), _ptr(lens), _ptr(o), _ptr(lse),
                                              B, Tq, Tcap, Hq, Hkv, D, float(rope_base), ctypes.byref(opts),
                                              _DT[q.dtype], _DT[o.dtype], _stream()))
@@ -332,7 +332,7 @@ def ne_rope_attn_decode_noalloc(q, cache, cache_lens, Tcap, Hkv, rope_base, wind
 # QKV projection with the RoPE epilogue.
 # ---------------------------------------------------------------------------------------------
 def ne_qkv_rope_proj(x, w, Hq, Hkv, rope_base, qk_norm=None, out_dtype=torch.float32, q=None, k=None, v=None,
-                     workspace=None, events=None):
+                     workspace=None, events=None, rope_half_split=False):
     """q', k', v from x [B, T, C] and w [(Hq + 2 Hkv) D, C]: y = x w^T, RoPE (after the optional QK norm)
     applied to the query and key heads in the product's epilogue."""
     _require_gpu(x, w)
@@ -349,7 +349,7 @@ def ne_qkv_rope_proj(x, w, Hq, Hkv, rope_base, qk_norm=None, out_dtype=torch.flo
         v = torch.empty((B, T, Hkv, D), dtype=out_dtype, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(int(lib().ne_qkv_rope_workspace_bytes(T, D)), x.device)
-    opts = make_opts(0, qk_norm)
+    opts = make_opts(0, qk_norm, rope_half_split)
     _check(lib().ne_qkv_rope_proj(_ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v), B, T, C, Hq, Hkv, D, float(rope_base),
                                   ctypes.byref(opts), _DT[x.dtype], _DT[q.dtype], _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(), _events_arg(events, 4)))

@@ -452,7 +452,8 @@ ne_status_t ne_rope_attn_fwd_ex(const void* q, const void* k, const void* v, voi
                                 int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
                                 const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                                 void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
-    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, opts, in_dtype, out_dtype, flags,
+    const unsigned fl = flags | (opts && opts->rope_half_split ? NE_FLAG_ROPE_HALF_SPLIT : 0u);
+    return fwd_impl(q, k, v, o, lse, B, T, Hq, Hkv, head_dim, rope_base, opts, in_dtype, out_dtype, fl,
                     workspace, workspace_bytes, stream, events);
 }
 
@@ -461,8 +462,9 @@ ne_status_t ne_rope_attn_bwd_ex(const void* q, const void* k, const void* v, con
                                 int B, int T, int Hq, int Hkv, int head_dim, double rope_base,
                                 const ne_attn_opts_t* opts, ne_dtype_t in_dtype, ne_dtype_t out_dtype, unsigned flags,
                                 void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    const unsigned fl = flags | (opts && opts->rope_half_split ? NE_FLAG_ROPE_HALF_SPLIT : 0u);
     return bwd_impl(q, k, v, o, lse, dO, dq, dk, dv, B, T, Hq, Hkv, head_dim, rope_base, opts, in_dtype,
-                    out_dtype, flags, workspace, workspace_bytes, stream, events);
+                    out_dtype, fl, workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"
@@ -565,6 +567,7 @@ ne_status_t ne_kv_cache_append(void* cache, size_t cache_bytes, const int* cache
     a.qkn = qkn;
     a.k = k_new; a.v = v_new; a.cache = cache; a.lens = cache_lens;
     a.B = B; a.Tn = Tn; a.Tcap = Tcap; a.Hkv = Hkv; a.rope_base = rope_base;
+    a.half = opts && opts->rope_half_split && rope_base > 0.0 ? 1 : 0;
     for (int i = 0; i < head_dim / 2; ++i)
         a.theta[i] = rope_base > 0.0 ? std::pow(rope_base, -2.0 * i / head_dim) : 0.0;
     hipError_t e = ne::launch_append((int)in_dtype, head_dim, a, (hipStream_t)stream);
@@ -629,6 +632,7 @@ ne_status_t decode_impl(const void* q, const void* cache, size_t cache_bytes, co
     a.window = visible_keys(opts->window, Tcap);
     a.qkn = qkn;
     a.rope_base = rope_base;
+    a.half = opts->rope_half_split && rope_base > 0.0 ? 1 : 0;
     a.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
     for (int i = 0; i < head_dim / 2; ++i)
         a.theta[i] = rope_base > 0.0 ? std::pow(rope_base, -2.0 * i / head_dim) : 0.0;
@@ -701,6 +705,7 @@ ne_status_t ne_qkv_rope_proj(const void* x, const void* w, void* q, void* k, voi
     a.x = x; a.w = w; a.q = q; a.k = k; a.v = v; a.table = (float2*)workspace;
     a.M = (int)M; a.C = C; a.N = (int)N; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.D = head_dim;
     a.rope_base = rope_base; a.qkn = qkn;
+    a.half = opts && opts->rope_half_split && rope_base > 0.0 ? 1 : 0;
     for (int i = 0; i < head_dim / 2; ++i)
         a.theta[i] = rope_base > 0.0 ? std::pow(rope_base, -2.0 * i / head_dim) : 0.0;
     hipError_t e = ne::launch_qkv((int)in_dtype, (int)out_dtype, head_dim, a, (hipStream_t)stream,

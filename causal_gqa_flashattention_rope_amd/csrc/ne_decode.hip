@@ -9,7 +9,9 @@
 //   V' block: for load (kk < 2, db < D / 32) and lane l, 16 bytes: fp16(v) at d = 32 db + l % 32 of
 //             the 8 keys 16 kk + vt_key_of_pos(8 (l / 32) + j), j < 8: the A operand of
 //             O^T += V'^T P^T for k-step kk, in the order the S^T accumulator hands P over.
-// Every 16-byte load of the decode kernel is thus one lane's part of a contiguous 1 KiB.
+// Every 16-byte load of the decode kernel is thus one lane's part of a contiguous 1 KiB.  With the
+// half-split rotary pairs (i, i + D/2) the key's elements i and i + D/2 take dimensions 2i and 2i + 1
+// of this layout, and the decode gathers its queries in the same order (scores are sums over them).
 //
 // Decode is bound by reading the cache, which no two workgroups share, so the kernels stream it
 // from HBM straight into registers (no LDS staging) and spread every group's keys over many
@@ -88,7 +90,16 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
         const int tl = idx / CPR, chunk = idx % CPR, t = t0 + tl;
         const size_t in_off = (((size_t)b * Tn + min(t, Tn - 1)) * a.Hkv + hkv) * D + chunk * 8;
         float x[8];
-        load8_in((const TI*)a.k + in_off, x);
+        if (a.half) {   // half-split pairs: slot 2i takes element i, slot 2i + 1 element i + D/2
+            const TI* row = (const TI*)a.k + (in_off - chunk * 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                x[2 * q] = to_f32(row[chunk * 4 + q]);
+                x[2 * q + 1] = to_f32(row[D / 2 + chunk * 4 + q]);
+            }
+        } else {
+            load8_in((const TI*)a.k + in_off, x);
+        }
         float fac = 1.f;  // QK norm of this key row (its chunks sit in consecutive lanes)
         if (a.qkn.on) {
             float ss = 0.f;
@@ -191,7 +202,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         half8 out = half8{};
         const int Rr = R0 + min(r, nvalid - 1), t = Rr / G, hq = hkv * G + (Rr - t * G);
         float x[8];
-        load8_in((const TI*)a.q + (((size_t)b * Tq + t) * a.Hq + hq) * D + chunk * 8, x);
+        const TI* qrow = (const TI*)a.q + (((size_t)b * Tq + t) * a.Hq + hq) * D;
+        if (a.half) {   // half-split pairs, in the slot order of the cached keys
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                x[2 * q] = to_f32(qrow[chunk * 4 + q]);
+                x[2 * q + 1] = to_f32(qrow[D / 2 + chunk * 4 + q]);
+            }
+        } else {
+            load8_in(qrow + chunk * 8, x);
+        }
         float mul = a.qscale;  // times the QK norm of this query row (its chunks in consecutive lanes)
         if (a.qkn.on) {
             float ss = 0.f;

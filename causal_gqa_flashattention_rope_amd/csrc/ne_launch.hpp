@@ -154,6 +154,7 @@ struct AppendArgs {
     int B, Tn, Tcap, Hkv;
     QkNorm qkn;
     double rope_base;
+    int half;                                       // half-split pairs: keys stored in slot order
     double theta[64];                               // base^(-2i/D), i < D/2 (RoPE on)
 };
 
@@ -168,6 +169,7 @@ struct DecodeArgs {
     double rope_base;
     float qscale;                                   // softmax scale * log2(e)
     QkNorm qkn;
+    int half;                                       // half-split pairs: queries gathered into slots
     double theta[64];                               // base^(-2i/D), i < D/2 (RoPE on)
 };
 
@@ -179,6 +181,7 @@ struct QkvArgs {
     int M, C, N, T, Hq, Hkv, D;
     double rope_base;
     QkNorm qkn;
+    int half;                                       // half-split pairs (i, i + D/2)
     double theta[64];                               // base^(-2i/D), i < D/2 (RoPE on)
 };
 

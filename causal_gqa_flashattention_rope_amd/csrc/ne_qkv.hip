@@ -190,7 +190,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_QKV_WPE)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) y[f][r] *= fac;
             }
-            if (qk && rope) {
+            if (qk && rope && a.half) {
+                // half-split pairs (i, i + D/2): both in this lane -- feature block f + FPH / 2 for
+                // D >= 64, the same block 16 features on (q4 + 2) for D = 32
+                const float2* cs = a.table + (size_t)t * (D / 2);
+                constexpr int FL = FPH >= 2 ? FPH / 2 : 1, QL = FPH >= 2 ? 4 : 2;
+#pragma unroll
+                for (int f = 0; f < FL; ++f)
+#pragma unroll
+                    for (int q4 = 0; q4 < QL; ++q4)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = 32 * f + 8 * q4 + 4 * h + e;   // < D / 2
+                            const int fh = FPH >= 2 ? f + FPH / 2 : f, rh = FPH >= 2 ? 4 * q4 + e : 4 * (q4 + 2) + e;
+                            const float2 r = cs[i];
+                            const float u = y[f][4 * q4 + e], v = y[fh][rh];
+                            y[f][4 * q4 + e] = u * r.x - v * r.y;
+                            y[fh][rh] = u * r.y + v * r.x;
+                        }
+            } else if (qk && rope) {
                 const float2* cs = a.table + (size_t)t * (D / 2);
 #pragma unroll
                 for (int f = 0; f < FPH; ++f)
@@ -422,9 +440,10 @@ hipError_t launch_qkv_t(const QkvArgs& a, hipStream_t s, hipEvent_t const* ev) {
     // half the rate of whole 128-byte rows.
     const int cus3 = 3 * cu_count();
     const int t320 = (a.M + 255) / 256 * ((a.N + 319) / 320), t640 = (a.M + 127) / 128 * ((a.N + 639) / 640);
-    if ((!a.qkn.on || 320 % D == 0) && 4 * t320 >= cus3) {
+    // the half-split pairs of a head sit in one lane only in the narrow tiling
+    if (!a.half && (!a.qkn.on || 320 % D == 0) && 4 * t320 >= cus3) {
         hipLaunchKernelGGL((qkv_wide_kernel<TI, TO, D, 4, 64, 2>), dim3(t320), dim3(512), 0, s, a);
-    } else if (4 * t640 >= cus3) {
+    } else if (!a.half && 4 * t640 >= cus3) {
         hipLaunchKernelGGL((qkv_wide_kernel<TI, TO, D, 2, 32, 3>), dim3(t640), dim3(512), 0, s, a);
     } else {
         const int grid = (a.M + 255) / 256 * (a.N / 128);

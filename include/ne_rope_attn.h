@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define NE_ABI_VERSION 2
+#define NE_ABI_VERSION 3
 
 typedef enum { NE_F32 = 0, NE_BF16 = 1, NE_F16 = 2 } ne_dtype_t;
 
@@ -189,6 +189,11 @@ typedef struct {
                        backward returns gradients with respect to the raw q and k                     */
     float qk_gain;  /* 1.2 in the guide; finite                                                       */
     float qk_eps;   /* added to the mean square; finite, >= 0 (0 with an all-zero row: non-finite)    */
+    int rope_half_split; /* nonzero: RoPE rotates element i with element i + head_dim/2 (the pairing of
+                       NE_FLAG_ROPE_HALF_SPLIT, which the fwd / bwd calls also take as a flag).  The
+                       KV cache holds keys rotated with the pairing of its appends, so appends and
+                       decodes must agree; the QKV projection then runs its narrower tiling (the
+                       pairs of a head are in one lane only there).                                   */
 } ne_attn_opts_t;
 
 /* The forward and backward with every option (window and QK norm) and, for measurement, HIP events:
@@ -232,7 +237,9 @@ ne_status_t ne_rope_attn_bwd_ex(const void* q, const void* k, const void* v,
  * layout: for each (b, kv head) group g = b * Hkv + h, its Tcap / 32 tiles of 32 positions, tile i
  * at element offset (g * Tcap / 32 + i) * 64 * head_dim, each holding
  *   keys after RoPE (fp16): for u < head_dim / 16 and lane l < 64, 8 elements: key i * 32 + l % 32,
- *     dimensions 16 u + 8 (l / 32) .. + 7, at element (u * 64 + l) * 8 of the tile;
+ *     dimensions 16 u + 8 (l / 32) .. + 7, at element (u * 64 + l) * 8 of the tile (appended with
+ *     opts->rope_half_split, "dimension" 2m holds element m of the rotated key and 2m + 1 element
+ *     m + head_dim / 2: the slot order the decode then gives its queries too);
  *   values (fp16), from element 32 * head_dim of the tile: for kk < 2, db < head_dim / 32 and lane
  *     l, 8 elements: dimension 32 db + l % 32 of the keys i * 32 + 16 kk + s(8 (l / 32) + j),
  *     j < 8, at element ((kk * head_dim / 32 + db) * 64 + l) * 8 + j, where s swaps bits 2 and 3

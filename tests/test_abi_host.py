@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.ne_abi_version() == 2
+    assert L.ne_abi_version() == 3
     names = [L.ne_status_str(st) for st in range(8)]
     assert len(set(names)) == 8 and all(names)
     assert b"table" in names[6] and b"HIP" in names[7]

@@ -4,16 +4,21 @@ i + D/2 by t * theta_i) against the oracle's half-split path; needs an MI355X.
 Bars as in test_gpu_parity (2e-3 of each output's scale with 16-bit inputs, 1e-5 on the fp32 path;
 16-bit outputs add half an ulp).  The library runs its adjacent-pair kernels on rows whose slots hold
 the elements in the order i -> 2i, i + D/2 -> 2i + 1, so a half-split call must give bitwise the
-results of an adjacent-pair call on inputs reordered that way (gradients reordered back); the last
-test checks exactly that.
+results of an adjacent-pair call on inputs reordered that way (gradients reordered back), which one
+test checks exactly.  The options field rope_half_split carries the same pairing to the _ex calls
+(bitwise the flag's results), to the KV-cache append and decode (against the decode oracle's
+half-split path) and to the QKV projection (against its oracle).
 """
-import numpy as np
+import ctypes
+
 import pytest
 import torch
 
 import oracle
 from causal_gqa_flashattention_rope_amd import binding, inputs
+from tests.test_gpu_decode import seqs
 from tests.test_gpu_parity import ATOMIC, DEV, STORE_DS, check, f64, zero_ref_scale
+from tests.test_gpu_qkv import check_qkv, make
 
 pytestmark = pytest.mark.gpu
 
@@ -105,3 +110,81 @@ def test_half_split_without_rope_is_the_plain_call():
     a = _run(q, k, v, dO, 0.0, torch.float32, 0, 0, None)
     for x, y in zip(h, a):
         assert torch.equal(x, y)
+
+
+# ---- the same pairing through the options struct: KV cache, decode, QKV projection -----------------
+
+
+def test_options_field_equals_the_flag():
+    """ne_attn_opts_t.rope_half_split on the _ex calls gives the bits of NE_FLAG_ROPE_HALF_SPLIT."""
+    B, T, Hq, Hkv, D = 1, 300, 6, 2, 64
+    q, k, v, dO = (t.to(DEV) for t in inputs.random_case(B, T, Hq, Hkv, D, seed=902, dtype="bf16"))
+    ws = binding.new_workspace(True, q, k, 1e4, HALF)
+    o1, l1 = binding.ne_rope_attn_fwd(q, k, v, 1e4, workspace=ws, flags=HALF, window=T // 2)
+    g1 = [t.clone() for t in binding.ne_rope_attn_bwd(q, k, v, o1, l1, dO, 1e4, workspace=ws, flags=HALF,
+                                                       window=T // 2)]
+    o1, l1 = o1.clone(), l1.clone()
+    opts = binding.make_opts(T // 2, None, rope_half_split=True)
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    L = binding.lib()
+    rc = L.ne_rope_attn_fwd_ex(binding._ptr(q), binding._ptr(k), binding._ptr(v), binding._ptr(o2), binding._ptr(l2),
+                               B, T, Hq, Hkv, D, 1e4, ctypes.byref(opts), binding._DT[q.dtype],
+                               binding._DT[o2.dtype], 0, binding._ptr(ws), binding._nbytes(ws), binding._stream(), None)
+    assert rc == 0
+    g2 = [torch.empty_like(t) for t in g1]
+    rc = L.ne_rope_attn_bwd_ex(binding._ptr(q), binding._ptr(k), binding._ptr(v), binding._ptr(o2), binding._ptr(l2),
+                               binding._ptr(dO), *(binding._ptr(t) for t in g2), B, T, Hq, Hkv, D, 1e4,
+                               ctypes.byref(opts), binding._DT[q.dtype], binding._DT[o2.dtype], 0, binding._ptr(ws),
+                               binding._nbytes(ws), binding._stream(), None)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("case", [
+    # B, P, Tq, Hq, Hkv, D, lens, window, in, out, QK norm
+    (3, 200, 1, 8, 2, 128, [0, 57, 199], 0, torch.bfloat16, torch.float32, None),
+    (2, 300, 5, 12, 4, 64, [10, 295], 0, torch.bfloat16, torch.bfloat16, None),
+    (1, 640, 1, 4, 4, 32, [639], 100, torch.float16, torch.float32, None),
+    (2, 256, 9, 6, 2, 128, [100, 247], 64, torch.bfloat16, torch.float32, QKN),
+])
+def test_half_split_decode_parity(case):
+    B, P, Tq, Hq, Hkv, D, lens, window, in_dt, out_dt, qkn = case
+    Tcap = (P + 63) // 64 * 64
+    base = 1e4
+    q, k, v = seqs(B, P, Hq, Hkv, D, 610, _NAME[in_dt])
+    cache = binding.new_kv_cache(B, Tcap, Hkv, D, k.dtype, DEV)
+    kd, vd = k.to(DEV), v.to(DEV)
+    for p0 in range(0, P, 64):
+        n = min(64, P - p0)
+        lens0 = torch.full((B,), p0, dtype=torch.int32, device=DEV)
+        binding.ne_kv_cache_append(cache, lens0, kd[:, p0:p0 + n].contiguous(), vd[:, p0:p0 + n].contiguous(), Tcap,
+                                   base, qk_norm=qkn, rope_half_split=True)
+    q_new = torch.stack([q[b, lens[b]:lens[b] + Tq] for b in range(B)]).to(DEV)
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o, lse = binding.ne_rope_attn_decode(q_new, cache, lens_d, Tcap, Hkv, base, window, out_dtype=out_dt, qk_norm=qkn,
+                                         rope_half_split=True)
+    o2, lse2 = binding.ne_rope_attn_decode_noalloc(q_new, cache, lens_d, Tcap, Hkv, base, window, out_dtype=out_dt,
+                                                   qk_norm=qkn, rope_half_split=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    ro, rlse = oracle.decode_fwd(f64(q_new.cpu()), [f64(k[b]) for b in range(B)], [f64(v[b]) for b in range(B)], lens,
+                                 base, window, qk_norm=qkn, half_split=True)
+    check("o", o.cpu(), ro, in_dt, out_dt)
+    check("lse", lse.cpu(), rlse, in_dt, out_dt)
+
+
+@pytest.mark.parametrize("shape", [(2, 100, 128, 4, 2, 32), (1, 300, 256, 6, 1, 64), (2, 129, 192, 4, 2, 128),
+                                   (1, 8100, 64, 12, 4, 128)])
+@pytest.mark.parametrize("qkn", [None, QKN])
+def test_half_split_qkv_parity(shape, qkn):
+    B, T, C, Hq, Hkv, D = shape
+    x, w = make(B, T, C, Hq, Hkv, D, 5100 + T, "bf16")
+    q, k, v = binding.ne_qkv_rope_proj(x.to(DEV), w.to(DEV), Hq, Hkv, 1e4, qk_norm=qkn, rope_half_split=True)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_rope_proj(f64(x), f64(w), Hq, Hkv, 1e4, qk_norm=qkn, half_split=True)
+    for nm, g, r in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        check_qkv(nm, g.cpu(), r, torch.float32)

@@ -153,6 +153,27 @@ def test_parity_split_row_blocks(shape, dtypes):
         assert torch.equal(a, b)
 
 
+# Group extremes: 16 to 64 query heads per KV head (one or two KV heads), where a 64-row tile of the
+# flattened rows t * G + h holds four positions or fewer (one at G = 64) and every key block's first
+# row tile carries its diagonal for all heads; and many (batch, KV head) groups of a few positions,
+# where most tiles are partial and the launch holds more blocks than the chip has slots.
+GROUP_EXTREMES = [(1, 150, 16, 1, 128), (2, 70, 32, 1, 64), (1, 45, 64, 1, 32), (1, 97, 32, 2, 128),
+                  (16, 3, 8, 8, 128), (4, 33, 64, 16, 64)]
+GROUP_VARIANTS = [(torch.bfloat16, torch.float32, f) for f in BWD_FLAGS] + [
+    (torch.float16, torch.float16, 0), (torch.float32, torch.float32, 0)]
+
+
+@pytest.mark.parametrize("shape", GROUP_EXTREMES, ids=lambda s: "B%dT%dHq%dHkv%dD%d" % s)
+@pytest.mark.parametrize("variant", GROUP_VARIANTS,
+                         ids=["bf16-f32-" + i for i in BWD_IDS] + ["f16-f16-recompute", "f32-f32"])
+def test_parity_group_extremes(shape, variant):
+    in_dt, out_dt, flags = variant
+    B, T, Hq, Hkv, D = shape
+    q, k, v, dO = inputs.random_case(B, T, Hq, Hkv, D, seed=4000 + T + Hq,
+                                     dtype={torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[in_dt])
+    parity(q, k, v, dO, 1.0e4, out_dt, in_dt, flags=flags)
+
+
 def ds_group_bytes(T, G):
     nrt, nkb = -(-T * G // 64), -(-T // 64)
     return sum(1 for kb in range(nkb) for rt in range(nrt) if rt >= kb * G) * 8192

@@ -61,7 +61,7 @@ typedef enum {
                                  for fp32 inputs, else 2 -- a KV group's rows are addressed
                                  with 32-bit byte offsets)                                   */
     NE_ERR_UNSUPPORTED = 3,   /* head_dim not in {32, 64, 128}, dtype pair not supported, or a
-                                 flag this build does not implement                         */
+                                 flag the library does not implement                        */
     NE_ERR_ALIGN = 4,         /* a pointer is not 16-byte aligned                             */
     NE_ERR_WORKSPACE = 5,     /* workspace_bytes smaller than ne_rope_attn_workspace_bytes()  */
     NE_ERR_NO_ROPE_TABLE = 6, /* the workspace holds no cos/sin table for (T, head_dim,

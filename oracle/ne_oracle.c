@@ -27,7 +27,7 @@
  *     list entry on window_pattern: "S" layers see a quarter of the context, "L" layers
  *     the full context.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   RoPE pairs adjacent elements (2i, 2i+1) and rotates them by +t*theta_i with
  *   theta_i = base^(-2i/D), positions t = 0..T-1, over the whole head dimension;
  *   base <= 0 disables RoPE.  Softmax scale 1/sqrt(D) applied after RoPE.  Key j

@@ -68,6 +68,10 @@ __device__ __forceinline__ float sum_lanes(float x, int n) {
 __device__ __forceinline__ bool visible(int j, int t, int W) { return (unsigned)(t - j) < (unsigned)W; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// The wave index within the workgroup, read into a scalar register: every value derived from it
+// (role, row half, fill counts) is then wave-uniform to the compiler, so branches on it are
+// scalar branches and its arithmetic stays out of the vector registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ---- storage element conversions ------------------------------------------------------
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -300,7 +304,7 @@ __device__ __forceinline__ void lds_fill(OP* tile, const OP* src, int n0, int nr
     constexpr int CHUNKS = ROWS * TL::CPR;
     constexpr int WL = CHUNKS / 64;                    // 1 KiB wave loads per tile
     static_assert(CHUNKS % 64 == 0, "tile must be a whole number of wave loads");
-    const int l = lane_id(), w = threadIdx.x >> 6;
+    const int l = lane_id(), w = wave_id();
 #pragma unroll
     for (int i = 0; i < (WL + NW - 1) / NW; ++i) {
         const int j = i * NW + w;                      // wave load index (uniform per wave)
@@ -419,7 +423,7 @@ __device__ __forceinline__ constexpr int lds_fill_vt_count(int w) {
 template <int D, int BN, int NW>
 __device__ __forceinline__ void lds_fill_vt(_Float16* tile, const _Float16* src, int n0, int Tp) {
     constexpr int CPR = BN / 8, WL = D * CPR / 64;     // 1 KiB wave loads per tile
-    const int l = lane_id(), w = threadIdx.x >> 6;
+    const int l = lane_id(), w = wave_id();
 #pragma unroll
     for (int i = 0; i < (WL + NW - 1) / NW; ++i) {
         const int j = i * NW + w;
@@ -439,7 +443,7 @@ __device__ __forceinline__ void lds_fill_at(unsigned tile, const OP* src, int n0
     constexpr int CHUNKS = ROWS * TL::CPR;
     constexpr int WL = CHUNKS / 64;
     static_assert(CHUNKS % 64 == 0, "tile must be a whole number of wave loads");
-    const int l = lane_id(), w = threadIdx.x >> 6;
+    const int l = lane_id(), w = wave_id();
 #pragma unroll
     for (int i = 0; i < (WL + NW - 1) / NW; ++i) {
         const int j = i * NW + w;
@@ -454,7 +458,7 @@ __device__ __forceinline__ void lds_fill_at(unsigned tile, const OP* src, int n0
 template <int D, int BN, int NW>
 __device__ __forceinline__ void lds_fill_vt_at(unsigned tile, const _Float16* src, int n0, int Tp) {
     constexpr int CPR = BN / 8, WL = D * CPR / 64;
-    const int l = lane_id(), w = threadIdx.x >> 6;
+    const int l = lane_id(), w = wave_id();
 #pragma unroll
     for (int i = 0; i < (WL + NW - 1) / NW; ++i) {
         const int j = i * NW + w;

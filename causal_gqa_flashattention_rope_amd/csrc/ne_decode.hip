@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int nsplit = a.nsplit, nrb = a.nrb;
     const int s = blockIdx.x % nsplit, rb = (blockIdx.x / nsplit) % nrb, g = blockIdx.x / (nsplit * nrb);
     const int b = g / a.Hkv, hkv = g % a.Hkv;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, c = l & 31;
     const int Tq = a.Tq, G = a.G, TqG = Tq * G, Tcap = a.Tcap, W = a.window;
     const int len = cache_len(a.lens, b, Tq, Tcap), L = len + Tq;
 

@@ -533,7 +533,7 @@ void fwd_kernel(FwdArgs a) {
     const Work wk = map_block(a.nrb, a.B * a.Hkv, true);
     const int rb = wk.blk;
     const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, c = l & 31;
     const int R0 = rb * BM;
     const int Rw = R0 + 32 * w;
     const int R = Rw + c;
@@ -721,7 +721,7 @@ void fwd_kernel_h(FwdArgs a, SplitPlan sp) {
     const RowJob job = map_row_job<SPLIT>(sp, a.nrb, a.B * a.Hkv);
     const int rb = job.rb;
     const int hkv = job.grp % a.Hkv, b = job.grp / a.Hkv;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, c = l & 31;
     const int R0 = rb * BM;
     const int Rw = R0 + 32 * w;
     const int R = Rw + c;
@@ -1072,7 +1072,7 @@ void dkdv_kernel(BwdArgs a) {
     const int npair = (nkb + 1) / 2;
     const Work wk = map_block(npair, a.B * a.Hkv, false);
     const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, c = l & 31;
     // waves w and w + 4 (one per role, same row half and key sub-block) share a SIMD, so the
     // exp/VALU phase of one overlaps the MFMA phase of the other
     const int rh = w & 1, kq = (w >> 1) & 1, role = w >> 2;
@@ -1362,7 +1362,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
     }
     const int gg = a.grp0 + wk.grp;                   // the (batch, KV head) group
     const int hkv = gg % a.Hkv, b = gg / a.Hkv;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, c = l & 31;
     // waves w and w + 4 (same row half and key sub-block, the two roles) share a SIMD
     const int rh = w & 1, kq = (w >> 1) & 1, role = w >> 2;
     const int per_fill = 2 * lds_fill_count<OP, D, BMR, NW>(w) + (w < 2 ? 1 : 0);  // loads per fill
@@ -1800,7 +1800,7 @@ void dq_kernel(BwdArgs a) {
     const Work wk = map_block(a.nrb, a.B * a.Hkv, true);
     const int rb = wk.blk;
     const int hkv = wk.grp % a.Hkv, b = wk.grp / a.Hkv;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, c = l & 31;
     const int R0 = rb * BM;
     const int Rw = R0 + 32 * w;
     const int R = Rw + c;
@@ -1950,7 +1950,7 @@ void dq_kernel_h(BwdArgs a, SplitPlan sp) {
     const RowJob job = map_row_job<SPLIT>(sp, a.nrb, a.B * a.Hkv);
     const int rb = job.rb;
     const int hkv = job.grp % a.Hkv, b = job.grp / a.Hkv;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, c = l & 31;
     const int R0 = rb * BM;
     const int Rw = R0 + 32 * w;
     const int R = Rw + c;
@@ -2191,7 +2191,7 @@ __global__ __launch_bounds__(128 * RT) void dq_ds_kernel(BwdArgs a) {
     const Work wk = map_block((nrt + RT - 1) / RT, a.ngrp, true);
     const int gg = a.grp0 + wk.grp;                   // the (batch, KV head) group
     const int hkv = gg % a.Hkv, b = gg / a.Hkv;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, c = l & 31;
     const int rt0 = RT * wk.blk;
     const int W = a.window;
     const size_t grp = (size_t)gg;

@@ -42,7 +42,7 @@ __device__ __forceinline__ void fill_rows(OP* tile, const OP* src, int row0, int
     using TL = Tile<OP, BK>;
     constexpr int WL = ROWS * TL::CPR / 64;
     static_assert(ROWS * TL::CPR % 64 == 0 && WL % NW == 0, "whole wave loads per wave");
-    const int l = lane_id(), w = threadIdx.x >> 6;
+    const int l = lane_id(), w = wave_id();
 #pragma unroll
     for (int i = 0; i < WL / NW; ++i) {
         const int j = i * NW + w;
@@ -60,7 +60,7 @@ __device__ __forceinline__ void fill_rows_at(unsigned tile, const OP* src, int r
     using TL = Tile<OP, BK>;
     constexpr int WL = ROWS * TL::CPR / 64;
     static_assert(ROWS * TL::CPR % 64 == 0 && WL % NW == 0, "whole wave loads per wave");
-    const int l = lane_id(), w = threadIdx.x >> 6;
+    const int l = lane_id(), w = wave_id();
 #pragma unroll
     for (int i = 0; i < WL / NW; ++i) {
         const int j = i * NW + w;
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NE_QKV_WPE)
         }
     }
     const int m0 = mb * BM, n0 = nb * BN;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, c = l & 31;
     const _Float16* x = (const _Float16*)a.x;   // 16-bit words; the MFMA reinterprets them as TI
     const _Float16* wt = (const _Float16*)a.w;
 
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void q
         }
     }
     const int m0 = mb * BM, n0 = nb * BN;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, h = l >> 5, c = l & 31;
     const int wt_ = w % WT, wf = w / WT;        // token block of 64, feature block of 160
     const _Float16* x = (const _Float16*)a.x;   // 16-bit words; the MFMA reinterprets them as TI
     const _Float16* wt = (const _Float16*)a.w;

@@ -95,7 +95,8 @@ typedef enum {
  *                             and to the backward (and to the backward's workspace query: it adds
  *                             slot-ordered copies of q and k, read by the QK-norm backward).  No
  *                             effect with rope_base <= 0.  The KV-cache, decode and QKV-projection
- *                             calls take no flags and use adjacent pairs. */
+ *                             calls take no flags: they select this pairing with the options
+ *                             struct's rope_half_split (ne_attn_opts_t, below). */
 #define NE_FLAG_NONDETERMINISTIC 0x1u
 #define NE_FLAG_BF16_OPERANDS 0x2u
 #define NE_FLAG_ROPE_HALF_SPLIT 0x4u
@@ -119,13 +120,15 @@ typedef enum {
  *   backward: the rotated, scaled copies of q, k, dO (and v), Delta = rowsum(dO * o), the
  *             log2-scaled lse, the per-row 1/rms of the QK norm, the dO scales; with
  *             NE_FLAG_NONDETERMINISTIC the fp32 dQ accumulator [B][Hq][T][head_dim]; with
- *             NE_FLAG_STORE_DS the stored dS; otherwise (16-bit) the split regions of the dQ pass;
+ *             NE_FLAG_STORE_DS the stored dS; otherwise (16-bit) the split regions of the dQ and
+ *             dK/dV passes;
  *             with NE_FLAG_ROPE_HALF_SPLIT and rope_base > 0 copies of q and k in in_dtype.
- * Split row blocks: when a call has few causal row blocks per CU, the longest blocks of the forward
- * and of the recomputing dQ pass are cut into 2-4 ranges of keys run by separate workgroups; the
- * last to finish combines the others' partial results in a fixed order (the result does not depend
- * on which finishes last).  The plan depends only on the shape; a window shorter than T or the QK
- * norm (dQ pass) turns it off.
+ * Split blocks: when a call has few causal blocks per CU, the longest row blocks of the forward and
+ * of the recomputing dQ pass are cut into 2-4 ranges of keys, and the dK/dV pass of the default
+ * backward runs single key blocks instead of mirrored pairs, the longest cut into 2-4 ranges of row
+ * tiles; the pieces of a block run on separate workgroups and the last to finish combines the others'
+ * partial results in a fixed order (the result does not depend on which finishes last).  The plan
+ * depends only on the shape; a window shorter than T turns it off, and the QK norm the dQ pass's.
  * For is_bwd != 0 the size returned is at least the forward's, so a backward workspace of that size
  * is also a valid forward workspace for the same arguments: the table sits at the same place, so
  * one ne_rope_table_init serves both calls. */
@@ -281,8 +284,8 @@ ne_status_t ne_rope_attn_decode(const void* q, const void* cache, size_t cache_b
 /* The same decode for callers that cannot allocate (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): no workspace argument.  The split partials live in a
  * scratch array inside the library, NE_DECODE_SCRATCH_BYTES (64 MiB) per GPU, held until the process
- * ends; its address on the current device is looked up on the first call there and kept (the one
- * piece of library state besides the error message).  Shapes whose partials
+ * ends; its address on the current device is looked up on the first call there and kept (library
+ * state, like the error message and the cache of split plans).  Shapes whose partials
  * (ne_rope_attn_decode_workspace_bytes) exceed it are rejected with NE_ERR_WORKSPACE before anything
  * is enqueued.  Nothing is allocated or freed.  Every call on a device shares that device's array, so
  * calls that overlap on one device (different streams, or threads) race: order them on one stream.

@@ -798,8 +798,8 @@ void fwd_kernel_h(FwdArgs a, SplitPlan sp) {
         mf = m_run > 0.5f * kMFloor ? m_run : 0.f;
         fmf = fold_frag(-mf, h);
     };
-    // mask of tile j (if it crosses a diagonal or a window edge), then the row max
-    auto mask_max = [&](int j) {
+    // mask of tile j (if it crosses a diagonal or a window edge)
+    auto mask = [&](int j) {
         const int n0 = j * BN;
         if (n0 + BN - 1 > wave_tmin || wave_tmax - n0 >= W) {
 #pragma unroll
@@ -808,12 +808,19 @@ void fwd_kernel_h(FwdArgs a, SplitPlan sp) {
                 for (int r = 0; r < 16; ++r)
                     if (!visible(n0 + 32 * mb + acc_row(r, h), t_lane, W)) s[mb][r] = -INFINITY;
         }
+    };
+    // row max of the scores in s (relative to mf)
+    auto row_max = [&]() {
         float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
         for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
         return max_halves(mx);
+    };
+    auto mask_max = [&](int j) {
+        mask(j);
+        return row_max();
     };
     // phase 2: scores of tile j, products alternating between the two 32-key accumulators
     auto phase2 = [&](int j, auto SK) {
@@ -874,9 +881,14 @@ void fwd_kernel_h(FwdArgs a, SplitPlan sp) {
                              hp[4 * kk + 2][0], hp[4 * kk + 2][1], hp[4 * kk + 3][0], hp[4 * kk + 3][1]};
         return ps;
     };
-    // after the scores of tile j are in s: mask, max and the (rare) refresh of m
+    // after the scores of tile j are in s: the mask and, while a row of the wave has not seen a key
+    // (m at the floor), the max and the refresh of m.  Once every row has its m, the scores are not
+    // scanned: a tile whose probabilities exceed the fp16 range (a score 16 or more above m, rare) is
+    // caught by its row sum in phase 1 and redone there (overflow below)
     auto refresh = [&](int j) {
-        const float mx = mask_max(j);
+        mask(j);
+        if (__builtin_amdgcn_ballot_w64(m_run <= 0.5f * kMFloor) == 0) return;
+        const float mx = row_max();
         if (__builtin_amdgcn_ballot_w64(mf + mx > m_run + TAU) != 0) {  // raise m to this tile's max
             const float m_new = fmaxf(m_run, mf + mx);
             apend = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -901,7 +913,22 @@ void fwd_kernel_h(FwdArgs a, SplitPlan sp) {
         constexpr int s = decltype(S)::value;
         sync_fill(it, S);
         if (it >= first - 1 && it <= last + 1) {
-            const float ps = phase1(it, PAR, IC<1>{}, IC<(s + 2) % NST>{});
+            float ps = phase1(it, PAR, IC<1>{}, IC<(s + 2) % NST>{});
+            if (it <= last && __builtin_amdgcn_ballot_w64(!(ps < INFINITY)) != 0) {
+                // overflow: a probability of tile it exceeded fp16.  O (tiles up to it - 1, just
+                // completed) and l use the old m: raise m to this tile's max, rescale both, redo the
+                // probabilities of tile it
+                const float m_new = fmaxf(m_run, mf + row_max());
+                const float al = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                rebase();
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= al;
+                l_run *= al;
+                ps = phase1(it, PAR, IC<0>{}, IC<(s + 2) % NST>{});
+            }
             l_run += it <= last ? ps : 0.f;  // iteration last + 1 only finishes the product
             if (it + 1 <= last) phase2(it + 1, IC<(s + 1) % NST>{});
             if (pend) {  // O now holds every tile whose probabilities used the old m

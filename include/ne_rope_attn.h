@@ -108,7 +108,10 @@ typedef enum {
  * Range of 16-bit inputs: k and v become fp16 MFMA operands, so |k|, |v| must stay below 65504
  * (values under 2^-14 lose relative precision as fp16 subnormals).  dO is scaled per (batch, KV
  * head) group by a power of two before its conversion to fp16 and the gradients are scaled back, so
- * any finite dO is supported. */
+ * any finite dO is supported.  Scores are formed from fp16 operands, so a score carries an error of
+ * about 2^-11 of |q'| |k'| / sqrt(head_dim): rows whose logits reach ~100 get probabilities accurate
+ * to a few percent (their o and lse still meet 2e-3 of scale; dq of such nearly one-hot rows can
+ * cancel to a few percent of its scale).  The fp32 path does not have this limit. */
 
 /* Bytes of device workspace a forward (is_bwd = 0) or backward (is_bwd != 0) call needs for these
  * arguments and flags (256-byte aligned base recommended; 16 is required).  0 for invalid

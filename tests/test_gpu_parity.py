@@ -174,6 +174,36 @@ def test_parity_group_extremes(shape, variant):
     parity(q, k, v, dO, 1.0e4, out_dt, in_dt, flags=flags)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("window", [0, 70])
+@pytest.mark.parametrize("in_dt", [torch.bfloat16, torch.float16])
+def test_rising_scores_take_the_overflow_path(D, window, in_dt):
+    """Scores that rise by about 30 per 64-key tile along each row (keys growing along one direction,
+    RoPE off): every tile after a row's first holds probabilities beyond the fp16 range relative to
+    the reference maximum kept so far, so the forward raises the maximum and redoes the tile's
+    probabilities at each step.  o, lse, dk and dv against the oracle at the usual bars.  dq is not
+    compared: with logits near 140 the fp16 operands shift each score by a few hundredths, the rows
+    are nearly one-hot, and dq = sum dS k (|k| up to 400) cancels to a few percent of its scale --
+    a limit of 16-bit operands on such inputs that the fp32 path does not have."""
+    B, T, Hq, Hkv = 1, 300, 4, 2
+    g = torch.Generator().manual_seed(88 + D + window)
+    q = 0.05 * torch.randn(B, T, Hq, D, generator=g, dtype=torch.float64)
+    k = 0.05 * torch.randn(B, T, Hkv, D, generator=g, dtype=torch.float64)
+    v = torch.randn(B, T, Hkv, D, generator=g, dtype=torch.float64)
+    dO = torch.randn(B, T, Hq, D, generator=g, dtype=torch.float64)
+    q[..., 0] += 4.0
+    k[..., 0] += 0.47 * D ** 0.5 / 4.0 * torch.arange(T, dtype=torch.float64)[None, :, None]
+    q, k, v, dO = (t.to(in_dt) for t in (q, k, v, dO))
+    o, lse, dq, dk, dv = run_gpu(q, k, v, dO, 0.0, torch.float32, window=window)
+    ro, rlse = oracle.fwd(f64(q), f64(k), f64(v), 0.0, window=window)
+    rdq, rdk, rdv = oracle.bwd(f64(q), f64(k), f64(v), f64(dO), 0.0, window=window)
+    assert float(np.max(rlse[:, :, -1])) > 100.0      # the last rows' scores reach far past the first tiles'
+    gscale = zero_ref_scale(in_dt, (rdq, rdk, rdv))
+    for name, gv, rv in (("o", o, ro), ("lse", lse, rlse), ("dk", dk, rdk), ("dv", dv, rdv)):
+        check(name, gv, rv, in_dt, torch.float32, zero_scale=gscale)
+    assert torch.isfinite(dq).all()
+
+
 def ds_group_bytes(T, G):
     nrt, nkb = -(-T * G // 64), -(-T // 64)
     return sum(1 for kb in range(nkb) for rt in range(nrt) if rt >= kb * G) * 8192

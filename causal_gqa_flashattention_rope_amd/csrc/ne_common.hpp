@@ -465,8 +465,10 @@ __device__ __forceinline__ void lds_fill_vt_at(unsigned tile, const _Float16* sr
         if (WL % NW != 0 && j >= WL) break;
         const int q = 64 * j + l;
         const int r = q / CPR, sl = q % CPR;
-        const _Float16* g = src + (size_t)r * Tp + n0 + 8 * VtTile<BN>::slot(r, sl);
-        dma16(g, __builtin_amdgcn_readfirstlane(tile + 1024u * (unsigned)j));
+        // per-lane byte offset (the same for every tile; below D * Tp * 2 < 2^32) from the tile's
+        // uniform base src + n0
+        const unsigned off = ((unsigned)r * (unsigned)Tp + 8u * (unsigned)VtTile<BN>::slot(r, sl)) * 2u;
+        dma16_s(off, src + n0, __builtin_amdgcn_readfirstlane(tile + 1024u * (unsigned)j));
     }
 }
 

@@ -1433,7 +1433,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
     // registers the dQ product needs)
     auto chain = [&](const OP* rows, auto KT) {
         constexpr bool FROM_TILE = decltype(KT)::value;
-        constexpr int AH = W4 ? 2 : (KS < 4 ? KS : 4);
+        constexpr int AH = W4 ? 2 : (KS < 2 ? KS : 2);
         half8 fr[KS];
 #pragma unroll
         for (int i = 0; i < AH; ++i) fr[i] = row_frag_sw<OP, D>(rows, 32 * rh + c, i, h);
@@ -1533,16 +1533,22 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
         constexpr int RL = decltype(ROLE)::value;
         int natom = 0;  // AT: atomic adds this wave issued after its share of the latest fill
         half8 pcar[2] = {};  // role 0: P of tile s, formed in step s, multiplied into dV^T in step s + 1
-        for (int s = 0; s <= ntiles + (AT ? 1 : 0); ++s) {
+        // step s with K = s % UN known at compile time (UN a multiple of the ring stages and of the two
+        // P-buffer parities), so stage and parity offsets are constants
+        constexpr int UN = NST == 4 ? 4 : 6;
+        auto step = [&](int s, auto K) {
+            constexpr int k = decltype(K)::value;
+            constexpr int S0 = k % NST, SM1 = (k + UN - 1) % NST, SA = (k + AHEAD) % NST;
+            constexpr int P0 = k & 1, PM1 = (k + 1) & 1;
             // tile s has landed (tile s + 1 may still be in flight); the P of tile s - 1 is in
-            // pbuf[(s - 1) & 1]; every wave is done with tile s - 2 and with pbuf[s & 1]
+            // pbuf[PM1]; every wave is done with tile s - 2 and with pbuf[P0]
             // (with DS, role 1's two dS stores of the previous step are its most recent operations;
             // with AT, the fill is one step ahead and role 0's atomic adds of the previous step were
             // issued after it: vector memory operations complete in order)
             if constexpr (AT) lds_fill_wait_keep_atomics(natom);
             else lds_fill_wait_keep((AHEAD == 2 && s + 1 < ntiles ? per_fill : 0) + (DS && RL == 1 && s >= 2 ? 2 : 0));
             natom = 0;
-            if (s + AHEAD < ntiles) fill((s + AHEAD) % NST, rstart + (s + AHEAD) * BMR);
+            if (s + AHEAD < ntiles) fill(SA, rstart + (s + AHEAD) * BMR);
             if constexpr (RL == 0) {
                 if constexpr (AT) {
                     // dQ of this wave's 32 rows of tile s - 2 (whose dS^T the role-1 waves left in
@@ -1552,7 +1558,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
                     // above is exact
                     const int j = s - 2;
                     if (j >= 0 && j < ntiles && (NDB >= 2 || kq == 0) && (active_kq(j, 0) || active_kq(j, 1))) {
-                        const OP* dt = dstile + (s & 1) * (BN * BMR);
+                        const OP* dt = dstile + P0 * (BN * BMR);
                         half8 af[4];
 #pragma unroll
                         for (int kk = 0; kk < 4; ++kk) af[kk] = tr_frag_f16_sw<64>((const _Float16*)dt, kk, 32 * rh);
@@ -1576,13 +1582,13 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
                 // dV^T += dO^T P of tile s - 1 (P kept from the previous step), then S and P of tile s:
                 // the exponentials come last, while role 1 runs its products
                 if (s >= 1 && active(s - 1)) {
-                    const OP* Os1 = lds + ((s - 1) % NST) * 2 * TILE + TILE;
+                    const OP* Os1 = lds + SM1 * 2 * TILE + TILE;
                     half8 tf0[NDB];
                     tr_frags0(Os1, tf0);
                     product2(Os1, tf0, pcar, acc);
                 }
                 if (s < ntiles && active(s)) {
-                    const int st = s % NST;
+                    constexpr int st = S0;
                     const OP* Qs = lds + st * 2 * TILE;
                     const int Rh = rstart + s * BMR + 32 * rh;
                     const half8 fl = fold_frag(-rowv[st][0][32 * rh + c], h);  // ahead of the chain
@@ -1599,12 +1605,12 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
                     for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
                         for (int j = 0; j < 8; ++j) pcar[cc][j] = (_Float16)__builtin_amdgcn_exp2f(x[8 * cc + j]);
-                        pbuf[s & 1][kq][rh][cc][l] = pcar[cc];
+                        pbuf[P0][kq][rh][cc][l] = pcar[cc];
                     }
                 }
             } else {
                 if (AT && s >= 1 && !active(s - 1)) {  // this quadrant of dS^T is zero
-                    char* dt = reinterpret_cast<char*>(dstile + ((s - 1) & 1) * (BN * BMR));
+                    char* dt = reinterpret_cast<char*>(dstile + PM1 * (BN * BMR));
 #pragma unroll
                     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
@@ -1617,7 +1623,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
                     __builtin_nontemporal_store(half8{}, &dsg[(dsb + s - 1) * 512 + ds1]);
                 }
                 if (s >= 1 && active(s - 1)) {
-                    const int st = (s - 1) % NST;
+                    constexpr int st = SM1;
                     const OP* Qs = lds + st * 2 * TILE;
                     const OP* Os = Qs + TILE;
                     const half8 fd = fold_frag(-rowv[st][1][32 * rh + c], h);  // ahead of the chain
@@ -1628,7 +1634,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
                     half8 dsf[2];
 #pragma unroll
                     for (int cc = 0; cc < 2; ++cc) {
-                        const half8 pv = pbuf[(s - 1) & 1][kq][rh][cc][l];
+                        const half8 pv = pbuf[PM1][kq][rh][cc][l];
 #pragma unroll
                         for (int j = 0; j < 8; ++j) dsf[cc][j] = (_Float16)((float)pv[j] * y[8 * cc + j]);
                     }
@@ -1639,7 +1645,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
                     if constexpr (AT) {
                         // dS^T as [key][row] (swizzled 64 x 64 tile): lane (h, c) holds key 32 kq + c and,
                         // per k-step cc, the rows 32 rh + 16 cc + 8 (j / 4) + 4 h + j % 4
-                        char* dt = reinterpret_cast<char*>(dstile + ((s - 1) & 1) * (BN * BMR));
+                        char* dt = reinterpret_cast<char*>(dstile + PM1 * (BN * BMR));
 #pragma unroll
                         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
@@ -1649,6 +1655,22 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
                     }
                     product2(Qs, tf0, dsf, acc);
                 }
+            }
+        };
+        const int send = ntiles + (AT ? 1 : 0);
+        for (int s0 = 0; s0 <= send; s0 += UN) {
+            step(s0, IC<0>{});
+            if (s0 + 1 > send) break;
+            step(s0 + 1, IC<1>{});
+            if (s0 + 2 > send) break;
+            step(s0 + 2, IC<2>{});
+            if (s0 + 3 > send) break;
+            step(s0 + 3, IC<3>{});
+            if constexpr (UN == 6) {
+                if (s0 + 4 > send) break;
+                step(s0 + 4, IC<4>{});
+                if (s0 + 5 > send) break;
+                step(s0 + 5, IC<5>{});
             }
         }
         };

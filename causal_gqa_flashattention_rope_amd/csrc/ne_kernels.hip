@@ -2042,14 +2042,16 @@ void dq_kernel_h(BwdArgs a, SplitPlan sp) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[db] = floatx16{};
 
-    for (int it = j0; it < ntiles; ++it) {
-        const OP* Ks = lds + ((it - j0) & 1) * 2 * TILE;
+    // tile it, with its ring stage P = (it - j0) & 1 known at compile time (LDS offsets are constants)
+    auto tile = [&](int it, auto PS) {
+        constexpr int P = decltype(PS)::value;
+        const OP* Ks = lds + P * 2 * TILE;
         const OP* Vs = Ks + TILE;
         lds_fill_wait();
-        if (it + 1 < ntiles) fill(it + 1, (it + 1 - j0) & 1);
+        if (it + 1 < ntiles) fill(it + 1, P ^ 1);
         const int n0 = it * BN;
-        if (n0 > wave_tmax) continue;                 // every row of this wave precedes the tile
-        if (wave_tmin - (n0 + BN - 1) >= W) continue;  // the tile is older than every row's window
+        if (n0 > wave_tmax) return;                 // every row of this wave precedes the tile
+        if (wave_tmin - (n0 + BN - 1) >= W) return;  // the tile is older than every row's window
 
         // the tile crosses some row's diagonal or window edge
         const bool diag = n0 + BN - 1 > wave_tmin || wave_tmax - n0 >= W;
@@ -2119,6 +2121,11 @@ void dq_kernel_h(BwdArgs a, SplitPlan sp) {
             if (i + AHD < NQ) kt[i + AHD] = rk(i + AHD);
         }
         __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int it = j0; it < ntiles; it += 2) {
+        tile(it, IC<0>{});
+        if (it + 1 >= ntiles) break;
+        tile(it + 1, IC<1>{});
     }
 
     if (SPLIT && job.np > 1) {

@@ -1433,7 +1433,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
     // registers the dQ product needs)
     auto chain = [&](const OP* rows, auto KT) {
         constexpr bool FROM_TILE = decltype(KT)::value;
-        constexpr int AH = W4 ? 2 : (KS < 2 ? KS : 2);
+        constexpr int AH = W4 || MODE == 0 ? (KS < 2 ? KS : 2) : (KS < 4 ? KS : 4);
         half8 fr[KS];
 #pragma unroll
         for (int i = 0; i < AH; ++i) fr[i] = row_frag_sw<OP, D>(rows, 32 * rh + c, i, h);
@@ -1533,13 +1533,16 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
         constexpr int RL = decltype(ROLE)::value;
         int natom = 0;  // AT: atomic adds this wave issued after its share of the latest fill
         half8 pcar[2] = {};  // role 0: P of tile s, formed in step s, multiplied into dV^T in step s + 1
-        // step s with K = s % UN known at compile time (UN a multiple of the ring stages and of the two
-        // P-buffer parities), so stage and parity offsets are constants
-        constexpr int UN = NST == 4 ? 4 : 6;
+        // step s; in the default design with K = s % UN known at compile time (UN a multiple of the ring
+        // stages and of the two P-buffer parities), so stage and parity offsets are constants (the
+        // stored-dS and atomic designs, whose registers are fuller, keep one copy of the step)
+        constexpr bool UNR = MODE == 0;
+        constexpr int UN = !UNR ? 1 : NST == 4 ? 4 : 6;
         auto step = [&](int s, auto K) {
             constexpr int k = decltype(K)::value;
-            constexpr int S0 = k % NST, SM1 = (k + UN - 1) % NST, SA = (k + AHEAD) % NST;
-            constexpr int P0 = k & 1, PM1 = (k + 1) & 1;
+            const int S0 = UNR ? k % NST : s % NST, SM1 = UNR ? (k + UN - 1) % NST : (s + NST - 1) % NST;
+            const int SA = UNR ? (k + AHEAD) % NST : (s + AHEAD) % NST;
+            const int P0 = UNR ? k & 1 : s & 1, PM1 = UNR ? (k + 1) & 1 : (s + 1) & 1;
             // tile s has landed (tile s + 1 may still be in flight); the P of tile s - 1 is in
             // pbuf[PM1]; every wave is done with tile s - 2 and with pbuf[P0]
             // (with DS, role 1's two dS stores of the previous step are its most recent operations;
@@ -1588,7 +1591,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
                     product2(Os1, tf0, pcar, acc);
                 }
                 if (s < ntiles && active(s)) {
-                    constexpr int st = S0;
+                    const int st = S0;
                     const OP* Qs = lds + st * 2 * TILE;
                     const int Rh = rstart + s * BMR + 32 * rh;
                     const half8 fl = fold_frag(-rowv[st][0][32 * rh + c], h);  // ahead of the chain
@@ -1623,7 +1626,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
                     __builtin_nontemporal_store(half8{}, &dsg[(dsb + s - 1) * 512 + ds1]);
                 }
                 if (s >= 1 && active(s - 1)) {
-                    constexpr int st = SM1;
+                    const int st = SM1;
                     const OP* Qs = lds + st * 2 * TILE;
                     const OP* Os = Qs + TILE;
                     const half8 fd = fold_frag(-rowv[st][1][32 * rh + c], h);  // ahead of the chain
@@ -1660,6 +1663,7 @@ void dkdv_kernel_h(BwdArgs a, SplitPlan sp) {
         const int send = ntiles + (AT ? 1 : 0);
         for (int s0 = 0; s0 <= send; s0 += UN) {
             step(s0, IC<0>{});
+            if constexpr (UN == 1) continue;
             if (s0 + 1 > send) break;
             step(s0 + 1, IC<1>{});
             if (s0 + 2 > send) break;

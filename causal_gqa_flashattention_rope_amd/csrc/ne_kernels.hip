@@ -1157,14 +1157,15 @@ void dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int s0 = 0; s0 < NST - 1; ++s0)
             if (s0 < ntiles) fill(s0, rstart + s0 * BMR);
-        for (int it = 0; it < ntiles; ++it) {
-            const int st = it % NST;
+        // tile it, with its ring stage st = it % NST known at compile time (LDS offsets are constants)
+        auto tile = [&](int it, auto ST) {
+            constexpr int st = decltype(ST)::value;
             const OP* Qs = lds + st * 2 * TILE;
             const OP* Os = Qs + TILE;
             const int R0 = rstart + it * BMR;
             // barrier 1: tile it is in LDS (the fills of the younger tiles may still be in flight)
             lds_fill_wait_keep(per_fill * min(NST - 2, ntiles - 1 - it));
-            if (it + NST - 1 < ntiles) fill((it + NST - 1) % NST, R0 + (NST - 1) * BMR);
+            if (it + NST - 1 < ntiles) fill((st + NST - 1) % NST, R0 + (NST - 1) * BMR);
             const int Rh = R0 + 32 * rh;                       // first row of this wave's half
             const bool active = min(Rh + 31, TG - 1) >= n0 * G && Rh < wlim;
             const bool need_mask = Rh < (n0 + 31) * G || Rh + 32 > wedge;
@@ -1272,6 +1273,15 @@ void dkdv_kernel(BwdArgs a) {
                         for (int s2 = 0; s2 < 16; ++s2)
                             acc[db] = M::mma(tr_frag_f32_sw<D>(trt, rh, s2, 32 * db), src[s2], acc[db]);
                 }
+            }
+        };
+        for (int it0 = 0; it0 < ntiles; it0 += NST) {
+            tile(it0, IC<0>{});
+            if (it0 + 1 >= ntiles) break;
+            tile(it0 + 1, IC<1>{});
+            if constexpr (NST == 3) {
+                if (it0 + 2 >= ntiles) break;
+                tile(it0 + 2, IC<2>{});
             }
         }
 
